@@ -1,0 +1,206 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) dropless top-k MoE expert layer.
+ *
+ * One layer, forward and backward, on one GPU: a softmax top-k router, a
+ * row-wise dispatch of every (token, slot) straight into its expert's rows,
+ * routing metadata that never leaves the GPU, SwiGLU experts run as grouped
+ * GEMMs (bf16 or MXFP8 on MFMA, fp32 on the vector units) and a weighted
+ * combine.  Sources, by page and section:
+ *   - "OLMoE in HF Transformers" walkthrough, section 2 (router) and section 3
+ *     (expert layer: 3-D expert weights; per expert gate/up, SiLU(gate)*up,
+ *     down, times the top-k weight, index_add back to the token);
+ *   - olmoforge README, module table (row-wise expert parallel: token rows
+ *     written straight into the expert input buffer; grouped GEMM: the small
+ *     per-expert matmuls merged into one kernel; GPU-resident routing table:
+ *     metadata stays on the device and the CPU never waits for a copy) and
+ *     its MXFP8 snippet (block of 32 with one shared scale, e4m3 max 448);
+ *   - OLMo-core 3 release summary (wedoingai), features and technical
+ *     principle sections: paired SwiGLU backward, bf16-rounded weight
+ *     gradients.
+ *
+ * Conventions shared by every entry point
+ *   - Shapes: T tokens (rows of x), d model width, E experts, f expert
+ *     width, k experts per token, R = T*k routed rows.
+ *   - All buffers are device memory owned by the caller, dense and row-major,
+ *     16-byte aligned.  The library allocates nothing and keeps no state
+ *     between calls; a call may use the caller's workspace `ws` (size from
+ *     moe_workspace_size) and must not overlap another call using the same
+ *     workspace.
+ *   - Every call only enqueues kernels on `stream` (a hipStream_t; NULL is
+ *     the default stream) and returns; nothing is copied back to the host and
+ *     nothing synchronises.  Routing metadata (counts, offsets, rows) is read
+ *     on the device by the kernels that need it.
+ *   - dtype: MOE_F32 or MOE_BF16, the storage type of x, the weights and every
+ *     activation and gradient tensor.  Logits, top-k weights, dw and dlogits
+ *     are always float32; indices and metadata are int32.
+ *   - prec: MOE_PREC_F32 (dtype must be MOE_F32), MOE_PREC_BF16 (dtype
+ *     MOE_BF16) or MOE_PREC_MXFP8 (dtype MOE_BF16; expert forward and dgrad
+ *     GEMMs in e4m3 with one power-of-two E8M0 scale per 32 elements along
+ *     the contraction axis, weight gradients in bf16).
+ *   - Errors are detected on the host before anything is enqueued and come
+ *     back as a negative status; nothing is launched then.  There is no
+ *     silent fallback to another precision or algorithm.  Values the host
+ *     cannot see (indices inside topk_idx, finiteness of logits) are
+ *     preconditions: topk_idx entries must lie in [0, E) and be distinct
+ *     within a token.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_NULL = -1,        /* a required pointer is NULL */
+  MOE_ERR_SHAPE = -2,       /* a size is non-positive, or T*k / sizes overflow int32 */
+  MOE_ERR_DTYPE = -3,       /* unknown dtype/prec, or a dtype/prec pair that does not exist */
+  MOE_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned */
+  MOE_ERR_WORKSPACE = -5,   /* ws_bytes below moe_workspace_size */
+  MOE_ERR_UNSUPPORTED = -6, /* E > 256, k > min(E, 16), d or f not a multiple of 64 */
+  MOE_ERR_LAUNCH = -7       /* the HIP runtime rejected a launch */
+};
+
+enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 };
+enum moe_prec { MOE_PREC_F32 = 0, MOE_PREC_BF16 = 1, MOE_PREC_MXFP8 = 2 };
+
+/* moe_route flags */
+#define MOE_ROUTE_LOGITS_IN 0x1u   /* logits are an input: x and Wr are not read */
+/* moe_grouped_ffn_bwd / moe_dispatch_bwd / moe_route_bwd flags */
+#define MOE_ACCUMULATE 0x2u        /* add into the output (dW*, dx, dWr) instead of overwriting */
+
+/* Operation ids for moe_workspace_size. */
+enum moe_op {
+  MOE_OP_ROUTE = 0, MOE_OP_DISPATCH = 1, MOE_OP_FFN_FWD = 2, MOE_OP_COMBINE = 3,
+  MOE_OP_COMBINE_BWD = 4, MOE_OP_FFN_BWD = 5, MOE_OP_DISPATCH_BWD = 6, MOE_OP_ROUTE_BWD = 7
+};
+
+/*
+ * moe_route -- router logits, softmax and top-k.
+ * HF OLMoE walkthrough, section 2: logits = x . Wr (router weight without
+ * bias; the page stores it as (E, d), here it is its transpose Wr[d,E]),
+ * softmax over the experts in float32, the top_k experts per token, the
+ * softmax probabilities of the chosen experts as weights (no
+ * renormalisation, the page's default).
+ *   x[T,d] (dtype), Wr[d,E] (dtype) -> logits[T,E] f32 (written unless
+ *   MOE_ROUTE_LOGITS_IN, then read), topk_idx[T,k] i32, topk_w[T,k] f32.
+ *   Slots are ordered by (logit desc, expert index asc): ties go to the
+ *   lower index; selection is made on the float32 logits.
+ *   Limits: 1 <= E <= 256, 1 <= k <= min(E, 16).  d % 64 == 0.
+ */
+int moe_route(const void* x, const void* Wr, int T, int d, int E, int k, int dtype,
+              unsigned flags, float* logits, int32_t* topk_idx, float* topk_w,
+              void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_dispatch -- routing metadata and row-wise dispatch.
+ * olmoforge README (row-wise expert parallel, GPU-resident routing table):
+ * every (token t, slot j) gets one row of its expert's segment and x[t] is
+ * copied straight there; there is no separate sort of the activations.
+ *   counts[E]     rows per expert
+ *   offsets[E+1]  exclusive scan of counts; offsets[E] = R
+ *   dest_row[T,k] row of (t, j): offsets[e] + number of tokens t' < t routed
+ *                 to e (rows of one expert are in ascending token order)
+ *   src_token[R]  inverse map: the token of every row
+ *   Xs[R,d]       Xs[dest_row[t,j]] = x[t].  prec MXFP8: Xs holds e4m3 codes
+ *                 (1 byte each) and Xs_scale[R, d/32] the E8M0 exponent bytes
+ *                 (biased by 127) of every 32-element block along d; in other
+ *                 precisions Xs has the dtype and Xs_scale is ignored.
+ *   Workspace: moe_workspace_size(MOE_OP_DISPATCH, ...).
+ */
+int moe_dispatch(const void* x, const int32_t* topk_idx, int T, int d, int E, int k,
+                 int dtype, int prec, int32_t* counts, int32_t* offsets,
+                 int32_t* dest_row, int32_t* src_token, void* Xs, uint8_t* Xs_scale,
+                 void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_grouped_ffn_fwd -- all SwiGLU experts as grouped GEMMs.
+ * HF OLMoE walkthrough, section 3; olmoforge README (grouped GEMM).  For each
+ * expert e and its rows r in [offsets[e], offsets[e+1]):
+ *   Hg = Xs.Wg[e], Hu = Xs.Wu[e], A = silu(Hg) * Hu, Ys = A.Wd[e]
+ *   Wg, Wu [E,d,f], Wd [E,f,d] (dtype); Hg, Hu, A [R,f], Ys [R,d] (dtype),
+ *   stored from float32 accumulators (A from the unrounded Hg, Hu).
+ *   offsets is read on the device.  prec MXFP8: Xs/Xs_scale as written by
+ *   moe_dispatch; weights are block-quantised inside (Wg, Wu along d, Wd
+ *   along f) and A along f before the down GEMM.
+ */
+int moe_grouped_ffn_fwd(const void* Xs, const uint8_t* Xs_scale, const int32_t* offsets,
+                        int T, int k, int d, int f, int E, const void* Wg, const void* Wu,
+                        const void* Wd, int dtype, int prec, void* Hg, void* Hu, void* A,
+                        void* Ys, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_combine -- weighted un-dispatch.
+ * HF OLMoE walkthrough, section 3 (multiply by the top-k weight and
+ * index_add back to the token): y[t] = sum_j topk_w[t,j] * Ys[dest_row[t,j]],
+ * summed in float32 in slot order, stored in dtype.  y[T,d].
+ */
+int moe_combine(const void* Ys, const float* topk_w, const int32_t* dest_row, int T, int d,
+                int k, int dtype, void* y, void* stream);
+
+/*
+ * moe_combine_bwd -- backward of moe_combine for upstream gradient dY[T,d]:
+ *   dYs[dest_row[t,j]] = topk_w[t,j] * dY[t]       (dtype, [R,d])
+ *   dtopk_w[t,j]       = <dY[t], Ys[dest_row[t,j]]> (f32, [T,k])
+ */
+int moe_combine_bwd(const void* dY, const void* Ys, const float* topk_w,
+                    const int32_t* dest_row, int T, int d, int k, int dtype, void* dYs,
+                    float* dtopk_w, void* stream);
+
+/*
+ * moe_grouped_ffn_bwd -- backward of moe_grouped_ffn_fwd.
+ * OLMo-core 3 release summary: paired SwiGLU backward (gate and up gradients
+ * in one pass), bf16-rounded weight gradients.  Per expert e:
+ *   dA  = dYs.Wd[e]^T
+ *   dHg = dA * Hu * silu'(Hg), dHu = dA * silu(Hg)  -> dH[R,2f]: columns
+ *         [0,f) hold dHg, [f,2f) hold dHu (dtype)
+ *   dXs = dHg.Wg[e]^T + dHu.Wu[e]^T                  -> dXs[R,d] (dtype)
+ *   dWd[e] = A^T.dYs, dWg[e] = Xs^T.dHg, dWu[e] = Xs^T.dHu, summed in float32
+ *   over the expert's rows and stored in dtype (an expert with no rows gets
+ *   zeros; with MOE_ACCUMULATE the sum is added to the existing values).
+ *   Xs: the dispatched rows (bf16/fp32).  prec MXFP8: the two dgrad GEMMs are
+ *   block-quantised (dYs and Wd along d; dH, Wg, Wu along f) and the weight
+ *   gradients read the bf16 token rows x[src_token[r]] instead of Xs.
+ */
+int moe_grouped_ffn_bwd(const void* dYs, const void* Xs, const void* x,
+                        const int32_t* src_token, const void* Hg, const void* Hu,
+                        const void* A, const int32_t* offsets, int T, int k, int d, int f,
+                        int E, const void* Wg, const void* Wu, const void* Wd, int dtype,
+                        int prec, unsigned flags, void* dH, void* dXs, void* dWg, void* dWu,
+                        void* dWd, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_dispatch_bwd -- dx[t] = sum_j dXs[dest_row[t,j]] (float32 sum in slot
+ * order, stored in dtype; with MOE_ACCUMULATE added to dx).
+ */
+int moe_dispatch_bwd(const void* dXs, const int32_t* dest_row, int T, int d, int k,
+                     int dtype, unsigned flags, void* dx, void* stream);
+
+/*
+ * moe_route_bwd -- router backward for the weight gradient dtopk_w.
+ *   dp[t,e] = dtopk_w[t,j] where e = topk_idx[t,j], else 0
+ *   dlogits = p * (dp - <p, dp>), p = softmax(logits)    (f32 [T,E])
+ *   dWr     = x^T . dlogits                               (dtype [d,E])
+ *   dx     += dlogits . Wr^T                              (dtype [T,d], always added)
+ *   With bf16 the two GEMMs read dlogits rounded to bf16 (held in ws).
+ */
+int moe_route_bwd(const void* x, const void* Wr, const float* logits,
+                  const int32_t* topk_idx, const float* dtopk_w, int T, int d, int E, int k,
+                  int dtype, unsigned flags, float* dlogits, void* dWr, void* dx, void* ws,
+                  size_t ws_bytes, void* stream);
+
+/* Workspace bytes an operation needs for these sizes (0 is a valid answer). */
+int moe_workspace_size(int op, int T, int d, int E, int f, int k, int dtype, int prec,
+                       size_t* bytes);
+
+/* Text of a status code (static storage). */
+const char* moe_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

@@ -93,9 +93,9 @@ WORKLOADS: Dict[str, Workload] = {
 }
 
 
-def workload(name: str, **overrides) -> Workload:
+def workload(base: str, **overrides) -> Workload:
     """A named workload, optionally with some fields replaced (smaller T, ...)."""
-    w = WORKLOADS[name]
+    w = WORKLOADS[base]
     if overrides:
         w = dataclasses.replace(w, **overrides)
     return w

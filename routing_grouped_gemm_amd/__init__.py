@@ -1,0 +1,268 @@
+"""Python binding of libmoe_hip.so, the MI355X MoE expert-layer library.
+
+Argument marshalling only: every function here takes torch tensors that live
+on the GPU, checks nothing the C library does not check itself, passes their
+data pointers, sizes and torch's current HIP stream to the C entry point of
+the same name (declared in include/moe.h), and raises RuntimeError on a
+non-zero status.  All computation happens in the library's HIP kernels; there
+is no CPU or PyTorch fallback, and importing the binding fails loudly when
+the library has not been built.
+
+ExpertLayer owns the buffers of one layer (forward and backward) and calls
+the entry points in the order of the layer: route -> dispatch ->
+grouped_ffn_fwd -> combine, then combine_bwd -> grouped_ffn_bwd ->
+dispatch_bwd -> route_bwd.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "lib", "moe_route", "moe_dispatch", "moe_grouped_ffn_fwd", "moe_combine",
+    "moe_combine_bwd", "moe_grouped_ffn_bwd", "moe_dispatch_bwd", "moe_route_bwd",
+    "moe_workspace_size", "moe_status_string", "ExpertLayer", "LIB_PATH",
+    "MOE_ROUTE_LOGITS_IN", "MOE_ACCUMULATE",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_hip.so")
+
+MOE_F32, MOE_BF16 = 0, 1
+PREC = {"fp32": 0, "bf16": 1, "mxfp8": 2}
+MOE_ROUTE_LOGITS_IN = 0x1
+MOE_ACCUMULATE = 0x2
+OPS = {"route": 0, "dispatch": 1, "ffn_fwd": 2, "combine": 3, "combine_bwd": 4,
+       "ffn_bwd": 5, "dispatch_bwd": 6, "route_bwd": 7}
+
+_P, _I, _U, _S = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint, ctypes.c_size_t
+_SIGS = {
+    "moe_route": [_P, _P, _I, _I, _I, _I, _I, _U, _P, _P, _P, _P, _S, _P],
+    "moe_dispatch": [_P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _S, _P],
+    "moe_grouped_ffn_fwd": [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _I, _I, _P, _P, _P, _P,
+                            _P, _S, _P],
+    "moe_combine": [_P, _P, _P, _I, _I, _I, _I, _P, _P],
+    "moe_combine_bwd": [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _P],
+    "moe_grouped_ffn_bwd": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _I,
+                            _I, _U, _P, _P, _P, _P, _P, _P, _S, _P],
+    "moe_dispatch_bwd": [_P, _P, _I, _I, _I, _I, _U, _P, _P],
+    "moe_route_bwd": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _U, _P, _P, _P, _P, _S, _P],
+    "moe_workspace_size": [_I, _I, _I, _I, _I, _I, _I, _I, ctypes.POINTER(ctypes.c_size_t)],
+}
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m routing_grouped_gemm_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, args in _SIGS.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_int
+        L.moe_status_string.argtypes = [ctypes.c_int]
+        L.moe_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def moe_status_string(status: int) -> str:
+    return lib().moe_status_string(int(status)).decode()
+
+
+def _check(status: int, name: str) -> None:
+    if status != 0:
+        raise RuntimeError(f"{name}: {moe_status_string(status)} (status {status})")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return MOE_F32
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    raise TypeError(f"unsupported storage dtype {t.dtype}")
+
+
+def _ws(ws: Optional[torch.Tensor]):
+    return (None, 0) if ws is None else (_ptr(ws), ws.numel() * ws.element_size())
+
+
+def moe_workspace_size(op: str, T: int, d: int, E: int, f: int, k: int, dtype: torch.dtype,
+                       prec: str) -> int:
+    out = ctypes.c_size_t(0)
+    dt = MOE_F32 if dtype == torch.float32 else MOE_BF16
+    _check(lib().moe_workspace_size(OPS[op], T, d, E, f, k, dt, PREC[prec], ctypes.byref(out)),
+           "moe_workspace_size")
+    return out.value
+
+
+def moe_route(x, Wr, k, logits, topk_idx, topk_w, logits_in=False, stream=None):
+    T, E = logits.shape
+    d = x.shape[1] if x is not None else 64
+    dt = _dtype(x) if x is not None else MOE_BF16
+    _check(lib().moe_route(_ptr(x), _ptr(Wr), T, d, E, k, dt,
+                           MOE_ROUTE_LOGITS_IN if logits_in else 0, _ptr(logits),
+                           _ptr(topk_idx), _ptr(topk_w), None, 0, _stream(stream)), "moe_route")
+
+
+def moe_dispatch(x, topk_idx, E, counts, offsets, dest_row, src_token, Xs, Xs_scale, ws,
+                 prec="bf16", stream=None):
+    T, d = x.shape
+    k = topk_idx.shape[1]
+    wp, wb = _ws(ws)
+    _check(lib().moe_dispatch(_ptr(x), _ptr(topk_idx), T, d, E, k, _dtype(x), PREC[prec],
+                              _ptr(counts), _ptr(offsets), _ptr(dest_row), _ptr(src_token),
+                              _ptr(Xs), _ptr(Xs_scale), wp, wb, _stream(stream)), "moe_dispatch")
+
+
+def moe_grouped_ffn_fwd(Xs, Xs_scale, offsets, T, k, Wg, Wu, Wd, Hg, Hu, A, Ys, ws=None,
+                        prec="bf16", stream=None):
+    E, d, f = Wg.shape
+    wp, wb = _ws(ws)
+    _check(lib().moe_grouped_ffn_fwd(_ptr(Xs), _ptr(Xs_scale), _ptr(offsets), T, k, d, f, E,
+                                     _ptr(Wg), _ptr(Wu), _ptr(Wd), _dtype(Wg), PREC[prec],
+                                     _ptr(Hg), _ptr(Hu), _ptr(A), _ptr(Ys), wp, wb,
+                                     _stream(stream)), "moe_grouped_ffn_fwd")
+
+
+def moe_combine(Ys, topk_w, dest_row, y, stream=None):
+    T, d = y.shape
+    k = topk_w.shape[1]
+    _check(lib().moe_combine(_ptr(Ys), _ptr(topk_w), _ptr(dest_row), T, d, k, _dtype(y), _ptr(y),
+                             _stream(stream)), "moe_combine")
+
+
+def moe_combine_bwd(dY, Ys, topk_w, dest_row, dYs, dtopk_w, stream=None):
+    T, d = dY.shape
+    k = topk_w.shape[1]
+    _check(lib().moe_combine_bwd(_ptr(dY), _ptr(Ys), _ptr(topk_w), _ptr(dest_row), T, d, k,
+                                 _dtype(dY), _ptr(dYs), _ptr(dtopk_w), _stream(stream)),
+           "moe_combine_bwd")
+
+
+def moe_grouped_ffn_bwd(dYs, Xs, x, src_token, Hg, Hu, A, offsets, T, k, Wg, Wu, Wd, dH, dXs,
+                        dWg, dWu, dWd, ws=None, prec="bf16", accumulate=False, stream=None):
+    E, d, f = Wg.shape
+    wp, wb = _ws(ws)
+    _check(lib().moe_grouped_ffn_bwd(_ptr(dYs), _ptr(Xs), _ptr(x), _ptr(src_token), _ptr(Hg),
+                                     _ptr(Hu), _ptr(A), _ptr(offsets), T, k, d, f, E, _ptr(Wg),
+                                     _ptr(Wu), _ptr(Wd), _dtype(Wg), PREC[prec],
+                                     MOE_ACCUMULATE if accumulate else 0, _ptr(dH), _ptr(dXs),
+                                     _ptr(dWg), _ptr(dWu), _ptr(dWd), wp, wb, _stream(stream)),
+           "moe_grouped_ffn_bwd")
+
+
+def moe_dispatch_bwd(dXs, dest_row, dx, accumulate=False, stream=None):
+    T, d = dx.shape
+    k = dest_row.shape[1]
+    _check(lib().moe_dispatch_bwd(_ptr(dXs), _ptr(dest_row), T, d, k, _dtype(dx),
+                                  MOE_ACCUMULATE if accumulate else 0, _ptr(dx), _stream(stream)),
+           "moe_dispatch_bwd")
+
+
+def moe_route_bwd(x, Wr, logits, topk_idx, dtopk_w, dlogits, dWr, dx, ws=None, accumulate=False,
+                  stream=None):
+    T, d = x.shape
+    E = Wr.shape[1]
+    k = topk_idx.shape[1]
+    wp, wb = _ws(ws)
+    _check(lib().moe_route_bwd(_ptr(x), _ptr(Wr), _ptr(logits), _ptr(topk_idx), _ptr(dtopk_w), T,
+                               d, E, k, _dtype(x), MOE_ACCUMULATE if accumulate else 0,
+                               _ptr(dlogits), _ptr(dWr), _ptr(dx), wp, wb, _stream(stream)),
+           "moe_route_bwd")
+
+
+class ExpertLayer:
+    """Buffers and launch order of one MoE expert layer, forward and backward.
+
+    router=True: top-k softmax router on x.Wr (or on given logits).
+    router=False: pre-routed rows (topk_idx / topk_w are inputs, no router
+    backward).  All buffers are allocated once, on construction."""
+
+    def __init__(self, T: int, d: int, E: int, f: int, k: int, dtype=torch.bfloat16,
+                 prec: str = "bf16", router: bool = True, device="cuda"):
+        lib()
+        self.T, self.d, self.E, self.f, self.k = T, d, E, f, k
+        self.R = R = T * k
+        self.dtype, self.prec, self.router = dtype, prec, router
+        dev = torch.device(device)
+        z = lambda *s, dt=dtype: torch.empty(*s, dtype=dt, device=dev)
+        i32, f32 = torch.int32, torch.float32
+        self.logits = z(T, E, dt=f32)
+        self.topk_idx = z(T, k, dt=i32)
+        self.topk_w = z(T, k, dt=f32)
+        self.counts = z(E, dt=i32)
+        self.offsets = z(E + 1, dt=i32)
+        self.dest_row = z(T, k, dt=i32)
+        self.src_token = z(R, dt=i32)
+        if prec == "mxfp8":
+            self.Xs = z(R, d, dt=torch.uint8)
+            self.Xs_scale = z(R, d // 32, dt=torch.uint8)
+        else:
+            self.Xs = z(R, d)
+            self.Xs_scale = None
+        self.Hg, self.Hu, self.A = z(R, f), z(R, f), z(R, f)
+        self.Ys = z(R, d)
+        self.y = z(T, d)
+        self.dYs = z(R, d)
+        self.dw = z(T, k, dt=f32)
+        self.dH = z(R, 2 * f)
+        self.dXs = z(R, d)
+        self.dx = z(T, d)
+        self.dWg, self.dWu, self.dWd = z(E, d, f), z(E, d, f), z(E, f, d)
+        self.dlogits = z(T, E, dt=f32)
+        self.dWr = z(d, E)
+
+        def ws(op):
+            n = moe_workspace_size(op, T, d, E, f, k, dtype, prec)
+            return torch.empty(max(n, 256), dtype=torch.uint8, device=dev)
+        self.ws_dispatch = ws("dispatch")
+        self.ws_fwd = ws("ffn_fwd")
+        self.ws_bwd = ws("ffn_bwd")
+        self.ws_route_bwd = ws("route_bwd")
+
+    def forward(self, x, Wr, Wg, Wu, Wd, topk_idx=None, topk_w=None, logits=None, stream=None):
+        self.x, self.Wr, self.Wg, self.Wu, self.Wd = x, Wr, Wg, Wu, Wd
+        if self.router:
+            if logits is not None:
+                self.logits.copy_(logits)
+            moe_route(x, Wr, self.k, self.logits, self.topk_idx, self.topk_w,
+                      logits_in=logits is not None, stream=stream)
+        else:
+            self.topk_idx.copy_(topk_idx)
+            self.topk_w.copy_(topk_w)
+        moe_dispatch(x, self.topk_idx, self.E, self.counts, self.offsets, self.dest_row,
+                     self.src_token, self.Xs, self.Xs_scale, self.ws_dispatch, self.prec, stream)
+        moe_grouped_ffn_fwd(self.Xs, self.Xs_scale, self.offsets, self.T, self.k, Wg, Wu, Wd,
+                            self.Hg, self.Hu, self.A, self.Ys, self.ws_fwd, self.prec, stream)
+        moe_combine(self.Ys, self.topk_w, self.dest_row, self.y, stream)
+        return self.y
+
+    def backward(self, dY, stream=None):
+        moe_combine_bwd(dY, self.Ys, self.topk_w, self.dest_row, self.dYs, self.dw, stream)
+        moe_grouped_ffn_bwd(self.dYs, None if self.prec == "mxfp8" else self.Xs, self.x,
+                            self.src_token, self.Hg, self.Hu, self.A, self.offsets, self.T, self.k,
+                            self.Wg, self.Wu, self.Wd, self.dH, self.dXs, self.dWg, self.dWu,
+                            self.dWd, self.ws_bwd, self.prec, False, stream)
+        moe_dispatch_bwd(self.dXs, self.dest_row, self.dx, False, stream)
+        if self.router:
+            moe_route_bwd(self.x, self.Wr, self.logits, self.topk_idx, self.dw, self.dlogits,
+                          self.dWr, self.dx, self.ws_route_bwd, False, stream)
+        return self.dx

@@ -1,0 +1,360 @@
+// C ABI of the MoE expert layer: host-side validation, workspace carving and
+// launch order.  Declarations and argument meanings: include/moe.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/moe.h"
+#include "gemm.h"
+#include "mx.h"
+#include "route.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+// The MXFP8 GEMMs are not built yet: MXFP8 requests are rejected.
+constexpr bool kMxReady = false;
+inline size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int num_cu() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+inline int status_of(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH; }
+
+#define MOE_TRY(expr)                                    \
+  do {                                                   \
+    hipError_t e_ = (expr);                              \
+    if (e_ != hipSuccess) return MOE_ERR_LAUNCH;         \
+  } while (0)
+
+inline int check_dtype(int dtype) { return (dtype == MOE_F32 || dtype == MOE_BF16) ? MOE_OK : MOE_ERR_DTYPE; }
+
+inline int check_prec(int dtype, int prec) {
+  if (check_dtype(dtype) != MOE_OK) return MOE_ERR_DTYPE;
+  if (prec == MOE_PREC_F32) return dtype == MOE_F32 ? MOE_OK : MOE_ERR_DTYPE;
+  if (prec == MOE_PREC_BF16) return dtype == MOE_BF16 ? MOE_OK : MOE_ERR_DTYPE;
+  if (prec == MOE_PREC_MXFP8) return dtype == MOE_BF16 ? (kMxReady ? MOE_OK : MOE_ERR_UNSUPPORTED) : MOE_ERR_DTYPE;
+  return MOE_ERR_DTYPE;
+}
+
+// T, k, E shape rules shared by the routed entry points.
+inline int check_route_shape(int T, int E, int k) {
+  if (T <= 0 || E <= 0 || k <= 0) return MOE_ERR_SHAPE;
+  if ((long long)T * k > 0x7fffffffLL) return MOE_ERR_SHAPE;
+  if (E > 256 || k > E) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+inline int check_width(int v) {
+  if (v <= 0) return MOE_ERR_SHAPE;
+  return (v % 64) ? MOE_ERR_UNSUPPORTED : MOE_OK;
+}
+
+// Element counts of the largest tensors must stay below 2^31 * 2^31; row
+// indices are int32, element offsets are 64-bit.
+inline int check_elems(long long rows, long long cols) {
+  return (rows * cols > (1LL << 46)) ? MOE_ERR_SHAPE : MOE_OK;
+}
+
+template <typename... P>
+inline bool all_nonnull(P... p) { return ((p != nullptr) && ...); }
+template <typename... P>
+inline bool all_aligned(P... p) { return ((p == nullptr || aligned16(p)) && ...); }
+
+inline size_t dispatch_ws(int T, int E) {
+  const size_t nblk = (size_t)(T + 63) / 64;
+  return 2 * align_up(nblk * (size_t)E * sizeof(int32_t));
+}
+
+inline int gemm_engine(int dtype, int router_E = 8) {
+  if (dtype == MOE_F32) return GEMM_F32_SIMT;
+  return (router_E % 8 == 0) ? GEMM_BF16_MFMA : GEMM_BF16_SIMT;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "invalid shape (non-positive size or int32 overflow)";
+    case MOE_ERR_DTYPE: return "unknown dtype/precision or invalid dtype/precision pair";
+    case MOE_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape (E > 256, k > E, or d/f not a multiple of 64)";
+    case MOE_ERR_LAUNCH: return "HIP kernel launch failed";
+  }
+  return "unknown status";
+}
+
+int moe_workspace_size(int op, int T, int d, int E, int f, int k, int dtype, int prec,
+                       size_t* bytes) {
+  if (!bytes) return MOE_ERR_NULL;
+  *bytes = 0;
+  if (T <= 0 || d <= 0 || E <= 0 || f <= 0 || k <= 0) return MOE_ERR_SHAPE;
+  if (int s = check_prec(dtype, prec)) return s;
+  const size_t R = (size_t)T * k;
+  switch (op) {
+    case MOE_OP_ROUTE:
+    case MOE_OP_COMBINE:
+    case MOE_OP_COMBINE_BWD:
+    case MOE_OP_DISPATCH_BWD:
+      return MOE_OK;
+    case MOE_OP_DISPATCH:
+      *bytes = dispatch_ws(T, E);
+      return MOE_OK;
+    case MOE_OP_FFN_FWD:
+      *bytes = (prec == MOE_PREC_MXFP8) ? mx_fwd_workspace(R, d, f, E) : 0;
+      return MOE_OK;
+    case MOE_OP_FFN_BWD:
+      *bytes = (prec == MOE_PREC_MXFP8) ? mx_bwd_workspace(R, d, f, E) : 0;
+      return MOE_OK;
+    case MOE_OP_ROUTE_BWD:
+      *bytes = (dtype == MOE_BF16) ? align_up((size_t)T * E * 2) : 0;
+      return MOE_OK;
+  }
+  return MOE_ERR_SHAPE;
+}
+
+int moe_route(const void* x, const void* Wr, int T, int d, int E, int k, int dtype,
+              unsigned flags, float* logits, int32_t* topk_idx, float* topk_w, void* ws,
+              size_t ws_bytes, void* stream) {
+  (void)ws; (void)ws_bytes;
+  const bool lin = (flags & MOE_ROUTE_LOGITS_IN) != 0;
+  if (!all_nonnull(logits, topk_idx, topk_w)) return MOE_ERR_NULL;
+  if (!lin && !all_nonnull(x, Wr)) return MOE_ERR_NULL;
+  if (int s = check_dtype(dtype)) return s;
+  if (int s = check_route_shape(T, E, k)) return s;
+  if (!lin) {
+    if (int s = check_width(d)) return s;
+    if (int s = check_elems(T, d)) return s;
+  }
+  if (!all_aligned(x, Wr, logits, topk_idx, topk_w)) return MOE_ERR_ALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (!lin) {
+    GemmArgs g{};
+    g.E = 1; g.offsets = nullptr; g.rows_total = T; g.ragged = RAG_M;
+    g.M = T; g.N = E; g.K = d;
+    g.a = x; g.lda = d;
+    g.b0 = Wr; g.ldb = E;
+    g.c0 = logits; g.ldc = E;
+    MOE_TRY(launch_grouped_gemm(GK_ROUTER_LOGITS, gemm_engine(dtype, E), g, num_cu(), st));
+  }
+  return status_of(launch_topk_softmax(logits, T, E, k, topk_idx, topk_w, st));
+}
+
+int moe_dispatch(const void* x, const int32_t* topk_idx, int T, int d, int E, int k, int dtype,
+                 int prec, int32_t* counts, int32_t* offsets, int32_t* dest_row,
+                 int32_t* src_token, void* Xs, uint8_t* Xs_scale, void* ws, size_t ws_bytes,
+                 void* stream) {
+  if (!all_nonnull(x, topk_idx, counts, offsets, dest_row, src_token, Xs, ws)) return MOE_ERR_NULL;
+  if (int s = check_prec(dtype, prec)) return s;
+  if (prec == MOE_PREC_MXFP8 && !Xs_scale) return MOE_ERR_NULL;
+  if (int s = check_route_shape(T, E, k)) return s;
+  if (int s = check_width(d)) return s;
+  if (int s = check_elems((long long)T * k, d)) return s;
+  if (!all_aligned(x, topk_idx, counts, offsets, dest_row, src_token, Xs, ws)) return MOE_ERR_ALIGN;
+  if (ws_bytes < dispatch_ws(T, E)) return MOE_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const size_t nblk = (size_t)(T + 63) / 64;
+  int32_t* hist = static_cast<int32_t*>(ws);
+  int32_t* base = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + align_up(nblk * E * 4));
+  MOE_TRY(launch_dispatch_meta(topk_idx, T, E, k, hist, base, counts, offsets, dest_row,
+                               src_token, st));
+  const int R = T * k;
+  if (prec == MOE_PREC_MXFP8)
+    return status_of(launch_mx_dispatch_copy(x, src_token, R, T, d, Xs, Xs_scale, st));
+  return status_of(launch_dispatch_copy(dtype, x, src_token, R, T, d, Xs, st));
+}
+
+int moe_grouped_ffn_fwd(const void* Xs, const uint8_t* Xs_scale, const int32_t* offsets, int T,
+                        int k, int d, int f, int E, const void* Wg, const void* Wu,
+                        const void* Wd, int dtype, int prec, void* Hg, void* Hu, void* A,
+                        void* Ys, void* ws, size_t ws_bytes, void* stream) {
+  if (!all_nonnull(Xs, offsets, Wg, Wu, Wd, Hg, Hu, A, Ys)) return MOE_ERR_NULL;
+  if (int s = check_prec(dtype, prec)) return s;
+  if (prec == MOE_PREC_MXFP8 && !all_nonnull(Xs_scale, ws)) return MOE_ERR_NULL;
+  if (int s = check_route_shape(T, E, k)) return s;
+  if (int s = check_width(d)) return s;
+  if (int s = check_width(f)) return s;
+  const long long R = (long long)T * k;
+  if (int s = check_elems(R, 2LL * (d > f ? d : f))) return s;
+  if (int s = check_elems(E, (long long)d * f)) return s;
+  if (!all_aligned(Xs, offsets, Wg, Wu, Wd, Hg, Hu, A, Ys, ws)) return MOE_ERR_ALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (prec == MOE_PREC_MXFP8) {
+    if (ws_bytes < mx_fwd_workspace(R, d, f, E)) return MOE_ERR_WORKSPACE;
+    return status_of(mx_ffn_fwd(Xs, Xs_scale, offsets, (int)R, d, f, E, Wg, Wu, Wd, Hg, Hu, A,
+                                Ys, ws, num_cu(), st));
+  }
+  const int eng = gemm_engine(dtype);
+  GemmArgs g{};
+  g.E = E; g.offsets = offsets; g.rows_total = (int)R; g.ragged = RAG_M;
+  g.N = f; g.K = d;
+  g.a = Xs; g.lda = d;
+  g.b0 = Wg; g.b1 = Wu; g.ldb = f; g.b_es = (long)d * f;
+  g.c0 = Hg; g.c1 = Hu; g.c2 = A; g.ldc = f;
+  MOE_TRY(launch_grouped_gemm(GK_FWD_GATEUP, eng, g, num_cu(), st));
+  GemmArgs h{};
+  h.E = E; h.offsets = offsets; h.rows_total = (int)R; h.ragged = RAG_M;
+  h.N = d; h.K = f;
+  h.a = A; h.lda = f;
+  h.b0 = Wd; h.ldb = d; h.b_es = (long)f * d;
+  h.c0 = Ys; h.ldc = d;
+  return status_of(launch_grouped_gemm(GK_FWD_DOWN, eng, h, num_cu(), st));
+}
+
+int moe_combine(const void* Ys, const float* topk_w, const int32_t* dest_row, int T, int d, int k,
+                int dtype, void* y, void* stream) {
+  if (!all_nonnull(Ys, topk_w, dest_row, y)) return MOE_ERR_NULL;
+  if (int s = check_dtype(dtype)) return s;
+  if (T <= 0 || k <= 0 || (long long)T * k > 0x7fffffffLL) return MOE_ERR_SHAPE;
+  if (int s = check_width(d)) return s;
+  if (!all_aligned(Ys, topk_w, dest_row, y)) return MOE_ERR_ALIGN;
+  return status_of(launch_combine(dtype, Ys, topk_w, dest_row, T, d, k, y,
+                                  static_cast<hipStream_t>(stream)));
+}
+
+int moe_combine_bwd(const void* dY, const void* Ys, const float* topk_w, const int32_t* dest_row,
+                    int T, int d, int k, int dtype, void* dYs, float* dtopk_w, void* stream) {
+  if (!all_nonnull(dY, Ys, topk_w, dest_row, dYs, dtopk_w)) return MOE_ERR_NULL;
+  if (int s = check_dtype(dtype)) return s;
+  if (T <= 0 || k <= 0 || (long long)T * k > 0x7fffffffLL) return MOE_ERR_SHAPE;
+  if (int s = check_width(d)) return s;
+  if (!all_aligned(dY, Ys, topk_w, dest_row, dYs, dtopk_w)) return MOE_ERR_ALIGN;
+  return status_of(launch_combine_bwd(dtype, dY, Ys, topk_w, dest_row, T, d, k, dYs, dtopk_w,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+int moe_grouped_ffn_bwd(const void* dYs, const void* Xs, const void* x, const int32_t* src_token,
+                        const void* Hg, const void* Hu, const void* A, const int32_t* offsets,
+                        int T, int k, int d, int f, int E, const void* Wg, const void* Wu,
+                        const void* Wd, int dtype, int prec, unsigned flags, void* dH,
+                        void* dXs, void* dWg, void* dWu, void* dWd, void* ws, size_t ws_bytes,
+                        void* stream) {
+  if (!all_nonnull(dYs, Hg, Hu, A, offsets, Wg, Wu, Wd, dH, dXs, dWg, dWu, dWd))
+    return MOE_ERR_NULL;
+  if (int s = check_prec(dtype, prec)) return s;
+  if (prec == MOE_PREC_MXFP8) {
+    if (!all_nonnull(x, src_token, ws)) return MOE_ERR_NULL;
+  } else if (!Xs) {
+    return MOE_ERR_NULL;
+  }
+  if (int s = check_route_shape(T, E, k)) return s;
+  if (int s = check_width(d)) return s;
+  if (int s = check_width(f)) return s;
+  const long long R = (long long)T * k;
+  if (int s = check_elems(R, 2LL * (d > f ? d : f))) return s;
+  if (int s = check_elems(E, (long long)d * f)) return s;
+  if (!all_aligned(dYs, Xs, x, src_token, Hg, Hu, A, offsets, Wg, Wu, Wd, dH, dXs, dWg, dWu, dWd, ws))
+    return MOE_ERR_ALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int acc = (flags & MOE_ACCUMULATE) ? 1 : 0;
+  const int eng = gemm_engine(dtype);
+  if (prec == MOE_PREC_MXFP8) {
+    if (ws_bytes < mx_bwd_workspace(R, d, f, E)) return MOE_ERR_WORKSPACE;
+    MOE_TRY(mx_ffn_dgrad(dYs, Hg, Hu, offsets, (int)R, d, f, E, Wg, Wu, Wd, dH, dXs, ws,
+                         num_cu(), st));
+  } else {
+    GemmArgs g{};
+    g.E = E; g.offsets = offsets; g.rows_total = (int)R; g.ragged = RAG_M;
+    g.N = f; g.K = d;
+    g.a = dYs; g.lda = d;
+    g.b0 = Wd; g.ldb = d; g.b_es = (long)f * d;
+    g.c0 = dH; g.ldc = 2L * f; g.c_split = f;
+    g.h0 = Hg; g.h1 = Hu; g.ldh = f;
+    MOE_TRY(launch_grouped_gemm(GK_DGRAD_DOWN, eng, g, num_cu(), st));
+    GemmArgs h{};
+    h.E = E; h.offsets = offsets; h.rows_total = (int)R; h.ragged = RAG_M;
+    h.N = d; h.K = 2 * f;
+    h.a = dH; h.lda = 2L * f;
+    h.b0 = Wg; h.b1 = Wu; h.ldb = f; h.b_es = (long)d * f; h.b_split = f;
+    h.c0 = dXs; h.ldc = d;
+    MOE_TRY(launch_grouped_gemm(GK_DGRAD_GATEUP, eng, h, num_cu(), st));
+  }
+  // weight gradients: dWg|dWu = Xs^T . dH, dWd = A^T . dYs (ragged K = rows of e)
+  GemmArgs w{};
+  w.E = E; w.offsets = offsets; w.rows_total = (int)R; w.ragged = RAG_K;
+  w.M = d; w.N = 2 * f;
+  if (prec == MOE_PREC_MXFP8) { w.a = x; w.a_gather = src_token; }
+  else { w.a = Xs; }
+  w.lda = d;
+  w.b0 = dH; w.ldb = 2L * f;
+  w.c0 = dWg; w.c1 = dWu; w.ldc = f; w.c_es = (long)d * f; w.c_split = f;
+  w.accumulate = acc;
+  MOE_TRY(launch_grouped_gemm(GK_WGRAD, eng, w, num_cu(), st));
+  GemmArgs v{};
+  v.E = E; v.offsets = offsets; v.rows_total = (int)R; v.ragged = RAG_K;
+  v.M = f; v.N = d;
+  v.a = A; v.lda = f;
+  v.b0 = dYs; v.ldb = d;
+  v.c0 = dWd; v.ldc = d; v.c_es = (long)f * d; v.c_split = d;
+  v.accumulate = acc;
+  return status_of(launch_grouped_gemm(GK_WGRAD, eng, v, num_cu(), st));
+}
+
+int moe_dispatch_bwd(const void* dXs, const int32_t* dest_row, int T, int d, int k, int dtype,
+                     unsigned flags, void* dx, void* stream) {
+  if (!all_nonnull(dXs, dest_row, dx)) return MOE_ERR_NULL;
+  if (int s = check_dtype(dtype)) return s;
+  if (T <= 0 || k <= 0 || (long long)T * k > 0x7fffffffLL) return MOE_ERR_SHAPE;
+  if (int s = check_width(d)) return s;
+  if (!all_aligned(dXs, dest_row, dx)) return MOE_ERR_ALIGN;
+  return status_of(launch_gather_sum(dtype, dXs, dest_row, T, d, k,
+                                     (flags & MOE_ACCUMULATE) ? 1 : 0, dx,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+int moe_route_bwd(const void* x, const void* Wr, const float* logits, const int32_t* topk_idx,
+                  const float* dtopk_w, int T, int d, int E, int k, int dtype, unsigned flags,
+                  float* dlogits, void* dWr, void* dx, void* ws, size_t ws_bytes, void* stream) {
+  if (!all_nonnull(x, Wr, logits, topk_idx, dtopk_w, dlogits, dWr, dx)) return MOE_ERR_NULL;
+  if (int s = check_dtype(dtype)) return s;
+  if (int s = check_route_shape(T, E, k)) return s;
+  if (int s = check_width(d)) return s;
+  if (int s = check_elems(T, d)) return s;
+  if (!all_aligned(x, Wr, logits, topk_idx, dtopk_w, dlogits, dWr, dx, ws)) return MOE_ERR_ALIGN;
+  const size_t need = (dtype == MOE_BF16) ? align_up((size_t)T * E * 2) : 0;
+  if (need && !ws) return MOE_ERR_NULL;
+  if (ws_bytes < need) return MOE_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint16_t* dl16 = (dtype == MOE_BF16) ? static_cast<uint16_t*>(ws) : nullptr;
+  MOE_TRY(launch_router_bwd_softmax(logits, topk_idx, dtopk_w, T, E, k, dlogits, dl16, st));
+  const void* dl = (dtype == MOE_BF16) ? static_cast<const void*>(dl16) : dlogits;
+  const int eng = gemm_engine(dtype, E);
+  GemmArgs g{};
+  g.E = 1; g.offsets = nullptr; g.rows_total = T; g.ragged = RAG_K;
+  g.M = d; g.N = E;
+  g.a = x; g.lda = d;
+  g.b0 = dl; g.ldb = E;
+  g.c0 = dWr; g.ldc = E;
+  g.accumulate = (flags & MOE_ACCUMULATE) ? 1 : 0;
+  MOE_TRY(launch_grouped_gemm(GK_ROUTER_DWR, eng, g, num_cu(), st));
+  GemmArgs h{};
+  h.E = 1; h.offsets = nullptr; h.rows_total = T; h.ragged = RAG_M;
+  h.M = T; h.N = d; h.K = E;
+  h.a = dl; h.lda = E;
+  h.b0 = Wr; h.ldb = E;
+  h.c0 = dx; h.ldc = d;
+  h.accumulate = 1;
+  return status_of(launch_grouped_gemm(GK_ROUTER_DX, eng, h, num_cu(), st));
+}
+
+}  // extern "C"

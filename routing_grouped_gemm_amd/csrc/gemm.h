@@ -1,0 +1,80 @@
+// Grouped GEMM engine of the MoE expert layer: problem description shared by
+// the host launchers and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// What the epilogue does with a finished tile.
+enum EpiKind : int {
+  EPI_STORE = 0,       // C[row][n] = acc (dtype), or += with accumulate
+  EPI_STORE_F32 = 1,   // C[row][n] = acc as float32
+  EPI_SWIGLU_FWD = 2,  // acc pair (gate, up): Hg, Hu and A = silu(Hg)*Hu
+  EPI_SWIGLU_BWD = 3,  // acc = dA: dHg = dA*Hu*silu'(Hg), dHu = dA*silu(Hg) into dH[R,2f]
+  EPI_WGRAD_SPLIT = 4  // columns [0,c_split) -> c0, [c_split, N) -> c1 (dWg | dWu)
+};
+
+// How the B operand is assembled from two sources.
+enum BSplit : int {
+  BS_NONE = 0,
+  BS_DUAL_N = 1,  // gate/up: tile columns alternate 64 from b0 (Wg), 64 from b1 (Wu)
+  BS_SPLIT_K = 2  // k < b_split from b0, k >= b_split from b1 (shifted by b_split)
+};
+
+// Which dimension is ragged across groups (experts).
+enum Ragged : int { RAG_M = 0, RAG_K = 1 };
+
+struct GemmArgs {
+  int E;               // number of groups
+  const int* offsets;  // [E+1] device row offsets of the groups, or nullptr: one group
+  int rows_total;      // rows of the row-indexed operands (R, or T for router GEMMs)
+  int ragged;          // RAG_M: group rows are GEMM rows; RAG_K: group rows are the K axis
+  int M, N, K;         // the fixed dimensions (the ragged one is read from offsets)
+  // A: RAG_M -> A[row][k] (K contiguous), row = global row; RAG_K -> A[krow][m]
+  const void* a;
+  long lda;
+  long a_es;            // per-group element stride (0: rows are global)
+  const int* a_gather;  // RAG_K only: source row of each global k-row, or nullptr
+  // B: per-group matrix b + e*b_es, [N][K] (K contiguous) or [K][N] (N contiguous);
+  // RAG_K: B[krow][n] with global k-rows.
+  const void* b0;
+  const void* b1;
+  long ldb;
+  long b_es;
+  int b_split;
+  // epilogue
+  void* c0;
+  void* c1;
+  void* c2;
+  long ldc;
+  long c_es;  // RAG_K: per-group stride of C; RAG_M: 0 (C rows are global rows)
+  int c_split;
+  const void* h0;  // SWIGLU_BWD: Hg
+  const void* h1;  // SWIGLU_BWD: Hu
+  long ldh;
+  int accumulate;
+};
+
+// Operand layouts of the five GEMM kinds of the layer and of the router.
+enum GemmKind : int {
+  GK_FWD_GATEUP = 0,    // Xs[R,d] . [Wg|Wu][e][d,f]  -> Hg, Hu, A    (ragged M)
+  GK_FWD_DOWN = 1,      // A[R,f] . Wd[e][f,d]        -> Ys           (ragged M)
+  GK_DGRAD_DOWN = 2,    // dYs[R,d] . Wd[e]^T         -> dHg, dHu     (ragged M)
+  GK_DGRAD_GATEUP = 3,  // dH[R,2f] . [Wg|Wu][e]^T    -> dXs          (ragged M)
+  GK_WGRAD = 4,         // P[rows,M]^T . Q[rows,N]    -> dW[e][M,N]   (ragged K)
+  GK_ROUTER_LOGITS = 5, // x[T,d] . Wr[d,E]           -> logits f32   (one group)
+  GK_ROUTER_DWR = 6,    // x[T,d]^T . dl[T,E]         -> dWr[d,E]     (one group, K = T)
+  GK_ROUTER_DX = 7      // dl[T,E] . Wr[d,E]^T        -> dx += [T,d]  (one group, K = E)
+};
+
+// Engines: float32 storage on the SIMT engine, bf16 on MFMA, and bf16 on the
+// SIMT engine for router shapes the MFMA engine does not take (E % 8 != 0).
+enum GemmEngine : int { GEMM_F32_SIMT = 0, GEMM_BF16_MFMA = 1, GEMM_BF16_SIMT = 2 };
+
+// Launch a grouped GEMM of the given kind.  num_cu sizes the persistent grid.
+hipError_t launch_grouped_gemm(GemmKind kind, int engine, const GemmArgs& g, int num_cu,
+                               hipStream_t stream);
+
+}  // namespace moe

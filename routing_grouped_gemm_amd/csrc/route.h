@@ -1,0 +1,28 @@
+// Launchers of the routing, dispatch and combine kernels (route.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+hipError_t launch_topk_softmax(const float* logits, int T, int E, int k, int32_t* idx, float* w,
+                               hipStream_t s);
+// hist and base: E * ceil(T/64) int32 each (workspace).
+hipError_t launch_dispatch_meta(const int32_t* idx, int T, int E, int k, int32_t* hist,
+                                int32_t* base, int32_t* counts, int32_t* offsets,
+                                int32_t* dest_row, int32_t* src_token, hipStream_t s);
+hipError_t launch_dispatch_copy(int dtype, const void* x, const int32_t* src_token, int R, int T,
+                                int d, void* Xs, hipStream_t s);
+hipError_t launch_combine(int dtype, const void* Ys, const float* w, const int32_t* dest, int T,
+                          int d, int k, void* y, hipStream_t s);
+hipError_t launch_combine_bwd(int dtype, const void* dY, const void* Ys, const float* w,
+                              const int32_t* dest, int T, int d, int k, void* dYs, float* dw,
+                              hipStream_t s);
+hipError_t launch_gather_sum(int dtype, const void* dXs, const int32_t* dest, int T, int d, int k,
+                             int accumulate, void* dx, hipStream_t s);
+hipError_t launch_router_bwd_softmax(const float* logits, const int32_t* idx, const float* dw,
+                                     int T, int E, int k, float* dl, uint16_t* dl16,
+                                     hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,453 @@
+// Router, routing metadata, row-wise dispatch, combine and their backwards.
+//
+// Router (HF OLMoE walkthrough, section 2): softmax of the float32 logits
+// over the experts and the top_k experts per token, weights = the chosen
+// probabilities (no renormalisation).  One wave per token; every lane holds
+// up to four logits; the k winners are taken by k wave-wide arg-max rounds
+// ordered by (logit desc, index asc), so ties go to the lower expert index.
+//
+// Metadata and dispatch (olmoforge README: row-wise expert parallel writes
+// every token row straight into its expert's input buffer; the routing table
+// stays on the GPU): a per-64-token histogram, one scan workgroup that turns
+// the histograms into counts, offsets and per-block bases, a rank kernel that
+// gives every (token, slot) its row (stable: ascending token order inside an
+// expert, by ballot masks and popcount, no atomics on the result), and a copy
+// kernel that writes each row of Xs from its source token with 16-byte loads
+// and stores.  The combine and the gathers of the backward run one wave per
+// token and sum in float32 in slot order.
+#include "moe_common.h"
+#include "route.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// softmax + top-k
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restrict__ logits, int T,
+                                                           int E, int k,
+                                                           int32_t* __restrict__ topk_idx,
+                                                           float* __restrict__ topk_w) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float* row = logits + (long)t * E;
+  float v[4];
+  int taken = 0;  // bit q: logit q of this lane already chosen
+  float mx = -INFINITY;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    int e = lane + 64 * q;
+    v[q] = (e < E) ? row[e] : -INFINITY;
+    if (e < E) mx = fmaxf(mx, v[q]);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+  float se = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    if (lane + 64 * q < E) se += expf(v[q] - mx);
+  se = wave_sum(se);
+  for (int j = 0; j < k; ++j) {
+    // lane-local best among the untaken: larger logit, then lower index
+    float bv = -INFINITY;
+    int be = 0x7fffffff;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      int e = lane + 64 * q;
+      if (e < E && !((taken >> q) & 1)) {
+        if (v[q] > bv || (v[q] == bv && e < be) || be == 0x7fffffff) {
+          bv = v[q];
+          be = e;
+        }
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      float ov = __shfl_xor(bv, o, 64);
+      int oe = __shfl_xor(be, o, 64);
+      bool better = (oe != 0x7fffffff) &&
+                    (be == 0x7fffffff || ov > bv || (ov == bv && oe < be));
+      if (better) { bv = ov; be = oe; }
+    }
+    if ((be & 63) == lane) taken |= 1 << (be >> 6);
+    if (lane == 0) {
+      topk_idx[(long)t * k + j] = be;
+      topk_w[(long)t * k + j] = expf(bv - mx) / se;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// metadata: histogram per 64-token block, scan, rank
+// ---------------------------------------------------------------------------
+// hist[e][b]: rows of expert e among the (token, slot) pairs of block b.
+__global__ __launch_bounds__(64) void block_hist_kernel(const int32_t* __restrict__ idx, int T,
+                                                        int E, int k, int nblk,
+                                                        int32_t* __restrict__ hist) {
+  __shared__ int cnt[256];
+  const int lane = threadIdx.x;
+  for (int e = lane; e < E; e += 64) cnt[e] = 0;
+  __syncthreads();
+  const int t = blockIdx.x * 64 + lane;
+  if (t < T)
+    for (int j = 0; j < k; ++j) {
+      int e = idx[(long)t * k + j];
+      if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+    }
+  __syncthreads();
+  for (int e = lane; e < E; e += 64) hist[(long)e * nblk + blockIdx.x] = cnt[e];
+}
+
+// One workgroup per expert: exclusive scan of its block counts into
+// base[e][b]; the total is counts[e].
+__global__ __launch_bounds__(256) void scan_kernel(const int32_t* __restrict__ hist, int nblk,
+                                                   int32_t* __restrict__ base,
+                                                   int32_t* __restrict__ counts) {
+  __shared__ int wsum[4];
+  const int e = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int32_t* h = hist + (long)e * nblk;
+  int32_t* bo = base + (long)e * nblk;
+  int carry = 0;
+  for (int b0 = 0; b0 < nblk; b0 += 256) {
+    const int b = b0 + tid;
+    const int c = (b < nblk) ? h[b] : 0;
+    int incl = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      int v = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += v;
+    }
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    int wbase = 0;
+    for (int w = 0; w < wave; ++w) wbase += wsum[w];
+    const int total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    if (b < nblk) bo[b] = carry + wbase + incl - c;
+    carry += total;
+    __syncthreads();
+  }
+  if (tid == 0) counts[e] = carry;
+}
+
+// Row of every (token, slot): offsets[e] + base[e][block] + rank of the token
+// among the block's tokens routed to e.  The workgroup also forms offsets
+// from counts (block 0 writes them out for the grouped GEMMs).
+__global__ __launch_bounds__(64) void rank_kernel(const int32_t* __restrict__ idx, int T, int E,
+                                                  int k, int nblk,
+                                                  const int32_t* __restrict__ base,
+                                                  const int32_t* __restrict__ counts,
+                                                  int32_t* __restrict__ offsets,
+                                                  int32_t* __restrict__ dest_row,
+                                                  int32_t* __restrict__ src_token) {
+  __shared__ unsigned long long mask[256];
+  __shared__ int off[257];
+  const int lane = threadIdx.x;
+  {
+    int c[4], sum = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      int e = lane * 4 + q;
+      c[q] = (e < E) ? counts[e] : 0;
+      sum += c[q];
+    }
+    int incl = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      int v = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += v;
+    }
+    int run = incl - sum;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      int e = lane * 4 + q;
+      if (e <= E) off[e] = run;
+      run += c[q];
+    }
+    if (lane == 63 && E == 256) off[256] = incl;
+  }
+  for (int e = lane; e < E; e += 64) mask[e] = 0ull;
+  __syncthreads();
+  if (blockIdx.x == 0)
+    for (int e = lane; e <= E; e += 64) offsets[e] = off[e];
+  const int t = blockIdx.x * 64 + lane;
+  if (t < T)
+    for (int j = 0; j < k; ++j) {
+      int e = idx[(long)t * k + j];
+      if (e >= 0 && e < E) atomicOr(&mask[e], 1ull << lane);
+    }
+  __syncthreads();
+  if (t >= T) return;
+  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int j = 0; j < k; ++j) {
+    int e = idx[(long)t * k + j];
+    if (e < 0 || e >= E) { dest_row[(long)t * k + j] = -1; continue; }
+    int r = off[e] + base[(long)e * nblk + blockIdx.x] + __popcll(mask[e] & below);
+    dest_row[(long)t * k + j] = r;
+    src_token[r] = t;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// row copies
+// ---------------------------------------------------------------------------
+// Xs[r] = x[src_token[r]]: one wave per row, 8 elements per lane per step.
+template <typename TS>
+__global__ __launch_bounds__(256) void dispatch_copy_kernel(const TS* __restrict__ x,
+                                                            const int32_t* __restrict__ src_token,
+                                                            int R, int T, int d,
+                                                            TS* __restrict__ Xs) {
+  const int lane = threadIdx.x & 63;
+  const long r = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= R) return;
+  int t = src_token[r];
+  t = min(max(t, 0), T - 1);
+  const TS* src = x + (long)t * d;
+  TS* dst = Xs + r * d;
+  for (int c = lane * 8; c < d; c += 64 * 8) {
+    if constexpr (sizeof(TS) == 2)
+      *reinterpret_cast<uint4*>(dst + c) = *reinterpret_cast<const uint4*>(src + c);
+    else {
+      *reinterpret_cast<float4*>(dst + c) = *reinterpret_cast<const float4*>(src + c);
+      *reinterpret_cast<float4*>(dst + c + 4) = *reinterpret_cast<const float4*>(src + c + 4);
+    }
+  }
+}
+
+__device__ __forceinline__ int clamp_row(int r, int R) { return min(max(r, 0), R - 1); }
+
+// y[t] = sum_j w[t,j] Ys[dest_row[t,j]]
+template <typename TS>
+__global__ __launch_bounds__(256) void combine_kernel(const TS* __restrict__ Ys,
+                                                      const float* __restrict__ w,
+                                                      const int32_t* __restrict__ dest_row, int T,
+                                                      int d, int k, TS* __restrict__ y) {
+  const int lane = threadIdx.x & 63;
+  const long t = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int R = T * k;
+  for (int c = lane * 8; c < d; c += 64 * 8) {
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int j = 0; j < k; ++j) {
+      const int r = clamp_row(dest_row[t * k + j], R);
+      const float wj = w[t * k + j];
+      float v[8];
+      load8(Ys + (long)r * d + c, v);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] = fmaf(wj, v[q], acc[q]);
+    }
+    store8(y + t * d + c, acc);
+  }
+}
+
+// dYs[dest] = w * dY[t]; dw[t,j] = <dY[t], Ys[dest]>
+template <typename TS>
+__global__ __launch_bounds__(256) void combine_bwd_kernel(const TS* __restrict__ dY,
+                                                          const TS* __restrict__ Ys,
+                                                          const float* __restrict__ w,
+                                                          const int32_t* __restrict__ dest_row,
+                                                          int T, int d, int k,
+                                                          TS* __restrict__ dYs,
+                                                          float* __restrict__ dw) {
+  const int lane = threadIdx.x & 63;
+  const long t = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int R = T * k;
+  for (int j = 0; j < k; ++j) {
+    const int r = clamp_row(dest_row[t * k + j], R);
+    const float wj = w[t * k + j];
+    float dot = 0.0f;
+    for (int c = lane * 8; c < d; c += 64 * 8) {
+      float g[8], v[8], o[8];
+      load8(dY + t * d + c, g);
+      load8(Ys + (long)r * d + c, v);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        dot = fmaf(g[q], v[q], dot);
+        o[q] = wj * g[q];
+      }
+      store8(dYs + (long)r * d + c, o);
+    }
+    dot = wave_sum(dot);
+    if (lane == 0) dw[t * k + j] = dot;
+  }
+}
+
+// dx[t] (+)= sum_j dXs[dest_row[t,j]]
+template <typename TS>
+__global__ __launch_bounds__(256) void gather_sum_kernel(const TS* __restrict__ dXs,
+                                                         const int32_t* __restrict__ dest_row,
+                                                         int T, int d, int k, int accumulate,
+                                                         TS* __restrict__ dx) {
+  const int lane = threadIdx.x & 63;
+  const long t = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int R = T * k;
+  for (int c = lane * 8; c < d; c += 64 * 8) {
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int j = 0; j < k; ++j) {
+      const int r = clamp_row(dest_row[t * k + j], R);
+      float v[8];
+      load8(dXs + (long)r * d + c, v);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] += v[q];
+    }
+    if (accumulate) {
+      float o[8];
+      load8(dx + t * d + c, o);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] += o[q];
+    }
+    store8(dx + t * d + c, acc);
+  }
+}
+
+// Router backward, softmax part: dl = p * (dp - <p, dp>), one wave per token.
+// Also writes dl rounded to bf16 when dl16 is given (GEMM operand).
+__global__ __launch_bounds__(256) void router_bwd_softmax_kernel(
+    const float* __restrict__ logits, const int32_t* __restrict__ idx,
+    const float* __restrict__ dw, int T, int E, int k, float* __restrict__ dl,
+    bf16_t* __restrict__ dl16) {
+  const int lane = threadIdx.x & 63;
+  const long t = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float* row = logits + t * E;
+  float v[4], dp[4];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    int e = lane + 64 * q;
+    v[q] = (e < E) ? row[e] : -INFINITY;
+    if (e < E) mx = fmaxf(mx, v[q]);
+    dp[q] = 0.0f;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+  float se = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    int e = lane + 64 * q;
+    v[q] = (e < E) ? expf(v[q] - mx) : 0.0f;
+    se += v[q];
+  }
+  se = wave_sum(se);
+  for (int j = 0; j < k; ++j) {
+    int e = idx[t * k + j];
+    float g = dw[t * k + j];
+    if (e >= 0 && e < E && (e & 63) == lane) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if ((e >> 6) == q) dp[q] = g;
+    }
+  }
+  float inner = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    v[q] = v[q] / se;  // p
+    inner = fmaf(v[q], dp[q], inner);
+  }
+  inner = wave_sum(inner);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    int e = lane + 64 * q;
+    if (e < E) {
+      float g = v[q] * (dp[q] - inner);
+      dl[t * E + e] = g;
+      if (dl16) dl16[t * E + e] = f32_to_bf16(g);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+#define MOE_LAUNCH_CHECK() \
+  do {                     \
+    hipError_t e_ = hipGetLastError(); if (e_ != hipSuccess) return e_; \
+  } while (0)
+
+hipError_t launch_topk_softmax(const float* logits, int T, int E, int k, int32_t* idx, float* w,
+                               hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  hipLaunchKernelGGL(topk_softmax_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k,
+                     idx, w);
+  return hipGetLastError();
+}
+
+hipError_t launch_dispatch_meta(const int32_t* idx, int T, int E, int k, int32_t* hist,
+                                int32_t* base, int32_t* counts, int32_t* offsets,
+                                int32_t* dest_row, int32_t* src_token, hipStream_t s) {
+  const int nblk = (T + 63) / 64;
+  hipLaunchKernelGGL(block_hist_kernel, dim3(nblk), dim3(64), 0, s, idx, T, E, k, nblk, hist);
+  MOE_LAUNCH_CHECK();
+  hipLaunchKernelGGL(scan_kernel, dim3(E), dim3(256), 0, s, hist, nblk, base, counts);
+  MOE_LAUNCH_CHECK();
+  hipLaunchKernelGGL(rank_kernel, dim3(nblk), dim3(64), 0, s, idx, T, E, k, nblk, base, counts,
+                     offsets, dest_row, src_token);
+  return hipGetLastError();
+}
+
+template <typename TS>
+static hipError_t copy_impl(const void* x, const int32_t* src, int R, int T, int d, void* Xs,
+                            hipStream_t s) {
+  hipLaunchKernelGGL(dispatch_copy_kernel<TS>, dim3((R + 3) / 4), dim3(256), 0, s,
+                     static_cast<const TS*>(x), src, R, T, d, static_cast<TS*>(Xs));
+  return hipGetLastError();
+}
+
+hipError_t launch_dispatch_copy(int dtype, const void* x, const int32_t* src_token, int R, int T,
+                                int d, void* Xs, hipStream_t s) {
+  if (R == 0) return hipSuccess;
+  return dtype ? copy_impl<bf16_t>(x, src_token, R, T, d, Xs, s)
+               : copy_impl<float>(x, src_token, R, T, d, Xs, s);
+}
+
+hipError_t launch_combine(int dtype, const void* Ys, const float* w, const int32_t* dest, int T,
+                          int d, int k, void* y, hipStream_t s) {
+  dim3 grid((T + 3) / 4);
+  if (dtype)
+    hipLaunchKernelGGL(combine_kernel<bf16_t>, grid, dim3(256), 0, s,
+                       static_cast<const bf16_t*>(Ys), w, dest, T, d, k, static_cast<bf16_t*>(y));
+  else
+    hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, s,
+                       static_cast<const float*>(Ys), w, dest, T, d, k, static_cast<float*>(y));
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_bwd(int dtype, const void* dY, const void* Ys, const float* w,
+                              const int32_t* dest, int T, int d, int k, void* dYs, float* dw,
+                              hipStream_t s) {
+  dim3 grid((T + 3) / 4);
+  if (dtype)
+    hipLaunchKernelGGL(combine_bwd_kernel<bf16_t>, grid, dim3(256), 0, s,
+                       static_cast<const bf16_t*>(dY), static_cast<const bf16_t*>(Ys), w, dest,
+                       T, d, k, static_cast<bf16_t*>(dYs), dw);
+  else
+    hipLaunchKernelGGL(combine_bwd_kernel<float>, grid, dim3(256), 0, s,
+                       static_cast<const float*>(dY), static_cast<const float*>(Ys), w, dest, T,
+                       d, k, static_cast<float*>(dYs), dw);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_sum(int dtype, const void* dXs, const int32_t* dest, int T, int d, int k,
+                             int accumulate, void* dx, hipStream_t s) {
+  dim3 grid((T + 3) / 4);
+  if (dtype)
+    hipLaunchKernelGGL(gather_sum_kernel<bf16_t>, grid, dim3(256), 0, s,
+                       static_cast<const bf16_t*>(dXs), dest, T, d, k, accumulate,
+                       static_cast<bf16_t*>(dx));
+  else
+    hipLaunchKernelGGL(gather_sum_kernel<float>, grid, dim3(256), 0, s,
+                       static_cast<const float*>(dXs), dest, T, d, k, accumulate,
+                       static_cast<float*>(dx));
+  return hipGetLastError();
+}
+
+hipError_t launch_router_bwd_softmax(const float* logits, const int32_t* idx, const float* dw,
+                                     int T, int E, int k, float* dl, bf16_t* dl16,
+                                     hipStream_t s) {
+  hipLaunchKernelGGL(router_bwd_softmax_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, idx,
+                     dw, T, E, k, dl, dl16);
+  return hipGetLastError();
+}
+
+}  // namespace moe

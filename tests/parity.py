@@ -1,0 +1,106 @@
+"""Helpers of the GPU parity tests: upload seeded inputs, run the layer
+through the C ABI, run the oracle on the same inputs, compare."""
+from __future__ import annotations
+
+import sys
+from typing import Dict, Optional
+
+import numpy as np
+import torch
+
+from moe_synth import Workload, make_inputs
+from oracle import moe_oracle as O
+
+TOL = {"fp32": 1e-4, "bf16": 2e-2, "mxfp8": 6e-2}
+
+
+def say(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def dev_tensor(inp: Dict[str, np.ndarray], name: str, dtype: torch.dtype) -> torch.Tensor:
+    if dtype == torch.bfloat16:
+        bits = inp[name + "_bits"]
+        return torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(inp[name], dtype=np.float32)).cuda()
+
+
+def to_np(t: torch.Tensor) -> np.ndarray:
+    if t.dtype == torch.bfloat16:
+        t = t.float()
+    return t.detach().cpu().numpy().astype(np.float64) if t.is_floating_point() else t.detach().cpu().numpy()
+
+
+def relerr(gpu: np.ndarray, ref: np.ndarray) -> float:
+    """Normwise relative error ||gpu - ref|| / ||ref|| (0 when both are 0)."""
+    gpu = np.asarray(gpu, np.float64); ref = np.asarray(ref, np.float64)
+    nr = np.linalg.norm(ref)
+    nd = np.linalg.norm(gpu - ref)
+    if nr == 0.0:
+        return 0.0 if nd == 0.0 else float("inf")
+    return float(nd / nr)
+
+
+def run_gpu(wl: Workload, inp: Dict[str, np.ndarray], logits: Optional[np.ndarray] = None):
+    """Forward + backward of the layer on the GPU; returns every buffer as numpy."""
+    import routing_grouped_gemm_amd as rgg
+    dt = torch.float32 if wl.dtype == "fp32" else torch.bfloat16
+    router = wl.routing == "router"
+    layer = rgg.ExpertLayer(wl.T, wl.d, wl.E, wl.f, wl.k, dt, wl.prec, router=router)
+    x = dev_tensor(inp, "x", dt)
+    Wg, Wu, Wd = (dev_tensor(inp, n, dt) for n in ("Wg", "Wu", "Wd"))
+    Wr = dev_tensor(inp, "Wr", dt) if router else None
+    dY = dev_tensor(inp, "dY", dt)
+    kw = {}
+    if router and logits is not None:
+        kw["logits"] = torch.from_numpy(np.ascontiguousarray(logits, np.float32)).cuda()
+    if not router:
+        kw["topk_idx"] = torch.from_numpy(inp["topk_idx"]).cuda()
+        kw["topk_w"] = torch.from_numpy(inp["topk_w"]).cuda()
+    layer.forward(x, Wr, Wg, Wu, Wd, **kw)
+    layer.backward(dY)
+    torch.cuda.synchronize()
+    names = ["topk_idx", "topk_w", "counts", "offsets", "dest_row", "src_token", "Hg", "Hu",
+             "A", "Ys", "y", "dYs", "dw", "dH", "dXs", "dx", "dWg", "dWu", "dWd"]
+    if wl.prec != "mxfp8":
+        names.append("Xs")
+    if router:
+        names += ["logits", "dlogits", "dWr"]
+    out = {n: to_np(getattr(layer, n)) for n in names}
+    f = wl.f
+    out["dHg"], out["dHu"] = out["dH"][:, :f], out["dH"][:, f:]
+    return out
+
+
+def run_oracle(wl: Workload, inp: Dict[str, np.ndarray], logits: Optional[np.ndarray] = None):
+    prec = wl.prec
+    if wl.routing == "router":
+        return O.layer(inp["x"], inp["Wr"], inp["Wg"], inp["Wu"], inp["Wd"], wl.k, inp["dY"], prec,
+                       logits=logits)
+    return O.layer(inp["x"], None, inp["Wg"], inp["Wu"], inp["Wd"], wl.k, inp["dY"], prec,
+                   topk_idx=inp["topk_idx"], topk_w=inp["topk_w"])
+
+
+EXACT = ("topk_idx", "counts", "offsets", "dest_row", "src_token")
+FLOATS = ("Xs", "Hg", "Hu", "A", "Ys", "y", "dYs", "dw", "dHg", "dHu", "dXs", "dx", "dWg",
+          "dWu", "dWd", "dlogits", "dWr")
+
+
+def compare(wl: Workload, gpu, ref, tol: Optional[float] = None, skip=()):
+    """Bit-exact integer metadata; normwise relative error per float tensor."""
+    tol = TOL[wl.prec] if tol is None else tol
+    errs = {}
+    for n in EXACT:
+        if n in gpu and n in ref and n not in skip:
+            np.testing.assert_array_equal(gpu[n], np.asarray(ref[n]), err_msg=f"{wl.name}: {n}")
+    if "topk_w" in gpu and "topk_w" in ref:
+        errs["topk_w"] = relerr(gpu["topk_w"], ref["topk_w"])
+        assert errs["topk_w"] <= 1e-5, (wl.name, "topk_w", errs["topk_w"])
+    for n in FLOATS:
+        if n in gpu and n in ref and n not in skip:
+            errs[n] = relerr(gpu[n], ref[n])
+    bad = {n: e for n, e in errs.items() if not (e <= tol)}
+    say(f"  {wl.name}: " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
+    assert not bad, f"{wl.name}: over tolerance {tol}: {bad}"
+    return errs

@@ -1,0 +1,148 @@
+"""The C-ABI library on the host: it loads, exports every entry point that
+include/moe.h declares, sizes workspaces, and rejects bad arguments with the
+documented status before anything is enqueued (no call here reaches a kernel
+launch, so these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+OK, NULL, SHAPE, DTYPE, ALIGN, WS, UNSUP = 0, -1, -2, -3, -4, -5, -6
+F32, BF16 = 0, 1
+P_F32, P_BF16, P_MX = 0, 1, 2
+
+# Fake device addresses: never dereferenced, because every call below fails
+# validation before it could launch anything.
+A = 0x10000          # 16-byte aligned
+MIS = 0x10008        # misaligned
+
+
+@pytest.fixture(scope="module")
+def L():
+    import routing_grouped_gemm_amd as rgg
+    if not os.path.exists(rgg.LIB_PATH):
+        pytest.fail("libmoe_hip.so is not built (python -m routing_grouped_gemm_amd.build)")
+    return rgg.lib()
+
+
+def declared_entry_points():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:int|const char\*)\s+(moe_\w+)\(", txt, flags=re.M)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_entry_points()
+    assert len(names) == 10, names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    for s in (OK, NULL, SHAPE, DTYPE, ALIGN, WS, UNSUP, -7):
+        assert L.moe_status_string(s)
+    assert b"unknown" in L.moe_status_string(12345)
+
+
+def ws_size(L, op, T, d, E, f, k, dtype, prec):
+    out = ctypes.c_size_t(7)
+    s = L.moe_workspace_size(op, T, d, E, f, k, dtype, prec, ctypes.byref(out))
+    return s, out.value
+
+
+def test_workspace_sizes(L):
+    # dispatch: two int32 tables of E * ceil(T/64), each rounded up to 256 bytes
+    s, n = ws_size(L, 1, 8192, 2048, 64, 1024, 8, BF16, P_BF16)
+    assert s == OK and n == 2 * 128 * 64 * 4
+    s, n = ws_size(L, 1, 100, 64, 3, 64, 1, F32, P_F32)
+    assert s == OK and n == 2 * 256
+    # route backward: bf16 copy of dlogits; none in fp32
+    assert ws_size(L, 7, 8192, 2048, 64, 1024, 8, BF16, P_BF16) == (OK, 8192 * 64 * 2)
+    assert ws_size(L, 7, 256, 64, 8, 128, 2, F32, P_F32) == (OK, 0)
+    for op in (0, 2, 3, 4, 5, 6):
+        assert ws_size(L, op, 256, 64, 8, 128, 2, BF16, P_BF16) == (OK, 0)
+    assert ws_size(L, 1, 0, 64, 8, 128, 2, BF16, P_BF16)[0] == SHAPE
+    assert ws_size(L, 1, 8, 64, 8, 128, 2, F32, P_BF16)[0] == DTYPE
+    assert ws_size(L, 1, 8, 64, 8, 128, 2, BF16, 7)[0] == DTYPE
+    assert ws_size(L, 99, 8, 64, 8, 128, 2, BF16, P_BF16)[0] == SHAPE
+    assert L.moe_workspace_size(1, 8, 64, 8, 128, 2, BF16, P_BF16, None) == NULL
+
+
+def route(L, x=A, Wr=A, T=16, d=64, E=8, k=2, dt=BF16, flags=0, lg=A, idx=A, w=A):
+    return L.moe_route(x, Wr, T, d, E, k, dt, flags, lg, idx, w, None, 0, None)
+
+
+def test_route_validation(L):
+    assert route(L, x=None) == NULL
+    assert route(L, lg=None) == NULL
+    assert route(L, T=0) == SHAPE
+    assert route(L, k=0) == SHAPE
+    assert route(L, T=1 << 28, k=16, E=16) == SHAPE      # T*k overflows int32
+    assert route(L, E=300, k=2) == UNSUP
+    assert route(L, E=4, k=5) == UNSUP
+    assert route(L, d=96) == UNSUP
+    assert route(L, dt=5) == DTYPE
+    assert route(L, x=MIS) == ALIGN
+    assert route(L, idx=MIS) == ALIGN
+
+
+def dispatch(L, T=16, d=64, E=8, k=2, dt=BF16, prec=P_BF16, ws=A, wsb=1 << 20, xs=A, sc=A, x=A):
+    return L.moe_dispatch(x, A, T, d, E, k, dt, prec, A, A, A, A, xs, sc, ws, wsb, None)
+
+
+def test_dispatch_validation(L):
+    assert dispatch(L, ws=None) == NULL
+    assert dispatch(L, xs=None) == NULL
+    assert dispatch(L, dt=F32, prec=P_BF16) == DTYPE
+    assert dispatch(L, dt=BF16, prec=P_F32) == DTYPE
+    assert dispatch(L, d=100) == UNSUP
+    assert dispatch(L, x=MIS) == ALIGN
+    assert dispatch(L, wsb=2 * 256 - 1) == WS
+
+
+def ffn_fwd(L, T=16, k=2, d=64, f=64, E=8, dt=BF16, prec=P_BF16, Xs=A, Wg=A):
+    return L.moe_grouped_ffn_fwd(Xs, A, A, T, k, d, f, E, Wg, A, A, dt, prec, A, A, A, A,
+                                 A, 1 << 20, None)
+
+
+def test_ffn_fwd_validation(L):
+    assert ffn_fwd(L, Xs=None) == NULL
+    assert ffn_fwd(L, f=96) == UNSUP
+    assert ffn_fwd(L, f=0) == SHAPE
+    assert ffn_fwd(L, dt=F32) == DTYPE
+    assert ffn_fwd(L, Wg=MIS) == ALIGN
+    assert ffn_fwd(L, E=257) == UNSUP
+
+
+def ffn_bwd(L, Xs=A, x=A, src=A, dt=BF16, prec=P_BF16, f=64, dH=A):
+    return L.moe_grouped_ffn_bwd(A, Xs, x, src, A, A, A, A, 16, 2, 64, f, 8, A, A, A, dt, prec,
+                                 0, dH, A, A, A, A, A, 1 << 20, None)
+
+
+def test_ffn_bwd_validation(L):
+    assert ffn_bwd(L, Xs=None) == NULL             # bf16 needs the dispatched rows
+    assert ffn_bwd(L, dH=None) == NULL
+    assert ffn_bwd(L, f=32) == UNSUP
+    assert ffn_bwd(L, dH=MIS) == ALIGN
+    assert ffn_bwd(L, dt=F32, prec=P_MX) == DTYPE
+
+
+def test_combine_and_gather_validation(L):
+    assert L.moe_combine(A, A, A, 16, 64, 2, BF16, None, None) == NULL
+    assert L.moe_combine(A, A, A, 0, 64, 2, BF16, A, None) == SHAPE
+    assert L.moe_combine(A, A, A, 16, 72, 2, BF16, A, None) == UNSUP
+    assert L.moe_combine(A, A, A, 16, 64, 2, BF16, MIS, None) == ALIGN
+    assert L.moe_combine_bwd(A, A, A, A, 16, 64, 2, 9, A, A, None) == DTYPE
+    assert L.moe_dispatch_bwd(A, A, 16, 64, 0, BF16, 0, A, None) == SHAPE
+    assert L.moe_dispatch_bwd(None, A, 16, 64, 2, BF16, 0, A, None) == NULL
+
+
+def test_route_bwd_validation(L):
+    f = L.moe_route_bwd
+    assert f(A, A, A, A, A, 16, 64, 8, 2, BF16, 0, A, A, A, None, 0, None) == NULL   # bf16 needs ws
+    assert f(A, A, A, A, A, 16, 64, 8, 2, BF16, 0, A, A, A, A, 16 * 8 * 2 - 1, None) == WS
+    assert f(A, A, A, A, A, 16, 64, 8, 2, BF16, 0, A, A, MIS, A, 1 << 20, None) == ALIGN
+    assert f(A, A, A, A, A, 16, 64, 8, 9, BF16, 0, A, A, A, A, 1 << 20, None) == UNSUP
