@@ -1,0 +1,209 @@
+#!/usr/bin/env python3
+"""Benchmark of one dropless top-k MoE expert layer, forward + backward, on
+one MI355X.
+
+A step is one pass of the whole layer over one batch of synthetic inputs
+already resident in HBM: route -> dispatch -> grouped FFN forward ->
+combine, then combine backward -> grouped FFN backward -> dispatch backward
+-> router backward, all through the C ABI (libmoe_hip.so).
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME]
+
+Prints one JSON line.  `value` is tokens per second of the whole layer
+(forward + backward).  Per-kernel durations come from HIP events recorded on
+the library's stream after every kernel launch inside the timed region; the
+dominant kernel gives the `roofline` object.  `cpu_baseline` times the CPU
+oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer fwd+bwd tokens/s and TFLOP/s (% of MI355X bf16/MXFP8 MFMA peak)"
+PEAK_TFLOPS = {"bf16": 2500.0, "mxfp8": 5000.0, "fp32": 157.3}
+HBM_PEAK_GBS = 8000.0
+
+
+def gemm_flops(name: str, wl) -> float:
+    """Algorithmic FLOPs of one launch of a GEMM kernel: 2 * rows * (output
+    width) * (contraction) with only the routed rows counted."""
+    R, T, d, f, E = wl.R, wl.T, wl.d, wl.f, wl.E
+    per_row = {
+        "gemm_fwd_gateup_swiglu": 4.0 * d * f,      # Xs . [Wg|Wu]
+        "gemm_fwd_down": 2.0 * f * d,               # A . Wd
+        "gemm_dgrad_down_swiglu_bwd": 2.0 * d * f,  # dYs . Wd^T
+        "gemm_dgrad_gateup": 4.0 * f * d,           # [dHg|dHu] . [Wg|Wu]^T
+        "gemm_wgrad_gateup": 4.0 * d * f,           # Xs^T . [dHg|dHu]
+        "gemm_wgrad_down": 2.0 * f * d,             # A^T . dYs
+    }
+    if name in per_row:
+        return per_row[name] * R
+    if name in ("gemm_router_logits", "gemm_router_dwr", "gemm_router_dx"):
+        return 2.0 * T * d * E
+    return 0.0
+
+
+def cpu_baseline(wl, inp, tokens: int):
+    """The CPU oracle, as it is, on the first `tokens` tokens (or rows)."""
+    import numpy as np
+    from oracle import moe_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    S = min(tokens, wl.T)
+    t0 = time.perf_counter()
+    if wl.routing == "router":
+        O.layer(inp["x"][:S], inp["Wr"], inp["Wg"], inp["Wu"], inp["Wd"], wl.k, inp["dY"][:S],
+                wl.prec)
+    else:
+        O.layer(inp["x"][:S], None, inp["Wg"], inp["Wu"], inp["Wd"], wl.k, inp["dY"][:S], wl.prec,
+                topk_idx=inp["topk_idx"][:S], topk_w=inp["topk_w"][:S])
+    dt = time.perf_counter() - t0
+    return {"value": S / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "seconds": round(dt, 2),
+            "sample": f"forward+backward of the first {S} of {wl.T} tokens with the full "
+                      f"expert weights (numpy float64 oracle with {wl.prec} storage rounding)"}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="olmoe_bf16")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-tokens", type=int, default=1024,
+                    help="tokens of the CPU-oracle sample (0 = skip the CPU baseline)")
+    ap.add_argument("--kernels", action="store_true", help="per-kernel table on stderr")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py: this layer runs on one GPU; --gpus {args.gpus} is not supported "
+              "(expert-parallel exchange across GPUs is not built)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    import routing_grouped_gemm_amd as rgg
+    from moe_synth import workload, make_inputs
+
+    wl = workload(args.workload)
+    inp = make_inputs(wl, seed=args.seed)
+    dt = torch.float32 if wl.dtype == "fp32" else torch.bfloat16
+
+    def dev(name):
+        if dt == torch.bfloat16:
+            return rgg.upload(inp[name + "_bits"], torch.bfloat16)
+        return rgg.upload(inp[name])
+
+    router = wl.routing == "router"
+    x, dY = dev("x"), dev("dY")
+    Wg, Wu, Wd = dev("Wg"), dev("Wu"), dev("Wd")
+    Wr = dev("Wr") if router else None
+    kw = {}
+    if not router:
+        kw = dict(topk_idx=rgg.upload(inp["topk_idx"]), topk_w=rgg.upload(inp["topk_w"]))
+    layer = rgg.ExpertLayer(wl.T, wl.d, wl.E, wl.f, wl.k, dt, wl.prec, router=router)
+
+    def step():
+        layer.forward(x, Wr, Wg, Wu, Wd, **kw)
+        layer.backward(dY)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    timer = rgg.KernelTimer(capacity=K * 32)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    with timer:
+        t_start.record()
+        for _ in range(K):
+            step()
+        t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms = t_start.elapsed_time(t_end) / K
+    kern = timer.durations()
+
+    per = {}
+    for name, dur in kern:
+        c = per.setdefault(name, [0, 0.0])
+        c[0] += 1
+        c[1] += dur
+    table = sorted(((n, c[0] / K, c[1] / K, c[1] / c[0]) for n, c in per.items()),
+                   key=lambda r: -r[2])
+    gemm_ms = sum(r[2] for r in table if r[0].startswith("gemm_") and "router" not in r[0])
+    dom = table[0]
+    dom_name, dom_launch_ms = dom[0], dom[3]
+    dom_flops = gemm_flops(dom_name, wl)
+    peak = PEAK_TFLOPS[wl.prec]
+    if dom_flops > 0:
+        ach = dom_flops / (dom_launch_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "kernel": dom_name, "achieved": round(ach, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": None,
+                "per_launch_ms": round(dom_launch_ms, 4),
+                "algorithmic_flops_per_launch": dom_flops}
+    else:
+        roof = {"bound": "hbm", "kernel": dom_name, "achieved": None, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": None, "traffic": None}
+
+    flops = wl.flops()
+    tok_s = wl.T / (ms * 1e-3)
+    tflops = flops / (ms * 1e-3) / 1e12
+    ffn_tflops = wl.expert_flops() / (gemm_ms * 1e-3) / 1e12 if gemm_ms > 0 else None
+
+    cpu = None
+    if args.cpu_tokens > 0:
+        cpu = cpu_baseline(wl, inp, args.cpu_tokens)
+
+    if args.kernels:
+        print(f"{'kernel':32s} {'launches/step':>13s} {'ms/step':>9s} {'ms/launch':>10s}",
+              file=sys.stderr)
+        for n, c, tot, one in table:
+            print(f"{n:32s} {c:13.0f} {tot:9.4f} {one:10.4f}", file=sys.stderr)
+
+    out = {
+        "metric": METRIC,
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.prec,
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02^2) weights)",
+        "config": {"workload": wl.name, "T": wl.T, "d_model": wl.d, "experts": wl.E,
+                   "d_ff": wl.f, "top_k": wl.k, "routed_rows": wl.R, "routing": wl.routing,
+                   "parallelism": "single GPU"},
+        "tflops": round(tflops, 2),
+        "pct_peak": round(100.0 * tflops / peak, 2),
+        "ffn_gemm_tflops": None if ffn_tflops is None else round(ffn_tflops, 2),
+        "ffn_gemm_pct_peak": None if ffn_tflops is None else round(100.0 * ffn_tflops / peak, 2),
+        "wall_ms_per_step": round(wall * 1e3 / K, 4),
+        "kernels_ms_per_step": {n: round(tot, 4) for n, _, tot, _ in table},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -61,7 +61,7 @@ enum moe_status {
   MOE_ERR_DTYPE = -3,       /* unknown dtype/prec, or a dtype/prec pair that does not exist */
   MOE_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned */
   MOE_ERR_WORKSPACE = -5,   /* ws_bytes below moe_workspace_size */
-  MOE_ERR_UNSUPPORTED = -6, /* E > 256, k > min(E, 16), d or f not a multiple of 64 */
+  MOE_ERR_UNSUPPORTED = -6, /* E > 256, k > E, d or f not a multiple of 64 */
   MOE_ERR_LAUNCH = -7       /* the HIP runtime rejected a launch */
 };
 
@@ -90,7 +90,8 @@ enum moe_op {
  *   MOE_ROUTE_LOGITS_IN, then read), topk_idx[T,k] i32, topk_w[T,k] f32.
  *   Slots are ordered by (logit desc, expert index asc): ties go to the
  *   lower index; selection is made on the float32 logits.
- *   Limits: 1 <= E <= 256, 1 <= k <= min(E, 16).  d % 64 == 0.
+ *   Limits: 1 <= E <= 256, 1 <= k <= E.  d % 64 == 0 (unless logits are an
+ *   input).
  */
 int moe_route(const void* x, const void* Wr, int T, int d, int E, int k, int dtype,
               unsigned flags, float* logits, int32_t* topk_idx, float* topk_w,
@@ -199,6 +200,23 @@ int moe_workspace_size(int op, int T, int d, int E, int f, int k, int dtype, int
 
 /* Text of a status code (static storage). */
 const char* moe_status_string(int status);
+
+/* Name of the HIP error behind the last MOE_ERR_LAUNCH on this thread, or
+   "none" (static storage). */
+const char* moe_last_launch_error(void);
+
+/*
+ * moe_set_kernel_events -- per-kernel timing hook (observability only).
+ * While set, every kernel launched by an entry point on the calling thread
+ * is followed by hipEventRecord(events[i], stream), i = 0, 1, ... up to
+ * `capacity`, and names[i] (when names is not NULL) receives a static label
+ * of that kernel; *count (when not NULL) tracks how many were recorded.
+ * The events are caller-created hipEvent_t handles.  If a record fails the
+ * hook switches itself off and *count becomes -(HIP error code); the kernel
+ * launches are not affected.  Pass events = NULL to switch the hook off.  This thread-local hook is the only state the library
+ * keeps between calls; it is off by default.
+ */
+int moe_set_kernel_events(void* const* events, const char** names, int capacity, int* count);
 
 #ifdef __cplusplus
 }

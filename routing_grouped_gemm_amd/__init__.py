@@ -25,7 +25,7 @@ __all__ = [
     "lib", "moe_route", "moe_dispatch", "moe_grouped_ffn_fwd", "moe_combine",
     "moe_combine_bwd", "moe_grouped_ffn_bwd", "moe_dispatch_bwd", "moe_route_bwd",
     "moe_workspace_size", "moe_status_string", "ExpertLayer", "LIB_PATH",
-    "MOE_ROUTE_LOGITS_IN", "MOE_ACCUMULATE",
+    "MOE_ROUTE_LOGITS_IN", "MOE_ACCUMULATE", "KernelTimer", "upload",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_hip.so")
@@ -67,10 +67,30 @@ def lib() -> ctypes.CDLL:
             fn = getattr(L, name)
             fn.argtypes = args
             fn.restype = ctypes.c_int
+        L.moe_set_kernel_events.argtypes = [_P, _P, _I, _P]
+        L.moe_set_kernel_events.restype = ctypes.c_int
+        L.moe_last_launch_error.argtypes = []
+        L.moe_last_launch_error.restype = ctypes.c_char_p
         L.moe_status_string.argtypes = [ctypes.c_int]
         L.moe_status_string.restype = ctypes.c_char_p
         _lib = L
     return _lib
+
+
+def upload(a, dtype: Optional[torch.dtype] = None, device="cuda") -> torch.Tensor:
+    """Copy a host numpy array to the GPU through a freshly allocated pinned
+    buffer.  Large copies straight from pageable memory make the runtime pin
+    the user's pages in place, which some hosts refuse; staging through
+    allocated pinned memory avoids that.  dtype=torch.bfloat16 takes an
+    array of raw bf16 bit patterns (uint16/int16)."""
+    import numpy as np
+    a = np.ascontiguousarray(a)
+    if dtype == torch.bfloat16:
+        t = torch.from_numpy(a.view(np.int16))
+    else:
+        t = torch.from_numpy(a)
+    out = t.pin_memory().to(device)
+    return out.view(torch.bfloat16) if dtype == torch.bfloat16 else out
 
 
 def moe_status_string(status: int) -> str:
@@ -79,7 +99,10 @@ def moe_status_string(status: int) -> str:
 
 def _check(status: int, name: str) -> None:
     if status != 0:
-        raise RuntimeError(f"{name}: {moe_status_string(status)} (status {status})")
+        detail = ""
+        if status == -7:
+            detail = f", HIP error {lib().moe_last_launch_error().decode()}"
+        raise RuntimeError(f"{name}: {moe_status_string(status)} (status {status}{detail})")
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -187,6 +210,48 @@ def moe_route_bwd(x, Wr, logits, topk_idx, dtopk_w, dlogits, dWr, dx, ws=None, a
                                d, E, k, _dtype(x), MOE_ACCUMULATE if accumulate else 0,
                                _ptr(dlogits), _ptr(dWr), _ptr(dx), wp, wb, _stream(stream)),
            "moe_route_bwd")
+
+
+class KernelTimer:
+    """Per-kernel durations through moe_set_kernel_events: a start event, then
+    one event after every kernel the library launches on this thread."""
+
+    def __init__(self, capacity: int = 4096):
+        self.capacity = capacity
+        self.events = [torch.cuda.Event(enable_timing=True) for _ in range(capacity)]
+        self.start = torch.cuda.Event(enable_timing=True)
+        self._names = (ctypes.c_char_p * capacity)()
+        self._count = ctypes.c_int(0)
+        self._handles = None
+
+    def __enter__(self):
+        # torch creates the HIP events lazily, on their first record()
+        for e in self.events:
+            e.record()
+        torch.cuda.synchronize()
+        handles = [e.cuda_event for e in self.events]
+        if not all(handles):
+            raise RuntimeError("KernelTimer: torch did not create the HIP events")
+        self._handles = (ctypes.c_void_p * self.capacity)(*handles)
+        self.start.record()
+        _check(lib().moe_set_kernel_events(self._handles, self._names, self.capacity,
+                                           ctypes.byref(self._count)), "moe_set_kernel_events")
+        return self
+
+    def __exit__(self, *exc):
+        lib().moe_set_kernel_events(None, None, 0, None)
+        return False
+
+    def durations(self):
+        """[(kernel name, milliseconds)] in launch order (after synchronising)."""
+        torch.cuda.synchronize()
+        if self._count.value < 0:
+            raise RuntimeError(f"KernelTimer: hipEventRecord failed (HIP error {-self._count.value})")
+        out, prev = [], self.start
+        for i in range(self._count.value):
+            out.append((self._names[i].decode(), prev.elapsed_time(self.events[i])))
+            prev = self.events[i]
+        return out
 
 
 class ExpertLayer:

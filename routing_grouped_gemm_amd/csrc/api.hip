@@ -34,13 +34,25 @@ int num_cu() {
   return cache[dev];
 }
 
-inline int status_of(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH; }
+thread_local hipError_t g_last_launch_error = hipSuccess;
+
+inline int status_of(hipError_t e) {
+  if (e == hipSuccess) return MOE_OK;
+  g_last_launch_error = e;
+  return MOE_ERR_LAUNCH;
+}
 
 #define MOE_TRY(expr)                                    \
   do {                                                   \
     hipError_t e_ = (expr);                              \
-    if (e_ != hipSuccess) return MOE_ERR_LAUNCH;         \
+    if (e_ != hipSuccess) return status_of(e_);          \
   } while (0)
+
+// hipGetLastError reports the last error of any earlier runtime call on this
+// thread (for example a not-ready event query made by another library);
+// every entry point clears it once its arguments are valid, so that the
+// check after each of its own launches sees only that launch.
+inline void clear_stale_error() { (void)hipGetLastError(); }
 
 inline int check_dtype(int dtype) { return (dtype == MOE_F32 || dtype == MOE_BF16) ? MOE_OK : MOE_ERR_DTYPE; }
 
@@ -89,6 +101,10 @@ inline int gemm_engine(int dtype, int router_E = 8) {
 }  // namespace
 
 extern "C" {
+
+const char* moe_last_launch_error(void) {
+  return g_last_launch_error == hipSuccess ? "none" : hipGetErrorName(g_last_launch_error);
+}
 
 const char* moe_status_string(int status) {
   switch (status) {
@@ -148,6 +164,7 @@ int moe_route(const void* x, const void* Wr, int T, int d, int E, int k, int dty
   }
   if (!all_aligned(x, Wr, logits, topk_idx, topk_w)) return MOE_ERR_ALIGN;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  clear_stale_error();
   if (!lin) {
     GemmArgs g{};
     g.E = 1; g.offsets = nullptr; g.rows_total = T; g.ragged = RAG_M;
@@ -173,6 +190,7 @@ int moe_dispatch(const void* x, const int32_t* topk_idx, int T, int d, int E, in
   if (!all_aligned(x, topk_idx, counts, offsets, dest_row, src_token, Xs, ws)) return MOE_ERR_ALIGN;
   if (ws_bytes < dispatch_ws(T, E)) return MOE_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  clear_stale_error();
   const size_t nblk = (size_t)(T + 63) / 64;
   int32_t* hist = static_cast<int32_t*>(ws);
   int32_t* base = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + align_up(nblk * E * 4));
@@ -199,6 +217,7 @@ int moe_grouped_ffn_fwd(const void* Xs, const uint8_t* Xs_scale, const int32_t* 
   if (int s = check_elems(E, (long long)d * f)) return s;
   if (!all_aligned(Xs, offsets, Wg, Wu, Wd, Hg, Hu, A, Ys, ws)) return MOE_ERR_ALIGN;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  clear_stale_error();
   if (prec == MOE_PREC_MXFP8) {
     if (ws_bytes < mx_fwd_workspace(R, d, f, E)) return MOE_ERR_WORKSPACE;
     return status_of(mx_ffn_fwd(Xs, Xs_scale, offsets, (int)R, d, f, E, Wg, Wu, Wd, Hg, Hu, A,
@@ -228,6 +247,7 @@ int moe_combine(const void* Ys, const float* topk_w, const int32_t* dest_row, in
   if (T <= 0 || k <= 0 || (long long)T * k > 0x7fffffffLL) return MOE_ERR_SHAPE;
   if (int s = check_width(d)) return s;
   if (!all_aligned(Ys, topk_w, dest_row, y)) return MOE_ERR_ALIGN;
+  clear_stale_error();
   return status_of(launch_combine(dtype, Ys, topk_w, dest_row, T, d, k, y,
                                   static_cast<hipStream_t>(stream)));
 }
@@ -239,6 +259,7 @@ int moe_combine_bwd(const void* dY, const void* Ys, const float* topk_w, const i
   if (T <= 0 || k <= 0 || (long long)T * k > 0x7fffffffLL) return MOE_ERR_SHAPE;
   if (int s = check_width(d)) return s;
   if (!all_aligned(dY, Ys, topk_w, dest_row, dYs, dtopk_w)) return MOE_ERR_ALIGN;
+  clear_stale_error();
   return status_of(launch_combine_bwd(dtype, dY, Ys, topk_w, dest_row, T, d, k, dYs, dtopk_w,
                                       static_cast<hipStream_t>(stream)));
 }
@@ -266,6 +287,7 @@ int moe_grouped_ffn_bwd(const void* dYs, const void* Xs, const void* x, const in
   if (!all_aligned(dYs, Xs, x, src_token, Hg, Hu, A, offsets, Wg, Wu, Wd, dH, dXs, dWg, dWu, dWd, ws))
     return MOE_ERR_ALIGN;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  clear_stale_error();
   const int acc = (flags & MOE_ACCUMULATE) ? 1 : 0;
   const int eng = gemm_engine(dtype);
   if (prec == MOE_PREC_MXFP8) {
@@ -317,6 +339,7 @@ int moe_dispatch_bwd(const void* dXs, const int32_t* dest_row, int T, int d, int
   if (T <= 0 || k <= 0 || (long long)T * k > 0x7fffffffLL) return MOE_ERR_SHAPE;
   if (int s = check_width(d)) return s;
   if (!all_aligned(dXs, dest_row, dx)) return MOE_ERR_ALIGN;
+  clear_stale_error();
   return status_of(launch_gather_sum(dtype, dXs, dest_row, T, d, k,
                                      (flags & MOE_ACCUMULATE) ? 1 : 0, dx,
                                      static_cast<hipStream_t>(stream)));
@@ -335,6 +358,7 @@ int moe_route_bwd(const void* x, const void* Wr, const float* logits, const int3
   if (need && !ws) return MOE_ERR_NULL;
   if (ws_bytes < need) return MOE_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  clear_stale_error();
   uint16_t* dl16 = (dtype == MOE_BF16) ? static_cast<uint16_t*>(ws) : nullptr;
   MOE_TRY(launch_router_bwd_softmax(logits, topk_idx, dtopk_w, T, E, k, dlogits, dl16, st));
   const void* dl = (dtype == MOE_BF16) ? static_cast<const void*>(dl16) : dlogits;

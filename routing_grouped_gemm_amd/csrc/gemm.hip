@@ -21,6 +21,7 @@
 // float32 engine (the fp32 layer and odd router shapes): a plain LDS-tiled
 // SIMT kernel with the same tile schedule and the same epilogues.
 #include "gemm.h"
+#include "hook.h"
 #include "moe_common.h"
 
 namespace moe {
@@ -649,6 +650,20 @@ int tiles_upper_bound(const GemmArgs& g, int BM, int BNT) {
   return E * ((g.M + BM - 1) / BM) * ntn;
 }
 
+const char* kind_name(int kind, const GemmArgs& g) {
+  switch (kind) {
+    case GK_FWD_GATEUP: return "gemm_fwd_gateup_swiglu";
+    case GK_FWD_DOWN: return "gemm_fwd_down";
+    case GK_DGRAD_DOWN: return "gemm_dgrad_down_swiglu_bwd";
+    case GK_DGRAD_GATEUP: return "gemm_dgrad_gateup";
+    case GK_WGRAD: return g.c1 ? "gemm_wgrad_gateup" : "gemm_wgrad_down";
+    case GK_ROUTER_LOGITS: return "gemm_router_logits";
+    case GK_ROUTER_DWR: return "gemm_router_dwr";
+    case GK_ROUTER_DX: return "gemm_router_dx";
+  }
+  return "gemm";
+}
+
 template <int KIND>
 hipError_t launch_kind(int dtype, const GemmArgs& g, int num_cu, hipStream_t stream) {
   if (dtype == GEMM_BF16_MFMA) {
@@ -666,6 +681,7 @@ hipError_t launch_kind(int dtype, const GemmArgs& g, int num_cu, hipStream_t str
     else
       hipLaunchKernelGGL((st::gemm_simt_kernel<KIND, bf16_t>), dim3(grid), dim3(st::NTHR), 0, stream, g);
   }
+  note_launch(kind_name(KIND, g), stream);
   return hipGetLastError();
 }
 

@@ -16,6 +16,7 @@
 // and stores.  The combine and the gathers of the backward run one wave per
 // token and sum in float32 in slot order.
 #include "moe_common.h"
+#include "hook.h"
 #include "route.h"
 
 namespace moe {
@@ -370,6 +371,7 @@ hipError_t launch_topk_softmax(const float* logits, int T, int E, int k, int32_t
   if (T == 0) return hipSuccess;
   hipLaunchKernelGGL(topk_softmax_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k,
                      idx, w);
+  note_launch("topk_softmax", s);
   return hipGetLastError();
 }
 
@@ -378,11 +380,14 @@ hipError_t launch_dispatch_meta(const int32_t* idx, int T, int E, int k, int32_t
                                 int32_t* dest_row, int32_t* src_token, hipStream_t s) {
   const int nblk = (T + 63) / 64;
   hipLaunchKernelGGL(block_hist_kernel, dim3(nblk), dim3(64), 0, s, idx, T, E, k, nblk, hist);
+  note_launch("block_hist", s);
   MOE_LAUNCH_CHECK();
   hipLaunchKernelGGL(scan_kernel, dim3(E), dim3(256), 0, s, hist, nblk, base, counts);
+  note_launch("expert_scan", s);
   MOE_LAUNCH_CHECK();
   hipLaunchKernelGGL(rank_kernel, dim3(nblk), dim3(64), 0, s, idx, T, E, k, nblk, base, counts,
                      offsets, dest_row, src_token);
+  note_launch("rank", s);
   return hipGetLastError();
 }
 
@@ -391,6 +396,7 @@ static hipError_t copy_impl(const void* x, const int32_t* src, int R, int T, int
                             hipStream_t s) {
   hipLaunchKernelGGL(dispatch_copy_kernel<TS>, dim3((R + 3) / 4), dim3(256), 0, s,
                      static_cast<const TS*>(x), src, R, T, d, static_cast<TS*>(Xs));
+  note_launch("dispatch_copy", s);
   return hipGetLastError();
 }
 
@@ -410,6 +416,7 @@ hipError_t launch_combine(int dtype, const void* Ys, const float* w, const int32
   else
     hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, s,
                        static_cast<const float*>(Ys), w, dest, T, d, k, static_cast<float*>(y));
+  note_launch("combine", s);
   return hipGetLastError();
 }
 
@@ -425,6 +432,7 @@ hipError_t launch_combine_bwd(int dtype, const void* dY, const void* Ys, const f
     hipLaunchKernelGGL(combine_bwd_kernel<float>, grid, dim3(256), 0, s,
                        static_cast<const float*>(dY), static_cast<const float*>(Ys), w, dest, T,
                        d, k, static_cast<float*>(dYs), dw);
+  note_launch("combine_bwd", s);
   return hipGetLastError();
 }
 
@@ -439,6 +447,7 @@ hipError_t launch_gather_sum(int dtype, const void* dXs, const int32_t* dest, in
     hipLaunchKernelGGL(gather_sum_kernel<float>, grid, dim3(256), 0, s,
                        static_cast<const float*>(dXs), dest, T, d, k, accumulate,
                        static_cast<float*>(dx));
+  note_launch("gather_sum", s);
   return hipGetLastError();
 }
 
@@ -447,6 +456,7 @@ hipError_t launch_router_bwd_softmax(const float* logits, const int32_t* idx, co
                                      hipStream_t s) {
   hipLaunchKernelGGL(router_bwd_softmax_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, idx,
                      dw, T, E, k, dl, dl16);
+  note_launch("router_bwd_softmax", s);
   return hipGetLastError();
 }
 

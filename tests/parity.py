@@ -20,10 +20,10 @@ def say(msg: str) -> None:
 
 
 def dev_tensor(inp: Dict[str, np.ndarray], name: str, dtype: torch.dtype) -> torch.Tensor:
+    from routing_grouped_gemm_amd import upload
     if dtype == torch.bfloat16:
-        bits = inp[name + "_bits"]
-        return torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
-    return torch.from_numpy(np.ascontiguousarray(inp[name], dtype=np.float32)).cuda()
+        return upload(inp[name + "_bits"], torch.bfloat16)
+    return upload(np.ascontiguousarray(inp[name], dtype=np.float32))
 
 
 def to_np(t: torch.Tensor) -> np.ndarray:
@@ -54,10 +54,10 @@ def run_gpu(wl: Workload, inp: Dict[str, np.ndarray], logits: Optional[np.ndarra
     dY = dev_tensor(inp, "dY", dt)
     kw = {}
     if router and logits is not None:
-        kw["logits"] = torch.from_numpy(np.ascontiguousarray(logits, np.float32)).cuda()
+        kw["logits"] = rgg.upload(np.ascontiguousarray(logits, np.float32))
     if not router:
-        kw["topk_idx"] = torch.from_numpy(inp["topk_idx"]).cuda()
-        kw["topk_w"] = torch.from_numpy(inp["topk_w"]).cuda()
+        kw["topk_idx"] = rgg.upload(inp["topk_idx"])
+        kw["topk_w"] = rgg.upload(inp["topk_w"])
     layer.forward(x, Wr, Wg, Wu, Wd, **kw)
     layer.backward(dY)
     torch.cuda.synchronize()

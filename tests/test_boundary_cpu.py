@@ -36,15 +36,26 @@ def declared_entry_points():
 
 def test_exports_every_declared_symbol(L):
     names = declared_entry_points()
-    assert len(names) == 10, names
+    assert len(names) == 12, names
     for n in names:
         assert hasattr(L, n), n
+
+
+def test_kernel_event_hook_switches(L):
+    # switching the hook on and off needs no device
+    cnt = ctypes.c_int(5)
+    assert L.moe_set_kernel_events(None, None, 0, ctypes.byref(cnt)) == OK and cnt.value == 0
+    ev = (ctypes.c_void_p * 4)()
+    assert L.moe_set_kernel_events(ev, None, 0, None) == SHAPE
+    assert L.moe_set_kernel_events(ev, None, 4, ctypes.byref(cnt)) == OK and cnt.value == 0
+    assert L.moe_set_kernel_events(None, None, 0, None) == OK
 
 
 def test_status_strings(L):
     for s in (OK, NULL, SHAPE, DTYPE, ALIGN, WS, UNSUP, -7):
         assert L.moe_status_string(s)
     assert b"unknown" in L.moe_status_string(12345)
+    assert L.moe_last_launch_error() == b"none"
 
 
 def ws_size(L, op, T, d, E, f, k, dtype, prec):

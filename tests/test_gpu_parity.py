@@ -89,7 +89,7 @@ def test_topk_with_ties(E, k):
     T = 333
     lg = rng.integers(-3, 4, size=(T, E)).astype(np.float32)
     lg[:7] = 0.0
-    logits = torch.from_numpy(lg).cuda()
+    logits = rgg.upload(lg)
     idx = torch.empty(T, k, dtype=torch.int32, device="cuda")
     w = torch.empty(T, k, dtype=torch.float32, device="cuda")
     rgg.moe_route(None, None, k, logits, idx, w, logits_in=True)
