@@ -93,6 +93,9 @@ inline size_t dispatch_ws(int T, int E) {
   return 2 * align_up(nblk * (size_t)E * sizeof(int32_t));
 }
 
+// Width of the bf16 copy of dlogits: E rounded up to the MFMA engine's K step.
+inline int router_ld16(int E) { return (E + 31) / 32 * 32; }
+
 inline int gemm_engine(int dtype, int router_E = 8) {
   if (dtype == MOE_F32) return GEMM_F32_SIMT;
   return (router_E % 8 == 0) ? GEMM_BF16_MFMA : GEMM_BF16_SIMT;
@@ -143,7 +146,7 @@ int moe_workspace_size(int op, int T, int d, int E, int f, int k, int dtype, int
       *bytes = (prec == MOE_PREC_MXFP8) ? mx_bwd_workspace(R, d, f, E) : 0;
       return MOE_OK;
     case MOE_OP_ROUTE_BWD:
-      *bytes = (dtype == MOE_BF16) ? align_up((size_t)T * E * 2) : 0;
+      *bytes = (dtype == MOE_BF16) ? align_up((size_t)T * router_ld16(E) * 2) : 0;
       return MOE_OK;
   }
   return MOE_ERR_SHAPE;
@@ -354,27 +357,30 @@ int moe_route_bwd(const void* x, const void* Wr, const float* logits, const int3
   if (int s = check_width(d)) return s;
   if (int s = check_elems(T, d)) return s;
   if (!all_aligned(x, Wr, logits, topk_idx, dtopk_w, dlogits, dWr, dx, ws)) return MOE_ERR_ALIGN;
-  const size_t need = (dtype == MOE_BF16) ? align_up((size_t)T * E * 2) : 0;
+  const int ld16 = router_ld16(E);
+  const size_t need = (dtype == MOE_BF16) ? align_up((size_t)T * ld16 * 2) : 0;
   if (need && !ws) return MOE_ERR_NULL;
   if (ws_bytes < need) return MOE_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   clear_stale_error();
   uint16_t* dl16 = (dtype == MOE_BF16) ? static_cast<uint16_t*>(ws) : nullptr;
-  MOE_TRY(launch_router_bwd_softmax(logits, topk_idx, dtopk_w, T, E, k, dlogits, dl16, st));
+  MOE_TRY(launch_router_bwd_softmax(logits, topk_idx, dtopk_w, T, E, k, dlogits, dl16, ld16, st));
   const void* dl = (dtype == MOE_BF16) ? static_cast<const void*>(dl16) : dlogits;
+  const int ldl = (dtype == MOE_BF16) ? ld16 : E;
   const int eng = gemm_engine(dtype, E);
   GemmArgs g{};
   g.E = 1; g.offsets = nullptr; g.rows_total = T; g.ragged = RAG_K;
   g.M = d; g.N = E;
   g.a = x; g.lda = d;
-  g.b0 = dl; g.ldb = E;
+  g.b0 = dl; g.ldb = ldl;
   g.c0 = dWr; g.ldc = E;
   g.accumulate = (flags & MOE_ACCUMULATE) ? 1 : 0;
   MOE_TRY(launch_grouped_gemm(GK_ROUTER_DWR, eng, g, num_cu(), st));
   GemmArgs h{};
   h.E = 1; h.offsets = nullptr; h.rows_total = T; h.ragged = RAG_M;
-  h.M = T; h.N = d; h.K = E;
-  h.a = dl; h.lda = E;
+  // the MFMA engine runs K over the zero-padded width; the SIMT engine over E
+  h.M = T; h.N = d; h.K = (eng == GEMM_BF16_MFMA) ? ld16 : E;
+  h.a = dl; h.lda = ldl;
   h.b0 = Wr; h.ldb = E;
   h.c0 = dx; h.ldc = d;
   h.accumulate = 1;

@@ -7,16 +7,17 @@
 //
 // bf16 engine: persistent workgroups of 256 threads (4 waves, one per SIMD)
 // walk a tile list over the ragged expert segments.  Tiles are 256x256
-// outputs with a K step of 64, staged through LDS in two buffers (128 KiB);
-// each wave owns a 128x128 sub-tile as 4x4 MFMA 32x32x16 bf16 blocks with
-// float32 accumulators.  LDS holds both operands K-contiguous (rows of 64
-// bf16 = 128 bytes, 16-byte chunks XOR-swizzled by row), so every MFMA
-// fragment is a single ds_read_b128.  Operands that are contiguous along M or
-// N in HBM (the weights in the forward GEMMs, both operands of the weight
-// gradient) are transposed in registers on their way into LDS (8x8 blocks of
-// bf16 through v_perm_b32).  Consecutive logical tiles go to workgroups of the
-// same XCD, so tiles that share an activation panel or a weight panel meet in
-// the same L2.
+// outputs with a K step of 32 through a 4-stage LDS ring (128 KiB).  Each
+// stage of both operands arrives by buffer->LDS DMA (16 bytes per lane, no
+// register staging); the ring keeps three stages in flight.  Operands that
+// are K-contiguous in HBM sit in LDS as rows of 32 k; operands that are
+// contiguous along M or N (the weights in the forward GEMMs, both operands of
+// the weight gradient) sit as rows of k and are read transposed by
+// ds_read_b64_tr_b16.  Each wave owns a 128x128 sub-tile as 4x4 MFMA
+// 32x32x16 bf16 blocks with float32 accumulators.  Buffer resources bound
+// every operand, so rows past a ragged K or past the end of a tensor read as
+// zeros.  Consecutive logical tiles go to workgroups of the same XCD, so tiles
+// that share an activation or weight panel meet in the same L2.
 //
 // float32 engine (the fp32 layer and odd router shapes): a plain LDS-tiled
 // SIMT kernel with the same tile schedule and the same epilogues.
@@ -217,20 +218,23 @@ __device__ __forceinline__ void store_part(TS* p, const float (&v)[4], int nv, b
 // SwiGLU kinds), n < N.  u: the up-projection values for EPI_SWIGLU_FWD.
 // The SwiGLU and weight-gradient kinds always have n + 3 < N and 4-aligned
 // rows; the plain stores may end in a partial quad.
-template <int EPI, typename TS>
+// PARTIAL: the engine may hand over quads that end past N or rows whose width
+// is not a multiple of 4 (SIMT engine on router shapes); the MFMA engine only
+// takes widths that are multiples of 8 and never does.
+template <int EPI, typename TS, bool PARTIAL = true>
 __device__ __forceinline__ void epilogue4(const GemmArgs& g, const Tile& t, int m, int n,
                                           const float (&v)[4], const float (&u)[4]) {
   if constexpr (EPI == EPI_STORE_F32) {
     long row = (long)t.row0 + m;
     float* p = static_cast<float*>(g.c0) + row * g.ldc + n;
-    if (n + 4 <= g.N && (g.ldc & 3) == 0)
+    if (!PARTIAL || (n + 4 <= g.N && (g.ldc & 3) == 0))
       *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
     else
       store_part(p, v, min(4, g.N - n), false);
   } else if constexpr (EPI == EPI_STORE) {
     long row = (g.ragged == RAG_M) ? (long)t.row0 + m : (long)t.m0 + m;
     TS* p = static_cast<TS*>(g.c0) + (g.ragged == RAG_M ? 0 : (long)t.e * g.c_es) + row * g.ldc + n;
-    if (n + 4 <= g.N && (g.ldc & 3) == 0)
+    if (!PARTIAL || (n + 4 <= g.N && (g.ldc & 3) == 0))
       store4(p, v, g.accumulate != 0);
     else
       store_part(p, v, min(4, g.N - n), g.accumulate != 0);
@@ -272,177 +276,226 @@ __device__ __forceinline__ void epilogue4(const GemmArgs& g, const Tile& t, int 
 // ---------------------------------------------------------------------------
 namespace mf {
 
-constexpr int BM = 256, BN = 256, BK = 64, NTHR = 256;
-constexpr int ROWB = BK * 2;                       // bytes per LDS row
-constexpr int STAGE = (BM + BN) * ROWB;            // bytes per LDS stage
+constexpr int BM = 256, BN = 256, BK = 32, NST = 4, NTHR = 256;
+constexpr int OPB = BM * BK * 2;    // bytes of one operand in one stage (16 KiB)
+constexpr int STAGE = 2 * OPB;      // A then B
+constexpr int DMA_PER_STAGE = 8;    // buffer->LDS loads per wave per stage (4 per operand)
 
-__device__ __forceinline__ int lds_off(int row, int chunk) {
-  return row * ROWB + ((chunk ^ ((row ^ (row >> 3)) & 7)) << 4);
+typedef __attribute__((ext_vector_type(4))) int i32x4_t;
+typedef __attribute__((ext_vector_type(4))) short i16x4_t;
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+// Raw buffer resource over [base, base + bytes): loads beyond it return 0
+// (and write 0 into LDS for the LDS-targeted form).
+__device__ __forceinline__ i32x4_t make_rsrc(const void* base, long long bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint32_t n = bytes <= 0 ? 0u : (bytes >= 0xffffffffLL ? 0xffffffffu : (uint32_t)bytes);
+  i32x4_t r;
+  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  r.y = __builtin_amdgcn_readfirstlane((int)((b >> 32) & 0xffffu));
+  r.z = __builtin_amdgcn_readfirstlane((int)n);
+  r.w = 0x00020000;
+  return r;
 }
 
-// 8x8 bf16 transpose: in[r] holds row r (8 elements); out[i] holds column i.
-__device__ __forceinline__ void transpose8x8(const uint4 (&in)[8], uint4 (&out)[8]) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
-    uint32_t w[4];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const uint4& lo = in[2 * p];
-      const uint4& hi = in[2 * p + 1];
-      uint32_t l = (i >> 1) == 0 ? lo.x : (i >> 1) == 1 ? lo.y : (i >> 1) == 2 ? lo.z : lo.w;
-      uint32_t h = (i >> 1) == 0 ? hi.x : (i >> 1) == 1 ? hi.y : (i >> 1) == 2 ? hi.z : hi.w;
-      w[p] = __builtin_amdgcn_perm(h, l, sel);
-    }
-    out[i] = make_uint4(w[0], w[1], w[2], w[3]);
-  }
+// 16 bytes per lane from the buffer straight into LDS at lds_addr + 16*lane.
+// Issued as inline asm so that the compiler's LDS-DMA tracking does not turn
+// the ring's partial waits into full ones; completion is awaited explicitly
+// with vmcnt before the barrier of the stage that reads the data.
+__device__ __forceinline__ void dma16(i32x4_t rsrc, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
+  i32x4_t r;
+  r.x = __builtin_amdgcn_readfirstlane(rsrc.x);
+  r.y = __builtin_amdgcn_readfirstlane(rsrc.y);
+  r.z = __builtin_amdgcn_readfirstlane(rsrc.z);
+  r.w = __builtin_amdgcn_readfirstlane(rsrc.w);
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr);
+  const uint32_t so = __builtin_amdgcn_readfirstlane(soff);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(m0), "v"(voff), "s"(r), "s"(so) : "memory");
 }
 
-// Per-thread register image of one operand's stage.
-struct Regs {
-  uint4 v[8];
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)p);
+}
+
+// LDS layouts of one operand stage (16 KiB).
+//  K-major ("KM": rows are M or N, 32 contiguous k per row = 64 B = 4 chunks):
+//    byte = row*64 + ((chunk ^ ((row >> 1) & 3)) << 4)
+//  MN-major ("MN": rows are k, two panels of 128 contiguous columns):
+//    byte = panel*8192 + k*256 + ((chunk ^ (2*(k & 3))) << 4) + 2*(col & 7)
+// Both swizzles keep the fragment reads free of LDS bank conflicts.
+__device__ __forceinline__ int km_off(int row, int chunk) {
+  return row * 64 + ((chunk ^ ((row >> 1) & 3)) << 4);
+}
+__device__ __forceinline__ int mn_off(int k, int col) {
+  const int panel = col >> 7, cc = col & 127;
+  return panel * 8192 + k * 256 + ((((cc >> 3) ^ (2 * (k & 3)))) << 4) + 2 * (cc & 7);
+}
+
+// Per-wave DMA plan of one operand for one tile.
+struct Plan {
+  i32x4_t rs0, rs1;   // resources (rs1: second source: SPLIT_K, or MN panel of waves 2-3)
+  uint32_t voff[4];   // per-lane byte offsets of the wave's four 1 KiB blocks
+  uint32_t lds[4];    // LDS offsets of those blocks inside the operand stage
+  uint32_t kstep;     // bytes the source advances per stage (BK elements along K)
+  int split_stage;    // SPLIT_K: first stage read from rs1 (else a large value)
 };
 
-// ---- operand A ----
-// K-contiguous A (RAG_M): rows are global rows t.row0 + r (clamped into the group).
+// K-major operand: rows r of the tile are rows of a matrix with ld elements,
+// starting at `base`; `bytes` are readable from base.
+__device__ __forceinline__ void plan_km(Plan& P, const void* base, long long bytes, const void* base1,
+                                        long long bytes1, int split_stage, long ld, int wave,
+                                        int lane) {
+  P.rs0 = make_rsrc(base, bytes);
+  P.rs1 = make_rsrc(base1 ? base1 : base, base1 ? bytes1 : bytes);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int blk = wave * 4 + i;
+    const int row = blk * 16 + (lane >> 2);
+    const int c = (lane & 3) ^ ((row >> 1) & 3);
+    P.voff[i] = (uint32_t)(row * ld * 2 + c * 16);
+    P.lds[i] = blk * 1024;
+  }
+  P.kstep = BK * 2;
+  P.split_stage = split_stage;
+}
+
+// MN-major operand: k-rows of a matrix with ld elements; panel p of the tile
+// starts at base_p (its column 0 at k = 0); bytes_p readable from base_p.
+__device__ __forceinline__ void plan_mn(Plan& P, const void* base0, long long bytes0,
+                                        const void* base1, long long bytes1, long ld, int wave,
+                                        int lane) {
+  P.rs0 = make_rsrc(base0, bytes0);
+  P.rs1 = make_rsrc(base1, bytes1);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int blk = wave * 4 + i;   // blocks 0-7: panel 0, 8-15: panel 1
+    const int rb = blk & 7;
+    const int k = rb * 4 + (lane >> 4);
+    const int c = (lane & 15) ^ (2 * (k & 3));
+    P.voff[i] = (uint32_t)(k * ld * 2 + c * 16);
+    P.lds[i] = (blk >> 3) * 8192 + rb * 1024;
+  }
+  P.kstep = (uint32_t)(BK * ld * 2);
+  P.split_stage = 1 << 30;
+}
+
+// Issue the wave's four DMA blocks of one operand for stage kt into the LDS
+// operand region at lds_base.
+template <bool MN>
+__device__ __forceinline__ void issue(const Plan& P, int kt, uint32_t lds_base, int wave) {
+  i32x4_t rs;
+  uint32_t soff;
+  if constexpr (MN) {
+    rs = (wave >= 2) ? P.rs1 : P.rs0;
+    soff = (uint32_t)kt * P.kstep;
+  } else {
+    const bool second = kt >= P.split_stage;
+    rs = second ? P.rs1 : P.rs0;
+    soff = (uint32_t)(second ? kt - P.split_stage : kt) * P.kstep;
+  }
+  soff = __builtin_amdgcn_readfirstlane(soff);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dma16(rs, lds_base + P.lds[i], P.voff[i], soff);
+}
+
+// MFMA fragment (8 consecutive k of one row/column) from an operand stage.
+// row: M or N index inside the tile; s: k16 step inside the stage.
+template <bool MN>
+__device__ __forceinline__ bf16x8_t frag(const char* op, int rowblk, int s, int lane) {
+  if constexpr (!MN) {
+    const int row = rowblk + (lane & 31);
+    return *reinterpret_cast<const bf16x8_t*>(op + km_off(row, 2 * s + (lane >> 5)));
+  } else {
+    // ds_read_b64_tr_b16: within each 16-lane group the lanes' 8-byte reads
+    // (4 k-rows x 4 column quads) come back transposed, so lane i of the
+    // group receives column i at 4 consecutive k.
+    const int g = lane >> 4, r = lane & 15;
+    const int k = 16 * s + 8 * (g >> 1) + (r >> 2);
+    const int col = rowblk + 16 * (g & 1) + 4 * (r & 3);
+    const char* p = op + mn_off(k, col);
+    i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p));
+    i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p + 4 * 256));
+    typedef __attribute__((ext_vector_type(8))) short i16x8_t;
+    i16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8_t, v);
+  }
+}
+
+// Operand plans of one tile for each GEMM kind.
 template <int KIND>
-__device__ __forceinline__ void load_a(const GemmArgs& g, const Tile& t, int k0, Regs& R) {
-  const int tid = threadIdx.x;
+__device__ __forceinline__ void plan_tile(const GemmArgs& g, const Tile& t, int wave, int lane,
+                                          Plan& pa, Plan& pb) {
   const bf16_t* A = static_cast<const bf16_t*>(g.a);
-  if constexpr (KT<KIND>::AK) {
-    const int c = tid & 7;
-    const int k = k0 + c * 8;
-    const bool kv = k < t.klen;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      int r = (tid >> 3) + 32 * i;
-      r = min(r, t.mlim - 1);
-      const bf16_t* p = A + ((long)t.row0 + r) * g.lda + k;
-      R.v[i] = kv ? *reinterpret_cast<const uint4*>(p) : make_uint4(0, 0, 0, 0);
-    }
-  } else {
-    // A[krow][m], M contiguous: 8 k-rows x 8 m per thread
-    const int kb = tid >> 5, mb = tid & 31;
-    const int m = t.m0 + mb * 8;
-    const bool mv = m < g.M;
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      int k = k0 + kb * 8 + r;
-      bool v = mv && k < t.klen;
-      long row = (long)t.row0 + k;
-      if (v && g.a_gather) row = g.a_gather[row];
-      const bf16_t* p = A + row * g.lda + m;
-      R.v[r] = v ? *reinterpret_cast<const uint4*>(p) : make_uint4(0, 0, 0, 0);
-    }
-  }
-}
-
-template <int KIND>
-__device__ __forceinline__ void store_a(char* lds, const Regs& R) {
-  const int tid = threadIdx.x;
-  if constexpr (KT<KIND>::AK) {
-    const int c = tid & 7;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      int r = (tid >> 3) + 32 * i;
-      *reinterpret_cast<uint4*>(lds + lds_off(r, c)) = R.v[i];
-    }
-  } else {
-    const int kb = tid >> 5, mb = tid & 31;
-    uint4 col[8];
-    transpose8x8(R.v, col);
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      *reinterpret_cast<uint4*>(lds + lds_off(mb * 8 + i, kb)) = col[i];
-  }
-}
-
-// ---- operand B ----
-template <int KIND>
-__device__ __forceinline__ void load_b(const GemmArgs& g, const Tile& t, int k0, Regs& R) {
-  const int tid = threadIdx.x;
+  const bf16_t* B0 = static_cast<const bf16_t*>(g.b0);
+  const bf16_t* B1 = static_cast<const bf16_t*>(g.b1);
   constexpr int BSP = KT<KIND>::BSP;
-  if constexpr (KT<KIND>::BK_) {
-    // B[n][k] (K contiguous), per-group matrix
-    const int c = tid & 7;
-    int kk = k0;
-    const bf16_t* base;
-    if constexpr (BSP == BS_SPLIT_K) {
-      bool second = k0 >= g.b_split;
-      base = static_cast<const bf16_t*>(second ? g.b1 : g.b0);
-      kk = second ? k0 - g.b_split : k0;
-    } else {
-      base = static_cast<const bf16_t*>(g.b0);
-    }
-    base += (long)t.e * g.b_es;
-    const int k = kk + c * 8;
-    const bool kv = (k0 + c * 8) < t.klen;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      int n = min(t.n0 + (tid >> 3) + 32 * i, g.N - 1);
-      const bf16_t* p = base + (long)n * g.ldb + k;
-      R.v[i] = kv ? *reinterpret_cast<const uint4*>(p) : make_uint4(0, 0, 0, 0);
-    }
+  // ---- A ----
+  if constexpr (KT<KIND>::AK) {
+    // rows t.row0.. of A (global rows), K contiguous
+    const bf16_t* base = A + (long)t.row0 * g.lda;
+    const long long bytes = ((long long)g.rows_total - t.row0) * g.lda * 2;
+    plan_km(pa, base, bytes, nullptr, 0, 1 << 30, g.lda, wave, lane);
   } else {
-    // B[k][n] (N contiguous): 8 k-rows x 8 n per thread
-    const int kb = tid >> 5, nb = tid & 31;
-    const bf16_t* base;
-    int n;
-    if constexpr (BSP == BS_DUAL_N) {
-      const int c = nb * 8, blk = c >> 6;
-      base = static_cast<const bf16_t*>((blk & 1) ? g.b1 : g.b0);
-      n = t.n0 + (blk >> 1) * 64 + (c & 63);
-    } else {
-      base = static_cast<const bf16_t*>(g.b0);
-      n = t.n0 + nb * 8;
-    }
-    const bool nv = n < g.N;
-    if (g.ragged == RAG_M) base += (long)t.e * g.b_es;
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      int k = k0 + kb * 8 + r;
-      bool v = nv && k < t.klen;
-      long row = (g.ragged == RAG_M) ? (long)k : (long)t.row0 + k;
-      const bf16_t* p = base + row * g.ldb + n;
-      R.v[r] = v ? *reinterpret_cast<const uint4*>(p) : make_uint4(0, 0, 0, 0);
-    }
+    // k-rows t.row0 .. t.row0 + klen of A, M contiguous; columns t.m0 + 128 p
+    const bf16_t* b0 = A + (long)t.row0 * g.lda + t.m0;
+    const long long avail = (long long)t.klen * g.lda * 2;
+    plan_mn(pa, b0, avail - 2LL * t.m0, b0 + 128, avail - 2LL * (t.m0 + 128), g.lda, wave, lane);
   }
-}
-
-template <int KIND>
-__device__ __forceinline__ void store_b(char* lds, const Regs& R) {
-  const int tid = threadIdx.x;
+  // ---- B ----
   if constexpr (KT<KIND>::BK_) {
-    const int c = tid & 7;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      int r = (tid >> 3) + 32 * i;
-      *reinterpret_cast<uint4*>(lds + lds_off(r, c)) = R.v[i];
+    // B[n][k] per group, rows t.n0..
+    const long e_off = (long)t.e * g.b_es + (long)t.n0 * g.ldb;
+    const long long bytes = ((long long)g.N - t.n0) * g.ldb * 2;
+    if constexpr (BSP == BS_SPLIT_K)
+      plan_km(pb, B0 + e_off, bytes, B1 + e_off, bytes, g.b_split / BK, g.ldb, wave, lane);
+    else
+      plan_km(pb, B0 + e_off, bytes, nullptr, 0, 1 << 30, g.ldb, wave, lane);
+  } else if (g.ragged == RAG_M) {
+    // B[k][n] per group (weights), N contiguous
+    const bf16_t* w0 = B0 + (long)t.e * g.b_es;
+    const long long total = (long long)g.K * g.ldb * 2;
+    if constexpr (BSP == BS_DUAL_N) {
+      const bf16_t* w1 = B1 + (long)t.e * g.b_es;
+      plan_mn(pb, w0 + t.n0, total - 2LL * t.n0, w1 + t.n0, total - 2LL * t.n0, g.ldb, wave, lane);
+    } else {
+      plan_mn(pb, w0 + t.n0, total - 2LL * t.n0, w0 + t.n0 + 128, total - 2LL * (t.n0 + 128),
+              g.ldb, wave, lane);
     }
   } else {
-    const int kb = tid >> 5, nb = tid & 31;
-    uint4 col[8];
-    transpose8x8(R.v, col);
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      *reinterpret_cast<uint4*>(lds + lds_off(nb * 8 + i, kb)) = col[i];
+    // B[krow][n] with global k-rows t.row0 .. t.row0 + klen
+    const bf16_t* b0 = B0 + (long)t.row0 * g.ldb + t.n0;
+    const long long avail = (long long)t.klen * g.ldb * 2;
+    plan_mn(pb, b0, avail - 2LL * t.n0, b0 + 128, avail - 2LL * (t.n0 + 128), g.ldb, wave, lane);
   }
 }
 
 template <int KIND>
 __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem[NST * STAGE];
   __shared__ Sched sch;
-  constexpr int BNT = (KT<KIND>::BSP == BS_DUAL_N) ? BN / 2 : BN;
+  constexpr bool DUAL = KT<KIND>::BSP == BS_DUAL_N;
+  constexpr bool AMN = !KT<KIND>::AK, BMN = !KT<KIND>::BK_;
+  constexpr int BNT = DUAL ? BN / 2 : BN;
   const int ntiles = sched_setup<BM, BNT>(g, sch);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform in the wave
   const int wm = wave >> 1, wn = wave & 1;
+  const uint32_t lds0 = lds_u32(smem);
 
   for (int it = 0;; ++it) {
     const int L = logical_tile(it);
     if (L >= ntiles) break;
     const Tile t = sched_decode<BM, BNT>(g, sch, L);
+    Plan pa, pb;
+    plan_tile<KIND>(g, t, wave, lane, pa, pb);
 
     f32x16_t acc[4][4];
 #pragma unroll
@@ -453,49 +506,47 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(GemmArgs g) {
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
     const int nk = (t.klen + BK - 1) / BK;
-    Regs ra, rb;
-    if (nk > 0) {
-      load_a<KIND>(g, t, 0, ra);
-      load_b<KIND>(g, t, 0, rb);
-      store_a<KIND>(smem, ra);
-      store_b<KIND>(smem + BM * ROWB, rb);
-    }
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      char* cur = smem + (kt & 1) * STAGE;
-      char* nxt = smem + ((kt + 1) & 1) * STAGE;
-      const bool more = kt + 1 < nk;
-      if (more) {
-        load_a<KIND>(g, t, (kt + 1) * BK, ra);
-        load_b<KIND>(g, t, (kt + 1) * BK, rb);
+#pragma unroll
+    for (int s = 0; s < NST - 1; ++s)
+      if (s < nk) {
+        issue<AMN>(pa, s, lds0 + s * STAGE, wave);
+        issue<BMN>(pb, s, lds0 + s * STAGE + OPB, wave);
       }
-      const char* As = cur;
-      const char* Bs = cur + BM * ROWB;
+    for (int kt = 0; kt < nk; ++kt) {
+      const int after = nk - 1 - kt;  // stages issued after kt (at most NST - 2)
+      if (after >= 2) wait_vmcnt<2 * DMA_PER_STAGE>();
+      else if (after == 1) wait_vmcnt<DMA_PER_STAGE>();
+      else wait_vmcnt<0>();
+      barrier();
+      if (kt + NST - 1 < nk) {
+        const uint32_t nb = lds0 + ((kt + NST - 1) & (NST - 1)) * STAGE;
+        issue<AMN>(pa, kt + NST - 1, nb, wave);
+        issue<BMN>(pb, kt + NST - 1, nb + OPB, wave);
+      }
+      const char* As = smem + (kt & (NST - 1)) * STAGE;
+      const char* Bs = As + OPB;
 #pragma unroll
       for (int s = 0; s < BK / 16; ++s) {
-        const int chunk = 2 * s + (lane >> 5);
         bf16x8_t af[4], bfr[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          af[i] = *reinterpret_cast<const bf16x8_t*>(As + lds_off(wm * 128 + i * 32 + (lane & 31), chunk));
+        for (int i = 0; i < 4; ++i) af[i] = frag<AMN>(As, wm * 128 + i * 32, s, lane);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          bfr[j] = *reinterpret_cast<const bf16x8_t*>(Bs + lds_off(wn * 128 + j * 32 + (lane & 31), chunk));
+        for (int j = 0; j < 4; ++j) {
+          const int col = DUAL ? ((j >> 1) * 128 + wn * 64 + (j & 1) * 32) : (wn * 128 + j * 32);
+          bfr[j] = frag<BMN>(Bs, col, s, lane);
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int j = 0; j < 4; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
       }
-      if (more) {
-        store_a<KIND>(nxt, ra);
-        store_b<KIND>(nxt + BM * ROWB, rb);
-      }
-      __syncthreads();
     }
+    // every wave is done reading the ring before the next tile refills it
+    barrier();
 
     // Epilogue.  Lane holds C[m][n..n+3] with m = wm*128 + i*32 + lane%32 and
-    // n = wn*128 + j*32 + 8*grp + 4*(lane/32) for register group grp.
+    // n = (column block of j) + 8*grp + 4*(lane/32) for register group grp.
     constexpr int EPI = KT<KIND>::EPI;
     const int nq = 4 * (lane >> 5);
 #pragma unroll
@@ -515,7 +566,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(GemmArgs g) {
               v[q] = acc[i][j][4 * grp + q];
               u[q] = acc[i][j + 2][4 * grp + q];
             }
-            epilogue4<EPI, bf16_t>(g, t, m, n, v, u);
+            epilogue4<EPI, bf16_t, false>(g, t, m, n, v, u);
           }
       } else {
 #pragma unroll
@@ -527,7 +578,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(GemmArgs g) {
             float v[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) v[q] = acc[i][j][4 * grp + q];
-            epilogue4<EPI, bf16_t>(g, t, m, n, v, v);
+            epilogue4<EPI, bf16_t, false>(g, t, m, n, v, v);
           }
       }
     }

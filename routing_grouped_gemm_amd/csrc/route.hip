@@ -8,8 +8,8 @@
 //
 // Metadata and dispatch (olmoforge README: row-wise expert parallel writes
 // every token row straight into its expert's input buffer; the routing table
-// stays on the GPU): a per-64-token histogram, one scan workgroup that turns
-// the histograms into counts, offsets and per-block bases, a rank kernel that
+// stays on the GPU): a per-64-token histogram, one scan workgroup per expert
+// that turns the histograms into counts and per-block bases, a rank kernel that
 // gives every (token, slot) its row (stable: ascending token order inside an
 // expert, by ballot masks and popcount, no atomics on the result), and a copy
 // kernel that writes each row of Xs from its source token with 16-byte loads
@@ -303,11 +303,12 @@ __global__ __launch_bounds__(256) void gather_sum_kernel(const TS* __restrict__ 
 }
 
 // Router backward, softmax part: dl = p * (dp - <p, dp>), one wave per token.
-// Also writes dl rounded to bf16 when dl16 is given (GEMM operand).
+// Also writes dl rounded to bf16 when dl16 is given (GEMM operand), as rows
+// of ld16 >= E entries whose tail is zero.
 __global__ __launch_bounds__(256) void router_bwd_softmax_kernel(
     const float* __restrict__ logits, const int32_t* __restrict__ idx,
     const float* __restrict__ dw, int T, int E, int k, float* __restrict__ dl,
-    bf16_t* __restrict__ dl16) {
+    bf16_t* __restrict__ dl16, int ld16) {
   const int lane = threadIdx.x & 63;
   const long t = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
@@ -353,7 +354,9 @@ __global__ __launch_bounds__(256) void router_bwd_softmax_kernel(
     if (e < E) {
       float g = v[q] * (dp[q] - inner);
       dl[t * E + e] = g;
-      if (dl16) dl16[t * E + e] = f32_to_bf16(g);
+      if (dl16) dl16[t * ld16 + e] = f32_to_bf16(g);
+    } else if (dl16 && e < ld16) {
+      dl16[t * ld16 + e] = 0;
     }
   }
 }
@@ -452,10 +455,10 @@ hipError_t launch_gather_sum(int dtype, const void* dXs, const int32_t* dest, in
 }
 
 hipError_t launch_router_bwd_softmax(const float* logits, const int32_t* idx, const float* dw,
-                                     int T, int E, int k, float* dl, bf16_t* dl16,
+                                     int T, int E, int k, float* dl, bf16_t* dl16, int ld16,
                                      hipStream_t s) {
   hipLaunchKernelGGL(router_bwd_softmax_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, idx,
-                     dw, T, E, k, dl, dl16);
+                     dw, T, E, k, dl, dl16, ld16);
   note_launch("router_bwd_softmax", s);
   return hipGetLastError();
 }
