@@ -428,6 +428,40 @@ __device__ __forceinline__ bf16x8_t frag(const char* op, int rowblk, int s, int 
   }
 }
 
+// Fragments of one k16 step of stage kt: 4 A fragments (rows wm*128 + 32i)
+// and 4 B fragments (columns of wave column wn; gate/up pairs when DUAL).
+template <bool AMN, bool BMN, bool DUAL>
+__device__ __forceinline__ void load_frags(const char* smem, int kt, int s, int wm, int wn,
+                                           int lane, bf16x8_t (&fa)[4], bf16x8_t (&fb)[4]) {
+  const char* As = smem + (kt & (NST - 1)) * STAGE;
+  const char* Bs = As + OPB;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) fa[i] = frag<AMN>(As, wm * 128 + i * 32, s, lane);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int col = DUAL ? ((j >> 1) * 128 + wn * 64 + (j & 1) * 32) : (wn * 128 + j * 32);
+    fb[j] = frag<BMN>(Bs, col, s, lane);
+  }
+}
+
+__device__ __forceinline__ void mfma16(f32x16_t (&acc)[4][4], const bf16x8_t (&fa)[4],
+                                       const bf16x8_t (&fb)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+}
+
+// Wait until stage st has landed, given that stages up to last_issued are in flight.
+__device__ __forceinline__ void wait_stage(int st, int last_issued) {
+  const int after = last_issued - st;
+  if (after >= 3) wait_vmcnt<3 * DMA_PER_STAGE>();
+  else if (after == 2) wait_vmcnt<2 * DMA_PER_STAGE>();
+  else if (after == 1) wait_vmcnt<DMA_PER_STAGE>();
+  else wait_vmcnt<0>();
+}
+
 // Operand plans of one tile for each GEMM kind.
 template <int KIND>
 __device__ __forceinline__ void plan_tile(const GemmArgs& g, const Tile& t, int wave, int lane,
@@ -476,6 +510,123 @@ __device__ __forceinline__ void plan_tile(const GemmArgs& g, const Tile& t, int 
   }
 }
 
+// Float32 staging slice of one wave: 64 rows x 128 columns, 16-byte chunks
+// XOR-swizzled by row so that both the accumulator writes (32 rows, one
+// chunk) and the row reads (one row, 16 chunks) avoid bank conflicts.
+__device__ __forceinline__ int stage_off(int r, int chunk) { return r * 512 + ((chunk ^ (r & 31)) << 4); }
+
+// Epilogue of one 8-column piece: v = tile values (gate for the SwiGLU
+// forward), u = up values (SwiGLU forward only).  grow: global row (RAG_M)
+// or row inside the group's C (RAG_K); n: output column.
+template <int EPI>
+__device__ __forceinline__ void epi8(const GemmArgs& g, const Tile& t, long row, int n,
+                                     const float (&v)[8], const float (&u)[8]) {
+  if constexpr (EPI == EPI_STORE_F32) {
+    float* p = static_cast<float*>(g.c0) + row * g.ldc + n;
+    store8(p, v);
+  } else if constexpr (EPI == EPI_STORE || EPI == EPI_WGRAD_SPLIT) {
+    bf16_t* p;
+    if constexpr (EPI == EPI_WGRAD_SPLIT) {
+      if (n < g.c_split)
+        p = static_cast<bf16_t*>(g.c0) + (long)t.e * g.c_es + row * g.ldc + n;
+      else
+        p = static_cast<bf16_t*>(g.c1) + (long)t.e * g.c_es + row * g.ldc + (n - g.c_split);
+    } else {
+      p = static_cast<bf16_t*>(g.c0) + (g.ragged == RAG_M ? 0 : (long)t.e * g.c_es) + row * g.ldc + n;
+    }
+    if (g.accumulate) {
+      float o[8], w[8];
+      load8(p, o);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) w[q] = v[q] + o[q];
+      store8(p, w);
+    } else {
+      store8(p, v);
+    }
+  } else if constexpr (EPI == EPI_SWIGLU_FWD) {
+    const long off = row * g.ldc + n;
+    float a[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) a[q] = silu_f(v[q]) * u[q];
+    store8(static_cast<bf16_t*>(g.c0) + off, v);
+    store8(static_cast<bf16_t*>(g.c1) + off, u);
+    store8(static_cast<bf16_t*>(g.c2) + off, a);
+  } else if constexpr (EPI == EPI_SWIGLU_BWD) {
+    float hg[8], hu[8], dg[8], du[8];
+    load8(static_cast<const bf16_t*>(g.h0) + row * g.ldh + n, hg);
+    load8(static_cast<const bf16_t*>(g.h1) + row * g.ldh + n, hu);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const float sg = 1.0f / (1.0f + __expf(-hg[q]));
+      du[q] = v[q] * hg[q] * sg;
+      dg[q] = v[q] * hu[q] * sg * (1.0f + hg[q] * (1.0f - sg));
+    }
+    bf16_t* p = static_cast<bf16_t*>(g.c0) + row * g.ldc + n;
+    store8(p, dg);
+    store8(p + g.c_split, du);
+  }
+}
+
+template <int KIND>
+__device__ __forceinline__ void epilogue_lds(const GemmArgs& g, const Tile& t, char* slice,
+                                             f32x16_t (&acc)[4][4], int wm, int wn, int lane) {
+  constexpr int EPI = KT<KIND>::EPI;
+  constexpr bool DUAL = KT<KIND>::BSP == BS_DUAL_N;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    // accumulators of row blocks i = 2h, 2h+1 into the slice
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int grp = 0; grp < 4; ++grp) {
+          const int r = ii * 32 + (lane & 31);
+          const int chunk = j * 8 + 2 * grp + (lane >> 5);
+          f32x4_t v = {acc[2 * h + ii][j][4 * grp], acc[2 * h + ii][j][4 * grp + 1],
+                       acc[2 * h + ii][j][4 * grp + 2], acc[2 * h + ii][j][4 * grp + 3]};
+          *reinterpret_cast<f32x4_t*>(slice + stage_off(r, chunk)) = v;
+        }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    // rows of this half: tile rows wm*128 + h*64 + r
+    if constexpr (DUAL) {
+      // slice columns 0..63: gate, 64..127: up, for f columns n0 + wn*64 + c
+#pragma unroll 2
+      for (int it = 0; it < 8; ++it) {
+        const int r = it * 8 + (lane >> 3);
+        const int c = (lane & 7) * 8;
+        const int m = wm * 128 + h * 64 + r;
+        float v[8], u[8];
+        const f32x4_t* p0 = reinterpret_cast<const f32x4_t*>(slice + stage_off(r, c >> 2));
+        const f32x4_t* p1 = reinterpret_cast<const f32x4_t*>(slice + stage_off(r, (c >> 2) + 1));
+        const f32x4_t* q0 = reinterpret_cast<const f32x4_t*>(slice + stage_off(r, (c >> 2) + 16));
+        const f32x4_t* q1 = reinterpret_cast<const f32x4_t*>(slice + stage_off(r, (c >> 2) + 17));
+        f32x4_t a0 = *p0, a1 = *p1, b0 = *q0, b1 = *q1;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) { v[q] = a0[q]; v[q + 4] = a1[q]; u[q] = b0[q]; u[q + 4] = b1[q]; }
+        const int n = t.n0 + wn * 64 + c;
+        if (m < t.mlim && n < g.N) epi8<EPI>(g, t, (long)t.row0 + m, n, v, u);
+      }
+    } else {
+#pragma unroll 2
+      for (int it = 0; it < 16; ++it) {
+        const int r = it * 4 + (lane >> 4);
+        const int c = (lane & 15) * 8;
+        const int m = wm * 128 + h * 64 + r;
+        float v[8];
+        const f32x4_t a0 = *reinterpret_cast<const f32x4_t*>(slice + stage_off(r, c >> 2));
+        const f32x4_t a1 = *reinterpret_cast<const f32x4_t*>(slice + stage_off(r, (c >> 2) + 1));
+#pragma unroll
+        for (int q = 0; q < 4; ++q) { v[q] = a0[q]; v[q + 4] = a1[q]; }
+        const int n = t.n0 + wn * 128 + c;
+        const long row = (g.ragged == RAG_M) ? (long)t.row0 + m : (long)t.m0 + m;
+        if (m < t.mlim && n < g.N) epi8<EPI>(g, t, row, n, v, v);
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  }
+}
+
 template <int KIND>
 __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) char smem[NST * STAGE];
@@ -501,87 +652,53 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+      for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
 
+    // Ring of NST = 4 buffers, prefetch distance 4.  Stage kt's two k16 steps
+    // use fragment sets F0 (step 0) and F1 (step 1).  F1 is read while the
+    // MFMAs of F0 run; then every wave has finished reading stage kt, and one
+    // barrier both publishes stage kt+1 (each wave waited for its own DMA) and
+    // frees stage kt's buffer for stage kt+4.  The MFMAs of F1 then run while
+    // F0 of stage kt+1 is read.
     const int nk = (t.klen + BK - 1) / BK;
 #pragma unroll
-    for (int s = 0; s < NST - 1; ++s)
+    for (int s = 0; s < NST; ++s)
       if (s < nk) {
         issue<AMN>(pa, s, lds0 + s * STAGE, wave);
         issue<BMN>(pb, s, lds0 + s * STAGE + OPB, wave);
       }
-    for (int kt = 0; kt < nk; ++kt) {
-      const int after = nk - 1 - kt;  // stages issued after kt (at most NST - 2)
-      if (after >= 2) wait_vmcnt<2 * DMA_PER_STAGE>();
-      else if (after == 1) wait_vmcnt<DMA_PER_STAGE>();
-      else wait_vmcnt<0>();
+    bf16x8_t fa0[4], fb0[4], fa1[4], fb1[4];
+    if (nk > 0) {
+      wait_stage(0, min(nk - 1, NST - 1));
       barrier();
-      if (kt + NST - 1 < nk) {
-        const uint32_t nb = lds0 + ((kt + NST - 1) & (NST - 1)) * STAGE;
-        issue<AMN>(pa, kt + NST - 1, nb, wave);
-        issue<BMN>(pb, kt + NST - 1, nb + OPB, wave);
+      load_frags<AMN, BMN, DUAL>(smem, 0, 0, wm, wn, lane, fa0, fb0);
+    }
+    for (int kt = 0; kt < nk; ++kt) {
+      load_frags<AMN, BMN, DUAL>(smem, kt, 1, wm, wn, lane, fa1, fb1);
+      mfma16(acc, fa0, fb0);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      const bool more = kt + 1 < nk;
+      if (more) wait_stage(kt + 1, min(nk - 1, kt + NST - 1));
+      barrier();
+      if (kt + NST < nk) {
+        const uint32_t nb = lds0 + (kt & (NST - 1)) * STAGE;
+        issue<AMN>(pa, kt + NST, nb, wave);
+        issue<BMN>(pb, kt + NST, nb + OPB, wave);
       }
-      const char* As = smem + (kt & (NST - 1)) * STAGE;
-      const char* Bs = As + OPB;
-#pragma unroll
-      for (int s = 0; s < BK / 16; ++s) {
-        bf16x8_t af[4], bfr[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) af[i] = frag<AMN>(As, wm * 128 + i * 32, s, lane);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int col = DUAL ? ((j >> 1) * 128 + wn * 64 + (j & 1) * 32) : (wn * 128 + j * 32);
-          bfr[j] = frag<BMN>(Bs, col, s, lane);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
-      }
+      if (more) load_frags<AMN, BMN, DUAL>(smem, kt + 1, 0, wm, wn, lane, fa0, fb0);
+      mfma16(acc, fa1, fb1);
     }
     // every wave is done reading the ring before the next tile refills it
     barrier();
 
-    // Epilogue.  Lane holds C[m][n..n+3] with m = wm*128 + i*32 + lane%32 and
-    // n = (column block of j) + 8*grp + 4*(lane/32) for register group grp.
-    constexpr int EPI = KT<KIND>::EPI;
-    const int nq = 4 * (lane >> 5);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = wm * 128 + i * 32 + (lane & 31);
-      if (m >= t.mlim) continue;
-      if constexpr (EPI == EPI_SWIGLU_FWD) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int grp = 0; grp < 4; ++grp) {
-            const int n = t.n0 + wn * 64 + j * 32 + 8 * grp + nq;
-            if (n >= g.N) continue;
-            float v[4], u[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              v[q] = acc[i][j][4 * grp + q];
-              u[q] = acc[i][j + 2][4 * grp + q];
-            }
-            epilogue4<EPI, bf16_t, false>(g, t, m, n, v, u);
-          }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int grp = 0; grp < 4; ++grp) {
-            const int n = t.n0 + wn * 128 + j * 32 + 8 * grp + nq;
-            if (n >= g.N) continue;
-            float v[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) v[q] = acc[i][j][4 * grp + q];
-            epilogue4<EPI, bf16_t, false>(g, t, m, n, v, v);
-          }
-      }
-    }
+    // Epilogue through LDS.  The ring is idle now: each wave takes a private
+    // 32 KiB slice and, for each half of its 128 rows, writes its float32
+    // accumulators there straight from the accumulator registers, then reads
+    // back 8 consecutive columns of a row per lane and applies the epilogue
+    // with 16-byte global accesses.
+    epilogue_lds<KIND>(g, t, smem + wave * 32768, acc, wm, wn, lane);
+    // the slices are ring buffers of the next tile
+    barrier();
   }
 }
 
