@@ -85,7 +85,21 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-tokens", type=int, default=1024,
                     help="tokens of the CPU-oracle sample (0 = skip the CPU baseline)")
     ap.add_argument("--kernels", action="store_true", help="per-kernel table on stderr")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB three times (the "
+                         "known-size reference for HBM byte counters) and exit")
     args = ap.parse_args(argv)
+
+    if args.calibrate_copy:
+        import torch
+        n = args.calibrate_copy << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "launches": 3}))
+        return 0
 
     if args.gpus != 1:
         print(f"bench.py: this layer runs on one GPU; --gpus {args.gpus} is not supported "

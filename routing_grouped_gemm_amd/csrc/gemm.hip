@@ -324,18 +324,24 @@ __device__ __forceinline__ uint32_t lds_u32(const void* p) {
   return (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)p);
 }
 
-// LDS layouts of one operand stage (16 KiB).
+// LDS layouts of one operand stage (16 KiB), in 16-byte chunks.
 //  K-major ("KM": rows are M or N, 32 contiguous k per row = 64 B = 4 chunks):
-//    byte = row*64 + ((chunk ^ ((row >> 1) & 3)) << 4)
+//    byte = row*64 + ((chunk ^ km_swz(row)) << 4)
 //  MN-major ("MN": rows are k, two panels of 128 contiguous columns):
-//    byte = panel*8192 + k*256 + ((chunk ^ (2*(k & 3))) << 4) + 2*(col & 7)
-// Both swizzles keep the fragment reads free of LDS bank conflicts.
+//    byte = panel*8192 + k*256 + (((col/8) ^ mn_swz(k)) << 4) + 2*(col & 7)
+// The swizzles make every fragment read conflict-free whether the LDS serves
+// 128 or 256 bytes per clock: a ds_read_b128 fragment touches 16 consecutive
+// rows at one chunk (km_swz gives each residue of row mod 4 all four
+// chunks), a ds_read_b64_tr_b16 pair touches 4 k-rows x 4 chunks (mn_swz
+// spreads them over 16 distinct chunk slots, and over 8 for any 16 lanes).
+__device__ __forceinline__ int km_swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+__device__ __forceinline__ int mn_swz(int k) { return (4 * (k & 3)) ^ (2 * ((k >> 1) & 1)); }
 __device__ __forceinline__ int km_off(int row, int chunk) {
-  return row * 64 + ((chunk ^ ((row >> 1) & 3)) << 4);
+  return row * 64 + ((chunk ^ km_swz(row)) << 4);
 }
 __device__ __forceinline__ int mn_off(int k, int col) {
   const int panel = col >> 7, cc = col & 127;
-  return panel * 8192 + k * 256 + ((((cc >> 3) ^ (2 * (k & 3)))) << 4) + 2 * (cc & 7);
+  return panel * 8192 + k * 256 + (((cc >> 3) ^ mn_swz(k)) << 4) + 2 * (cc & 7);
 }
 
 // Per-wave DMA plan of one operand for one tile.
@@ -358,7 +364,7 @@ __device__ __forceinline__ void plan_km(Plan& P, const void* base, long long byt
   for (int i = 0; i < 4; ++i) {
     const int blk = wave * 4 + i;
     const int row = blk * 16 + (lane >> 2);
-    const int c = (lane & 3) ^ ((row >> 1) & 3);
+    const int c = (lane & 3) ^ km_swz(row);
     P.voff[i] = (uint32_t)(row * ld * 2 + c * 16);
     P.lds[i] = blk * 1024;
   }
@@ -378,7 +384,7 @@ __device__ __forceinline__ void plan_mn(Plan& P, const void* base0, long long by
     const int blk = wave * 4 + i;   // blocks 0-7: panel 0, 8-15: panel 1
     const int rb = blk & 7;
     const int k = rb * 4 + (lane >> 4);
-    const int c = (lane & 15) ^ (2 * (k & 3));
+    const int c = (lane & 15) ^ mn_swz(k);
     P.voff[i] = (uint32_t)(k * ld * 2 + c * 16);
     P.lds[i] = (blk >> 3) * 8192 + rb * 1024;
   }
@@ -451,6 +457,19 @@ __device__ __forceinline__ void mfma16(f32x16_t (&acc)[4][4], const bf16x8_t (&f
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+}
+
+// s_waitcnt with lgkmcnt(0) and the other counters left alone (gfx9 encoding).
+constexpr int kLgkm0 = 0xC07F;
+
+// Ask the scheduler to alternate MFMAs and LDS reads (16 each at most) in the
+// region since the last scheduling barrier.
+__device__ __forceinline__ void interleave_mfma_ds() {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+  }
 }
 
 // Wait until stage st has landed, given that stages up to last_issued are in flight.
@@ -674,9 +693,14 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(GemmArgs g) {
       load_frags<AMN, BMN, DUAL>(smem, 0, 0, wm, wn, lane, fa0, fb0);
     }
     for (int kt = 0; kt < nk; ++kt) {
+      // F0 was read a whole phase ago: this wait is nearly free, and it lets
+      // the compiler issue F0's MFMAs without waiting on the F1 reads that
+      // are interleaved with them (lgkmcnt cannot count all 16 reads of a set).
+      __builtin_amdgcn_s_waitcnt(kLgkm0);
       load_frags<AMN, BMN, DUAL>(smem, kt, 1, wm, wn, lane, fa1, fb1);
       mfma16(acc, fa0, fb0);
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      interleave_mfma_ds();
+      __builtin_amdgcn_s_waitcnt(kLgkm0);
       const bool more = kt + 1 < nk;
       if (more) wait_stage(kt + 1, min(nk - 1, kt + NST - 1));
       barrier();
@@ -687,6 +711,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(GemmArgs g) {
       }
       if (more) load_frags<AMN, BMN, DUAL>(smem, kt + 1, 0, wm, wn, lane, fa0, fb0);
       mfma16(acc, fa1, fb1);
+      interleave_mfma_ds();
     }
     // every wave is done reading the ring before the next tile refills it
     barrier();
