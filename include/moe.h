@@ -107,15 +107,18 @@ int moe_route(const void* x, const void* Wr, int T, int d, int E, int k, int dty
  *   dest_row[T,k] row of (t, j): offsets[e] + number of tokens t' < t routed
  *                 to e (rows of one expert are in ascending token order)
  *   src_token[R]  inverse map: the token of every row
- *   Xs[R,d]       Xs[dest_row[t,j]] = x[t].  prec MXFP8: Xs holds e4m3 codes
- *                 (1 byte each) and Xs_scale[R, d/32] the E8M0 exponent bytes
- *                 (biased by 127) of every 32-element block along d; in other
- *                 precisions Xs has the dtype and Xs_scale is ignored.
+ *   Xs[R,d]       Xs[dest_row[t,j]] = x[t] (dtype).
+ *   Xq, Xq_scale  prec MXFP8 only (ignored, may be NULL, otherwise): the
+ *                 rows of Xs block-quantised along d.  Xq[R,d] holds e4m3
+ *                 codes (1 byte each); Xq_scale holds the E8M0 bytes (2^E
+ *                 stored as E + 127) block-major: the scale of block b
+ *                 (elements 32b..32b+31) of row r is Xq_scale[b*Rp + r],
+ *                 Rp = R rounded up to a multiple of 16, (d/32)*Rp bytes.
  *   Workspace: moe_workspace_size(MOE_OP_DISPATCH, ...).
  */
 int moe_dispatch(const void* x, const int32_t* topk_idx, int T, int d, int E, int k,
                  int dtype, int prec, int32_t* counts, int32_t* offsets,
-                 int32_t* dest_row, int32_t* src_token, void* Xs, uint8_t* Xs_scale,
+                 int32_t* dest_row, int32_t* src_token, void* Xs, void* Xq, uint8_t* Xq_scale,
                  void* ws, size_t ws_bytes, void* stream);
 
 /*
@@ -125,9 +128,11 @@ int moe_dispatch(const void* x, const int32_t* topk_idx, int T, int d, int E, in
  *   Hg = Xs.Wg[e], Hu = Xs.Wu[e], A = silu(Hg) * Hu, Ys = A.Wd[e]
  *   Wg, Wu [E,d,f], Wd [E,f,d] (dtype); Hg, Hu, A [R,f], Ys [R,d] (dtype),
  *   stored from float32 accumulators (A from the unrounded Hg, Hu).
- *   offsets is read on the device.  prec MXFP8: Xs/Xs_scale as written by
- *   moe_dispatch; weights are block-quantised inside (Wg, Wu along d, Wd
- *   along f) and A along f before the down GEMM.
+ *   offsets is read on the device.  Xs_scale is ignored except for prec
+ *   MXFP8, where Xs and Xs_scale are the Xq codes and Xq_scale scales that
+ *   moe_dispatch wrote; the weights are block-quantised inside (Wg, Wu along
+ *   d, Wd along f) and A along f before the down GEMM.  Workspace:
+ *   moe_workspace_size(MOE_OP_FFN_FWD, ...) (0 bytes except for MXFP8).
  */
 int moe_grouped_ffn_fwd(const void* Xs, const uint8_t* Xs_scale, const int32_t* offsets,
                         int T, int k, int d, int f, int E, const void* Wg, const void* Wu,
@@ -163,12 +168,13 @@ int moe_combine_bwd(const void* dY, const void* Ys, const float* topk_w,
  *   dWd[e] = A^T.dYs, dWg[e] = Xs^T.dHg, dWu[e] = Xs^T.dHu, summed in float32
  *   over the expert's rows and stored in dtype (an expert with no rows gets
  *   zeros; with MOE_ACCUMULATE the sum is added to the existing values).
- *   Xs: the dispatched rows (bf16/fp32).  prec MXFP8: the two dgrad GEMMs are
- *   block-quantised (dYs and Wd along d; dH, Wg, Wu along f) and the weight
- *   gradients read the bf16 token rows x[src_token[r]] instead of Xs.
+ *   Xs: the dispatched rows in dtype (also for MXFP8).  prec MXFP8: both
+ *   operands of the two dgrad GEMMs are block-quantised along their
+ *   contraction axis (dYs and Wd along d; dH, Wg, Wu along f); the weight
+ *   gradients take the unquantised operands.  Workspace:
+ *   moe_workspace_size(MOE_OP_FFN_BWD, ...) (0 bytes except for MXFP8).
  */
-int moe_grouped_ffn_bwd(const void* dYs, const void* Xs, const void* x,
-                        const int32_t* src_token, const void* Hg, const void* Hu,
+int moe_grouped_ffn_bwd(const void* dYs, const void* Xs, const void* Hg, const void* Hu,
                         const void* A, const int32_t* offsets, int T, int k, int d, int f,
                         int E, const void* Wg, const void* Wu, const void* Wd, int dtype,
                         int prec, unsigned flags, void* dH, void* dXs, void* dWg, void* dWu,

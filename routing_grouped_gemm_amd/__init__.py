@@ -25,7 +25,7 @@ __all__ = [
     "lib", "moe_route", "moe_dispatch", "moe_grouped_ffn_fwd", "moe_combine",
     "moe_combine_bwd", "moe_grouped_ffn_bwd", "moe_dispatch_bwd", "moe_route_bwd",
     "moe_workspace_size", "moe_status_string", "ExpertLayer", "LIB_PATH",
-    "MOE_ROUTE_LOGITS_IN", "MOE_ACCUMULATE", "KernelTimer", "upload",
+    "MOE_ROUTE_LOGITS_IN", "MOE_ACCUMULATE", "KernelTimer", "upload", "mx_scale_pitch",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_hip.so")
@@ -40,13 +40,13 @@ OPS = {"route": 0, "dispatch": 1, "ffn_fwd": 2, "combine": 3, "combine_bwd": 4,
 _P, _I, _U, _S = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint, ctypes.c_size_t
 _SIGS = {
     "moe_route": [_P, _P, _I, _I, _I, _I, _I, _U, _P, _P, _P, _P, _S, _P],
-    "moe_dispatch": [_P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _S, _P],
+    "moe_dispatch": [_P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _S, _P],
     "moe_grouped_ffn_fwd": [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _I, _I, _P, _P, _P, _P,
                             _P, _S, _P],
     "moe_combine": [_P, _P, _P, _I, _I, _I, _I, _P, _P],
     "moe_combine_bwd": [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _P],
-    "moe_grouped_ffn_bwd": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _I,
-                            _I, _U, _P, _P, _P, _P, _P, _P, _S, _P],
+    "moe_grouped_ffn_bwd": [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _I, _I, _U,
+                            _P, _P, _P, _P, _P, _P, _S, _P],
     "moe_dispatch_bwd": [_P, _P, _I, _I, _I, _I, _U, _P, _P],
     "moe_route_bwd": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _U, _P, _P, _P, _P, _S, _P],
     "moe_workspace_size": [_I, _I, _I, _I, _I, _I, _I, _I, ctypes.POINTER(ctypes.c_size_t)],
@@ -145,14 +145,20 @@ def moe_route(x, Wr, k, logits, topk_idx, topk_w, logits_in=False, stream=None):
                            _ptr(topk_idx), _ptr(topk_w), None, 0, _stream(stream)), "moe_route")
 
 
-def moe_dispatch(x, topk_idx, E, counts, offsets, dest_row, src_token, Xs, Xs_scale, ws,
-                 prec="bf16", stream=None):
+def moe_dispatch(x, topk_idx, E, counts, offsets, dest_row, src_token, Xs, ws, Xq=None,
+                 Xq_scale=None, prec="bf16", stream=None):
     T, d = x.shape
     k = topk_idx.shape[1]
     wp, wb = _ws(ws)
     _check(lib().moe_dispatch(_ptr(x), _ptr(topk_idx), T, d, E, k, _dtype(x), PREC[prec],
                               _ptr(counts), _ptr(offsets), _ptr(dest_row), _ptr(src_token),
-                              _ptr(Xs), _ptr(Xs_scale), wp, wb, _stream(stream)), "moe_dispatch")
+                              _ptr(Xs), _ptr(Xq), _ptr(Xq_scale), wp, wb, _stream(stream)),
+           "moe_dispatch")
+
+
+def mx_scale_pitch(R: int) -> int:
+    """Row pitch of the block-major MXFP8 activation scales: R rounded up to 16."""
+    return (R + 15) // 16 * 16
 
 
 def moe_grouped_ffn_fwd(Xs, Xs_scale, offsets, T, k, Wg, Wu, Wd, Hg, Hu, A, Ys, ws=None,
@@ -180,12 +186,12 @@ def moe_combine_bwd(dY, Ys, topk_w, dest_row, dYs, dtopk_w, stream=None):
            "moe_combine_bwd")
 
 
-def moe_grouped_ffn_bwd(dYs, Xs, x, src_token, Hg, Hu, A, offsets, T, k, Wg, Wu, Wd, dH, dXs,
+def moe_grouped_ffn_bwd(dYs, Xs, Hg, Hu, A, offsets, T, k, Wg, Wu, Wd, dH, dXs,
                         dWg, dWu, dWd, ws=None, prec="bf16", accumulate=False, stream=None):
     E, d, f = Wg.shape
     wp, wb = _ws(ws)
-    _check(lib().moe_grouped_ffn_bwd(_ptr(dYs), _ptr(Xs), _ptr(x), _ptr(src_token), _ptr(Hg),
-                                     _ptr(Hu), _ptr(A), _ptr(offsets), T, k, d, f, E, _ptr(Wg),
+    _check(lib().moe_grouped_ffn_bwd(_ptr(dYs), _ptr(Xs), _ptr(Hg), _ptr(Hu), _ptr(A),
+                                     _ptr(offsets), T, k, d, f, E, _ptr(Wg),
                                      _ptr(Wu), _ptr(Wd), _dtype(Wg), PREC[prec],
                                      MOE_ACCUMULATE if accumulate else 0, _ptr(dH), _ptr(dXs),
                                      _ptr(dWg), _ptr(dWu), _ptr(dWd), wp, wb, _stream(stream)),
@@ -277,12 +283,12 @@ class ExpertLayer:
         self.offsets = z(E + 1, dt=i32)
         self.dest_row = z(T, k, dt=i32)
         self.src_token = z(R, dt=i32)
+        self.Xs = z(R, d)
         if prec == "mxfp8":
-            self.Xs = z(R, d, dt=torch.uint8)
-            self.Xs_scale = z(R, d // 32, dt=torch.uint8)
+            self.Xq = z(R, d, dt=torch.uint8)
+            self.Xq_scale = z(d // 32, mx_scale_pitch(R), dt=torch.uint8)
         else:
-            self.Xs = z(R, d)
-            self.Xs_scale = None
+            self.Xq = self.Xq_scale = None
         self.Hg, self.Hu, self.A = z(R, f), z(R, f), z(R, f)
         self.Ys = z(R, d)
         self.y = z(T, d)
@@ -314,16 +320,18 @@ class ExpertLayer:
             self.topk_idx.copy_(topk_idx)
             self.topk_w.copy_(topk_w)
         moe_dispatch(x, self.topk_idx, self.E, self.counts, self.offsets, self.dest_row,
-                     self.src_token, self.Xs, self.Xs_scale, self.ws_dispatch, self.prec, stream)
-        moe_grouped_ffn_fwd(self.Xs, self.Xs_scale, self.offsets, self.T, self.k, Wg, Wu, Wd,
-                            self.Hg, self.Hu, self.A, self.Ys, self.ws_fwd, self.prec, stream)
+                     self.src_token, self.Xs, self.ws_dispatch, self.Xq, self.Xq_scale, self.prec,
+                     stream)
+        mx = self.prec == "mxfp8"
+        moe_grouped_ffn_fwd(self.Xq if mx else self.Xs, self.Xq_scale, self.offsets, self.T,
+                            self.k, Wg, Wu, Wd, self.Hg, self.Hu, self.A, self.Ys, self.ws_fwd,
+                            self.prec, stream)
         moe_combine(self.Ys, self.topk_w, self.dest_row, self.y, stream)
         return self.y
 
     def backward(self, dY, stream=None):
         moe_combine_bwd(dY, self.Ys, self.topk_w, self.dest_row, self.dYs, self.dw, stream)
-        moe_grouped_ffn_bwd(self.dYs, None if self.prec == "mxfp8" else self.Xs, self.x,
-                            self.src_token, self.Hg, self.Hu, self.A, self.offsets, self.T, self.k,
+        moe_grouped_ffn_bwd(self.dYs, self.Xs, self.Hg, self.Hu, self.A, self.offsets, self.T, self.k,
                             self.Wg, self.Wu, self.Wd, self.dH, self.dXs, self.dWg, self.dWu,
                             self.dWd, self.ws_bwd, self.prec, False, stream)
         moe_dispatch_bwd(self.dXs, self.dest_row, self.dx, False, stream)

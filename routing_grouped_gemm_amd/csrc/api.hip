@@ -15,8 +15,6 @@ using namespace moe;
 namespace {
 
 constexpr size_t kAlign = 256;
-// The MXFP8 GEMMs are not built yet: MXFP8 requests are rejected.
-constexpr bool kMxReady = false;
 inline size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -60,7 +58,7 @@ inline int check_prec(int dtype, int prec) {
   if (check_dtype(dtype) != MOE_OK) return MOE_ERR_DTYPE;
   if (prec == MOE_PREC_F32) return dtype == MOE_F32 ? MOE_OK : MOE_ERR_DTYPE;
   if (prec == MOE_PREC_BF16) return dtype == MOE_BF16 ? MOE_OK : MOE_ERR_DTYPE;
-  if (prec == MOE_PREC_MXFP8) return dtype == MOE_BF16 ? (kMxReady ? MOE_OK : MOE_ERR_UNSUPPORTED) : MOE_ERR_DTYPE;
+  if (prec == MOE_PREC_MXFP8) return dtype == MOE_BF16 ? MOE_OK : MOE_ERR_DTYPE;
   return MOE_ERR_DTYPE;
 }
 
@@ -182,15 +180,17 @@ int moe_route(const void* x, const void* Wr, int T, int d, int E, int k, int dty
 
 int moe_dispatch(const void* x, const int32_t* topk_idx, int T, int d, int E, int k, int dtype,
                  int prec, int32_t* counts, int32_t* offsets, int32_t* dest_row,
-                 int32_t* src_token, void* Xs, uint8_t* Xs_scale, void* ws, size_t ws_bytes,
-                 void* stream) {
+                 int32_t* src_token, void* Xs, void* Xq, uint8_t* Xq_scale, void* ws,
+                 size_t ws_bytes, void* stream) {
   if (!all_nonnull(x, topk_idx, counts, offsets, dest_row, src_token, Xs, ws)) return MOE_ERR_NULL;
   if (int s = check_prec(dtype, prec)) return s;
-  if (prec == MOE_PREC_MXFP8 && !Xs_scale) return MOE_ERR_NULL;
+  const bool mx = prec == MOE_PREC_MXFP8;
+  if (mx && !all_nonnull(Xq, Xq_scale)) return MOE_ERR_NULL;
   if (int s = check_route_shape(T, E, k)) return s;
   if (int s = check_width(d)) return s;
   if (int s = check_elems((long long)T * k, d)) return s;
   if (!all_aligned(x, topk_idx, counts, offsets, dest_row, src_token, Xs, ws)) return MOE_ERR_ALIGN;
+  if (mx && !all_aligned(Xq, Xq_scale)) return MOE_ERR_ALIGN;
   if (ws_bytes < dispatch_ws(T, E)) return MOE_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   clear_stale_error();
@@ -200,8 +200,7 @@ int moe_dispatch(const void* x, const int32_t* topk_idx, int T, int d, int E, in
   MOE_TRY(launch_dispatch_meta(topk_idx, T, E, k, hist, base, counts, offsets, dest_row,
                                src_token, st));
   const int R = T * k;
-  if (prec == MOE_PREC_MXFP8)
-    return status_of(launch_mx_dispatch_copy(x, src_token, R, T, d, Xs, Xs_scale, st));
+  if (mx) return status_of(launch_mx_dispatch_copy(x, src_token, R, T, d, Xs, Xq, Xq_scale, st));
   return status_of(launch_dispatch_copy(dtype, x, src_token, R, T, d, Xs, st));
 }
 
@@ -219,6 +218,7 @@ int moe_grouped_ffn_fwd(const void* Xs, const uint8_t* Xs_scale, const int32_t* 
   if (int s = check_elems(R, 2LL * (d > f ? d : f))) return s;
   if (int s = check_elems(E, (long long)d * f)) return s;
   if (!all_aligned(Xs, offsets, Wg, Wu, Wd, Hg, Hu, A, Ys, ws)) return MOE_ERR_ALIGN;
+  if (prec == MOE_PREC_MXFP8 && !aligned16(Xs_scale)) return MOE_ERR_ALIGN;
   hipStream_t st = static_cast<hipStream_t>(stream);
   clear_stale_error();
   if (prec == MOE_PREC_MXFP8) {
@@ -267,27 +267,22 @@ int moe_combine_bwd(const void* dY, const void* Ys, const float* topk_w, const i
                                       static_cast<hipStream_t>(stream)));
 }
 
-int moe_grouped_ffn_bwd(const void* dYs, const void* Xs, const void* x, const int32_t* src_token,
-                        const void* Hg, const void* Hu, const void* A, const int32_t* offsets,
-                        int T, int k, int d, int f, int E, const void* Wg, const void* Wu,
-                        const void* Wd, int dtype, int prec, unsigned flags, void* dH,
-                        void* dXs, void* dWg, void* dWu, void* dWd, void* ws, size_t ws_bytes,
-                        void* stream) {
-  if (!all_nonnull(dYs, Hg, Hu, A, offsets, Wg, Wu, Wd, dH, dXs, dWg, dWu, dWd))
+int moe_grouped_ffn_bwd(const void* dYs, const void* Xs, const void* Hg, const void* Hu,
+                        const void* A, const int32_t* offsets, int T, int k, int d, int f, int E,
+                        const void* Wg, const void* Wu, const void* Wd, int dtype, int prec,
+                        unsigned flags, void* dH, void* dXs, void* dWg, void* dWu, void* dWd,
+                        void* ws, size_t ws_bytes, void* stream) {
+  if (!all_nonnull(dYs, Xs, Hg, Hu, A, offsets, Wg, Wu, Wd, dH, dXs, dWg, dWu, dWd))
     return MOE_ERR_NULL;
   if (int s = check_prec(dtype, prec)) return s;
-  if (prec == MOE_PREC_MXFP8) {
-    if (!all_nonnull(x, src_token, ws)) return MOE_ERR_NULL;
-  } else if (!Xs) {
-    return MOE_ERR_NULL;
-  }
+  if (prec == MOE_PREC_MXFP8 && !ws) return MOE_ERR_NULL;
   if (int s = check_route_shape(T, E, k)) return s;
   if (int s = check_width(d)) return s;
   if (int s = check_width(f)) return s;
   const long long R = (long long)T * k;
   if (int s = check_elems(R, 2LL * (d > f ? d : f))) return s;
   if (int s = check_elems(E, (long long)d * f)) return s;
-  if (!all_aligned(dYs, Xs, x, src_token, Hg, Hu, A, offsets, Wg, Wu, Wd, dH, dXs, dWg, dWu, dWd, ws))
+  if (!all_aligned(dYs, Xs, Hg, Hu, A, offsets, Wg, Wu, Wd, dH, dXs, dWg, dWu, dWd, ws))
     return MOE_ERR_ALIGN;
   hipStream_t st = static_cast<hipStream_t>(stream);
   clear_stale_error();
@@ -318,9 +313,7 @@ int moe_grouped_ffn_bwd(const void* dYs, const void* Xs, const void* x, const in
   GemmArgs w{};
   w.E = E; w.offsets = offsets; w.rows_total = (int)R; w.ragged = RAG_K;
   w.M = d; w.N = 2 * f;
-  if (prec == MOE_PREC_MXFP8) { w.a = x; w.a_gather = src_token; }
-  else { w.a = Xs; }
-  w.lda = d;
+  w.a = Xs; w.lda = d;
   w.b0 = dH; w.ldb = 2L * f;
   w.c0 = dWg; w.c1 = dWu; w.ldc = f; w.c_es = (long)d * f; w.c_split = f;
   w.accumulate = acc;

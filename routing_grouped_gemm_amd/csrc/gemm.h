@@ -55,6 +55,15 @@ struct GemmArgs {
   const void* h1;  // SWIGLU_BWD: Hu
   long ldh;
   int accumulate;
+  // MXFP8 kinds: E8M0 scale bytes, block-major.  Block b (32 consecutive k)
+  // of A row r is sa[b * sa_pitch + r]; of B row n of group e is
+  // sb[e * sb_es + b * sb_pitch + n].  Operands a / b0 hold e4m3 codes, and
+  // lda / ldb / b_es are in bytes (= elements).
+  const uint8_t* sa;
+  long sa_pitch;
+  const uint8_t* sb;
+  long sb_es;
+  long sb_pitch;
 };
 
 // Operand layouts of the five GEMM kinds of the layer and of the router.
@@ -66,7 +75,12 @@ enum GemmKind : int {
   GK_WGRAD = 4,         // P[rows,M]^T . Q[rows,N]    -> dW[e][M,N]   (ragged K)
   GK_ROUTER_LOGITS = 5, // x[T,d] . Wr[d,E]           -> logits f32   (one group)
   GK_ROUTER_DWR = 6,    // x[T,d]^T . dl[T,E]         -> dWr[d,E]     (one group, K = T)
-  GK_ROUTER_DX = 7      // dl[T,E] . Wr[d,E]^T        -> dx += [T,d]  (one group, K = E)
+  GK_ROUTER_DX = 7,     // dl[T,E] . Wr[d,E]^T        -> dx += [T,d]  (one group, K = E)
+  // MXFP8 kinds: both operands K-contiguous e4m3 codes with E8M0 block scales
+  GK_MX_GATEUP = 8,       // Xq[R,d] . WguT[e][2f',d] (256-row panels: 128 gate rows, 128 up rows)
+  GK_MX_DOWN = 9,         // Aq[R,f] . WdT[e][d,f]   -> Ys
+  GK_MX_DGRAD_DOWN = 10,  // dYsq[R,d] . Wd[e][f,d]  -> dHg, dHu
+  GK_MX_DGRAD_GATEUP = 11 // dHq[R,2f] . Wgu[e][d,2f] -> dXs
 };
 
 // Engines: float32 storage on the SIMT engine, bf16 on MFMA, and bf16 on the
@@ -76,5 +90,8 @@ enum GemmEngine : int { GEMM_F32_SIMT = 0, GEMM_BF16_MFMA = 1, GEMM_BF16_SIMT = 
 // Launch a grouped GEMM of the given kind.  num_cu sizes the persistent grid.
 hipError_t launch_grouped_gemm(GemmKind kind, int engine, const GemmArgs& g, int num_cu,
                                hipStream_t stream);
+
+// Launch an MXFP8 grouped GEMM (kinds GK_MX_*).
+hipError_t launch_grouped_gemm_mx(GemmKind kind, const GemmArgs& g, int num_cu, hipStream_t stream);
 
 }  // namespace moe

@@ -22,629 +22,12 @@
 // float32 engine (the fp32 layer and odd router shapes): a plain LDS-tiled
 // SIMT kernel with the same tile schedule and the same epilogues.
 #include "gemm.h"
+#include "gemm_dev.h"
 #include "hook.h"
 #include "moe_common.h"
 
 namespace moe {
-
-// ---------------------------------------------------------------------------
-// kind traits
-// ---------------------------------------------------------------------------
-template <int KIND> struct KT;
-template <> struct KT<GK_FWD_GATEUP> {
-  static constexpr bool AK = true, BK_ = false;
-  static constexpr int BSP = BS_DUAL_N, EPI = EPI_SWIGLU_FWD;
-};
-template <> struct KT<GK_FWD_DOWN> {
-  static constexpr bool AK = true, BK_ = false;
-  static constexpr int BSP = BS_NONE, EPI = EPI_STORE;
-};
-template <> struct KT<GK_DGRAD_DOWN> {
-  static constexpr bool AK = true, BK_ = true;
-  static constexpr int BSP = BS_NONE, EPI = EPI_SWIGLU_BWD;
-};
-template <> struct KT<GK_DGRAD_GATEUP> {
-  static constexpr bool AK = true, BK_ = true;
-  static constexpr int BSP = BS_SPLIT_K, EPI = EPI_STORE;
-};
-template <> struct KT<GK_WGRAD> {
-  static constexpr bool AK = false, BK_ = false;
-  static constexpr int BSP = BS_NONE, EPI = EPI_WGRAD_SPLIT;
-};
-template <> struct KT<GK_ROUTER_LOGITS> {
-  static constexpr bool AK = true, BK_ = false;
-  static constexpr int BSP = BS_NONE, EPI = EPI_STORE_F32;
-};
-template <> struct KT<GK_ROUTER_DWR> {
-  static constexpr bool AK = false, BK_ = false;
-  static constexpr int BSP = BS_NONE, EPI = EPI_STORE;
-};
-template <> struct KT<GK_ROUTER_DX> {
-  static constexpr bool AK = true, BK_ = true;
-  static constexpr int BSP = BS_NONE, EPI = EPI_STORE;
-};
-
-// One output tile of one group.
-struct Tile {
-  int e;      // group (expert)
-  int m0;     // first row of the tile inside the group (RAG_M) or inside C (RAG_K)
-  int n0;     // first column (for BS_DUAL_N: first f column of the gate/up pair)
-  int mlim;   // rows of the tile that exist
-  int row0;   // RAG_M: global row of tile row 0; RAG_K: global row of k = 0
-  int klen;   // length of the K loop
-};
-
-// ---------------------------------------------------------------------------
-// schedule: group offsets and per-group tile starts cached in LDS
-// ---------------------------------------------------------------------------
-struct Sched {
-  int off[257];
-  int ts[257];  // RAG_M: exclusive prefix of M tiles per group
-};
-
-// Fill the schedule; returns the number of tiles.  All threads must call it.
-template <int BM, int BNT>
-__device__ int sched_setup(const GemmArgs& g, Sched& s) {
-  const int tid = threadIdx.x;
-  const int E = g.offsets ? g.E : 1;
-  if (g.offsets) {
-    for (int e = tid; e <= E; e += blockDim.x) s.off[e] = g.offsets[e];
-  } else if (tid == 0) {
-    s.off[0] = 0;
-    s.off[1] = g.rows_total;
-  }
-  __syncthreads();
-  const int ntn = (g.N + BNT - 1) / BNT;
-  if (g.ragged == RAG_M) {
-    // wave 0 scans ceil(n_e / BM) over the groups, 4 groups per lane
-    if (tid < kWave) {
-      int c[4], sum = 0;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        int e = tid * 4 + q;
-        c[q] = (e < E) ? (s.off[e + 1] - s.off[e] + BM - 1) / BM : 0;
-        sum += c[q];
-      }
-      int incl = sum;
-#pragma unroll
-      for (int o = 1; o < kWave; o <<= 1) {
-        int v = __shfl_up(incl, o, kWave);
-        if (tid >= o) incl += v;
-      }
-      int run = incl - sum;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        int e = tid * 4 + q;
-        if (e <= E) s.ts[e] = run;
-        run += c[q];
-      }
-      if (tid == kWave - 1 && E == 256) s.ts[256] = incl;
-    }
-    __syncthreads();
-    return s.ts[E] * ntn;
-  }
-  const int ntm = (g.M + BM - 1) / BM;
-  return E * ntm * ntn;
-}
-
-template <int BM, int BNT>
-__device__ __forceinline__ Tile sched_decode(const GemmArgs& g, const Sched& s, int L) {
-  const int ntn = (g.N + BNT - 1) / BNT;
-  Tile t;
-  if (g.ragged == RAG_M) {
-    const int E = g.offsets ? g.E : 1;
-    int mt = L / ntn, nt = L - mt * ntn;
-    int lo = 0, hi = E;  // largest e in [0,E) with ts[e] <= mt
-    while (hi - lo > 1) {
-      int mid = (lo + hi) >> 1;
-      if (s.ts[mid] <= mt) lo = mid; else hi = mid;
-    }
-    t.e = lo;
-    t.m0 = (mt - s.ts[lo]) * BM;
-    int ne = s.off[lo + 1] - s.off[lo];
-    t.mlim = min(BM, ne - t.m0);
-    t.row0 = s.off[lo] + t.m0;
-    t.n0 = nt * BNT;
-    t.klen = g.K;
-  } else {
-    const int ntm = (g.M + BM - 1) / BM;
-    int per = ntm * ntn;
-    t.e = L / per;
-    int r = L - t.e * per;
-    int mt = r / ntn, nt = r - mt * ntn;
-    t.m0 = mt * BM;
-    t.mlim = min(BM, g.M - t.m0);
-    t.n0 = nt * BNT;
-    t.row0 = s.off[t.e];
-    t.klen = s.off[t.e + 1] - s.off[t.e];
-  }
-  return t;
-}
-
-// Logical tile for iteration `it` of workgroup blockIdx.x: with G = 8*P
-// workgroups, workgroup b sits on XCD b % 8, and the P workgroups of one XCD
-// take P consecutive logical tiles.
-__device__ __forceinline__ int logical_tile(int it) {
-  const int G = gridDim.x, b = blockIdx.x;
-  if (G % 8) return it * G + b;
-  return it * G + (b & 7) * (G >> 3) + (b >> 3);
-}
-
-// ---------------------------------------------------------------------------
-// epilogue: four consecutive columns of one output row
-// ---------------------------------------------------------------------------
-template <typename TS>
-__device__ __forceinline__ void store4(TS* p, const float (&v)[4], bool acc) {
-  if constexpr (sizeof(TS) == 2) {
-    uint2 u;
-    if (acc) {
-      uint2 o = *reinterpret_cast<const uint2*>(p);
-      u.x = pack_bf16x2(v[0] + __uint_as_float(o.x << 16), v[1] + __uint_as_float(o.x & 0xffff0000u));
-      u.y = pack_bf16x2(v[2] + __uint_as_float(o.y << 16), v[3] + __uint_as_float(o.y & 0xffff0000u));
-    } else {
-      u.x = pack_bf16x2(v[0], v[1]);
-      u.y = pack_bf16x2(v[2], v[3]);
-    }
-    *reinterpret_cast<uint2*>(p) = u;
-  } else {
-    float4 o = acc ? *reinterpret_cast<const float4*>(p) : make_float4(0.f, 0.f, 0.f, 0.f);
-    *reinterpret_cast<float4*>(p) = make_float4(v[0] + o.x, v[1] + o.y, v[2] + o.z, v[3] + o.w);
-  }
-}
-
-template <typename TS>
-__device__ __forceinline__ void load4(const TS* p, float (&v)[4]) {
-  if constexpr (sizeof(TS) == 2) {
-    uint2 u = *reinterpret_cast<const uint2*>(p);
-    v[0] = __uint_as_float(u.x << 16); v[1] = __uint_as_float(u.x & 0xffff0000u);
-    v[2] = __uint_as_float(u.y << 16); v[3] = __uint_as_float(u.y & 0xffff0000u);
-  } else {
-    float4 u = *reinterpret_cast<const float4*>(p);
-    v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
-  }
-}
-
-// Scalar store of the first nv of four values (router shapes whose width is
-// not a multiple of 4).
-template <typename TS>
-__device__ __forceinline__ void store_part(TS* p, const float (&v)[4], int nv, bool acc) {
-  for (int q = 0; q < nv; ++q) {
-    float o = acc ? St<TS>::load(p + q) : 0.0f;
-    St<TS>::store(p + q, v[q] + o);
-  }
-}
-
-// m: row inside the tile (< t.mlim); n: output column (f column for the
-// SwiGLU kinds), n < N.  u: the up-projection values for EPI_SWIGLU_FWD.
-// The SwiGLU and weight-gradient kinds always have n + 3 < N and 4-aligned
-// rows; the plain stores may end in a partial quad.
-// PARTIAL: the engine may hand over quads that end past N or rows whose width
-// is not a multiple of 4 (SIMT engine on router shapes); the MFMA engine only
-// takes widths that are multiples of 8 and never does.
-template <int EPI, typename TS, bool PARTIAL = true>
-__device__ __forceinline__ void epilogue4(const GemmArgs& g, const Tile& t, int m, int n,
-                                          const float (&v)[4], const float (&u)[4]) {
-  if constexpr (EPI == EPI_STORE_F32) {
-    long row = (long)t.row0 + m;
-    float* p = static_cast<float*>(g.c0) + row * g.ldc + n;
-    if (!PARTIAL || (n + 4 <= g.N && (g.ldc & 3) == 0))
-      *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
-    else
-      store_part(p, v, min(4, g.N - n), false);
-  } else if constexpr (EPI == EPI_STORE) {
-    long row = (g.ragged == RAG_M) ? (long)t.row0 + m : (long)t.m0 + m;
-    TS* p = static_cast<TS*>(g.c0) + (g.ragged == RAG_M ? 0 : (long)t.e * g.c_es) + row * g.ldc + n;
-    if (!PARTIAL || (n + 4 <= g.N && (g.ldc & 3) == 0))
-      store4(p, v, g.accumulate != 0);
-    else
-      store_part(p, v, min(4, g.N - n), g.accumulate != 0);
-  } else if constexpr (EPI == EPI_WGRAD_SPLIT) {
-    long row = (long)t.m0 + m;
-    TS* p;
-    if (n < g.c_split)
-      p = static_cast<TS*>(g.c0) + (long)t.e * g.c_es + row * g.ldc + n;
-    else
-      p = static_cast<TS*>(g.c1) + (long)t.e * g.c_es + row * g.ldc + (n - g.c_split);
-    store4(p, v, g.accumulate != 0);
-  } else if constexpr (EPI == EPI_SWIGLU_FWD) {
-    long off = ((long)t.row0 + m) * g.ldc + n;
-    float a[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) a[q] = silu_f(v[q]) * u[q];
-    store4(static_cast<TS*>(g.c0) + off, v, false);
-    store4(static_cast<TS*>(g.c1) + off, u, false);
-    store4(static_cast<TS*>(g.c2) + off, a, false);
-  } else if constexpr (EPI == EPI_SWIGLU_BWD) {
-    long row = (long)t.row0 + m;
-    float hg[4], hu[4], dg[4], du[4];
-    load4(static_cast<const TS*>(g.h0) + row * g.ldh + n, hg);
-    load4(static_cast<const TS*>(g.h1) + row * g.ldh + n, hu);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      float s = 1.0f / (1.0f + __expf(-hg[q]));
-      du[q] = v[q] * hg[q] * s;
-      dg[q] = v[q] * hu[q] * s * (1.0f + hg[q] * (1.0f - s));
-    }
-    TS* p = static_cast<TS*>(g.c0) + row * g.ldc + n;
-    store4(p, dg, false);
-    store4(p + g.c_split, du, false);
-  }
-}
-
-// ---------------------------------------------------------------------------
-// bf16 MFMA engine
-// ---------------------------------------------------------------------------
 namespace mf {
-
-constexpr int BM = 256, BN = 256, BK = 32, NST = 4, NTHR = 256;
-constexpr int OPB = BM * BK * 2;    // bytes of one operand in one stage (16 KiB)
-constexpr int STAGE = 2 * OPB;      // A then B
-constexpr int DMA_PER_STAGE = 8;    // buffer->LDS loads per wave per stage (4 per operand)
-
-typedef __attribute__((ext_vector_type(4))) int i32x4_t;
-typedef __attribute__((ext_vector_type(4))) short i16x4_t;
-typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
-
-// Raw buffer resource over [base, base + bytes): loads beyond it return 0
-// (and write 0 into LDS for the LDS-targeted form).
-__device__ __forceinline__ i32x4_t make_rsrc(const void* base, long long bytes) {
-  const uint64_t b = reinterpret_cast<uint64_t>(base);
-  const uint32_t n = bytes <= 0 ? 0u : (bytes >= 0xffffffffLL ? 0xffffffffu : (uint32_t)bytes);
-  i32x4_t r;
-  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)b);
-  r.y = __builtin_amdgcn_readfirstlane((int)((b >> 32) & 0xffffu));
-  r.z = __builtin_amdgcn_readfirstlane((int)n);
-  r.w = 0x00020000;
-  return r;
-}
-
-// 16 bytes per lane from the buffer straight into LDS at lds_addr + 16*lane.
-// Issued as inline asm so that the compiler's LDS-DMA tracking does not turn
-// the ring's partial waits into full ones; completion is awaited explicitly
-// with vmcnt before the barrier of the stage that reads the data.
-__device__ __forceinline__ void dma16(i32x4_t rsrc, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
-  i32x4_t r;
-  r.x = __builtin_amdgcn_readfirstlane(rsrc.x);
-  r.y = __builtin_amdgcn_readfirstlane(rsrc.y);
-  r.z = __builtin_amdgcn_readfirstlane(rsrc.z);
-  r.w = __builtin_amdgcn_readfirstlane(rsrc.w);
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr);
-  const uint32_t so = __builtin_amdgcn_readfirstlane(soff);
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :: "s"(m0), "v"(voff), "s"(r), "s"(so) : "memory");
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
-}
-__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
-
-__device__ __forceinline__ uint32_t lds_u32(const void* p) {
-  return (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)p);
-}
-
-// LDS layouts of one operand stage (16 KiB), in 16-byte chunks.
-//  K-major ("KM": rows are M or N, 32 contiguous k per row = 64 B = 4 chunks):
-//    byte = row*64 + ((chunk ^ km_swz(row)) << 4)
-//  MN-major ("MN": rows are k, two panels of 128 contiguous columns):
-//    byte = panel*8192 + k*256 + (((col/8) ^ mn_swz(k)) << 4) + 2*(col & 7)
-// The swizzles make every fragment read conflict-free whether the LDS serves
-// 128 or 256 bytes per clock: a ds_read_b128 fragment touches 16 consecutive
-// rows at one chunk (km_swz gives each residue of row mod 4 all four
-// chunks), a ds_read_b64_tr_b16 pair touches 4 k-rows x 4 chunks (mn_swz
-// spreads them over 16 distinct chunk slots, and over 8 for any 16 lanes).
-__device__ __forceinline__ int km_swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
-__device__ __forceinline__ int mn_swz(int k) { return (4 * (k & 3)) ^ (2 * ((k >> 1) & 1)); }
-__device__ __forceinline__ int km_off(int row, int chunk) {
-  return row * 64 + ((chunk ^ km_swz(row)) << 4);
-}
-__device__ __forceinline__ int mn_off(int k, int col) {
-  const int panel = col >> 7, cc = col & 127;
-  return panel * 8192 + k * 256 + (((cc >> 3) ^ mn_swz(k)) << 4) + 2 * (cc & 7);
-}
-
-// Per-wave DMA plan of one operand for one tile.
-struct Plan {
-  i32x4_t rs0, rs1;   // resources (rs1: second source: SPLIT_K, or MN panel of waves 2-3)
-  uint32_t voff[4];   // per-lane byte offsets of the wave's four 1 KiB blocks
-  uint32_t lds[4];    // LDS offsets of those blocks inside the operand stage
-  uint32_t kstep;     // bytes the source advances per stage (BK elements along K)
-  int split_stage;    // SPLIT_K: first stage read from rs1 (else a large value)
-};
-
-// K-major operand: rows r of the tile are rows of a matrix with ld elements,
-// starting at `base`; `bytes` are readable from base.
-__device__ __forceinline__ void plan_km(Plan& P, const void* base, long long bytes, const void* base1,
-                                        long long bytes1, int split_stage, long ld, int wave,
-                                        int lane) {
-  P.rs0 = make_rsrc(base, bytes);
-  P.rs1 = make_rsrc(base1 ? base1 : base, base1 ? bytes1 : bytes);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int blk = wave * 4 + i;
-    const int row = blk * 16 + (lane >> 2);
-    const int c = (lane & 3) ^ km_swz(row);
-    P.voff[i] = (uint32_t)(row * ld * 2 + c * 16);
-    P.lds[i] = blk * 1024;
-  }
-  P.kstep = BK * 2;
-  P.split_stage = split_stage;
-}
-
-// MN-major operand: k-rows of a matrix with ld elements; panel p of the tile
-// starts at base_p (its column 0 at k = 0); bytes_p readable from base_p.
-__device__ __forceinline__ void plan_mn(Plan& P, const void* base0, long long bytes0,
-                                        const void* base1, long long bytes1, long ld, int wave,
-                                        int lane) {
-  P.rs0 = make_rsrc(base0, bytes0);
-  P.rs1 = make_rsrc(base1, bytes1);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int blk = wave * 4 + i;   // blocks 0-7: panel 0, 8-15: panel 1
-    const int rb = blk & 7;
-    const int k = rb * 4 + (lane >> 4);
-    const int c = (lane & 15) ^ mn_swz(k);
-    P.voff[i] = (uint32_t)(k * ld * 2 + c * 16);
-    P.lds[i] = (blk >> 3) * 8192 + rb * 1024;
-  }
-  P.kstep = (uint32_t)(BK * ld * 2);
-  P.split_stage = 1 << 30;
-}
-
-// Issue the wave's four DMA blocks of one operand for stage kt into the LDS
-// operand region at lds_base.
-template <bool MN>
-__device__ __forceinline__ void issue(const Plan& P, int kt, uint32_t lds_base, int wave) {
-  i32x4_t rs;
-  uint32_t soff;
-  if constexpr (MN) {
-    rs = (wave >= 2) ? P.rs1 : P.rs0;
-    soff = (uint32_t)kt * P.kstep;
-  } else {
-    const bool second = kt >= P.split_stage;
-    rs = second ? P.rs1 : P.rs0;
-    soff = (uint32_t)(second ? kt - P.split_stage : kt) * P.kstep;
-  }
-  soff = __builtin_amdgcn_readfirstlane(soff);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) dma16(rs, lds_base + P.lds[i], P.voff[i], soff);
-}
-
-// MFMA fragment (8 consecutive k of one row/column) from an operand stage.
-// row: M or N index inside the tile; s: k16 step inside the stage.
-template <bool MN>
-__device__ __forceinline__ bf16x8_t frag(const char* op, int rowblk, int s, int lane) {
-  if constexpr (!MN) {
-    const int row = rowblk + (lane & 31);
-    return *reinterpret_cast<const bf16x8_t*>(op + km_off(row, 2 * s + (lane >> 5)));
-  } else {
-    // ds_read_b64_tr_b16: within each 16-lane group the lanes' 8-byte reads
-    // (4 k-rows x 4 column quads) come back transposed, so lane i of the
-    // group receives column i at 4 consecutive k.
-    const int g = lane >> 4, r = lane & 15;
-    const int k = 16 * s + 8 * (g >> 1) + (r >> 2);
-    const int col = rowblk + 16 * (g & 1) + 4 * (r & 3);
-    const char* p = op + mn_off(k, col);
-    i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p));
-    i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p + 4 * 256));
-    typedef __attribute__((ext_vector_type(8))) short i16x8_t;
-    i16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    return __builtin_bit_cast(bf16x8_t, v);
-  }
-}
-
-// Fragments of one k16 step of stage kt: 4 A fragments (rows wm*128 + 32i)
-// and 4 B fragments (columns of wave column wn; gate/up pairs when DUAL).
-template <bool AMN, bool BMN, bool DUAL>
-__device__ __forceinline__ void load_frags(const char* smem, int kt, int s, int wm, int wn,
-                                           int lane, bf16x8_t (&fa)[4], bf16x8_t (&fb)[4]) {
-  const char* As = smem + (kt & (NST - 1)) * STAGE;
-  const char* Bs = As + OPB;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) fa[i] = frag<AMN>(As, wm * 128 + i * 32, s, lane);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int col = DUAL ? ((j >> 1) * 128 + wn * 64 + (j & 1) * 32) : (wn * 128 + j * 32);
-    fb[j] = frag<BMN>(Bs, col, s, lane);
-  }
-}
-
-__device__ __forceinline__ void mfma16(f32x16_t (&acc)[4][4], const bf16x8_t (&fa)[4],
-                                       const bf16x8_t (&fb)[4]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
-}
-
-// s_waitcnt with lgkmcnt(0) and the other counters left alone (gfx9 encoding).
-constexpr int kLgkm0 = 0xC07F;
-
-// Ask the scheduler to alternate MFMAs and LDS reads (16 each at most) in the
-// region since the last scheduling barrier.
-__device__ __forceinline__ void interleave_mfma_ds() {
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-  }
-}
-
-// Wait until stage st has landed, given that stages up to last_issued are in flight.
-__device__ __forceinline__ void wait_stage(int st, int last_issued) {
-  const int after = last_issued - st;
-  if (after >= 3) wait_vmcnt<3 * DMA_PER_STAGE>();
-  else if (after == 2) wait_vmcnt<2 * DMA_PER_STAGE>();
-  else if (after == 1) wait_vmcnt<DMA_PER_STAGE>();
-  else wait_vmcnt<0>();
-}
-
-// Operand plans of one tile for each GEMM kind.
-template <int KIND>
-__device__ __forceinline__ void plan_tile(const GemmArgs& g, const Tile& t, int wave, int lane,
-                                          Plan& pa, Plan& pb) {
-  const bf16_t* A = static_cast<const bf16_t*>(g.a);
-  const bf16_t* B0 = static_cast<const bf16_t*>(g.b0);
-  const bf16_t* B1 = static_cast<const bf16_t*>(g.b1);
-  constexpr int BSP = KT<KIND>::BSP;
-  // ---- A ----
-  if constexpr (KT<KIND>::AK) {
-    // rows t.row0.. of A (global rows), K contiguous
-    const bf16_t* base = A + (long)t.row0 * g.lda;
-    const long long bytes = ((long long)g.rows_total - t.row0) * g.lda * 2;
-    plan_km(pa, base, bytes, nullptr, 0, 1 << 30, g.lda, wave, lane);
-  } else {
-    // k-rows t.row0 .. t.row0 + klen of A, M contiguous; columns t.m0 + 128 p
-    const bf16_t* b0 = A + (long)t.row0 * g.lda + t.m0;
-    const long long avail = (long long)t.klen * g.lda * 2;
-    plan_mn(pa, b0, avail - 2LL * t.m0, b0 + 128, avail - 2LL * (t.m0 + 128), g.lda, wave, lane);
-  }
-  // ---- B ----
-  if constexpr (KT<KIND>::BK_) {
-    // B[n][k] per group, rows t.n0..
-    const long e_off = (long)t.e * g.b_es + (long)t.n0 * g.ldb;
-    const long long bytes = ((long long)g.N - t.n0) * g.ldb * 2;
-    if constexpr (BSP == BS_SPLIT_K)
-      plan_km(pb, B0 + e_off, bytes, B1 + e_off, bytes, g.b_split / BK, g.ldb, wave, lane);
-    else
-      plan_km(pb, B0 + e_off, bytes, nullptr, 0, 1 << 30, g.ldb, wave, lane);
-  } else if (g.ragged == RAG_M) {
-    // B[k][n] per group (weights), N contiguous
-    const bf16_t* w0 = B0 + (long)t.e * g.b_es;
-    const long long total = (long long)g.K * g.ldb * 2;
-    if constexpr (BSP == BS_DUAL_N) {
-      const bf16_t* w1 = B1 + (long)t.e * g.b_es;
-      plan_mn(pb, w0 + t.n0, total - 2LL * t.n0, w1 + t.n0, total - 2LL * t.n0, g.ldb, wave, lane);
-    } else {
-      plan_mn(pb, w0 + t.n0, total - 2LL * t.n0, w0 + t.n0 + 128, total - 2LL * (t.n0 + 128),
-              g.ldb, wave, lane);
-    }
-  } else {
-    // B[krow][n] with global k-rows t.row0 .. t.row0 + klen
-    const bf16_t* b0 = B0 + (long)t.row0 * g.ldb + t.n0;
-    const long long avail = (long long)t.klen * g.ldb * 2;
-    plan_mn(pb, b0, avail - 2LL * t.n0, b0 + 128, avail - 2LL * (t.n0 + 128), g.ldb, wave, lane);
-  }
-}
-
-// Float32 staging slice of one wave: 64 rows x 128 columns, 16-byte chunks
-// XOR-swizzled by row so that both the accumulator writes (32 rows, one
-// chunk) and the row reads (one row, 16 chunks) avoid bank conflicts.
-__device__ __forceinline__ int stage_off(int r, int chunk) { return r * 512 + ((chunk ^ (r & 31)) << 4); }
-
-// Epilogue of one 8-column piece: v = tile values (gate for the SwiGLU
-// forward), u = up values (SwiGLU forward only).  grow: global row (RAG_M)
-// or row inside the group's C (RAG_K); n: output column.
-template <int EPI>
-__device__ __forceinline__ void epi8(const GemmArgs& g, const Tile& t, long row, int n,
-                                     const float (&v)[8], const float (&u)[8]) {
-  if constexpr (EPI == EPI_STORE_F32) {
-    float* p = static_cast<float*>(g.c0) + row * g.ldc + n;
-    store8(p, v);
-  } else if constexpr (EPI == EPI_STORE || EPI == EPI_WGRAD_SPLIT) {
-    bf16_t* p;
-    if constexpr (EPI == EPI_WGRAD_SPLIT) {
-      if (n < g.c_split)
-        p = static_cast<bf16_t*>(g.c0) + (long)t.e * g.c_es + row * g.ldc + n;
-      else
-        p = static_cast<bf16_t*>(g.c1) + (long)t.e * g.c_es + row * g.ldc + (n - g.c_split);
-    } else {
-      p = static_cast<bf16_t*>(g.c0) + (g.ragged == RAG_M ? 0 : (long)t.e * g.c_es) + row * g.ldc + n;
-    }
-    if (g.accumulate) {
-      float o[8], w[8];
-      load8(p, o);
-#pragma unroll
-      for (int q = 0; q < 8; ++q) w[q] = v[q] + o[q];
-      store8(p, w);
-    } else {
-      store8(p, v);
-    }
-  } else if constexpr (EPI == EPI_SWIGLU_FWD) {
-    const long off = row * g.ldc + n;
-    float a[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) a[q] = silu_f(v[q]) * u[q];
-    store8(static_cast<bf16_t*>(g.c0) + off, v);
-    store8(static_cast<bf16_t*>(g.c1) + off, u);
-    store8(static_cast<bf16_t*>(g.c2) + off, a);
-  } else if constexpr (EPI == EPI_SWIGLU_BWD) {
-    float hg[8], hu[8], dg[8], du[8];
-    load8(static_cast<const bf16_t*>(g.h0) + row * g.ldh + n, hg);
-    load8(static_cast<const bf16_t*>(g.h1) + row * g.ldh + n, hu);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const float sg = 1.0f / (1.0f + __expf(-hg[q]));
-      du[q] = v[q] * hg[q] * sg;
-      dg[q] = v[q] * hu[q] * sg * (1.0f + hg[q] * (1.0f - sg));
-    }
-    bf16_t* p = static_cast<bf16_t*>(g.c0) + row * g.ldc + n;
-    store8(p, dg);
-    store8(p + g.c_split, du);
-  }
-}
-
-template <int KIND>
-__device__ __forceinline__ void epilogue_lds(const GemmArgs& g, const Tile& t, char* slice,
-                                             f32x16_t (&acc)[4][4], int wm, int wn, int lane) {
-  constexpr int EPI = KT<KIND>::EPI;
-  constexpr bool DUAL = KT<KIND>::BSP == BS_DUAL_N;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    // accumulators of row blocks i = 2h, 2h+1 into the slice
-#pragma unroll
-    for (int ii = 0; ii < 2; ++ii)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int grp = 0; grp < 4; ++grp) {
-          const int r = ii * 32 + (lane & 31);
-          const int chunk = j * 8 + 2 * grp + (lane >> 5);
-          f32x4_t v = {acc[2 * h + ii][j][4 * grp], acc[2 * h + ii][j][4 * grp + 1],
-                       acc[2 * h + ii][j][4 * grp + 2], acc[2 * h + ii][j][4 * grp + 3]};
-          *reinterpret_cast<f32x4_t*>(slice + stage_off(r, chunk)) = v;
-        }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    // rows of this half: tile rows wm*128 + h*64 + r
-    if constexpr (DUAL) {
-      // slice columns 0..63: gate, 64..127: up, for f columns n0 + wn*64 + c
-#pragma unroll 2
-      for (int it = 0; it < 8; ++it) {
-        const int r = it * 8 + (lane >> 3);
-        const int c = (lane & 7) * 8;
-        const int m = wm * 128 + h * 64 + r;
-        float v[8], u[8];
-        const f32x4_t* p0 = reinterpret_cast<const f32x4_t*>(slice + stage_off(r, c >> 2));
-        const f32x4_t* p1 = reinterpret_cast<const f32x4_t*>(slice + stage_off(r, (c >> 2) + 1));
-        const f32x4_t* q0 = reinterpret_cast<const f32x4_t*>(slice + stage_off(r, (c >> 2) + 16));
-        const f32x4_t* q1 = reinterpret_cast<const f32x4_t*>(slice + stage_off(r, (c >> 2) + 17));
-        f32x4_t a0 = *p0, a1 = *p1, b0 = *q0, b1 = *q1;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) { v[q] = a0[q]; v[q + 4] = a1[q]; u[q] = b0[q]; u[q + 4] = b1[q]; }
-        const int n = t.n0 + wn * 64 + c;
-        if (m < t.mlim && n < g.N) epi8<EPI>(g, t, (long)t.row0 + m, n, v, u);
-      }
-    } else {
-#pragma unroll 2
-      for (int it = 0; it < 16; ++it) {
-        const int r = it * 4 + (lane >> 4);
-        const int c = (lane & 15) * 8;
-        const int m = wm * 128 + h * 64 + r;
-        float v[8];
-        const f32x4_t a0 = *reinterpret_cast<const f32x4_t*>(slice + stage_off(r, c >> 2));
-        const f32x4_t a1 = *reinterpret_cast<const f32x4_t*>(slice + stage_off(r, (c >> 2) + 1));
-#pragma unroll
-        for (int q = 0; q < 4; ++q) { v[q] = a0[q]; v[q + 4] = a1[q]; }
-        const int n = t.n0 + wn * 128 + c;
-        const long row = (g.ragged == RAG_M) ? (long)t.row0 + m : (long)t.m0 + m;
-        if (m < t.mlim && n < g.N) epi8<EPI>(g, t, row, n, v, v);
-      }
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  }
-}
 
 template <int KIND>
 __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(GemmArgs g) {

@@ -10,10 +10,13 @@ namespace moe {
 
 size_t mx_fwd_workspace(long long R, int d, int f, int E);
 size_t mx_bwd_workspace(long long R, int d, int f, int E);
+// Row pitch of block-major activation scales: R rounded up to 16.
+long mx_scale_pitch(long long R);
 
-// Xs[r] = e4m3(x[src_token[r]] / 2^E_b), Xs_scale[r][b] = E_b + 127 per 32-block b along d.
+// Xs[r] = x[src_token[r]] (bf16); Xq[r] = its e4m3 codes along d and
+// Xq_scale[b * pitch + r] = E_b + 127 for each 32-element block b.
 hipError_t launch_mx_dispatch_copy(const void* x, const int32_t* src_token, int R, int T, int d,
-                                   void* Xs, uint8_t* Xs_scale, hipStream_t s);
+                                   void* Xs, void* Xq, uint8_t* Xq_scale, hipStream_t s);
 hipError_t mx_ffn_fwd(const void* Xq, const uint8_t* Xscale, const int32_t* offsets, int R, int d,
                       int f, int E, const void* Wg, const void* Wu, const void* Wd, void* Hg,
                       void* Hu, void* A, void* Ys, void* ws, int num_cu, hipStream_t s);

@@ -1,15 +1,532 @@
-// MXFP8 path (not built yet): every entry reports hipErrorNotSupported.
+// MXFP8 path of the expert layer (gfx950).
+//
+// MXFP8 block quantisation (olmoforge README, MXFP8 snippet and module
+// table: blocks of 32 values share one scale; e4m3 elements up to 448).
+// Reading of the snippet: the block scale is 2^E with E the least integer such
+// that 448 * 2^E >= max|block| (0 for an all-zero block, clamped to the E8M0
+// range [-127, 127]); each element is rounded to the nearest OCP e4m3 value,
+// ties to even, saturating at 448.  Scales are stored as E8M0 bytes, E + 127.
+//
+// Every MX GEMM operand is quantised along that GEMM's contraction axis and
+// laid out K-contiguous, so one grouped GEMM kernel (both operands K-major)
+// serves all four MX GEMMs:
+//   forward gate/up  Xq[R,d]   x WguT[e][rows, d]  (Wg, Wu along d, transposed;
+//                    256-row panels of 128 gate rows then the 128 up rows of
+//                    the same f columns, so the gate/up epilogue applies)
+//   forward down     Aq[R,f]   x WdT[e][d, f]      (Wd along f, transposed)
+//   down dgrad       dYsq[R,d] x Wd[e][f, d]       (Wd along d, as stored)
+//   gate/up dgrad    dHq[R,2f] x Wgu[e][d, 2f]     (Wg | Wu along f, as stored)
+// Scales are block-major ([block][row]) with the activation row pitch rounded
+// up to 16, so each stage's scales arrive by the same buffer->LDS DMA as the
+// codes.  The MFMA is v_mfma_scale_f32_32x32x64_f8f6f4 (e4m3 x e4m3, float32
+// accumulate): within a lane's 32 code bytes, bytes 0-15 belong to the first
+// 32-element K block (scale from lanes 0-31) and bytes 16-31 to the second
+// (scale from lanes 32-63); lane half h holds k = 16h + 0..15 and 32 + 16h +
+// 0..15.
+#include "gemm.h"
+#include "gemm_dev.h"
+#include "hook.h"
+#include "moe_common.h"
 #include "mx.h"
 
 namespace moe {
-size_t mx_fwd_workspace(long long, int, int, int) { return 0; }
-size_t mx_bwd_workspace(long long, int, int, int) { return 0; }
-hipError_t launch_mx_dispatch_copy(const void*, const int32_t*, int, int, int, void*, uint8_t*,
-                                   hipStream_t) { return hipErrorNotSupported; }
-hipError_t mx_ffn_fwd(const void*, const uint8_t*, const int32_t*, int, int, int, int, const void*,
-                      const void*, const void*, void*, void*, void*, void*, void*, int,
-                      hipStream_t) { return hipErrorNotSupported; }
-hipError_t mx_ffn_dgrad(const void*, const void*, const void*, const int32_t*, int, int, int, int,
-                        const void*, const void*, const void*, void*, void*, void*, int,
-                        hipStream_t) { return hipErrorNotSupported; }
+
+// ---------------------------------------------------------------------------
+// codec
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int mx_block_exponent(float amax) {
+  if (!(amax > 0.0f)) return 0;
+  int ex;
+  const float m = frexpf(amax, &ex);  // amax = m * 2^ex, m in [0.5, 1)
+  const int top = ex - 1;             // amax in [2^top, 2^(top+1))
+  // 448 * 2^(top-8) = 1.75 * 2^top >= amax iff 2m <= 1.75; else top-7 suffices
+  const int E = (2.0f * m <= 1.75f) ? top - 8 : top - 7;
+  return min(max(E, -127), 127);
+}
+
+// e4m3 byte of v (already divided by the block scale), RNE, saturating.
+__device__ __forceinline__ uint32_t e4m3_code(float v) {
+  const uint32_t sign = (__float_as_uint(v) >> 31) << 7;
+  const float a = fabsf(v);
+  uint32_t code;
+  if (a < 0.015625f) {                   // below 2^-6: spacing 2^-9
+    code = (uint32_t)rintf(a * 512.0f);  // 0..8 (8 is the smallest normal, 0x08)
+  } else {
+    int ex;
+    frexpf(a, &ex);
+    int e = ex - 1;                      // a in [2^e, 2^(e+1)), e >= -6
+    int q = (int)rintf(ldexpf(a, 3 - e));  // 8..16
+    if (q == 16) { ++e; q = 8; }
+    code = (uint32_t)(((e + 7) << 3) | (q - 8));
+    if (code > 0x7Eu) code = 0x7Eu;      // 448
+  }
+  return sign | code;
+}
+
+// 8 values of one lane; the 32-element block spans the 4 lanes 4g..4g+3.
+// Returns the block exponent; codes[0..1] receive the 8 bytes.
+__device__ __forceinline__ int quant8(const float (&v)[8], uint32_t (&codes)[2]) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) amax = fmaxf(amax, fabsf(v[q]));
+  amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
+  amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
+  const int E = mx_block_exponent(amax);
+  codes[0] = codes[1] = 0;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) codes[q >> 2] |= e4m3_code(ldexpf(v[q], -E)) << (8 * (q & 3));
+  return E;
+}
+
+// ---------------------------------------------------------------------------
+// quantisation kernels
+// ---------------------------------------------------------------------------
+// Dispatch row copy with quantisation: Xs[r] = x[src[r]] in bf16 (for the
+// weight gradients) and Xq[r] / scales along d.  One wave per row.
+__global__ __launch_bounds__(256) void mx_dispatch_kernel(const bf16_t* __restrict__ x,
+                                                          const int32_t* __restrict__ src_token,
+                                                          int R, int T, int d, bf16_t* __restrict__ Xs,
+                                                          uint8_t* __restrict__ Xq,
+                                                          uint8_t* __restrict__ scale, long pitch) {
+  const int lane = threadIdx.x & 63;
+  const long r = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= R) return;
+  const int t = min(max(src_token[r], 0), T - 1);
+  const bf16_t* src = x + (long)t * d;
+  for (int c = lane * 8; c < d; c += 512) {
+    const uint4 raw = *reinterpret_cast<const uint4*>(src + c);
+    *reinterpret_cast<uint4*>(Xs + r * d + c) = raw;
+    float v[8];
+    load8(src + c, v);
+    uint32_t codes[2];
+    const int E = quant8(v, codes);
+    *reinterpret_cast<uint2*>(Xq + r * d + c) = make_uint2(codes[0], codes[1]);
+    if ((lane & 3) == 0) scale[(long)(c >> 5) * pitch + r] = (uint8_t)(E + 127);
+  }
+}
+
+// Rows of a bf16 matrix quantised along their length K.  Row r belongs to
+// group r / grows (index i = r % grows); codes go to dst + r*dst_ld + col0,
+// the scale of block b to scale[g*sg_stride + (block0 + b)*pitch + i].
+__global__ __launch_bounds__(256) void mx_quant_rows_kernel(
+    const bf16_t* __restrict__ src, long nrows, int K, long src_ld, uint8_t* __restrict__ dst,
+    long dst_ld, long col0, uint8_t* __restrict__ scale, long grows, long sg_stride, long pitch,
+    int block0) {
+  const int lane = threadIdx.x & 63;
+  const long r = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= nrows) return;
+  const long g = r / grows, i = r - g * grows;
+  for (int c = lane * 8; c < K; c += 512) {
+    float v[8];
+    load8(src + r * src_ld + c, v);
+    uint32_t codes[2];
+    const int E = quant8(v, codes);
+    *reinterpret_cast<uint2*>(dst + r * dst_ld + col0 + c) = make_uint2(codes[0], codes[1]);
+    if ((lane & 3) == 0) scale[g * sg_stride + (long)(block0 + (c >> 5)) * pitch + i] = (uint8_t)(E + 127);
+  }
+}
+
+// Columns of W[e][K][N] quantised along K and written transposed: column n
+// becomes row rowmap(n) of dst[e] (rows of K codes); the scale of block b to
+// scale[e*s_es + b*pitch + rowmap(n)].  half >= 0 selects the gate/up panel
+// map rowmap(n) = 256*(n/128) + 128*half + n%128; half < 0 keeps rowmap(n) = n.
+__global__ __launch_bounds__(256) void mx_quant_cols_kernel(
+    const bf16_t* __restrict__ W, int K, int N, uint8_t* __restrict__ dst, long dst_es,
+    int half, uint8_t* __restrict__ scale, long s_es, long pitch) {
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  const int kb = blockIdx.y, e = blockIdx.z;
+  if (n >= N) return;
+  const bf16_t* col = W + (long)e * K * N + (long)kb * 32 * N + n;
+  float v[32];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    v[i] = bf16_to_f32(col[(long)i * N]);
+    amax = fmaxf(amax, fabsf(v[i]));
+  }
+  const int E = mx_block_exponent(amax);
+  uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < 32; ++i) w[i >> 2] |= e4m3_code(ldexpf(v[i], -E)) << (8 * (i & 3));
+  const long row = half >= 0 ? (long)((n >> 7) << 8) + 128 * half + (n & 127) : (long)n;
+  uint8_t* out = dst + (long)e * dst_es + row * K + kb * 32;
+  *reinterpret_cast<uint4*>(out) = make_uint4(w[0], w[1], w[2], w[3]);
+  *reinterpret_cast<uint4*>(out + 16) = make_uint4(w[4], w[5], w[6], w[7]);
+  scale[(long)e * s_es + (long)kb * pitch + row] = (uint8_t)(E + 127);
+}
+
+// ---------------------------------------------------------------------------
+// MX grouped GEMM
+// ---------------------------------------------------------------------------
+namespace mf {
+
+constexpr int MX_BK = 64;                        // k per stage (64 code bytes per row)
+constexpr int SCALE_BYTES = 4096;                // per stage: A blocks 0,1 and B blocks 0,1
+constexpr int MSTAGE = STAGE + SCALE_BYTES;      // codes A, codes B, scales
+constexpr int MX_DMA_PER_STAGE = 9;              // 4 A + 4 B + 1 scale per wave
+
+typedef __attribute__((ext_vector_type(8))) int i32x8_t;
+
+struct MxPlan {
+  Plan a, b;
+  i32x4_t srs;       // this wave's scale resource (waves 0-1: A, 2-3: B)
+  uint32_t svoff;    // per-lane offset of the scale DMA
+  uint32_t spitch;   // bytes between consecutive K blocks of the scales
+  int sblk;          // K block inside the stage this wave loads (0 or 1)
+  int amis;          // A rows: tile row 0 sits amis bytes into the scale stage
+};
+
+// Fragment of 32 codes (two 16-byte chunks) of one row of a K-major stage.
+__device__ __forceinline__ i32x8_t fragq(const char* op, int rowblk, int lane) {
+  const int row = rowblk + (lane & 31), h = lane >> 5;
+  const uint4 lo = *reinterpret_cast<const uint4*>(op + km_off(row, h));
+  const uint4 hi = *reinterpret_cast<const uint4*>(op + km_off(row, h + 2));
+  i32x8_t r = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  return r;
+}
+
+struct MxFrags {
+  i32x8_t a[4], b[4];
+  int sa[4], sb[4];
+};
+
+template <bool DUAL>
+__device__ __forceinline__ void load_mx_frags(const char* smem, int kt, int wm, int wn, int lane,
+                                              int amis, MxFrags& F) {
+  const char* st = smem + (kt & (NST - 1)) * MSTAGE;
+  const char* As = st;
+  const char* Bs = st + OPB;
+  const uint8_t* Ss = reinterpret_cast<const uint8_t*>(st + STAGE);
+  const int h = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = wm * 128 + i * 32;
+    F.a[i] = fragq(As, row, lane);
+    F.sa[i] = Ss[h * 1024 + amis + row + (lane & 31)];
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int col = DUAL ? ((j >> 1) * 128 + wn * 64 + (j & 1) * 32) : (wn * 128 + j * 32);
+    F.b[j] = fragq(Bs, col, lane);
+    F.sb[j] = Ss[2048 + h * 1024 + col + (lane & 31)];
+  }
+}
+
+template <int I0>
+__device__ __forceinline__ void mx_mfma8(f32x16_t (&acc)[4][4], const MxFrags& F) {
+#pragma unroll
+  for (int i = I0; i < I0 + 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.b[j], F.a[i], acc[i][j], 0, 0,
+                                                                  0, F.sb[j], 0, F.sa[i]);
+}
+
+__device__ __forceinline__ void mx_issue(const MxPlan& P, int kt, uint32_t st_base, int wave) {
+  issue<false>(P.a, kt, st_base, wave);
+  issue<false>(P.b, kt, st_base + OPB, wave);
+  // the block offset goes into the per-lane offset, which the range check covers
+  const uint32_t voff = P.svoff + (uint32_t)(2 * kt + P.sblk) * P.spitch;
+  const uint32_t dst = st_base + STAGE + (wave >> 1) * 2048 + P.sblk * 1024;
+  dma16(P.srs, dst, voff, 0u);
+}
+
+__device__ __forceinline__ void mx_wait_stage(int st, int last_issued) {
+  const int after = last_issued - st;
+  if (after >= 3) wait_vmcnt<3 * MX_DMA_PER_STAGE>();
+  else if (after == 2) wait_vmcnt<2 * MX_DMA_PER_STAGE>();
+  else if (after == 1) wait_vmcnt<MX_DMA_PER_STAGE>();
+  else wait_vmcnt<0>();
+}
+
+// Ask the scheduler to alternate MFMAs and LDS reads in the current region.
+__device__ __forceinline__ void interleave_mx() {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+  }
+}
+
+template <int KIND>
+__global__ __launch_bounds__(NTHR, 1) void gemm_mx_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(1024))) char smem[NST * MSTAGE];
+  __shared__ Sched sch;
+  constexpr bool DUAL = KT<KIND>::BSP == BS_DUAL_N;
+  constexpr int BNT = DUAL ? BN / 2 : BN;
+  const int ntiles = sched_setup<BM, BNT>(g, sch);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const uint32_t lds0 = lds_u32(smem);
+  const uint8_t* A = static_cast<const uint8_t*>(g.a);
+  const uint8_t* B = static_cast<const uint8_t*>(g.b0);
+
+  for (int it = 0;; ++it) {
+    const int L = logical_tile(it);
+    if (L >= ntiles) break;
+    const Tile t = sched_decode<BM, BNT>(g, sch, L);
+    // rows of B for this tile: gate/up panels hold 256 rows per 128 f columns
+    const long brow0 = DUAL ? 2L * t.n0 : (long)t.n0;
+    const long brows = DUAL ? 2L * ((g.N + 127) / 128) * 128 : (long)g.N;
+    MxPlan P;
+    plan_km(P.a, A + (long)t.row0 * g.lda, ((long long)g.rows_total - t.row0) * g.lda, nullptr, 0,
+            1 << 30, g.lda / 2, wave, lane);
+    plan_km(P.b, B + (long)t.e * g.b_es + brow0 * g.ldb, (brows - brow0) * g.ldb, nullptr, 0,
+            1 << 30, g.ldb / 2, wave, lane);
+    P.sblk = wave & 1;
+    const int row_al = t.row0 & ~15;
+    P.amis = t.row0 - row_al;
+    if (wave < 2) {
+      P.srs = make_rsrc(g.sa, (long long)(g.K / 32) * g.sa_pitch);
+      P.svoff = (uint32_t)(row_al + lane * 16);
+      P.spitch = (uint32_t)g.sa_pitch;
+    } else {
+      P.srs = make_rsrc(g.sb + (long)t.e * g.sb_es, (long long)(g.K / 32) * g.sb_pitch);
+      P.svoff = (uint32_t)(brow0 + lane * 16);
+      P.spitch = (uint32_t)g.sb_pitch;
+    }
+
+    f32x16_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
+
+    const int nk = t.klen / MX_BK;
+#pragma unroll
+    for (int s = 0; s < NST; ++s)
+      if (s < nk) mx_issue(P, s, lds0 + s * MSTAGE, wave);
+    MxFrags F0, F1;
+    auto step = [&](int kt, MxFrags& cur, MxFrags& nxt) {
+      __builtin_amdgcn_s_waitcnt(kLgkm0);
+      mx_mfma8<0>(acc, cur);
+      const bool more = kt + 1 < nk;
+      if (more) mx_wait_stage(kt + 1, min(nk - 1, kt + NST - 1));
+      barrier();
+      if (kt + NST < nk) mx_issue(P, kt + NST, lds0 + (kt & (NST - 1)) * MSTAGE, wave);
+      if (more) load_mx_frags<DUAL>(smem, kt + 1, wm, wn, lane, P.amis, nxt);
+      mx_mfma8<2>(acc, cur);
+      interleave_mx();
+    };
+    if (nk > 0) {
+      mx_wait_stage(0, min(nk - 1, NST - 1));
+      barrier();
+      load_mx_frags<DUAL>(smem, 0, wm, wn, lane, P.amis, F0);
+    }
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+      step(kt, F0, F1);
+      step(kt + 1, F1, F0);
+    }
+    if (kt < nk) step(kt, F0, F1);
+    __builtin_amdgcn_s_waitcnt(kLgkm0);
+    barrier();
+    epilogue_lds<KIND>(g, t, smem + wave * 32768, acc, wm, wn, lane);
+    barrier();
+  }
+}
+
+}  // namespace mf
+
+namespace {
+const char* mx_name(int kind) {
+  switch (kind) {
+    case GK_MX_GATEUP: return "gemm_mx_fwd_gateup_swiglu";
+    case GK_MX_DOWN: return "gemm_mx_fwd_down";
+    case GK_MX_DGRAD_DOWN: return "gemm_mx_dgrad_down_swiglu_bwd";
+    case GK_MX_DGRAD_GATEUP: return "gemm_mx_dgrad_gateup";
+  }
+  return "gemm_mx";
+}
+
+template <int KIND>
+hipError_t launch_mx_kind(const GemmArgs& g, int num_cu, hipStream_t s) {
+  constexpr int BNT = (KT<KIND>::BSP == BS_DUAL_N) ? mf::BN / 2 : mf::BN;
+  const int E = g.offsets ? g.E : 1;
+  const long ub = ((long)g.rows_total / mf::BM + E) * ((g.N + BNT - 1) / BNT);
+  const int grid = (int)(ub < num_cu ? ub : (long)num_cu);
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL(mf::gemm_mx_kernel<KIND>, dim3(grid), dim3(mf::NTHR), 0, s, g);
+  note_launch(mx_name(KIND), s);
+  return hipGetLastError();
+}
+
+constexpr size_t kAl = 256;
+inline size_t al(size_t v) { return (v + kAl - 1) & ~(kAl - 1); }
+
+// Bump allocator over the caller's workspace.
+struct Carve {
+  char* base;
+  size_t used = 0;
+  template <typename T> T* take(size_t bytes) {
+    T* p = reinterpret_cast<T*>(base ? base + used : nullptr);
+    used += al(bytes);
+    return p;
+  }
+};
+
+#define MX_TRY(expr)                        \
+  do {                                      \
+    hipError_t e_ = (expr);                 \
+    if (e_ != hipSuccess) return e_;        \
+  } while (0)
+
+hipError_t quant_rows(const void* src, long nrows, int K, long src_ld, uint8_t* dst, long dst_ld,
+                      long col0, uint8_t* scale, long grows, long sg_stride, long pitch, int block0,
+                      hipStream_t s) {
+  if (nrows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(mx_quant_rows_kernel, dim3((unsigned)((nrows + 3) / 4)), dim3(256), 0, s,
+                     static_cast<const bf16_t*>(src), nrows, K, src_ld, dst, dst_ld, col0, scale,
+                     grows, sg_stride, pitch, block0);
+  note_launch("mx_quant_rows", s);
+  return hipGetLastError();
+}
+
+hipError_t quant_cols(const void* W, int E, int K, int N, uint8_t* dst, long dst_es, int half,
+                      uint8_t* scale, long s_es, long pitch, hipStream_t s) {
+  hipLaunchKernelGGL(mx_quant_cols_kernel, dim3((N + 255) / 256, K / 32, E), dim3(256), 0, s,
+                     static_cast<const bf16_t*>(W), K, N, dst, dst_es, half, scale, s_es, pitch);
+  note_launch("mx_quant_cols", s);
+  return hipGetLastError();
+}
+
+inline long pitch_rows(long R) { return (R + 15) / 16 * 16; }
+inline long fpanel(int f) { return (f + 127) / 128 * 128; }
+
+// Forward workspace pieces, in carving order.
+struct FwdWs {
+  uint8_t *wgu, *wgu_s, *wd, *wd_s, *aq, *aq_s;
+};
+FwdWs carve_fwd(void* ws, long long R, int d, int f, int E, size_t* total) {
+  Carve c{static_cast<char*>(ws)};
+  FwdWs w;
+  const long fp = fpanel(f), Rp = pitch_rows(R);
+  w.wgu = c.take<uint8_t>((size_t)E * 2 * fp * d);
+  w.wgu_s = c.take<uint8_t>((size_t)E * (d / 32) * 2 * fp);
+  w.wd = c.take<uint8_t>((size_t)E * d * f);
+  w.wd_s = c.take<uint8_t>((size_t)E * (f / 32) * d);
+  w.aq = c.take<uint8_t>((size_t)R * f);
+  w.aq_s = c.take<uint8_t>((size_t)(f / 32) * Rp);
+  if (total) *total = c.used;
+  return w;
+}
+
+struct BwdWs {
+  uint8_t *dysq, *dysq_s, *wd, *wd_s, *dhq, *dhq_s, *wgu, *wgu_s;
+};
+BwdWs carve_bwd(void* ws, long long R, int d, int f, int E, size_t* total) {
+  Carve c{static_cast<char*>(ws)};
+  BwdWs w;
+  const long Rp = pitch_rows(R);
+  w.dysq = c.take<uint8_t>((size_t)R * d);
+  w.dysq_s = c.take<uint8_t>((size_t)(d / 32) * Rp);
+  w.wd = c.take<uint8_t>((size_t)E * f * d);
+  w.wd_s = c.take<uint8_t>((size_t)E * (d / 32) * f);
+  w.dhq = c.take<uint8_t>((size_t)R * 2 * f);
+  w.dhq_s = c.take<uint8_t>((size_t)(2 * f / 32) * Rp);
+  w.wgu = c.take<uint8_t>((size_t)E * d * 2 * f);
+  w.wgu_s = c.take<uint8_t>((size_t)E * (2 * f / 32) * d);
+  if (total) *total = c.used;
+  return w;
+}
+}  // namespace
+
+hipError_t launch_grouped_gemm_mx(GemmKind kind, const GemmArgs& g, int num_cu, hipStream_t s) {
+  switch (kind) {
+    case GK_MX_GATEUP: return launch_mx_kind<GK_MX_GATEUP>(g, num_cu, s);
+    case GK_MX_DOWN: return launch_mx_kind<GK_MX_DOWN>(g, num_cu, s);
+    case GK_MX_DGRAD_DOWN: return launch_mx_kind<GK_MX_DGRAD_DOWN>(g, num_cu, s);
+    case GK_MX_DGRAD_GATEUP: return launch_mx_kind<GK_MX_DGRAD_GATEUP>(g, num_cu, s);
+    default: break;
+  }
+  return hipErrorInvalidValue;
+}
+
+long mx_scale_pitch(long long R) { return pitch_rows(R); }
+
+size_t mx_fwd_workspace(long long R, int d, int f, int E) {
+  size_t t = 0;
+  carve_fwd(nullptr, R, d, f, E, &t);
+  return t;
+}
+
+size_t mx_bwd_workspace(long long R, int d, int f, int E) {
+  size_t t = 0;
+  carve_bwd(nullptr, R, d, f, E, &t);
+  return t;
+}
+
+hipError_t launch_mx_dispatch_copy(const void* x, const int32_t* src_token, int R, int T, int d,
+                                   void* Xs, void* Xq, uint8_t* Xq_scale, hipStream_t s) {
+  if (R == 0) return hipSuccess;
+  hipLaunchKernelGGL(mx_dispatch_kernel, dim3((R + 3) / 4), dim3(256), 0, s,
+                     static_cast<const bf16_t*>(x), src_token, R, T, d, static_cast<bf16_t*>(Xs),
+                     static_cast<uint8_t*>(Xq), Xq_scale, pitch_rows(R));
+  note_launch("mx_dispatch_quant", s);
+  return hipGetLastError();
+}
+
+hipError_t mx_ffn_fwd(const void* Xq, const uint8_t* Xscale, const int32_t* offsets, int R, int d,
+                      int f, int E, const void* Wg, const void* Wu, const void* Wd, void* Hg,
+                      void* Hu, void* A, void* Ys, void* ws, int num_cu, hipStream_t s) {
+  const FwdWs w = carve_fwd(ws, R, d, f, E, nullptr);
+  const long fp = fpanel(f), Rp = pitch_rows(R);
+  // weights: Wg, Wu along d into the gate/up panels; Wd along f, transposed
+  MX_TRY(quant_cols(Wg, E, d, f, w.wgu, 2 * fp * d, 0, w.wgu_s, (d / 32) * 2 * fp, 2 * fp, s));
+  MX_TRY(quant_cols(Wu, E, d, f, w.wgu, 2 * fp * d, 1, w.wgu_s, (d / 32) * 2 * fp, 2 * fp, s));
+  MX_TRY(quant_cols(Wd, E, f, d, w.wd, (long)d * f, -1, w.wd_s, (long)(f / 32) * d, d, s));
+  GemmArgs g{};
+  g.E = E; g.offsets = offsets; g.rows_total = R; g.ragged = RAG_M;
+  g.N = f; g.K = d;
+  g.a = Xq; g.lda = d; g.sa = Xscale; g.sa_pitch = Rp;
+  g.b0 = w.wgu; g.ldb = d; g.b_es = 2 * fp * d;
+  g.sb = w.wgu_s; g.sb_es = (d / 32) * 2 * fp; g.sb_pitch = 2 * fp;
+  g.c0 = Hg; g.c1 = Hu; g.c2 = A; g.ldc = f;
+  MX_TRY(launch_grouped_gemm_mx(GK_MX_GATEUP, g, num_cu, s));
+  MX_TRY(quant_rows(A, R, f, f, w.aq, f, 0, w.aq_s, R > 0 ? R : 1, 0, Rp, 0, s));
+  GemmArgs h{};
+  h.E = E; h.offsets = offsets; h.rows_total = R; h.ragged = RAG_M;
+  h.N = d; h.K = f;
+  h.a = w.aq; h.lda = f; h.sa = w.aq_s; h.sa_pitch = Rp;
+  h.b0 = w.wd; h.ldb = f; h.b_es = (long)d * f;
+  h.sb = w.wd_s; h.sb_es = (long)(f / 32) * d; h.sb_pitch = d;
+  h.c0 = Ys; h.ldc = d;
+  return launch_grouped_gemm_mx(GK_MX_DOWN, h, num_cu, s);
+}
+
+hipError_t mx_ffn_dgrad(const void* dYs, const void* Hg, const void* Hu, const int32_t* offsets,
+                        int R, int d, int f, int E, const void* Wg, const void* Wu, const void* Wd,
+                        void* dH, void* dXs, void* ws, int num_cu, hipStream_t s) {
+  const BwdWs w = carve_bwd(ws, R, d, f, E, nullptr);
+  const long Rp = pitch_rows(R);
+  const long one = R > 0 ? R : 1;
+  // down dgrad: dYs and Wd along d
+  MX_TRY(quant_rows(dYs, R, d, d, w.dysq, d, 0, w.dysq_s, one, 0, Rp, 0, s));
+  MX_TRY(quant_rows(Wd, (long)E * f, d, d, w.wd, d, 0, w.wd_s, f, (long)(d / 32) * f, f, 0, s));
+  GemmArgs g{};
+  g.E = E; g.offsets = offsets; g.rows_total = R; g.ragged = RAG_M;
+  g.N = f; g.K = d;
+  g.a = w.dysq; g.lda = d; g.sa = w.dysq_s; g.sa_pitch = Rp;
+  g.b0 = w.wd; g.ldb = d; g.b_es = (long)f * d;
+  g.sb = w.wd_s; g.sb_es = (long)(d / 32) * f; g.sb_pitch = f;
+  g.c0 = dH; g.ldc = 2L * f; g.c_split = f;
+  g.h0 = Hg; g.h1 = Hu; g.ldh = f;
+  MX_TRY(launch_grouped_gemm_mx(GK_MX_DGRAD_DOWN, g, num_cu, s));
+  // gate/up dgrad: dH along 2f; Wg | Wu along f into one [d][2f] matrix per expert
+  MX_TRY(quant_rows(dH, R, 2 * f, 2L * f, w.dhq, 2L * f, 0, w.dhq_s, one, 0, Rp, 0, s));
+  MX_TRY(quant_rows(Wg, (long)E * d, f, f, w.wgu, 2L * f, 0, w.wgu_s, d, (long)(2 * f / 32) * d, d,
+                    0, s));
+  MX_TRY(quant_rows(Wu, (long)E * d, f, f, w.wgu, 2L * f, f, w.wgu_s, d, (long)(2 * f / 32) * d, d,
+                    f / 32, s));
+  GemmArgs h{};
+  h.E = E; h.offsets = offsets; h.rows_total = R; h.ragged = RAG_M;
+  h.N = d; h.K = 2 * f;
+  h.a = w.dhq; h.lda = 2L * f; h.sa = w.dhq_s; h.sa_pitch = Rp;
+  h.b0 = w.wgu; h.ldb = 2L * f; h.b_es = (long)d * 2 * f;
+  h.sb = w.wgu_s; h.sb_es = (long)(2 * f / 32) * d; h.sb_pitch = d;
+  h.c0 = dXs; h.ldc = d;
+  return launch_grouped_gemm_mx(GK_MX_DGRAD_GATEUP, h, num_cu, s);
+}
+
 }  // namespace moe

@@ -62,9 +62,9 @@ def run_gpu(wl: Workload, inp: Dict[str, np.ndarray], logits: Optional[np.ndarra
     layer.backward(dY)
     torch.cuda.synchronize()
     names = ["topk_idx", "topk_w", "counts", "offsets", "dest_row", "src_token", "Hg", "Hu",
-             "A", "Ys", "y", "dYs", "dw", "dH", "dXs", "dx", "dWg", "dWu", "dWd"]
-    if wl.prec != "mxfp8":
-        names.append("Xs")
+             "A", "Ys", "y", "dYs", "dw", "dH", "dXs", "dx", "dWg", "dWu", "dWd", "Xs"]
+    if wl.prec == "mxfp8":
+        names += ["Xq", "Xq_scale"]
     if router:
         names += ["logits", "dlogits", "dWr"]
     out = {n: to_np(getattr(layer, n)) for n in names}

@@ -80,6 +80,15 @@ def test_workspace_sizes(L):
     assert ws_size(L, 1, 8, 64, 8, 128, 2, BF16, 7)[0] == DTYPE
     assert ws_size(L, 99, 8, 64, 8, 128, 2, BF16, P_BF16)[0] == SHAPE
     assert L.moe_workspace_size(1, 8, 64, 8, 128, 2, BF16, P_BF16, None) == NULL
+    # MXFP8: quantised copies of the three weights (1 byte per element, one
+    # scale byte per 32) plus the quantised activations of the second GEMM
+    T, d, E, f, k = 8192, 2048, 64, 1024, 8
+    R = T * k
+    s, n = ws_size(L, 2, T, d, E, f, k, BF16, P_MX)
+    assert s == OK and 3 * E * d * f * 33 // 32 + R * f * 33 // 32 <= n <= 3 * E * d * f * 1.1 + R * f * 1.1
+    s, n = ws_size(L, 5, T, d, E, f, k, BF16, P_MX)
+    assert s == OK and 3 * E * d * f * 33 // 32 + R * (d + 2 * f) * 33 // 32 <= n
+    assert ws_size(L, 2, T, d, E, f, k, F32, P_MX)[0] == DTYPE
 
 
 def route(L, x=A, Wr=A, T=16, d=64, E=8, k=2, dt=BF16, flags=0, lg=A, idx=A, w=A):
@@ -100,8 +109,9 @@ def test_route_validation(L):
     assert route(L, idx=MIS) == ALIGN
 
 
-def dispatch(L, T=16, d=64, E=8, k=2, dt=BF16, prec=P_BF16, ws=A, wsb=1 << 20, xs=A, sc=A, x=A):
-    return L.moe_dispatch(x, A, T, d, E, k, dt, prec, A, A, A, A, xs, sc, ws, wsb, None)
+def dispatch(L, T=16, d=64, E=8, k=2, dt=BF16, prec=P_BF16, ws=A, wsb=1 << 20, xs=A, xq=A, sc=A,
+             x=A):
+    return L.moe_dispatch(x, A, T, d, E, k, dt, prec, A, A, A, A, xs, xq, sc, ws, wsb, None)
 
 
 def test_dispatch_validation(L):
@@ -112,6 +122,10 @@ def test_dispatch_validation(L):
     assert dispatch(L, d=100) == UNSUP
     assert dispatch(L, x=MIS) == ALIGN
     assert dispatch(L, wsb=2 * 256 - 1) == WS
+    assert dispatch(L, prec=P_MX, xq=None) == NULL      # MXFP8 needs the codes
+    assert dispatch(L, prec=P_MX, sc=None) == NULL      # ... and the scales
+    assert dispatch(L, prec=P_MX, sc=MIS) == ALIGN
+    assert dispatch(L, prec=P_MX, dt=F32) == DTYPE
 
 
 def ffn_fwd(L, T=16, k=2, d=64, f=64, E=8, dt=BF16, prec=P_BF16, Xs=A, Wg=A):
@@ -128,13 +142,15 @@ def test_ffn_fwd_validation(L):
     assert ffn_fwd(L, E=257) == UNSUP
 
 
-def ffn_bwd(L, Xs=A, x=A, src=A, dt=BF16, prec=P_BF16, f=64, dH=A):
-    return L.moe_grouped_ffn_bwd(A, Xs, x, src, A, A, A, A, 16, 2, 64, f, 8, A, A, A, dt, prec,
-                                 0, dH, A, A, A, A, A, 1 << 20, None)
+def ffn_bwd(L, Xs=A, dt=BF16, prec=P_BF16, f=64, dH=A, ws=A):
+    return L.moe_grouped_ffn_bwd(A, Xs, A, A, A, A, 16, 2, 64, f, 8, A, A, A, dt, prec,
+                                 0, dH, A, A, A, A, ws, 1 << 20, None)
 
 
 def test_ffn_bwd_validation(L):
-    assert ffn_bwd(L, Xs=None) == NULL             # bf16 needs the dispatched rows
+    assert ffn_bwd(L, Xs=None) == NULL             # the weight gradients read Xs
+    assert ffn_bwd(L, Xs=None, prec=P_MX) == NULL
+    assert ffn_bwd(L, ws=None, prec=P_MX) == NULL  # MXFP8 quantises into the workspace
     assert ffn_bwd(L, dH=None) == NULL
     assert ffn_bwd(L, f=32) == UNSUP
     assert ffn_bwd(L, dH=MIS) == ALIGN
