@@ -44,6 +44,8 @@ def gemm_flops(name: str, wl) -> float:
         "gemm_wgrad_gateup": 4.0 * d * f,           # Xs^T . [dHg|dHu]
         "gemm_wgrad_down": 2.0 * f * d,             # A^T . dYs
     }
+    if name.startswith("gemm_mx_"):
+        name = "gemm_" + name[len("gemm_mx_"):]
     if name in per_row:
         return per_row[name] * R
     if name in ("gemm_router_logits", "gemm_router_dwr", "gemm_router_dx"):
@@ -165,10 +167,13 @@ def main(argv=None) -> int:
     dom_name, dom_launch_ms = dom[0], dom[3]
     dom_flops = gemm_flops(dom_name, wl)
     peak = PEAK_TFLOPS[wl.prec]
+    # a kernel is priced at the peak of its own operand type: the scaled fp8
+    # GEMMs at the fp8 peak, the rest (bf16 weight gradients, router) at bf16
+    dom_peak = PEAK_TFLOPS["mxfp8" if dom_name.startswith("gemm_mx_") else wl.dtype]
     if dom_flops > 0:
         ach = dom_flops / (dom_launch_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "kernel": dom_name, "achieved": round(ach, 2), "peak": peak,
-                "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": None,
+        roof = {"bound": "mfma", "kernel": dom_name, "achieved": round(ach, 2), "peak": dom_peak,
+                "unit": "TFLOP/s", "frac": round(ach / dom_peak, 4), "traffic": None,
                 "per_launch_ms": round(dom_launch_ms, 4),
                 "algorithmic_flops_per_launch": dom_flops}
     else:

@@ -92,7 +92,7 @@ inline size_t dispatch_ws(int T, int E) {
 }
 
 // Width of the bf16 copy of dlogits: E rounded up to the MFMA engine's K step.
-inline int router_ld16(int E) { return (E + 31) / 32 * 32; }
+inline int router_ld16(int E) { return (E + 63) / 64 * 64; }
 
 inline int gemm_engine(int dtype, int router_E = 8) {
   if (dtype == MOE_F32) return GEMM_F32_SIMT;

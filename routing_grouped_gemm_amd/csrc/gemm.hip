@@ -7,10 +7,12 @@
 //
 // bf16 engine: persistent workgroups of 256 threads (4 waves, one per SIMD)
 // walk a tile list over the ragged expert segments.  Tiles are 256x256
-// outputs with a K step of 32 through a 4-stage LDS ring (128 KiB).  Each
+// outputs with a K step of 64 through two 64 KiB LDS stages; the next
+// tile's first stage loads while the current tile's epilogue runs.  Each
 // stage of both operands arrives by buffer->LDS DMA (16 bytes per lane, no
-// register staging); the ring keeps three stages in flight.  Operands that
-// are K-contiguous in HBM sit in LDS as rows of 32 k; operands that are
+// register staging); one stage is in flight while the other is consumed.
+// Operands that are K-contiguous in HBM sit in LDS as rows of 64 k (whole
+// 128-byte lines); operands that are
 // contiguous along M or N (the weights in the forward GEMMs, both operands of
 // the weight gradient) sit as rows of k and are read transposed by
 // ds_read_b64_tr_b16.  Each wave owns a 128x128 sub-tile as 4x4 MFMA
@@ -33,6 +35,7 @@ template <int KIND>
 __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) char smem[NST * STAGE];
   __shared__ Sched sch;
+  __shared__ __attribute__((aligned(256))) uint32_t pf_sink[64];
   constexpr bool DUAL = KT<KIND>::BSP == BS_DUAL_N;
   constexpr bool AMN = !KT<KIND>::AK, BMN = !KT<KIND>::BK_;
   constexpr int BNT = DUAL ? BN / 2 : BN;
@@ -41,72 +44,113 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(GemmArgs g) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform in the wave
   const int wm = wave >> 1, wn = wave & 1;
-  const uint32_t lds0 = lds_u32(smem);
+  const uint32_t lds0 = lds_u32(smem), sink = lds_u32(pf_sink);
+  // L2 prefetch of the K-contiguous operands (waves 0-1: A, 2-3: B); an
+  // operand that is contiguous along M or N is not prefetched, as measured
+  // prefetching it slows the kernel down.
+  const bool pf_on = (wave < 2) ? !AMN : !BMN;
+  const Pf pf = plan_pf_km((wave < 2 ? g.lda : g.ldb) * 2, wave, lane);
+  // DMA of stage s, then the prefetch of stage s + PF_AHEAD (issued even past
+  // the last stage, where it touches no memory or a line of another row, so
+  // that every stage adds the same number of loads to vmcnt)
+  auto issue_stage = [&](const Plan& qa, const Plan& qb, int s) {
+    issue<AMN>(qa, s, lds0 + (s & 1) * STAGE, wave);
+    issue<BMN>(qb, s, lds0 + (s & 1) * STAGE + OPB, wave);
+    if constexpr (!AMN) {
+      if (wave < 2) issue_pf<false>(qa, pf, s + PF_AHEAD, sink, wave);
+    }
+    if constexpr (!BMN) {
+      if (wave >= 2) issue_pf<false>(qb, pf, s + PF_AHEAD, sink, wave);
+    }
+  };
 
-  for (int it = 0;; ++it) {
-    const int L = logical_tile(it);
-    if (L >= ntiles) break;
-    const Tile t = sched_decode<BM, BNT>(g, sch, L);
-    Plan pa, pb;
-    plan_tile<KIND>(g, t, wave, lane, pa, pb);
+  int it = 0;
+  int L = logical_tile(it);
+  if (L >= ntiles) return;
+  Tile t = sched_decode<BM, BNT>(g, sch, L);
+  Plan pa, pb;
+  plan_tile<KIND>(g, t, wave, lane, pa, pb);
+  int nk = (t.klen + BK - 1) / BK;
+  if (nk > 0) issue_stage(pa, pb, 0);
+  if (nk > 1) issue_stage(pa, pb, 1);
 
+  for (;;) {
+    // Stages 0 and 1 of tile t are in flight (as far as they exist).
     f32x16_t acc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
 
-    // Ring of NST = 4 buffers, prefetch distance 4.  Stage kt's two k16 steps
-    // use fragment sets F0 (step 0) and F1 (step 1).  F1 is read while the
-    // MFMAs of F0 run; then every wave has finished reading stage kt, and one
-    // barrier both publishes stage kt+1 (each wave waited for its own DMA) and
-    // frees stage kt's buffer for stage kt+4.  The MFMAs of F1 then run while
-    // F0 of stage kt+1 is read.
-    const int nk = (t.klen + BK - 1) / BK;
-#pragma unroll
-    for (int s = 0; s < NST; ++s)
-      if (s < nk) {
-        issue<AMN>(pa, s, lds0 + s * STAGE, wave);
-        issue<BMN>(pb, s, lds0 + s * STAGE + OPB, wave);
-      }
+    // Two stage buffers; stage kt+1 loads while stage kt is consumed in four
+    // k16 steps with alternating fragment sets F0 / F1: the fragments of
+    // step s+1 are read while the MFMAs of step s run.  After the reads of
+    // step 3, one barrier publishes stage kt+1 (each wave waited for its own
+    // DMA) and frees stage kt's buffer for stage kt+2, whose DMA then runs
+    // under the MFMAs of step 3 and of the whole of stage kt+1.
     bf16x8_t fa0[4], fb0[4], fa1[4], fb1[4];
     if (nk > 0) {
-      wait_stage(0, min(nk - 1, NST - 1));
+      // stage 1 and both prefetches may still be in flight
+      if (nk <= 1) wait_vmcnt<0>();
+      else if (pf_on) wait_vmcnt<DMA_PER_OP * 2 + 2 * PF_PER_STAGE>();
+      else wait_vmcnt<DMA_PER_OP * 2>();
       barrier();
       load_frags<AMN, BMN, DUAL>(smem, 0, 0, wm, wn, lane, fa0, fb0);
     }
     for (int kt = 0; kt < nk; ++kt) {
-      // F0 was read a whole phase ago: this wait is nearly free, and it lets
-      // the compiler issue F0's MFMAs without waiting on the F1 reads that
-      // are interleaved with them (lgkmcnt cannot count all 16 reads of a set).
       __builtin_amdgcn_s_waitcnt(kLgkm0);
       load_frags<AMN, BMN, DUAL>(smem, kt, 1, wm, wn, lane, fa1, fb1);
       mfma16(acc, fa0, fb0);
       interleave_mfma_ds();
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(kLgkm0);
+      load_frags<AMN, BMN, DUAL>(smem, kt, 2, wm, wn, lane, fa0, fb0);
+      mfma16(acc, fa1, fb1);
+      interleave_mfma_ds();
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(kLgkm0);
+      load_frags<AMN, BMN, DUAL>(smem, kt, 3, wm, wn, lane, fa1, fb1);
+      mfma16(acc, fa0, fb0);
+      interleave_mfma_ds();
+      __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_waitcnt(kLgkm0);
       const bool more = kt + 1 < nk;
-      if (more) wait_stage(kt + 1, min(nk - 1, kt + NST - 1));
-      barrier();
-      if (kt + NST < nk) {
-        const uint32_t nb = lds0 + (kt & (NST - 1)) * STAGE;
-        issue<AMN>(pa, kt + NST, nb, wave);
-        issue<BMN>(pb, kt + NST, nb + OPB, wave);
+      // stage kt+1 has landed once only its prefetch loads may be pending
+      if (more) {
+        if (pf_on) wait_vmcnt<PF_PER_STAGE>(); else wait_vmcnt<0>();
       }
+      barrier();
+      if (kt + 2 < nk) issue_stage(pa, pb, kt + 2);
       if (more) load_frags<AMN, BMN, DUAL>(smem, kt + 1, 0, wm, wn, lane, fa0, fb0);
       mfma16(acc, fa1, fb1);
       interleave_mfma_ds();
+      __builtin_amdgcn_sched_barrier(0);
     }
-    // every wave is done reading the ring before the next tile refills it
+    // every wave is done reading the ring
+    __builtin_amdgcn_s_waitcnt(kLgkm0);
     barrier();
 
-    // Epilogue through LDS.  The ring is idle now: each wave takes a private
-    // 32 KiB slice and, for each half of its 128 rows, writes its float32
-    // accumulators there straight from the accumulator registers, then reads
-    // back 8 consecutive columns of a row per lane and applies the epilogue
-    // with 16-byte global accesses.
-    epilogue_lds<KIND>(g, t, smem + wave * 32768, acc, wm, wn, lane);
-    // the slices are ring buffers of the next tile
+    // The next tile's stage 0 loads into buffer 0 while this tile's epilogue
+    // stages through buffer 1 (one 16 KiB slice per wave); its stage 1
+    // follows once the slices are read.  Loads complete in order, so the
+    // stage waits of the next tile stay exact whatever the epilogue's own
+    // global accesses do.
+    L = logical_tile(++it);
+    const bool has_next = L < ntiles;
+    Tile tn = t;
+    Plan pan = pa, pbn = pb;
+    int nkn = 0;
+    if (has_next) {
+      tn = sched_decode<BM, BNT>(g, sch, L);
+      plan_tile<KIND>(g, tn, wave, lane, pan, pbn);
+      nkn = (tn.klen + BK - 1) / BK;
+      if (nkn > 0) issue_stage(pan, pbn, 0);
+    }
+    epilogue_lds<KIND>(g, t, smem + STAGE + wave * EPI_SLICE, acc, wm, wn, lane);
     barrier();
+    if (!has_next) break;
+    if (nkn > 1) issue_stage(pan, pbn, 1);
+    t = tn; pa = pan; pb = pbn; nk = nkn;
   }
 }
 

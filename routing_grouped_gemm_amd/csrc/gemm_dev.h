@@ -272,14 +272,20 @@ __device__ __forceinline__ void epilogue4(const GemmArgs& g, const Tile& t, int 
 }
 
 // ---------------------------------------------------------------------------
-// bf16 MFMA engine
+// MFMA engines (bf16 and MXFP8): shared stage ring
 // ---------------------------------------------------------------------------
 namespace mf {
 
-constexpr int BM = 256, BN = 256, BK = 32, NST = 4, NTHR = 256;
-constexpr int OPB = BM * BK * 2;    // bytes of one operand in one stage (16 KiB)
-constexpr int STAGE = 2 * OPB;      // A then B
-constexpr int DMA_PER_STAGE = 8;    // buffer->LDS loads per wave per stage (4 per operand)
+// Tiles of 256x256 outputs; each stage holds 128 bytes of K for every tile
+// row of both operands (64 bf16 or 128 e4m3 values): K-contiguous rows are
+// fetched as whole 128-byte lines, which the buffer->LDS path moves about
+// twice as fast as half lines.  Two stages (128 KiB) double-buffer the ring.
+constexpr int BM = 256, BN = 256, NST = 2, NTHR = 256;
+constexpr int ROWB = 128;             // bytes of K per tile row per stage
+constexpr int BK = ROWB / 2;          // bf16 elements of K per stage
+constexpr int OPB = BM * ROWB;        // bytes of one operand in one stage (32 KiB)
+constexpr int STAGE = 2 * OPB;        // A then B
+constexpr int DMA_PER_OP = 8;         // buffer->LDS loads per wave per operand per stage
 
 typedef __attribute__((ext_vector_type(4))) int i32x4_t;
 typedef __attribute__((ext_vector_type(4))) short i16x4_t;
@@ -300,8 +306,8 @@ __device__ __forceinline__ i32x4_t make_rsrc(const void* base, long long bytes) 
 
 // 16 bytes per lane from the buffer straight into LDS at lds_addr + 16*lane.
 // Issued as inline asm so that the compiler's LDS-DMA tracking does not turn
-// the ring's partial waits into full ones; completion is awaited explicitly
-// with vmcnt before the barrier of the stage that reads the data.
+// the ring's waits into full ones; completion is awaited explicitly with
+// vmcnt before the barrier of the stage that reads the data.
 __device__ __forceinline__ void dma16(i32x4_t rsrc, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
   i32x4_t r;
   r.x = __builtin_amdgcn_readfirstlane(rsrc.x);
@@ -324,75 +330,73 @@ __device__ __forceinline__ uint32_t lds_u32(const void* p) {
   return (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)p);
 }
 
-// LDS layouts of one operand stage (16 KiB), in 16-byte chunks.
-//  K-major ("KM": rows are M or N, 32 contiguous k per row = 64 B = 4 chunks):
-//    byte = row*64 + ((chunk ^ km_swz(row)) << 4)
-//  MN-major ("MN": rows are k, two panels of 128 contiguous columns):
-//    byte = panel*8192 + k*256 + (((col/8) ^ mn_swz(k)) << 4) + 2*(col & 7)
-// The swizzles make every fragment read conflict-free whether the LDS serves
-// 128 or 256 bytes per clock: a ds_read_b128 fragment touches 16 consecutive
-// rows at one chunk (km_swz gives each residue of row mod 4 all four
-// chunks), a ds_read_b64_tr_b16 pair touches 4 k-rows x 4 chunks (mn_swz
-// spreads them over 16 distinct chunk slots, and over 8 for any 16 lanes).
-__device__ __forceinline__ int km_swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+// LDS layouts of one operand stage (32 KiB), in 16-byte chunks.
+//  K-major ("KM": rows are M or N, 128 bytes of K per row = 8 chunks):
+//    byte = row*128 + ((chunk ^ km_swz(row)) << 4)
+//  MN-major ("MN": rows are k (64 of them), two panels of 128 columns):
+//    byte = panel*16384 + k*256 + (((col/8) ^ mn_swz(k)) << 4) + 2*(col & 7)
+// Both swizzles were chosen by measuring the LDS bank-conflict counter on
+// gfx950 for the fragment reads below (32 rows x one chunk per half-wave
+// with ds_read_b128; 4 k-rows x 4 column quads per 16 lanes with
+// ds_read_b64_tr_b16): both read conflict-free.
+__device__ __forceinline__ int km_swz(int row) { return (row >> 1) & 7; }
 __device__ __forceinline__ int mn_swz(int k) { return (4 * (k & 3)) ^ (2 * ((k >> 1) & 1)); }
 __device__ __forceinline__ int km_off(int row, int chunk) {
-  return row * 64 + ((chunk ^ km_swz(row)) << 4);
+  return row * ROWB + ((chunk ^ km_swz(row)) << 4);
 }
 __device__ __forceinline__ int mn_off(int k, int col) {
   const int panel = col >> 7, cc = col & 127;
-  return panel * 8192 + k * 256 + (((cc >> 3) ^ mn_swz(k)) << 4) + 2 * (cc & 7);
+  return panel * 16384 + k * 256 + (((cc >> 3) ^ mn_swz(k)) << 4) + 2 * (cc & 7);
 }
 
-// Per-wave DMA plan of one operand for one tile.
+// Per-wave DMA plan of one operand for one tile.  Block i of the wave reads
+// at per-lane offset (i odd ? v1 : v0) plus the uniform offset i*bstep plus
+// the stage's K offset; both uniform parts travel in the instruction's
+// scalar offset, which the buffer range check includes.
 struct Plan {
   i32x4_t rs0, rs1;   // resources (rs1: second source: SPLIT_K, or MN panel of waves 2-3)
-  uint32_t voff[4];   // per-lane byte offsets of the wave's four 1 KiB blocks
-  uint32_t lds[4];    // LDS offsets of those blocks inside the operand stage
-  uint32_t kstep;     // bytes the source advances per stage (BK elements along K)
+  uint32_t v0, v1;    // per-lane byte offsets of the wave's even / odd blocks
+  uint32_t bstep;     // bytes between consecutive blocks of the wave
+  uint32_t kstep;     // bytes the source advances per stage
   int split_stage;    // SPLIT_K: first stage read from rs1 (else a large value)
 };
+// LDS offset of the wave's i-th block inside the operand stage.
+__device__ __forceinline__ uint32_t plan_lds(int wave, int i) { return (uint32_t)(wave * DMA_PER_OP + i) * 1024u; }
 
-// K-major operand: rows r of the tile are rows of a matrix with ld elements,
-// starting at `base`; `bytes` are readable from base.
+// K-major operand: row r of the tile is a row of `ldb` bytes at base + r*ldb;
+// `bytes` are readable from base.  Block blk = wave*8 + i holds rows
+// 8*blk .. 8*blk+7, 128 bytes each; the swizzle of a row depends only on the
+// parity of its block and on the lane.
 __device__ __forceinline__ void plan_km(Plan& P, const void* base, long long bytes, const void* base1,
-                                        long long bytes1, int split_stage, long ld, int wave,
+                                        long long bytes1, int split_stage, long ldb, int wave,
                                         int lane) {
   P.rs0 = make_rsrc(base, bytes);
   P.rs1 = make_rsrc(base1 ? base1 : base, base1 ? bytes1 : bytes);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int blk = wave * 4 + i;
-    const int row = blk * 16 + (lane >> 2);
-    const int c = (lane & 3) ^ km_swz(row);
-    P.voff[i] = (uint32_t)(row * ld * 2 + c * 16);
-    P.lds[i] = blk * 1024;
-  }
-  P.kstep = BK * 2;
+  const int row0 = wave * DMA_PER_OP * 8 + (lane >> 3);
+  P.v0 = (uint32_t)(row0 * ldb + (((lane & 7) ^ km_swz(row0)) * 16));
+  P.v1 = (uint32_t)(row0 * ldb + (((lane & 7) ^ km_swz(row0 + 8)) * 16));
+  P.bstep = (uint32_t)(8 * ldb);
+  P.kstep = ROWB;
   P.split_stage = split_stage;
 }
 
-// MN-major operand: k-rows of a matrix with ld elements; panel p of the tile
-// starts at base_p (its column 0 at k = 0); bytes_p readable from base_p.
+// MN-major operand (bf16): k-rows of a matrix with ld elements; panel p of
+// the tile starts at base_p (its column 0 at k = 0); bytes_p readable from
+// base_p.  Blocks 0-15 fill panel 0 (waves 0-1), 16-31 panel 1 (waves 2-3);
+// block blk holds k-rows 4*(blk%16) .. +3, 256 bytes each.
 __device__ __forceinline__ void plan_mn(Plan& P, const void* base0, long long bytes0,
                                         const void* base1, long long bytes1, long ld, int wave,
                                         int lane) {
   P.rs0 = make_rsrc(base0, bytes0);
   P.rs1 = make_rsrc(base1, bytes1);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int blk = wave * 4 + i;   // blocks 0-7: panel 0, 8-15: panel 1
-    const int rb = blk & 7;
-    const int k = rb * 4 + (lane >> 4);
-    const int c = (lane & 15) ^ mn_swz(k);
-    P.voff[i] = (uint32_t)(k * ld * 2 + c * 16);
-    P.lds[i] = (blk >> 3) * 8192 + rb * 1024;
-  }
+  const int k0 = (wave & 1) * DMA_PER_OP * 4 + (lane >> 4);
+  P.v0 = P.v1 = (uint32_t)(k0 * ld * 2 + (((lane & 15) ^ mn_swz(k0)) * 16));
+  P.bstep = (uint32_t)(4 * ld * 2);
   P.kstep = (uint32_t)(BK * ld * 2);
   P.split_stage = 1 << 30;
 }
 
-// Issue the wave's four DMA blocks of one operand for stage kt into the LDS
+// Issue the wave's DMA blocks of one operand for stage kt into the LDS
 // operand region at lds_base.
 template <bool MN>
 __device__ __forceinline__ void issue(const Plan& P, int kt, uint32_t lds_base, int wave) {
@@ -406,13 +410,52 @@ __device__ __forceinline__ void issue(const Plan& P, int kt, uint32_t lds_base, 
     rs = second ? P.rs1 : P.rs0;
     soff = (uint32_t)(second ? kt - P.split_stage : kt) * P.kstep;
   }
-  soff = __builtin_amdgcn_readfirstlane(soff);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) dma16(rs, lds_base + P.lds[i], P.voff[i], soff);
+  for (int i = 0; i < DMA_PER_OP; ++i)
+    dma16(rs, lds_base + plan_lds(wave, i), (i & 1) ? P.v1 : P.v0, soff + (uint32_t)i * P.bstep);
+}
+
+// L2 prefetch: one 4-byte buffer->LDS load per 128-byte line of a future
+// stage pulls the line into L2 (the bytes land in a scratch word that is
+// never read), so that the stage's own DMA, issued two stages later, hits in
+// L2 instead of waiting on HBM.  Each wave covers 128 lines of one operand
+// (waves 0-1: A, 2-3: B) with two loads.
+__device__ __forceinline__ void pf4(i32x4_t rsrc, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
+  i32x4_t r;
+  r.x = __builtin_amdgcn_readfirstlane(rsrc.x);
+  r.y = __builtin_amdgcn_readfirstlane(rsrc.y);
+  r.z = __builtin_amdgcn_readfirstlane(rsrc.z);
+  r.w = __builtin_amdgcn_readfirstlane(rsrc.w);
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr);
+  const uint32_t so = __builtin_amdgcn_readfirstlane(soff);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               :: "s"(m0), "v"(voff), "s"(r), "s"(so) : "memory");
+}
+constexpr int PF_PER_STAGE = 2;   // prefetch loads per wave per stage
+constexpr int PF_AHEAD = 2;       // stages between a line's prefetch and its DMA
+
+struct Pf {
+  uint32_t v[2];
+};
+// K-major operand: rows (wave&1)*128 + 64i + lane, one line each.
+__device__ __forceinline__ Pf plan_pf_km(long ldb, int wave, int lane) {
+  Pf f;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) f.v[i] = (uint32_t)(((wave & 1) * 128 + 64 * i + lane) * ldb);
+  return f;
+}
+template <bool MN>
+__device__ __forceinline__ void issue_pf(const Plan& P, const Pf& f, int kt, uint32_t sink, int wave) {
+  static_assert(!MN, "only K-contiguous operands are prefetched");
+  const bool second = kt >= P.split_stage;
+  const i32x4_t rs = second ? P.rs1 : P.rs0;
+  const uint32_t soff = (uint32_t)(second ? kt - P.split_stage : kt) * P.kstep;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) pf4(rs, sink, f.v[i], soff);
 }
 
 // MFMA fragment (8 consecutive k of one row/column) from an operand stage.
-// row: M or N index inside the tile; s: k16 step inside the stage.
+// row: M or N index inside the tile; s: k16 step inside the stage (0-3).
 template <bool MN>
 __device__ __forceinline__ bf16x8_t frag(const char* op, int rowblk, int s, int lane) {
   if constexpr (!MN) {
@@ -472,16 +515,7 @@ __device__ __forceinline__ void interleave_mfma_ds() {
   }
 }
 
-// Wait until stage st has landed, given that stages up to last_issued are in flight.
-__device__ __forceinline__ void wait_stage(int st, int last_issued) {
-  const int after = last_issued - st;
-  if (after >= 3) wait_vmcnt<3 * DMA_PER_STAGE>();
-  else if (after == 2) wait_vmcnt<2 * DMA_PER_STAGE>();
-  else if (after == 1) wait_vmcnt<DMA_PER_STAGE>();
-  else wait_vmcnt<0>();
-}
-
-// Operand plans of one tile for each GEMM kind.
+// Operand plans of one tile for each bf16 GEMM kind.
 template <int KIND>
 __device__ __forceinline__ void plan_tile(const GemmArgs& g, const Tile& t, int wave, int lane,
                                           Plan& pa, Plan& pb) {
@@ -494,7 +528,7 @@ __device__ __forceinline__ void plan_tile(const GemmArgs& g, const Tile& t, int 
     // rows t.row0.. of A (global rows), K contiguous
     const bf16_t* base = A + (long)t.row0 * g.lda;
     const long long bytes = ((long long)g.rows_total - t.row0) * g.lda * 2;
-    plan_km(pa, base, bytes, nullptr, 0, 1 << 30, g.lda, wave, lane);
+    plan_km(pa, base, bytes, nullptr, 0, 1 << 30, g.lda * 2, wave, lane);
   } else {
     // k-rows t.row0 .. t.row0 + klen of A, M contiguous; columns t.m0 + 128 p
     const bf16_t* b0 = A + (long)t.row0 * g.lda + t.m0;
@@ -507,9 +541,9 @@ __device__ __forceinline__ void plan_tile(const GemmArgs& g, const Tile& t, int 
     const long e_off = (long)t.e * g.b_es + (long)t.n0 * g.ldb;
     const long long bytes = ((long long)g.N - t.n0) * g.ldb * 2;
     if constexpr (BSP == BS_SPLIT_K)
-      plan_km(pb, B0 + e_off, bytes, B1 + e_off, bytes, g.b_split / BK, g.ldb, wave, lane);
+      plan_km(pb, B0 + e_off, bytes, B1 + e_off, bytes, g.b_split / BK, g.ldb * 2, wave, lane);
     else
-      plan_km(pb, B0 + e_off, bytes, nullptr, 0, 1 << 30, g.ldb, wave, lane);
+      plan_km(pb, B0 + e_off, bytes, nullptr, 0, 1 << 30, g.ldb * 2, wave, lane);
   } else if (g.ragged == RAG_M) {
     // B[k][n] per group (weights), N contiguous
     const bf16_t* w0 = B0 + (long)t.e * g.b_es;
@@ -529,9 +563,10 @@ __device__ __forceinline__ void plan_tile(const GemmArgs& g, const Tile& t, int 
   }
 }
 
-// Float32 staging slice of one wave: 64 rows x 128 columns, 16-byte chunks
-// XOR-swizzled by row so that both the accumulator writes (32 rows, one
-// chunk) and the row reads (one row, 16 chunks) avoid bank conflicts.
+// Float32 staging slice of one wave: 32 rows x 128 columns (16 KiB), 16-byte
+// chunks XOR-swizzled by row so that both the accumulator writes (32 rows,
+// one chunk) and the row reads (one row, 16 chunks) avoid bank conflicts.
+constexpr int EPI_SLICE = 16384;
 __device__ __forceinline__ int stage_off(int r, int chunk) { return r * 512 + ((chunk ^ (r & 31)) << 4); }
 
 // Epilogue of one 8-column piece: v = tile values (gate for the SwiGLU
@@ -586,41 +621,42 @@ __device__ __forceinline__ void epi8(const GemmArgs& g, const Tile& t, long row,
   }
 }
 
+// Epilogue of a wave's 128x128 accumulator sub-tile through its private
+// 16 KiB slice, one 32-row block at a time: the accumulators go to the slice
+// straight from the accumulator registers, then each lane reads back 8
+// consecutive columns of a row and applies the epilogue with 16-byte global
+// accesses.
 template <int KIND>
 __device__ __forceinline__ void epilogue_lds(const GemmArgs& g, const Tile& t, char* slice,
                                              f32x16_t (&acc)[4][4], int wm, int wn, int lane) {
   constexpr int EPI = KT<KIND>::EPI;
   constexpr bool DUAL = KT<KIND>::BSP == BS_DUAL_N;
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    // accumulators of row blocks i = 2h, 2h+1 into the slice
+  for (int i = 0; i < 4; ++i) {
 #pragma unroll
-    for (int ii = 0; ii < 2; ++ii)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int grp = 0; grp < 4; ++grp) {
-          const int r = ii * 32 + (lane & 31);
-          const int chunk = j * 8 + 2 * grp + (lane >> 5);
-          f32x4_t v = {acc[2 * h + ii][j][4 * grp], acc[2 * h + ii][j][4 * grp + 1],
-                       acc[2 * h + ii][j][4 * grp + 2], acc[2 * h + ii][j][4 * grp + 3]};
-          *reinterpret_cast<f32x4_t*>(slice + stage_off(r, chunk)) = v;
-        }
+      for (int grp = 0; grp < 4; ++grp) {
+        const int r = lane & 31;
+        const int chunk = j * 8 + 2 * grp + (lane >> 5);
+        f32x4_t v = {acc[i][j][4 * grp], acc[i][j][4 * grp + 1], acc[i][j][4 * grp + 2],
+                     acc[i][j][4 * grp + 3]};
+        *reinterpret_cast<f32x4_t*>(slice + stage_off(r, chunk)) = v;
+      }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    // rows of this half: tile rows wm*128 + h*64 + r
+    // rows of this block: tile rows wm*128 + i*32 + r
     if constexpr (DUAL) {
       // slice columns 0..63: gate, 64..127: up, for f columns n0 + wn*64 + c
 #pragma unroll 2
-      for (int it = 0; it < 8; ++it) {
+      for (int it = 0; it < 4; ++it) {
         const int r = it * 8 + (lane >> 3);
         const int c = (lane & 7) * 8;
-        const int m = wm * 128 + h * 64 + r;
+        const int m = wm * 128 + i * 32 + r;
         float v[8], u[8];
-        const f32x4_t* p0 = reinterpret_cast<const f32x4_t*>(slice + stage_off(r, c >> 2));
-        const f32x4_t* p1 = reinterpret_cast<const f32x4_t*>(slice + stage_off(r, (c >> 2) + 1));
-        const f32x4_t* q0 = reinterpret_cast<const f32x4_t*>(slice + stage_off(r, (c >> 2) + 16));
-        const f32x4_t* q1 = reinterpret_cast<const f32x4_t*>(slice + stage_off(r, (c >> 2) + 17));
-        f32x4_t a0 = *p0, a1 = *p1, b0 = *q0, b1 = *q1;
+        const f32x4_t a0 = *reinterpret_cast<const f32x4_t*>(slice + stage_off(r, c >> 2));
+        const f32x4_t a1 = *reinterpret_cast<const f32x4_t*>(slice + stage_off(r, (c >> 2) + 1));
+        const f32x4_t b0 = *reinterpret_cast<const f32x4_t*>(slice + stage_off(r, (c >> 2) + 16));
+        const f32x4_t b1 = *reinterpret_cast<const f32x4_t*>(slice + stage_off(r, (c >> 2) + 17));
 #pragma unroll
         for (int q = 0; q < 4; ++q) { v[q] = a0[q]; v[q + 4] = a1[q]; u[q] = b0[q]; u[q + 4] = b1[q]; }
         const int n = t.n0 + wn * 64 + c;
@@ -628,10 +664,10 @@ __device__ __forceinline__ void epilogue_lds(const GemmArgs& g, const Tile& t, c
       }
     } else {
 #pragma unroll 2
-      for (int it = 0; it < 16; ++it) {
+      for (int it = 0; it < 8; ++it) {
         const int r = it * 4 + (lane >> 4);
         const int c = (lane & 15) * 8;
-        const int m = wm * 128 + h * 64 + r;
+        const int m = wm * 128 + i * 32 + r;
         float v[8];
         const f32x4_t a0 = *reinterpret_cast<const f32x4_t*>(slice + stage_off(r, c >> 2));
         const f32x4_t a1 = *reinterpret_cast<const f32x4_t*>(slice + stage_off(r, (c >> 2) + 1));

@@ -160,10 +160,14 @@ __global__ __launch_bounds__(256) void mx_quant_cols_kernel(
 // ---------------------------------------------------------------------------
 namespace mf {
 
-constexpr int MX_BK = 64;                        // k per stage (64 code bytes per row)
-constexpr int SCALE_BYTES = 4096;                // per stage: A blocks 0,1 and B blocks 0,1
-constexpr int MSTAGE = STAGE + SCALE_BYTES;      // codes A, codes B, scales
-constexpr int MX_DMA_PER_STAGE = 9;              // 4 A + 4 B + 1 scale per wave
+// A stage holds 128 code bytes (four 32-element scale blocks) of every tile
+// row of both operands, plus those rows' scales: block b of the A rows at
+// STAGE + b*1024, of the B rows at STAGE + 4096 + b*1024.  One MFMA k-step
+// takes 64 codes (two blocks), so a stage is two k-steps.
+constexpr int MX_KSTEP = 64;
+constexpr int SCALE_BYTES = 8192;
+constexpr int MSTAGE = STAGE + SCALE_BYTES;
+constexpr int MX_DMA_PER_STAGE = 2 * DMA_PER_OP + 2;   // codes of A and B, two scale blocks
 
 typedef __attribute__((ext_vector_type(8))) int i32x8_t;
 
@@ -172,15 +176,17 @@ struct MxPlan {
   i32x4_t srs;       // this wave's scale resource (waves 0-1: A, 2-3: B)
   uint32_t svoff;    // per-lane offset of the scale DMA
   uint32_t spitch;   // bytes between consecutive K blocks of the scales
-  int sblk;          // K block inside the stage this wave loads (0 or 1)
-  int amis;          // A rows: tile row 0 sits amis bytes into the scale stage
+  int sblk;          // first of the two K blocks of a stage this wave loads (0 or 2)
+  int amis;          // A rows: tile row 0 sits amis bytes into an A scale block
 };
 
-// Fragment of 32 codes (two 16-byte chunks) of one row of a K-major stage.
-__device__ __forceinline__ i32x8_t fragq(const char* op, int rowblk, int lane) {
+// Codes of one row for k-step j of a stage: lane half h takes 16-byte chunks
+// 4j + h (its bytes 0-15, first scale block) and 4j + 2 + h (bytes 16-31,
+// second scale block).
+__device__ __forceinline__ i32x8_t fragq(const char* op, int rowblk, int j, int lane) {
   const int row = rowblk + (lane & 31), h = lane >> 5;
-  const uint4 lo = *reinterpret_cast<const uint4*>(op + km_off(row, h));
-  const uint4 hi = *reinterpret_cast<const uint4*>(op + km_off(row, h + 2));
+  const uint4 lo = *reinterpret_cast<const uint4*>(op + km_off(row, 4 * j + h));
+  const uint4 hi = *reinterpret_cast<const uint4*>(op + km_off(row, 4 * j + 2 + h));
   i32x8_t r = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
   return r;
 }
@@ -190,32 +196,33 @@ struct MxFrags {
   int sa[4], sb[4];
 };
 
+// Fragments and scales of k-step j of stage kt.  Lanes 0-31 supply the
+// scale of the first block of the k-step, lanes 32-63 of the second.
 template <bool DUAL>
-__device__ __forceinline__ void load_mx_frags(const char* smem, int kt, int wm, int wn, int lane,
-                                              int amis, MxFrags& F) {
+__device__ __forceinline__ void load_mx_frags(const char* smem, int kt, int j, int wm, int wn,
+                                              int lane, int amis, MxFrags& F) {
   const char* st = smem + (kt & (NST - 1)) * MSTAGE;
   const char* As = st;
   const char* Bs = st + OPB;
   const uint8_t* Ss = reinterpret_cast<const uint8_t*>(st + STAGE);
-  const int h = lane >> 5;
+  const int blk = 2 * j + (lane >> 5);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = wm * 128 + i * 32;
-    F.a[i] = fragq(As, row, lane);
-    F.sa[i] = Ss[h * 1024 + amis + row + (lane & 31)];
+    F.a[i] = fragq(As, row, j, lane);
+    F.sa[i] = Ss[blk * 1024 + amis + row + (lane & 31)];
   }
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int col = DUAL ? ((j >> 1) * 128 + wn * 64 + (j & 1) * 32) : (wn * 128 + j * 32);
-    F.b[j] = fragq(Bs, col, lane);
-    F.sb[j] = Ss[2048 + h * 1024 + col + (lane & 31)];
+  for (int q = 0; q < 4; ++q) {
+    const int col = DUAL ? ((q >> 1) * 128 + wn * 64 + (q & 1) * 32) : (wn * 128 + q * 32);
+    F.b[q] = fragq(Bs, col, j, lane);
+    F.sb[q] = Ss[4096 + blk * 1024 + col + (lane & 31)];
   }
 }
 
-template <int I0>
-__device__ __forceinline__ void mx_mfma8(f32x16_t (&acc)[4][4], const MxFrags& F) {
+__device__ __forceinline__ void mx_mfma16(f32x16_t (&acc)[4][4], const MxFrags& F) {
 #pragma unroll
-  for (int i = I0; i < I0 + 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.b[j], F.a[i], acc[i][j], 0, 0,
@@ -226,25 +233,20 @@ __device__ __forceinline__ void mx_issue(const MxPlan& P, int kt, uint32_t st_ba
   issue<false>(P.a, kt, st_base, wave);
   issue<false>(P.b, kt, st_base + OPB, wave);
   // the block offset goes into the per-lane offset, which the range check covers
-  const uint32_t voff = P.svoff + (uint32_t)(2 * kt + P.sblk) * P.spitch;
-  const uint32_t dst = st_base + STAGE + (wave >> 1) * 2048 + P.sblk * 1024;
-  dma16(P.srs, dst, voff, 0u);
-}
-
-__device__ __forceinline__ void mx_wait_stage(int st, int last_issued) {
-  const int after = last_issued - st;
-  if (after >= 3) wait_vmcnt<3 * MX_DMA_PER_STAGE>();
-  else if (after == 2) wait_vmcnt<2 * MX_DMA_PER_STAGE>();
-  else if (after == 1) wait_vmcnt<MX_DMA_PER_STAGE>();
-  else wait_vmcnt<0>();
+  const uint32_t dst = st_base + STAGE + (wave >> 1) * 4096 + P.sblk * 1024;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const uint32_t voff = P.svoff + (uint32_t)(4 * kt + P.sblk + b) * P.spitch;
+    dma16(P.srs, dst + b * 1024, voff, 0u);
+  }
 }
 
 // Ask the scheduler to alternate MFMAs and LDS reads in the current region.
 __device__ __forceinline__ void interleave_mx() {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < 16; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
   }
 }
 
@@ -262,19 +264,15 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mx_kernel(GemmArgs g) {
   const uint8_t* A = static_cast<const uint8_t*>(g.a);
   const uint8_t* B = static_cast<const uint8_t*>(g.b0);
 
-  for (int it = 0;; ++it) {
-    const int L = logical_tile(it);
-    if (L >= ntiles) break;
-    const Tile t = sched_decode<BM, BNT>(g, sch, L);
+  auto plan = [&](const Tile& t, MxPlan& P) {
     // rows of B for this tile: gate/up panels hold 256 rows per 128 f columns
     const long brow0 = DUAL ? 2L * t.n0 : (long)t.n0;
     const long brows = DUAL ? 2L * ((g.N + 127) / 128) * 128 : (long)g.N;
-    MxPlan P;
     plan_km(P.a, A + (long)t.row0 * g.lda, ((long long)g.rows_total - t.row0) * g.lda, nullptr, 0,
-            1 << 30, g.lda / 2, wave, lane);
+            1 << 30, g.lda, wave, lane);
     plan_km(P.b, B + (long)t.e * g.b_es + brow0 * g.ldb, (brows - brow0) * g.ldb, nullptr, 0,
-            1 << 30, g.ldb / 2, wave, lane);
-    P.sblk = wave & 1;
+            1 << 30, g.ldb, wave, lane);
+    P.sblk = 2 * (wave & 1);
     const int row_al = t.row0 & ~15;
     P.amis = t.row0 - row_al;
     if (wave < 2) {
@@ -286,44 +284,80 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mx_kernel(GemmArgs g) {
       P.svoff = (uint32_t)(brow0 + lane * 16);
       P.spitch = (uint32_t)g.sb_pitch;
     }
+  };
+  auto stage_base = [&](int s) { return lds0 + (s & 1) * MSTAGE; };
 
+  int it = 0;
+  int L = logical_tile(it);
+  if (L >= ntiles) return;
+  Tile t = sched_decode<BM, BNT>(g, sch, L);
+  MxPlan P;
+  plan(t, P);
+  // K is a multiple of 64: a last stage may hold a single k-step
+  int ns = t.klen / MX_KSTEP, nk = (ns + 1) / 2;
+  if (nk > 0) mx_issue(P, 0, stage_base(0), wave);
+  if (nk > 1) mx_issue(P, 1, stage_base(1), wave);
+
+  for (;;) {
     f32x16_t acc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
 
-    const int nk = t.klen / MX_BK;
-#pragma unroll
-    for (int s = 0; s < NST; ++s)
-      if (s < nk) mx_issue(P, s, lds0 + s * MSTAGE, wave);
+    // k-steps q = 0 .. ns-1; step q reads stage q/2, half q%2.  After the
+    // reads of a stage's second step, one barrier publishes the next stage
+    // and frees this one for the stage after next.
     MxFrags F0, F1;
-    auto step = [&](int kt, MxFrags& cur, MxFrags& nxt) {
+    auto step = [&](int q, MxFrags& cur, MxFrags& nxt) {
       __builtin_amdgcn_s_waitcnt(kLgkm0);
-      mx_mfma8<0>(acc, cur);
-      const bool more = kt + 1 < nk;
-      if (more) mx_wait_stage(kt + 1, min(nk - 1, kt + NST - 1));
-      barrier();
-      if (kt + NST < nk) mx_issue(P, kt + NST, lds0 + (kt & (NST - 1)) * MSTAGE, wave);
-      if (more) load_mx_frags<DUAL>(smem, kt + 1, wm, wn, lane, P.amis, nxt);
-      mx_mfma8<2>(acc, cur);
+      const int kt = q >> 1;
+      if ((q & 1) == 0) {
+        if (q + 1 < ns) load_mx_frags<DUAL>(smem, kt, 1, wm, wn, lane, P.amis, nxt);
+      } else {
+        const bool more = q + 1 < ns;
+        if (more) wait_vmcnt<0>();
+        barrier();
+        if (kt + 2 < nk) mx_issue(P, kt + 2, stage_base(kt), wave);
+        if (more) load_mx_frags<DUAL>(smem, kt + 1, 0, wm, wn, lane, P.amis, nxt);
+      }
+      mx_mfma16(acc, cur);
       interleave_mx();
+      __builtin_amdgcn_sched_barrier(0);
     };
     if (nk > 0) {
-      mx_wait_stage(0, min(nk - 1, NST - 1));
+      if (nk > 1) wait_vmcnt<MX_DMA_PER_STAGE>(); else wait_vmcnt<0>();
       barrier();
-      load_mx_frags<DUAL>(smem, 0, wm, wn, lane, P.amis, F0);
+      load_mx_frags<DUAL>(smem, 0, 0, wm, wn, lane, P.amis, F0);
     }
-    int kt = 0;
-    for (; kt + 1 < nk; kt += 2) {
-      step(kt, F0, F1);
-      step(kt + 1, F1, F0);
+    int q = 0;
+    for (; q + 1 < ns; q += 2) {
+      step(q, F0, F1);
+      step(q + 1, F1, F0);
     }
-    if (kt < nk) step(kt, F0, F1);
+    if (q < ns) step(q, F0, F1);
     __builtin_amdgcn_s_waitcnt(kLgkm0);
     barrier();
-    epilogue_lds<KIND>(g, t, smem + wave * 32768, acc, wm, wn, lane);
+
+    // next tile's stage 0 loads into buffer 0 during this epilogue, which
+    // stages through buffer 1; its stage 1 follows the epilogue
+    L = logical_tile(++it);
+    const bool has_next = L < ntiles;
+    Tile tn = t;
+    MxPlan Pn = P;
+    int nsn = 0, nkn = 0;
+    if (has_next) {
+      tn = sched_decode<BM, BNT>(g, sch, L);
+      plan(tn, Pn);
+      nsn = tn.klen / MX_KSTEP;
+      nkn = (nsn + 1) / 2;
+      if (nkn > 0) mx_issue(Pn, 0, stage_base(0), wave);
+    }
+    epilogue_lds<KIND>(g, t, smem + MSTAGE + wave * EPI_SLICE, acc, wm, wn, lane);
     barrier();
+    if (!has_next) break;
+    if (nkn > 1) mx_issue(Pn, 1, stage_base(1), wave);
+    t = tn; P = Pn; ns = nsn; nk = nkn;
   }
 }
 
