@@ -193,7 +193,10 @@ int moe_dispatch_bwd(const void* dXs, const int32_t* dest_row, int T, int d, int
  *   dlogits = p * (dp - <p, dp>), p = softmax(logits)    (f32 [T,E])
  *   dWr     = x^T . dlogits                               (dtype [d,E])
  *   dx     += dlogits . Wr^T                              (dtype [T,d], always added)
- *   With bf16 the two GEMMs read dlogits rounded to bf16 (held in ws).
+ *   With bf16 the two GEMMs read dlogits rounded to bf16 (held in ws), and
+ *   dWr is summed over chunks of tokens into float32 partials (also in ws)
+ *   that are added in chunk order: the result does not depend on timing.
+ *   Workspace: moe_workspace_size(MOE_OP_ROUTE_BWD, ...).
  */
 int moe_route_bwd(const void* x, const void* Wr, const float* logits,
                   const int32_t* topk_idx, const float* dtopk_w, int T, int d, int E, int k,

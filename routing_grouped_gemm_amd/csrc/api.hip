@@ -94,6 +94,20 @@ inline size_t dispatch_ws(int T, int E) {
 // Width of the bf16 copy of dlogits: E rounded up to the MFMA engine's K step.
 inline int router_ld16(int E) { return (E + 63) / 64 * 64; }
 
+// Router weight gradient on the MFMA engine: K = T is split into chunks of
+// at least 256 tokens (at most 64 chunks) whose float32 partials
+// [S][d][E] are summed in chunk order.
+inline int router_splits(int T) {
+  const int s = (T + 255) / 256;
+  return s < 1 ? 1 : (s > 64 ? 64 : s);
+}
+inline size_t route_bwd_ws(int T, int d, int E, int dtype) {
+  if (dtype != MOE_BF16) return 0;
+  size_t n = align_up((size_t)T * router_ld16(E) * 2);
+  if (E % 8 == 0) n += align_up((size_t)router_splits(T) * d * E * 4);
+  return n;
+}
+
 inline int gemm_engine(int dtype, int router_E = 8) {
   if (dtype == MOE_F32) return GEMM_F32_SIMT;
   return (router_E % 8 == 0) ? GEMM_BF16_MFMA : GEMM_BF16_SIMT;
@@ -144,7 +158,7 @@ int moe_workspace_size(int op, int T, int d, int E, int f, int k, int dtype, int
       *bytes = (prec == MOE_PREC_MXFP8) ? mx_bwd_workspace(R, d, f, E) : 0;
       return MOE_OK;
     case MOE_OP_ROUTE_BWD:
-      *bytes = (dtype == MOE_BF16) ? align_up((size_t)T * router_ld16(E) * 2) : 0;
+      *bytes = route_bwd_ws(T, d, E, dtype);
       return MOE_OK;
   }
   return MOE_ERR_SHAPE;
@@ -351,7 +365,7 @@ int moe_route_bwd(const void* x, const void* Wr, const float* logits, const int3
   if (int s = check_elems(T, d)) return s;
   if (!all_aligned(x, Wr, logits, topk_idx, dtopk_w, dlogits, dWr, dx, ws)) return MOE_ERR_ALIGN;
   const int ld16 = router_ld16(E);
-  const size_t need = (dtype == MOE_BF16) ? align_up((size_t)T * ld16 * 2) : 0;
+  const size_t need = route_bwd_ws(T, d, E, dtype);
   if (need && !ws) return MOE_ERR_NULL;
   if (ws_bytes < need) return MOE_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -361,14 +375,25 @@ int moe_route_bwd(const void* x, const void* Wr, const float* logits, const int3
   const void* dl = (dtype == MOE_BF16) ? static_cast<const void*>(dl16) : dlogits;
   const int ldl = (dtype == MOE_BF16) ? ld16 : E;
   const int eng = gemm_engine(dtype, E);
+  const int acc = (flags & MOE_ACCUMULATE) ? 1 : 0;
   GemmArgs g{};
   g.E = 1; g.offsets = nullptr; g.rows_total = T; g.ragged = RAG_K;
   g.M = d; g.N = E;
   g.a = x; g.lda = d;
   g.b0 = dl; g.ldb = ldl;
-  g.c0 = dWr; g.ldc = E;
-  g.accumulate = (flags & MOE_ACCUMULATE) ? 1 : 0;
-  MOE_TRY(launch_grouped_gemm(GK_ROUTER_DWR, eng, g, num_cu(), st));
+  if (eng == GEMM_BF16_MFMA) {
+    // split K: d/256 output tiles alone would leave most of the chip idle
+    const int S = router_splits(T);
+    float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up((size_t)T * ld16 * 2));
+    g.E = S; g.kchunk = (T + S - 1) / S;
+    g.c0 = part; g.ldc = E; g.c_es = (long)d * E;
+    MOE_TRY(launch_grouped_gemm(GK_ROUTER_DWR_SPLIT, eng, g, num_cu(), st));
+    MOE_TRY(launch_split_reduce(dtype, part, S, (long)d * E, acc, dWr, st));
+  } else {
+    g.c0 = dWr; g.ldc = E;
+    g.accumulate = acc;
+    MOE_TRY(launch_grouped_gemm(GK_ROUTER_DWR, eng, g, num_cu(), st));
+  }
   GemmArgs h{};
   h.E = 1; h.offsets = nullptr; h.rows_total = T; h.ragged = RAG_M;
   // the MFMA engine runs K over the zero-padded width; the SIMT engine over E

@@ -28,7 +28,9 @@ enum Ragged : int { RAG_M = 0, RAG_K = 1 };
 
 struct GemmArgs {
   int E;               // number of groups
-  const int* offsets;  // [E+1] device row offsets of the groups, or nullptr: one group
+  const int* offsets;  // [E+1] device row offsets of the groups, or nullptr: see kchunk
+  int kchunk;          // offsets == nullptr: 0 = one group; else (RAG_K) group e covers
+                       // rows [e*kchunk, min((e+1)*kchunk, rows_total)) (split K)
   int rows_total;      // rows of the row-indexed operands (R, or T for router GEMMs)
   int ragged;          // RAG_M: group rows are GEMM rows; RAG_K: group rows are the K axis
   int M, N, K;         // the fixed dimensions (the ragged one is read from offsets)
@@ -76,6 +78,7 @@ enum GemmKind : int {
   GK_ROUTER_LOGITS = 5, // x[T,d] . Wr[d,E]           -> logits f32   (one group)
   GK_ROUTER_DWR = 6,    // x[T,d]^T . dl[T,E]         -> dWr[d,E]     (one group, K = T)
   GK_ROUTER_DX = 7,     // dl[T,E] . Wr[d,E]^T        -> dx += [T,d]  (one group, K = E)
+  GK_ROUTER_DWR_SPLIT = 12, // x^T . dl over K chunks     -> float32 partials [S][d][E]
   // MXFP8 kinds: both operands K-contiguous e4m3 codes with E8M0 block scales
   GK_MX_GATEUP = 8,       // Xq[R,d] . WguT[e][2f',d] (256-row panels: 128 gate rows, 128 up rows)
   GK_MX_DOWN = 9,         // Aq[R,f] . WdT[e][d,f]   -> Ys
@@ -86,6 +89,11 @@ enum GemmKind : int {
 // Engines: float32 storage on the SIMT engine, bf16 on MFMA, and bf16 on the
 // SIMT engine for router shapes the MFMA engine does not take (E % 8 != 0).
 enum GemmEngine : int { GEMM_F32_SIMT = 0, GEMM_BF16_MFMA = 1, GEMM_BF16_SIMT = 2 };
+
+// Number of groups of a GEMM: the offsets' groups, the K chunks, or one.
+inline __host__ __device__ int ngroups(const GemmArgs& g) {
+  return (g.offsets || g.kchunk > 0) ? g.E : 1;
+}
 
 // Launch a grouped GEMM of the given kind.  num_cu sizes the persistent grid.
 hipError_t launch_grouped_gemm(GemmKind kind, int engine, const GemmArgs& g, int num_cu,

@@ -261,13 +261,12 @@ namespace {
 int tiles_upper_bound(const GemmArgs& g, int BM, int BNT) {
   const int ntn = (g.N + BNT - 1) / BNT;
   if (g.ragged == RAG_M) {
-    const int E = g.offsets ? g.E : 1;
+    const int E = ngroups(g);
     long mt = (long)g.rows_total / BM + E;
     long ub = mt * ntn;
     return (int)(ub < (1L << 30) ? ub : (1L << 30));
   }
-  const int E = g.offsets ? g.E : 1;
-  return E * ((g.M + BM - 1) / BM) * ntn;
+  return ngroups(g) * ((g.M + BM - 1) / BM) * ntn;
 }
 
 const char* kind_name(int kind, const GemmArgs& g) {
@@ -279,6 +278,7 @@ const char* kind_name(int kind, const GemmArgs& g) {
     case GK_WGRAD: return g.c1 ? "gemm_wgrad_gateup" : "gemm_wgrad_down";
     case GK_ROUTER_LOGITS: return "gemm_router_logits";
     case GK_ROUTER_DWR: return "gemm_router_dwr";
+    case GK_ROUTER_DWR_SPLIT: return "gemm_router_dwr";
     case GK_ROUTER_DX: return "gemm_router_dx";
   }
   return "gemm";
@@ -318,6 +318,8 @@ hipError_t launch_grouped_gemm(GemmKind kind, int dtype, const GemmArgs& g, int 
     case GK_ROUTER_LOGITS: return launch_kind<GK_ROUTER_LOGITS>(dtype, g, num_cu, stream);
     case GK_ROUTER_DWR: return launch_kind<GK_ROUTER_DWR>(dtype, g, num_cu, stream);
     case GK_ROUTER_DX: return launch_kind<GK_ROUTER_DX>(dtype, g, num_cu, stream);
+    case GK_ROUTER_DWR_SPLIT: return launch_kind<GK_ROUTER_DWR_SPLIT>(dtype, g, num_cu, stream);
+    default: break;
   }
   return hipErrorInvalidValue;
 }

@@ -45,6 +45,10 @@ template <> struct KT<GK_ROUTER_DX> {
   static constexpr bool AK = true, BK_ = true;
   static constexpr int BSP = BS_NONE, EPI = EPI_STORE;
 };
+template <> struct KT<GK_ROUTER_DWR_SPLIT> {
+  static constexpr bool AK = false, BK_ = false;
+  static constexpr int BSP = BS_NONE, EPI = EPI_STORE_F32;
+};
 // MXFP8 kinds: BS_DUAL_N only marks the gate/up tile layout for the epilogue
 // (tile columns 0-127 gate, 128-255 up); the codes are one K-major matrix.
 template <> struct KT<GK_MX_GATEUP> {
@@ -86,9 +90,11 @@ struct Sched {
 template <int BM, int BNT>
 __device__ int sched_setup(const GemmArgs& g, Sched& s) {
   const int tid = threadIdx.x;
-  const int E = g.offsets ? g.E : 1;
+  const int E = ngroups(g);
   if (g.offsets) {
     for (int e = tid; e <= E; e += blockDim.x) s.off[e] = g.offsets[e];
+  } else if (g.kchunk > 0) {
+    for (int e = tid; e <= E; e += blockDim.x) s.off[e] = min(e * g.kchunk, g.rows_total);
   } else if (tid == 0) {
     s.off[0] = 0;
     s.off[1] = g.rows_total;
@@ -132,7 +138,7 @@ __device__ __forceinline__ Tile sched_decode(const GemmArgs& g, const Sched& s, 
   const int ntn = (g.N + BNT - 1) / BNT;
   Tile t;
   if (g.ragged == RAG_M) {
-    const int E = g.offsets ? g.E : 1;
+    const int E = ngroups(g);
     int mt = L / ntn, nt = L - mt * ntn;
     int lo = 0, hi = E;  // largest e in [0,E) with ts[e] <= mt
     while (hi - lo > 1) {
@@ -225,8 +231,8 @@ template <int EPI, typename TS, bool PARTIAL = true>
 __device__ __forceinline__ void epilogue4(const GemmArgs& g, const Tile& t, int m, int n,
                                           const float (&v)[4], const float (&u)[4]) {
   if constexpr (EPI == EPI_STORE_F32) {
-    long row = (long)t.row0 + m;
-    float* p = static_cast<float*>(g.c0) + row * g.ldc + n;
+    long row = (g.ragged == RAG_M) ? (long)t.row0 + m : (long)t.m0 + m;
+    float* p = static_cast<float*>(g.c0) + (g.ragged == RAG_M ? 0 : (long)t.e * g.c_es) + row * g.ldc + n;
     if (!PARTIAL || (n + 4 <= g.N && (g.ldc & 3) == 0))
       *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
     else
@@ -576,7 +582,7 @@ template <int EPI>
 __device__ __forceinline__ void epi8(const GemmArgs& g, const Tile& t, long row, int n,
                                      const float (&v)[8], const float (&u)[8]) {
   if constexpr (EPI == EPI_STORE_F32) {
-    float* p = static_cast<float*>(g.c0) + row * g.ldc + n;
+    float* p = static_cast<float*>(g.c0) + (g.ragged == RAG_M ? 0 : (long)t.e * g.c_es) + row * g.ldc + n;
     store8(p, v);
   } else if constexpr (EPI == EPI_STORE || EPI == EPI_WGRAD_SPLIT) {
     bf16_t* p;
@@ -627,12 +633,34 @@ __device__ __forceinline__ void epi8(const GemmArgs& g, const Tile& t, long row,
 // consecutive columns of a row and applies the epilogue with 16-byte global
 // accesses.
 template <int KIND>
-__device__ __forceinline__ void epilogue_lds(const GemmArgs& g, const Tile& t, char* slice,
-                                             f32x16_t (&acc)[4][4], int wm, int wn, int lane) {
+__device__ __forceinline__ void epilogue_lds(const GemmArgs& g, const Tile& tile, char* slice,
+                                             f32x16_t (&acc)[4][4], int wm, int wn, int lane_in) {
   constexpr int EPI = KT<KIND>::EPI;
   constexpr bool DUAL = KT<KIND>::BSP == BS_DUAL_N;
+  // The tile's coordinates and the lane pass through an empty asm statement so that the
+  // compiler cannot hoist the epilogue's address arithmetic above the K loop
+  // (where it would hold those registers, or spill them, for the whole loop).
+  Tile t = tile;
+  int lane = lane_in;
+  asm volatile("" : "+v"(t.row0), "+v"(t.n0), "+v"(t.m0), "+v"(t.e), "+v"(t.mlim), "+v"(lane));
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
+    // keep each block's loads inside its own pass (registers)
+    __builtin_amdgcn_sched_barrier(0);
+    uint4 hg[8], hu[8];
+    if constexpr (EPI == EPI_SWIGLU_BWD) {
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const int m = wm * 128 + i * 32 + it * 4 + (lane >> 4);
+        const int n = t.n0 + wn * 128 + (lane & 15) * 8;
+        hg[it] = hu[it] = make_uint4(0, 0, 0, 0);
+        if (m < t.mlim && n < g.N) {
+          const long off = ((long)t.row0 + m) * g.ldh + n;
+          hg[it] = *reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(g.h0) + off);
+          hu[it] = *reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(g.h1) + off);
+        }
+      }
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -661,6 +689,34 @@ __device__ __forceinline__ void epilogue_lds(const GemmArgs& g, const Tile& t, c
         for (int q = 0; q < 4; ++q) { v[q] = a0[q]; v[q + 4] = a1[q]; u[q] = b0[q]; u[q + 4] = b1[q]; }
         const int n = t.n0 + wn * 64 + c;
         if (m < t.mlim && n < g.N) epi8<EPI>(g, t, (long)t.row0 + m, n, v, u);
+      }
+    } else if constexpr (EPI == EPI_SWIGLU_BWD) {
+      // Hg, Hu of the block's rows were loaded before the accumulators went
+      // to the slice (hg / hu below), so their latency overlaps the staging.
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const int r = it * 4 + (lane >> 4);
+        const int c = (lane & 15) * 8;
+        const int m = wm * 128 + i * 32 + r;
+        const int n = t.n0 + wn * 128 + c;
+        if (m < t.mlim && n < g.N) {
+          const f32x4_t a0 = *reinterpret_cast<const f32x4_t*>(slice + stage_off(r, c >> 2));
+          const f32x4_t a1 = *reinterpret_cast<const f32x4_t*>(slice + stage_off(r, (c >> 2) + 1));
+          float v[8], h0[8], h1[8], dg[8], du[8];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) { v[q] = a0[q]; v[q + 4] = a1[q]; }
+          unpack8(hg[it], h0);
+          unpack8(hu[it], h1);
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const float sg = 1.0f / (1.0f + __expf(-h0[q]));
+            du[q] = v[q] * h0[q] * sg;
+            dg[q] = v[q] * h1[q] * sg * (1.0f + h0[q] * (1.0f - sg));
+          }
+          bf16_t* p = static_cast<bf16_t*>(g.c0) + ((long)t.row0 + m) * g.ldc + n;
+          store8(p, dg);
+          store8(p + g.c_split, du);
+        }
       }
     } else {
 #pragma unroll 2

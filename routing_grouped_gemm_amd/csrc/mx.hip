@@ -377,8 +377,7 @@ const char* mx_name(int kind) {
 template <int KIND>
 hipError_t launch_mx_kind(const GemmArgs& g, int num_cu, hipStream_t s) {
   constexpr int BNT = (KT<KIND>::BSP == BS_DUAL_N) ? mf::BN / 2 : mf::BN;
-  const int E = g.offsets ? g.E : 1;
-  const long ub = ((long)g.rows_total / mf::BM + E) * ((g.N + BNT - 1) / BNT);
+  const long ub = ((long)g.rows_total / mf::BM + ngroups(g)) * ((g.N + BNT - 1) / BNT);
   const int grid = (int)(ub < num_cu ? ub : (long)num_cu);
   if (grid <= 0) return hipSuccess;
   hipLaunchKernelGGL(mf::gemm_mx_kernel<KIND>, dim3(grid), dim3(mf::NTHR), 0, s, g);

@@ -21,6 +21,10 @@ hipError_t launch_combine_bwd(int dtype, const void* dY, const void* Ys, const f
                               hipStream_t s);
 hipError_t launch_gather_sum(int dtype, const void* dXs, const int32_t* dest, int T, int d, int k,
                              int accumulate, void* dx, hipStream_t s);
+// out[i] = (accumulate ? out[i] : 0) + sum over s of part[s*n + i], summed in
+// float32 in order of s; out has the dtype.
+hipError_t launch_split_reduce(int dtype, const float* part, int S, long n, int accumulate,
+                               void* out, hipStream_t s);
 // dl16 (optional): bf16 copy of dl as rows of ld16 >= E entries, tail zeroed.
 hipError_t launch_router_bwd_softmax(const float* logits, const int32_t* idx, const float* dw,
                                      int T, int E, int k, float* dl, uint16_t* dl16, int ld16,

@@ -439,6 +439,41 @@ hipError_t launch_combine_bwd(int dtype, const void* dY, const void* Ys, const f
   return hipGetLastError();
 }
 
+template <typename TS>
+__global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restrict__ part, int S,
+                                                           long n, int accumulate,
+                                                           TS* __restrict__ out) {
+  const long i = ((long)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= n) return;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  if (accumulate)
+    for (int q = 0; q < 4; ++q) acc[q] = (i + q < n) ? St<TS>::load(out + i + q) : 0.f;
+  for (int s = 0; s < S; ++s) {
+    const float* p = part + (long)s * n + i;
+    if (i + 4 <= n) {
+      const float4 v = *reinterpret_cast<const float4*>(p);
+      acc[0] += v.x; acc[1] += v.y; acc[2] += v.z; acc[3] += v.w;
+    } else {
+      for (int q = 0; q < 4 && i + q < n; ++q) acc[q] += p[q];
+    }
+  }
+  for (int q = 0; q < 4 && i + q < n; ++q) St<TS>::store(out + i + q, acc[q]);
+}
+
+hipError_t launch_split_reduce(int dtype, const float* part, int S, long n, int accumulate,
+                               void* out, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const dim3 grid((unsigned)((n + 1023) / 1024));
+  if (dtype)
+    hipLaunchKernelGGL(split_reduce_kernel<bf16_t>, grid, dim3(256), 0, s, part, S, n, accumulate,
+                       static_cast<bf16_t*>(out));
+  else
+    hipLaunchKernelGGL(split_reduce_kernel<float>, grid, dim3(256), 0, s, part, S, n, accumulate,
+                       static_cast<float*>(out));
+  note_launch("router_dwr_reduce", s);
+  return hipGetLastError();
+}
+
 hipError_t launch_gather_sum(int dtype, const void* dXs, const int32_t* dest, int T, int d, int k,
                              int accumulate, void* dx, hipStream_t s) {
   dim3 grid((T + 3) / 4);

@@ -70,8 +70,10 @@ def test_workspace_sizes(L):
     assert s == OK and n == 2 * 128 * 64 * 4
     s, n = ws_size(L, 1, 100, 64, 3, 64, 1, F32, P_F32)
     assert s == OK and n == 2 * 256
-    # route backward: bf16 copy of dlogits; none in fp32
-    assert ws_size(L, 7, 8192, 2048, 64, 1024, 8, BF16, P_BF16) == (OK, 8192 * 64 * 2)
+    # route backward: bf16 copy of dlogits (E padded to 64) plus float32 dWr
+    # partials of 32 token chunks; none in fp32
+    assert ws_size(L, 7, 8192, 2048, 64, 1024, 8, BF16, P_BF16) == (OK, 8192 * 64 * 2 + 32 * 2048 * 64 * 4)
+    assert ws_size(L, 7, 100, 64, 6, 64, 2, BF16, P_BF16) == (OK, 100 * 64 * 2)  # E % 8: no split
     assert ws_size(L, 7, 256, 64, 8, 128, 2, F32, P_F32) == (OK, 0)
     for op in (0, 2, 3, 4, 5, 6):
         assert ws_size(L, op, 256, 64, 8, 128, 2, BF16, P_BF16) == (OK, 0)
