@@ -152,10 +152,14 @@ int moe_combine(const void* Ys, const float* topk_w, const int32_t* dest_row, in
  * moe_combine_bwd -- backward of moe_combine for upstream gradient dY[T,d]:
  *   dYs[dest_row[t,j]] = topk_w[t,j] * dY[t]       (dtype, [R,d])
  *   dtopk_w[t,j]       = <dY[t], Ys[dest_row[t,j]]> (f32, [T,k])
+ *   dYs_q, dYs_q_scale (optional; both NULL or both set, bf16 only): the rows
+ *   of dYs as stored, block-quantised along d for an MXFP8 backward, laid out
+ *   like moe_dispatch's Xq / Xq_scale (codes [R,d]; scale of block b of row r
+ *   at dYs_q_scale[b*Rp + r], Rp = R rounded up to 16).
  */
 int moe_combine_bwd(const void* dY, const void* Ys, const float* topk_w,
                     const int32_t* dest_row, int T, int d, int k, int dtype, void* dYs,
-                    float* dtopk_w, void* stream);
+                    float* dtopk_w, void* dYs_q, uint8_t* dYs_q_scale, void* stream);
 
 /*
  * moe_grouped_ffn_bwd -- backward of moe_grouped_ffn_fwd.
@@ -170,11 +174,15 @@ int moe_combine_bwd(const void* dY, const void* Ys, const float* topk_w,
  *   zeros; with MOE_ACCUMULATE the sum is added to the existing values).
  *   Xs: the dispatched rows in dtype (also for MXFP8).  prec MXFP8: both
  *   operands of the two dgrad GEMMs are block-quantised along their
- *   contraction axis (dYs and Wd along d; dH, Wg, Wu along f); the weight
- *   gradients take the unquantised operands.  Workspace:
- *   moe_workspace_size(MOE_OP_FFN_BWD, ...) (0 bytes except for MXFP8).
+ *   contraction axis (dYs and Wd along d; dH, Wg, Wu along f); dYs_q /
+ *   dYs_q_scale are dYs quantised along d as moe_combine_bwd writes them
+ *   (ignored, may be NULL, in other precisions); dH is quantised as the down
+ *   dgrad's epilogue writes it; the weight gradients take the unquantised
+ *   operands.  Workspace: moe_workspace_size(MOE_OP_FFN_BWD, ...) (0 bytes
+ *   except for MXFP8).
  */
-int moe_grouped_ffn_bwd(const void* dYs, const void* Xs, const void* Hg, const void* Hu,
+int moe_grouped_ffn_bwd(const void* dYs, const void* dYs_q, const uint8_t* dYs_q_scale,
+                        const void* Xs, const void* Hg, const void* Hu,
                         const void* A, const int32_t* offsets, int T, int k, int d, int f,
                         int E, const void* Wg, const void* Wu, const void* Wd, int dtype,
                         int prec, unsigned flags, void* dH, void* dXs, void* dWg, void* dWu,

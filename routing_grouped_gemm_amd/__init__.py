@@ -44,9 +44,9 @@ _SIGS = {
     "moe_grouped_ffn_fwd": [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _I, _I, _P, _P, _P, _P,
                             _P, _S, _P],
     "moe_combine": [_P, _P, _P, _I, _I, _I, _I, _P, _P],
-    "moe_combine_bwd": [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _P],
-    "moe_grouped_ffn_bwd": [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _I, _I, _U,
-                            _P, _P, _P, _P, _P, _P, _S, _P],
+    "moe_combine_bwd": [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P],
+    "moe_grouped_ffn_bwd": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _I,
+                            _I, _U, _P, _P, _P, _P, _P, _P, _S, _P],
     "moe_dispatch_bwd": [_P, _P, _I, _I, _I, _I, _U, _P, _P],
     "moe_route_bwd": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _U, _P, _P, _P, _P, _S, _P],
     "moe_workspace_size": [_I, _I, _I, _I, _I, _I, _I, _I, ctypes.POINTER(ctypes.c_size_t)],
@@ -178,19 +178,22 @@ def moe_combine(Ys, topk_w, dest_row, y, stream=None):
                              _stream(stream)), "moe_combine")
 
 
-def moe_combine_bwd(dY, Ys, topk_w, dest_row, dYs, dtopk_w, stream=None):
+def moe_combine_bwd(dY, Ys, topk_w, dest_row, dYs, dtopk_w, dYs_q=None, dYs_q_scale=None,
+                    stream=None):
     T, d = dY.shape
     k = topk_w.shape[1]
     _check(lib().moe_combine_bwd(_ptr(dY), _ptr(Ys), _ptr(topk_w), _ptr(dest_row), T, d, k,
-                                 _dtype(dY), _ptr(dYs), _ptr(dtopk_w), _stream(stream)),
-           "moe_combine_bwd")
+                                 _dtype(dY), _ptr(dYs), _ptr(dtopk_w), _ptr(dYs_q),
+                                 _ptr(dYs_q_scale), _stream(stream)), "moe_combine_bwd")
 
 
 def moe_grouped_ffn_bwd(dYs, Xs, Hg, Hu, A, offsets, T, k, Wg, Wu, Wd, dH, dXs,
-                        dWg, dWu, dWd, ws=None, prec="bf16", accumulate=False, stream=None):
+                        dWg, dWu, dWd, ws=None, prec="bf16", accumulate=False, dYs_q=None,
+                        dYs_q_scale=None, stream=None):
     E, d, f = Wg.shape
     wp, wb = _ws(ws)
-    _check(lib().moe_grouped_ffn_bwd(_ptr(dYs), _ptr(Xs), _ptr(Hg), _ptr(Hu), _ptr(A),
+    _check(lib().moe_grouped_ffn_bwd(_ptr(dYs), _ptr(dYs_q), _ptr(dYs_q_scale), _ptr(Xs),
+                                     _ptr(Hg), _ptr(Hu), _ptr(A),
                                      _ptr(offsets), T, k, d, f, E, _ptr(Wg),
                                      _ptr(Wu), _ptr(Wd), _dtype(Wg), PREC[prec],
                                      MOE_ACCUMULATE if accumulate else 0, _ptr(dH), _ptr(dXs),
@@ -287,8 +290,10 @@ class ExpertLayer:
         if prec == "mxfp8":
             self.Xq = z(R, d, dt=torch.uint8)
             self.Xq_scale = z(d // 32, mx_scale_pitch(R), dt=torch.uint8)
+            self.dYs_q = z(R, d, dt=torch.uint8)
+            self.dYs_q_scale = z(d // 32, mx_scale_pitch(R), dt=torch.uint8)
         else:
-            self.Xq = self.Xq_scale = None
+            self.Xq = self.Xq_scale = self.dYs_q = self.dYs_q_scale = None
         self.Hg, self.Hu, self.A = z(R, f), z(R, f), z(R, f)
         self.Ys = z(R, d)
         self.y = z(T, d)
@@ -330,10 +335,12 @@ class ExpertLayer:
         return self.y
 
     def backward(self, dY, stream=None):
-        moe_combine_bwd(dY, self.Ys, self.topk_w, self.dest_row, self.dYs, self.dw, stream)
+        moe_combine_bwd(dY, self.Ys, self.topk_w, self.dest_row, self.dYs, self.dw, self.dYs_q,
+                        self.dYs_q_scale, stream)
         moe_grouped_ffn_bwd(self.dYs, self.Xs, self.Hg, self.Hu, self.A, self.offsets, self.T, self.k,
                             self.Wg, self.Wu, self.Wd, self.dH, self.dXs, self.dWg, self.dWu,
-                            self.dWd, self.ws_bwd, self.prec, False, stream)
+                            self.dWd, self.ws_bwd, self.prec, False, self.dYs_q, self.dYs_q_scale,
+                            stream)
         moe_dispatch_bwd(self.dXs, self.dest_row, self.dx, False, stream)
         if self.router:
             moe_route_bwd(self.x, self.Wr, self.logits, self.topk_idx, self.dw, self.dlogits,

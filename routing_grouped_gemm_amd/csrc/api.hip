@@ -270,26 +270,30 @@ int moe_combine(const void* Ys, const float* topk_w, const int32_t* dest_row, in
 }
 
 int moe_combine_bwd(const void* dY, const void* Ys, const float* topk_w, const int32_t* dest_row,
-                    int T, int d, int k, int dtype, void* dYs, float* dtopk_w, void* stream) {
+                    int T, int d, int k, int dtype, void* dYs, float* dtopk_w, void* dYs_q,
+                    uint8_t* dYs_q_scale, void* stream) {
   if (!all_nonnull(dY, Ys, topk_w, dest_row, dYs, dtopk_w)) return MOE_ERR_NULL;
   if (int s = check_dtype(dtype)) return s;
+  if ((dYs_q == nullptr) != (dYs_q_scale == nullptr)) return MOE_ERR_NULL;
+  if (dYs_q && dtype != MOE_BF16) return MOE_ERR_DTYPE;
   if (T <= 0 || k <= 0 || (long long)T * k > 0x7fffffffLL) return MOE_ERR_SHAPE;
   if (int s = check_width(d)) return s;
-  if (!all_aligned(dY, Ys, topk_w, dest_row, dYs, dtopk_w)) return MOE_ERR_ALIGN;
+  if (!all_aligned(dY, Ys, topk_w, dest_row, dYs, dtopk_w, dYs_q, dYs_q_scale)) return MOE_ERR_ALIGN;
   clear_stale_error();
   return status_of(launch_combine_bwd(dtype, dY, Ys, topk_w, dest_row, T, d, k, dYs, dtopk_w,
-                                      static_cast<hipStream_t>(stream)));
+                                      dYs_q, dYs_q_scale, static_cast<hipStream_t>(stream)));
 }
 
-int moe_grouped_ffn_bwd(const void* dYs, const void* Xs, const void* Hg, const void* Hu,
-                        const void* A, const int32_t* offsets, int T, int k, int d, int f, int E,
-                        const void* Wg, const void* Wu, const void* Wd, int dtype, int prec,
-                        unsigned flags, void* dH, void* dXs, void* dWg, void* dWu, void* dWd,
-                        void* ws, size_t ws_bytes, void* stream) {
+int moe_grouped_ffn_bwd(const void* dYs, const void* dYs_q, const uint8_t* dYs_q_scale,
+                        const void* Xs, const void* Hg, const void* Hu, const void* A,
+                        const int32_t* offsets, int T, int k, int d, int f, int E, const void* Wg,
+                        const void* Wu, const void* Wd, int dtype, int prec, unsigned flags,
+                        void* dH, void* dXs, void* dWg, void* dWu, void* dWd, void* ws,
+                        size_t ws_bytes, void* stream) {
   if (!all_nonnull(dYs, Xs, Hg, Hu, A, offsets, Wg, Wu, Wd, dH, dXs, dWg, dWu, dWd))
     return MOE_ERR_NULL;
   if (int s = check_prec(dtype, prec)) return s;
-  if (prec == MOE_PREC_MXFP8 && !ws) return MOE_ERR_NULL;
+  if (prec == MOE_PREC_MXFP8 && !all_nonnull(ws, dYs_q, dYs_q_scale)) return MOE_ERR_NULL;
   if (int s = check_route_shape(T, E, k)) return s;
   if (int s = check_width(d)) return s;
   if (int s = check_width(f)) return s;
@@ -298,14 +302,15 @@ int moe_grouped_ffn_bwd(const void* dYs, const void* Xs, const void* Hg, const v
   if (int s = check_elems(E, (long long)d * f)) return s;
   if (!all_aligned(dYs, Xs, Hg, Hu, A, offsets, Wg, Wu, Wd, dH, dXs, dWg, dWu, dWd, ws))
     return MOE_ERR_ALIGN;
+  if (prec == MOE_PREC_MXFP8 && !all_aligned(dYs_q, dYs_q_scale)) return MOE_ERR_ALIGN;
   hipStream_t st = static_cast<hipStream_t>(stream);
   clear_stale_error();
   const int acc = (flags & MOE_ACCUMULATE) ? 1 : 0;
   const int eng = gemm_engine(dtype);
   if (prec == MOE_PREC_MXFP8) {
     if (ws_bytes < mx_bwd_workspace(R, d, f, E)) return MOE_ERR_WORKSPACE;
-    MOE_TRY(mx_ffn_dgrad(dYs, Hg, Hu, offsets, (int)R, d, f, E, Wg, Wu, Wd, dH, dXs, ws,
-                         num_cu(), st));
+    MOE_TRY(mx_ffn_dgrad(dYs_q, dYs_q_scale, Hg, Hu, offsets, (int)R, d, f, E, Wg, Wu, Wd, dH,
+                         dXs, ws, num_cu(), st));
   } else {
     GemmArgs g{};
     g.E = E; g.offsets = offsets; g.rows_total = (int)R; g.ragged = RAG_M;

@@ -66,6 +66,13 @@ struct GemmArgs {
   const uint8_t* sb;
   long sb_es;
   long sb_pitch;
+  // MXFP8 kinds whose epilogue output feeds the next MX GEMM (gate/up: A,
+  // down dgrad: dH): that output, as stored, block-quantised along its row:
+  // codes at q0 (same layout as the output), block b of row r at
+  // qs[b * qs_pitch + r].
+  uint8_t* q0;
+  uint8_t* qs;
+  long qs_pitch;
 };
 
 // Operand layouts of the five GEMM kinds of the layer and of the router.

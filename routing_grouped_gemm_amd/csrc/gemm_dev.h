@@ -6,6 +6,7 @@
 
 #include "gemm.h"
 #include "moe_common.h"
+#include "mx_codec.h"
 
 namespace moe {
 
@@ -67,6 +68,10 @@ template <> struct KT<GK_MX_DGRAD_GATEUP> {
   static constexpr bool AK = true, BK_ = true;
   static constexpr int BSP = BS_NONE, EPI = EPI_STORE;
 };
+
+// Kinds whose epilogue also writes the block-quantised output (MXFP8).
+template <int KIND>
+constexpr bool qout_of() { return KIND == GK_MX_GATEUP || KIND == GK_MX_DGRAD_DOWN; }
 
 // One output tile of one group.
 struct Tile {
@@ -627,31 +632,22 @@ __device__ __forceinline__ void epi8(const GemmArgs& g, const Tile& t, long row,
   }
 }
 
-// Epilogue of a wave's 128x128 accumulator sub-tile through its private
-// 16 KiB slice, one 32-row block at a time: the accumulators go to the slice
-// straight from the accumulator registers, then each lane reads back 8
-// consecutive columns of a row and applies the epilogue with 16-byte global
-// accesses.
-template <int KIND>
-__device__ __forceinline__ void epilogue_lds(const GemmArgs& g, const Tile& tile, char* slice,
-                                             f32x16_t (&acc)[4][4], int wm, int wn, int lane_in) {
+// One 32-row block (I) of a wave's epilogue; a separate instantiation per
+// block keeps every accumulator index static, so the accumulators stay in
+// registers however large the block's code gets.
+template <int KIND, int I>
+__device__ __forceinline__ void epilogue_block(const GemmArgs& g, const Tile& t, char* slice,
+                                               f32x16_t (&acc)[4][4], int wm, int wn, int lane) {
   constexpr int EPI = KT<KIND>::EPI;
   constexpr bool DUAL = KT<KIND>::BSP == BS_DUAL_N;
-  // The tile's coordinates and the lane pass through an empty asm statement so that the
-  // compiler cannot hoist the epilogue's address arithmetic above the K loop
-  // (where it would hold those registers, or spill them, for the whole loop).
-  Tile t = tile;
-  int lane = lane_in;
-  asm volatile("" : "+v"(t.row0), "+v"(t.n0), "+v"(t.m0), "+v"(t.e), "+v"(t.mlim), "+v"(lane));
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  {
     // keep each block's loads inside its own pass (registers)
     __builtin_amdgcn_sched_barrier(0);
     uint4 hg[8], hu[8];
     if constexpr (EPI == EPI_SWIGLU_BWD) {
 #pragma unroll
       for (int it = 0; it < 8; ++it) {
-        const int m = wm * 128 + i * 32 + it * 4 + (lane >> 4);
+        const int m = wm * 128 + I * 32 + it * 4 + (lane >> 4);
         const int n = t.n0 + wn * 128 + (lane & 15) * 8;
         hg[it] = hu[it] = make_uint4(0, 0, 0, 0);
         if (m < t.mlim && n < g.N) {
@@ -667,8 +663,8 @@ __device__ __forceinline__ void epilogue_lds(const GemmArgs& g, const Tile& tile
       for (int grp = 0; grp < 4; ++grp) {
         const int r = lane & 31;
         const int chunk = j * 8 + 2 * grp + (lane >> 5);
-        f32x4_t v = {acc[i][j][4 * grp], acc[i][j][4 * grp + 1], acc[i][j][4 * grp + 2],
-                     acc[i][j][4 * grp + 3]};
+        f32x4_t v = {acc[I][j][4 * grp], acc[I][j][4 * grp + 1], acc[I][j][4 * grp + 2],
+                     acc[I][j][4 * grp + 3]};
         *reinterpret_cast<f32x4_t*>(slice + stage_off(r, chunk)) = v;
       }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -679,7 +675,7 @@ __device__ __forceinline__ void epilogue_lds(const GemmArgs& g, const Tile& tile
       for (int it = 0; it < 4; ++it) {
         const int r = it * 8 + (lane >> 3);
         const int c = (lane & 7) * 8;
-        const int m = wm * 128 + i * 32 + r;
+        const int m = wm * 128 + I * 32 + r;
         float v[8], u[8];
         const f32x4_t a0 = *reinterpret_cast<const f32x4_t*>(slice + stage_off(r, c >> 2));
         const f32x4_t a1 = *reinterpret_cast<const f32x4_t*>(slice + stage_off(r, (c >> 2) + 1));
@@ -688,7 +684,18 @@ __device__ __forceinline__ void epilogue_lds(const GemmArgs& g, const Tile& tile
 #pragma unroll
         for (int q = 0; q < 4; ++q) { v[q] = a0[q]; v[q + 4] = a1[q]; u[q] = b0[q]; u[q + 4] = b1[q]; }
         const int n = t.n0 + wn * 64 + c;
-        if (m < t.mlim && n < g.N) epi8<EPI>(g, t, (long)t.row0 + m, n, v, u);
+        const bool ok = m < t.mlim && n < g.N;  // uniform over each 4-lane block
+        if (ok) epi8<EPI>(g, t, (long)t.row0 + m, n, v, u);
+        if constexpr (qout_of<KIND>()) {
+          if (ok) {
+            float a[8], ar[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) a[q] = silu_f(v[q]) * u[q];
+            round_bf16_8(a, ar);
+            const long row = (long)t.row0 + m;
+            quant8_store(ar, g.q0 + row * g.ldc + n, g.qs + (n >> 5) * g.qs_pitch + row, lane);
+          }
+        }
       }
     } else if constexpr (EPI == EPI_SWIGLU_BWD) {
       // Hg, Hu of the block's rows were loaded before the accumulators went
@@ -697,7 +704,7 @@ __device__ __forceinline__ void epilogue_lds(const GemmArgs& g, const Tile& tile
       for (int it = 0; it < 8; ++it) {
         const int r = it * 4 + (lane >> 4);
         const int c = (lane & 15) * 8;
-        const int m = wm * 128 + i * 32 + r;
+        const int m = wm * 128 + I * 32 + r;
         const int n = t.n0 + wn * 128 + c;
         if (m < t.mlim && n < g.N) {
           const f32x4_t a0 = *reinterpret_cast<const f32x4_t*>(slice + stage_off(r, c >> 2));
@@ -713,9 +720,18 @@ __device__ __forceinline__ void epilogue_lds(const GemmArgs& g, const Tile& tile
             du[q] = v[q] * h0[q] * sg;
             dg[q] = v[q] * h1[q] * sg * (1.0f + h0[q] * (1.0f - sg));
           }
-          bf16_t* p = static_cast<bf16_t*>(g.c0) + ((long)t.row0 + m) * g.ldc + n;
+          const long row = (long)t.row0 + m;
+          bf16_t* p = static_cast<bf16_t*>(g.c0) + row * g.ldc + n;
           store8(p, dg);
           store8(p + g.c_split, du);
+          if constexpr (qout_of<KIND>()) {
+            float r[8];
+            round_bf16_8(dg, r);
+            quant8_store(r, g.q0 + row * g.ldc + n, g.qs + (n >> 5) * g.qs_pitch + row, lane);
+            round_bf16_8(du, r);
+            quant8_store(r, g.q0 + row * g.ldc + g.c_split + n,
+                         g.qs + ((g.c_split + n) >> 5) * g.qs_pitch + row, lane);
+          }
         }
       }
     } else {
@@ -723,7 +739,7 @@ __device__ __forceinline__ void epilogue_lds(const GemmArgs& g, const Tile& tile
       for (int it = 0; it < 8; ++it) {
         const int r = it * 4 + (lane >> 4);
         const int c = (lane & 15) * 8;
-        const int m = wm * 128 + i * 32 + r;
+        const int m = wm * 128 + I * 32 + r;
         float v[8];
         const f32x4_t a0 = *reinterpret_cast<const f32x4_t*>(slice + stage_off(r, c >> 2));
         const f32x4_t a1 = *reinterpret_cast<const f32x4_t*>(slice + stage_off(r, (c >> 2) + 1));
@@ -735,7 +751,27 @@ __device__ __forceinline__ void epilogue_lds(const GemmArgs& g, const Tile& tile
       }
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  }
+}
+}
+
+// Epilogue of a wave's 128x128 accumulator sub-tile through its private
+// 16 KiB slice, one 32-row block at a time: the accumulators go to the slice
+// straight from the accumulator registers, then each lane reads back 8
+// consecutive columns of a row and applies the epilogue with 16-byte global
+// accesses.
+template <int KIND>
+__device__ __forceinline__ void epilogue_lds(const GemmArgs& g, const Tile& tile, char* slice,
+                                             f32x16_t (&acc)[4][4], int wm, int wn, int lane_in) {
+  // The tile's coordinates and the lane pass through an empty asm statement so that the
+  // compiler cannot hoist the epilogue's address arithmetic above the K loop
+  // (where it would hold those registers, or spill them, for the whole loop).
+  Tile t = tile;
+  int lane = lane_in;
+  asm volatile("" : "+v"(t.row0), "+v"(t.n0), "+v"(t.m0), "+v"(t.e), "+v"(t.mlim), "+v"(lane));
+  epilogue_block<KIND, 0>(g, t, slice, acc, wm, wn, lane);
+  epilogue_block<KIND, 1>(g, t, slice, acc, wm, wn, lane);
+  epilogue_block<KIND, 2>(g, t, slice, acc, wm, wn, lane);
+  epilogue_block<KIND, 3>(g, t, slice, acc, wm, wn, lane);
 }
 
 }  // namespace mf

@@ -20,8 +20,10 @@ hipError_t launch_mx_dispatch_copy(const void* x, const int32_t* src_token, int 
 hipError_t mx_ffn_fwd(const void* Xq, const uint8_t* Xscale, const int32_t* offsets, int R, int d,
                       int f, int E, const void* Wg, const void* Wu, const void* Wd, void* Hg,
                       void* Hu, void* A, void* Ys, void* ws, int num_cu, hipStream_t s);
-hipError_t mx_ffn_dgrad(const void* dYs, const void* Hg, const void* Hu, const int32_t* offsets,
-                        int R, int d, int f, int E, const void* Wg, const void* Wu, const void* Wd,
-                        void* dH, void* dXs, void* ws, int num_cu, hipStream_t s);
+// dYsq / dYsq_scale: dYs quantised along d (as the combine backward writes it).
+hipError_t mx_ffn_dgrad(const void* dYsq, const uint8_t* dYsq_scale, const void* Hg,
+                        const void* Hu, const int32_t* offsets, int R, int d, int f, int E,
+                        const void* Wg, const void* Wu, const void* Wd, void* dH, void* dXs,
+                        void* ws, int num_cu, hipStream_t s);
 
 }  // namespace moe

@@ -28,55 +28,9 @@
 #include "hook.h"
 #include "moe_common.h"
 #include "mx.h"
+#include "mx_codec.h"
 
 namespace moe {
-
-// ---------------------------------------------------------------------------
-// codec
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ int mx_block_exponent(float amax) {
-  if (!(amax > 0.0f)) return 0;
-  int ex;
-  const float m = frexpf(amax, &ex);  // amax = m * 2^ex, m in [0.5, 1)
-  const int top = ex - 1;             // amax in [2^top, 2^(top+1))
-  // 448 * 2^(top-8) = 1.75 * 2^top >= amax iff 2m <= 1.75; else top-7 suffices
-  const int E = (2.0f * m <= 1.75f) ? top - 8 : top - 7;
-  return min(max(E, -127), 127);
-}
-
-// e4m3 byte of v (already divided by the block scale), RNE, saturating.
-__device__ __forceinline__ uint32_t e4m3_code(float v) {
-  const uint32_t sign = (__float_as_uint(v) >> 31) << 7;
-  const float a = fabsf(v);
-  uint32_t code;
-  if (a < 0.015625f) {                   // below 2^-6: spacing 2^-9
-    code = (uint32_t)rintf(a * 512.0f);  // 0..8 (8 is the smallest normal, 0x08)
-  } else {
-    int ex;
-    frexpf(a, &ex);
-    int e = ex - 1;                      // a in [2^e, 2^(e+1)), e >= -6
-    int q = (int)rintf(ldexpf(a, 3 - e));  // 8..16
-    if (q == 16) { ++e; q = 8; }
-    code = (uint32_t)(((e + 7) << 3) | (q - 8));
-    if (code > 0x7Eu) code = 0x7Eu;      // 448
-  }
-  return sign | code;
-}
-
-// 8 values of one lane; the 32-element block spans the 4 lanes 4g..4g+3.
-// Returns the block exponent; codes[0..1] receive the 8 bytes.
-__device__ __forceinline__ int quant8(const float (&v)[8], uint32_t (&codes)[2]) {
-  float amax = 0.0f;
-#pragma unroll
-  for (int q = 0; q < 8; ++q) amax = fmaxf(amax, fabsf(v[q]));
-  amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
-  amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
-  const int E = mx_block_exponent(amax);
-  codes[0] = codes[1] = 0;
-#pragma unroll
-  for (int q = 0; q < 8; ++q) codes[q >> 2] |= e4m3_code(ldexpf(v[q], -E)) << (8 * (q & 3));
-  return E;
-}
 
 // ---------------------------------------------------------------------------
 // quantisation kernels
@@ -116,13 +70,24 @@ __global__ __launch_bounds__(256) void mx_quant_rows_kernel(
   const long r = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= nrows) return;
   const long g = r / grows, i = r - g * grows;
-  for (int c = lane * 8; c < K; c += 512) {
-    float v[8];
-    load8(src + r * src_ld + c, v);
-    uint32_t codes[2];
-    const int E = quant8(v, codes);
-    *reinterpret_cast<uint2*>(dst + r * dst_ld + col0 + c) = make_uint2(codes[0], codes[1]);
-    if ((lane & 3) == 0) scale[g * sg_stride + (long)(block0 + (c >> 5)) * pitch + i] = (uint8_t)(E + 127);
+  // up to 8 chunks of 8 values per lane are loaded before any is quantised
+  for (int c0 = lane * 8; c0 < K; c0 += 8 * 512) {
+    uint4 raw[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int c = c0 + u * 512;
+      raw[u] = c < K ? *reinterpret_cast<const uint4*>(src + r * src_ld + c) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int c = c0 + u * 512;
+      if (c < K) {  // whole 4-lane blocks together (K is a multiple of 32)
+        float v[8];
+        unpack8(raw[u], v);
+        quant8_store(v, dst + r * dst_ld + col0 + c,
+                     scale + g * sg_stride + (long)(block0 + (c >> 5)) * pitch + i, lane);
+      }
+    }
   }
 }
 
@@ -130,29 +95,59 @@ __global__ __launch_bounds__(256) void mx_quant_rows_kernel(
 // becomes row rowmap(n) of dst[e] (rows of K codes); the scale of block b to
 // scale[e*s_es + b*pitch + rowmap(n)].  half >= 0 selects the gate/up panel
 // map rowmap(n) = 256*(n/128) + 128*half + n%128; half < 0 keeps rowmap(n) = n.
+// A workgroup stages a 64 (k) x 64 (n) tile in LDS with coalesced 16-byte
+// loads; thread t then takes column t/4 and rows 16*(t%4) .. +15, half of a
+// 32-row block whose other half sits in the neighbouring lane, and writes 16
+// codes (4 lanes write 64 contiguous bytes of the transposed row).
 __global__ __launch_bounds__(256) void mx_quant_cols_kernel(
     const bf16_t* __restrict__ W, int K, int N, uint8_t* __restrict__ dst, long dst_es,
     int half, uint8_t* __restrict__ scale, long s_es, long pitch) {
-  const int n = blockIdx.x * 256 + threadIdx.x;
-  const int kb = blockIdx.y, e = blockIdx.z;
-  if (n >= N) return;
-  const bf16_t* col = W + (long)e * K * N + (long)kb * 32 * N + n;
-  float v[32];
+  __shared__ __attribute__((aligned(16))) bf16_t tile[64][72];
+  const int e = blockIdx.z, k0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+  const int t = threadIdx.x, lane = t & 63;
+  {
+    const int r = t >> 2, c = (t & 3) * 16;
+    uint4 a = make_uint4(0, 0, 0, 0), b = a;
+    if (k0 + r < K && n0 + c < N) {
+      const bf16_t* src = W + (long)e * K * N + (long)(k0 + r) * N + n0 + c;
+      a = *reinterpret_cast<const uint4*>(src);
+      b = *reinterpret_cast<const uint4*>(src + 8);
+    }
+    *reinterpret_cast<uint4*>(&tile[r][c]) = a;
+    *reinterpret_cast<uint4*>(&tile[r][c + 8]) = b;
+  }
+  __syncthreads();
+  const int n = t >> 2, q = t & 3;
+  if (n0 + n >= N) return;  // whole 4-lane groups leave together
+  float v[16];
   float amax = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    v[i] = bf16_to_f32(col[(long)i * N]);
+  for (int i = 0; i < 16; ++i) {
+    v[i] = bf16_to_f32(tile[16 * q + i][n]);
     amax = fmaxf(amax, fabsf(v[i]));
   }
+  amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
   const int E = mx_block_exponent(amax);
-  uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  float sv[8];
+  uint32_t w[4];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) w[i >> 2] |= e4m3_code(ldexpf(v[i], -E)) << (8 * (i & 3));
-  const long row = half >= 0 ? (long)((n >> 7) << 8) + 128 * half + (n & 127) : (long)n;
-  uint8_t* out = dst + (long)e * dst_es + row * K + kb * 32;
-  *reinterpret_cast<uint4*>(out) = make_uint4(w[0], w[1], w[2], w[3]);
-  *reinterpret_cast<uint4*>(out + 16) = make_uint4(w[4], w[5], w[6], w[7]);
-  scale[(long)e * s_es + (long)kb * pitch + row] = (uint8_t)(E + 127);
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sv[i] = ldexpf(v[8 * h + i], -E);
+    uint32_t c2[2];
+    e4m3_codes8(sv, c2);
+    w[2 * h] = c2[0];
+    w[2 * h + 1] = c2[1];
+  }
+  const int col = n0 + n;
+  const long row = half >= 0 ? (long)((col >> 7) << 8) + 128 * half + (col & 127) : (long)col;
+  if (k0 + 16 * q < K) {
+    *reinterpret_cast<uint4*>(dst + (long)e * dst_es + row * K + k0 + 16 * q) =
+        make_uint4(w[0], w[1], w[2], w[3]);
+    if ((q & 1) == 0)
+      scale[(long)e * s_es + (long)((k0 >> 5) + (q >> 1)) * pitch + row] = (uint8_t)(E + 127);
+  }
+  (void)lane;
 }
 
 // ---------------------------------------------------------------------------
@@ -418,7 +413,7 @@ hipError_t quant_rows(const void* src, long nrows, int K, long src_ld, uint8_t* 
 
 hipError_t quant_cols(const void* W, int E, int K, int N, uint8_t* dst, long dst_es, int half,
                       uint8_t* scale, long s_es, long pitch, hipStream_t s) {
-  hipLaunchKernelGGL(mx_quant_cols_kernel, dim3((N + 255) / 256, K / 32, E), dim3(256), 0, s,
+  hipLaunchKernelGGL(mx_quant_cols_kernel, dim3((N + 63) / 64, (K + 63) / 64, E), dim3(256), 0, s,
                      static_cast<const bf16_t*>(W), K, N, dst, dst_es, half, scale, s_es, pitch);
   note_launch("mx_quant_cols", s);
   return hipGetLastError();
@@ -446,14 +441,12 @@ FwdWs carve_fwd(void* ws, long long R, int d, int f, int E, size_t* total) {
 }
 
 struct BwdWs {
-  uint8_t *dysq, *dysq_s, *wd, *wd_s, *dhq, *dhq_s, *wgu, *wgu_s;
+  uint8_t *wd, *wd_s, *dhq, *dhq_s, *wgu, *wgu_s;
 };
 BwdWs carve_bwd(void* ws, long long R, int d, int f, int E, size_t* total) {
   Carve c{static_cast<char*>(ws)};
   BwdWs w;
   const long Rp = pitch_rows(R);
-  w.dysq = c.take<uint8_t>((size_t)R * d);
-  w.dysq_s = c.take<uint8_t>((size_t)(d / 32) * Rp);
   w.wd = c.take<uint8_t>((size_t)E * f * d);
   w.wd_s = c.take<uint8_t>((size_t)E * (d / 32) * f);
   w.dhq = c.take<uint8_t>((size_t)R * 2 * f);
@@ -516,8 +509,8 @@ hipError_t mx_ffn_fwd(const void* Xq, const uint8_t* Xscale, const int32_t* offs
   g.b0 = w.wgu; g.ldb = d; g.b_es = 2 * fp * d;
   g.sb = w.wgu_s; g.sb_es = (d / 32) * 2 * fp; g.sb_pitch = 2 * fp;
   g.c0 = Hg; g.c1 = Hu; g.c2 = A; g.ldc = f;
+  g.q0 = w.aq; g.qs = w.aq_s; g.qs_pitch = Rp;   // A quantised along f in the epilogue
   MX_TRY(launch_grouped_gemm_mx(GK_MX_GATEUP, g, num_cu, s));
-  MX_TRY(quant_rows(A, R, f, f, w.aq, f, 0, w.aq_s, R > 0 ? R : 1, 0, Rp, 0, s));
   GemmArgs h{};
   h.E = E; h.offsets = offsets; h.rows_total = R; h.ragged = RAG_M;
   h.N = d; h.K = f;
@@ -528,26 +521,25 @@ hipError_t mx_ffn_fwd(const void* Xq, const uint8_t* Xscale, const int32_t* offs
   return launch_grouped_gemm_mx(GK_MX_DOWN, h, num_cu, s);
 }
 
-hipError_t mx_ffn_dgrad(const void* dYs, const void* Hg, const void* Hu, const int32_t* offsets,
-                        int R, int d, int f, int E, const void* Wg, const void* Wu, const void* Wd,
-                        void* dH, void* dXs, void* ws, int num_cu, hipStream_t s) {
+hipError_t mx_ffn_dgrad(const void* dYsq, const uint8_t* dYsq_scale, const void* Hg,
+                        const void* Hu, const int32_t* offsets, int R, int d, int f, int E,
+                        const void* Wg, const void* Wu, const void* Wd, void* dH, void* dXs,
+                        void* ws, int num_cu, hipStream_t s) {
   const BwdWs w = carve_bwd(ws, R, d, f, E, nullptr);
   const long Rp = pitch_rows(R);
-  const long one = R > 0 ? R : 1;
-  // down dgrad: dYs and Wd along d
-  MX_TRY(quant_rows(dYs, R, d, d, w.dysq, d, 0, w.dysq_s, one, 0, Rp, 0, s));
+  // down dgrad: dYs (quantised along d by the combine backward) and Wd along d
   MX_TRY(quant_rows(Wd, (long)E * f, d, d, w.wd, d, 0, w.wd_s, f, (long)(d / 32) * f, f, 0, s));
   GemmArgs g{};
   g.E = E; g.offsets = offsets; g.rows_total = R; g.ragged = RAG_M;
   g.N = f; g.K = d;
-  g.a = w.dysq; g.lda = d; g.sa = w.dysq_s; g.sa_pitch = Rp;
+  g.a = dYsq; g.lda = d; g.sa = dYsq_scale; g.sa_pitch = Rp;
   g.b0 = w.wd; g.ldb = d; g.b_es = (long)f * d;
   g.sb = w.wd_s; g.sb_es = (long)(d / 32) * f; g.sb_pitch = f;
   g.c0 = dH; g.ldc = 2L * f; g.c_split = f;
   g.h0 = Hg; g.h1 = Hu; g.ldh = f;
+  g.q0 = w.dhq; g.qs = w.dhq_s; g.qs_pitch = Rp;   // dH quantised along 2f in the epilogue
   MX_TRY(launch_grouped_gemm_mx(GK_MX_DGRAD_DOWN, g, num_cu, s));
-  // gate/up dgrad: dH along 2f; Wg | Wu along f into one [d][2f] matrix per expert
-  MX_TRY(quant_rows(dH, R, 2 * f, 2L * f, w.dhq, 2L * f, 0, w.dhq_s, one, 0, Rp, 0, s));
+  // gate/up dgrad: Wg | Wu along f into one [d][2f] matrix per expert
   MX_TRY(quant_rows(Wg, (long)E * d, f, f, w.wgu, 2L * f, 0, w.wgu_s, d, (long)(2 * f / 32) * d, d,
                     0, s));
   MX_TRY(quant_rows(Wu, (long)E * d, f, f, w.wgu, 2L * f, f, w.wgu_s, d, (long)(2 * f / 32) * d, d,

@@ -16,6 +16,7 @@
 // and stores.  The combine and the gathers of the backward run one wave per
 // token and sum in float32 in slot order.
 #include "moe_common.h"
+#include "mx_codec.h"
 #include "hook.h"
 #include "route.h"
 
@@ -241,14 +242,16 @@ __global__ __launch_bounds__(256) void combine_kernel(const TS* __restrict__ Ys,
 }
 
 // dYs[dest] = w * dY[t]; dw[t,j] = <dY[t], Ys[dest]>
-template <typename TS>
+template <typename TS, bool MXQ>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(const TS* __restrict__ dY,
                                                           const TS* __restrict__ Ys,
                                                           const float* __restrict__ w,
                                                           const int32_t* __restrict__ dest_row,
                                                           int T, int d, int k,
                                                           TS* __restrict__ dYs,
-                                                          float* __restrict__ dw) {
+                                                          float* __restrict__ dw,
+                                                          uint8_t* __restrict__ q,
+                                                          uint8_t* __restrict__ qs, long pitch) {
   const int lane = threadIdx.x & 63;
   const long t = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
@@ -267,6 +270,12 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const TS* __restrict__
         o[q] = wj * g[q];
       }
       store8(dYs + (long)r * d + c, o);
+      if constexpr (MXQ) {
+        // the stored (bf16) row, block-quantised along d for the down dgrad
+        float ro[8];
+        round_bf16_8(o, ro);
+        quant8_store(ro, q + (long)r * d + c, qs + (long)(c >> 5) * pitch + r, lane);
+      }
     }
     dot = wave_sum(dot);
     if (lane == 0) dw[t * k + j] = dot;
@@ -425,16 +434,22 @@ hipError_t launch_combine(int dtype, const void* Ys, const float* w, const int32
 
 hipError_t launch_combine_bwd(int dtype, const void* dY, const void* Ys, const float* w,
                               const int32_t* dest, int T, int d, int k, void* dYs, float* dw,
-                              hipStream_t s) {
+                              void* dYs_q, uint8_t* dYs_q_scale, hipStream_t s) {
   dim3 grid((T + 3) / 4);
-  if (dtype)
-    hipLaunchKernelGGL(combine_bwd_kernel<bf16_t>, grid, dim3(256), 0, s,
+  const long pitch = ((long)T * k + 15) / 16 * 16;
+  if (dtype && dYs_q)
+    hipLaunchKernelGGL((combine_bwd_kernel<bf16_t, true>), grid, dim3(256), 0, s,
                        static_cast<const bf16_t*>(dY), static_cast<const bf16_t*>(Ys), w, dest,
-                       T, d, k, static_cast<bf16_t*>(dYs), dw);
+                       T, d, k, static_cast<bf16_t*>(dYs), dw, static_cast<uint8_t*>(dYs_q),
+                       dYs_q_scale, pitch);
+  else if (dtype)
+    hipLaunchKernelGGL((combine_bwd_kernel<bf16_t, false>), grid, dim3(256), 0, s,
+                       static_cast<const bf16_t*>(dY), static_cast<const bf16_t*>(Ys), w, dest,
+                       T, d, k, static_cast<bf16_t*>(dYs), dw, nullptr, nullptr, 0L);
   else
-    hipLaunchKernelGGL(combine_bwd_kernel<float>, grid, dim3(256), 0, s,
+    hipLaunchKernelGGL((combine_bwd_kernel<float, false>), grid, dim3(256), 0, s,
                        static_cast<const float*>(dY), static_cast<const float*>(Ys), w, dest, T,
-                       d, k, static_cast<float*>(dYs), dw);
+                       d, k, static_cast<float*>(dYs), dw, nullptr, nullptr, 0L);
   note_launch("combine_bwd", s);
   return hipGetLastError();
 }

@@ -64,7 +64,7 @@ def run_gpu(wl: Workload, inp: Dict[str, np.ndarray], logits: Optional[np.ndarra
     names = ["topk_idx", "topk_w", "counts", "offsets", "dest_row", "src_token", "Hg", "Hu",
              "A", "Ys", "y", "dYs", "dw", "dH", "dXs", "dx", "dWg", "dWu", "dWd", "Xs"]
     if wl.prec == "mxfp8":
-        names += ["Xq", "Xq_scale"]
+        names += ["Xq", "Xq_scale", "dYs_q", "dYs_q_scale"]
     if router:
         names += ["logits", "dlogits", "dWr"]
     out = {n: to_np(getattr(layer, n)) for n in names}

@@ -89,7 +89,7 @@ def test_workspace_sizes(L):
     s, n = ws_size(L, 2, T, d, E, f, k, BF16, P_MX)
     assert s == OK and 3 * E * d * f * 33 // 32 + R * f * 33 // 32 <= n <= 3 * E * d * f * 1.1 + R * f * 1.1
     s, n = ws_size(L, 5, T, d, E, f, k, BF16, P_MX)
-    assert s == OK and 3 * E * d * f * 33 // 32 + R * (d + 2 * f) * 33 // 32 <= n
+    assert s == OK and 3 * E * d * f * 33 // 32 + R * 2 * f * 33 // 32 <= n  # weights + dH codes
     assert ws_size(L, 2, T, d, E, f, k, F32, P_MX)[0] == DTYPE
 
 
@@ -144,8 +144,8 @@ def test_ffn_fwd_validation(L):
     assert ffn_fwd(L, E=257) == UNSUP
 
 
-def ffn_bwd(L, Xs=A, dt=BF16, prec=P_BF16, f=64, dH=A, ws=A):
-    return L.moe_grouped_ffn_bwd(A, Xs, A, A, A, A, 16, 2, 64, f, 8, A, A, A, dt, prec,
+def ffn_bwd(L, Xs=A, dt=BF16, prec=P_BF16, f=64, dH=A, ws=A, dq=A, dqs=A):
+    return L.moe_grouped_ffn_bwd(A, dq, dqs, Xs, A, A, A, A, 16, 2, 64, f, 8, A, A, A, dt, prec,
                                  0, dH, A, A, A, A, ws, 1 << 20, None)
 
 
@@ -153,6 +153,8 @@ def test_ffn_bwd_validation(L):
     assert ffn_bwd(L, Xs=None) == NULL             # the weight gradients read Xs
     assert ffn_bwd(L, Xs=None, prec=P_MX) == NULL
     assert ffn_bwd(L, ws=None, prec=P_MX) == NULL  # MXFP8 quantises into the workspace
+    assert ffn_bwd(L, dq=None, prec=P_MX) == NULL  # ... and reads the quantised dYs
+    assert ffn_bwd(L, dqs=MIS, prec=P_MX) == ALIGN
     assert ffn_bwd(L, dH=None) == NULL
     assert ffn_bwd(L, f=32) == UNSUP
     assert ffn_bwd(L, dH=MIS) == ALIGN
@@ -164,7 +166,10 @@ def test_combine_and_gather_validation(L):
     assert L.moe_combine(A, A, A, 0, 64, 2, BF16, A, None) == SHAPE
     assert L.moe_combine(A, A, A, 16, 72, 2, BF16, A, None) == UNSUP
     assert L.moe_combine(A, A, A, 16, 64, 2, BF16, MIS, None) == ALIGN
-    assert L.moe_combine_bwd(A, A, A, A, 16, 64, 2, 9, A, A, None) == DTYPE
+    assert L.moe_combine_bwd(A, A, A, A, 16, 64, 2, 9, A, A, None, None, None) == DTYPE
+    assert L.moe_combine_bwd(A, A, A, A, 16, 64, 2, BF16, A, A, A, None, None) == NULL  # codes w/o scales
+    assert L.moe_combine_bwd(A, A, A, A, 16, 64, 2, F32, A, A, A, A, None) == DTYPE     # MX codes need bf16
+    assert L.moe_combine_bwd(A, A, A, A, 16, 64, 2, BF16, A, A, A, MIS, None) == ALIGN
     assert L.moe_dispatch_bwd(A, A, 16, 64, 0, BF16, 0, A, None) == SHAPE
     assert L.moe_dispatch_bwd(None, A, 16, 64, 2, BF16, 0, A, None) == NULL
 

@@ -151,6 +151,22 @@ def test_mx_dispatch_codes(name):
     np.testing.assert_array_equal(sc[:, :R].T.astype(np.int64), E + 127)
 
 
+def test_mx_combine_bwd_codes():
+    """The combine backward's block-quantised dYs, bit for bit.  With every
+    combine weight 1 the stored dYs rows are exactly the rows of dY (no
+    rounding on either side), so the oracle quantises dY[src_token]."""
+    wl, inp, _ = _layer_case("share_zipf_mxfp8")
+    inp["topk_w"] = np.ones_like(inp["topk_w"])
+    gpu = run_gpu(wl, inp, None)
+    R, d = wl.T * wl.k, wl.d
+    src = O.routing_metadata(inp["topk_idx"], wl.E)[3]
+    dYs = np.asarray(inp["dY"], np.float64)[np.asarray(src, np.int64)]
+    np.testing.assert_array_equal(gpu["dYs"], dYs)
+    _, E, q = O.mx_quantize(dYs, axis=1)
+    np.testing.assert_array_equal(gpu["dYs_q"], O.e4m3_encode(q))
+    np.testing.assert_array_equal(gpu["dYs_q_scale"][:, :R].T.astype(np.int64), E + 127)
+
+
 def test_mx_quantisation_is_applied():
     """The four block-quantised GEMM outputs match the MXFP8 oracle far more
     closely than the same layer computed in plain bf16: the 6e-2 bound alone
