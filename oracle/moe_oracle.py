@@ -437,3 +437,143 @@ def loss(x, Wr, Wg, Wu, Wd, k, dY) -> float:
     idx, w, _ = route(logits, k, "fp64")
     y = layer_forward(x, Wg, Wu, Wd, idx, w, "fp64")["y"]
     return float(np.sum(y * np.asarray(dY, F64)))
+
+
+# ---------------------------------------------------------------------------
+# sampled forms (full-size checks): the same definitions as layer_forward /
+# layer_backward / router_backward, evaluated only for chosen tokens or for
+# chosen columns of one expert, so that a full-size layer can be checked
+# without computing every output.
+# ---------------------------------------------------------------------------
+
+
+def _mxq(a, axis):
+    return mx_quantize(a, axis=axis)[0]
+
+
+def layer_tokens(x, Wr, Wg, Wu, Wd, topk_idx, topk_w, dY, tokens, prec: str = "fp64",
+                 logits=None) -> Dict[str, object]:
+    """Per-token forward + backward for the given tokens.
+
+    topk_idx / topk_w / logits are the routing of every token (logits only
+    with a router); the metadata is derived from topk_idx as in
+    routing_metadata.  Returns per-token arrays y, dw, dx (and dlogits with a
+    router) indexed like `tokens`, and per-row arrays Hg, Hu, A, Ys, dYs, dHg,
+    dHu, dXs for the rows rows = dest_row[tokens] (shape [len(tokens), k])."""
+    rnd = _storage_round(prec)
+    mx = prec == "mxfp8"
+    x = np.asarray(x, F64)
+    E = np.shape(Wg)[0]
+    idx = np.asarray(topk_idx, np.int64)
+    k = idx.shape[1]
+    _, _, dest_row, _ = routing_metadata(topk_idx, E)
+    w = np.asarray(topk_w, F64)
+    dYa = np.asarray(dY, F64)
+    tokens = np.asarray(tokens, np.int64)
+    n = len(tokens)
+    f = np.shape(Wg)[2]
+    d = x.shape[1]
+    shp_f, shp_d = (n, k, f), (n, k, d)
+    Hg, Hu, A, dHg, dHu = (np.zeros(shp_f) for _ in range(5))
+    Ys, dYs, dXs = (np.zeros(shp_d) for _ in range(3))
+    y, dx_e = np.zeros((n, d)), np.zeros((n, d))
+    dw = np.zeros((n, k))
+    cache: Dict[int, tuple] = {}
+    for a, t in enumerate(tokens):
+        for j in range(k):
+            e = int(idx[t, j])
+            if e not in cache:
+                Wge, Wue, Wde = (np.asarray(W[e], F64) for W in (Wg, Wu, Wd))
+                if mx:
+                    cache[e] = (_mxq(Wge, 0), _mxq(Wue, 0), _mxq(Wde, 0),
+                                _mxq(Wde, 1), _mxq(Wge, 1), _mxq(Wue, 1))
+                else:
+                    cache[e] = (Wge, Wue, Wde, Wde, Wge, Wue)
+            Wgf, Wuf, Wdf, Wdb, Wgb, Wub = cache[e]
+            xs = rnd(x[t])[None, :]
+            xq = _mxq(xs, 1) if mx else xs
+            hg, hu = xq @ Wgf, xq @ Wuf
+            Hg[a, j], Hu[a, j] = rnd(hg)[0], rnd(hu)[0]
+            A[a, j] = rnd(silu(hg) * hu)[0]
+            aq = _mxq(A[a, j][None, :], 1) if mx else A[a, j][None, :]
+            Ys[a, j] = rnd(aq @ Wdf)[0]
+    for a, t in enumerate(tokens):
+        acc = np.zeros(d)
+        for j in range(k):
+            acc += w[t, j] * Ys[a, j]
+        y[a] = acc
+    y = rnd(y)
+    for a, t in enumerate(tokens):
+        for j in range(k):
+            e = int(idx[t, j])
+            _, _, _, Wdb, Wgb, Wub = cache[e]
+            dw[a, j] = dYa[t] @ Ys[a, j]
+            dYs[a, j] = rnd(w[t, j] * dYa[t])
+            g = dYs[a, j][None, :]
+            gq = _mxq(g, 1) if mx else g
+            dA = (gq @ Wdb.T)[0]
+            dHg[a, j] = rnd(dA * Hu[a, j] * dsilu(Hg[a, j]))
+            dHu[a, j] = rnd(dA * silu(Hg[a, j]))
+            ag, au = dHg[a, j][None, :], dHu[a, j][None, :]
+            if mx:
+                ag, au = _mxq(ag, 1), _mxq(au, 1)
+            dXs[a, j] = rnd(ag @ Wgb.T + au @ Wub.T)[0]
+        for j in range(k):
+            dx_e[a] += dXs[a, j]
+    dw = _f32(prec)(dw)
+    dx_e = rnd(dx_e)
+    out: Dict[str, object] = dict(rows=dest_row[tokens], y=y, dw=dw, Hg=Hg, Hu=Hu, A=A, Ys=Ys,
+                                  dYs=dYs, dHg=dHg, dHu=dHu, dXs=dXs, dx=dx_e)
+    if Wr is not None:
+        p = softmax(np.asarray(logits)[tokens])
+        dp = np.zeros_like(p)
+        for a, t in enumerate(tokens):
+            for j in range(k):
+                dp[a, idx[t, j]] = dw[a, j]
+        inner = np.sum(p * dp, axis=1, keepdims=True)
+        dl = _f32(prec)(p * (dp - inner))
+        out["dlogits"] = dl
+        out["dx"] = rnd(dx_e + dl @ np.asarray(Wr, F64).T)
+    return out
+
+
+def expert_columns(x, Wg, Wu, Wd, topk_idx, topk_w, dY, e: int, cols,
+                   prec: str = "fp64") -> Dict[str, np.ndarray]:
+    """Weight gradients of expert e at the given columns c of d_ff:
+    dWg[e][:, cols], dWu[e][:, cols] and dWd[e][cols, :], each summed over all
+    of e's rows exactly as layer_backward does (the column c of Hg, Hu, A, dA
+    depends only on column c of Wg, Wu and on row c of Wd)."""
+    rnd = _storage_round(prec)
+    mx = prec == "mxfp8"
+    E = np.shape(Wg)[0]
+    _, offsets, _, src_token = routing_metadata(topk_idx, E)
+    lo, hi = int(offsets[e]), int(offsets[e + 1])
+    d = np.shape(x)[1]
+    cols = np.asarray(cols, np.int64)
+    if hi == lo:
+        z = np.zeros((d, len(cols)))
+        return dict(dWg=z, dWu=z.copy(), dWd=np.zeros((len(cols), d)))
+    # weight of each row of e: the (t, j) slot that lands on it
+    idx = np.asarray(topk_idx, np.int64)
+    w = np.asarray(topk_w, F64)
+    rows_w = np.zeros(hi - lo)
+    tok = np.asarray(src_token[lo:hi], np.int64)
+    for r, t in enumerate(tok):
+        rows_w[r] = w[t, list(idx[t]).index(e)]
+    Xs = rnd(np.asarray(x, F64)[tok])
+    Xq = _mxq(Xs, 1) if mx else Xs
+    Wgc = np.asarray(Wg[e], F64)[:, cols]
+    Wuc = np.asarray(Wu[e], F64)[:, cols]
+    Wdr = np.asarray(Wd[e], F64)[cols, :]
+    if mx:
+        Wgc, Wuc = _mxq(Wgc, 0), _mxq(Wuc, 0)
+    hg, hu = Xq @ Wgc, Xq @ Wuc
+    Hg, Hu = rnd(hg), rnd(hu)
+    A = rnd(silu(hg) * hu)
+    dYs = rnd(rows_w[:, None] * np.asarray(dY, F64)[tok])
+    g = _mxq(dYs, 1) if mx else dYs
+    Wdb = _mxq(Wdr, 1) if mx else Wdr
+    dA = g @ Wdb.T
+    dHg = rnd(dA * Hu * dsilu(Hg))
+    dHu = rnd(dA * silu(Hg))
+    return dict(dWg=rnd(Xs.T @ dHg), dWu=rnd(Xs.T @ dHu), dWd=rnd(A.T @ dYs))

@@ -444,3 +444,45 @@ def test_mx_layer_block_axes():
     for key in ("dHg", "dHu"):
         np.testing.assert_array_equal(r[key][rows0, 9], base[key][rows0, 9] * S)
         np.testing.assert_array_equal(np.delete(r[key], 9, 1), np.delete(base[key], 9, 1))
+
+
+# ---------------------------------------------------------------------------
+# sampled forms used by the full-size GPU checks
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("prec", ["fp64", "bf16", "mxfp8"])
+@pytest.mark.parametrize("router", [True, False])
+def test_sampled_forms_match_full_layer(prec, router):
+    """layer_tokens and expert_columns restate the layer for chosen tokens and
+    for chosen d_ff columns of one expert; on a small layer they must give the
+    full oracle's values at those places (up to float64 summation order)."""
+    rng = _rng(21)
+    T, d, E, f, k = 96, 64, 4, 64, 2
+    q = (lambda a: O.round_bf16(a)) if prec != "fp64" else (lambda a: a)
+    x = q(rng.standard_normal((T, d)))
+    Wg, Wu, Wd = (q(a) for a in _weights(rng, d, E, f, 0.1))
+    dY = q(rng.standard_normal((T, d)))
+    if router:
+        Wr = q(rng.standard_normal((d, E)) * 0.1)
+        ref = O.layer(x, Wr, Wg, Wu, Wd, k, dY, prec)
+        idx, w, logits = ref["topk_idx"], ref["topk_w"], ref["logits"]
+    else:
+        Wr, logits = None, None
+        idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+        w = rng.uniform(0, 1, (T, k)).astype(np.float32)
+        ref = O.layer(x, None, Wg, Wu, Wd, k, dY, prec, topk_idx=idx, topk_w=w)
+    tokens = np.array([0, 5, 17, 40, 95])
+    s = O.layer_tokens(x, Wr, Wg, Wu, Wd, idx, w, dY, tokens, prec, logits=logits)
+    close = dict(rtol=1e-9, atol=1e-12)
+    rows = s["rows"]
+    for key in ("Hg", "Hu", "A", "Ys", "dYs", "dHg", "dHu", "dXs"):
+        np.testing.assert_allclose(s[key], ref[key][rows], err_msg=key, **close)
+    for key in ("y", "dx") + (("dlogits",) if router else ()):
+        np.testing.assert_allclose(s[key], np.asarray(ref[key])[tokens], err_msg=key, **close)
+    np.testing.assert_allclose(s["dw"], ref["dw"][tokens], **close)
+    cols = np.array([3, 30, 63])
+    for e in range(E):
+        c = O.expert_columns(x, Wg, Wu, Wd, idx, w, dY, e, cols, prec)
+        np.testing.assert_allclose(c["dWg"], ref["dWg"][e][:, cols], **close)
+        np.testing.assert_allclose(c["dWu"], ref["dWu"][e][:, cols], **close)
+        np.testing.assert_allclose(c["dWd"], ref["dWd"][e][cols, :], **close)
