@@ -53,6 +53,119 @@ def gemm_flops(name: str, wl) -> float:
     return 0.0
 
 
+# ---------------------------------------------------------------------------
+# measured HBM traffic per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE)
+# ---------------------------------------------------------------------------
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+CSRC = os.path.join(ROOT, "routing_grouped_gemm_amd", "csrc")
+
+# rocprofv3 kernel symbol -> the library's launch names, in launch order
+# within one step (the weight-gradient kernel runs twice per step)
+_SYMBOLS = {
+    "gemm_bf16_kernel<0>": ["gemm_fwd_gateup_swiglu"],
+    "gemm_bf16_kernel<1>": ["gemm_fwd_down"],
+    "gemm_bf16_kernel<2>": ["gemm_dgrad_down_swiglu_bwd"],
+    "gemm_bf16_kernel<3>": ["gemm_dgrad_gateup"],
+    "gemm_bf16_kernel<4>": ["gemm_wgrad_gateup", "gemm_wgrad_down"],
+    "gemm_bf16_kernel<5>": ["gemm_router_logits"],
+    "gemm_bf16_kernel<7>": ["gemm_router_dx"],
+    "gemm_bf16_kernel<12>": ["gemm_router_dwr"],
+    "gemm_mx_kernel<8>": ["gemm_mx_fwd_gateup_swiglu"],
+    "gemm_mx_kernel<9>": ["gemm_mx_fwd_down"],
+    "gemm_mx_kernel<10>": ["gemm_mx_dgrad_down_swiglu_bwd"],
+    "gemm_mx_kernel<11>": ["gemm_mx_dgrad_gateup"],
+    "dispatch_copy_kernel": ["dispatch_copy"],
+    "mx_dispatch_kernel": ["mx_dispatch_quant"],
+    "combine_kernel": ["combine"],
+    "combine_bwd_kernel": ["combine_bwd"],
+    "gather_sum_kernel": ["gather_sum"],
+}
+
+
+def source_hash() -> str:
+    """Digest of the HIP sources: measured traffic is reported only for the
+    kernels it was measured on."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for path in sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.h"))):
+        h.update(os.path.basename(path).encode())
+        with open(path, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _counter_means(directory: str):
+    """Mean counter value per launch name from a rocprofv3 --pmc csv directory."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {directory}")
+    rows = []
+    for path in files:
+        with open(path) as fh:
+            rows += list(csv.DictReader(fh))
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    seen = {}
+    acc = {}
+    for r in rows:
+        name = r["Kernel_Name"].split("(")[0].replace("void ", "").replace("moe::mf::", "")
+        name = name.replace("moe::", "")
+        sym = next((k for k in _SYMBOLS if name.startswith(k.split("<")[0]) and
+                    (("<" not in k) or name.startswith(k))), name)
+        n = seen.get(sym, 0)
+        seen[sym] = n + 1
+        names = _SYMBOLS.get(sym, [sym])
+        launch = names[n % len(names)]
+        acc.setdefault(launch, []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def write_traffic(workload_name, fetch_dir, write_dir, cal_fetch_dir, cal_write_dir) -> int:
+    fetch, write = _counter_means(fetch_dir), _counter_means(write_dir)
+    cf = _counter_means(cal_fetch_dir)["__amd_rocclr_copyBuffer"]
+    cw = _counter_means(cal_write_dir)["__amd_rocclr_copyBuffer"]
+    # the calibration copy moves exactly 1 GiB each way; counters are in KiB
+    sf, sw = (1 << 30) / (cf * 1024.0), (1 << 30) / (cw * 1024.0)
+    data = {}
+    if os.path.exists(TRAFFIC_JSON):
+        with open(TRAFFIC_JSON) as fh:
+            data = json.load(fh)
+    h = source_hash()
+    if data.get("source_hash") != h:
+        data = {"source_hash": h, "workloads": {}}
+    data["workloads"][workload_name] = {
+        "calibration": {"fetch_scale": round(sf, 4), "write_scale": round(sw, 4),
+                        "copy_bytes": 1 << 30},
+        "kernels": {k: {"fetch_bytes": int(fetch[k] * 1024 * sf),
+                        "write_bytes": int(write.get(k, 0.0) * 1024 * sw)}
+                    for k in sorted(fetch)},
+    }
+    os.makedirs(os.path.dirname(TRAFFIC_JSON), exist_ok=True)
+    with open(TRAFFIC_JSON, "w") as fh:
+        json.dump(data, fh, indent=1, sort_keys=True)
+    print(json.dumps({"traffic_json": TRAFFIC_JSON, "workload": workload_name,
+                      "kernels": len(fetch), "source_hash": h}))
+    return 0
+
+
+def measured_traffic(workload_name: str, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or
+    None when there is none or the sources changed since it was taken."""
+    try:
+        with open(TRAFFIC_JSON) as fh:
+            data = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if data.get("source_hash") != source_hash():
+        return None
+    k = data.get("workloads", {}).get(workload_name, {}).get("kernels", {}).get(kernel)
+    if not k:
+        return None
+    return k["fetch_bytes"] + k["write_bytes"]
+
+
 def cpu_baseline(wl, inp, tokens: int):
     """The CPU oracle, as it is, on the first `tokens` tokens (or rows)."""
     import numpy as np
@@ -80,17 +193,24 @@ def cpu_baseline(wl, inp, tokens: int):
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="olmoe_bf16")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--cpu-tokens", type=int, default=1024,
+    ap.add_argument("--cpu-tokens", type=int, default=2048,
                     help="tokens of the CPU-oracle sample (0 = skip the CPU baseline)")
     ap.add_argument("--kernels", action="store_true", help="per-kernel table on stderr")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times (the "
                          "known-size reference for HBM byte counters) and exit")
+    ap.add_argument("--traffic", nargs=4, metavar=("FETCH", "WRITE", "CAL_FETCH", "CAL_WRITE"),
+                    help="only summarise four rocprofv3 --pmc output directories (FETCH_SIZE and "
+                         "WRITE_SIZE of this workload, then of --calibrate-copy 1024) into "
+                         + TRAFFIC_JSON + " and exit")
     args = ap.parse_args(argv)
+
+    if args.traffic:
+        return write_traffic(args.workload, *args.traffic)
 
     if args.calibrate_copy:
         import torch
@@ -144,15 +264,19 @@ def main(argv=None) -> int:
     t_end = torch.cuda.Event(enable_timing=True)
     timer = rgg.KernelTimer(capacity=K * 32)
     torch.cuda.synchronize()
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
     w0 = time.perf_counter()
     with timer:
         t_start.record()
-        for _ in range(K):
+        for i in range(K):
+            marks[i].record()
             step()
+        marks[K].record()
         t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     ms = t_start.elapsed_time(t_end) / K
+    step_ms = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(K)])
     kern = timer.durations()
 
     per = {}
@@ -162,7 +286,9 @@ def main(argv=None) -> int:
         c[1] += dur
     table = sorted(((n, c[0] / K, c[1] / K, c[1] / c[0]) for n, c in per.items()),
                    key=lambda r: -r[2])
-    gemm_ms = sum(r[2] for r in table if r[0].startswith("gemm_") and "router" not in r[0])
+    # expert FFN time: the expert GEMMs, and for MXFP8 also the quantizers
+    gemm_ms = sum(r[2] for r in table if (r[0].startswith("gemm_") and "router" not in r[0])
+                  or r[0].startswith("mx_"))
     dom = table[0]
     dom_name, dom_launch_ms = dom[0], dom[3]
     dom_flops = gemm_flops(dom_name, wl)
@@ -173,12 +299,13 @@ def main(argv=None) -> int:
     if dom_flops > 0:
         ach = dom_flops / (dom_launch_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "kernel": dom_name, "achieved": round(ach, 2), "peak": dom_peak,
-                "unit": "TFLOP/s", "frac": round(ach / dom_peak, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(ach / dom_peak, 4),
+                "traffic": measured_traffic(wl.name, dom_name),
                 "per_launch_ms": round(dom_launch_ms, 4),
                 "algorithmic_flops_per_launch": dom_flops}
     else:
         roof = {"bound": "hbm", "kernel": dom_name, "achieved": None, "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": None, "traffic": None}
+                "unit": "GB/s", "frac": None, "traffic": measured_traffic(wl.name, dom_name)}
 
     flops = wl.flops()
     tok_s = wl.T / (ms * 1e-3)
@@ -216,6 +343,9 @@ def main(argv=None) -> int:
         "ffn_gemm_tflops": None if ffn_tflops is None else round(ffn_tflops, 2),
         "ffn_gemm_pct_peak": None if ffn_tflops is None else round(100.0 * ffn_tflops / peak, 2),
         "wall_ms_per_step": round(wall * 1e3 / K, 4),
+        "step_ms": {"median": round(float(np.median(step_ms)), 4),
+                    "p10": round(float(np.percentile(step_ms, 10)), 4),
+                    "p90": round(float(np.percentile(step_ms, 90)), 4)},
         "kernels_ms_per_step": {n: round(tot, 4) for n, _, tot, _ in table},
         "roofline": roof,
         "cpu_baseline": cpu,
