@@ -199,12 +199,44 @@ def softmax(logits) -> np.ndarray:
     return z / z.sum(axis=-1, keepdims=True)
 
 
-def route(logits, k: int, prec: str = "bf16"):
-    """Top-k experts and their (unrenormalised) softmax weights, float32."""
+def route(logits, k: int, prec: str = "bf16", renorm: bool = False):
+    """Top-k experts and their softmax weights, float32.
+
+    renorm (the page's optional top-k renormalisation, off by default): the k
+    chosen probabilities are divided by their sum, so each token's weights
+    add up to 1."""
     idx = topk_select(logits, k)
     p = softmax(logits)
-    w = _f32(prec)(np.take_along_axis(p, idx.astype(np.int64), axis=1))
-    return idx, w, p
+    w = np.take_along_axis(p, idx.astype(np.int64), axis=1)
+    if renorm:
+        w = w / np.sum(w, axis=1, keepdims=True)
+    return idx, _f32(prec)(w), p
+
+
+def aux_loss(logits, topk_idx, E: int, coef: float = 0.01, prec: str = "bf16"):
+    """Switch-style load-balancing loss of one layer (HF OLMoE walkthrough,
+    section 4: the experts' assignment frequencies times their mean router
+    probabilities, summed; scaled by router_aux_loss_coef, default 0.01).
+
+    Reading of what the page leaves open: f_e is the share of the T*k routed
+    slots that go to expert e (sum_e f_e = 1), P_e the mean over tokens of the
+    softmax probability of e, and L = coef * E * sum_e f_e * P_e, so that
+    perfectly balanced routing gives L = coef.  The top-k choice (so f) is
+    piecewise constant in the logits; the gradient reaches the logits through
+    P only: dL/dp[t,e] = coef * E * f_e / T for every token t.
+    Returns (L, dL/dp per expert [E], float32 unless prec is fp64)."""
+    p = softmax(logits)
+    T = p.shape[0]
+    idx = np.asarray(topk_idx, np.int64)
+    k = idx.shape[1]
+    counts = np.zeros(E)
+    for t in range(T):
+        for j in range(k):
+            counts[idx[t, j]] += 1
+    f = counts / (T * k)
+    P = np.mean(p, axis=0)
+    L = coef * E * float(np.sum(f * P))
+    return L, _f32(prec)(coef * E * f / T)
 
 
 # ---------------------------------------------------------------------------
@@ -385,18 +417,34 @@ def layer_backward(fwd, x, Wg, Wu, Wd, topk_idx, topk_w, dY, prec: str = "fp64")
     return dict(dw=dw, dYs=dYs, dHg=dHg, dHu=dHu, dXs=dXs, dx=dx, dWg=dWg, dWu=dWu, dWd=dWd)
 
 
-def router_backward(x, Wr, logits, topk_idx, dw, dx_experts, prec: str = "fp64"):
+def router_backward(x, Wr, logits, topk_idx, dw, dx_experts, prec: str = "fp64",
+                    renorm: bool = False, aux_dp=None):
     """Router backward: dp[t,e] = dw[t,j] where e = idx[t,j], else 0;
     dlogits = p * (dp - <p, dp>) (softmax backward); dWr = x^T.dlogits;
-    dx = dx_experts + dlogits.Wr^T.  dlogits is float32."""
+    dx = dx_experts + dlogits.Wr^T.  dlogits is float32.
+
+    renorm: w_j = p_{e_j} / S with S the sum of the chosen probabilities, so
+    dp[t, e_m] = (dw_m - sum_j dw_j w_j) / S for the chosen experts (0 for the
+    others).  aux_dp (from aux_loss): added to dp[t, e] for every token."""
     rnd = _storage_round(prec)
     p = softmax(logits)
     T, E = p.shape
     dp = np.zeros((T, E))
     idx = np.asarray(topk_idx, np.int64)
+    dw = np.asarray(dw, F64)
     for t in range(T):
-        for j in range(idx.shape[1]):
-            dp[t, idx[t, j]] = dw[t, j]
+        if renorm:
+            pc = p[t, idx[t]]
+            S = float(np.sum(pc))
+            w = pc / S
+            inner_w = float(np.sum(dw[t] * w))
+            for j in range(idx.shape[1]):
+                dp[t, idx[t, j]] = (dw[t, j] - inner_w) / S
+        else:
+            for j in range(idx.shape[1]):
+                dp[t, idx[t, j]] = dw[t, j]
+    if aux_dp is not None:
+        dp += np.asarray(aux_dp, F64)[None, :]
     inner = np.sum(p * dp, axis=1, keepdims=True)
     dlogits = _f32(prec)(p * (dp - inner))
     x = np.asarray(x, F64)
@@ -406,37 +454,49 @@ def router_backward(x, Wr, logits, topk_idx, dw, dx_experts, prec: str = "fp64")
 
 
 def layer(x, Wr, Wg, Wu, Wd, k, dY, prec: str = "fp64", logits=None,
-          topk_idx=None, topk_w=None) -> Dict[str, np.ndarray]:
+          topk_idx=None, topk_w=None, renorm: bool = False,
+          aux_coef: float = 0.0) -> Dict[str, np.ndarray]:
     """Whole layer forward + backward.
 
     With a router (Wr given): logits = x.Wr unless `logits` is passed in,
-    then top-k routing.  Without one (pre-routed rows) topk_idx / topk_w are
+    then top-k routing (renormalised with `renorm`).  aux_coef > 0 adds the
+    load-balancing loss (aux_loss) to the loss whose gradient the backward
+    computes.  Without a router (pre-routed rows) topk_idx / topk_w are
     inputs and there is no router backward."""
     out: Dict[str, np.ndarray] = {}
+    aux_dp = None
     if Wr is not None:
         if logits is None:
             logits = router_logits(x, Wr, prec)
-        topk_idx, topk_w, _ = route(logits, k, prec)
+        topk_idx, topk_w, _ = route(logits, k, prec, renorm)
         out.update(logits=np.asarray(logits, F64), topk_idx=topk_idx, topk_w=topk_w)
+        if aux_coef:
+            L, aux_dp = aux_loss(logits, topk_idx, np.shape(Wg)[0], aux_coef, prec)
+            out.update(aux_loss=L, aux_dp=aux_dp)
     fwd = layer_forward(x, Wg, Wu, Wd, topk_idx, topk_w, prec)
     out.update(fwd)
     if dY is not None:
         bwd = layer_backward(fwd, x, Wg, Wu, Wd, topk_idx, topk_w, dY, prec)
         out.update(bwd)
         if Wr is not None:
-            rb = router_backward(x, Wr, logits, topk_idx, bwd["dw"], bwd["dx"], prec)
+            rb = router_backward(x, Wr, logits, topk_idx, bwd["dw"], bwd["dx"], prec, renorm,
+                                 aux_dp)
             out["dx_experts"] = bwd["dx"]
             out.update(rb)
     return out
 
 
-def loss(x, Wr, Wg, Wu, Wd, k, dY) -> float:
-    """L = sum_t <y[t], dY[t]> of the layer in float64 with no rounding,
-    routing taken on unrounded logits (used by the finite-difference pin)."""
+def loss(x, Wr, Wg, Wu, Wd, k, dY, renorm: bool = False, aux_coef: float = 0.0) -> float:
+    """L = sum_t <y[t], dY[t]> (+ the load-balancing loss) of the layer in
+    float64 with no rounding, routing taken on unrounded logits (used by the
+    finite-difference pins)."""
     logits = router_logits(x, Wr, "fp64")
-    idx, w, _ = route(logits, k, "fp64")
+    idx, w, _ = route(logits, k, "fp64", renorm)
     y = layer_forward(x, Wg, Wu, Wd, idx, w, "fp64")["y"]
-    return float(np.sum(y * np.asarray(dY, F64)))
+    L = float(np.sum(y * np.asarray(dY, F64)))
+    if aux_coef:
+        L += aux_loss(logits, idx, np.shape(Wg)[0], aux_coef, "fp64")[0]
+    return L
 
 
 # ---------------------------------------------------------------------------

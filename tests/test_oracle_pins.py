@@ -486,3 +486,85 @@ def test_sampled_forms_match_full_layer(prec, router):
         np.testing.assert_allclose(c["dWg"], ref["dWg"][e][:, cols], **close)
         np.testing.assert_allclose(c["dWu"], ref["dWu"][e][:, cols], **close)
         np.testing.assert_allclose(c["dWd"], ref["dWd"][e][cols, :], **close)
+
+
+# ---------------------------------------------------------------------------
+# router variants: top-k renormalisation and the load-balancing loss
+# ---------------------------------------------------------------------------
+
+def test_renorm_closed_forms():
+    rng = _rng(31)
+    T, E, k = 40, 8, 3
+    logits = rng.standard_normal((T, E))
+    idx, w, p = O.route(logits, k, "fp64")
+    idx_r, w_r, _ = O.route(logits, k, "fp64", renorm=True)
+    np.testing.assert_array_equal(idx, idx_r)                      # same choice
+    np.testing.assert_allclose(w_r.sum(axis=1), 1.0, rtol=1e-12)   # weights add to 1
+    np.testing.assert_allclose(w_r[:, 1:] / w_r[:, :1], w[:, 1:] / w[:, :1], rtol=1e-12)
+    # k = E: the chosen probabilities already add to 1
+    _, wE, _ = O.route(logits, E, "fp64")
+    _, wE_r, _ = O.route(logits, E, "fp64", renorm=True)
+    np.testing.assert_allclose(wE_r, wE, rtol=1e-12)
+
+
+def test_aux_loss_closed_forms():
+    T, E, k, c = 64, 8, 2, 0.01
+    # all logits equal: p = 1/E, ties choose experts 0..k-1 for every token
+    logits = np.zeros((T, E))
+    idx, _, _ = O.route(logits, k, "fp64")
+    L, dp = O.aux_loss(logits, idx, E, c, "fp64")
+    assert abs(L - c) < 1e-15
+    f = np.zeros(E); f[:k] = 1.0 / k
+    np.testing.assert_allclose(dp, c * E * f / T, rtol=1e-15)
+    # balanced routing (every expert gets T*k/E slots), any probabilities: L = c
+    rng = _rng(32)
+    logits = rng.standard_normal((T, E))
+    idx = np.array([[(2 * t) % E, (2 * t + 1) % E] for t in range(T)], np.int32)
+    L, _ = O.aux_loss(logits, idx, E, c, "fp64")
+    assert abs(L - c) < 1e-12
+    # collapse: top-1 to expert 0 with p_0 -> 1 gives L -> c * E
+    logits = np.full((T, E), -60.0); logits[:, 0] = 60.0
+    idx, _, _ = O.route(logits, 1, "fp64")
+    L, _ = O.aux_loss(logits, idx, E, c, "fp64")
+    assert abs(L - c * E) < 1e-12
+
+
+@pytest.mark.parametrize("renorm,aux", [(True, 0.0), (False, 0.05), (True, 0.05)])
+def test_finite_differences_router_variants(renorm, aux):
+    """Central differences of L = sum <y, dY> (+ the load-balancing loss) with
+    renormalised weights and/or the auxiliary loss, on all of Wr and 32 seeded
+    coordinates of x, skipping coordinates where the routing changes."""
+    from moe_synth import workload, make_inputs
+    wl = workload("tiny_fp32", T=48)
+    inp = make_inputs(wl, seed=1)
+    arrs = {n: inp[n].astype(np.float64) for n in ("x", "Wr", "Wg", "Wu", "Wd", "dY")}
+    out = O.layer(arrs["x"], arrs["Wr"], arrs["Wg"], arrs["Wu"], arrs["Wd"], wl.k, arrs["dY"],
+                  "fp64", renorm=renorm, aux_coef=aux)
+    grads = dict(x=out["dx"], Wr=out["dWr"])
+    rng = _rng(33)
+    h = 1e-5
+    skipped = 0
+    for name in ("Wr", "x"):
+        a = arrs[name]
+        if name == "Wr":
+            coords = list(np.ndindex(a.shape))
+        else:
+            coords = [np.unravel_index(i, a.shape) for i in rng.choice(a.size, 32, replace=False)]
+        fd, an = [], []
+        for c in coords:
+            vals, routes = [], []
+            for sgn in (1, -1):
+                b = dict(arrs)
+                b[name] = a.copy(); b[name][c] += sgn * h
+                routes.append(O.topk_select(b["x"] @ b["Wr"], wl.k))
+                vals.append(O.loss(b["x"], b["Wr"], b["Wg"], b["Wu"], b["Wd"], wl.k, b["dY"],
+                                   renorm, aux))
+            if not np.array_equal(routes[0], routes[1]):
+                skipped += 1
+                continue
+            fd.append((vals[0] - vals[1]) / (2 * h))
+            an.append(grads[name][c])
+        fd, an = np.array(fd), np.array(an)
+        err = np.linalg.norm(fd - an) / np.linalg.norm(an)
+        assert err <= 1e-6, (name, err)
+    assert skipped <= 8, skipped
