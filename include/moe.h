@@ -70,13 +70,16 @@ enum moe_prec { MOE_PREC_F32 = 0, MOE_PREC_BF16 = 1, MOE_PREC_MXFP8 = 2 };
 
 /* moe_route flags */
 #define MOE_ROUTE_LOGITS_IN 0x1u   /* logits are an input: x and Wr are not read */
+/* moe_route / moe_route_bwd flag: renormalise the top-k weights to sum to 1 */
+#define MOE_ROUTE_RENORM 0x4u
 /* moe_grouped_ffn_bwd / moe_dispatch_bwd / moe_route_bwd flags */
 #define MOE_ACCUMULATE 0x2u        /* add into the output (dW*, dx, dWr) instead of overwriting */
 
 /* Operation ids for moe_workspace_size. */
 enum moe_op {
   MOE_OP_ROUTE = 0, MOE_OP_DISPATCH = 1, MOE_OP_FFN_FWD = 2, MOE_OP_COMBINE = 3,
-  MOE_OP_COMBINE_BWD = 4, MOE_OP_FFN_BWD = 5, MOE_OP_DISPATCH_BWD = 6, MOE_OP_ROUTE_BWD = 7
+  MOE_OP_COMBINE_BWD = 4, MOE_OP_FFN_BWD = 5, MOE_OP_DISPATCH_BWD = 6, MOE_OP_ROUTE_BWD = 7,
+  MOE_OP_ROUTE_AUX = 8
 };
 
 /*
@@ -84,8 +87,9 @@ enum moe_op {
  * HF OLMoE walkthrough, section 2: logits = x . Wr (router weight without
  * bias; the page stores it as (E, d), here it is its transpose Wr[d,E]),
  * softmax over the experts in float32, the top_k experts per token, the
- * softmax probabilities of the chosen experts as weights (no
- * renormalisation, the page's default).
+ * softmax probabilities of the chosen experts as weights: as they are (the
+ * page's default), or with MOE_ROUTE_RENORM divided by their sum (the page's
+ * optional top-k renormalisation).
  *   x[T,d] (dtype), Wr[d,E] (dtype) -> logits[T,E] f32 (written unless
  *   MOE_ROUTE_LOGITS_IN, then read), topk_idx[T,k] i32, topk_w[T,k] f32.
  *   Slots are ordered by (logit desc, expert index asc): ties go to the
@@ -197,7 +201,11 @@ int moe_dispatch_bwd(const void* dXs, const int32_t* dest_row, int T, int d, int
 
 /*
  * moe_route_bwd -- router backward for the weight gradient dtopk_w.
- *   dp[t,e] = dtopk_w[t,j] where e = topk_idx[t,j], else 0
+ *   dp[t,e] = dtopk_w[t,j] where e = topk_idx[t,j], else 0; with
+ *             MOE_ROUTE_RENORM (weights p/S, S = sum of the chosen p):
+ *             dp[t,e_m] = (dtopk_w[t,m] - sum_j dtopk_w[t,j] w[t,j]) / S;
+ *             plus aux_dp[e] (optional, [E] f32, from moe_route_aux) for
+ *             every token
  *   dlogits = p * (dp - <p, dp>), p = softmax(logits)    (f32 [T,E])
  *   dWr     = x^T . dlogits                               (dtype [d,E])
  *   dx     += dlogits . Wr^T                              (dtype [T,d], always added)
@@ -207,9 +215,26 @@ int moe_dispatch_bwd(const void* dXs, const int32_t* dest_row, int T, int d, int
  *   Workspace: moe_workspace_size(MOE_OP_ROUTE_BWD, ...).
  */
 int moe_route_bwd(const void* x, const void* Wr, const float* logits,
-                  const int32_t* topk_idx, const float* dtopk_w, int T, int d, int E, int k,
-                  int dtype, unsigned flags, float* dlogits, void* dWr, void* dx, void* ws,
-                  size_t ws_bytes, void* stream);
+                  const int32_t* topk_idx, const float* dtopk_w, const float* aux_dp, int T,
+                  int d, int E, int k, int dtype, unsigned flags, float* dlogits, void* dWr,
+                  void* dx, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_route_aux -- load-balancing loss of the router and its gradient.
+ * HF OLMoE walkthrough, section 4 (Switch-Transformer-style loss: expert
+ * assignment frequencies times router probabilities, summed; coefficient
+ * router_aux_loss_coef, default 0.01).  With f_e = counts[e] / (T*k) (the
+ * share of routed slots, counts as written by moe_dispatch) and
+ * P_e = (1/T) sum_t softmax(logits[t])[e]:
+ *   aux_loss[0] = coef * E * sum_e f_e * P_e             (f32, device)
+ *   aux_dp[e]   = coef * E * f_e / T                      (f32 [E], the
+ *                 gradient with respect to every token's probability of e;
+ *                 pass it to moe_route_bwd)
+ *   Sums are in a fixed order (per 64-token block, then over blocks).
+ *   Workspace: moe_workspace_size(MOE_OP_ROUTE_AUX, ...).
+ */
+int moe_route_aux(const float* logits, const int32_t* counts, int T, int E, int k, float coef,
+                  float* aux_loss, float* aux_dp, void* ws, size_t ws_bytes, void* stream);
 
 /* Workspace bytes an operation needs for these sizes (0 is a valid answer). */
 int moe_workspace_size(int op, int T, int d, int E, int f, int k, int dtype, int prec,

@@ -24,8 +24,8 @@ import torch
 __all__ = [
     "lib", "moe_route", "moe_dispatch", "moe_grouped_ffn_fwd", "moe_combine",
     "moe_combine_bwd", "moe_grouped_ffn_bwd", "moe_dispatch_bwd", "moe_route_bwd",
-    "moe_workspace_size", "moe_status_string", "ExpertLayer", "LIB_PATH",
-    "MOE_ROUTE_LOGITS_IN", "MOE_ACCUMULATE", "KernelTimer", "upload", "mx_scale_pitch",
+    "moe_route_aux", "moe_workspace_size", "moe_status_string", "ExpertLayer", "LIB_PATH",
+    "MOE_ROUTE_LOGITS_IN", "MOE_ROUTE_RENORM", "MOE_ACCUMULATE", "KernelTimer", "upload", "mx_scale_pitch",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_hip.so")
@@ -34,8 +34,9 @@ MOE_F32, MOE_BF16 = 0, 1
 PREC = {"fp32": 0, "bf16": 1, "mxfp8": 2}
 MOE_ROUTE_LOGITS_IN = 0x1
 MOE_ACCUMULATE = 0x2
+MOE_ROUTE_RENORM = 0x4
 OPS = {"route": 0, "dispatch": 1, "ffn_fwd": 2, "combine": 3, "combine_bwd": 4,
-       "ffn_bwd": 5, "dispatch_bwd": 6, "route_bwd": 7}
+       "ffn_bwd": 5, "dispatch_bwd": 6, "route_bwd": 7, "route_aux": 8}
 
 _P, _I, _U, _S = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint, ctypes.c_size_t
 _SIGS = {
@@ -48,7 +49,8 @@ _SIGS = {
     "moe_grouped_ffn_bwd": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _I,
                             _I, _U, _P, _P, _P, _P, _P, _P, _S, _P],
     "moe_dispatch_bwd": [_P, _P, _I, _I, _I, _I, _U, _P, _P],
-    "moe_route_bwd": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _U, _P, _P, _P, _P, _S, _P],
+    "moe_route_bwd": [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _U, _P, _P, _P, _P, _S, _P],
+    "moe_route_aux": [_P, _P, _I, _I, _I, ctypes.c_float, _P, _P, _P, _S, _P],
     "moe_workspace_size": [_I, _I, _I, _I, _I, _I, _I, _I, ctypes.POINTER(ctypes.c_size_t)],
 }
 
@@ -136,12 +138,12 @@ def moe_workspace_size(op: str, T: int, d: int, E: int, f: int, k: int, dtype: t
     return out.value
 
 
-def moe_route(x, Wr, k, logits, topk_idx, topk_w, logits_in=False, stream=None):
+def moe_route(x, Wr, k, logits, topk_idx, topk_w, logits_in=False, renorm=False, stream=None):
     T, E = logits.shape
     d = x.shape[1] if x is not None else 64
     dt = _dtype(x) if x is not None else MOE_BF16
-    _check(lib().moe_route(_ptr(x), _ptr(Wr), T, d, E, k, dt,
-                           MOE_ROUTE_LOGITS_IN if logits_in else 0, _ptr(logits),
+    flags = (MOE_ROUTE_LOGITS_IN if logits_in else 0) | (MOE_ROUTE_RENORM if renorm else 0)
+    _check(lib().moe_route(_ptr(x), _ptr(Wr), T, d, E, k, dt, flags, _ptr(logits),
                            _ptr(topk_idx), _ptr(topk_w), None, 0, _stream(stream)), "moe_route")
 
 
@@ -210,15 +212,23 @@ def moe_dispatch_bwd(dXs, dest_row, dx, accumulate=False, stream=None):
 
 
 def moe_route_bwd(x, Wr, logits, topk_idx, dtopk_w, dlogits, dWr, dx, ws=None, accumulate=False,
-                  stream=None):
+                  renorm=False, aux_dp=None, stream=None):
     T, d = x.shape
     E = Wr.shape[1]
     k = topk_idx.shape[1]
     wp, wb = _ws(ws)
-    _check(lib().moe_route_bwd(_ptr(x), _ptr(Wr), _ptr(logits), _ptr(topk_idx), _ptr(dtopk_w), T,
-                               d, E, k, _dtype(x), MOE_ACCUMULATE if accumulate else 0,
-                               _ptr(dlogits), _ptr(dWr), _ptr(dx), wp, wb, _stream(stream)),
+    flags = (MOE_ACCUMULATE if accumulate else 0) | (MOE_ROUTE_RENORM if renorm else 0)
+    _check(lib().moe_route_bwd(_ptr(x), _ptr(Wr), _ptr(logits), _ptr(topk_idx), _ptr(dtopk_w),
+                               _ptr(aux_dp), T, d, E, k, _dtype(x), flags, _ptr(dlogits),
+                               _ptr(dWr), _ptr(dx), wp, wb, _stream(stream)),
            "moe_route_bwd")
+
+
+def moe_route_aux(logits, counts, k, coef, aux_loss, aux_dp, ws, stream=None):
+    T, E = logits.shape
+    wp, wb = _ws(ws)
+    _check(lib().moe_route_aux(_ptr(logits), _ptr(counts), T, E, k, float(coef), _ptr(aux_loss),
+                               _ptr(aux_dp), wp, wb, _stream(stream)), "moe_route_aux")
 
 
 class KernelTimer:
@@ -266,16 +276,21 @@ class KernelTimer:
 class ExpertLayer:
     """Buffers and launch order of one MoE expert layer, forward and backward.
 
-    router=True: top-k softmax router on x.Wr (or on given logits).
+    router=True: top-k softmax router on x.Wr (or on given logits), with the
+    top-k weights renormalised to sum to 1 when renorm=True, and the
+    load-balancing loss (coefficient aux_coef, into aux_loss) and its
+    gradient added to the router backward when aux_coef != 0.
     router=False: pre-routed rows (topk_idx / topk_w are inputs, no router
     backward).  All buffers are allocated once, on construction."""
 
     def __init__(self, T: int, d: int, E: int, f: int, k: int, dtype=torch.bfloat16,
-                 prec: str = "bf16", router: bool = True, device="cuda"):
+                 prec: str = "bf16", router: bool = True, device="cuda", renorm: bool = False,
+                 aux_coef: float = 0.0):
         lib()
         self.T, self.d, self.E, self.f, self.k = T, d, E, f, k
         self.R = R = T * k
         self.dtype, self.prec, self.router = dtype, prec, router
+        self.renorm, self.aux_coef = renorm, float(aux_coef)
         dev = torch.device(device)
         z = lambda *s, dt=dtype: torch.empty(*s, dtype=dt, device=dev)
         i32, f32 = torch.int32, torch.float32
@@ -305,6 +320,8 @@ class ExpertLayer:
         self.dWg, self.dWu, self.dWd = z(E, d, f), z(E, d, f), z(E, f, d)
         self.dlogits = z(T, E, dt=f32)
         self.dWr = z(d, E)
+        self.aux_loss = z(1, dt=f32)
+        self.aux_dp = z(E, dt=f32)
 
         def ws(op):
             n = moe_workspace_size(op, T, d, E, f, k, dtype, prec)
@@ -313,6 +330,7 @@ class ExpertLayer:
         self.ws_fwd = ws("ffn_fwd")
         self.ws_bwd = ws("ffn_bwd")
         self.ws_route_bwd = ws("route_bwd")
+        self.ws_route_aux = ws("route_aux")
 
     def forward(self, x, Wr, Wg, Wu, Wd, topk_idx=None, topk_w=None, logits=None, stream=None):
         self.x, self.Wr, self.Wg, self.Wu, self.Wd = x, Wr, Wg, Wu, Wd
@@ -320,13 +338,16 @@ class ExpertLayer:
             if logits is not None:
                 self.logits.copy_(logits)
             moe_route(x, Wr, self.k, self.logits, self.topk_idx, self.topk_w,
-                      logits_in=logits is not None, stream=stream)
+                      logits_in=logits is not None, renorm=self.renorm, stream=stream)
         else:
             self.topk_idx.copy_(topk_idx)
             self.topk_w.copy_(topk_w)
         moe_dispatch(x, self.topk_idx, self.E, self.counts, self.offsets, self.dest_row,
                      self.src_token, self.Xs, self.ws_dispatch, self.Xq, self.Xq_scale, self.prec,
                      stream)
+        if self.router and self.aux_coef != 0.0:
+            moe_route_aux(self.logits, self.counts, self.k, self.aux_coef, self.aux_loss,
+                          self.aux_dp, self.ws_route_aux, stream)
         mx = self.prec == "mxfp8"
         moe_grouped_ffn_fwd(self.Xq if mx else self.Xs, self.Xq_scale, self.offsets, self.T,
                             self.k, Wg, Wu, Wd, self.Hg, self.Hu, self.A, self.Ys, self.ws_fwd,
@@ -343,6 +364,7 @@ class ExpertLayer:
                             stream)
         moe_dispatch_bwd(self.dXs, self.dest_row, self.dx, False, stream)
         if self.router:
+            aux = self.aux_dp if self.aux_coef != 0.0 else None
             moe_route_bwd(self.x, self.Wr, self.logits, self.topk_idx, self.dw, self.dlogits,
-                          self.dWr, self.dx, self.ws_route_bwd, False, stream)
+                          self.dWr, self.dx, self.ws_route_bwd, False, self.renorm, aux, stream)
         return self.dx

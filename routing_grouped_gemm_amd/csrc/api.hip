@@ -160,6 +160,9 @@ int moe_workspace_size(int op, int T, int d, int E, int f, int k, int dtype, int
     case MOE_OP_ROUTE_BWD:
       *bytes = route_bwd_ws(T, d, E, dtype);
       return MOE_OK;
+    case MOE_OP_ROUTE_AUX:
+      *bytes = align_up((size_t)((T + 63) / 64) * E * sizeof(float));
+      return MOE_OK;
   }
   return MOE_ERR_SHAPE;
 }
@@ -189,7 +192,8 @@ int moe_route(const void* x, const void* Wr, int T, int d, int E, int k, int dty
     g.c0 = logits; g.ldc = E;
     MOE_TRY(launch_grouped_gemm(GK_ROUTER_LOGITS, gemm_engine(dtype, E), g, num_cu(), st));
   }
-  return status_of(launch_topk_softmax(logits, T, E, k, topk_idx, topk_w, st));
+  return status_of(launch_topk_softmax(logits, T, E, k, (flags & MOE_ROUTE_RENORM) ? 1 : 0,
+                                       topk_idx, topk_w, st));
 }
 
 int moe_dispatch(const void* x, const int32_t* topk_idx, int T, int d, int E, int k, int dtype,
@@ -361,14 +365,16 @@ int moe_dispatch_bwd(const void* dXs, const int32_t* dest_row, int T, int d, int
 }
 
 int moe_route_bwd(const void* x, const void* Wr, const float* logits, const int32_t* topk_idx,
-                  const float* dtopk_w, int T, int d, int E, int k, int dtype, unsigned flags,
-                  float* dlogits, void* dWr, void* dx, void* ws, size_t ws_bytes, void* stream) {
+                  const float* dtopk_w, const float* aux_dp, int T, int d, int E, int k, int dtype,
+                  unsigned flags, float* dlogits, void* dWr, void* dx, void* ws, size_t ws_bytes,
+                  void* stream) {
   if (!all_nonnull(x, Wr, logits, topk_idx, dtopk_w, dlogits, dWr, dx)) return MOE_ERR_NULL;
   if (int s = check_dtype(dtype)) return s;
   if (int s = check_route_shape(T, E, k)) return s;
   if (int s = check_width(d)) return s;
   if (int s = check_elems(T, d)) return s;
-  if (!all_aligned(x, Wr, logits, topk_idx, dtopk_w, dlogits, dWr, dx, ws)) return MOE_ERR_ALIGN;
+  if (!all_aligned(x, Wr, logits, topk_idx, dtopk_w, aux_dp, dlogits, dWr, dx, ws))
+    return MOE_ERR_ALIGN;
   const int ld16 = router_ld16(E);
   const size_t need = route_bwd_ws(T, d, E, dtype);
   if (need && !ws) return MOE_ERR_NULL;
@@ -376,7 +382,9 @@ int moe_route_bwd(const void* x, const void* Wr, const float* logits, const int3
   hipStream_t st = static_cast<hipStream_t>(stream);
   clear_stale_error();
   uint16_t* dl16 = (dtype == MOE_BF16) ? static_cast<uint16_t*>(ws) : nullptr;
-  MOE_TRY(launch_router_bwd_softmax(logits, topk_idx, dtopk_w, T, E, k, dlogits, dl16, ld16, st));
+  MOE_TRY(launch_router_bwd_softmax(logits, topk_idx, dtopk_w, T, E, k,
+                                    (flags & MOE_ROUTE_RENORM) ? 1 : 0, aux_dp, dlogits, dl16,
+                                    ld16, st));
   const void* dl = (dtype == MOE_BF16) ? static_cast<const void*>(dl16) : dlogits;
   const int ldl = (dtype == MOE_BF16) ? ld16 : E;
   const int eng = gemm_engine(dtype, E);
@@ -408,6 +416,18 @@ int moe_route_bwd(const void* x, const void* Wr, const float* logits, const int3
   h.c0 = dx; h.ldc = d;
   h.accumulate = 1;
   return status_of(launch_grouped_gemm(GK_ROUTER_DX, eng, h, num_cu(), st));
+}
+
+int moe_route_aux(const float* logits, const int32_t* counts, int T, int E, int k, float coef,
+                  float* aux_loss, float* aux_dp, void* ws, size_t ws_bytes, void* stream) {
+  if (!all_nonnull(logits, counts, aux_loss, aux_dp, ws)) return MOE_ERR_NULL;
+  if (int s = check_route_shape(T, E, k)) return s;
+  if (!(coef == coef)) return MOE_ERR_SHAPE;  // NaN coefficient
+  if (!all_aligned(logits, counts, aux_loss, aux_dp, ws)) return MOE_ERR_ALIGN;
+  if (ws_bytes < (size_t)((T + 63) / 64) * E * sizeof(float)) return MOE_ERR_WORKSPACE;
+  clear_stale_error();
+  return status_of(launch_router_aux(logits, counts, T, E, k, coef, static_cast<float*>(ws),
+                                     aux_loss, aux_dp, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

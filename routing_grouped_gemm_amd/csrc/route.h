@@ -6,8 +6,9 @@
 
 namespace moe {
 
-hipError_t launch_topk_softmax(const float* logits, int T, int E, int k, int32_t* idx, float* w,
-                               hipStream_t s);
+// renorm: divide the k chosen probabilities by their sum.
+hipError_t launch_topk_softmax(const float* logits, int T, int E, int k, int renorm, int32_t* idx,
+                               float* w, hipStream_t s);
 // hist and base: E * ceil(T/64) int32 each (workspace).
 hipError_t launch_dispatch_meta(const int32_t* idx, int T, int E, int k, int32_t* hist,
                                 int32_t* base, int32_t* counts, int32_t* offsets,
@@ -28,8 +29,14 @@ hipError_t launch_gather_sum(int dtype, const void* dXs, const int32_t* dest, in
 hipError_t launch_split_reduce(int dtype, const float* part, int S, long n, int accumulate,
                                void* out, hipStream_t s);
 // dl16 (optional): bf16 copy of dl as rows of ld16 >= E entries, tail zeroed.
+// renorm: the weights were renormalised; aux_dp (optional, [E]): a per-expert
+// gradient with respect to every token's probabilities (load-balancing loss).
 hipError_t launch_router_bwd_softmax(const float* logits, const int32_t* idx, const float* dw,
-                                     int T, int E, int k, float* dl, uint16_t* dl16, int ld16,
-                                     hipStream_t s);
+                                     int T, int E, int k, int renorm, const float* aux_dp,
+                                     float* dl, uint16_t* dl16, int ld16, hipStream_t s);
+// Load-balancing loss and its per-expert probability gradient; part: float
+// workspace of E * ceil(T/64).
+hipError_t launch_router_aux(const float* logits, const int32_t* counts, int T, int E, int k,
+                             float coef, float* part, float* loss, float* dp, hipStream_t s);
 
 }  // namespace moe

@@ -26,7 +26,7 @@ namespace moe {
 // softmax + top-k
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restrict__ logits, int T,
-                                                           int E, int k,
+                                                           int E, int k, int renorm,
                                                            int32_t* __restrict__ topk_idx,
                                                            float* __restrict__ topk_w) {
   const int lane = threadIdx.x & 63;
@@ -76,6 +76,12 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restri
       topk_idx[(long)t * k + j] = be;
       topk_w[(long)t * k + j] = expf(bv - mx) / se;
     }
+  }
+  if (renorm && lane == 0) {
+    // optional top-k renormalisation: the chosen probabilities over their sum
+    float S = 0.0f;
+    for (int j = 0; j < k; ++j) S += topk_w[(long)t * k + j];
+    for (int j = 0; j < k; ++j) topk_w[(long)t * k + j] /= S;
   }
 }
 
@@ -316,8 +322,9 @@ __global__ __launch_bounds__(256) void gather_sum_kernel(const TS* __restrict__ 
 // of ld16 >= E entries whose tail is zero.
 __global__ __launch_bounds__(256) void router_bwd_softmax_kernel(
     const float* __restrict__ logits, const int32_t* __restrict__ idx,
-    const float* __restrict__ dw, int T, int E, int k, float* __restrict__ dl,
-    bf16_t* __restrict__ dl16, int ld16) {
+    const float* __restrict__ dw, int T, int E, int k, int renorm,
+    const float* __restrict__ aux_dp, float* __restrict__ dl, bf16_t* __restrict__ dl16,
+    int ld16) {
   const int lane = threadIdx.x & 63;
   const long t = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
@@ -341,21 +348,42 @@ __global__ __launch_bounds__(256) void router_bwd_softmax_kernel(
     se += v[q];
   }
   se = wave_sum(se);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) v[q] = v[q] / se;  // p
+  float S = 1.0f, wdot = 0.0f;
+  if (renorm) {
+    // w_j = p_j / S over the chosen experts: dp_m = (dw_m - sum_j dw_j w_j) / S
+    float ps = 0.0f, pd = 0.0f;
+    for (int j = 0; j < k; ++j) {
+      const int e = idx[t * k + j];
+      if (e >= 0 && e < E && (e & 63) == lane) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if ((e >> 6) == q) { ps += v[q]; pd = fmaf(dw[t * k + j], v[q], pd); }
+      }
+    }
+    S = wave_sum(ps);
+    wdot = wave_sum(pd) / S;
+  }
   for (int j = 0; j < k; ++j) {
     int e = idx[t * k + j];
-    float g = dw[t * k + j];
+    float g = renorm ? (dw[t * k + j] - wdot) / S : dw[t * k + j];
     if (e >= 0 && e < E && (e & 63) == lane) {
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         if ((e >> 6) == q) dp[q] = g;
     }
   }
+  if (aux_dp) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = lane + 64 * q;
+      if (e < E) dp[q] += aux_dp[e];
+    }
+  }
   float inner = 0.0f;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    v[q] = v[q] / se;  // p
-    inner = fmaf(v[q], dp[q], inner);
-  }
+  for (int q = 0; q < 4; ++q) inner = fmaf(v[q], dp[q], inner);
   inner = wave_sum(inner);
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -371,6 +399,72 @@ __global__ __launch_bounds__(256) void router_bwd_softmax_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// load-balancing loss: per-expert mean router probability P_e (partial sums
+// per block of 64 tokens, then an ordered sum over blocks), then
+// L = coef * E * sum_e f_e P_e with f_e = counts[e] / (T k), and its gradient
+// with respect to every token's probabilities, coef * E * f_e / T.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void aux_partial_kernel(const float* __restrict__ logits, int T,
+                                                          int E, float* __restrict__ part) {
+  __shared__ float acc[4][256];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float s[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < 16; ++i) {
+    const long t = (long)blockIdx.x * 64 + wave * 16 + i;
+    if (t >= T) break;
+    const float* row = logits + t * E;
+    float v[4], mx = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = lane + 64 * q;
+      v[q] = (e < E) ? row[e] : -INFINITY;
+      mx = fmaxf(mx, v[q]);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    float se = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v[q] = (lane + 64 * q < E) ? expf(v[q] - mx) : 0.0f;
+      se += v[q];
+    }
+    se = wave_sum(se);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) s[q] += v[q] / se;
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) acc[wave][lane + 64 * q] = s[q];
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256)
+    part[(long)blockIdx.x * E + e] = ((acc[0][e] + acc[1][e]) + acc[2][e]) + acc[3][e];
+}
+
+__global__ __launch_bounds__(256) void aux_final_kernel(const float* __restrict__ part, int nblk,
+                                                        const int32_t* __restrict__ counts, int T,
+                                                        int E, int k, float coef,
+                                                        float* __restrict__ loss,
+                                                        float* __restrict__ dp) {
+  __shared__ float contrib[256];
+  const int e = threadIdx.x;
+  float term = 0.0f;
+  if (e < E) {
+    float P = 0.0f;
+    for (int b = 0; b < nblk; ++b) P += part[(long)b * E + e];
+    P /= (float)T;
+    const float f = (float)counts[e] / ((float)T * (float)k);
+    term = f * P;
+    dp[e] = coef * (float)E * f / (float)T;
+  }
+  contrib[e] = term;
+  __syncthreads();
+  if (e == 0) {
+    float sum = 0.0f;
+    for (int i = 0; i < E; ++i) sum += contrib[i];
+    *loss = coef * (float)E * sum;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 #define MOE_LAUNCH_CHECK() \
@@ -378,11 +472,11 @@ __global__ __launch_bounds__(256) void router_bwd_softmax_kernel(
     hipError_t e_ = hipGetLastError(); if (e_ != hipSuccess) return e_; \
   } while (0)
 
-hipError_t launch_topk_softmax(const float* logits, int T, int E, int k, int32_t* idx, float* w,
-                               hipStream_t s) {
+hipError_t launch_topk_softmax(const float* logits, int T, int E, int k, int renorm, int32_t* idx,
+                               float* w, hipStream_t s) {
   if (T == 0) return hipSuccess;
   hipLaunchKernelGGL(topk_softmax_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k,
-                     idx, w);
+                     renorm, idx, w);
   note_launch("topk_softmax", s);
   return hipGetLastError();
 }
@@ -505,11 +599,27 @@ hipError_t launch_gather_sum(int dtype, const void* dXs, const int32_t* dest, in
 }
 
 hipError_t launch_router_bwd_softmax(const float* logits, const int32_t* idx, const float* dw,
-                                     int T, int E, int k, float* dl, bf16_t* dl16, int ld16,
-                                     hipStream_t s) {
+                                     int T, int E, int k, int renorm, const float* aux_dp,
+                                     float* dl, bf16_t* dl16, int ld16, hipStream_t s) {
   hipLaunchKernelGGL(router_bwd_softmax_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, idx,
-                     dw, T, E, k, dl, dl16, ld16);
+                     dw, T, E, k, renorm, aux_dp, dl, dl16, ld16);
   note_launch("router_bwd_softmax", s);
+  return hipGetLastError();
+}
+
+}  // namespace moe
+
+namespace moe {
+
+hipError_t launch_router_aux(const float* logits, const int32_t* counts, int T, int E, int k,
+                             float coef, float* part, float* loss, float* dp, hipStream_t s) {
+  const int nblk = (T + 63) / 64;
+  hipLaunchKernelGGL(aux_partial_kernel, dim3(nblk), dim3(256), 0, s, logits, T, E, part);
+  note_launch("router_aux_partial", s);
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  hipLaunchKernelGGL(aux_final_kernel, dim3(1), dim3(256), 0, s, part, nblk, counts, T, E, k, coef,
+                     loss, dp);
+  note_launch("router_aux_final", s);
   return hipGetLastError();
 }
 

@@ -42,12 +42,14 @@ def relerr(gpu: np.ndarray, ref: np.ndarray) -> float:
     return float(nd / nr)
 
 
-def run_gpu(wl: Workload, inp: Dict[str, np.ndarray], logits: Optional[np.ndarray] = None):
+def run_gpu(wl: Workload, inp: Dict[str, np.ndarray], logits: Optional[np.ndarray] = None,
+            renorm: bool = False, aux_coef: float = 0.0):
     """Forward + backward of the layer on the GPU; returns every buffer as numpy."""
     import routing_grouped_gemm_amd as rgg
     dt = torch.float32 if wl.dtype == "fp32" else torch.bfloat16
     router = wl.routing == "router"
-    layer = rgg.ExpertLayer(wl.T, wl.d, wl.E, wl.f, wl.k, dt, wl.prec, router=router)
+    layer = rgg.ExpertLayer(wl.T, wl.d, wl.E, wl.f, wl.k, dt, wl.prec, router=router,
+                            renorm=renorm, aux_coef=aux_coef)
     x = dev_tensor(inp, "x", dt)
     Wg, Wu, Wd = (dev_tensor(inp, n, dt) for n in ("Wg", "Wu", "Wd"))
     Wr = dev_tensor(inp, "Wr", dt) if router else None
@@ -67,17 +69,20 @@ def run_gpu(wl: Workload, inp: Dict[str, np.ndarray], logits: Optional[np.ndarra
         names += ["Xq", "Xq_scale", "dYs_q", "dYs_q_scale"]
     if router:
         names += ["logits", "dlogits", "dWr"]
+    if router and aux_coef:
+        names += ["aux_loss", "aux_dp"]
     out = {n: to_np(getattr(layer, n)) for n in names}
     f = wl.f
     out["dHg"], out["dHu"] = out["dH"][:, :f], out["dH"][:, f:]
     return out
 
 
-def run_oracle(wl: Workload, inp: Dict[str, np.ndarray], logits: Optional[np.ndarray] = None):
+def run_oracle(wl: Workload, inp: Dict[str, np.ndarray], logits: Optional[np.ndarray] = None,
+               renorm: bool = False, aux_coef: float = 0.0):
     prec = wl.prec
     if wl.routing == "router":
         return O.layer(inp["x"], inp["Wr"], inp["Wg"], inp["Wu"], inp["Wd"], wl.k, inp["dY"], prec,
-                       logits=logits)
+                       logits=logits, renorm=renorm, aux_coef=aux_coef)
     return O.layer(inp["x"], None, inp["Wg"], inp["Wu"], inp["Wd"], wl.k, inp["dY"], prec,
                    topk_idx=inp["topk_idx"], topk_w=inp["topk_w"])
 

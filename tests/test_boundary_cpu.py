@@ -36,7 +36,7 @@ def declared_entry_points():
 
 def test_exports_every_declared_symbol(L):
     names = declared_entry_points()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(L, n), n
 
@@ -75,6 +75,9 @@ def test_workspace_sizes(L):
     assert ws_size(L, 7, 8192, 2048, 64, 1024, 8, BF16, P_BF16) == (OK, 8192 * 64 * 2 + 32 * 2048 * 64 * 4)
     assert ws_size(L, 7, 100, 64, 6, 64, 2, BF16, P_BF16) == (OK, 100 * 64 * 2)  # E % 8: no split
     assert ws_size(L, 7, 256, 64, 8, 128, 2, F32, P_F32) == (OK, 0)
+    # load-balancing loss: float32 partial sums of E per 64-token block
+    assert ws_size(L, 8, 8192, 2048, 64, 1024, 8, BF16, P_BF16) == (OK, 128 * 64 * 4)
+    assert ws_size(L, 8, 100, 64, 3, 64, 1, F32, P_F32) == (OK, 256)
     for op in (0, 2, 3, 4, 5, 6):
         assert ws_size(L, op, 256, 64, 8, 128, 2, BF16, P_BF16) == (OK, 0)
     assert ws_size(L, 1, 0, 64, 8, 128, 2, BF16, P_BF16)[0] == SHAPE
@@ -176,7 +179,20 @@ def test_combine_and_gather_validation(L):
 
 def test_route_bwd_validation(L):
     f = L.moe_route_bwd
-    assert f(A, A, A, A, A, 16, 64, 8, 2, BF16, 0, A, A, A, None, 0, None) == NULL   # bf16 needs ws
-    assert f(A, A, A, A, A, 16, 64, 8, 2, BF16, 0, A, A, A, A, 16 * 8 * 2 - 1, None) == WS
-    assert f(A, A, A, A, A, 16, 64, 8, 2, BF16, 0, A, A, MIS, A, 1 << 20, None) == ALIGN
-    assert f(A, A, A, A, A, 16, 64, 8, 9, BF16, 0, A, A, A, A, 1 << 20, None) == UNSUP
+    assert f(A, A, A, A, A, None, 16, 64, 8, 2, BF16, 0, A, A, A, None, 0, None) == NULL  # bf16 needs ws
+    assert f(A, A, A, A, A, None, 16, 64, 8, 2, BF16, 0, A, A, A, A, 16 * 8 * 2 - 1, None) == WS
+    assert f(A, A, A, A, A, None, 16, 64, 8, 2, BF16, 0, A, A, MIS, A, 1 << 20, None) == ALIGN
+    assert f(A, A, A, A, A, MIS, 16, 64, 8, 2, BF16, 4, A, A, A, A, 1 << 20, None) == ALIGN
+    assert f(A, A, A, A, A, None, 16, 64, 8, 9, BF16, 0, A, A, A, A, 1 << 20, None) == UNSUP
+
+
+def test_route_aux_validation(L):
+    f = L.moe_route_aux
+    assert f(None, A, 16, 8, 2, 0.01, A, A, A, 256, None) == NULL
+    assert f(A, A, 16, 8, 2, 0.01, A, None, A, 256, None) == NULL
+    assert f(A, A, 16, 8, 2, 0.01, A, A, None, 256, None) == NULL
+    assert f(A, A, 0, 8, 2, 0.01, A, A, A, 256, None) == SHAPE
+    assert f(A, A, 16, 8, 9, 0.01, A, A, A, 256, None) == UNSUP
+    assert f(A, A, 16, 8, 2, float("nan"), A, A, A, 256, None) == SHAPE
+    assert f(A, MIS, 16, 8, 2, 0.01, A, A, A, 256, None) == ALIGN
+    assert f(A, A, 200, 8, 2, 0.01, A, A, A, 4 * 8 * 4 - 1, None) == WS

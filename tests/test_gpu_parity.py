@@ -106,6 +106,104 @@ def test_topk_with_ties(E, k):
     np.testing.assert_allclose(w.cpu().numpy(), ref_w, rtol=2e-6, atol=0)
 
 
+@pytest.mark.parametrize("E,k", [(8, 2), (64, 8), (256, 16), (5, 5), (1, 1)])
+def test_topk_renorm_with_ties(E, k):
+    """Top-k renormalisation: the same choice as without it, the chosen
+    probabilities divided by their sum (each row sums to 1)."""
+    import routing_grouped_gemm_amd as rgg
+    say(f"[case] topk renorm E={E} k={k}")
+    rng = np.random.Generator(np.random.PCG64(E * 100 + k + 7))
+    T = 333
+    lg = rng.integers(-3, 4, size=(T, E)).astype(np.float32) * 0.7
+    logits = rgg.upload(lg)
+    idx = torch.empty(T, k, dtype=torch.int32, device="cuda")
+    w = torch.empty(T, k, dtype=torch.float32, device="cuda")
+    rgg.moe_route(None, None, k, logits, idx, w, logits_in=True, renorm=True)
+    torch.cuda.synchronize()
+    ref_idx, ref_w, _ = O.route(lg, k, "fp32", renorm=True)
+    np.testing.assert_array_equal(idx.cpu().numpy(), ref_idx)
+    np.testing.assert_allclose(w.cpu().numpy(), ref_w, rtol=4e-6, atol=0)
+
+
+# Router variants: renormalised top-k weights and the load-balancing loss,
+# through the full layer (router on the fp32 SIMT, bf16 MFMA split-K, bf16
+# SIMT (E % 8 != 0) and MXFP8 paths).
+VARIANT_SHAPES = ["tiny_fp32", "mid_bf16_E64", "edge_E6_bf16", "mid_mxfp8_E8"]
+
+
+# aux_coef = 100: large enough that the loss's gradient is a sizeable part of
+# dlogits (with 0.01 it is about 1e-4 of it)
+@pytest.mark.parametrize("renorm,aux", [(True, 0.0), (False, 0.01), (True, 100.0)])
+@pytest.mark.parametrize("name", VARIANT_SHAPES)
+def test_router_variants(name, renorm, aux):
+    wl, inp, logits = _layer_case(name)
+    say(f"  renorm={renorm} aux_coef={aux}")
+    ref = run_oracle(wl, inp, logits, renorm=renorm, aux_coef=aux)
+    gpu = run_gpu(wl, inp, logits, renorm=renorm, aux_coef=aux)
+    compare(wl, gpu, ref)
+    if renorm:
+        np.testing.assert_allclose(gpu["topk_w"].sum(axis=1), 1.0, rtol=2e-6)
+    if aux:
+        el = abs(float(gpu["aux_loss"][0]) - ref["aux_loss"]) / abs(ref["aux_loss"])
+        ed = relerr(gpu["aux_dp"], ref["aux_dp"])
+        say(f"  aux_loss relerr {el:.2e}, aux_dp relerr {ed:.2e}")
+        assert el <= 1e-5 and ed <= 1e-6
+
+
+@pytest.mark.parametrize("T,E,k,skew", [(1, 1, 1, 0.0), (63, 5, 2, 0.0), (5000, 128, 8, 1.5),
+                                        (4097, 256, 16, 0.0)])
+def test_route_aux_entry(T, E, k, skew):
+    """moe_route_aux alone on oracle routing: several 64-token blocks, a
+    ragged last block, skewed (Zipf-like) and uniform expert loads."""
+    import routing_grouped_gemm_amd as rgg
+    say(f"[case] route_aux T={T} E={E} k={k} skew={skew}")
+    rng = np.random.Generator(np.random.PCG64(T + E))
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    lg += (skew * -np.log1p(np.arange(E))).astype(np.float32)[None, :]
+    idx, _, _ = O.route(lg, k, "fp32")
+    counts = np.bincount(idx.reshape(-1), minlength=E).astype(np.int32)
+    ref_L, ref_dp = O.aux_loss(lg, idx, E, 0.01, "fp64")
+    ws = torch.empty(max(rgg.moe_workspace_size("route_aux", T, 64, E, 64, k, torch.bfloat16,
+                                                "bf16"), 256), dtype=torch.uint8, device="cuda")
+    loss = torch.full((1,), float("nan"), device="cuda")
+    dp = torch.full((E,), float("nan"), device="cuda")
+    rgg.moe_route_aux(rgg.upload(lg), rgg.upload(counts), k, 0.01, loss, dp, ws)
+    torch.cuda.synchronize()
+    el = abs(float(loss.item()) - ref_L) / abs(ref_L)
+    ed = relerr(to_np(dp), ref_dp)
+    say(f"  aux_loss {loss.item():.6f} vs {ref_L:.6f}: relerr {el:.2e}, aux_dp {ed:.2e}")
+    assert el <= 1e-5 and ed <= 1e-6
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "mid_bf16_E64", "edge_E6_bf16"])
+def test_route_bwd_aux_gradient_alone(name):
+    """moe_route_bwd with a zero top-k weight gradient: dlogits, dWr and dx
+    come from the load-balancing loss's gradient alone."""
+    import routing_grouped_gemm_amd as rgg
+    wl, inp, logits = _layer_case(name)
+    T, d, E, k = wl.T, wl.d, wl.E, wl.k
+    dt = torch.float32 if wl.dtype == "fp32" else torch.bfloat16
+    idx, _, _ = O.route(logits, k, "fp32")
+    _, aux_dp = O.aux_loss(logits, idx, E, 1.0, "fp32")
+    ref = O.router_backward(inp["x"], inp["Wr"], logits, idx, np.zeros((T, k)), np.zeros((T, d)),
+                            wl.prec, False, aux_dp)
+    x, Wr = dev_tensor(inp, "x", dt), dev_tensor(inp, "Wr", dt)
+    dlog = torch.empty(T, E, device="cuda")
+    dWr = torch.empty(d, E, dtype=dt, device="cuda")
+    dx = torch.zeros(T, d, dtype=dt, device="cuda")
+    n = rgg.moe_workspace_size("route_bwd", T, d, E, wl.f, k, dt, wl.prec)
+    ws = torch.empty(max(n, 256), dtype=torch.uint8, device="cuda")
+    rgg.moe_route_bwd(x, Wr, rgg.upload(logits.astype(np.float32)), rgg.upload(idx),
+                      torch.zeros(T, k, device="cuda"), dlog, dWr, dx, ws,
+                      aux_dp=rgg.upload(np.asarray(aux_dp, np.float32)))
+    torch.cuda.synchronize()
+    tol = 1e-4 if wl.dtype == "fp32" else 2e-2
+    e1, e2, e3 = (relerr(to_np(g), r) for g, r in
+                  ((dlog, ref["dlogits"]), (dWr, ref["dWr"]), (dx, ref["dx"])))
+    say(f"  dlogits {e1:.2e} dWr {e2:.2e} dx {e3:.2e}")
+    assert e1 <= 1e-4 and e2 <= tol and e3 <= tol
+
+
 def test_all_rows_to_one_expert():
     """Logits that send every token to expert 2 first: one expert takes all
     T rows (several M tiles); the others are empty."""
