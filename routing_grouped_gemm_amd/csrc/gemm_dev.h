@@ -272,7 +272,7 @@ __device__ __forceinline__ void epilogue4(const GemmArgs& g, const Tile& t, int 
     load4(static_cast<const TS*>(g.h1) + row * g.ldh + n, hu);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      float s = 1.0f / (1.0f + __expf(-hg[q]));
+      float s = sigmoid_f(hg[q]);
       du[q] = v[q] * hg[q] * s;
       dg[q] = v[q] * hu[q] * s * (1.0f + hg[q] * (1.0f - s));
     }
@@ -426,6 +426,22 @@ __device__ __forceinline__ void issue(const Plan& P, int kt, uint32_t lds_base, 
     dma16(rs, lds_base + plan_lds(wave, i), (i & 1) ? P.v1 : P.v0, soff + (uint32_t)i * P.bstep);
 }
 
+// Block i (0..DMA_PER_OP-1) of the wave's DMA of one operand for stage kt.
+template <bool MN>
+__device__ __forceinline__ void issue_one(const Plan& P, int kt, uint32_t lds_base, int wave, int i) {
+  i32x4_t rs;
+  uint32_t soff;
+  if constexpr (MN) {
+    rs = (wave >= 2) ? P.rs1 : P.rs0;
+    soff = (uint32_t)kt * P.kstep;
+  } else {
+    const bool second = kt >= P.split_stage;
+    rs = second ? P.rs1 : P.rs0;
+    soff = (uint32_t)(second ? kt - P.split_stage : kt) * P.kstep;
+  }
+  dma16(rs, lds_base + plan_lds(wave, i), (i & 1) ? P.v1 : P.v0, soff + (uint32_t)i * P.bstep);
+}
+
 // L2 prefetch: one 4-byte buffer->LDS load per 128-byte line of a future
 // stage pulls the line into L2 (the bytes land in a scratch word that is
 // never read), so that the stage's own DMA, issued two stages later, hits in
@@ -511,6 +527,14 @@ __device__ __forceinline__ void mfma16(f32x16_t (&acc)[4][4], const bf16x8_t (&f
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+}
+
+// MFMAs 2q and 2q+1 of mfma16 (row block q/2, column blocks 2(q%2), +1).
+__device__ __forceinline__ void mfma_pair(f32x16_t (&acc)[4][4], const bf16x8_t (&fa)[4],
+                                          const bf16x8_t (&fb)[4], int q) {
+  const int i = q >> 1, j = 2 * (q & 1);
+  acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+  acc[i][j + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j + 1], fa[i], acc[i][j + 1], 0, 0, 0);
 }
 
 // s_waitcnt with lgkmcnt(0) and the other counters left alone (gfx9 encoding).
@@ -622,7 +646,7 @@ __device__ __forceinline__ void epi8(const GemmArgs& g, const Tile& t, long row,
     load8(static_cast<const bf16_t*>(g.h1) + row * g.ldh + n, hu);
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      const float sg = 1.0f / (1.0f + __expf(-hg[q]));
+      const float sg = sigmoid_f(hg[q]);
       du[q] = v[q] * hg[q] * sg;
       dg[q] = v[q] * hu[q] * sg * (1.0f + hg[q] * (1.0f - sg));
     }
@@ -685,15 +709,20 @@ __device__ __forceinline__ void epilogue_block(const GemmArgs& g, const Tile& t,
         for (int q = 0; q < 4; ++q) { v[q] = a0[q]; v[q + 4] = a1[q]; u[q] = b0[q]; u[q + 4] = b1[q]; }
         const int n = t.n0 + wn * 64 + c;
         const bool ok = m < t.mlim && n < g.N;  // uniform over each 4-lane block
-        if (ok) epi8<EPI>(g, t, (long)t.row0 + m, n, v, u);
-        if constexpr (qout_of<KIND>()) {
-          if (ok) {
-            float a[8], ar[8];
+        static_assert(EPI == EPI_SWIGLU_FWD, "paired gate/up columns feed the SwiGLU forward");
+        if (ok) {
+          float a[8];
 #pragma unroll
-            for (int q = 0; q < 8; ++q) a[q] = silu_f(v[q]) * u[q];
+          for (int q = 0; q < 8; ++q) a[q] = silu_f(v[q]) * u[q];
+          const long row = (long)t.row0 + m;
+          const long off = row * g.ldc + n;
+          store8(static_cast<bf16_t*>(g.c0) + off, v);
+          store8(static_cast<bf16_t*>(g.c1) + off, u);
+          store8(static_cast<bf16_t*>(g.c2) + off, a);
+          if constexpr (qout_of<KIND>()) {
+            float ar[8];
             round_bf16_8(a, ar);
-            const long row = (long)t.row0 + m;
-            quant8_store(ar, g.q0 + row * g.ldc + n, g.qs + (n >> 5) * g.qs_pitch + row, lane);
+            quant8_store(ar, g.q0 + off, g.qs + (n >> 5) * g.qs_pitch + row, lane);
           }
         }
       }
@@ -716,7 +745,7 @@ __device__ __forceinline__ void epilogue_block(const GemmArgs& g, const Tile& t,
           unpack8(hu[it], h1);
 #pragma unroll
           for (int q = 0; q < 8; ++q) {
-            const float sg = 1.0f / (1.0f + __expf(-h0[q]));
+            const float sg = sigmoid_f(h0[q]);
             du[q] = v[q] * h0[q] * sg;
             dg[q] = v[q] * h1[q] * sg * (1.0f + h0[q] * (1.0f - sg));
           }

@@ -84,7 +84,12 @@ __device__ __forceinline__ void store8(float* p, const float (&v)[8]) {
   *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
 }
 
-__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
+// Logistic sigmoid and SiLU with the hardware reciprocal (1 ulp) in place of
+// an IEEE division: the results are rounded to bf16 or feed bf16 GEMMs.
+__device__ __forceinline__ float sigmoid_f(float z) {
+  return __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
+__device__ __forceinline__ float silu_f(float z) { return z * sigmoid_f(z); }
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
