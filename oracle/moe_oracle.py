@@ -352,7 +352,8 @@ def layer_forward(x, Wg, Wu, Wd, topk_idx, topk_w, prec: str = "fp64") -> Dict[s
                 Xs=Xs, Hg=Hg, Hu=Hu, A=A, Ys=Ys, y=y)
 
 
-def layer_backward(fwd, x, Wg, Wu, Wd, topk_idx, topk_w, dY, prec: str = "fp64") -> Dict[str, np.ndarray]:
+def layer_backward(fwd, x, Wg, Wu, Wd, topk_idx, topk_w, dY, prec: str = "fp64",
+                   wgrad_f32: bool = False) -> Dict[str, np.ndarray]:
     """Backward of the expert part for the loss L = sum_t <y[t], dY[t]>.
 
     dw[t,j] = <dY[t], Ys[row]>; dYs[row] = w[t,j] dY[t];
@@ -361,8 +362,12 @@ def layer_backward(fwd, x, Wg, Wu, Wd, topk_idx, topk_w, dY, prec: str = "fp64")
     dXs = dHg.Wg[e]^T + dHu.Wu[e]^T; dx[t] = sum_j dXs[row(t,j)];
     dWd[e] = A^T.dYs, dWg[e] = Xs^T.dHg, dWu[e] = Xs^T.dHu (empty expert: 0).
     'mxfp8' quantises both operands of the two dgrad GEMMs along their
-    contraction axis; weight gradients use the unquantised operands."""
+    contraction axis; weight gradients use the unquantised operands.
+    wgrad_f32 (OLMo-core 3 release summary, technical principle section:
+    optional FP32 gradient accumulation): the weight gradients are kept in
+    float32 instead of being rounded to the storage type."""
     rnd = _storage_round(prec)
+    wrnd = _f32(prec) if wgrad_f32 else rnd
     mx = prec == "mxfp8"
     T, d = np.shape(x)
     E, _, f = np.shape(Wg)
@@ -408,7 +413,7 @@ def layer_backward(fwd, x, Wg, Wu, Wd, topk_idx, topk_w, dY, prec: str = "fp64")
         dWd[e] = A[lo:hi].T @ dYs[lo:hi]
         dWg[e] = Xs[lo:hi].T @ dHg[lo:hi]
         dWu[e] = Xs[lo:hi].T @ dHu[lo:hi]
-    dWg, dWu, dWd = rnd(dWg), rnd(dWu), rnd(dWd)
+    dWg, dWu, dWd = wrnd(dWg), wrnd(dWu), wrnd(dWd)
     dx = np.zeros((T, d))
     for t in range(T):
         for j in range(k):
@@ -455,7 +460,7 @@ def router_backward(x, Wr, logits, topk_idx, dw, dx_experts, prec: str = "fp64",
 
 def layer(x, Wr, Wg, Wu, Wd, k, dY, prec: str = "fp64", logits=None,
           topk_idx=None, topk_w=None, renorm: bool = False,
-          aux_coef: float = 0.0) -> Dict[str, np.ndarray]:
+          aux_coef: float = 0.0, wgrad_f32: bool = False) -> Dict[str, np.ndarray]:
     """Whole layer forward + backward.
 
     With a router (Wr given): logits = x.Wr unless `logits` is passed in,
@@ -476,7 +481,7 @@ def layer(x, Wr, Wg, Wu, Wd, k, dY, prec: str = "fp64", logits=None,
     fwd = layer_forward(x, Wg, Wu, Wd, topk_idx, topk_w, prec)
     out.update(fwd)
     if dY is not None:
-        bwd = layer_backward(fwd, x, Wg, Wu, Wd, topk_idx, topk_w, dY, prec)
+        bwd = layer_backward(fwd, x, Wg, Wu, Wd, topk_idx, topk_w, dY, prec, wgrad_f32)
         out.update(bwd)
         if Wr is not None:
             rb = router_backward(x, Wr, logits, topk_idx, bwd["dw"], bwd["dx"], prec, renorm,

@@ -568,3 +568,33 @@ def test_finite_differences_router_variants(renorm, aux):
         err = np.linalg.norm(fd - an) / np.linalg.norm(an)
         assert err <= 1e-6, (name, err)
     assert skipped <= 8, skipped
+
+
+def test_wgrad_f32_variant():
+    """Float32 weight-gradient accumulation (OLMo-core 3 release summary,
+    technical principle section): the same sums as the bf16 layer, kept in
+    float32.  Rounding them to bf16 gives the bf16 layer's gradients (up to
+    the rare double-rounding tie, never more than one bf16 unit apart);
+    nothing else in the layer changes; a float32 layer is unaffected."""
+    rng = _rng(41)
+    T, d, E, f, k = 40, 16, 5, 24, 2
+    x = O.round_bf16(rng.standard_normal((T, d)))
+    Wr = O.round_bf16(rng.standard_normal((d, E)) * 0.3)
+    Wg, Wu, Wd = (O.round_bf16(a) for a in _weights(rng, d, E, f))
+    dY = O.round_bf16(rng.standard_normal((T, d)))
+    a = O.layer(x, Wr, Wg, Wu, Wd, k, dY, "bf16")
+    b = O.layer(x, Wr, Wg, Wu, Wd, k, dY, "bf16", wgrad_f32=True)
+    for n in a:
+        if n not in ("dWg", "dWu", "dWd"):
+            np.testing.assert_array_equal(np.asarray(a[n]), np.asarray(b[n]), err_msg=n)
+    for n in ("dWg", "dWu", "dWd"):
+        w32, w16 = np.asarray(b[n]), np.asarray(a[n])
+        np.testing.assert_array_equal(w32, w32.astype(np.float32).astype(np.float64))
+        assert np.mean(O.round_bf16(w32) == w16) > 0.999, n
+        ulp = np.abs(w16) * 2.0 ** -7 + 1e-30
+        assert np.all(np.abs(w32 - w16) <= ulp), n
+        assert np.any(w32 != w16), n   # the variant really keeps more bits
+    c = O.layer(x, Wr, Wg, Wu, Wd, k, dY, "fp32")
+    e = O.layer(x, Wr, Wg, Wu, Wd, k, dY, "fp32", wgrad_f32=True)
+    for n in ("dWg", "dWu", "dWd"):
+        np.testing.assert_array_equal(c[n], e[n])
