@@ -74,6 +74,8 @@ enum moe_prec { MOE_PREC_F32 = 0, MOE_PREC_BF16 = 1, MOE_PREC_MXFP8 = 2 };
 #define MOE_ROUTE_RENORM 0x4u
 /* moe_grouped_ffn_bwd / moe_dispatch_bwd / moe_route_bwd flags */
 #define MOE_ACCUMULATE 0x2u        /* add into the output (dW*, dx, dWr) instead of overwriting */
+/* moe_grouped_ffn_bwd flag (bf16 layer): dWg, dWu, dWd are float32 buffers */
+#define MOE_WGRAD_F32 0x8u
 
 /* Operation ids for moe_workspace_size. */
 enum moe_op {
@@ -176,6 +178,10 @@ int moe_combine_bwd(const void* dY, const void* Ys, const float* topk_w,
  *   dWd[e] = A^T.dYs, dWg[e] = Xs^T.dHg, dWu[e] = Xs^T.dHu, summed in float32
  *   over the expert's rows and stored in dtype (an expert with no rows gets
  *   zeros; with MOE_ACCUMULATE the sum is added to the existing values).
+ *   MOE_WGRAD_F32 (same summary: optional FP32 gradient accumulation): the
+ *   three weight gradients are float32 buffers, written, or with
+ *   MOE_ACCUMULATE added to, without rounding to bf16 (a float32 layer's
+ *   gradients are float32 anyway; the flag changes nothing there).
  *   Xs: the dispatched rows in dtype (also for MXFP8).  prec MXFP8: both
  *   operands of the two dgrad GEMMs are block-quantised along their
  *   contraction axis (dYs and Wd along d; dH, Wg, Wu along f); dYs_q /

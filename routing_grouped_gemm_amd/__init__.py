@@ -25,7 +25,7 @@ __all__ = [
     "lib", "moe_route", "moe_dispatch", "moe_grouped_ffn_fwd", "moe_combine",
     "moe_combine_bwd", "moe_grouped_ffn_bwd", "moe_dispatch_bwd", "moe_route_bwd",
     "moe_route_aux", "moe_workspace_size", "moe_status_string", "ExpertLayer", "LIB_PATH",
-    "MOE_ROUTE_LOGITS_IN", "MOE_ROUTE_RENORM", "MOE_ACCUMULATE", "KernelTimer", "upload", "mx_scale_pitch",
+    "MOE_ROUTE_LOGITS_IN", "MOE_ROUTE_RENORM", "MOE_ACCUMULATE", "MOE_WGRAD_F32", "KernelTimer", "upload", "mx_scale_pitch",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_hip.so")
@@ -35,6 +35,7 @@ PREC = {"fp32": 0, "bf16": 1, "mxfp8": 2}
 MOE_ROUTE_LOGITS_IN = 0x1
 MOE_ACCUMULATE = 0x2
 MOE_ROUTE_RENORM = 0x4
+MOE_WGRAD_F32 = 0x8
 OPS = {"route": 0, "dispatch": 1, "ffn_fwd": 2, "combine": 3, "combine_bwd": 4,
        "ffn_bwd": 5, "dispatch_bwd": 6, "route_bwd": 7, "route_aux": 8}
 
@@ -194,11 +195,14 @@ def moe_grouped_ffn_bwd(dYs, Xs, Hg, Hu, A, offsets, T, k, Wg, Wu, Wd, dH, dXs,
                         dYs_q_scale=None, stream=None):
     E, d, f = Wg.shape
     wp, wb = _ws(ws)
+    # float32 weight gradients of a bf16 layer select float32 accumulation
+    flags = (MOE_ACCUMULATE if accumulate else 0) | \
+        (MOE_WGRAD_F32 if dWg.dtype == torch.float32 and Wg.dtype == torch.bfloat16 else 0)
     _check(lib().moe_grouped_ffn_bwd(_ptr(dYs), _ptr(dYs_q), _ptr(dYs_q_scale), _ptr(Xs),
                                      _ptr(Hg), _ptr(Hu), _ptr(A),
                                      _ptr(offsets), T, k, d, f, E, _ptr(Wg),
                                      _ptr(Wu), _ptr(Wd), _dtype(Wg), PREC[prec],
-                                     MOE_ACCUMULATE if accumulate else 0, _ptr(dH), _ptr(dXs),
+                                     flags, _ptr(dH), _ptr(dXs),
                                      _ptr(dWg), _ptr(dWu), _ptr(dWd), wp, wb, _stream(stream)),
            "moe_grouped_ffn_bwd")
 
@@ -280,12 +284,14 @@ class ExpertLayer:
     top-k weights renormalised to sum to 1 when renorm=True, and the
     load-balancing loss (coefficient aux_coef, into aux_loss) and its
     gradient added to the router backward when aux_coef != 0.
+    wgrad_f32=True keeps the expert weight gradients dWg, dWu, dWd in float32
+    (float32 accumulation with backward(..., accumulate_wgrad=True)).
     router=False: pre-routed rows (topk_idx / topk_w are inputs, no router
     backward).  All buffers are allocated once, on construction."""
 
     def __init__(self, T: int, d: int, E: int, f: int, k: int, dtype=torch.bfloat16,
                  prec: str = "bf16", router: bool = True, device="cuda", renorm: bool = False,
-                 aux_coef: float = 0.0):
+                 aux_coef: float = 0.0, wgrad_f32: bool = False):
         lib()
         self.T, self.d, self.E, self.f, self.k = T, d, E, f, k
         self.R = R = T * k
@@ -317,7 +323,8 @@ class ExpertLayer:
         self.dH = z(R, 2 * f)
         self.dXs = z(R, d)
         self.dx = z(T, d)
-        self.dWg, self.dWu, self.dWd = z(E, d, f), z(E, d, f), z(E, f, d)
+        wdt = torch.float32 if wgrad_f32 else dtype
+        self.dWg, self.dWu, self.dWd = z(E, d, f, dt=wdt), z(E, d, f, dt=wdt), z(E, f, d, dt=wdt)
         self.dlogits = z(T, E, dt=f32)
         self.dWr = z(d, E)
         self.aux_loss = z(1, dt=f32)
@@ -355,13 +362,13 @@ class ExpertLayer:
         moe_combine(self.Ys, self.topk_w, self.dest_row, self.y, stream)
         return self.y
 
-    def backward(self, dY, stream=None):
+    def backward(self, dY, stream=None, accumulate_wgrad: bool = False):
         moe_combine_bwd(dY, self.Ys, self.topk_w, self.dest_row, self.dYs, self.dw, self.dYs_q,
                         self.dYs_q_scale, stream)
         moe_grouped_ffn_bwd(self.dYs, self.Xs, self.Hg, self.Hu, self.A, self.offsets, self.T, self.k,
                             self.Wg, self.Wu, self.Wd, self.dH, self.dXs, self.dWg, self.dWu,
-                            self.dWd, self.ws_bwd, self.prec, False, self.dYs_q, self.dYs_q_scale,
-                            stream)
+                            self.dWd, self.ws_bwd, self.prec, accumulate_wgrad, self.dYs_q,
+                            self.dYs_q_scale, stream)
         moe_dispatch_bwd(self.dXs, self.dest_row, self.dx, False, stream)
         if self.router:
             aux = self.aux_dp if self.aux_coef != 0.0 else None

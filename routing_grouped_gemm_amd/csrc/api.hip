@@ -333,6 +333,8 @@ int moe_grouped_ffn_bwd(const void* dYs, const void* dYs_q, const uint8_t* dYs_q
     MOE_TRY(launch_grouped_gemm(GK_DGRAD_GATEUP, eng, h, num_cu(), st));
   }
   // weight gradients: dWg|dWu = Xs^T . dH, dWd = A^T . dYs (ragged K = rows of e)
+  const GemmKind wk =
+      ((flags & MOE_WGRAD_F32) && dtype == MOE_BF16) ? GK_WGRAD_F32 : GK_WGRAD;
   GemmArgs w{};
   w.E = E; w.offsets = offsets; w.rows_total = (int)R; w.ragged = RAG_K;
   w.M = d; w.N = 2 * f;
@@ -340,7 +342,7 @@ int moe_grouped_ffn_bwd(const void* dYs, const void* dYs_q, const uint8_t* dYs_q
   w.b0 = dH; w.ldb = 2L * f;
   w.c0 = dWg; w.c1 = dWu; w.ldc = f; w.c_es = (long)d * f; w.c_split = f;
   w.accumulate = acc;
-  MOE_TRY(launch_grouped_gemm(GK_WGRAD, eng, w, num_cu(), st));
+  MOE_TRY(launch_grouped_gemm(wk, eng, w, num_cu(), st));
   GemmArgs v{};
   v.E = E; v.offsets = offsets; v.rows_total = (int)R; v.ragged = RAG_K;
   v.M = f; v.N = d;
@@ -348,7 +350,7 @@ int moe_grouped_ffn_bwd(const void* dYs, const void* dYs_q, const uint8_t* dYs_q
   v.b0 = dYs; v.ldb = d;
   v.c0 = dWd; v.ldc = d; v.c_es = (long)f * d; v.c_split = d;
   v.accumulate = acc;
-  return status_of(launch_grouped_gemm(GK_WGRAD, eng, v, num_cu(), st));
+  return status_of(launch_grouped_gemm(wk, eng, v, num_cu(), st));
 }
 
 int moe_dispatch_bwd(const void* dXs, const int32_t* dest_row, int T, int d, int k, int dtype,

@@ -13,7 +13,8 @@ enum EpiKind : int {
   EPI_STORE_F32 = 1,   // C[row][n] = acc as float32
   EPI_SWIGLU_FWD = 2,  // acc pair (gate, up): Hg, Hu and A = silu(Hg)*Hu
   EPI_SWIGLU_BWD = 3,  // acc = dA: dHg = dA*Hu*silu'(Hg), dHu = dA*silu(Hg) into dH[R,2f]
-  EPI_WGRAD_SPLIT = 4  // columns [0,c_split) -> c0, [c_split, N) -> c1 (dWg | dWu)
+  EPI_WGRAD_SPLIT = 4,     // columns [0,c_split) -> c0, [c_split, N) -> c1 (dWg | dWu)
+  EPI_WGRAD_SPLIT_F32 = 5  // as EPI_WGRAD_SPLIT into float32 outputs (float32 accumulation)
 };
 
 // How the B operand is assembled from two sources.
@@ -82,6 +83,7 @@ enum GemmKind : int {
   GK_DGRAD_DOWN = 2,    // dYs[R,d] . Wd[e]^T         -> dHg, dHu     (ragged M)
   GK_DGRAD_GATEUP = 3,  // dH[R,2f] . [Wg|Wu][e]^T    -> dXs          (ragged M)
   GK_WGRAD = 4,         // P[rows,M]^T . Q[rows,N]    -> dW[e][M,N]   (ragged K)
+  GK_WGRAD_F32 = 13,    // as GK_WGRAD, dW stored (or accumulated) as float32
   GK_ROUTER_LOGITS = 5, // x[T,d] . Wr[d,E]           -> logits f32   (one group)
   GK_ROUTER_DWR = 6,    // x[T,d]^T . dl[T,E]         -> dWr[d,E]     (one group, K = T)
   GK_ROUTER_DX = 7,     // dl[T,E] . Wr[d,E]^T        -> dx += [T,d]  (one group, K = E)

@@ -320,6 +320,7 @@ const char* kind_name(int kind, const GemmArgs& g) {
     case GK_DGRAD_DOWN: return "gemm_dgrad_down_swiglu_bwd";
     case GK_DGRAD_GATEUP: return "gemm_dgrad_gateup";
     case GK_WGRAD: return g.c1 ? "gemm_wgrad_gateup" : "gemm_wgrad_down";
+    case GK_WGRAD_F32: return g.c1 ? "gemm_wgrad_gateup_f32" : "gemm_wgrad_down_f32";
     case GK_ROUTER_LOGITS: return "gemm_router_logits";
     case GK_ROUTER_DWR: return "gemm_router_dwr";
     case GK_ROUTER_DWR_SPLIT: return "gemm_router_dwr";
@@ -359,6 +360,7 @@ hipError_t launch_grouped_gemm(GemmKind kind, int dtype, const GemmArgs& g, int 
     case GK_DGRAD_DOWN: return launch_kind<GK_DGRAD_DOWN>(dtype, g, num_cu, stream);
     case GK_DGRAD_GATEUP: return launch_kind<GK_DGRAD_GATEUP>(dtype, g, num_cu, stream);
     case GK_WGRAD: return launch_kind<GK_WGRAD>(dtype, g, num_cu, stream);
+    case GK_WGRAD_F32: return launch_kind<GK_WGRAD_F32>(dtype, g, num_cu, stream);
     case GK_ROUTER_LOGITS: return launch_kind<GK_ROUTER_LOGITS>(dtype, g, num_cu, stream);
     case GK_ROUTER_DWR: return launch_kind<GK_ROUTER_DWR>(dtype, g, num_cu, stream);
     case GK_ROUTER_DX: return launch_kind<GK_ROUTER_DX>(dtype, g, num_cu, stream);

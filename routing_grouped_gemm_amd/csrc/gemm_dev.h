@@ -34,6 +34,10 @@ template <> struct KT<GK_WGRAD> {
   static constexpr bool AK = false, BK_ = false;
   static constexpr int BSP = BS_NONE, EPI = EPI_WGRAD_SPLIT;
 };
+template <> struct KT<GK_WGRAD_F32> {
+  static constexpr bool AK = false, BK_ = false;
+  static constexpr int BSP = BS_NONE, EPI = EPI_WGRAD_SPLIT_F32;
+};
 template <> struct KT<GK_ROUTER_LOGITS> {
   static constexpr bool AK = true, BK_ = false;
   static constexpr int BSP = BS_NONE, EPI = EPI_STORE_F32;
@@ -256,6 +260,14 @@ __device__ __forceinline__ void epilogue4(const GemmArgs& g, const Tile& t, int 
       p = static_cast<TS*>(g.c0) + (long)t.e * g.c_es + row * g.ldc + n;
     else
       p = static_cast<TS*>(g.c1) + (long)t.e * g.c_es + row * g.ldc + (n - g.c_split);
+    store4(p, v, g.accumulate != 0);
+  } else if constexpr (EPI == EPI_WGRAD_SPLIT_F32) {
+    long row = (long)t.m0 + m;
+    float* p;
+    if (n < g.c_split)
+      p = static_cast<float*>(g.c0) + (long)t.e * g.c_es + row * g.ldc + n;
+    else
+      p = static_cast<float*>(g.c1) + (long)t.e * g.c_es + row * g.ldc + (n - g.c_split);
     store4(p, v, g.accumulate != 0);
   } else if constexpr (EPI == EPI_SWIGLU_FWD) {
     long off = ((long)t.row0 + m) * g.ldc + n;
@@ -628,6 +640,21 @@ __device__ __forceinline__ void epi8(const GemmArgs& g, const Tile& t, long row,
       load8(p, o);
 #pragma unroll
       for (int q = 0; q < 8; ++q) w[q] = v[q] + o[q];
+      store8(p, w);
+    } else {
+      store8(p, v);
+    }
+  } else if constexpr (EPI == EPI_WGRAD_SPLIT_F32) {
+    float* p;
+    if (n < g.c_split)
+      p = static_cast<float*>(g.c0) + (long)t.e * g.c_es + row * g.ldc + n;
+    else
+      p = static_cast<float*>(g.c1) + (long)t.e * g.c_es + row * g.ldc + (n - g.c_split);
+    if (g.accumulate) {
+      const float4 o0 = *reinterpret_cast<const float4*>(p);
+      const float4 o1 = *reinterpret_cast<const float4*>(p + 4);
+      const float w[8] = {v[0] + o0.x, v[1] + o0.y, v[2] + o0.z, v[3] + o0.w,
+                          v[4] + o1.x, v[5] + o1.y, v[6] + o1.z, v[7] + o1.w};
       store8(p, w);
     } else {
       store8(p, v);

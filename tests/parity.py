@@ -43,13 +43,16 @@ def relerr(gpu: np.ndarray, ref: np.ndarray) -> float:
 
 
 def run_gpu(wl: Workload, inp: Dict[str, np.ndarray], logits: Optional[np.ndarray] = None,
-            renorm: bool = False, aux_coef: float = 0.0):
-    """Forward + backward of the layer on the GPU; returns every buffer as numpy."""
+            renorm: bool = False, aux_coef: float = 0.0, wgrad_f32: bool = False,
+            wgrad_init: Optional[float] = None):
+    """Forward + backward of the layer on the GPU; returns every buffer as numpy.
+    wgrad_init: fill the weight-gradient buffers with this value and
+    accumulate into them."""
     import routing_grouped_gemm_amd as rgg
     dt = torch.float32 if wl.dtype == "fp32" else torch.bfloat16
     router = wl.routing == "router"
     layer = rgg.ExpertLayer(wl.T, wl.d, wl.E, wl.f, wl.k, dt, wl.prec, router=router,
-                            renorm=renorm, aux_coef=aux_coef)
+                            renorm=renorm, aux_coef=aux_coef, wgrad_f32=wgrad_f32)
     x = dev_tensor(inp, "x", dt)
     Wg, Wu, Wd = (dev_tensor(inp, n, dt) for n in ("Wg", "Wu", "Wd"))
     Wr = dev_tensor(inp, "Wr", dt) if router else None
@@ -61,7 +64,10 @@ def run_gpu(wl: Workload, inp: Dict[str, np.ndarray], logits: Optional[np.ndarra
         kw["topk_idx"] = rgg.upload(inp["topk_idx"])
         kw["topk_w"] = rgg.upload(inp["topk_w"])
     layer.forward(x, Wr, Wg, Wu, Wd, **kw)
-    layer.backward(dY)
+    if wgrad_init is not None:
+        for t in (layer.dWg, layer.dWu, layer.dWd):
+            t.fill_(wgrad_init)
+    layer.backward(dY, accumulate_wgrad=wgrad_init is not None)
     torch.cuda.synchronize()
     names = ["topk_idx", "topk_w", "counts", "offsets", "dest_row", "src_token", "Hg", "Hu",
              "A", "Ys", "y", "dYs", "dw", "dH", "dXs", "dx", "dWg", "dWu", "dWd", "Xs"]
@@ -78,13 +84,13 @@ def run_gpu(wl: Workload, inp: Dict[str, np.ndarray], logits: Optional[np.ndarra
 
 
 def run_oracle(wl: Workload, inp: Dict[str, np.ndarray], logits: Optional[np.ndarray] = None,
-               renorm: bool = False, aux_coef: float = 0.0):
+               renorm: bool = False, aux_coef: float = 0.0, wgrad_f32: bool = False):
     prec = wl.prec
     if wl.routing == "router":
         return O.layer(inp["x"], inp["Wr"], inp["Wg"], inp["Wu"], inp["Wd"], wl.k, inp["dY"], prec,
-                       logits=logits, renorm=renorm, aux_coef=aux_coef)
+                       logits=logits, renorm=renorm, aux_coef=aux_coef, wgrad_f32=wgrad_f32)
     return O.layer(inp["x"], None, inp["Wg"], inp["Wu"], inp["Wd"], wl.k, inp["dY"], prec,
-                   topk_idx=inp["topk_idx"], topk_w=inp["topk_w"])
+                   topk_idx=inp["topk_idx"], topk_w=inp["topk_w"], wgrad_f32=wgrad_f32)
 
 
 EXACT = ("topk_idx", "counts", "offsets", "dest_row", "src_token")

@@ -204,6 +204,33 @@ def test_route_bwd_aux_gradient_alone(name):
     assert e1 <= 1e-4 and e2 <= tol and e3 <= tol
 
 
+@pytest.mark.parametrize("name", ["mid_bf16_E64", "share_zipf_bf16", "mid_mxfp8_E8", "tiny_fp32"])
+def test_wgrad_f32(name):
+    """Float32 weight gradients of a bf16 layer (MOE_WGRAD_F32) against the
+    oracle's float32 variant; a float32 layer is unchanged by the option."""
+    wl, inp, logits = _layer_case(name)
+    ref = run_oracle(wl, inp, logits, wgrad_f32=True)
+    gpu = run_gpu(wl, inp, logits, wgrad_f32=True)
+    compare(wl, gpu, ref)
+
+
+@pytest.mark.parametrize("name", ["mid_bf16_E64", "mid_mxfp8_E8"])
+def test_wgrad_f32_accumulation_keeps_small_increments(name):
+    """Accumulating into float32 gradients that hold 1024: every increment is
+    below half a bf16 unit there (4), so bf16 accumulation would drop them
+    all; in float32 they survive and dW - 1024 matches the oracle."""
+    wl, inp, logits = _layer_case(name)
+    ref = run_oracle(wl, inp, logits, wgrad_f32=True)
+    big = max(float(np.max(np.abs(ref[n]))) for n in ("dWg", "dWu", "dWd"))
+    say(f"  largest |dW| {big:.2e}")
+    assert big < 4.0
+    gpu = run_gpu(wl, inp, logits, wgrad_f32=True, wgrad_init=1024.0)
+    for n in ("dWg", "dWu", "dWd"):
+        e = relerr(gpu[n] - 1024.0, ref[n])
+        say(f"  {n}: relerr of dW - 1024: {e:.2e}")
+        assert e <= 2e-2, (n, e)
+
+
 def test_all_rows_to_one_expert():
     """Logits that send every token to expert 2 first: one expert takes all
     T rows (several M tiles); the others are empty."""
