@@ -242,6 +242,9 @@ def main(argv=None) -> int:
             return rgg.upload(inp[name + "_bits"], torch.bfloat16)
         return rgg.upload(inp[name])
 
+    if wl.passes == "fwd":
+        return bench_forward(args, wl, inp, dev)
+
     router = wl.routing == "router"
     x, dY = dev("x"), dev("dY")
     Wg, Wu, Wd = dev("Wg"), dev("Wu"), dev("Wd")
@@ -347,6 +350,146 @@ def main(argv=None) -> int:
                     "p10": round(float(np.percentile(step_ms, 10)), 4),
                     "p90": round(float(np.percentile(step_ms, 90)), 4)},
         "kernels_ms_per_step": {n: round(tot, 4) for n, _, tot, _ in table},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def fwd_gemm_bytes(name: str, wl, active: int) -> float:
+    """Algorithmic HBM bytes of one forward expert GEMM launch on a small
+    batch: the weights of the experts that received rows, read once, plus
+    the activations read and written once (bf16)."""
+    R, d, f = wl.R, wl.d, wl.f
+    if name == "gemm_fwd_gateup_swiglu":
+        return 2.0 * (active * 2 * d * f + R * d + 3 * R * f)
+    if name == "gemm_fwd_down":
+        return 2.0 * (active * f * d + R * f + R * d)
+    return 0.0
+
+
+def bench_forward(args, wl, inp, dev) -> int:
+    """Inference-shaped workload: latency of one layer forward on a small
+    batch (route -> dispatch -> grouped FFN forward -> combine), launched
+    eagerly and replayed from a HIP graph captured once."""
+    import numpy as np
+    import torch
+    import routing_grouped_gemm_amd as rgg
+
+    x = dev("x")
+    Wg, Wu, Wd, Wr = dev("Wg"), dev("Wu"), dev("Wd"), dev("Wr")
+    dt = torch.float32 if wl.dtype == "fp32" else torch.bfloat16
+    layer = rgg.ExpertLayer(wl.T, wl.d, wl.E, wl.f, wl.k, dt, wl.prec, router=True)
+    K = args.steps
+
+    def fwd():
+        layer.forward(x, Wr, Wg, Wu, Wd)
+
+    for _ in range(args.warmup):
+        fwd()
+    torch.cuda.synchronize()
+    y_eager = layer.y.clone()
+    active = int((layer.counts > 0).sum().item())
+
+    # eager launches, with per-kernel events
+    timer = rgg.KernelTimer(capacity=K * 16)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    with timer:
+        for i in range(K):
+            marks[i].record()
+            fwd()
+        marks[K].record()
+    torch.cuda.synchronize()
+    eager_ms = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(K)])
+    kern = timer.durations()
+
+    # one capture, K replays
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fwd()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fwd()
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    same = bool(torch.equal(layer.y, y_eager))
+    gmarks = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    w0 = time.perf_counter()
+    for i in range(K):
+        gmarks[i].record()
+        graph.replay()
+    gmarks[K].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    graph_ms = np.array([gmarks[i].elapsed_time(gmarks[i + 1]) for i in range(K)])
+
+    per = {}
+    for name, dur in kern:
+        c = per.setdefault(name, [0, 0.0])
+        c[0] += 1
+        c[1] += dur
+    table = sorted(((n, c[0] / K, c[1] / K, c[1] / c[0]) for n, c in per.items()),
+                   key=lambda r: -r[2])
+    dom_name, dom_launch_ms = table[0][0], table[0][3]
+    nbytes = fwd_gemm_bytes(dom_name, wl, active)
+    if nbytes > 0:
+        ach = nbytes / (dom_launch_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "kernel": dom_name, "achieved": round(ach, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(wl.name, dom_name),
+                "per_launch_ms": round(dom_launch_ms, 4),
+                "algorithmic_bytes_per_launch": nbytes}
+    else:
+        roof = {"bound": "hbm", "kernel": dom_name, "achieved": None, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": None, "traffic": None}
+
+    cpu = None
+    if args.cpu_tokens > 0:
+        from oracle import moe_oracle as O
+        cores = len(os.sched_getaffinity(0))
+        t0 = time.perf_counter()
+        O.layer(inp["x"], inp["Wr"], inp["Wg"], inp["Wu"], inp["Wd"], wl.k, None, wl.prec)
+        sec = time.perf_counter() - t0
+        cpu = {"value": round(sec * 1e6, 1), "unit": "us", "cores": int(cores), "kind": "oracle",
+               "sample": f"forward of all {wl.T} token(s) (numpy float64 oracle with "
+                         f"{wl.prec} storage rounding)"}
+
+    if args.kernels:
+        for n, c, tot, one in table:
+            print(f"{n:32s} {c:13.0f} {tot:9.4f} {one:10.4f}", file=sys.stderr)
+
+    lat_us = float(np.median(graph_ms)) * 1e3
+    out = {
+        "metric": "MoE layer forward latency on a small batch (HIP graph replay)",
+        "value": round(lat_us, 2),
+        "unit": "us",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(lat_us / 1e3, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.prec,
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02^2) weights)",
+        "config": {"workload": wl.name, "T": wl.T, "d_model": wl.d, "experts": wl.E,
+                   "d_ff": wl.f, "top_k": wl.k, "routed_rows": wl.R, "passes": "forward",
+                   "active_experts": active, "parallelism": "single GPU"},
+        "tokens_per_s": round(wl.T / (lat_us * 1e-6), 1),
+        "graph_us": {"median": round(lat_us, 2),
+                     "p10": round(float(np.percentile(graph_ms, 10)) * 1e3, 2),
+                     "p90": round(float(np.percentile(graph_ms, 90)) * 1e3, 2)},
+        "eager_us": {"median": round(float(np.median(eager_ms)) * 1e3, 2),
+                     "p10": round(float(np.percentile(eager_ms, 10)) * 1e3, 2),
+                     "p90": round(float(np.percentile(eager_ms, 90)) * 1e3, 2)},
+        "graph_output_equals_eager": same,
+        "wall_us_per_replay": round(wall * 1e6 / K, 2),
+        "kernels_us_per_forward": {n: round(tot * 1e3, 2) for n, _, tot, _ in table},
         "roofline": roof,
         "cpu_baseline": cpu,
     }

@@ -98,6 +98,10 @@ enum moe_op {
  *   lower index; selection is made on the float32 logits.
  *   Limits: 1 <= E <= 256, 1 <= k <= E.  d % 64 == 0 (unless logits are an
  *   input).
+ *   Workspace: optional.  With moe_workspace_size(MOE_OP_ROUTE, ...) bytes
+ *   (non-zero for bf16 batches of at most 64 tokens with E % 8 == 0) the
+ *   small-batch router runs (partial logits over slices of Wr's rows, added
+ *   in slice order); without it the general one (one GEMM) does.
  */
 int moe_route(const void* x, const void* Wr, int T, int d, int E, int k, int dtype,
               unsigned flags, float* logits, int32_t* topk_idx, float* topk_w,

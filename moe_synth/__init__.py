@@ -48,6 +48,7 @@ class Workload:
     zipf_s: float = 1.1
     empty_experts: Tuple[int, ...] = ()
     note: str = ""
+    passes: str = "fwd+bwd"   # "fwd": inference-shaped, forward only
 
     @property
     def R(self) -> int:
@@ -66,6 +67,13 @@ class Workload:
 
     def expert_flops(self) -> float:
         return 18.0 * self.R * self.d * self.f
+
+    def fwd_flops(self) -> float:
+        """Forward only: 6*R*d*f in the experts plus 2*T*d*E in the router."""
+        g = 6.0 * self.R * self.d * self.f
+        if self.routing == "router":
+            g += 2.0 * self.T * self.d * self.E
+        return g
 
 
 WORKLOADS: Dict[str, Workload] = {
@@ -91,6 +99,13 @@ WORKLOADS: Dict[str, Workload] = {
     "tiny_mxfp8": Workload("tiny_mxfp8", T=256, d=64, E=8, f=128, k=2,
                            dtype="bf16", prec="mxfp8", routing="router"),
 }
+# Inference-shaped small batches of the OLMoE layer (token-by-token generation
+# and short prompts): forward only.
+for _t in (1, 8, 64):
+    WORKLOADS[f"olmoe_decode_t{_t}"] = Workload(
+        f"olmoe_decode_t{_t}", T=_t, d=2048, E=64, f=1024, k=8, dtype="bf16", prec="bf16",
+        routing="router", passes="fwd", note=f"OLMoE layer forward on {_t} token(s)")
+del _t
 
 
 def workload(base: str, **overrides) -> Workload:

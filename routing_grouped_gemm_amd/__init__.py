@@ -139,13 +139,15 @@ def moe_workspace_size(op: str, T: int, d: int, E: int, f: int, k: int, dtype: t
     return out.value
 
 
-def moe_route(x, Wr, k, logits, topk_idx, topk_w, logits_in=False, renorm=False, stream=None):
+def moe_route(x, Wr, k, logits, topk_idx, topk_w, logits_in=False, renorm=False, ws=None,
+              stream=None):
     T, E = logits.shape
     d = x.shape[1] if x is not None else 64
     dt = _dtype(x) if x is not None else MOE_BF16
     flags = (MOE_ROUTE_LOGITS_IN if logits_in else 0) | (MOE_ROUTE_RENORM if renorm else 0)
+    wp, wb = _ws(ws)
     _check(lib().moe_route(_ptr(x), _ptr(Wr), T, d, E, k, dt, flags, _ptr(logits),
-                           _ptr(topk_idx), _ptr(topk_w), None, 0, _stream(stream)), "moe_route")
+                           _ptr(topk_idx), _ptr(topk_w), wp, wb, _stream(stream)), "moe_route")
 
 
 def moe_dispatch(x, topk_idx, E, counts, offsets, dest_row, src_token, Xs, ws, Xq=None,
@@ -333,6 +335,7 @@ class ExpertLayer:
         def ws(op):
             n = moe_workspace_size(op, T, d, E, f, k, dtype, prec)
             return torch.empty(max(n, 256), dtype=torch.uint8, device=dev)
+        self.ws_route = ws("route")
         self.ws_dispatch = ws("dispatch")
         self.ws_fwd = ws("ffn_fwd")
         self.ws_bwd = ws("ffn_bwd")
@@ -345,7 +348,8 @@ class ExpertLayer:
             if logits is not None:
                 self.logits.copy_(logits)
             moe_route(x, Wr, self.k, self.logits, self.topk_idx, self.topk_w,
-                      logits_in=logits is not None, renorm=self.renorm, stream=stream)
+                      logits_in=logits is not None, renorm=self.renorm, ws=self.ws_route,
+                      stream=stream)
         else:
             self.topk_idx.copy_(topk_idx)
             self.topk_w.copy_(topk_w)

@@ -9,6 +9,7 @@
 #include "gemm.h"
 #include "mx.h"
 #include "route.h"
+#include "skinny.h"
 
 using namespace moe;
 
@@ -144,6 +145,9 @@ int moe_workspace_size(int op, int T, int d, int E, int f, int k, int dtype, int
   const size_t R = (size_t)T * k;
   switch (op) {
     case MOE_OP_ROUTE:
+      if (dtype == MOE_BF16 && route_small_applies(T, d, E))
+        *bytes = align_up(route_small_workspace(T, d, E));
+      return MOE_OK;
     case MOE_OP_COMBINE:
     case MOE_OP_COMBINE_BWD:
     case MOE_OP_DISPATCH_BWD:
@@ -152,7 +156,10 @@ int moe_workspace_size(int op, int T, int d, int E, int f, int k, int dtype, int
       *bytes = dispatch_ws(T, E);
       return MOE_OK;
     case MOE_OP_FFN_FWD:
-      *bytes = (prec == MOE_PREC_MXFP8) ? mx_fwd_workspace(R, d, f, E) : 0;
+      if (prec == MOE_PREC_MXFP8)
+        *bytes = mx_fwd_workspace(R, d, f, E);
+      else if (prec == MOE_PREC_BF16 && R <= (size_t)kSkinnyMaxRows)
+        *bytes = align_up(skinny_workspace((int)R, E, d, f));
       return MOE_OK;
     case MOE_OP_FFN_BWD:
       *bytes = (prec == MOE_PREC_MXFP8) ? mx_bwd_workspace(R, d, f, E) : 0;
@@ -170,7 +177,6 @@ int moe_workspace_size(int op, int T, int d, int E, int f, int k, int dtype, int
 int moe_route(const void* x, const void* Wr, int T, int d, int E, int k, int dtype,
               unsigned flags, float* logits, int32_t* topk_idx, float* topk_w, void* ws,
               size_t ws_bytes, void* stream) {
-  (void)ws; (void)ws_bytes;
   const bool lin = (flags & MOE_ROUTE_LOGITS_IN) != 0;
   if (!all_nonnull(logits, topk_idx, topk_w)) return MOE_ERR_NULL;
   if (!lin && !all_nonnull(x, Wr)) return MOE_ERR_NULL;
@@ -180,9 +186,15 @@ int moe_route(const void* x, const void* Wr, int T, int d, int E, int k, int dty
     if (int s = check_width(d)) return s;
     if (int s = check_elems(T, d)) return s;
   }
-  if (!all_aligned(x, Wr, logits, topk_idx, topk_w)) return MOE_ERR_ALIGN;
+  if (!all_aligned(x, Wr, logits, topk_idx, topk_w, ws)) return MOE_ERR_ALIGN;
   hipStream_t st = static_cast<hipStream_t>(stream);
   clear_stale_error();
+  const int renorm = (flags & MOE_ROUTE_RENORM) ? 1 : 0;
+  if (!lin && dtype == MOE_BF16 && route_small_applies(T, d, E) && ws &&
+      ws_bytes >= route_small_workspace(T, d, E))
+    return status_of(launch_route_small(static_cast<const uint16_t*>(x),
+                                        static_cast<const uint16_t*>(Wr), T, d, E, k, renorm,
+                                        static_cast<float*>(ws), logits, topk_idx, topk_w, st));
   if (!lin) {
     GemmArgs g{};
     g.E = 1; g.offsets = nullptr; g.rows_total = T; g.ragged = RAG_M;
@@ -192,8 +204,7 @@ int moe_route(const void* x, const void* Wr, int T, int d, int E, int k, int dty
     g.c0 = logits; g.ldc = E;
     MOE_TRY(launch_grouped_gemm(GK_ROUTER_LOGITS, gemm_engine(dtype, E), g, num_cu(), st));
   }
-  return status_of(launch_topk_softmax(logits, T, E, k, (flags & MOE_ROUTE_RENORM) ? 1 : 0,
-                                       topk_idx, topk_w, st));
+  return status_of(launch_topk_softmax(logits, T, E, k, renorm, topk_idx, topk_w, st));
 }
 
 int moe_dispatch(const void* x, const int32_t* topk_idx, int T, int d, int E, int k, int dtype,
@@ -212,6 +223,9 @@ int moe_dispatch(const void* x, const int32_t* topk_idx, int T, int d, int E, in
   if (ws_bytes < dispatch_ws(T, E)) return MOE_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   clear_stale_error();
+  if (!mx && dispatch_small_applies(T, k))
+    return status_of(launch_dispatch_small(dtype, x, topk_idx, T, d, E, k, counts, offsets,
+                                           dest_row, src_token, Xs, st));
   const size_t nblk = (size_t)(T + 63) / 64;
   int32_t* hist = static_cast<int32_t*>(ws);
   int32_t* base = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + align_up(nblk * E * 4));
@@ -244,6 +258,17 @@ int moe_grouped_ffn_fwd(const void* Xs, const uint8_t* Xs_scale, const int32_t* 
     return status_of(mx_ffn_fwd(Xs, Xs_scale, offsets, (int)R, d, f, E, Wg, Wu, Wd, Hg, Hu, A,
                                 Ys, ws, num_cu(), st));
   }
+  if (prec == MOE_PREC_BF16 && skinny_applies((int)R, E, d, f)) {
+    // a few rows per expert: the weight-streaming small-batch engine
+    const size_t need = skinny_workspace((int)R, E, d, f);
+    if (need && !ws) return MOE_ERR_NULL;
+    if (ws_bytes < need) return MOE_ERR_WORKSPACE;
+    return status_of(launch_skinny_ffn_fwd(
+        offsets, E, (int)R, d, f, static_cast<const bf16_t*>(Xs), static_cast<const bf16_t*>(Wg),
+        static_cast<const bf16_t*>(Wu), static_cast<const bf16_t*>(Wd), static_cast<bf16_t*>(Hg),
+        static_cast<bf16_t*>(Hu), static_cast<bf16_t*>(A), static_cast<bf16_t*>(Ys),
+        static_cast<float*>(ws), st));
+  }
   const int eng = gemm_engine(dtype);
   GemmArgs g{};
   g.E = E; g.offsets = offsets; g.rows_total = (int)R; g.ragged = RAG_M;
@@ -269,6 +294,9 @@ int moe_combine(const void* Ys, const float* topk_w, const int32_t* dest_row, in
   if (int s = check_width(d)) return s;
   if (!all_aligned(Ys, topk_w, dest_row, y)) return MOE_ERR_ALIGN;
   clear_stale_error();
+  if (combine_small_applies(T))
+    return status_of(launch_combine_small(dtype, Ys, topk_w, dest_row, T, d, k, y,
+                                          static_cast<hipStream_t>(stream)));
   return status_of(launch_combine(dtype, Ys, topk_w, dest_row, T, d, k, y,
                                   static_cast<hipStream_t>(stream)));
 }

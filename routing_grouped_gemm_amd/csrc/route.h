@@ -2,9 +2,31 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 namespace moe {
+
+// Small batches: the router runs as two kernels (partial logits over slices
+// of kRouteSlice rows of Wr, then sum, softmax and top-k), the dispatch
+// (metadata and copies) and the combine as one kernel each.
+constexpr int kSmallMaxTokens = 64;     // router and combine
+constexpr int kSmallMaxRows = 1024;     // dispatch: tokens * top_k
+constexpr int kRouteSlice = 128;
+
+bool route_small_applies(int T, int d, int E);
+// part: float workspace of route_small_workspace(T, d, E) bytes
+size_t route_small_workspace(int T, int d, int E);
+hipError_t launch_route_small(const uint16_t* x, const uint16_t* Wr, int T, int d, int E, int k,
+                              int renorm, float* part, float* logits, int32_t* idx, float* w,
+                              hipStream_t s);
+bool dispatch_small_applies(int T, int k);
+hipError_t launch_dispatch_small(int dtype, const void* x, const int32_t* idx, int T, int d, int E,
+                                 int k, int32_t* counts, int32_t* offsets, int32_t* dest_row,
+                                 int32_t* src_token, void* Xs, hipStream_t s);
+bool combine_small_applies(int T);
+hipError_t launch_combine_small(int dtype, const void* Ys, const float* w, const int32_t* dest,
+                                int T, int d, int k, void* y, hipStream_t s);
 
 // renorm: divide the k chosen probabilities by their sum.
 hipError_t launch_topk_softmax(const float* logits, int T, int E, int k, int renorm, int32_t* idx,

@@ -19,6 +19,7 @@
 #include "mx_codec.h"
 #include "hook.h"
 #include "route.h"
+#include "topk_dev.h"
 
 namespace moe {
 
@@ -32,57 +33,7 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restri
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  const float* row = logits + (long)t * E;
-  float v[4];
-  int taken = 0;  // bit q: logit q of this lane already chosen
-  float mx = -INFINITY;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    int e = lane + 64 * q;
-    v[q] = (e < E) ? row[e] : -INFINITY;
-    if (e < E) mx = fmaxf(mx, v[q]);
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-  float se = 0.0f;
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-    if (lane + 64 * q < E) se += expf(v[q] - mx);
-  se = wave_sum(se);
-  for (int j = 0; j < k; ++j) {
-    // lane-local best among the untaken: larger logit, then lower index
-    float bv = -INFINITY;
-    int be = 0x7fffffff;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      int e = lane + 64 * q;
-      if (e < E && !((taken >> q) & 1)) {
-        if (v[q] > bv || (v[q] == bv && e < be) || be == 0x7fffffff) {
-          bv = v[q];
-          be = e;
-        }
-      }
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      float ov = __shfl_xor(bv, o, 64);
-      int oe = __shfl_xor(be, o, 64);
-      bool better = (oe != 0x7fffffff) &&
-                    (be == 0x7fffffff || ov > bv || (ov == bv && oe < be));
-      if (better) { bv = ov; be = oe; }
-    }
-    if ((be & 63) == lane) taken |= 1 << (be >> 6);
-    if (lane == 0) {
-      topk_idx[(long)t * k + j] = be;
-      topk_w[(long)t * k + j] = expf(bv - mx) / se;
-    }
-  }
-  if (renorm && lane == 0) {
-    // optional top-k renormalisation: the chosen probabilities over their sum
-    float S = 0.0f;
-    for (int j = 0; j < k; ++j) S += topk_w[(long)t * k + j];
-    for (int j = 0; j < k; ++j) topk_w[(long)t * k + j] /= S;
-  }
+  topk_row(logits + (long)t * E, E, k, renorm, lane, topk_idx + (long)t * k, topk_w + (long)t * k);
 }
 
 // ---------------------------------------------------------------------------

@@ -75,6 +75,18 @@ def test_workspace_sizes(L):
     assert ws_size(L, 7, 8192, 2048, 64, 1024, 8, BF16, P_BF16) == (OK, 8192 * 64 * 2 + 32 * 2048 * 64 * 4)
     assert ws_size(L, 7, 100, 64, 6, 64, 2, BF16, P_BF16) == (OK, 100 * 64 * 2)  # E % 8: no split
     assert ws_size(L, 7, 256, 64, 8, 128, 2, F32, P_F32) == (OK, 0)
+    # small batches: router partial logits (slices of 128 rows of Wr) and the
+    # float partial sums of the sliced small-batch expert GEMMs
+    assert ws_size(L, 0, 1, 2048, 64, 1024, 8, BF16, P_BF16) == (OK, 16 * 1 * 64 * 4)
+    assert ws_size(L, 0, 64, 2048, 64, 1024, 8, BF16, P_BF16) == (OK, 16 * 64 * 64 * 4)
+    assert ws_size(L, 0, 65, 2048, 64, 1024, 8, BF16, P_BF16) == (OK, 0)     # general router
+    assert ws_size(L, 0, 8, 2048, 6, 1024, 2, BF16, P_BF16) == (OK, 0)      # E % 8 != 0
+    assert ws_size(L, 0, 8, 2048, 64, 1024, 8, F32, P_F32) == (OK, 0)
+    # T=1, top-8 of 64: 8 experts x 16 column blocks, sliced 4 ways (gate/up
+    # and down) into float partials
+    assert ws_size(L, 2, 1, 2048, 64, 1024, 8, BF16, P_BF16) == (OK, 4 * 8 * 2048 * 4)
+    assert ws_size(L, 2, 64, 2048, 64, 1024, 8, BF16, P_BF16) == (OK, 0)    # 1024 workgroups
+    assert ws_size(L, 2, 8192, 2048, 64, 1024, 8, BF16, P_BF16) == (OK, 0)   # general engine
     # load-balancing loss: float32 partial sums of E per 64-token block
     assert ws_size(L, 8, 8192, 2048, 64, 1024, 8, BF16, P_BF16) == (OK, 128 * 64 * 4)
     assert ws_size(L, 8, 100, 64, 3, 64, 1, F32, P_F32) == (OK, 256)

@@ -32,6 +32,11 @@ SHAPES = {
     "edge_kE": ("olmoe_bf16", dict(name="edge_kE", T=70, d=128, E=8, f=64, k=8)),
     "edge_E3_fp32": ("tiny_fp32", dict(name="edge_E3_fp32", T=50, d=64, E=3, f=64, k=2)),
     "edge_E6_bf16": ("olmoe_bf16", dict(name="edge_E6_bf16", T=130, d=128, E=6, f=128, k=2)),
+    # small batches (the weight-streaming forward engine): contraction slices
+    # with a float reduction (d = 256), a half-empty last down column block
+    # (d = 192), experts with more than 32 rows and empty experts (Zipf loads)
+    "skinny_d256": ("olmoe_bf16", dict(name="skinny_d256", T=40, d=256, E=8, f=320, k=2)),
+    "skinny_zipf_d192": ("share1t_bf16", dict(name="skinny_zipf_d192", T=700, d=192, f=256)),
     "tiny_mxfp8": ("tiny_mxfp8", {}),
     # d = 576: an odd number of 64-deep K stages; f = 320: a half-filled last gate/up panel
     "mid_mxfp8_E8": ("olmoe_mxfp8", dict(name="mid_mxfp8_E8", T=1000, d=576, E=8, f=320, k=2)),
