@@ -79,6 +79,14 @@ _SYMBOLS = {
     "combine_kernel": ["combine"],
     "combine_bwd_kernel": ["combine_bwd"],
     "gather_sum_kernel": ["gather_sum"],
+    "skinny_kernel<0>": ["skinny_fwd_gateup"],
+    "skinny_kernel<1>": ["skinny_fwd_down"],
+    "skinny_reduce_kernel<0>": ["skinny_reduce_gateup"],
+    "skinny_reduce_kernel<1>": ["skinny_reduce_down"],
+    "route_part_kernel": ["route_small_part"],
+    "route_final_kernel": ["route_small_final"],
+    "dispatch_small_kernel": ["dispatch_small"],
+    "combine_small_kernel": ["combine_small"],
 }
 
 
@@ -111,7 +119,7 @@ def _counter_means(directory: str):
     acc = {}
     for r in rows:
         name = r["Kernel_Name"].split("(")[0].replace("void ", "").replace("moe::mf::", "")
-        name = name.replace("moe::", "")
+        name = name.replace("moe::sk::", "").replace("moe::", "")
         sym = next((k for k in _SYMBOLS if name.startswith(k.split("<")[0]) and
                     (("<" not in k) or name.startswith(k))), name)
         n = seen.get(sym, 0)

@@ -91,10 +91,57 @@ __device__ __forceinline__ float sigmoid_f(float z) {
 }
 __device__ __forceinline__ float silu_f(float z) { return z * sigmoid_f(z); }
 
+// Cross-lane moves by DPP (gfx9 controls).  A lane that the row mask leaves
+// unwritten receives `old`.  Shuffles by ds_bpermute go through LDS and cost
+// an LDS round trip each; these stay in the VALU.
+constexpr int kDppQuad1032 = 0xB1;     // quad_perm [1,0,3,2]: lane ^ 1
+constexpr int kDppQuad2301 = 0x4E;     // quad_perm [2,3,0,1]: lane ^ 2
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+constexpr int kDppRowBcast15 = 0x142;  // lane 15 of a row to the next row
+constexpr int kDppRowBcast31 = 0x143;  // lane 31 to rows 2 and 3
+
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ float dpp_f(float old, float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old),
+                                                               __builtin_bit_cast(int, v), CTRL,
+                                                               ROWS, 0xF, false));
+}
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ int dpp_i(int old, int v) {
+  return __builtin_amdgcn_update_dpp(old, v, CTRL, ROWS, 0xF, false);
+}
+__device__ __forceinline__ float lane63_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+// Sum over the wave, returned to every lane: pairs, quads, half-rows, rows,
+// then rows 0+1 and 0+1+2+3 (fixed order).
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  v += dpp_f<kDppQuad1032>(0.0f, v);
+  v += dpp_f<kDppQuad2301>(0.0f, v);
+  v += dpp_f<kDppRowHalfMirror>(0.0f, v);
+  v += dpp_f<kDppRowMirror>(0.0f, v);
+  v += dpp_f<kDppRowBcast15, 0xA>(0.0f, v);
+  v += dpp_f<kDppRowBcast31, 0xC>(0.0f, v);
+  return lane63_f(v);
+}
+
+// Maximum over the wave, returned to every lane.
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_f<kDppQuad1032>(v, v));
+  v = fmaxf(v, dpp_f<kDppQuad2301>(v, v));
+  v = fmaxf(v, dpp_f<kDppRowHalfMirror>(v, v));
+  v = fmaxf(v, dpp_f<kDppRowMirror>(v, v));
+  v = fmaxf(v, dpp_f<kDppRowBcast15, 0xA>(v, v));
+  v = fmaxf(v, dpp_f<kDppRowBcast31, 0xC>(v, v));
+  return lane63_f(v);
+}
+
+// Maximum over the 4 lanes of each quad (lane ^ 1, lane ^ 2).
+__device__ __forceinline__ float quad_max(float v) {
+  v = fmaxf(v, dpp_f<kDppQuad1032>(v, v));
+  return fmaxf(v, dpp_f<kDppQuad2301>(v, v));
 }
 
 }  // namespace moe

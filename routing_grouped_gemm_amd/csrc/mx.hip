@@ -126,7 +126,7 @@ __global__ __launch_bounds__(256) void mx_quant_cols_kernel(
     v[i] = bf16_to_f32(tile[16 * q + i][n]);
     amax = fmaxf(amax, fabsf(v[i]));
   }
-  amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
+  amax = fmaxf(amax, dpp_f<kDppQuad1032>(amax, amax));   // the partner lane (lane ^ 1)
   const int E = mx_block_exponent(amax);
   float sv[8];
   uint32_t w[4];

@@ -42,8 +42,7 @@ __device__ __forceinline__ int quant8(const float (&v)[8], uint32_t (&codes)[2])
   float amax = 0.0f;
 #pragma unroll
   for (int q = 0; q < 8; ++q) amax = fmaxf(amax, fabsf(v[q]));
-  amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
-  amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
+  amax = quad_max(amax);
   const int E = mx_block_exponent(amax);
   float s[8];
 #pragma unroll

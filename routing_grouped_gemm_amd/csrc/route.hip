@@ -289,8 +289,7 @@ __global__ __launch_bounds__(256) void router_bwd_softmax_kernel(
     if (e < E) mx = fmaxf(mx, v[q]);
     dp[q] = 0.0f;
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+  mx = wave_max(mx);
   float se = 0.0f;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -371,8 +370,7 @@ __global__ __launch_bounds__(256) void aux_partial_kernel(const float* __restric
       v[q] = (e < E) ? row[e] : -INFINITY;
       mx = fmaxf(mx, v[q]);
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    mx = wave_max(mx);
     float se = 0.0f;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {

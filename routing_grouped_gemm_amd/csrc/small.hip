@@ -170,7 +170,7 @@ __global__ __launch_bounds__(256) void dispatch_small_kernel(
     if (e >= 0) atomicAdd(&cw[wave * E + e], 1);
     int rin = 0;
     for (int l = 0; l < 64; ++l) {
-      const int el = __shfl(e, l, 64);
+      const int el = __builtin_amdgcn_readlane(e, l);
       rin += (l < lane && el == e) ? 1 : 0;
     }
     __syncthreads();

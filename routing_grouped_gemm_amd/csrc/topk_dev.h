@@ -10,6 +10,33 @@
 
 namespace moe {
 
+// (value, expert) candidate o replaces the current one when it is present
+// and has the larger value, or the same value and the lower expert.
+__device__ __forceinline__ void take_better(float& bv, int& be, float ov, int oe) {
+  const bool better = (oe != 0x7fffffff) &&
+                      (be == 0x7fffffff || ov > bv || (ov == bv && oe < be));
+  if (better) { bv = ov; be = oe; }
+}
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ void argmax_step(float& bv, int& be) {
+  const float ov = dpp_f<CTRL, ROWS>(bv, bv);
+  const int oe = dpp_i<CTRL, ROWS>(be, be);
+  take_better(bv, be, ov, oe);
+}
+// Best (value, expert) of the wave, returned to every lane (DPP reduction in
+// the pattern of wave_sum; lanes outside a step's row mask compare with
+// themselves).
+__device__ __forceinline__ void wave_argmax(float& bv, int& be) {
+  argmax_step<kDppQuad1032>(bv, be);
+  argmax_step<kDppQuad2301>(bv, be);
+  argmax_step<kDppRowHalfMirror>(bv, be);
+  argmax_step<kDppRowMirror>(bv, be);
+  argmax_step<kDppRowBcast15, 0xA>(bv, be);
+  argmax_step<kDppRowBcast31, 0xC>(bv, be);
+  bv = lane63_f(bv);
+  be = __builtin_amdgcn_readlane(be, 63);
+}
+
 // One token's softmax and top-k, by one wave: row = its float32 logits (global
 // memory or LDS).  Slots are ordered by (logit desc, expert asc); weights are
 // the softmax probabilities of the chosen experts, divided by their sum when
@@ -25,8 +52,7 @@ __device__ __forceinline__ void topk_row(const float* row, int E, int k, int ren
     v[q] = (e < E) ? row[e] : -INFINITY;
     if (e < E) mx = fmaxf(mx, v[q]);
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+  mx = wave_max(mx);
   float se = 0.0f;
 #pragma unroll
   for (int q = 0; q < 4; ++q)
@@ -47,14 +73,7 @@ __device__ __forceinline__ void topk_row(const float* row, int E, int k, int ren
         }
       }
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      float ov = __shfl_xor(bv, o, 64);
-      int oe = __shfl_xor(be, o, 64);
-      bool better = (oe != 0x7fffffff) &&
-                    (be == 0x7fffffff || ov > bv || (ov == bv && oe < be));
-      if (better) { bv = ov; be = oe; }
-    }
+    wave_argmax(bv, be);
     if ((be & 63) == lane) taken |= 1 << (be >> 6);
     const float p = expf(bv - mx) / se;
     wsum += p;
