@@ -370,9 +370,9 @@ def fwd_gemm_bytes(name: str, wl, active: int) -> float:
     batch: the weights of the experts that received rows, read once, plus
     the activations read and written once (bf16)."""
     R, d, f = wl.R, wl.d, wl.f
-    if name == "gemm_fwd_gateup_swiglu":
+    if name in ("gemm_fwd_gateup_swiglu", "skinny_fwd_gateup"):
         return 2.0 * (active * 2 * d * f + R * d + 3 * R * f)
-    if name == "gemm_fwd_down":
+    if name in ("gemm_fwd_down", "skinny_fwd_down"):
         return 2.0 * (active * f * d + R * f + R * d)
     return 0.0
 
