@@ -81,11 +81,16 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(GemmArgs g) {
 
   for (;;) {
     // Stages 0 and 1 of tile t are in flight (as far as they exist).
+    // The first k16 step of the tile writes the accumulators from a zero
+    // operand, so they are not cleared first (256 register writes per tile);
+    // a tile with no K stage (an expert without rows) clears them here.
     f32x16_t acc[4][4];
+    if (nk == 0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
+    }
 
     // Two stage buffers; stage kt+1 loads while stage kt is consumed in four
     // k16 steps with alternating fragment sets F0 / F1: the fragments of
@@ -106,10 +111,20 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(GemmArgs g) {
     // kt, its B loads and prefetches with step 0 of stage kt+1 (pend_b).
     bool pend_b = false;
     int pend_stage = 0;
+    // The next tile's coordinates are decoded while this tile's first stage
+    // lands (a binary search over the group table in LDS).
+    L = logical_tile(it + 1);
+    const bool has_next = L < ntiles;
+    Tile tn = t;
+    if (has_next) tn = sched_decode<BM, BNT>(g, sch, L);
     for (int kt = 0; kt < nk; ++kt) {
       __builtin_amdgcn_s_waitcnt(kLgkm0);
       load_frags<AMN, BMN, DUAL>(smem, kt, 1, wm, wn, lane, fa1, fb1);
-      if constexpr (SPLIT) {
+      if (kt == 0) {
+        mfma16_first(acc, fa0, fb0);
+        interleave_mfma_ds();
+        __builtin_amdgcn_sched_barrier(0);
+      } else if constexpr (SPLIT) {
         const bool dma = pend_b;
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -179,13 +194,10 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(GemmArgs g) {
     // follows once the slices are read.  Loads complete in order, so the
     // stage waits of the next tile stay exact whatever the epilogue's own
     // global accesses do.
-    L = logical_tile(++it);
-    const bool has_next = L < ntiles;
-    Tile tn = t;
+    ++it;
     Plan pan = pa, pbn = pb;
     int nkn = 0;
     if (has_next) {
-      tn = sched_decode<BM, BNT>(g, sch, L);
       plan_tile<KIND>(g, tn, wave, lane, pan, pbn);
       nkn = (tn.klen + BK - 1) / BK;
       if (nkn > 0) issue_stage(pan, pbn, 0);

@@ -541,6 +541,16 @@ __device__ __forceinline__ void mfma16(f32x16_t (&acc)[4][4], const bf16x8_t (&f
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
 }
 
+// The first k16 step of a tile: accumulators from a zero operand.
+__device__ __forceinline__ void mfma16_first(f32x16_t (&acc)[4][4], const bf16x8_t (&fa)[4],
+                                             const bf16x8_t (&fb)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], f32x16_t{}, 0, 0, 0);
+}
+
 // MFMAs 2q and 2q+1 of mfma16 (row block q/2, column blocks 2(q%2), +1).
 __device__ __forceinline__ void mfma_pair(f32x16_t (&acc)[4][4], const bf16x8_t (&fa)[4],
                                           const bf16x8_t (&fb)[4], int q) {
