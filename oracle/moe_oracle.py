@@ -352,8 +352,42 @@ def layer_forward(x, Wg, Wu, Wd, topk_idx, topk_w, prec: str = "fp64") -> Dict[s
                 Xs=Xs, Hg=Hg, Hu=Hu, A=A, Ys=Ys, y=y)
 
 
+def mx_quantize_rows(a, block: int = 32):
+    """Block-quantise along the row axis (axis 0) in blocks of `block` rows
+    starting at row 0; a last partial block is taken as if padded with zero
+    rows (zeros change neither its largest magnitude nor any product).
+    Returns the dequantised values (float64)."""
+    a = np.asarray(a, dtype=F64)
+    n = a.shape[0]
+    pad = (-n) % block
+    if pad:
+        a = np.concatenate([a, np.zeros((pad,) + a.shape[1:])], axis=0)
+    return mx_quantize(a, axis=0, block=block)[0][:n]
+
+
+def weight_gradients(Xs, dHg, dHu, A, dYs, offsets, mx_tokens: bool = False):
+    """Per expert e with rows [lo, hi): dWg[e] = Xs^T.dHg, dWu[e] = Xs^T.dHu,
+    dWd[e] = A^T.dYs over the expert's rows, float64 sums (an expert without
+    rows gets zeros).  mx_tokens: every operand is first block-quantised
+    along its contraction axis, the tokens of the expert's segment, in blocks
+    of 32 rows from the segment's first row (mx_quantize_rows)."""
+    E = len(offsets) - 1
+    d, f, dm = np.shape(Xs)[1], np.shape(dHg)[1], np.shape(dYs)[1]
+    dWg = np.zeros((E, d, f)); dWu = np.zeros((E, d, f)); dWd = np.zeros((E, f, dm))
+    q = mx_quantize_rows if mx_tokens else (lambda a: np.asarray(a, dtype=F64))
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        xs, g, u, a, y = (q(t[lo:hi]) for t in (Xs, dHg, dHu, A, dYs))
+        dWd[e] = a.T @ y
+        dWg[e] = xs.T @ g
+        dWu[e] = xs.T @ u
+    return dWg, dWu, dWd
+
+
 def layer_backward(fwd, x, Wg, Wu, Wd, topk_idx, topk_w, dY, prec: str = "fp64",
-                   wgrad_f32: bool = False) -> Dict[str, np.ndarray]:
+                   wgrad_f32: bool = False, mx_wgrad: bool = False) -> Dict[str, np.ndarray]:
     """Backward of the expert part for the loss L = sum_t <y[t], dY[t]>.
 
     dw[t,j] = <dY[t], Ys[row]>; dYs[row] = w[t,j] dY[t];
@@ -365,7 +399,10 @@ def layer_backward(fwd, x, Wg, Wu, Wd, topk_idx, topk_w, dY, prec: str = "fp64",
     contraction axis; weight gradients use the unquantised operands.
     wgrad_f32 (OLMo-core 3 release summary, technical principle section:
     optional FP32 gradient accumulation): the weight gradients are kept in
-    float32 instead of being rounded to the storage type."""
+    float32 instead of being rounded to the storage type.
+    mx_wgrad ('mxfp8' only; olmoforge README, MXFP8 block quantisation applied
+    to the weight-gradient GEMMs as well): their operands are block-quantised
+    along the tokens of each expert (weight_gradients)."""
     rnd = _storage_round(prec)
     wrnd = _f32(prec) if wgrad_f32 else rnd
     mx = prec == "mxfp8"
@@ -387,7 +424,6 @@ def layer_backward(fwd, x, Wg, Wu, Wd, topk_idx, topk_w, dY, prec: str = "fp64",
     dw = _f32(prec)(dw)
     dYs = rnd(dYs)
     dHg = np.zeros((R, f)); dHu = np.zeros((R, f)); dXs = np.zeros((R, d))
-    dWg = np.zeros((E, d, f)); dWu = np.zeros((E, d, f)); dWd = np.zeros((E, f, d))
     Hg, Hu, A, Xs = fwd["Hg"], fwd["Hu"], fwd["A"], fwd["Xs"]
     for e in range(E):
         lo, hi = int(offsets[e]), int(offsets[e + 1])
@@ -410,9 +446,7 @@ def layer_backward(fwd, x, Wg, Wu, Wd, topk_idx, topk_w, dY, prec: str = "fp64",
             Wgq = mx_quantize(Wge, axis=1)[0]
             Wuq = mx_quantize(Wue, axis=1)[0]
         dXs[lo:hi] = rnd(a_g @ Wgq.T + a_u @ Wuq.T)
-        dWd[e] = A[lo:hi].T @ dYs[lo:hi]
-        dWg[e] = Xs[lo:hi].T @ dHg[lo:hi]
-        dWu[e] = Xs[lo:hi].T @ dHu[lo:hi]
+    dWg, dWu, dWd = weight_gradients(Xs, dHg, dHu, A, dYs, offsets, mx and mx_wgrad)
     dWg, dWu, dWd = wrnd(dWg), wrnd(dWu), wrnd(dWd)
     dx = np.zeros((T, d))
     for t in range(T):
@@ -460,7 +494,8 @@ def router_backward(x, Wr, logits, topk_idx, dw, dx_experts, prec: str = "fp64",
 
 def layer(x, Wr, Wg, Wu, Wd, k, dY, prec: str = "fp64", logits=None,
           topk_idx=None, topk_w=None, renorm: bool = False,
-          aux_coef: float = 0.0, wgrad_f32: bool = False) -> Dict[str, np.ndarray]:
+          aux_coef: float = 0.0, wgrad_f32: bool = False,
+          mx_wgrad: bool = False) -> Dict[str, np.ndarray]:
     """Whole layer forward + backward.
 
     With a router (Wr given): logits = x.Wr unless `logits` is passed in,
@@ -481,7 +516,7 @@ def layer(x, Wr, Wg, Wu, Wd, k, dY, prec: str = "fp64", logits=None,
     fwd = layer_forward(x, Wg, Wu, Wd, topk_idx, topk_w, prec)
     out.update(fwd)
     if dY is not None:
-        bwd = layer_backward(fwd, x, Wg, Wu, Wd, topk_idx, topk_w, dY, prec, wgrad_f32)
+        bwd = layer_backward(fwd, x, Wg, Wu, Wd, topk_idx, topk_w, dY, prec, wgrad_f32, mx_wgrad)
         out.update(bwd)
         if Wr is not None:
             rb = router_backward(x, Wr, logits, topk_idx, bwd["dw"], bwd["dx"], prec, renorm,
@@ -603,11 +638,12 @@ def layer_tokens(x, Wr, Wg, Wu, Wd, topk_idx, topk_w, dY, tokens, prec: str = "f
 
 
 def expert_columns(x, Wg, Wu, Wd, topk_idx, topk_w, dY, e: int, cols,
-                   prec: str = "fp64") -> Dict[str, np.ndarray]:
+                   prec: str = "fp64", mx_wgrad: bool = False) -> Dict[str, np.ndarray]:
     """Weight gradients of expert e at the given columns c of d_ff:
     dWg[e][:, cols], dWu[e][:, cols] and dWd[e][cols, :], each summed over all
     of e's rows exactly as layer_backward does (the column c of Hg, Hu, A, dA
-    depends only on column c of Wg, Wu and on row c of Wd)."""
+    depends only on column c of Wg, Wu and on row c of Wd; with mx_wgrad the
+    token-axis blocks of a column depend only on that column)."""
     rnd = _storage_round(prec)
     mx = prec == "mxfp8"
     E = np.shape(Wg)[0]
@@ -641,4 +677,6 @@ def expert_columns(x, Wg, Wu, Wd, topk_idx, topk_w, dY, e: int, cols,
     dA = g @ Wdb.T
     dHg = rnd(dA * Hu * dsilu(Hg))
     dHu = rnd(dA * silu(Hg))
+    if mx and mx_wgrad:
+        Xs, dHg, dHu, A, dYs = (mx_quantize_rows(t) for t in (Xs, dHg, dHu, A, dYs))
     return dict(dWg=rnd(Xs.T @ dHg), dWu=rnd(Xs.T @ dHu), dWd=rnd(A.T @ dYs))

@@ -598,3 +598,49 @@ def test_wgrad_f32_variant():
     e = O.layer(x, Wr, Wg, Wu, Wd, k, dY, "fp32", wgrad_f32=True)
     for n in ("dWg", "dWu", "dWd"):
         np.testing.assert_array_equal(c[n], e[n])
+
+
+def test_mx_weight_gradient_token_blocks():
+    """MXFP8 weight gradients block their operands along the tokens of each
+    expert: scaling one feature column of an operand by 2^16 scales exactly
+    the gradient entries it feeds (every token block of that column scales by
+    a power of two) and leaves every other entry bit-identical (blocked along
+    the features instead, the scaled column would share blocks with the
+    others and push them into e4m3's subnormals).  Blocks start at each
+    expert's first row: scaling all of expert 0's rows leaves expert 1's
+    gradients unchanged although expert 0 ends inside a 32-row block of the
+    whole tensor."""
+    S = 2.0 ** 16
+    rng = _rng(43)
+    R, d, f = 20 + 45, 48, 40
+    offsets = np.array([0, 20, 65])
+    Xs, A = rng.standard_normal((R, d)), rng.standard_normal((R, f))
+    dHg, dHu = rng.standard_normal((R, f)), rng.standard_normal((R, f))
+    dYs = rng.standard_normal((R, d))
+    base = O.weight_gradients(Xs, dHg, dHu, A, dYs, offsets, mx_tokens=True)
+    exact = O.weight_gradients(Xs, dHg, dHu, A, dYs, offsets, mx_tokens=False)
+    for b, x in zip(base, exact):
+        err = np.linalg.norm(b - x) / np.linalg.norm(x)
+        assert 1e-4 < err < 0.1, err        # quantised, within MX error
+
+    def check(args, changed):
+        got = O.weight_gradients(*args, offsets, mx_tokens=True)
+        for name, g, b in zip(("dWg", "dWu", "dWd"), got, base):
+            m = changed.get(name)
+            if m is None:
+                np.testing.assert_array_equal(g, b, err_msg=name)
+            else:
+                np.testing.assert_array_equal(g[m], b[m] * S, err_msg=name)
+                rest = np.ones(b.shape, bool); rest[m] = False
+                np.testing.assert_array_equal(g[rest], b[rest], err_msg=name)
+
+    X2 = Xs.copy(); X2[:, 5] *= S
+    check((X2, dHg, dHu, A, dYs), {"dWg": (slice(None), 5), "dWu": (slice(None), 5)})
+    G2 = dHg.copy(); G2[:, 7] *= S
+    check((Xs, G2, dHu, A, dYs), {"dWg": (slice(None), slice(None), 7)})
+    A2 = A.copy(); A2[:, 3] *= S
+    check((Xs, dHg, dHu, A2, dYs), {"dWd": (slice(None), 3)})
+    Y2 = dYs.copy(); Y2[:, 11] *= S
+    check((Xs, dHg, dHu, A, Y2), {"dWd": (slice(None), slice(None), 11)})
+    X3 = Xs.copy(); X3[:20] *= S
+    check((X3, dHg, dHu, A, dYs), {"dWg": (0,), "dWu": (0,)})
