@@ -74,6 +74,8 @@ _SYMBOLS = {
     "gemm_mx_kernel<9>": ["gemm_mx_fwd_down"],
     "gemm_mx_kernel<10>": ["gemm_mx_dgrad_down_swiglu_bwd"],
     "gemm_mx_kernel<11>": ["gemm_mx_dgrad_gateup"],
+    "gemm_mx_kernel<14>": ["gemm_mx_wgrad_gateup", "gemm_mx_wgrad_down"],
+    "gemm_mx_kernel<15>": ["gemm_mx_wgrad_gateup", "gemm_mx_wgrad_down"],
     "dispatch_copy_kernel": ["dispatch_copy"],
     "mx_dispatch_kernel": ["mx_dispatch_quant"],
     "combine_kernel": ["combine"],
@@ -187,7 +189,7 @@ def cpu_baseline(wl, inp, tokens: int):
     t0 = time.perf_counter()
     if wl.routing == "router":
         O.layer(inp["x"][:S], inp["Wr"], inp["Wg"], inp["Wu"], inp["Wd"], wl.k, inp["dY"][:S],
-                wl.prec)
+                wl.prec, mx_wgrad=wl.mx_wgrad)
     else:
         O.layer(inp["x"][:S], None, inp["Wg"], inp["Wu"], inp["Wd"], wl.k, inp["dY"][:S], wl.prec,
                 topk_idx=inp["topk_idx"][:S], topk_w=inp["topk_w"][:S])
@@ -260,7 +262,8 @@ def main(argv=None) -> int:
     kw = {}
     if not router:
         kw = dict(topk_idx=rgg.upload(inp["topk_idx"]), topk_w=rgg.upload(inp["topk_w"]))
-    layer = rgg.ExpertLayer(wl.T, wl.d, wl.E, wl.f, wl.k, dt, wl.prec, router=router)
+    layer = rgg.ExpertLayer(wl.T, wl.d, wl.E, wl.f, wl.k, dt, wl.prec, router=router,
+                            mx_wgrad=wl.mx_wgrad)
 
     def step():
         layer.forward(x, Wr, Wg, Wu, Wd, **kw)
@@ -348,7 +351,7 @@ def main(argv=None) -> int:
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02^2) weights)",
         "config": {"workload": wl.name, "T": wl.T, "d_model": wl.d, "experts": wl.E,
                    "d_ff": wl.f, "top_k": wl.k, "routed_rows": wl.R, "routing": wl.routing,
-                   "parallelism": "single GPU"},
+                   "mx_weight_gradients": wl.mx_wgrad, "parallelism": "single GPU"},
         "tflops": round(tflops, 2),
         "pct_peak": round(100.0 * tflops / peak, 2),
         "ffn_gemm_tflops": None if ffn_tflops is None else round(ffn_tflops, 2),

@@ -76,12 +76,15 @@ enum moe_prec { MOE_PREC_F32 = 0, MOE_PREC_BF16 = 1, MOE_PREC_MXFP8 = 2 };
 #define MOE_ACCUMULATE 0x2u        /* add into the output (dW*, dx, dWr) instead of overwriting */
 /* moe_grouped_ffn_bwd flag (bf16 layer): dWg, dWu, dWd are float32 buffers */
 #define MOE_WGRAD_F32 0x8u
+/* moe_grouped_ffn_bwd flag (MXFP8): the weight-gradient GEMMs in MXFP8 too */
+#define MOE_WGRAD_MX 0x10u
 
 /* Operation ids for moe_workspace_size. */
 enum moe_op {
   MOE_OP_ROUTE = 0, MOE_OP_DISPATCH = 1, MOE_OP_FFN_FWD = 2, MOE_OP_COMBINE = 3,
   MOE_OP_COMBINE_BWD = 4, MOE_OP_FFN_BWD = 5, MOE_OP_DISPATCH_BWD = 6, MOE_OP_ROUTE_BWD = 7,
-  MOE_OP_ROUTE_AUX = 8
+  MOE_OP_ROUTE_AUX = 8,
+  MOE_OP_FFN_BWD_MXW = 9   /* moe_grouped_ffn_bwd with MOE_WGRAD_MX */
 };
 
 /*
@@ -186,6 +189,13 @@ int moe_combine_bwd(const void* dY, const void* Ys, const float* topk_w,
  *   three weight gradients are float32 buffers, written, or with
  *   MOE_ACCUMULATE added to, without rounding to bf16 (a float32 layer's
  *   gradients are float32 anyway; the flag changes nothing there).
+ *   MOE_WGRAD_MX (prec MXFP8 only, else MOE_ERR_DTYPE; olmoforge README,
+ *   MXFP8 block quantisation, applied to the weight gradients as well): the
+ *   weight-gradient GEMMs run in MXFP8 too, each operand (Xs, dH, A, dYs)
+ *   block-quantised along the tokens of each expert in blocks of 32 from
+ *   the expert's first row (a last partial block padded with zeros); with
+ *   MOE_WGRAD_F32 the gradients are float32.  Workspace:
+ *   moe_workspace_size(MOE_OP_FFN_BWD_MXW, ...).
  *   Xs: the dispatched rows in dtype (also for MXFP8).  prec MXFP8: both
  *   operands of the two dgrad GEMMs are block-quantised along their
  *   contraction axis (dYs and Wd along d; dH, Wg, Wu along f); dYs_q /

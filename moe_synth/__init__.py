@@ -49,6 +49,7 @@ class Workload:
     empty_experts: Tuple[int, ...] = ()
     note: str = ""
     passes: str = "fwd+bwd"   # "fwd": inference-shaped, forward only
+    mx_wgrad: bool = False    # MXFP8 weight gradients as well (prec "mxfp8")
 
     @property
     def R(self) -> int:
@@ -98,6 +99,9 @@ WORKLOADS: Dict[str, Workload] = {
                             dtype="bf16", prec="mxfp8", routing="router"),
     "tiny_mxfp8": Workload("tiny_mxfp8", T=256, d=64, E=8, f=128, k=2,
                            dtype="bf16", prec="mxfp8", routing="router"),
+    "olmoe_mxfp8_wgrad": Workload("olmoe_mxfp8_wgrad", T=8192, d=2048, E=64, f=1024, k=8,
+                                  dtype="bf16", prec="mxfp8", routing="router", mx_wgrad=True,
+                                  note="every expert GEMM in MXFP8, weight gradients too"),
 }
 # Inference-shaped small batches of the OLMoE layer (token-by-token generation
 # and short prompts): forward only.

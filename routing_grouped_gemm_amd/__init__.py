@@ -36,8 +36,10 @@ MOE_ROUTE_LOGITS_IN = 0x1
 MOE_ACCUMULATE = 0x2
 MOE_ROUTE_RENORM = 0x4
 MOE_WGRAD_F32 = 0x8
+MOE_WGRAD_MX = 0x10
 OPS = {"route": 0, "dispatch": 1, "ffn_fwd": 2, "combine": 3, "combine_bwd": 4,
-       "ffn_bwd": 5, "dispatch_bwd": 6, "route_bwd": 7, "route_aux": 8}
+       "ffn_bwd": 5, "dispatch_bwd": 6, "route_bwd": 7, "route_aux": 8,
+       "ffn_bwd_mxw": 9}
 
 _P, _I, _U, _S = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint, ctypes.c_size_t
 _SIGS = {
@@ -194,12 +196,13 @@ def moe_combine_bwd(dY, Ys, topk_w, dest_row, dYs, dtopk_w, dYs_q=None, dYs_q_sc
 
 def moe_grouped_ffn_bwd(dYs, Xs, Hg, Hu, A, offsets, T, k, Wg, Wu, Wd, dH, dXs,
                         dWg, dWu, dWd, ws=None, prec="bf16", accumulate=False, dYs_q=None,
-                        dYs_q_scale=None, stream=None):
+                        dYs_q_scale=None, stream=None, mx_wgrad=False):
     E, d, f = Wg.shape
     wp, wb = _ws(ws)
     # float32 weight gradients of a bf16 layer select float32 accumulation
     flags = (MOE_ACCUMULATE if accumulate else 0) | \
-        (MOE_WGRAD_F32 if dWg.dtype == torch.float32 and Wg.dtype == torch.bfloat16 else 0)
+        (MOE_WGRAD_F32 if dWg.dtype == torch.float32 and Wg.dtype == torch.bfloat16 else 0) | \
+        (MOE_WGRAD_MX if mx_wgrad else 0)
     _check(lib().moe_grouped_ffn_bwd(_ptr(dYs), _ptr(dYs_q), _ptr(dYs_q_scale), _ptr(Xs),
                                      _ptr(Hg), _ptr(Hu), _ptr(A),
                                      _ptr(offsets), T, k, d, f, E, _ptr(Wg),
@@ -288,17 +291,19 @@ class ExpertLayer:
     gradient added to the router backward when aux_coef != 0.
     wgrad_f32=True keeps the expert weight gradients dWg, dWu, dWd in float32
     (float32 accumulation with backward(..., accumulate_wgrad=True)).
+    mx_wgrad=True (prec "mxfp8"): the weight-gradient GEMMs run in MXFP8 too.
     router=False: pre-routed rows (topk_idx / topk_w are inputs, no router
     backward).  All buffers are allocated once, on construction."""
 
     def __init__(self, T: int, d: int, E: int, f: int, k: int, dtype=torch.bfloat16,
                  prec: str = "bf16", router: bool = True, device="cuda", renorm: bool = False,
-                 aux_coef: float = 0.0, wgrad_f32: bool = False):
+                 aux_coef: float = 0.0, wgrad_f32: bool = False, mx_wgrad: bool = False):
         lib()
         self.T, self.d, self.E, self.f, self.k = T, d, E, f, k
         self.R = R = T * k
         self.dtype, self.prec, self.router = dtype, prec, router
         self.renorm, self.aux_coef = renorm, float(aux_coef)
+        self.mx_wgrad = bool(mx_wgrad)
         dev = torch.device(device)
         z = lambda *s, dt=dtype: torch.empty(*s, dtype=dt, device=dev)
         i32, f32 = torch.int32, torch.float32
@@ -338,7 +343,7 @@ class ExpertLayer:
         self.ws_route = ws("route")
         self.ws_dispatch = ws("dispatch")
         self.ws_fwd = ws("ffn_fwd")
-        self.ws_bwd = ws("ffn_bwd")
+        self.ws_bwd = ws("ffn_bwd_mxw" if self.mx_wgrad else "ffn_bwd")
         self.ws_route_bwd = ws("route_bwd")
         self.ws_route_aux = ws("route_aux")
 
@@ -372,7 +377,7 @@ class ExpertLayer:
         moe_grouped_ffn_bwd(self.dYs, self.Xs, self.Hg, self.Hu, self.A, self.offsets, self.T, self.k,
                             self.Wg, self.Wu, self.Wd, self.dH, self.dXs, self.dWg, self.dWu,
                             self.dWd, self.ws_bwd, self.prec, accumulate_wgrad, self.dYs_q,
-                            self.dYs_q_scale, stream)
+                            self.dYs_q_scale, stream, mx_wgrad=self.mx_wgrad)
         moe_dispatch_bwd(self.dXs, self.dest_row, self.dx, False, stream)
         if self.router:
             aux = self.aux_dp if self.aux_coef != 0.0 else None

@@ -170,6 +170,10 @@ int moe_workspace_size(int op, int T, int d, int E, int f, int k, int dtype, int
     case MOE_OP_ROUTE_AUX:
       *bytes = align_up((size_t)((T + 63) / 64) * E * sizeof(float));
       return MOE_OK;
+    case MOE_OP_FFN_BWD_MXW:
+      if (prec != MOE_PREC_MXFP8) return MOE_ERR_DTYPE;
+      *bytes = mx_wgrad_workspace(R, d, f, E);
+      return MOE_OK;
   }
   return MOE_ERR_SHAPE;
 }
@@ -339,6 +343,9 @@ int moe_grouped_ffn_bwd(const void* dYs, const void* dYs_q, const uint8_t* dYs_q
   clear_stale_error();
   const int acc = (flags & MOE_ACCUMULATE) ? 1 : 0;
   const int eng = gemm_engine(dtype);
+  const bool mxw = (flags & MOE_WGRAD_MX) != 0;
+  if (mxw && prec != MOE_PREC_MXFP8) return MOE_ERR_DTYPE;
+  if (mxw && ws_bytes < mx_wgrad_workspace(R, d, f, E)) return MOE_ERR_WORKSPACE;
   if (prec == MOE_PREC_MXFP8) {
     if (ws_bytes < mx_bwd_workspace(R, d, f, E)) return MOE_ERR_WORKSPACE;
     MOE_TRY(mx_ffn_dgrad(dYs_q, dYs_q_scale, Hg, Hu, offsets, (int)R, d, f, E, Wg, Wu, Wd, dH,
@@ -360,6 +367,10 @@ int moe_grouped_ffn_bwd(const void* dYs, const void* dYs_q, const uint8_t* dYs_q
     h.c0 = dXs; h.ldc = d;
     MOE_TRY(launch_grouped_gemm(GK_DGRAD_GATEUP, eng, h, num_cu(), st));
   }
+  if (mxw)
+    return status_of(mx_ffn_wgrad(Xs, dH, A, dYs, offsets, (int)R, d, f, E,
+                                  (flags & MOE_WGRAD_F32) ? 1 : 0, acc, dWg, dWu, dWd, ws,
+                                  num_cu(), st));
   // weight gradients: dWg|dWu = Xs^T . dH, dWd = A^T . dYs (ragged K = rows of e)
   const GemmKind wk =
       ((flags & MOE_WGRAD_F32) && dtype == MOE_BF16) ? GK_WGRAD_F32 : GK_WGRAD;

@@ -92,7 +92,11 @@ enum GemmKind : int {
   GK_MX_GATEUP = 8,       // Xq[R,d] . WguT[e][2f',d] (256-row panels: 128 gate rows, 128 up rows)
   GK_MX_DOWN = 9,         // Aq[R,f] . WdT[e][d,f]   -> Ys
   GK_MX_DGRAD_DOWN = 10,  // dYsq[R,d] . Wd[e][f,d]  -> dHg, dHu
-  GK_MX_DGRAD_GATEUP = 11 // dHq[R,2f] . Wgu[e][d,2f] -> dXs
+  GK_MX_DGRAD_GATEUP = 11, // dHq[R,2f] . Wgu[e][d,2f] -> dXs
+  // MXFP8 weight gradients: both operands transposed codes [rows][Kp] whose K
+  // axis is every expert's tokens, each expert's segment padded to 128
+  GK_MX_WGRAD = 14,       // P^T . Q over the expert's tokens -> dW[e] (bf16)
+  GK_MX_WGRAD_F32 = 15    // as GK_MX_WGRAD into float32 gradients
 };
 
 // Engines: float32 storage on the SIMT engine, bf16 on MFMA, and bf16 on the

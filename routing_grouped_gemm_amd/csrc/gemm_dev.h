@@ -72,6 +72,14 @@ template <> struct KT<GK_MX_DGRAD_GATEUP> {
   static constexpr bool AK = true, BK_ = true;
   static constexpr int BSP = BS_NONE, EPI = EPI_STORE;
 };
+template <> struct KT<GK_MX_WGRAD> {
+  static constexpr bool AK = true, BK_ = true;
+  static constexpr int BSP = BS_NONE, EPI = EPI_WGRAD_SPLIT;
+};
+template <> struct KT<GK_MX_WGRAD_F32> {
+  static constexpr bool AK = true, BK_ = true;
+  static constexpr int BSP = BS_NONE, EPI = EPI_WGRAD_SPLIT_F32;
+};
 
 // Kinds whose epilogue also writes the block-quantised output (MXFP8).
 template <int KIND>

@@ -10,6 +10,9 @@ namespace moe {
 
 size_t mx_fwd_workspace(long long R, int d, int f, int E);
 size_t mx_bwd_workspace(long long R, int d, int f, int E);
+// Backward workspace when the weight gradients are MXFP8 too (the dgrad
+// workspace, then the token-quantised operands).
+size_t mx_wgrad_workspace(long long R, int d, int f, int E);
 // Row pitch of block-major activation scales: R rounded up to 16.
 long mx_scale_pitch(long long R);
 
@@ -25,5 +28,12 @@ hipError_t mx_ffn_dgrad(const void* dYsq, const uint8_t* dYsq_scale, const void*
                         const void* Hu, const int32_t* offsets, int R, int d, int f, int E,
                         const void* Wg, const void* Wu, const void* Wd, void* dH, void* dXs,
                         void* ws, int num_cu, hipStream_t s);
+
+// Weight gradients in MXFP8: Xs, dH, A, dYs (bf16) quantised along each
+// expert's tokens; dW stored as bf16, or float32 with f32_out.
+hipError_t mx_ffn_wgrad(const void* Xs, const void* dH, const void* A, const void* dYs,
+                        const int32_t* offsets, int R, int d, int f, int E, int f32_out,
+                        int accumulate, void* dWg, void* dWu, void* dWd, void* ws, int num_cu,
+                        hipStream_t s);
 
 }  // namespace moe

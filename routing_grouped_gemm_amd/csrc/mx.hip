@@ -150,6 +150,101 @@ __global__ __launch_bounds__(256) void mx_quant_cols_kernel(
   (void)lane;
 }
 
+// Weight-gradient operands, quantised along the tokens of each expert.
+// poff[e] = sum over earlier experts of their row counts rounded up to 128:
+// each expert's token segment starts a 128-aligned column range of the
+// transposed codes (one GEMM stage holds 128 codes of a row).
+__global__ __launch_bounds__(64) void mx_pad_offsets_kernel(const int32_t* __restrict__ offsets,
+                                                            int E, int32_t* __restrict__ poff) {
+  const int lane = threadIdx.x;
+  int c[4], sum = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = lane * 4 + q;
+    c[q] = (e < E) ? (offsets[e + 1] - offsets[e] + 127) / 128 * 128 : 0;
+    sum += c[q];
+  }
+  int incl = sum;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += v;
+  }
+  int run = incl - sum;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = lane * 4 + q;
+    if (e <= E) poff[e] = run;
+    run += c[q];
+  }
+  if (lane == 63 && E == 256) poff[256] = incl;
+}
+
+// src[R][C] (bf16, rows grouped by expert) quantised along its rows in
+// blocks of 32 starting at each expert's first row and written transposed:
+// padded token p of expert e (p - poff[e] < its row count, else zero) is
+// column p of dst[C][dst_ld]; block p/32 of column c has its scale at
+// scale[(p/32) * C + c].  A workgroup stages 64 padded tokens x 64 columns
+// in LDS (a 64-token tile never straddles two experts' 128-aligned
+// segments); thread t then takes column t/4 and tokens 16*(t%4) .. +15, half
+// a 32-token block whose other half is in the neighbouring lane.
+__global__ __launch_bounds__(256) void mx_quant_tokens_kernel(
+    const bf16_t* __restrict__ src, int C, long src_ld, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ poff, int E, uint8_t* __restrict__ dst, long dst_ld,
+    uint8_t* __restrict__ scale) {
+  __shared__ __attribute__((aligned(16))) bf16_t tile[64][72];
+  __shared__ int po[257];
+  const int p0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const int t = threadIdx.x;
+  for (int e = t; e <= E; e += 256) po[e] = poff[e];
+  __syncthreads();
+  if (p0 >= po[E]) return;                 // past the last segment (uniform)
+  int lo = 0, hi = E;                      // the expert e with po[e] <= p0 < po[e+1]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (po[mid] <= p0) lo = mid; else hi = mid;
+  }
+  const int e = lo;
+  const int row0 = offsets[e], n = offsets[e + 1] - row0;
+  {
+    const int r = t >> 2, c = (t & 3) * 16;
+    const int pr = p0 + r - po[e];         // token inside the expert
+    uint4 a = make_uint4(0, 0, 0, 0), b = a;
+    if (pr < n) {
+      const bf16_t* sp = src + (long)(row0 + pr) * src_ld + c0 + c;
+      a = *reinterpret_cast<const uint4*>(sp);
+      b = *reinterpret_cast<const uint4*>(sp + 8);
+    }
+    *reinterpret_cast<uint4*>(&tile[r][c]) = a;
+    *reinterpret_cast<uint4*>(&tile[r][c + 8]) = b;
+  }
+  __syncthreads();
+  const int col = t >> 2, q = t & 3;
+  float v[16];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    v[i] = bf16_to_f32(tile[16 * q + i][col]);
+    amax = fmaxf(amax, fabsf(v[i]));
+  }
+  amax = fmaxf(amax, dpp_f<kDppQuad1032>(amax, amax));   // the partner lane (lane ^ 1)
+  const int E8 = mx_block_exponent(amax);
+  float sv[8];
+  uint32_t w[4];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sv[i] = ldexpf(v[8 * h + i], -E8);
+    uint32_t c2[2];
+    e4m3_codes8(sv, c2);
+    w[2 * h] = c2[0];
+    w[2 * h + 1] = c2[1];
+  }
+  *reinterpret_cast<uint4*>(dst + (long)(c0 + col) * dst_ld + p0 + 16 * q) =
+      make_uint4(w[0], w[1], w[2], w[3]);
+  if ((q & 1) == 0) scale[(long)((p0 >> 5) + (q >> 1)) * C + c0 + col] = (uint8_t)(E8 + 127);
+}
+
 // ---------------------------------------------------------------------------
 // MX grouped GEMM
 // ---------------------------------------------------------------------------
@@ -259,25 +354,48 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mx_kernel(GemmArgs g) {
   const uint8_t* A = static_cast<const uint8_t*>(g.a);
   const uint8_t* B = static_cast<const uint8_t*>(g.b0);
 
+  // RK (weight gradients): the K axis is the tokens; tile rows are M rows
+  // (features) of the transposed codes A[M][lda], columns N rows of B[N][ldb],
+  // and the expert's K segment starts at byte t.row0 of every row (scale
+  // block t.row0 / 32).  g.K is the padded token count.
+  constexpr bool RK = KIND == GK_MX_WGRAD || KIND == GK_MX_WGRAD_F32;
   auto plan = [&](const Tile& t, MxPlan& P) {
-    // rows of B for this tile: gate/up panels hold 256 rows per 128 f columns
-    const long brow0 = DUAL ? 2L * t.n0 : (long)t.n0;
-    const long brows = DUAL ? 2L * ((g.N + 127) / 128) * 128 : (long)g.N;
-    plan_km(P.a, A + (long)t.row0 * g.lda, ((long long)g.rows_total - t.row0) * g.lda, nullptr, 0,
-            1 << 30, g.lda, wave, lane);
-    plan_km(P.b, B + (long)t.e * g.b_es + brow0 * g.ldb, (brows - brow0) * g.ldb, nullptr, 0,
-            1 << 30, g.ldb, wave, lane);
     P.sblk = 2 * (wave & 1);
-    const int row_al = t.row0 & ~15;
-    P.amis = t.row0 - row_al;
-    if (wave < 2) {
-      P.srs = make_rsrc(g.sa, (long long)(g.K / 32) * g.sa_pitch);
-      P.svoff = (uint32_t)(row_al + lane * 16);
-      P.spitch = (uint32_t)g.sa_pitch;
+    if constexpr (RK) {
+      const long long abytes = (long long)g.M * g.lda, bbytes = (long long)g.N * g.ldb;
+      const long aoff = (long)t.m0 * g.lda + t.row0, boff = (long)t.n0 * g.ldb + t.row0;
+      plan_km(P.a, A + aoff, abytes - aoff, nullptr, 0, 1 << 30, g.lda, wave, lane);
+      plan_km(P.b, B + boff, bbytes - boff, nullptr, 0, 1 << 30, g.ldb, wave, lane);
+      P.amis = 0;
+      const int kb = t.row0 >> 5;
+      if (wave < 2) {
+        P.srs = make_rsrc(g.sa, (long long)(g.K / 32) * g.sa_pitch);
+        P.svoff = (uint32_t)((long)kb * g.sa_pitch + t.m0 + lane * 16);
+        P.spitch = (uint32_t)g.sa_pitch;
+      } else {
+        P.srs = make_rsrc(g.sb, (long long)(g.K / 32) * g.sb_pitch);
+        P.svoff = (uint32_t)((long)kb * g.sb_pitch + t.n0 + lane * 16);
+        P.spitch = (uint32_t)g.sb_pitch;
+      }
     } else {
-      P.srs = make_rsrc(g.sb + (long)t.e * g.sb_es, (long long)(g.K / 32) * g.sb_pitch);
-      P.svoff = (uint32_t)(brow0 + lane * 16);
-      P.spitch = (uint32_t)g.sb_pitch;
+      // rows of B for this tile: gate/up panels hold 256 rows per 128 f columns
+      const long brow0 = DUAL ? 2L * t.n0 : (long)t.n0;
+      const long brows = DUAL ? 2L * ((g.N + 127) / 128) * 128 : (long)g.N;
+      plan_km(P.a, A + (long)t.row0 * g.lda, ((long long)g.rows_total - t.row0) * g.lda, nullptr,
+              0, 1 << 30, g.lda, wave, lane);
+      plan_km(P.b, B + (long)t.e * g.b_es + brow0 * g.ldb, (brows - brow0) * g.ldb, nullptr, 0,
+              1 << 30, g.ldb, wave, lane);
+      const int row_al = t.row0 & ~15;
+      P.amis = t.row0 - row_al;
+      if (wave < 2) {
+        P.srs = make_rsrc(g.sa, (long long)(g.K / 32) * g.sa_pitch);
+        P.svoff = (uint32_t)(row_al + lane * 16);
+        P.spitch = (uint32_t)g.sa_pitch;
+      } else {
+        P.srs = make_rsrc(g.sb + (long)t.e * g.sb_es, (long long)(g.K / 32) * g.sb_pitch);
+        P.svoff = (uint32_t)(brow0 + lane * 16);
+        P.spitch = (uint32_t)g.sb_pitch;
+      }
     }
   };
   auto stage_base = [&](int s) { return lds0 + (s & 1) * MSTAGE; };
@@ -368,15 +486,22 @@ const char* mx_name(int kind) {
   }
   return "gemm_mx";
 }
+const char* mx_name(int kind, const GemmArgs& g) {
+  if (kind == GK_MX_WGRAD || kind == GK_MX_WGRAD_F32)
+    return g.c1 ? "gemm_mx_wgrad_gateup" : "gemm_mx_wgrad_down";
+  return mx_name(kind);
+}
 
 template <int KIND>
 hipError_t launch_mx_kind(const GemmArgs& g, int num_cu, hipStream_t s) {
   constexpr int BNT = (KT<KIND>::BSP == BS_DUAL_N) ? mf::BN / 2 : mf::BN;
-  const long ub = ((long)g.rows_total / mf::BM + ngroups(g)) * ((g.N + BNT - 1) / BNT);
+  const long ntn = (g.N + BNT - 1) / BNT;
+  const long ub = g.ragged == RAG_K ? (long)ngroups(g) * ((g.M + mf::BM - 1) / mf::BM) * ntn
+                                    : ((long)g.rows_total / mf::BM + ngroups(g)) * ntn;
   const int grid = (int)(ub < num_cu ? ub : (long)num_cu);
   if (grid <= 0) return hipSuccess;
   hipLaunchKernelGGL(mf::gemm_mx_kernel<KIND>, dim3(grid), dim3(mf::NTHR), 0, s, g);
-  note_launch(mx_name(KIND), s);
+  note_launch(mx_name(KIND, g), s);
   return hipGetLastError();
 }
 
@@ -440,6 +565,31 @@ FwdWs carve_fwd(void* ws, long long R, int d, int f, int E, size_t* total) {
   return w;
 }
 
+// Padded token count bound: every expert's segment rounded up to 128.
+inline long wgrad_kp(long long R, int E) { return (R + 127L * E + 127) / 128 * 128; }
+
+// Token-quantised weight-gradient operands (after the dgrad workspace):
+// padded offsets, the M-side codes [max(d,f)][Kp] and scales, the N-side codes
+// [max(2f,d)][Kp] and scales; reused by the gate/up and the down gradient.
+struct WgradWs {
+  int32_t* poff;
+  uint8_t *a, *a_s, *b, *b_s;
+};
+WgradWs carve_wgrad(void* ws, size_t skip, long long R, int d, int f, int E, size_t* total) {
+  Carve c{static_cast<char*>(ws)};
+  c.used = skip;
+  WgradWs w;
+  const long Kp = wgrad_kp(R, E);
+  const long Mx = d > f ? d : f, Nx = 2 * f > d ? 2 * f : d;
+  w.poff = c.take<int32_t>((size_t)(E + 1) * 4);
+  w.a = c.take<uint8_t>((size_t)Mx * Kp);
+  w.a_s = c.take<uint8_t>((size_t)(Kp / 32) * Mx);
+  w.b = c.take<uint8_t>((size_t)Nx * Kp);
+  w.b_s = c.take<uint8_t>((size_t)(Kp / 32) * Nx);
+  if (total) *total = c.used;
+  return w;
+}
+
 struct BwdWs {
   uint8_t *wd, *wd_s, *dhq, *dhq_s, *wgu, *wgu_s;
 };
@@ -464,6 +614,8 @@ hipError_t launch_grouped_gemm_mx(GemmKind kind, const GemmArgs& g, int num_cu, 
     case GK_MX_DOWN: return launch_mx_kind<GK_MX_DOWN>(g, num_cu, s);
     case GK_MX_DGRAD_DOWN: return launch_mx_kind<GK_MX_DGRAD_DOWN>(g, num_cu, s);
     case GK_MX_DGRAD_GATEUP: return launch_mx_kind<GK_MX_DGRAD_GATEUP>(g, num_cu, s);
+    case GK_MX_WGRAD: return launch_mx_kind<GK_MX_WGRAD>(g, num_cu, s);
+    case GK_MX_WGRAD_F32: return launch_mx_kind<GK_MX_WGRAD_F32>(g, num_cu, s);
     default: break;
   }
   return hipErrorInvalidValue;
@@ -480,6 +632,12 @@ size_t mx_fwd_workspace(long long R, int d, int f, int E) {
 size_t mx_bwd_workspace(long long R, int d, int f, int E) {
   size_t t = 0;
   carve_bwd(nullptr, R, d, f, E, &t);
+  return t;
+}
+
+size_t mx_wgrad_workspace(long long R, int d, int f, int E) {
+  size_t t = 0;
+  carve_wgrad(nullptr, mx_bwd_workspace(R, d, f, E), R, d, f, E, &t);
   return t;
 }
 
@@ -552,6 +710,51 @@ hipError_t mx_ffn_dgrad(const void* dYsq, const uint8_t* dYsq_scale, const void*
   h.sb = w.wgu_s; h.sb_es = (long)(2 * f / 32) * d; h.sb_pitch = d;
   h.c0 = dXs; h.ldc = d;
   return launch_grouped_gemm_mx(GK_MX_DGRAD_GATEUP, h, num_cu, s);
+}
+
+namespace {
+hipError_t quant_tokens(const void* src, int C, long src_ld, const int32_t* offsets,
+                        const int32_t* poff, int E, long Kp, uint8_t* dst, uint8_t* scale,
+                        hipStream_t s) {
+  hipLaunchKernelGGL(mx_quant_tokens_kernel, dim3(C / 64, (unsigned)(Kp / 64)), dim3(256), 0, s,
+                     static_cast<const bf16_t*>(src), C, src_ld, offsets, poff, E, dst, Kp, scale);
+  note_launch("mx_quant_tokens", s);
+  return hipGetLastError();
+}
+}  // namespace
+
+hipError_t mx_ffn_wgrad(const void* Xs, const void* dH, const void* A, const void* dYs,
+                        const int32_t* offsets, int R, int d, int f, int E, int f32_out,
+                        int accumulate, void* dWg, void* dWu, void* dWd, void* ws, int num_cu,
+                        hipStream_t s) {
+  const WgradWs w = carve_wgrad(ws, mx_bwd_workspace(R, d, f, E), R, d, f, E, nullptr);
+  const long Kp = wgrad_kp(R, E);
+  hipLaunchKernelGGL(mx_pad_offsets_kernel, dim3(1), dim3(64), 0, s, offsets, E, w.poff);
+  note_launch("mx_pad_offsets", s);
+  MX_TRY(hipGetLastError());
+  const GemmKind kind = f32_out ? GK_MX_WGRAD_F32 : GK_MX_WGRAD;
+  // dWg | dWu = Xs^T . dH: Xs along its tokens -> a [d][Kp], dH -> b [2f][Kp]
+  MX_TRY(quant_tokens(Xs, d, d, offsets, w.poff, E, Kp, w.a, w.a_s, s));
+  MX_TRY(quant_tokens(dH, 2 * f, 2L * f, offsets, w.poff, E, Kp, w.b, w.b_s, s));
+  GemmArgs g{};
+  g.E = E; g.offsets = w.poff; g.rows_total = (int)Kp; g.ragged = RAG_K;
+  g.M = d; g.N = 2 * f; g.K = (int)Kp;
+  g.a = w.a; g.lda = Kp; g.sa = w.a_s; g.sa_pitch = d;
+  g.b0 = w.b; g.ldb = Kp; g.sb = w.b_s; g.sb_pitch = 2 * f;
+  g.c0 = dWg; g.c1 = dWu; g.ldc = f; g.c_es = (long)d * f; g.c_split = f;
+  g.accumulate = accumulate;
+  MX_TRY(launch_grouped_gemm_mx(kind, g, num_cu, s));
+  // dWd = A^T . dYs: A -> a [f][Kp], dYs -> b [d][Kp]
+  MX_TRY(quant_tokens(A, f, f, offsets, w.poff, E, Kp, w.a, w.a_s, s));
+  MX_TRY(quant_tokens(dYs, d, d, offsets, w.poff, E, Kp, w.b, w.b_s, s));
+  GemmArgs h{};
+  h.E = E; h.offsets = w.poff; h.rows_total = (int)Kp; h.ragged = RAG_K;
+  h.M = f; h.N = d; h.K = (int)Kp;
+  h.a = w.a; h.lda = Kp; h.sa = w.a_s; h.sa_pitch = f;
+  h.b0 = w.b; h.ldb = Kp; h.sb = w.b_s; h.sb_pitch = d;
+  h.c0 = dWd; h.ldc = d; h.c_es = (long)f * d; h.c_split = d;
+  h.accumulate = accumulate;
+  return launch_grouped_gemm_mx(kind, h, num_cu, s);
 }
 
 }  // namespace moe

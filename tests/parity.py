@@ -44,7 +44,7 @@ def relerr(gpu: np.ndarray, ref: np.ndarray) -> float:
 
 def run_gpu(wl: Workload, inp: Dict[str, np.ndarray], logits: Optional[np.ndarray] = None,
             renorm: bool = False, aux_coef: float = 0.0, wgrad_f32: bool = False,
-            wgrad_init: Optional[float] = None):
+            wgrad_init: Optional[float] = None, mx_wgrad: bool = False):
     """Forward + backward of the layer on the GPU; returns every buffer as numpy.
     wgrad_init: fill the weight-gradient buffers with this value and
     accumulate into them."""
@@ -52,7 +52,8 @@ def run_gpu(wl: Workload, inp: Dict[str, np.ndarray], logits: Optional[np.ndarra
     dt = torch.float32 if wl.dtype == "fp32" else torch.bfloat16
     router = wl.routing == "router"
     layer = rgg.ExpertLayer(wl.T, wl.d, wl.E, wl.f, wl.k, dt, wl.prec, router=router,
-                            renorm=renorm, aux_coef=aux_coef, wgrad_f32=wgrad_f32)
+                            renorm=renorm, aux_coef=aux_coef, wgrad_f32=wgrad_f32,
+                            mx_wgrad=mx_wgrad)
     x = dev_tensor(inp, "x", dt)
     Wg, Wu, Wd = (dev_tensor(inp, n, dt) for n in ("Wg", "Wu", "Wd"))
     Wr = dev_tensor(inp, "Wr", dt) if router else None
@@ -84,13 +85,16 @@ def run_gpu(wl: Workload, inp: Dict[str, np.ndarray], logits: Optional[np.ndarra
 
 
 def run_oracle(wl: Workload, inp: Dict[str, np.ndarray], logits: Optional[np.ndarray] = None,
-               renorm: bool = False, aux_coef: float = 0.0, wgrad_f32: bool = False):
+               renorm: bool = False, aux_coef: float = 0.0, wgrad_f32: bool = False,
+               mx_wgrad: bool = False):
     prec = wl.prec
     if wl.routing == "router":
         return O.layer(inp["x"], inp["Wr"], inp["Wg"], inp["Wu"], inp["Wd"], wl.k, inp["dY"], prec,
-                       logits=logits, renorm=renorm, aux_coef=aux_coef, wgrad_f32=wgrad_f32)
+                       logits=logits, renorm=renorm, aux_coef=aux_coef, wgrad_f32=wgrad_f32,
+                       mx_wgrad=mx_wgrad)
     return O.layer(inp["x"], None, inp["Wg"], inp["Wu"], inp["Wd"], wl.k, inp["dY"], prec,
-                   topk_idx=inp["topk_idx"], topk_w=inp["topk_w"], wgrad_f32=wgrad_f32)
+                   topk_idx=inp["topk_idx"], topk_w=inp["topk_w"], wgrad_f32=wgrad_f32,
+                   mx_wgrad=mx_wgrad)
 
 
 EXACT = ("topk_idx", "counts", "offsets", "dest_row", "src_token")

@@ -106,6 +106,13 @@ def test_workspace_sizes(L):
     s, n = ws_size(L, 5, T, d, E, f, k, BF16, P_MX)
     assert s == OK and 3 * E * d * f * 33 // 32 + R * 2 * f * 33 // 32 <= n  # weights + dH codes
     assert ws_size(L, 2, T, d, E, f, k, F32, P_MX)[0] == DTYPE
+    # MXFP8 weight gradients: the dgrad workspace, then the padded offsets and
+    # the token-quantised operands (codes [max(d,f)][Kp], [max(2f,d)][Kp] with
+    # Kp = R + 127 E rounded up to 128, one scale byte per 32 codes)
+    s, n = ws_size(L, 9, T, d, E, f, k, BF16, P_MX)
+    Kp = (R + 127 * E + 127) // 128 * 128
+    assert s == OK and n >= ws_size(L, 5, T, d, E, f, k, BF16, P_MX)[1] + 2 * 2048 * Kp * 33 // 32
+    assert ws_size(L, 9, T, d, E, f, k, BF16, P_BF16)[0] == DTYPE
 
 
 def route(L, x=A, Wr=A, T=16, d=64, E=8, k=2, dt=BF16, flags=0, lg=A, idx=A, w=A):
@@ -162,6 +169,15 @@ def test_ffn_fwd_validation(L):
 def ffn_bwd(L, Xs=A, dt=BF16, prec=P_BF16, f=64, dH=A, ws=A, dq=A, dqs=A):
     return L.moe_grouped_ffn_bwd(A, dq, dqs, Xs, A, A, A, A, 16, 2, 64, f, 8, A, A, A, dt, prec,
                                  0, dH, A, A, A, A, ws, 1 << 20, None)
+
+
+def test_ffn_bwd_mx_weight_gradient_flag(L):
+    # MOE_WGRAD_MX needs the MXFP8 precision and its larger workspace
+    f = L.moe_grouped_ffn_bwd
+    args = lambda prec, flags, wsb: (A, A, A, A, A, A, A, A, 16, 2, 64, 64, 8, A, A, A, BF16, prec,
+                                     flags, A, A, A, A, A, A, wsb, None)
+    assert f(*args(P_BF16, 0x10, 1 << 30)) == DTYPE
+    assert f(*args(P_MX, 0x10, 4096)) == WS
 
 
 def test_ffn_bwd_validation(L):
