@@ -642,7 +642,7 @@ __device__ __forceinline__ void epi8(const GemmArgs& g, const Tile& t, long row,
                                      const float (&v)[8], const float (&u)[8]) {
   if constexpr (EPI == EPI_STORE_F32) {
     float* p = static_cast<float*>(g.c0) + (g.ragged == RAG_M ? 0 : (long)t.e * g.c_es) + row * g.ldc + n;
-    store8(p, v);
+    store8_nt(p, v);
   } else if constexpr (EPI == EPI_STORE || EPI == EPI_WGRAD_SPLIT) {
     bf16_t* p;
     if constexpr (EPI == EPI_WGRAD_SPLIT) {
@@ -658,9 +658,9 @@ __device__ __forceinline__ void epi8(const GemmArgs& g, const Tile& t, long row,
       load8(p, o);
 #pragma unroll
       for (int q = 0; q < 8; ++q) w[q] = v[q] + o[q];
-      store8(p, w);
+      store8_nt(p, w);
     } else {
-      store8(p, v);
+      store8_nt(p, v);
     }
   } else if constexpr (EPI == EPI_WGRAD_SPLIT_F32) {
     float* p;
@@ -673,18 +673,18 @@ __device__ __forceinline__ void epi8(const GemmArgs& g, const Tile& t, long row,
       const float4 o1 = *reinterpret_cast<const float4*>(p + 4);
       const float w[8] = {v[0] + o0.x, v[1] + o0.y, v[2] + o0.z, v[3] + o0.w,
                           v[4] + o1.x, v[5] + o1.y, v[6] + o1.z, v[7] + o1.w};
-      store8(p, w);
+      store8_nt(p, w);
     } else {
-      store8(p, v);
+      store8_nt(p, v);
     }
   } else if constexpr (EPI == EPI_SWIGLU_FWD) {
     const long off = row * g.ldc + n;
     float a[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) a[q] = silu_f(v[q]) * u[q];
-    store8(static_cast<bf16_t*>(g.c0) + off, v);
-    store8(static_cast<bf16_t*>(g.c1) + off, u);
-    store8(static_cast<bf16_t*>(g.c2) + off, a);
+    store8_nt(static_cast<bf16_t*>(g.c0) + off, v);
+    store8_nt(static_cast<bf16_t*>(g.c1) + off, u);
+    store8_nt(static_cast<bf16_t*>(g.c2) + off, a);
   } else if constexpr (EPI == EPI_SWIGLU_BWD) {
     float hg[8], hu[8], dg[8], du[8];
     load8(static_cast<const bf16_t*>(g.h0) + row * g.ldh + n, hg);
@@ -696,8 +696,8 @@ __device__ __forceinline__ void epi8(const GemmArgs& g, const Tile& t, long row,
       dg[q] = v[q] * hu[q] * sg * (1.0f + hg[q] * (1.0f - sg));
     }
     bf16_t* p = static_cast<bf16_t*>(g.c0) + row * g.ldc + n;
-    store8(p, dg);
-    store8(p + g.c_split, du);
+    store8_nt(p, dg);
+    store8_nt(p + g.c_split, du);
   }
 }
 
@@ -761,9 +761,9 @@ __device__ __forceinline__ void epilogue_block(const GemmArgs& g, const Tile& t,
           for (int q = 0; q < 8; ++q) a[q] = silu_f(v[q]) * u[q];
           const long row = (long)t.row0 + m;
           const long off = row * g.ldc + n;
-          store8(static_cast<bf16_t*>(g.c0) + off, v);
-          store8(static_cast<bf16_t*>(g.c1) + off, u);
-          store8(static_cast<bf16_t*>(g.c2) + off, a);
+          store8_nt(static_cast<bf16_t*>(g.c0) + off, v);
+          store8_nt(static_cast<bf16_t*>(g.c1) + off, u);
+          store8_nt(static_cast<bf16_t*>(g.c2) + off, a);
           if constexpr (qout_of<KIND>()) {
             float ar[8];
             round_bf16_8(a, ar);
@@ -796,8 +796,8 @@ __device__ __forceinline__ void epilogue_block(const GemmArgs& g, const Tile& t,
           }
           const long row = (long)t.row0 + m;
           bf16_t* p = static_cast<bf16_t*>(g.c0) + row * g.ldc + n;
-          store8(p, dg);
-          store8(p + g.c_split, du);
+          store8_nt(p, dg);
+          store8_nt(p + g.c_split, du);
           if constexpr (qout_of<KIND>()) {
             float r[8];
             round_bf16_8(dg, r);

@@ -79,6 +79,19 @@ __device__ __forceinline__ void store8(bf16_t* p, const float (&v)[8]) {
   u.w = pack_bf16x2(v[6], v[7]);
   *reinterpret_cast<uint4*>(p) = u;
 }
+// Streaming (non-temporal) 16-byte stores of 8 values, for the GEMM
+// epilogues: measured ~1% faster there than plain stores.
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
+__device__ __forceinline__ void store8_nt(bf16_t* p, const float (&v)[8]) {
+  const u32x4_t w = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                     pack_bf16x2(v[6], v[7])};
+  __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t*>(p));
+}
+__device__ __forceinline__ void store8_nt(float* p, const float (&v)[8]) {
+  const f32x4_t a = {v[0], v[1], v[2], v[3]}, b = {v[4], v[5], v[6], v[7]};
+  __builtin_nontemporal_store(a, reinterpret_cast<f32x4_t*>(p));
+  __builtin_nontemporal_store(b, reinterpret_cast<f32x4_t*>(p + 4));
+}
 __device__ __forceinline__ void store8(float* p, const float (&v)[8]) {
   *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
   *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
