@@ -444,6 +444,22 @@ def test_mx_layer_block_axes():
     for key in ("dHg", "dHu"):
         np.testing.assert_array_equal(r[key][rows0, 9], base[key][rows0, 9] * S)
         np.testing.assert_array_equal(np.delete(r[key], 9, 1), np.delete(base[key], 9, 1))
+    # gate/up dgrad: Wg[e], Wu[e] rows blocked along f (the forward kept fixed,
+    # so only the backward sees the scaled weights)
+    fwd = O.layer_forward(x, Wg, Wu, Wd, idx, w, "mxfp8")
+    b0 = O.layer_backward(fwd, x, Wg, Wu, Wd, idx, w, dY, "mxfp8")
+    Wg4, Wu4 = Wg.copy(), Wu.copy()
+    Wg4[0][11, :] *= S; Wu4[0][11, :] *= S
+    r = O.layer_backward(fwd, x, Wg4, Wu4, Wd, idx, w, dY, "mxfp8")
+    np.testing.assert_array_equal(r["dXs"][rows0, 11], b0["dXs"][rows0, 11] * S)
+    np.testing.assert_array_equal(np.delete(r["dXs"], 11, 1), np.delete(b0["dXs"], 11, 1))
+    # gate/up dgrad: dH rows blocked along 2f (one token's upstream gradient
+    # scaled: its dYs row, dA row, dHg and dHu rows scale; only its dXs row follows)
+    dY5 = dY.copy(); dY5[6] *= S
+    r = O.layer_backward(fwd, x, Wg, Wu, Wd, idx, w, dY5, "mxfp8")
+    r6 = fwd["dest_row"][6, 0]
+    np.testing.assert_array_equal(r["dXs"][r6], b0["dXs"][r6] * S)
+    np.testing.assert_array_equal(np.delete(r["dXs"], r6, 0), np.delete(b0["dXs"], r6, 0))
 
 
 # ---------------------------------------------------------------------------
