@@ -4,6 +4,8 @@
 // mx.hip only.
 #pragma once
 
+#include <type_traits>
+
 #include "gemm.h"
 #include "moe_common.h"
 #include "mx_codec.h"
@@ -701,6 +703,19 @@ __device__ __forceinline__ void epi8(const GemmArgs& g, const Tile& t, long row,
   }
 }
 
+// Output element (row, n) of a plain bf16 store or of a split weight-gradient
+// store (bf16 or float).
+template <int EPI>
+__device__ __forceinline__ auto epi_ptr(const GemmArgs& g, const Tile& t, long row, int n) {
+  using T = std::conditional_t<EPI == EPI_WGRAD_SPLIT_F32, float, bf16_t>;
+  if constexpr (EPI == EPI_WGRAD_SPLIT || EPI == EPI_WGRAD_SPLIT_F32) {
+    if (n < g.c_split) return static_cast<T*>(g.c0) + (long)t.e * g.c_es + row * g.ldc + n;
+    return static_cast<T*>(g.c1) + (long)t.e * g.c_es + row * g.ldc + (n - g.c_split);
+  } else {
+    return static_cast<T*>(g.c0) + (g.ragged == RAG_M ? 0 : (long)t.e * g.c_es) + row * g.ldc + n;
+  }
+}
+
 // One 32-row block (I) of a wave's epilogue; a separate instantiation per
 // block keeps every accumulator index static, so the accumulators stay in
 // registers however large the block's code gets.
@@ -713,6 +728,30 @@ __device__ __forceinline__ void epilogue_block(const GemmArgs& g, const Tile& t,
     // keep each block's loads inside its own pass (registers)
     __builtin_amdgcn_sched_barrier(0);
     uint4 hg[8], hu[8];
+    // Stores that add to the output (router dx, accumulated gradients): the
+    // old values of the block's rows are loaded here, so that their latency
+    // overlaps the staging instead of serialising the store loop (bf16: hg,
+    // float: hg then hu).
+    constexpr bool PRE_ACC =
+        EPI == EPI_STORE || EPI == EPI_WGRAD_SPLIT || EPI == EPI_WGRAD_SPLIT_F32;
+    const bool pre_acc = PRE_ACC && g.accumulate;
+    if constexpr (PRE_ACC) {
+      if (pre_acc) {
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
+          const int m = wm * 128 + I * 32 + it * 4 + (lane >> 4);
+          const int n = t.n0 + wn * 128 + (lane & 15) * 8;
+          hg[it] = make_uint4(0, 0, 0, 0);
+          hu[it] = make_uint4(0, 0, 0, 0);
+          if (m < t.mlim && n < g.N) {
+            const long row = (g.ragged == RAG_M) ? (long)t.row0 + m : (long)t.m0 + m;
+            const uint4* p = reinterpret_cast<const uint4*>(epi_ptr<EPI>(g, t, row, n));
+            hg[it] = p[0];
+            if constexpr (EPI == EPI_WGRAD_SPLIT_F32) hu[it] = p[1];
+          }
+        }
+      }
+    }
     if constexpr (EPI == EPI_SWIGLU_BWD) {
 #pragma unroll
       for (int it = 0; it < 8; ++it) {
@@ -806,6 +845,31 @@ __device__ __forceinline__ void epilogue_block(const GemmArgs& g, const Tile& t,
             quant8_store(r, g.q0 + row * g.ldc + g.c_split + n,
                          g.qs + ((g.c_split + n) >> 5) * g.qs_pitch + row, lane);
           }
+        }
+      }
+    } else if (pre_acc) {
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const int r = it * 4 + (lane >> 4);
+        const int c = (lane & 15) * 8;
+        const int m = wm * 128 + I * 32 + r;
+        const f32x4_t a0 = *reinterpret_cast<const f32x4_t*>(slice + stage_off(r, c >> 2));
+        const f32x4_t a1 = *reinterpret_cast<const f32x4_t*>(slice + stage_off(r, (c >> 2) + 1));
+        const int n = t.n0 + wn * 128 + c;
+        if (m < t.mlim && n < g.N) {
+          float o[8], v[8];
+          if constexpr (EPI == EPI_WGRAD_SPLIT_F32) {
+            const uint32_t* a = reinterpret_cast<const uint32_t*>(&hg[it]);
+            const uint32_t* b = reinterpret_cast<const uint32_t*>(&hu[it]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) { o[q] = __uint_as_float(a[q]); o[q + 4] = __uint_as_float(b[q]); }
+          } else {
+            unpack8(hg[it], o);
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) { v[q] = a0[q] + o[q]; v[q + 4] = a1[q] + o[q + 4]; }
+          const long row = (g.ragged == RAG_M) ? (long)t.row0 + m : (long)t.m0 + m;
+          store8_nt(epi_ptr<EPI>(g, t, row, n), v);
         }
       }
     } else {
