@@ -237,7 +237,7 @@ int moe_dispatch(const void* x, const int32_t* topk_idx, int T, int d, int E, in
                                src_token, st));
   const int R = T * k;
   if (mx) return status_of(launch_mx_dispatch_copy(x, src_token, R, T, d, Xs, Xq, Xq_scale, st));
-  return status_of(launch_dispatch_copy(dtype, x, src_token, R, T, d, Xs, st));
+  return status_of(launch_dispatch_copy(dtype, x, dest_row, T, d, k, Xs, st));
 }
 
 int moe_grouped_ffn_fwd(const void* Xs, const uint8_t* Xs_scale, const int32_t* offsets, int T,

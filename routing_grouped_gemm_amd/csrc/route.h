@@ -35,8 +35,9 @@ hipError_t launch_topk_softmax(const float* logits, int T, int E, int k, int ren
 hipError_t launch_dispatch_meta(const int32_t* idx, int T, int E, int k, int32_t* hist,
                                 int32_t* base, int32_t* counts, int32_t* offsets,
                                 int32_t* dest_row, int32_t* src_token, hipStream_t s);
-hipError_t launch_dispatch_copy(int dtype, const void* x, const int32_t* src_token, int R, int T,
-                                int d, void* Xs, hipStream_t s);
+// Xs[dest_row[t,j]] = x[t].
+hipError_t launch_dispatch_copy(int dtype, const void* x, const int32_t* dest_row, int T, int d,
+                                int k, void* Xs, hipStream_t s);
 hipError_t launch_combine(int dtype, const void* Ys, const float* w, const int32_t* dest, int T,
                           int d, int k, void* y, hipStream_t s);
 // dYs_q / dYs_q_scale (optional, bf16 only): the stored dYs rows block-quantised

@@ -150,55 +150,157 @@ __global__ __launch_bounds__(64) void rank_kernel(const int32_t* __restrict__ id
 // row copies
 // ---------------------------------------------------------------------------
 // Xs[r] = x[src_token[r]]: one wave per row, 8 elements per lane per step.
+// ---------------------------------------------------------------------------
+// row kernels: one wave per token.  A pass covers kPassCols columns, each lane
+// kPassChunks chunks of 8 consecutive elements 512 columns apart.  A lane
+// whose chunk lies past the row end reads the row's last chunk instead (in
+// bounds, result discarded), so that every load of a pass is issued without
+// a branch and the loads of two rows are in flight together.
+// ---------------------------------------------------------------------------
+constexpr int kPassChunks = 4;
+constexpr int kPassCols = kPassChunks * 512;
+
+__device__ __forceinline__ int clamp_row(int r, int R) { return min(max(r, 0), R - 1); }
+__device__ __forceinline__ int chunk_col(int c0, int u, int d) { return min(c0 + 512 * u, d - 8); }
+
+// 8 raw elements (one or two 16-byte words).
 template <typename TS>
-__global__ __launch_bounds__(256) void dispatch_copy_kernel(const TS* __restrict__ x,
-                                                            const int32_t* __restrict__ src_token,
-                                                            int R, int T, int d,
-                                                            TS* __restrict__ Xs) {
+struct Raw8 {
+  uint4 w[sizeof(TS) / 2];
+  __device__ __forceinline__ void load(const TS* p) {
+#pragma unroll
+    for (int i = 0; i < (int)(sizeof(TS) / 2); ++i) w[i] = reinterpret_cast<const uint4*>(p)[i];
+  }
+  __device__ __forceinline__ void store(TS* p) const {
+#pragma unroll
+    for (int i = 0; i < (int)(sizeof(TS) / 2); ++i) reinterpret_cast<uint4*>(p)[i] = w[i];
+  }
+};
+
+// Xs[dest_row[t,j]] = x[t] for every slot j: each token row is read once and
+// written k times.  Rows of Xs that no slot names are left as they are (the
+// rank kernel makes dest_row a permutation of [0, T*k)).
+template <typename TS>
+__global__ __launch_bounds__(256) void dispatch_scatter_kernel(const TS* __restrict__ x,
+                                                               const int32_t* __restrict__ dest_row,
+                                                               int T, int d, int k,
+                                                               TS* __restrict__ Xs) {
   const int lane = threadIdx.x & 63;
-  const long r = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (r >= R) return;
-  int t = src_token[r];
-  t = min(max(t, 0), T - 1);
-  const TS* src = x + (long)t * d;
-  TS* dst = Xs + r * d;
-  for (int c = lane * 8; c < d; c += 64 * 8) {
-    if constexpr (sizeof(TS) == 2)
-      *reinterpret_cast<uint4*>(dst + c) = *reinterpret_cast<const uint4*>(src + c);
-    else {
-      *reinterpret_cast<float4*>(dst + c) = *reinterpret_cast<const float4*>(src + c);
-      *reinterpret_cast<float4*>(dst + c + 4) = *reinterpret_cast<const float4*>(src + c + 4);
+  const long t = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int R = T * k;
+  for (int c0 = lane * 8; c0 < d; c0 += kPassCols) {
+    Raw8<TS> v[kPassChunks];
+#pragma unroll
+    for (int u = 0; u < kPassChunks; ++u) v[u].load(x + t * d + chunk_col(c0, u, d));
+    for (int j = 0; j < k; ++j) {
+      const int r = dest_row[t * k + j];
+      if (r < 0 || r >= R) continue;
+#pragma unroll
+      for (int u = 0; u < kPassChunks; ++u)
+        if (c0 + 512 * u < d) v[u].store(Xs + (long)r * d + c0 + 512 * u);
     }
   }
 }
 
-__device__ __forceinline__ int clamp_row(int r, int R) { return min(max(r, 0), R - 1); }
+// y[t] = sum_j w[t,j] Ys[dest_row[t,j]], in float32 in slot order.
+// dXs gather (W == false): dx[t] (+)= sum_j dXs[dest_row[t,j]].
+template <typename TS, bool W>
+__device__ __forceinline__ void gather_rows(const TS* __restrict__ src, const float* __restrict__ w,
+                                            const int32_t* __restrict__ dest_row, long t, int T,
+                                            int d, int k, int accumulate, TS* __restrict__ out,
+                                            int lane) {
+  const int R = T * k;
+  const int32_t* dr = dest_row + t * k;
+  for (int c0 = lane * 8; c0 < d; c0 += kPassCols) {
+    float acc[kPassChunks][8];
+#pragma unroll
+    for (int u = 0; u < kPassChunks; ++u)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[u][q] = 0.0f;
+    auto add = [&](const float (&v)[kPassChunks][8], float wj) {
+#pragma unroll
+      for (int u = 0; u < kPassChunks; ++u)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[u][q] = W ? fmaf(wj, v[u][q], acc[u][q]) : acc[u][q] + v[u][q];
+    };
+    int j = 0;
+    for (; j + 2 <= k; j += 2) {
+      const TS* p0 = src + (long)clamp_row(dr[j], R) * d;
+      const TS* p1 = src + (long)clamp_row(dr[j + 1], R) * d;
+      float v0[kPassChunks][8], v1[kPassChunks][8];
+#pragma unroll
+      for (int u = 0; u < kPassChunks; ++u) load8(p0 + chunk_col(c0, u, d), v0[u]);
+#pragma unroll
+      for (int u = 0; u < kPassChunks; ++u) load8(p1 + chunk_col(c0, u, d), v1[u]);
+      add(v0, W ? w[t * k + j] : 1.0f);
+      add(v1, W ? w[t * k + j + 1] : 1.0f);
+    }
+    if (j < k) {
+      const TS* p0 = src + (long)clamp_row(dr[j], R) * d;
+      float v0[kPassChunks][8];
+#pragma unroll
+      for (int u = 0; u < kPassChunks; ++u) load8(p0 + chunk_col(c0, u, d), v0[u]);
+      add(v0, W ? w[t * k + j] : 1.0f);
+    }
+#pragma unroll
+    for (int u = 0; u < kPassChunks; ++u) {
+      const int c = c0 + 512 * u;
+      if (c < d) {
+        if (accumulate) {
+          float o[8];
+          load8(out + t * d + c, o);
+#pragma unroll
+          for (int q = 0; q < 8; ++q) acc[u][q] += o[q];
+        }
+        store8(out + t * d + c, acc[u]);
+      }
+    }
+  }
+}
 
-// y[t] = sum_j w[t,j] Ys[dest_row[t,j]]
 template <typename TS>
 __global__ __launch_bounds__(256) void combine_kernel(const TS* __restrict__ Ys,
                                                       const float* __restrict__ w,
                                                       const int32_t* __restrict__ dest_row, int T,
                                                       int d, int k, TS* __restrict__ y) {
-  const int lane = threadIdx.x & 63;
   const long t = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  const int R = T * k;
-  for (int c = lane * 8; c < d; c += 64 * 8) {
-    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int j = 0; j < k; ++j) {
-      const int r = clamp_row(dest_row[t * k + j], R);
-      const float wj = w[t * k + j];
-      float v[8];
-      load8(Ys + (long)r * d + c, v);
+  gather_rows<TS, true>(Ys, w, dest_row, t, T, d, k, 0, y, threadIdx.x & 63);
+}
+
+template <typename TS>
+__global__ __launch_bounds__(256) void gather_sum_kernel(const TS* __restrict__ dXs,
+                                                         const int32_t* __restrict__ dest_row,
+                                                         int T, int d, int k, int accumulate,
+                                                         TS* __restrict__ dx) {
+  const long t = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  gather_rows<TS, false>(dXs, nullptr, dest_row, t, T, d, k, accumulate, dx, threadIdx.x & 63);
+}
+
+// dYs[dest] = w * dY[t]; dw[t,j] = <dY[t], Ys[dest]>.  Each lane sums its
+// products in column order, then the wave sums the lanes.
+template <typename TS, bool MXQ>
+__device__ __forceinline__ void combine_bwd_slot(const float (&g)[8], const float (&v)[8], float wj,
+                                                 long r, int c, TS* __restrict__ dYs,
+                                                 uint8_t* __restrict__ q, uint8_t* __restrict__ qs,
+                                                 long pitch, int d, int lane, float& dot) {
+  float o[8];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) acc[q] = fmaf(wj, v[q], acc[q]);
-    }
-    store8(y + t * d + c, acc);
+  for (int i = 0; i < 8; ++i) {
+    dot = fmaf(g[i], v[i], dot);
+    o[i] = wj * g[i];
+  }
+  store8(dYs + r * d + c, o);
+  if constexpr (MXQ) {
+    // the stored (bf16) row, block-quantised along d for the down dgrad
+    float ro[8];
+    round_bf16_8(o, ro);
+    quant8_store(ro, q + r * d + c, qs + (long)(c >> 5) * pitch + r, lane);
   }
 }
 
-// dYs[dest] = w * dY[t]; dw[t,j] = <dY[t], Ys[dest]>
 template <typename TS, bool MXQ>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(const TS* __restrict__ dY,
                                                           const TS* __restrict__ Ys,
@@ -213,58 +315,56 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const TS* __restrict__
   const long t = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const int R = T * k;
+  if (d <= kPassCols) {
+    // one pass: the dY row stays in registers and two slots' rows are read together
+    const int c0 = lane * 8;
+    float g[kPassChunks][8];
+#pragma unroll
+    for (int u = 0; u < kPassChunks; ++u) load8(dY + t * d + chunk_col(c0, u, d), g[u]);
+    int j = 0;
+    auto slot = [&](int jj, const float (&v)[kPassChunks][8]) {
+      const long r = clamp_row(dest_row[t * k + jj], R);
+      const float wj = w[t * k + jj];
+      float dot = 0.0f;
+#pragma unroll
+      for (int u = 0; u < kPassChunks; ++u)
+        if (c0 + 512 * u < d)
+          combine_bwd_slot<TS, MXQ>(g[u], v[u], wj, r, c0 + 512 * u, dYs, q, qs, pitch, d, lane, dot);
+      dot = wave_sum(dot);
+      if (lane == 0) dw[t * k + jj] = dot;
+    };
+    for (; j + 2 <= k; j += 2) {
+      const TS* p0 = Ys + (long)clamp_row(dest_row[t * k + j], R) * d;
+      const TS* p1 = Ys + (long)clamp_row(dest_row[t * k + j + 1], R) * d;
+      float v0[kPassChunks][8], v1[kPassChunks][8];
+#pragma unroll
+      for (int u = 0; u < kPassChunks; ++u) load8(p0 + chunk_col(c0, u, d), v0[u]);
+#pragma unroll
+      for (int u = 0; u < kPassChunks; ++u) load8(p1 + chunk_col(c0, u, d), v1[u]);
+      slot(j, v0);
+      slot(j + 1, v1);
+    }
+    if (j < k) {
+      const TS* p0 = Ys + (long)clamp_row(dest_row[t * k + j], R) * d;
+      float v0[kPassChunks][8];
+#pragma unroll
+      for (int u = 0; u < kPassChunks; ++u) load8(p0 + chunk_col(c0, u, d), v0[u]);
+      slot(j, v0);
+    }
+    return;
+  }
   for (int j = 0; j < k; ++j) {
-    const int r = clamp_row(dest_row[t * k + j], R);
+    const long r = clamp_row(dest_row[t * k + j], R);
     const float wj = w[t * k + j];
     float dot = 0.0f;
     for (int c = lane * 8; c < d; c += 64 * 8) {
-      float g[8], v[8], o[8];
+      float g[8], v[8];
       load8(dY + t * d + c, g);
-      load8(Ys + (long)r * d + c, v);
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        dot = fmaf(g[q], v[q], dot);
-        o[q] = wj * g[q];
-      }
-      store8(dYs + (long)r * d + c, o);
-      if constexpr (MXQ) {
-        // the stored (bf16) row, block-quantised along d for the down dgrad
-        float ro[8];
-        round_bf16_8(o, ro);
-        quant8_store(ro, q + (long)r * d + c, qs + (long)(c >> 5) * pitch + r, lane);
-      }
+      load8(Ys + r * d + c, v);
+      combine_bwd_slot<TS, MXQ>(g, v, wj, r, c, dYs, q, qs, pitch, d, lane, dot);
     }
     dot = wave_sum(dot);
     if (lane == 0) dw[t * k + j] = dot;
-  }
-}
-
-// dx[t] (+)= sum_j dXs[dest_row[t,j]]
-template <typename TS>
-__global__ __launch_bounds__(256) void gather_sum_kernel(const TS* __restrict__ dXs,
-                                                         const int32_t* __restrict__ dest_row,
-                                                         int T, int d, int k, int accumulate,
-                                                         TS* __restrict__ dx) {
-  const int lane = threadIdx.x & 63;
-  const long t = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  const int R = T * k;
-  for (int c = lane * 8; c < d; c += 64 * 8) {
-    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int j = 0; j < k; ++j) {
-      const int r = clamp_row(dest_row[t * k + j], R);
-      float v[8];
-      load8(dXs + (long)r * d + c, v);
-#pragma unroll
-      for (int q = 0; q < 8; ++q) acc[q] += v[q];
-    }
-    if (accumulate) {
-      float o[8];
-      load8(dx + t * d + c, o);
-#pragma unroll
-      for (int q = 0; q < 8; ++q) acc[q] += o[q];
-    }
-    store8(dx + t * d + c, acc);
   }
 }
 
@@ -447,19 +547,19 @@ hipError_t launch_dispatch_meta(const int32_t* idx, int T, int E, int k, int32_t
 }
 
 template <typename TS>
-static hipError_t copy_impl(const void* x, const int32_t* src, int R, int T, int d, void* Xs,
+static hipError_t copy_impl(const void* x, const int32_t* dest, int T, int d, int k, void* Xs,
                             hipStream_t s) {
-  hipLaunchKernelGGL(dispatch_copy_kernel<TS>, dim3((R + 3) / 4), dim3(256), 0, s,
-                     static_cast<const TS*>(x), src, R, T, d, static_cast<TS*>(Xs));
+  hipLaunchKernelGGL(dispatch_scatter_kernel<TS>, dim3((T + 3) / 4), dim3(256), 0, s,
+                     static_cast<const TS*>(x), dest, T, d, k, static_cast<TS*>(Xs));
   note_launch("dispatch_copy", s);
   return hipGetLastError();
 }
 
-hipError_t launch_dispatch_copy(int dtype, const void* x, const int32_t* src_token, int R, int T,
-                                int d, void* Xs, hipStream_t s) {
-  if (R == 0) return hipSuccess;
-  return dtype ? copy_impl<bf16_t>(x, src_token, R, T, d, Xs, s)
-               : copy_impl<float>(x, src_token, R, T, d, Xs, s);
+hipError_t launch_dispatch_copy(int dtype, const void* x, const int32_t* dest_row, int T, int d,
+                                int k, void* Xs, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  return dtype ? copy_impl<bf16_t>(x, dest_row, T, d, k, Xs, s)
+               : copy_impl<float>(x, dest_row, T, d, k, Xs, s);
 }
 
 hipError_t launch_combine(int dtype, const void* Ys, const float* w, const int32_t* dest, int T,

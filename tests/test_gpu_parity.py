@@ -37,6 +37,10 @@ SHAPES = {
     # (d = 192), experts with more than 32 rows and empty experts (Zipf loads)
     "skinny_d256": ("olmoe_bf16", dict(name="skinny_d256", T=40, d=256, E=8, f=320, k=2)),
     "skinny_zipf_d192": ("share1t_bf16", dict(name="skinny_zipf_d192", T=700, d=192, f=256)),
+    # rows wider than one 2048-column pass of the row kernels (dispatch,
+    # combine and their backwards), the second pass partly filled
+    "wide_bf16_d2560": ("olmoe_bf16", dict(name="wide_bf16_d2560", T=200, d=2560, E=8, f=128, k=3)),
+    "wide_fp32_d2112": ("tiny_fp32", dict(name="wide_fp32_d2112", T=90, d=2112, E=4, f=64, k=2)),
     "tiny_mxfp8": ("tiny_mxfp8", {}),
     # d = 576: an odd number of 64-deep K stages; f = 320: a half-filled last gate/up panel
     "mid_mxfp8_E8": ("olmoe_mxfp8", dict(name="mid_mxfp8_E8", T=1000, d=576, E=8, f=320, k=2)),
