@@ -199,7 +199,10 @@ int moe_route(const void* x, const void* Wr, int T, int d, int E, int k, int dty
     return status_of(launch_route_small(static_cast<const uint16_t*>(x),
                                         static_cast<const uint16_t*>(Wr), T, d, E, k, renorm,
                                         static_cast<float*>(ws), logits, topk_idx, topk_w, st));
-  if (!lin) {
+  if (!lin && dtype == MOE_BF16 && router_logits_applies(d, E)) {
+    MOE_TRY(launch_router_logits(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(Wr),
+                                 T, d, E, logits, st));
+  } else if (!lin) {
     GemmArgs g{};
     g.E = 1; g.offsets = nullptr; g.rows_total = T; g.ragged = RAG_M;
     g.M = T; g.N = E; g.K = d;

@@ -28,6 +28,12 @@ bool combine_small_applies(int T);
 hipError_t launch_combine_small(int dtype, const void* Ys, const float* w, const int32_t* dest,
                                 int T, int d, int k, void* y, hipStream_t s);
 
+// Router logits of a bf16 batch on the thin-product MFMA kernel (router.hip):
+// E % 8 == 0, E <= 256, d % 64 == 0.
+bool router_logits_applies(int d, int E);
+hipError_t launch_router_logits(const uint16_t* x, const uint16_t* Wr, int T, int d, int E,
+                                float* logits, hipStream_t s);
+
 // renorm: divide the k chosen probabilities by their sum.
 hipError_t launch_topk_softmax(const float* logits, int T, int E, int k, int renorm, int32_t* idx,
                                float* w, hipStream_t s);

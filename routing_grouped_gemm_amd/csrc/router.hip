@@ -1,0 +1,233 @@
+// Router logits of a bf16 batch: logits[t][e] = sum_k x[t][k] Wr[k][e] with
+// float32 accumulation (HF OLMoE walkthrough, section 2: the router is one
+// linear map from a token's hidden state to a logit per expert).
+//
+// The product is thin (at most 256 expert columns), so the general grouped
+// GEMM's 256x256 tiles would use a few dozen workgroups and waste most of
+// their MFMA work on absent columns.  Here a workgroup takes 32 tokens and
+// every expert over the whole contraction: the router weights
+// pass through LDS in chunks of KC k-rows, transposed on the way in so that
+// each expert's k run is contiguous, and each wave multiplies them with its
+// tokens' rows, read straight from HBM into registers, on 16x16x32 bf16
+// MFMAs.  Later chunks of both operands are loaded while the current one is
+// multiplied.  No workspace, one kernel; softmax and top-k follow in their
+// own kernel.
+#include <type_traits>
+
+#include "hook.h"
+#include "moe_common.h"
+#include "route.h"
+
+namespace moe {
+
+constexpr int kRlTokens = 32;    // tokens per workgroup
+
+typedef __attribute__((ext_vector_type(4))) short i16x4_t;
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+// NB blocks of 16 experts (1, 2, 4, 8 or 16): chunk length KC (a multiple
+// of 64 in [64, 256], chunk within 32 KiB) and bytes per chunk row (one k).
+__host__ __device__ constexpr int rl_kc(int nb) {
+  return (16384 / (16 * nb)) / 64 * 64 < 64    ? 64
+         : (16384 / (16 * nb)) / 64 * 64 > 256 ? 256
+                                                : (16384 / (16 * nb)) / 64 * 64;
+}
+__host__ __device__ constexpr int rl_rowb(int nb) { return 32 * nb; }
+__host__ __device__ constexpr int rl_lds(int nb) { return 2 * rl_kc(nb) * rl_rowb(nb); }
+
+// A chunk sits in LDS as Wr's own rows (k-major, 16-byte chunks of 8
+// experts), each row's chunks XOR-permuted in pairs by a function of k.
+// Weight fragments are read with ds_read_b64_tr_b16: a 16-lane group reads
+// 4 k-rows x 16 experts and each lane receives one expert at 4 consecutive
+// k.  One fragment read of a wave touches k-rows kb + 8G + j (G = lane/16,
+// j = 0..3) and one 32-byte pair per row; the permutation puts those 16 rows
+// on distinct 32-byte bank positions two by two (the least a 512-byte read
+// needs), given where each row starts in the 256-byte bank window.
+template <int NB>
+__device__ __forceinline__ int rl_swz(int k) {
+  const int j = k & 3, G = (k >> 3) & 3;
+  if constexpr (NB >= 8) return j | ((G & 1) << 2);
+  else if constexpr (NB == 4) return ((j >> 1) ^ G) & 3;
+  else if constexpr (NB == 2) return G & 1;
+  else return 0;
+}
+template <int NB>
+__device__ __forceinline__ int rl_off(int k, int chunk) {
+  return k * rl_rowb(NB) + ((chunk ^ (2 * rl_swz<NB>(k))) << 4);
+}
+
+// Waves 0-1 take tokens 0-15 and 16-31 of the workgroup for k 0-31 of every
+// 64-row piece, waves 2-3 the same tokens for k 32-63; the two halves are
+// added at the end.  Each wave's rows of x arrive three chunks ahead of
+// their use and the weight chunks two ahead (in registers), so several HBM
+// and L2 round trips are in flight at once.  Every global load is issued
+// unconditionally (addresses past the end are clamped to loaded data that is
+// then not used), which keeps the compiler's wait counts exact.
+template <int NB>
+__global__ __launch_bounds__(256, 1) void router_logits_kernel(const uint16_t* __restrict__ x,
+                                                               const uint16_t* __restrict__ Wr,
+                                                               int T, int d, int E,
+                                                               float* __restrict__ logits) {
+  constexpr int KC = rl_kc(NB), NP = KC / 64, RB = rl_rowb(NB);
+  constexpr int NCH = 2 * NB;               // 16-byte chunks per row
+  constexpr int UPT = KC * NCH / 256;       // fill units (one chunk of one row) per thread
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  char* const buf0 = lds;
+  char* const buf1 = lds + KC * RB;
+  const int tg = wave & 1, h = wave >> 1;
+  const int t0 = blockIdx.x * kRlTokens + tg * 16;
+  const int tl = lane & 15, G = lane >> 4;
+  const long trow = min(t0 + tl, T - 1);
+  // lane (token tl, k-group G) of half h supplies k = 64p + 32h + 8G + (0..7)
+  // of piece p; the weight fragments use the same k assignment
+  const uint16_t* xp = x + trow * d + 32 * h + 8 * G;
+  const int oct = E >> 3;                  // chunks of a row that hold experts
+  const int units = KC * oct;              // fill units per chunk
+  const int nch = (d + KC - 1) / KC;
+  const int np_last = (d - (nch - 1) * KC) >> 6;  // pieces of the last chunk
+
+  // chunks oct.. of every row of both buffers hold the zero padding experts
+  if (oct < NCH) {
+    const int per = KC * (NCH - oct);
+    for (int i = tid; i < 2 * per; i += 256) {
+      const int b = i / per, r = i - b * per;
+      const int k = r / (NCH - oct), c = oct + r % (NCH - oct);
+      *reinterpret_cast<u32x4_t*>((b ? buf1 : buf0) + rl_off<NB>(k, c)) = u32x4_t{0, 0, 0, 0};
+    }
+  }
+
+  // this thread's fill units: row uk and 8-expert group uo (clamped into
+  // range for the loads; units past the end are not stored)
+  int uk[UPT], uo[UPT];
+#pragma unroll
+  for (int i = 0; i < UPT; ++i) {
+    const int u = min(tid + 256 * i, units - 1);
+    uk[i] = u / oct;
+    uo[i] = u - uk[i] * oct;
+  }
+  auto load_w = [&](int c, u32x4_t (&wr)[UPT]) __attribute__((always_inline)) {
+    const int k0 = c * KC, klast = min(KC, d - k0) - 1;
+    const uint16_t* const base = Wr + (long)k0 * E;
+#pragma unroll
+    for (int i = 0; i < UPT; ++i)
+      wr[i] = *reinterpret_cast<const u32x4_t*>(base + min(uk[i], klast) * E + 8 * uo[i]);
+  };
+  auto store_w = [&](int c, const u32x4_t (&wr)[UPT]) __attribute__((always_inline)) {
+    char* const B = (c & 1) ? buf1 : buf0;
+#pragma unroll
+    for (int i = 0; i < UPT; ++i)
+      if (tid + 256 * i < units) *reinterpret_cast<u32x4_t*>(B + rl_off<NB>(uk[i], uo[i])) = wr[i];
+  };
+  auto load_x = [&](int c, u32x4_t (&xv)[NP]) __attribute__((always_inline)) {
+    const int k0 = c * KC, pl = (min(KC, d - k0) >> 6) - 1;
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+      xv[p] = *reinterpret_cast<const u32x4_t*>(xp + k0 + 64 * min(p, pl));
+  };
+  // weight fragment of expert block nb, piece p: experts 16nb + tl at
+  // k = 64p + 32h + 8G + (0..7), from two transposing reads of 4 k-rows
+  auto wfrag = [&](const char* B, int nb, int p) __attribute__((always_inline)) {
+    const int r = tl;
+    const int k = 64 * p + 32 * h + 8 * G + (r >> 2);
+    const int chunk = 2 * nb + ((r & 3) >> 1);
+    const char* q = B + rl_off<NB>(k, chunk) + 8 * (r & 1);
+    const char* q4 = B + rl_off<NB>(k + 4, chunk) + 8 * (r & 1);
+    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(q));
+    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(q4));
+    typedef __attribute__((ext_vector_type(8))) short i16x8_t;
+    const i16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8_t, v);
+  };
+
+  f32x4_t acc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // D[expert][token]: this lane gets experts 16nb + 4G + (0..3) of token tl
+  auto mma = [&](int c, const u32x4_t (&xv)[NP]) __attribute__((always_inline)) {
+    const char* const B = (c & 1) ? buf1 : buf0;
+    const int np = (c < nch - 1) ? NP : np_last;
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+      if (p < np) {
+        const bf16x8_t xf = __builtin_bit_cast(bf16x8_t, xv[p]);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wfrag(B, nb, p), xf, acc[nb], 0, 0, 0);
+      }
+  };
+
+  u32x4_t xr[4][NP];    // x pieces of chunks c .. c+3 (slot c & 3)
+  u32x4_t wr[2][UPT];   // weight units of chunks c+1, c+2 (slot c & 1)
+  load_w(0, wr[0]);
+#pragma unroll
+  for (int i = 0; i < 3; ++i) load_x(min(i, nch - 1), xr[i]);
+  store_w(0, wr[0]);
+  load_w(min(1, nch - 1), wr[1]);
+  load_w(min(2, nch - 1), wr[0]);
+  __syncthreads();
+  // chunk c: x and weights of chunk c+3 are requested, chunk c is
+  // multiplied, chunk c+1's weights go to the other buffer (which every wave
+  // left at the barrier closing chunk c-1); past the last chunk the loads
+  // repeat it and the rest is skipped
+  auto step = [&](auto slot, int c) __attribute__((always_inline)) {
+    constexpr int X = decltype(slot)::value;
+    load_x(min(c + 3, nch - 1), xr[(X + 3) & 3]);
+    if (c < nch) mma(c, xr[X]);
+    if (c + 1 < nch) store_w(c + 1, wr[(X + 1) & 1]);
+    load_w(min(c + 3, nch - 1), wr[(X + 1) & 1]);
+    __syncthreads();
+  };
+  for (int c = 0; c < nch; c += 4) {
+    step(std::integral_constant<int, 0>{}, c);
+    step(std::integral_constant<int, 1>{}, c + 1);
+    step(std::integral_constant<int, 2>{}, c + 2);
+    step(std::integral_constant<int, 3>{}, c + 3);
+  }
+
+  // k halves: waves 2-3 leave their sums in LDS, waves 0-1 add them (in that
+  // order) and store
+  float* const red = reinterpret_cast<float*>(lds);  // [2 token groups][NB][64 lanes][4]
+  if (h == 1) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+      *reinterpret_cast<f32x4_t*>(red + ((tg * NB + nb) * 64 + lane) * 4) = acc[nb];
+  }
+  __syncthreads();
+  const int t = t0 + tl;
+  if (h == 0 && t < T) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int e = 16 * nb + 4 * G;
+      if (e < E) {
+        const f32x4_t o = *reinterpret_cast<const f32x4_t*>(red + ((tg * NB + nb) * 64 + lane) * 4);
+        *reinterpret_cast<f32x4_t*>(logits + (long)t * E + e) = acc[nb] + o;
+      }
+    }
+  }
+}
+
+bool router_logits_applies(int d, int E) { return E % 8 == 0 && E <= 256 && d % 64 == 0; }
+
+hipError_t launch_router_logits(const uint16_t* x, const uint16_t* Wr, int T, int d, int E,
+                                float* logits, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const dim3 grid((T + kRlTokens - 1) / kRlTokens);
+  const int nb = (E + 15) / 16;
+  // expert blocks rounded up to a power of two (the padding experts are zero)
+  if (nb <= 1)
+    hipLaunchKernelGGL(router_logits_kernel<1>, grid, dim3(256), rl_lds(1), s, x, Wr, T, d, E, logits);
+  else if (nb <= 2)
+    hipLaunchKernelGGL(router_logits_kernel<2>, grid, dim3(256), rl_lds(2), s, x, Wr, T, d, E, logits);
+  else if (nb <= 4)
+    hipLaunchKernelGGL(router_logits_kernel<4>, grid, dim3(256), rl_lds(4), s, x, Wr, T, d, E, logits);
+  else if (nb <= 8)
+    hipLaunchKernelGGL(router_logits_kernel<8>, grid, dim3(256), rl_lds(8), s, x, Wr, T, d, E, logits);
+  else
+    hipLaunchKernelGGL(router_logits_kernel<16>, grid, dim3(256), rl_lds(16), s, x, Wr, T, d, E,
+                       logits);
+  note_launch("router_logits", s);
+  return hipGetLastError();
+}
+
+}  // namespace moe

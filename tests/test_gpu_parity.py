@@ -41,6 +41,11 @@ SHAPES = {
     # combine and their backwards), the second pass partly filled
     "wide_bf16_d2560": ("olmoe_bf16", dict(name="wide_bf16_d2560", T=200, d=2560, E=8, f=128, k=3)),
     "wide_fp32_d2112": ("tiny_fp32", dict(name="wide_fp32_d2112", T=90, d=2112, E=4, f=64, k=2)),
+    # the router's thin-product kernel: 16 blocks of 16 experts with 64-row
+    # chunks and a partial last one (E = 256, d = 576); a half-empty last
+    # expert block (E = 40) and a chunk of one 64-row piece (d = 320)
+    "router_E256": ("olmoe_bf16", dict(name="router_E256", T=300, d=576, E=256, f=64, k=8)),
+    "router_E40": ("olmoe_bf16", dict(name="router_E40", T=130, d=320, E=40, f=64, k=4)),
     "tiny_mxfp8": ("tiny_mxfp8", {}),
     # d = 576: an odd number of 64-deep K stages; f = 320: a half-filled last gate/up panel
     "mid_mxfp8_E8": ("olmoe_mxfp8", dict(name="mid_mxfp8_E8", T=1000, d=576, E=8, f=320, k=2)),
@@ -71,7 +76,8 @@ def test_layer_parity(name):
         assert np.all(np.diff(src[offs[e]:offs[e + 1]]) > 0)
 
 
-@pytest.mark.parametrize("name", ["tiny_fp32", "mid_bf16_E8", "mid_bf16_E64", "edge_E6_bf16"])
+@pytest.mark.parametrize("name", ["tiny_fp32", "mid_bf16_E8", "mid_bf16_E64", "edge_E6_bf16",
+                                  "router_E256", "router_E40", "wide_bf16_d2560"])
 def test_router_logits_and_topk(name):
     """Router GEMM on the GPU against the oracle's logits; top-k bit-exact on
     every token whose k-th/(k+1)-th logit gap exceeds the logit error."""
