@@ -451,6 +451,9 @@ int moe_route_bwd(const void* x, const void* Wr, const float* logits, const int3
     g.accumulate = acc;
     MOE_TRY(launch_grouped_gemm(GK_ROUTER_DWR, eng, g, num_cu(), st));
   }
+  if (dtype == MOE_BF16 && router_dx_applies(d, E))
+    return status_of(launch_router_dx(dl16, ld16, static_cast<const uint16_t*>(Wr), T, d, E,
+                                      static_cast<uint16_t*>(dx), st));
   GemmArgs h{};
   h.E = 1; h.offsets = nullptr; h.rows_total = T; h.ragged = RAG_M;
   // the MFMA engine runs K over the zero-padded width; the SIMT engine over E

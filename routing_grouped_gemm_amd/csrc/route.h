@@ -34,6 +34,12 @@ bool router_logits_applies(int d, int E);
 hipError_t launch_router_logits(const uint16_t* x, const uint16_t* Wr, int T, int d, int E,
                                 float* logits, hipStream_t s);
 
+// Router input gradient dx += dl16 . Wr^T on MFMAs (router.hip): dl16 [T][ld]
+// bf16 with a zero tail, ld = 64 * ceil(E / 64); E % 8 == 0, E <= 256, d % 64 == 0.
+bool router_dx_applies(int d, int E);
+hipError_t launch_router_dx(const uint16_t* dl16, int ld, const uint16_t* Wr, int T, int d, int E,
+                            uint16_t* dx, hipStream_t s);
+
 // renorm: divide the k chosen probabilities by their sum.
 hipError_t launch_topk_softmax(const float* logits, int T, int E, int k, int renorm, int32_t* idx,
                                float* w, hipStream_t s);

@@ -602,23 +602,37 @@ hipError_t launch_combine_bwd(int dtype, const void* dY, const void* Ys, const f
   return hipGetLastError();
 }
 
+// out[i] (+)= sum over s of part[s][i], in order of s; each thread four
+// consecutive outputs with eight partials in flight (16-byte loads: n is a
+// multiple of 4, as d * E is).
 template <typename TS>
-__global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restrict__ part, int S,
-                                                           long n, int accumulate,
-                                                           TS* __restrict__ out) {
-  const long i = ((long)blockIdx.x * 256 + threadIdx.x) * 4;
+__global__ __launch_bounds__(64) void split_reduce_kernel(const float* __restrict__ part, int S,
+                                                          long n, int accumulate,
+                                                          TS* __restrict__ out) {
+  const long i = ((long)blockIdx.x * 64 + threadIdx.x) * 4;
   if (i >= n) return;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   if (accumulate)
     for (int q = 0; q < 4; ++q) acc[q] = (i + q < n) ? St<TS>::load(out + i + q) : 0.f;
-  for (int s = 0; s < S; ++s) {
-    const float* p = part + (long)s * n + i;
-    if (i + 4 <= n) {
-      const float4 v = *reinterpret_cast<const float4*>(p);
-      acc[0] += v.x; acc[1] += v.y; acc[2] += v.z; acc[3] += v.w;
-    } else {
-      for (int q = 0; q < 4 && i + q < n; ++q) acc[q] += p[q];
+  if (i + 4 <= n) {
+    const float* p = part + i;
+    int s = 0;
+    for (; s + 8 <= S; s += 8) {
+      float4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const float4*>(p + (long)(s + u) * n);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        acc[0] += v[u].x; acc[1] += v[u].y; acc[2] += v[u].z; acc[3] += v[u].w;
+      }
     }
+    for (; s < S; ++s) {
+      const float4 v = *reinterpret_cast<const float4*>(p + (long)s * n);
+      acc[0] += v.x; acc[1] += v.y; acc[2] += v.z; acc[3] += v.w;
+    }
+  } else {
+    for (int s = 0; s < S; ++s)
+      for (int q = 0; q < 4 && i + q < n; ++q) acc[q] += part[(long)s * n + i + q];
   }
   for (int q = 0; q < 4 && i + q < n; ++q) St<TS>::store(out + i + q, acc[q]);
 }
@@ -626,12 +640,12 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restri
 hipError_t launch_split_reduce(int dtype, const float* part, int S, long n, int accumulate,
                                void* out, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  const dim3 grid((unsigned)((n + 1023) / 1024));
+  const dim3 grid((unsigned)((n + 255) / 256));
   if (dtype)
-    hipLaunchKernelGGL(split_reduce_kernel<bf16_t>, grid, dim3(256), 0, s, part, S, n, accumulate,
+    hipLaunchKernelGGL(split_reduce_kernel<bf16_t>, grid, dim3(64), 0, s, part, S, n, accumulate,
                        static_cast<bf16_t*>(out));
   else
-    hipLaunchKernelGGL(split_reduce_kernel<float>, grid, dim3(256), 0, s, part, S, n, accumulate,
+    hipLaunchKernelGGL(split_reduce_kernel<float>, grid, dim3(64), 0, s, part, S, n, accumulate,
                        static_cast<float*>(out));
   note_launch("router_dwr_reduce", s);
   return hipGetLastError();

@@ -230,4 +230,139 @@ hipError_t launch_router_logits(const uint16_t* x, const uint16_t* Wr, int T, in
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// router backward, input gradient: dx[t][c] += sum_e dl[t][e] Wr[c][e]
+// ---------------------------------------------------------------------------
+// dl16 [T][ld] bf16 (zero past E, ld = 64 * ceil(E / 64)) and Wr [d][E] both
+// run along e in memory, so both MFMA operands come straight from global
+// memory (Wr from L2).  A wave takes 16 tokens and one of P column parts (P
+// sized so that the chip holds four such waves per SIMD), 64 columns at a
+// time as four 16x16 blocks (D[column][token] on 16x16x32 bf16 MFMAs over
+// K = ld).  The block sums pass through a private LDS slice so that dx is
+// read and written in 16-byte pieces along its rows (8 tokens x 128 bytes
+// per instruction); each element gets one bf16 rounding of old + sum.  The
+// old dx of the next 64 columns is loaded while the current ones are
+// computed; loads are unconditional (clamped to the last group, whose
+// duplicate is not stored).
+// NK = ld / 32 K-steps.
+constexpr int kRdxPitch = 68;  // floats per token row of a wave's LDS slice (64 + skew)
+
+template <int NK>
+__global__ __launch_bounds__(256) void router_dx_kernel(const uint16_t* __restrict__ dl16, int ld,
+                                                        const uint16_t* __restrict__ Wr, int T,
+                                                        int d, int E, uint16_t* __restrict__ dx) {
+  __shared__ __attribute__((aligned(16))) float slice_all[4][16 * kRdxPitch];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tg = wave & 1, part = blockIdx.y * 2 + (wave >> 1), P = gridDim.y * 2;
+  const int tl = lane & 15, G = lane >> 4;
+  const int tbase = blockIdx.x * 32 + tg * 16;
+  float* const slice = slice_all[wave];
+  // MFMA side: lane (row tl, k-group G) supplies k = 32s + 8G + (0..7)
+  const long trow = min(tbase + tl, T - 1);
+  bf16x8_t bfr[NK];
+#pragma unroll
+  for (int s = 0; s < NK; ++s)
+    bfr[s] = __builtin_bit_cast(bf16x8_t,
+                                *reinterpret_cast<const u32x4_t*>(dl16 + trow * ld + 32 * s + 8 * G));
+  bool eok[NK];
+  int eoff[NK];
+#pragma unroll
+  for (int s = 0; s < NK; ++s) {
+    const int e = 32 * s + 8 * G;
+    eok[s] = e < E;
+    eoff[s] = min(e, E - 8);
+  }
+  // dx side: lane (row r and r + 8, 8 columns at 8cq)
+  const int r = lane >> 3, cq = lane & 7;
+  const int ta = tbase + r, tb = tbase + r + 8;
+  uint16_t* const xa = dx + (long)min(ta, T - 1) * d + 8 * cq;
+  uint16_t* const xb = dx + (long)min(tb, T - 1) * d + 8 * cq;
+
+  const int ngrp = d / 64;
+  const int per = (ngrp + P - 1) / P;  // 64-column groups of each part
+  const int g0 = part * per;
+  const int ng = min(per, ngrp - g0);
+  if (ng <= 0) return;
+
+  auto load_old = [&](int gi, u32x4_t& oa, u32x4_t& ob) __attribute__((always_inline)) {
+    const int c0 = 64 * (g0 + min(gi, ng - 1));
+    oa = *reinterpret_cast<const u32x4_t*>(xa + c0);
+    ob = *reinterpret_cast<const u32x4_t*>(xb + c0);
+  };
+  auto compute = [&](int gi, const u32x4_t& oa, const u32x4_t& ob) __attribute__((always_inline)) {
+    const int c0 = 64 * (g0 + gi);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint16_t* const wr = Wr + (long)(c0 + 16 * j + tl) * E;
+      u32x4_t w[NK];
+#pragma unroll
+      for (int s = 0; s < NK; ++s) w[s] = *reinterpret_cast<const u32x4_t*>(wr + eoff[s]);
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < NK; ++s) {
+        const u32x4_t a = eok[s] ? w[s] : u32x4_t{0, 0, 0, 0};
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), bfr[s], acc,
+                                                      0, 0, 0);
+      }
+      // columns 16j + 4G + (0..3) of token tl
+      *reinterpret_cast<f32x4_t*>(slice + tl * kRdxPitch + 16 * j + 4 * G) = acc;
+    }
+    // the slice is private to the wave and LDS accesses of a wave complete in order
+    __builtin_amdgcn_wave_barrier();
+    float va[8], vb[8], oa8[8], ob8[8];
+    const f32x4_t* pa = reinterpret_cast<const f32x4_t*>(slice + r * kRdxPitch + 8 * cq);
+    const f32x4_t* pb = reinterpret_cast<const f32x4_t*>(slice + (r + 8) * kRdxPitch + 8 * cq);
+    const f32x4_t a0 = pa[0], a1 = pa[1], b0 = pb[0], b1 = pb[1];
+    __builtin_amdgcn_wave_barrier();
+    unpack8(uint4{oa[0], oa[1], oa[2], oa[3]}, oa8);
+    unpack8(uint4{ob[0], ob[1], ob[2], ob[3]}, ob8);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      va[q] = a0[q] + oa8[q]; va[q + 4] = a1[q] + oa8[q + 4];
+      vb[q] = b0[q] + ob8[q]; vb[q + 4] = b1[q] + ob8[q + 4];
+    }
+    if (ta < T) store8(xa + c0, va);
+    if (tb < T) store8(xb + c0, vb);
+  };
+
+  u32x4_t oa0, ob0, oa1, ob1;
+  load_old(0, oa0, ob0);
+  for (int gi = 0; gi < ng; gi += 2) {
+    load_old(gi + 1, oa1, ob1);
+    compute(gi, oa0, ob0);
+    load_old(gi + 2, oa0, ob0);
+    if (gi + 1 < ng) compute(gi + 1, oa1, ob1);
+  }
+}
+
+bool router_dx_applies(int d, int E) { return E % 8 == 0 && E <= 256 && d % 64 == 0; }
+
+hipError_t launch_router_dx(const uint16_t* dl16, int ld, const uint16_t* Wr, int T, int d, int E,
+                            uint16_t* dx, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  // column parts: about 4096 waves in all, 2 to d/64 parts
+  const int tiles = (T + 31) / 32;
+  int P = 2;
+  while (2 * P <= d / 64 && (long)tiles * 2 * P < 4096) P *= 2;
+  const dim3 grid(tiles, P / 2);
+  switch (ld / 32) {
+    case 2:
+      hipLaunchKernelGGL(router_dx_kernel<2>, grid, dim3(256), 0, s, dl16, ld, Wr, T, d, E, dx);
+      break;
+    case 4:
+      hipLaunchKernelGGL(router_dx_kernel<4>, grid, dim3(256), 0, s, dl16, ld, Wr, T, d, E, dx);
+      break;
+    case 6:
+      hipLaunchKernelGGL(router_dx_kernel<6>, grid, dim3(256), 0, s, dl16, ld, Wr, T, d, E, dx);
+      break;
+    case 8:
+      hipLaunchKernelGGL(router_dx_kernel<8>, grid, dim3(256), 0, s, dl16, ld, Wr, T, d, E, dx);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  note_launch("router_dx", s);
+  return hipGetLastError();
+}
+
 }  // namespace moe
