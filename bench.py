@@ -68,6 +68,7 @@ _SYMBOLS = {
     "gemm_bf16_kernel<2>": ["gemm_dgrad_down_swiglu_bwd"],
     "gemm_bf16_kernel<3>": ["gemm_dgrad_gateup"],
     "gemm_bf16_kernel<4>": ["gemm_wgrad_gateup", "gemm_wgrad_down"],
+    "gemm8_kernel<4>": ["gemm_wgrad_gateup", "gemm_wgrad_down"],
     "gemm_bf16_kernel<5>": ["gemm_router_logits"],
     "gemm_bf16_kernel<7>": ["gemm_router_dx"],
     "gemm_bf16_kernel<12>": ["gemm_router_dwr"],
@@ -124,7 +125,7 @@ def _counter_means(directory: str):
     acc = {}
     for r in rows:
         name = r["Kernel_Name"].split("(")[0].replace("void ", "").replace("moe::mf::", "")
-        name = name.replace("moe::sk::", "").replace("moe::", "")
+        name = name.replace("moe::sk::", "").replace("moe::mf8::", "").replace("moe::", "")
         sym = next((k for k in _SYMBOLS if name.startswith(k.split("<")[0]) and
                     (("<" not in k) or name.startswith(k))), name)
         n = seen.get(sym, 0)

@@ -112,6 +112,10 @@ inline __host__ __device__ int ngroups(const GemmArgs& g) {
 hipError_t launch_grouped_gemm(GemmKind kind, int engine, const GemmArgs& g, int num_cu,
                                hipStream_t stream);
 
+// Eight-wave form of the bf16 MFMA engine (gemm8.hip), launched for GK_WGRAD;
+// grid: persistent workgroups.
+hipError_t launch_gemm8(GemmKind kind, const GemmArgs& g, int grid, hipStream_t stream);
+
 // Launch an MXFP8 grouped GEMM (kinds GK_MX_*).
 hipError_t launch_grouped_gemm_mx(GemmKind kind, const GemmArgs& g, int num_cu, hipStream_t stream);
 

@@ -348,7 +348,12 @@ hipError_t launch_kind(int dtype, const GemmArgs& g, int num_cu, hipStream_t str
     int ub = tiles_upper_bound(g, mf::BM, BNT);
     int grid = min(num_cu, ub);
     if (grid <= 0) return hipSuccess;
-    hipLaunchKernelGGL(mf::gemm_bf16_kernel<KIND>, dim3(grid), dim3(mf::NTHR), 0, stream, g);
+    if constexpr (KIND == GK_WGRAD) {  // eight-wave form (gemm8.hip)
+      if (hipError_t e = launch_gemm8(static_cast<GemmKind>(KIND), g, grid, stream); e != hipSuccess)
+        return e;
+    } else {
+      hipLaunchKernelGGL(mf::gemm_bf16_kernel<KIND>, dim3(grid), dim3(mf::NTHR), 0, stream, g);
+    }
   } else {
     int ub = tiles_upper_bound(g, st::BM, st::BN);
     int grid = min(num_cu * 8, ub);

@@ -393,19 +393,22 @@ struct Plan {
   uint32_t kstep;     // bytes the source advances per stage
   int split_stage;    // SPLIT_K: first stage read from rs1 (else a large value)
 };
-// LDS offset of the wave's i-th block inside the operand stage.
-__device__ __forceinline__ uint32_t plan_lds(int wave, int i) { return (uint32_t)(wave * DMA_PER_OP + i) * 1024u; }
+// LDS offset of the wave's i-th block inside the operand stage (DPO blocks
+// per wave).
+template <int DPO = DMA_PER_OP>
+__device__ __forceinline__ uint32_t plan_lds(int wave, int i) { return (uint32_t)(wave * DPO + i) * 1024u; }
 
 // K-major operand: row r of the tile is a row of `ldb` bytes at base + r*ldb;
-// `bytes` are readable from base.  Block blk = wave*8 + i holds rows
+// `bytes` are readable from base.  Block blk = wave*DPO + i holds rows
 // 8*blk .. 8*blk+7, 128 bytes each; the swizzle of a row depends only on the
 // parity of its block and on the lane.
+template <int DPO = DMA_PER_OP>
 __device__ __forceinline__ void plan_km(Plan& P, const void* base, long long bytes, const void* base1,
                                         long long bytes1, int split_stage, long ldb, int wave,
                                         int lane) {
   P.rs0 = make_rsrc(base, bytes);
   P.rs1 = make_rsrc(base1 ? base1 : base, base1 ? bytes1 : bytes);
-  const int row0 = wave * DMA_PER_OP * 8 + (lane >> 3);
+  const int row0 = wave * DPO * 8 + (lane >> 3);
   P.v0 = (uint32_t)(row0 * ldb + (((lane & 7) ^ km_swz(row0)) * 16));
   P.v1 = (uint32_t)(row0 * ldb + (((lane & 7) ^ km_swz(row0 + 8)) * 16));
   P.bstep = (uint32_t)(8 * ldb);
@@ -415,14 +418,15 @@ __device__ __forceinline__ void plan_km(Plan& P, const void* base, long long byt
 
 // MN-major operand (bf16): k-rows of a matrix with ld elements; panel p of
 // the tile starts at base_p (its column 0 at k = 0); bytes_p readable from
-// base_p.  Blocks 0-15 fill panel 0 (waves 0-1), 16-31 panel 1 (waves 2-3);
+// base_p.  Blocks 0-15 fill panel 0 (the first NWV/2 waves), 16-31 panel 1;
 // block blk holds k-rows 4*(blk%16) .. +3, 256 bytes each.
+template <int DPO = DMA_PER_OP, int NWV = 4>
 __device__ __forceinline__ void plan_mn(Plan& P, const void* base0, long long bytes0,
                                         const void* base1, long long bytes1, long ld, int wave,
                                         int lane) {
   P.rs0 = make_rsrc(base0, bytes0);
   P.rs1 = make_rsrc(base1, bytes1);
-  const int k0 = (wave & 1) * DMA_PER_OP * 4 + (lane >> 4);
+  const int k0 = (wave % (NWV / 2)) * DPO * 4 + (lane >> 4);
   P.v0 = P.v1 = (uint32_t)(k0 * ld * 2 + (((lane & 15) ^ mn_swz(k0)) * 16));
   P.bstep = (uint32_t)(4 * ld * 2);
   P.kstep = (uint32_t)(BK * ld * 2);
@@ -431,12 +435,12 @@ __device__ __forceinline__ void plan_mn(Plan& P, const void* base0, long long by
 
 // Issue the wave's DMA blocks of one operand for stage kt into the LDS
 // operand region at lds_base.
-template <bool MN>
+template <bool MN, int DPO = DMA_PER_OP, int NWV = 4>
 __device__ __forceinline__ void issue(const Plan& P, int kt, uint32_t lds_base, int wave) {
   i32x4_t rs;
   uint32_t soff;
   if constexpr (MN) {
-    rs = (wave >= 2) ? P.rs1 : P.rs0;
+    rs = (wave >= NWV / 2) ? P.rs1 : P.rs0;
     soff = (uint32_t)kt * P.kstep;
   } else {
     const bool second = kt >= P.split_stage;
@@ -444,24 +448,24 @@ __device__ __forceinline__ void issue(const Plan& P, int kt, uint32_t lds_base, 
     soff = (uint32_t)(second ? kt - P.split_stage : kt) * P.kstep;
   }
 #pragma unroll
-  for (int i = 0; i < DMA_PER_OP; ++i)
-    dma16(rs, lds_base + plan_lds(wave, i), (i & 1) ? P.v1 : P.v0, soff + (uint32_t)i * P.bstep);
+  for (int i = 0; i < DPO; ++i)
+    dma16(rs, lds_base + plan_lds<DPO>(wave, i), (i & 1) ? P.v1 : P.v0, soff + (uint32_t)i * P.bstep);
 }
 
-// Block i (0..DMA_PER_OP-1) of the wave's DMA of one operand for stage kt.
-template <bool MN>
+// Block i (0..DPO-1) of the wave's DMA of one operand for stage kt.
+template <bool MN, int DPO = DMA_PER_OP, int NWV = 4>
 __device__ __forceinline__ void issue_one(const Plan& P, int kt, uint32_t lds_base, int wave, int i) {
   i32x4_t rs;
   uint32_t soff;
   if constexpr (MN) {
-    rs = (wave >= 2) ? P.rs1 : P.rs0;
+    rs = (wave >= NWV / 2) ? P.rs1 : P.rs0;
     soff = (uint32_t)kt * P.kstep;
   } else {
     const bool second = kt >= P.split_stage;
     rs = second ? P.rs1 : P.rs0;
     soff = (uint32_t)(second ? kt - P.split_stage : kt) * P.kstep;
   }
-  dma16(rs, lds_base + plan_lds(wave, i), (i & 1) ? P.v1 : P.v0, soff + (uint32_t)i * P.bstep);
+  dma16(rs, lds_base + plan_lds<DPO>(wave, i), (i & 1) ? P.v1 : P.v0, soff + (uint32_t)i * P.bstep);
 }
 
 // L2 prefetch: one 4-byte buffer->LDS load per 128-byte line of a future
@@ -582,8 +586,9 @@ __device__ __forceinline__ void interleave_mfma_ds() {
   }
 }
 
-// Operand plans of one tile for each bf16 GEMM kind.
-template <int KIND>
+// Operand plans of one tile for each bf16 GEMM kind (NWV waves, DPO DMA
+// blocks per wave and operand).
+template <int KIND, int DPO = DMA_PER_OP, int NWV = 4>
 __device__ __forceinline__ void plan_tile(const GemmArgs& g, const Tile& t, int wave, int lane,
                                           Plan& pa, Plan& pb) {
   const bf16_t* A = static_cast<const bf16_t*>(g.a);
@@ -595,12 +600,12 @@ __device__ __forceinline__ void plan_tile(const GemmArgs& g, const Tile& t, int 
     // rows t.row0.. of A (global rows), K contiguous
     const bf16_t* base = A + (long)t.row0 * g.lda;
     const long long bytes = ((long long)g.rows_total - t.row0) * g.lda * 2;
-    plan_km(pa, base, bytes, nullptr, 0, 1 << 30, g.lda * 2, wave, lane);
+    plan_km<DPO>(pa, base, bytes, nullptr, 0, 1 << 30, g.lda * 2, wave, lane);
   } else {
     // k-rows t.row0 .. t.row0 + klen of A, M contiguous; columns t.m0 + 128 p
     const bf16_t* b0 = A + (long)t.row0 * g.lda + t.m0;
     const long long avail = (long long)t.klen * g.lda * 2;
-    plan_mn(pa, b0, avail - 2LL * t.m0, b0 + 128, avail - 2LL * (t.m0 + 128), g.lda, wave, lane);
+    plan_mn<DPO, NWV>(pa, b0, avail - 2LL * t.m0, b0 + 128, avail - 2LL * (t.m0 + 128), g.lda, wave, lane);
   }
   // ---- B ----
   if constexpr (KT<KIND>::BK_) {
@@ -608,25 +613,25 @@ __device__ __forceinline__ void plan_tile(const GemmArgs& g, const Tile& t, int 
     const long e_off = (long)t.e * g.b_es + (long)t.n0 * g.ldb;
     const long long bytes = ((long long)g.N - t.n0) * g.ldb * 2;
     if constexpr (BSP == BS_SPLIT_K)
-      plan_km(pb, B0 + e_off, bytes, B1 + e_off, bytes, g.b_split / BK, g.ldb * 2, wave, lane);
+      plan_km<DPO>(pb, B0 + e_off, bytes, B1 + e_off, bytes, g.b_split / BK, g.ldb * 2, wave, lane);
     else
-      plan_km(pb, B0 + e_off, bytes, nullptr, 0, 1 << 30, g.ldb * 2, wave, lane);
+      plan_km<DPO>(pb, B0 + e_off, bytes, nullptr, 0, 1 << 30, g.ldb * 2, wave, lane);
   } else if (g.ragged == RAG_M) {
     // B[k][n] per group (weights), N contiguous
     const bf16_t* w0 = B0 + (long)t.e * g.b_es;
     const long long total = (long long)g.K * g.ldb * 2;
     if constexpr (BSP == BS_DUAL_N) {
       const bf16_t* w1 = B1 + (long)t.e * g.b_es;
-      plan_mn(pb, w0 + t.n0, total - 2LL * t.n0, w1 + t.n0, total - 2LL * t.n0, g.ldb, wave, lane);
+      plan_mn<DPO, NWV>(pb, w0 + t.n0, total - 2LL * t.n0, w1 + t.n0, total - 2LL * t.n0, g.ldb, wave, lane);
     } else {
-      plan_mn(pb, w0 + t.n0, total - 2LL * t.n0, w0 + t.n0 + 128, total - 2LL * (t.n0 + 128),
+      plan_mn<DPO, NWV>(pb, w0 + t.n0, total - 2LL * t.n0, w0 + t.n0 + 128, total - 2LL * (t.n0 + 128),
               g.ldb, wave, lane);
     }
   } else {
     // B[krow][n] with global k-rows t.row0 .. t.row0 + klen
     const bf16_t* b0 = B0 + (long)t.row0 * g.ldb + t.n0;
     const long long avail = (long long)t.klen * g.ldb * 2;
-    plan_mn(pb, b0, avail - 2LL * t.n0, b0 + 128, avail - 2LL * (t.n0 + 128), g.ldb, wave, lane);
+    plan_mn<DPO, NWV>(pb, b0, avail - 2LL * t.n0, b0 + 128, avail - 2LL * (t.n0 + 128), g.ldb, wave, lane);
   }
 }
 
