@@ -30,10 +30,18 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restri
                                                            int E, int k, int renorm,
                                                            int32_t* __restrict__ topk_idx,
                                                            float* __restrict__ topk_w) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  __shared__ __attribute__((aligned(16))) float row[4][64];
+  __shared__ float ps[4][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + wave;
   if (t >= T) return;
-  topk_row(logits + (long)t * E, E, k, renorm, lane, topk_idx + (long)t * k, topk_w + (long)t * k);
+  if (E <= 64) {
+    if (lane < E) row[wave][lane] = logits[(long)t * E + lane];
+    __builtin_amdgcn_wave_barrier();
+    topk_rank64(row[wave], E, k, renorm, lane, ps[wave], topk_idx + (long)t * k, topk_w + (long)t * k);
+  } else {
+    topk_row(logits + (long)t * E, E, k, renorm, lane, topk_idx + (long)t * k, topk_w + (long)t * k);
+  }
 }
 
 // ---------------------------------------------------------------------------

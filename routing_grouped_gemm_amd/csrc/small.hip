@@ -90,7 +90,8 @@ __global__ __launch_bounds__(256) void route_final_kernel(const float* __restric
                                                           float* __restrict__ logits,
                                                           int32_t* __restrict__ topk_idx,
                                                           float* __restrict__ topk_w) {
-  __shared__ float lg[4][256];
+  __shared__ __attribute__((aligned(16))) float lg[4][256];
+  __shared__ float ps[4][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t0 = blockIdx.x * 4;
   const int nt = min(4, T - t0);
@@ -103,9 +104,14 @@ __global__ __launch_bounds__(256) void route_final_kernel(const float* __restric
     logits[(long)(t0 + t) * E + e] = sum;
   }
   __syncthreads();
-  if (wave < nt)
-    topk_row(lg[wave], E, k, renorm, lane, topk_idx + (long)(t0 + wave) * k,
-             topk_w + (long)(t0 + wave) * k);
+  if (wave < nt) {
+    if (E <= 64)
+      topk_rank64(lg[wave], E, k, renorm, lane, ps[wave], topk_idx + (long)(t0 + wave) * k,
+                  topk_w + (long)(t0 + wave) * k);
+    else
+      topk_row(lg[wave], E, k, renorm, lane, topk_idx + (long)(t0 + wave) * k,
+               topk_w + (long)(t0 + wave) * k);
+  }
 }
 
 // ---------------------------------------------------------------------------

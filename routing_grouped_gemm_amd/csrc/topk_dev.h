@@ -88,4 +88,51 @@ __device__ __forceinline__ void topk_row(const float* row, int E, int k, int ren
   }
 }
 
+// The same for E <= 64 experts with one logit per lane and no serial rounds:
+// a chosen expert's slot is its rank among the E logits by (logit desc,
+// expert asc), counted against the row held in LDS (sv: the E logits,
+// 16-byte aligned, readable by the wave); ps: k floats of wave-private LDS
+// for the renormalising sum, which is taken in slot order.  Choice, order and
+// weights are those of topk_row, bit for bit.
+__device__ __forceinline__ void topk_rank64(const float* sv, int E, int k, int renorm, int lane,
+                                            float* ps, int32_t* __restrict__ idx_out,
+                                            float* __restrict__ w_out) {
+  const bool act = lane < E;
+  const float v = act ? sv[lane] : -INFINITY;
+  const float mx = wave_max(v);
+  const float se = wave_sum(act ? expf(v - mx) : 0.0f);
+  int rank = 0;
+  int f = 0;
+  for (; f + 4 <= E; f += 4) {
+    const float4 u = *reinterpret_cast<const float4*>(sv + f);
+    rank += (u.x > v || (u.x == v && f < lane)) ? 1 : 0;
+    rank += (u.y > v || (u.y == v && f + 1 < lane)) ? 1 : 0;
+    rank += (u.z > v || (u.z == v && f + 2 < lane)) ? 1 : 0;
+    rank += (u.w > v || (u.w == v && f + 3 < lane)) ? 1 : 0;
+  }
+  for (; f < E; ++f) {
+    const float u = sv[f];
+    rank += (u > v || (u == v && f < lane)) ? 1 : 0;
+  }
+  const bool chosen = act && rank < k;
+  const float p = expf(v - mx) / se;
+  if (renorm) {
+    if (chosen) ps[rank] = p;
+    // the wave's own LDS writes are seen by its later reads
+    __builtin_amdgcn_wave_barrier();
+    float wsum = 0.0f;
+    if (lane == 0)
+      for (int j = 0; j < k; ++j) wsum += ps[j];
+    wsum = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(wsum)));
+    __builtin_amdgcn_wave_barrier();
+    if (chosen) {
+      idx_out[rank] = lane;
+      w_out[rank] = p / wsum;
+    }
+  } else if (chosen) {
+    idx_out[rank] = lane;
+    w_out[rank] = p;
+  }
+}
+
 }  // namespace moe
