@@ -175,9 +175,12 @@ __device__ __forceinline__ int chunk_col(int c0, int u, int d) { return min(c0 +
 template <typename TS>
 struct Raw8 {
   uint4 w[sizeof(TS) / 2];
-  __device__ __forceinline__ void load(const TS* p) {
+  __device__ __forceinline__ void load_nt(const TS* p) {
 #pragma unroll
-    for (int i = 0; i < (int)(sizeof(TS) / 2); ++i) w[i] = reinterpret_cast<const uint4*>(p)[i];
+    for (int i = 0; i < (int)(sizeof(TS) / 2); ++i) {
+      const u32x4_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p) + i);
+      w[i] = uint4{x[0], x[1], x[2], x[3]};
+    }
   }
   // Non-temporal stores: the dispatch copy measured 28% faster with them; the
   // combine backward's dYs rows measured slower and keep plain stores.
@@ -205,7 +208,7 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(const TS* __restr
   for (int c0 = lane * 8; c0 < d; c0 += kPassCols) {
     Raw8<TS> v[kPassChunks];
 #pragma unroll
-    for (int u = 0; u < kPassChunks; ++u) v[u].load(x + t * d + chunk_col(c0, u, d));
+    for (int u = 0; u < kPassChunks; ++u) v[u].load_nt(x + t * d + chunk_col(c0, u, d));
     for (int j = 0; j < k; ++j) {
       const int r = dest_row[t * k + j];
       if (r < 0 || r >= R) continue;
@@ -214,6 +217,19 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(const TS* __restr
         if (c0 + 512 * u < d) v[u].store_nt(Xs + (long)r * d + c0 + 512 * u);
     }
   }
+}
+
+// 8 elements as floats through a non-temporal 16-byte load (rows read once:
+// measured 10-20% faster for the gathers than plain loads).
+__device__ __forceinline__ void load8_nt(const bf16_t* p, float (&v)[8]) {
+  const u32x4_t u = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  unpack8(uint4{u[0], u[1], u[2], u[3]}, v);
+}
+__device__ __forceinline__ void load8_nt(const float* p, float (&v)[8]) {
+  const f32x4_t a = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
+  const f32x4_t b = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p + 4));
+  v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
+  v[4] = b[0]; v[5] = b[1]; v[6] = b[2]; v[7] = b[3];
 }
 
 // y[t] = sum_j w[t,j] Ys[dest_row[t,j]], in float32 in slot order.
@@ -243,9 +259,9 @@ __device__ __forceinline__ void gather_rows(const TS* __restrict__ src, const fl
       const TS* p1 = src + (long)clamp_row(dr[j + 1], R) * d;
       float v0[kPassChunks][8], v1[kPassChunks][8];
 #pragma unroll
-      for (int u = 0; u < kPassChunks; ++u) load8(p0 + chunk_col(c0, u, d), v0[u]);
+      for (int u = 0; u < kPassChunks; ++u) load8_nt(p0 + chunk_col(c0, u, d), v0[u]);
 #pragma unroll
-      for (int u = 0; u < kPassChunks; ++u) load8(p1 + chunk_col(c0, u, d), v1[u]);
+      for (int u = 0; u < kPassChunks; ++u) load8_nt(p1 + chunk_col(c0, u, d), v1[u]);
       add(v0, W ? w[t * k + j] : 1.0f);
       add(v1, W ? w[t * k + j + 1] : 1.0f);
     }
@@ -253,7 +269,7 @@ __device__ __forceinline__ void gather_rows(const TS* __restrict__ src, const fl
       const TS* p0 = src + (long)clamp_row(dr[j], R) * d;
       float v0[kPassChunks][8];
 #pragma unroll
-      for (int u = 0; u < kPassChunks; ++u) load8(p0 + chunk_col(c0, u, d), v0[u]);
+      for (int u = 0; u < kPassChunks; ++u) load8_nt(p0 + chunk_col(c0, u, d), v0[u]);
       add(v0, W ? w[t * k + j] : 1.0f);
     }
 #pragma unroll
@@ -351,9 +367,9 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const TS* __restrict__
       const TS* p1 = Ys + (long)clamp_row(dest_row[t * k + j + 1], R) * d;
       float v0[kPassChunks][8], v1[kPassChunks][8];
 #pragma unroll
-      for (int u = 0; u < kPassChunks; ++u) load8(p0 + chunk_col(c0, u, d), v0[u]);
+      for (int u = 0; u < kPassChunks; ++u) load8_nt(p0 + chunk_col(c0, u, d), v0[u]);
 #pragma unroll
-      for (int u = 0; u < kPassChunks; ++u) load8(p1 + chunk_col(c0, u, d), v1[u]);
+      for (int u = 0; u < kPassChunks; ++u) load8_nt(p1 + chunk_col(c0, u, d), v1[u]);
       slot(j, v0);
       slot(j + 1, v1);
     }
@@ -361,7 +377,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const TS* __restrict__
       const TS* p0 = Ys + (long)clamp_row(dest_row[t * k + j], R) * d;
       float v0[kPassChunks][8];
 #pragma unroll
-      for (int u = 0; u < kPassChunks; ++u) load8(p0 + chunk_col(c0, u, d), v0[u]);
+      for (int u = 0; u < kPassChunks; ++u) load8_nt(p0 + chunk_col(c0, u, d), v0[u]);
       slot(j, v0);
     }
     return;
@@ -373,7 +389,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const TS* __restrict__
     for (int c = lane * 8; c < d; c += 64 * 8) {
       float g[8], v[8];
       load8(dY + t * d + c, g);
-      load8(Ys + r * d + c, v);
+      load8_nt(Ys + r * d + c, v);
       combine_bwd_slot<TS, MXQ>(g, v, wj, r, c, dYs, q, qs, pitch, d, lane, dot);
     }
     dot = wave_sum(dot);
