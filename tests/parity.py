@@ -44,10 +44,10 @@ def relerr(gpu: np.ndarray, ref: np.ndarray) -> float:
 
 def run_gpu(wl: Workload, inp: Dict[str, np.ndarray], logits: Optional[np.ndarray] = None,
             renorm: bool = False, aux_coef: float = 0.0, wgrad_f32: bool = False,
-            wgrad_init: Optional[float] = None, mx_wgrad: bool = False):
+            wgrad_init=None, mx_wgrad: bool = False):
     """Forward + backward of the layer on the GPU; returns every buffer as numpy.
-    wgrad_init: fill the weight-gradient buffers with this value and
-    accumulate into them."""
+    wgrad_init: a value, or a dict of arrays by name ("dWg", "dWu", "dWd"),
+    to fill the weight-gradient buffers with before accumulating into them."""
     import routing_grouped_gemm_amd as rgg
     dt = torch.float32 if wl.dtype == "fp32" else torch.bfloat16
     router = wl.routing == "router"
@@ -65,7 +65,11 @@ def run_gpu(wl: Workload, inp: Dict[str, np.ndarray], logits: Optional[np.ndarra
         kw["topk_idx"] = rgg.upload(inp["topk_idx"])
         kw["topk_w"] = rgg.upload(inp["topk_w"])
     layer.forward(x, Wr, Wg, Wu, Wd, **kw)
-    if wgrad_init is not None:
+    if isinstance(wgrad_init, dict):
+        for n in ("dWg", "dWu", "dWd"):
+            t = getattr(layer, n)
+            t.copy_(torch.as_tensor(np.ascontiguousarray(wgrad_init[n], np.float32)).to(t.dtype))
+    elif wgrad_init is not None:
         for t in (layer.dWg, layer.dWu, layer.dWd):
             t.fill_(wgrad_init)
     layer.backward(dY, accumulate_wgrad=wgrad_init is not None)

@@ -246,6 +246,33 @@ def test_wgrad_f32_accumulation_keeps_small_increments(name):
         assert e <= 2e-2, (n, e)
 
 
+@pytest.mark.parametrize("name", ["mid_bf16_E64", "share_zipf_bf16", "mid_bf16_E8"])
+def test_wgrad_bf16_accumulation(name):
+    """bf16 weight gradients accumulated into buffers that hold random
+    bf16 values G0 (the same order of magnitude as dW): the result is G0 + dW
+    with one bf16 rounding, including the experts that receive no rows (Zipf
+    loads), whose gradients must keep G0."""
+    wl, inp, logits = _layer_case(name)
+    ref = run_oracle(wl, inp, logits)
+    rng = np.random.default_rng(7)
+    init = {}
+    for n in ("dWg", "dWu", "dWd"):
+        scale = float(np.sqrt(np.mean(ref[n] ** 2))) + 1e-3
+        g0 = (rng.standard_normal(ref[n].shape) * scale).astype(np.float32)
+        init[n] = torch.as_tensor(g0).to(torch.bfloat16).float().numpy()
+    gpu = run_gpu(wl, inp, logits, wgrad_init=init)
+    for n in ("dWg", "dWu", "dWd"):
+        e = relerr(gpu[n], init[n].astype(np.float64) + ref[n])
+        say(f"  {n}: relerr of G0 + dW {e:.2e}")
+        assert e <= 2e-2, (n, e)
+    if name == "share_zipf_bf16":
+        empty = np.flatnonzero(np.diff(gpu["offsets"]) == 0)
+        say(f"  empty experts {empty.tolist()}")
+        assert empty.size > 0
+        for n in ("dWg", "dWu", "dWd"):
+            np.testing.assert_array_equal(gpu[n][empty], init[n][empty])
+
+
 @pytest.mark.parametrize("name,f32", [("tiny_mxfp8", False), ("mid_mxfp8_E8", False),
                                       ("mid_mxfp8_E64", True), ("share_zipf_mxfp8", False)])
 def test_mx_weight_gradients(name, f32):
