@@ -48,8 +48,8 @@ def gemm_flops(name: str, wl) -> float:
         name = "gemm_" + name[len("gemm_mx_"):]
     if name in per_row:
         return per_row[name] * R
-    if name in ("router_logits", "router_dx", "gemm_router_logits", "gemm_router_dwr",
-                "gemm_router_dx"):
+    if name in ("router_logits", "router_dx", "router_dwr", "gemm_router_logits",
+                "gemm_router_dwr", "gemm_router_dx"):
         return 2.0 * T * d * E
     return 0.0
 
@@ -81,6 +81,7 @@ _SYMBOLS = {
     "dispatch_scatter_kernel": ["dispatch_copy"],
     "router_logits_kernel": ["router_logits"],
     "router_dx_kernel": ["router_dx"],
+    "router_dwr_kernel": ["router_dwr"],
     "mx_dispatch_kernel": ["mx_dispatch_quant"],
     "combine_kernel": ["combine"],
     "combine_bwd_kernel": ["combine_bwd"],

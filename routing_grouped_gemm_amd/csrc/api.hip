@@ -438,7 +438,12 @@ int moe_route_bwd(const void* x, const void* Wr, const float* logits, const int3
   g.M = d; g.N = E;
   g.a = x; g.lda = d;
   g.b0 = dl; g.ldb = ldl;
-  if (eng == GEMM_BF16_MFMA) {
+  if (dtype == MOE_BF16 && router_dwr_applies(d, E)) {
+    float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up((size_t)T * ld16 * 2));
+    const int S = router_dwr_launch_slices(T, d, E, router_splits(T));
+    MOE_TRY(launch_router_dwr(static_cast<const uint16_t*>(x), dl16, ld16, T, d, E, S, part, st));
+    MOE_TRY(launch_split_reduce(dtype, part, S, (long)d * E, acc, dWr, st));
+  } else if (eng == GEMM_BF16_MFMA) {
     // split K: d/256 output tiles alone would leave most of the chip idle
     const int S = router_splits(T);
     float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up((size_t)T * ld16 * 2));

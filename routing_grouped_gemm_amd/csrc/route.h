@@ -40,6 +40,15 @@ bool router_dx_applies(int d, int E);
 hipError_t launch_router_dx(const uint16_t* dl16, int ld, const uint16_t* Wr, int T, int d, int E,
                             uint16_t* dx, hipStream_t s);
 
+// Router weight-gradient partials on MFMAs (router.hip): part[s][d][E] float
+// over S token slices (router_dwr_launch_slices picks S <= max_slices), to be
+// added in slice order; dl16 as for launch_router_dx; E % 8 == 0, E <= 256,
+// d % 64 == 0.
+bool router_dwr_applies(int d, int E);
+int router_dwr_launch_slices(int T, int d, int E, int max_slices);
+hipError_t launch_router_dwr(const uint16_t* x, const uint16_t* dl16, int ld, int T, int d, int E,
+                             int S, float* part, hipStream_t s);
+
 // renorm: divide the k chosen probabilities by their sum.
 hipError_t launch_topk_softmax(const float* logits, int T, int E, int k, int renorm, int32_t* idx,
                                float* w, hipStream_t s);

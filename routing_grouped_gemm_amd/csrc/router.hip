@@ -14,6 +14,7 @@
 // own kernel.
 #include <type_traits>
 
+#include "gemm_dev.h"
 #include "hook.h"
 #include "moe_common.h"
 #include "route.h"
@@ -362,6 +363,107 @@ hipError_t launch_router_dx(const uint16_t* dl16, int ld, const uint16_t* Wr, in
       return hipErrorInvalidValue;
   }
   note_launch("router_dx", s);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// router backward, weight gradient: part[s][c][e] = sum over the tokens of
+// slice s of x[t][c] dl[t][e]  (the slices' partials are then added in order)
+// ---------------------------------------------------------------------------
+// Both operands run along the tokens (the contraction), so a workgroup (64
+// x-columns x 64 experts, one token slice) stages 64-token chunks of both as
+// token rows in LDS, in the engine's M/N-major layout (rows of 256 bytes with
+// XOR-permuted 16-byte chunks), and reads the MFMA fragments with
+// ds_read_b64_tr_b16; each wave owns a 32x32 block (32x32x16 bf16 MFMAs).
+// The next chunk is loaded into registers while the current one multiplies.
+constexpr int kRdwChunk = 64;
+
+__global__ __launch_bounds__(256) void router_dwr_kernel(const uint16_t* __restrict__ x,
+                                                         const uint16_t* __restrict__ dl16, int ld,
+                                                         int T, int d, int E, int ts,
+                                                         float* __restrict__ part) {
+  __shared__ __attribute__((aligned(1024))) char smem[2][2][16384];  // [buffer][x | dl]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c0 = blockIdx.x * 64, e0 = blockIdx.z * 64, sl = blockIdx.y;
+  const int t0 = sl * ts, t1 = min(T, t0 + ts);
+  const int nch = t1 > t0 ? (t1 - t0 + kRdwChunk - 1) / kRdwChunk : 0;
+  // fill units: operand o (x, dl), token row r of the chunk, 8-column group q
+  int uo[4], ur[4], uq[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int u = tid + 256 * i;
+    uo[i] = u >> 9;
+    ur[i] = (u >> 3) & 63;
+    uq[i] = u & 7;
+  }
+  u32x4_t v[4];
+  auto load = [&](int ch) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = t0 + ch * kRdwChunk + ur[i];
+      const long tc = min(t, T - 1);
+      const u32x4_t a = uo[i] == 0
+                            ? *reinterpret_cast<const u32x4_t*>(x + tc * d + c0 + 8 * uq[i])
+                            : *reinterpret_cast<const u32x4_t*>(dl16 + tc * ld + e0 + 8 * uq[i]);
+      v[i] = t < t1 ? a : u32x4_t{0, 0, 0, 0};
+    }
+  };
+  auto store = [&](int b) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<u32x4_t*>(smem[b][uo[i]] + mf::mn_off(ur[i], 8 * uq[i])) = v[i];
+  };
+  const int cb = (wave >> 1) * 32, eb = (wave & 1) * 32;
+  f32x16_t acc = {};
+  if (nch > 0) {
+    load(0);
+    store(0);
+    __syncthreads();
+  }
+  for (int ch = 0; ch < nch; ++ch) {
+    const bool more = ch + 1 < nch;
+    if (more) load(ch + 1);
+    const char* const xs = smem[ch & 1][0];
+    const char* const ds = smem[ch & 1][1];
+#pragma unroll
+    for (int s16 = 0; s16 < kRdwChunk / 16; ++s16) {
+      const bf16x8_t fc = mf::frag<true>(xs, cb, s16, lane);
+      const bf16x8_t fe = mf::frag<true>(ds, eb, s16, lane);
+      // D[c][e]: this lane gets column c = cb + lane%32, experts eb + 8grp + 4(lane/32) + q
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fe, fc, acc, 0, 0, 0);
+    }
+    if (more) store((ch + 1) & 1);
+    __syncthreads();
+  }
+  const int c = c0 + cb + (lane & 31);
+  if (c < d) {
+    float* const out = part + ((long)sl * d + c) * E;
+#pragma unroll
+    for (int grp = 0; grp < 4; ++grp) {
+      const int e = e0 + eb + 8 * grp + 4 * (lane >> 5);
+      if (e < E)
+        *reinterpret_cast<f32x4_t*>(out + e) =
+            f32x4_t{acc[4 * grp], acc[4 * grp + 1], acc[4 * grp + 2], acc[4 * grp + 3]};
+    }
+  }
+}
+
+bool router_dwr_applies(int d, int E) { return E % 8 == 0 && E <= 256 && d % 64 == 0; }
+
+int router_dwr_launch_slices(int T, int d, int E, int max_slices) {
+  const int blocks = (d / 64) * ((E + 63) / 64);
+  int S = (1024 + blocks - 1) / blocks;
+  if (S > max_slices) S = max_slices;
+  if (S > (T + kRdwChunk - 1) / kRdwChunk) S = (T + kRdwChunk - 1) / kRdwChunk;
+  return S < 1 ? 1 : S;
+}
+
+hipError_t launch_router_dwr(const uint16_t* x, const uint16_t* dl16, int ld, int T, int d, int E,
+                             int S, float* part, hipStream_t s) {
+  const int ts = ((T + S - 1) / S + kRdwChunk - 1) / kRdwChunk * kRdwChunk;
+  const dim3 grid(d / 64, S, (E + 63) / 64);
+  hipLaunchKernelGGL(router_dwr_kernel, grid, dim3(256), 0, s, x, dl16, ld, T, d, E, ts, part);
+  note_launch("router_dwr", s);
   return hipGetLastError();
 }
 
