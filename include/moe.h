@@ -104,7 +104,8 @@ enum moe_op {
  *   Workspace: optional.  With moe_workspace_size(MOE_OP_ROUTE, ...) bytes
  *   (non-zero for bf16 batches of at most 64 tokens with E % 8 == 0) the
  *   small-batch router runs (partial logits over slices of Wr's rows, added
- *   in slice order); without it the general one (one GEMM) does.
+ *   in slice order); without it the general one (a logits kernel over all
+ *   of Wr, then the top-k kernel) does.
  */
 int moe_route(const void* x, const void* Wr, int T, int d, int E, int k, int dtype,
               unsigned flags, float* logits, int32_t* topk_idx, float* topk_w,
