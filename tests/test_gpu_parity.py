@@ -46,6 +46,10 @@ SHAPES = {
     # expert block (E = 40) and a chunk of one 64-row piece (d = 320)
     "router_E256": ("olmoe_bf16", dict(name="router_E256", T=300, d=576, E=256, f=64, k=8)),
     "router_E40": ("olmoe_bf16", dict(name="router_E40", T=130, d=320, E=40, f=64, k=4)),
+    # eight expert blocks (128-row chunks, two 64-wide dl16 blocks) and six
+    # real blocks padded to eight (E = 96)
+    "router_E128": ("olmoe_bf16", dict(name="router_E128", T=200, d=384, E=128, f=64, k=4)),
+    "router_E96": ("olmoe_bf16", dict(name="router_E96", T=100, d=448, E=96, f=64, k=6)),
     "tiny_mxfp8": ("tiny_mxfp8", {}),
     # d = 576: an odd number of 64-deep K stages; f = 320: a half-filled last gate/up panel
     "mid_mxfp8_E8": ("olmoe_mxfp8", dict(name="mid_mxfp8_E8", T=1000, d=576, E=8, f=320, k=2)),
@@ -77,7 +81,8 @@ def test_layer_parity(name):
 
 
 @pytest.mark.parametrize("name", ["tiny_fp32", "mid_bf16_E8", "mid_bf16_E64", "edge_E6_bf16",
-                                  "router_E256", "router_E40", "wide_bf16_d2560"])
+                                  "router_E256", "router_E40", "router_E128", "router_E96",
+                                  "wide_bf16_d2560"])
 def test_router_logits_and_topk(name):
     """Router GEMM on the GPU against the oracle's logits; top-k bit-exact on
     every token whose k-th/(k+1)-th logit gap exceeds the logit error."""
