@@ -93,6 +93,8 @@ __device__ __forceinline__ void interleave8() {
 // Epilogue staging slice of one wave: 32 rows x 64 floats (256 bytes), the
 // 16-byte chunks of a row XOR-permuted by the row.
 __device__ __forceinline__ int stage8_off(int r, int chunk) { return r * 256 + ((chunk ^ (r & 15)) << 4); }
+// bf16 staging of the same block: 128 bytes a row, chunk c of row r at c ^ (r & 7)
+__device__ __forceinline__ int stage8_bf_off(int r, int chunk) { return r * 128 + ((chunk ^ (r & 7)) << 4); }
 
 // One 32-row block (I) of a wave's 128x64 sub-tile.
 template <int KIND, int I>
@@ -138,6 +140,37 @@ __device__ __forceinline__ void epilogue8_block(const GemmArgs& g, const Tile& t
         hg[it] = *reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(g.h0) + off);
         hu[it] = *reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(g.h1) + off);
       }
+    }
+  }
+  // Plain bf16 stores that do not accumulate: rounded to bf16 in registers
+  // and staged as bf16, 128 bytes a row (half the LDS traffic; the same
+  // rounding, so the same bytes).
+  constexpr bool BF_STAGE = EPI == EPI_STORE || EPI == EPI_WGRAD_SPLIT;
+  if constexpr (BF_STAGE) {
+    if (!g.accumulate) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int grp = 0; grp < 4; ++grp) {
+          const int r = lane & 31;
+          const uint2 w = make_uint2(pack_bf16x2(acc[I][j][4 * grp], acc[I][j][4 * grp + 1]),
+                                     pack_bf16x2(acc[I][j][4 * grp + 2], acc[I][j][4 * grp + 3]));
+          *reinterpret_cast<uint2*>(slice + stage8_bf_off(r, 4 * j + grp) + 8 * (lane >> 5)) = w;
+        }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int r = it * 8 + (lane >> 3);
+        const int m = wm * 128 + I * 32 + r;
+        const int n = t.n0 + wn * 64 + cc;
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(slice + stage8_bf_off(r, lane & 7));
+        if (m < t.mlim && n < g.N) {
+          const long row = (g.ragged == RAG_M) ? (long)t.row0 + m : (long)t.m0 + m;
+          __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(epi_ptr<EPI>(g, t, row, n)));
+        }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      return;
     }
   }
 #pragma unroll

@@ -640,6 +640,9 @@ __device__ __forceinline__ void plan_tile(const GemmArgs& g, const Tile& t, int 
 // one chunk) and the row reads (one row, 16 chunks) avoid bank conflicts.
 constexpr int EPI_SLICE = 16384;
 __device__ __forceinline__ int stage_off(int r, int chunk) { return r * 512 + ((chunk ^ (r & 31)) << 4); }
+// bf16 staging of the same block: 32 rows x 128 columns, 256 bytes a row,
+// 16-byte chunk c of row r at chunk c ^ (r & 15).
+__device__ __forceinline__ int stage_bf_off(int r, int chunk) { return r * 256 + ((chunk ^ (r & 15)) << 4); }
 
 // Epilogue of one 8-column piece: v = tile values (gate for the SwiGLU
 // forward), u = up values (SwiGLU forward only).  grow: global row (RAG_M)
@@ -768,6 +771,41 @@ __device__ __forceinline__ void epilogue_block(const GemmArgs& g, const Tile& t,
           hg[it] = *reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(g.h0) + off);
           hu[it] = *reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(g.h1) + off);
         }
+      }
+    }
+    // Plain bf16 stores that do not accumulate: the accumulators are rounded
+    // to bf16 in registers and staged as bf16 (half the LDS traffic of the
+    // float32 staging below; the same rounding, so the same bytes).  Not in
+    // the MXFP8 engine, whose registers this second store path overflows.
+    constexpr bool MX_KIND = (KIND >= GK_MX_GATEUP && KIND <= GK_MX_DGRAD_GATEUP) ||
+                             KIND == GK_MX_WGRAD || KIND == GK_MX_WGRAD_F32;
+    constexpr bool BF_STAGE = !MX_KIND && (EPI == EPI_STORE || EPI == EPI_WGRAD_SPLIT);
+    if constexpr (BF_STAGE) {
+      if (!g.accumulate) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int grp = 0; grp < 4; ++grp) {
+            const int r = lane & 31;
+            const uint2 w = make_uint2(pack_bf16x2(acc[I][j][4 * grp], acc[I][j][4 * grp + 1]),
+                                       pack_bf16x2(acc[I][j][4 * grp + 2], acc[I][j][4 * grp + 3]));
+            *reinterpret_cast<uint2*>(slice + stage_bf_off(r, 4 * j + grp) + 8 * (lane >> 5)) = w;
+          }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll 2
+        for (int it = 0; it < 8; ++it) {
+          const int r = it * 4 + (lane >> 4);
+          const int c = (lane & 15) * 8;
+          const int m = wm * 128 + I * 32 + r;
+          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(slice + stage_bf_off(r, lane & 15));
+          const int n = t.n0 + wn * 128 + c;
+          if (m < t.mlim && n < g.N) {
+            const long row = (g.ragged == RAG_M) ? (long)t.row0 + m : (long)t.m0 + m;
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(epi_ptr<EPI>(g, t, row, n)));
+          }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        return;
       }
     }
 #pragma unroll
