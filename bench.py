@@ -10,10 +10,11 @@ combine, then combine backward -> grouped FFN backward -> dispatch backward
     python bench.py [--steps K] [--warmup W] [--workload NAME]
 
 Prints one JSON line.  `value` is tokens per second of the whole layer
-(forward + backward).  Per-kernel durations come from HIP events recorded on
-the library's stream after every kernel launch inside the timed region; the
-dominant kernel gives the `roofline` object.  `cpu_baseline` times the CPU
-oracle on a bounded sample of the same workload.
+(forward + backward).  A few untimed steps with a HIP event after every
+kernel give the per-kernel table and name the dominant kernel; inside the
+timed region only that kernel's launches are bracketed by HIP events on the
+library's stream, and their mean duration gives the `roofline` object.
+`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -278,10 +279,31 @@ def main(argv=None) -> int:
         step()
     torch.cuda.synchronize()
 
+    # Kernel table (untimed): an event after every kernel of a few steps
+    # gives each kernel's share of a step, and names the dominant kernel.
+    P = max(1, min(args.steps, 10))
+    full = rgg.KernelTimer(capacity=P * 32)
+    with full:
+        for _ in range(P):
+            step()
+    per = {}
+    for name, dur in full.durations():
+        c = per.setdefault(name, [0, 0.0])
+        c[0] += 1
+        c[1] += dur
+    table = sorted(((n, c[0] / P, c[1] / P, c[1] / c[0]) for n, c in per.items()),
+                   key=lambda r: -r[2])
+    # expert FFN time: the expert GEMMs, and for MXFP8 also the quantizers
+    gemm_ms = sum(r[2] for r in table if (r[0].startswith("gemm_") and "router" not in r[0])
+                  or r[0].startswith("mx_"))
+    dom_name = table[0][0]
+
+    # Timed region: K steps; events only right before and after each launch
+    # of the dominant kernel, so that the other kernels run back to back.
     K = args.steps
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
-    timer = rgg.KernelTimer(capacity=K * 32)
+    timer = rgg.KernelTimer(capacity=K * 8, only=dom_name)
     torch.cuda.synchronize()
     marks = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
     w0 = time.perf_counter()
@@ -296,20 +318,10 @@ def main(argv=None) -> int:
     wall = time.perf_counter() - w0
     ms = t_start.elapsed_time(t_end) / K
     step_ms = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(K)])
-    kern = timer.durations()
-
-    per = {}
-    for name, dur in kern:
-        c = per.setdefault(name, [0, 0.0])
-        c[0] += 1
-        c[1] += dur
-    table = sorted(((n, c[0] / K, c[1] / K, c[1] / c[0]) for n, c in per.items()),
-                   key=lambda r: -r[2])
-    # expert FFN time: the expert GEMMs, and for MXFP8 also the quantizers
-    gemm_ms = sum(r[2] for r in table if (r[0].startswith("gemm_") and "router" not in r[0])
-                  or r[0].startswith("mx_"))
-    dom = table[0]
-    dom_name, dom_launch_ms = dom[0], dom[3]
+    dom_runs = [dur for _, dur in timer.durations()]
+    if not dom_runs:
+        raise RuntimeError(f"bench: no launch of {dom_name} was timed")
+    dom_launch_ms = float(np.mean(dom_runs))
     dom_flops = gemm_flops(dom_name, wl)
     peak = PEAK_TFLOPS[wl.prec]
     # a kernel is priced at the peak of its own operand type: the scaled fp8
@@ -320,7 +332,7 @@ def main(argv=None) -> int:
         roof = {"bound": "mfma", "kernel": dom_name, "achieved": round(ach, 2), "peak": dom_peak,
                 "unit": "TFLOP/s", "frac": round(ach / dom_peak, 4),
                 "traffic": measured_traffic(wl.name, dom_name),
-                "per_launch_ms": round(dom_launch_ms, 4),
+                "per_launch_ms": round(dom_launch_ms, 4), "timed_launches": len(dom_runs),
                 "algorithmic_flops_per_launch": dom_flops}
     else:
         roof = {"bound": "hbm", "kernel": dom_name, "achieved": None, "peak": HBM_PEAK_GBS,
@@ -451,14 +463,23 @@ def bench_forward(args, wl, inp, dev) -> int:
         c[1] += dur
     table = sorted(((n, c[0] / K, c[1] / K, c[1] / c[0]) for n, c in per.items()),
                    key=lambda r: -r[2])
-    dom_name, dom_launch_ms = table[0][0], table[0][3]
+    dom_name = table[0][0]
+    # the dominant kernel alone, bracketed by events, over K eager forwards
+    only = rgg.KernelTimer(capacity=K * 8, only=dom_name)
+    with only:
+        for i in range(K):
+            fwd()
+    dom_runs = [dur for _, dur in only.durations()]
+    if not dom_runs:
+        raise RuntimeError(f"bench: no launch of {dom_name} was timed")
+    dom_launch_ms = float(np.mean(dom_runs))
     nbytes = fwd_gemm_bytes(dom_name, wl, active)
     if nbytes > 0:
         ach = nbytes / (dom_launch_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "kernel": dom_name, "achieved": round(ach, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
                 "traffic": measured_traffic(wl.name, dom_name),
-                "per_launch_ms": round(dom_launch_ms, 4),
+                "per_launch_ms": round(dom_launch_ms, 4), "timed_launches": len(dom_runs),
                 "algorithmic_bytes_per_launch": nbytes}
     else:
         roof = {"bound": "hbm", "kernel": dom_name, "achieved": None, "peak": HBM_PEAK_GBS,

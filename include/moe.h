@@ -270,16 +270,31 @@ const char* moe_last_launch_error(void);
 
 /*
  * moe_set_kernel_events -- per-kernel timing hook (observability only).
- * While set, every kernel launched by an entry point on the calling thread
+ * While set (and no filter is set, see moe_set_kernel_filter), every kernel
+ * launched by an entry point on the calling thread
  * is followed by hipEventRecord(events[i], stream), i = 0, 1, ... up to
  * `capacity`, and names[i] (when names is not NULL) receives a static label
  * of that kernel; *count (when not NULL) tracks how many were recorded.
  * The events are caller-created hipEvent_t handles.  If a record fails the
  * hook switches itself off and *count becomes -(HIP error code); the kernel
- * launches are not affected.  Pass events = NULL to switch the hook off.  This thread-local hook is the only state the library
+ * launches are not affected.  Pass events = NULL to switch the hook off.
+ * This thread-local hook, with its filter, is the only state the library
  * keeps between calls; it is off by default.
  */
 int moe_set_kernel_events(void* const* events, const char** names, int capacity, int* count);
+
+/*
+ * moe_set_kernel_filter -- narrows the timing hook to one kernel (observability
+ * only).  With `name` set (a label as moe_set_kernel_events reports it, at most
+ * 63 characters, copied), the hook records, for each launch of that kernel on
+ * the calling thread, one event right before it and one right after it
+ * (events[2i] and events[2i+1], both labelled), and nothing for other kernels,
+ * so that the rest of the work runs without events between its kernels.
+ * NULL (the default) times every kernel again.  Returns MOE_ERR_SHAPE for a
+ * longer name (the filter is then unchanged).  The filter is thread-local and
+ * outlives moe_set_kernel_events calls.
+ */
+int moe_set_kernel_filter(const char* name);
 
 #ifdef __cplusplus
 }

@@ -74,6 +74,8 @@ def lib() -> ctypes.CDLL:
             fn.restype = ctypes.c_int
         L.moe_set_kernel_events.argtypes = [_P, _P, _I, _P]
         L.moe_set_kernel_events.restype = ctypes.c_int
+        L.moe_set_kernel_filter.argtypes = [ctypes.c_char_p]
+        L.moe_set_kernel_filter.restype = ctypes.c_int
         L.moe_last_launch_error.argtypes = []
         L.moe_last_launch_error.restype = ctypes.c_char_p
         L.moe_status_string.argtypes = [ctypes.c_int]
@@ -242,10 +244,14 @@ def moe_route_aux(logits, counts, k, coef, aux_loss, aux_dp, ws, stream=None):
 
 class KernelTimer:
     """Per-kernel durations through moe_set_kernel_events: a start event, then
-    one event after every kernel the library launches on this thread."""
+    one event after every kernel the library launches on this thread.  With
+    only="<label>" (moe_set_kernel_filter), just that kernel is timed, by an
+    event right before and one right after each of its launches, and the
+    other kernels run with no events between them."""
 
-    def __init__(self, capacity: int = 4096):
+    def __init__(self, capacity: int = 4096, only: str | None = None):
         self.capacity = capacity
+        self.only = only
         self.events = [torch.cuda.Event(enable_timing=True) for _ in range(capacity)]
         self.start = torch.cuda.Event(enable_timing=True)
         self._names = (ctypes.c_char_p * capacity)()
@@ -262,12 +268,15 @@ class KernelTimer:
             raise RuntimeError("KernelTimer: torch did not create the HIP events")
         self._handles = (ctypes.c_void_p * self.capacity)(*handles)
         self.start.record()
+        _check(lib().moe_set_kernel_filter(self.only.encode() if self.only else None),
+               "moe_set_kernel_filter")
         _check(lib().moe_set_kernel_events(self._handles, self._names, self.capacity,
                                            ctypes.byref(self._count)), "moe_set_kernel_events")
         return self
 
     def __exit__(self, *exc):
         lib().moe_set_kernel_events(None, None, 0, None)
+        lib().moe_set_kernel_filter(None)
         return False
 
     def durations(self):
@@ -275,6 +284,9 @@ class KernelTimer:
         torch.cuda.synchronize()
         if self._count.value < 0:
             raise RuntimeError(f"KernelTimer: hipEventRecord failed (HIP error {-self._count.value})")
+        if self.only:
+            return [(self._names[i].decode(), self.events[i].elapsed_time(self.events[i + 1]))
+                    for i in range(0, self._count.value, 2)]
         out, prev = [], self.start
         for i in range(self._count.value):
             out.append((self._names[i].decode(), prev.elapsed_time(self.events[i])))

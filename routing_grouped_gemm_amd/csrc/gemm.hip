@@ -348,6 +348,7 @@ hipError_t launch_kind(int dtype, const GemmArgs& g, int num_cu, hipStream_t str
     int ub = tiles_upper_bound(g, mf::BM, BNT);
     int grid = min(num_cu, ub);
     if (grid <= 0) return hipSuccess;
+    note_prelaunch(kind_name(KIND, g), stream);
     if constexpr (KIND == GK_WGRAD) {  // eight-wave form (gemm8.hip)
       if (hipError_t e = launch_gemm8(static_cast<GemmKind>(KIND), g, grid, stream); e != hipSuccess)
         return e;
@@ -358,6 +359,7 @@ hipError_t launch_kind(int dtype, const GemmArgs& g, int num_cu, hipStream_t str
     int ub = tiles_upper_bound(g, st::BM, st::BN);
     int grid = min(num_cu * 8, ub);
     if (grid <= 0) return hipSuccess;
+    note_prelaunch(kind_name(KIND, g), stream);
     if (dtype == GEMM_F32_SIMT)
       hipLaunchKernelGGL((st::gemm_simt_kernel<KIND, float>), dim3(grid), dim3(st::NTHR), 0, stream, g);
     else

@@ -1,34 +1,58 @@
-// Per-kernel timing hook (see moe_set_kernel_events in include/moe.h).
+// Per-kernel timing hook (see moe_set_kernel_events and moe_set_kernel_filter
+// in include/moe.h).
+#include <string.h>
+
 #include "../../include/moe.h"
 #include "hook.h"
 
 namespace {
+constexpr int kFilterMax = 64;  // longest filter name, with its terminating 0
 struct Hook {
   hipEvent_t const* events = nullptr;
   const char** names = nullptr;
   int capacity = 0;
   int* count = nullptr;
   int n = 0;
+  char only[kFilterMax] = {};  // empty: every kernel
+  bool pending = false;        // filter: events[n] holds a start not yet closed
 };
 thread_local Hook g_hook;
+
+// A failed record switches the hook off and reports -(HIP error) through
+// *count; the error is cleared so that it cannot be mistaken for a failure of
+// the kernel launch around it.
+bool record(Hook& h, int i, const char* name, hipStream_t stream) {
+  if (h.names) h.names[i] = name;
+  hipError_t e = hipEventRecord(h.events[i], stream);
+  if (e == hipSuccess) return true;
+  (void)hipGetLastError();
+  if (h.count) *h.count = -static_cast<int>(e);
+  h.events = nullptr;
+  h.pending = false;
+  return false;
+}
 }  // namespace
 
 namespace moe {
-// A failed record switches the hook off and reports -(HIP error) through
-// *count; the error is cleared so that it cannot be mistaken for a failure of
-// the kernel launch that precedes it.
+void note_prelaunch(const char* name, hipStream_t stream) {
+  Hook& h = g_hook;
+  if (!h.events || !h.only[0] || strcmp(name, h.only) != 0 || h.n + 2 > h.capacity) return;
+  // a start left open (a launch that returned early) is overwritten
+  h.pending = record(h, h.n, name, stream);
+}
+
 void note_launch(const char* name, hipStream_t stream) {
   Hook& h = g_hook;
-  if (!h.events || h.n >= h.capacity) return;
-  if (h.names) h.names[h.n] = name;
-  hipError_t e = hipEventRecord(h.events[h.n], stream);
-  if (e != hipSuccess) {
-    (void)hipGetLastError();
-    if (h.count) *h.count = -static_cast<int>(e);
-    h.events = nullptr;
-    return;
+  if (!h.events) return;
+  if (h.only[0]) {
+    if (!h.pending || strcmp(name, h.only) != 0) return;
+    h.pending = false;
+    if (!record(h, h.n + 1, name, stream)) return;
+    h.n += 2;
+  } else {
+    if (h.n >= h.capacity || !record(h, h.n, name, stream)) return;
+    ++h.n;
   }
-  ++h.n;
   if (h.count) *h.count = h.n;
 }
 }  // namespace moe
@@ -41,6 +65,17 @@ extern "C" int moe_set_kernel_events(void* const* events, const char** names, in
   g_hook.capacity = events ? capacity : 0;
   g_hook.count = count;
   g_hook.n = 0;
+  g_hook.pending = false;
   if (count) *count = 0;
+  return MOE_OK;
+}
+
+extern "C" int moe_set_kernel_filter(const char* name) {
+  if (name && strlen(name) >= static_cast<size_t>(kFilterMax)) return MOE_ERR_SHAPE;
+  if (name)
+    strcpy(g_hook.only, name);
+  else
+    g_hook.only[0] = 0;
+  g_hook.pending = false;
   return MOE_OK;
 }

@@ -500,6 +500,7 @@ hipError_t launch_mx_kind(const GemmArgs& g, int num_cu, hipStream_t s) {
                                     : ((long)g.rows_total / mf::BM + ngroups(g)) * ntn;
   const int grid = (int)(ub < num_cu ? ub : (long)num_cu);
   if (grid <= 0) return hipSuccess;
+  note_prelaunch(mx_name(KIND, g), s);
   hipLaunchKernelGGL(mf::gemm_mx_kernel<KIND>, dim3(grid), dim3(mf::NTHR), 0, s, g);
   note_launch(mx_name(KIND, g), s);
   return hipGetLastError();
@@ -529,6 +530,7 @@ hipError_t quant_rows(const void* src, long nrows, int K, long src_ld, uint8_t* 
                       long col0, uint8_t* scale, long grows, long sg_stride, long pitch, int block0,
                       hipStream_t s) {
   if (nrows <= 0) return hipSuccess;
+  note_prelaunch("mx_quant_rows", s);
   hipLaunchKernelGGL(mx_quant_rows_kernel, dim3((unsigned)((nrows + 3) / 4)), dim3(256), 0, s,
                      static_cast<const bf16_t*>(src), nrows, K, src_ld, dst, dst_ld, col0, scale,
                      grows, sg_stride, pitch, block0);
@@ -538,6 +540,7 @@ hipError_t quant_rows(const void* src, long nrows, int K, long src_ld, uint8_t* 
 
 hipError_t quant_cols(const void* W, int E, int K, int N, uint8_t* dst, long dst_es, int half,
                       uint8_t* scale, long s_es, long pitch, hipStream_t s) {
+  note_prelaunch("mx_quant_cols", s);
   hipLaunchKernelGGL(mx_quant_cols_kernel, dim3((N + 63) / 64, (K + 63) / 64, E), dim3(256), 0, s,
                      static_cast<const bf16_t*>(W), K, N, dst, dst_es, half, scale, s_es, pitch);
   note_launch("mx_quant_cols", s);
@@ -644,6 +647,7 @@ size_t mx_wgrad_workspace(long long R, int d, int f, int E) {
 hipError_t launch_mx_dispatch_copy(const void* x, const int32_t* src_token, int R, int T, int d,
                                    void* Xs, void* Xq, uint8_t* Xq_scale, hipStream_t s) {
   if (R == 0) return hipSuccess;
+  note_prelaunch("mx_dispatch_quant", s);
   hipLaunchKernelGGL(mx_dispatch_kernel, dim3((R + 3) / 4), dim3(256), 0, s,
                      static_cast<const bf16_t*>(x), src_token, R, T, d, static_cast<bf16_t*>(Xs),
                      static_cast<uint8_t*>(Xq), Xq_scale, pitch_rows(R));
@@ -716,6 +720,7 @@ namespace {
 hipError_t quant_tokens(const void* src, int C, long src_ld, const int32_t* offsets,
                         const int32_t* poff, int E, long Kp, uint8_t* dst, uint8_t* scale,
                         hipStream_t s) {
+  note_prelaunch("mx_quant_tokens", s);
   hipLaunchKernelGGL(mx_quant_tokens_kernel, dim3(C / 64, (unsigned)(Kp / 64)), dim3(256), 0, s,
                      static_cast<const bf16_t*>(src), C, src_ld, offsets, poff, E, dst, Kp, scale);
   note_launch("mx_quant_tokens", s);
@@ -729,6 +734,7 @@ hipError_t mx_ffn_wgrad(const void* Xs, const void* dH, const void* A, const voi
                         hipStream_t s) {
   const WgradWs w = carve_wgrad(ws, mx_bwd_workspace(R, d, f, E), R, d, f, E, nullptr);
   const long Kp = wgrad_kp(R, E);
+  note_prelaunch("mx_pad_offsets", s);
   hipLaunchKernelGGL(mx_pad_offsets_kernel, dim3(1), dim3(64), 0, s, offsets, E, w.poff);
   note_launch("mx_pad_offsets", s);
   MX_TRY(hipGetLastError());

@@ -553,6 +553,7 @@ __global__ __launch_bounds__(256) void aux_final_kernel(const float* __restrict_
 hipError_t launch_topk_softmax(const float* logits, int T, int E, int k, int renorm, int32_t* idx,
                                float* w, hipStream_t s) {
   if (T == 0) return hipSuccess;
+  note_prelaunch("topk_softmax", s);
   hipLaunchKernelGGL(topk_softmax_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k,
                      renorm, idx, w);
   note_launch("topk_softmax", s);
@@ -563,12 +564,15 @@ hipError_t launch_dispatch_meta(const int32_t* idx, int T, int E, int k, int32_t
                                 int32_t* base, int32_t* counts, int32_t* offsets,
                                 int32_t* dest_row, int32_t* src_token, hipStream_t s) {
   const int nblk = (T + 63) / 64;
+  note_prelaunch("block_hist", s);
   hipLaunchKernelGGL(block_hist_kernel, dim3(nblk), dim3(64), 0, s, idx, T, E, k, nblk, hist);
   note_launch("block_hist", s);
   MOE_LAUNCH_CHECK();
+  note_prelaunch("expert_scan", s);
   hipLaunchKernelGGL(scan_kernel, dim3(E), dim3(256), 0, s, hist, nblk, base, counts);
   note_launch("expert_scan", s);
   MOE_LAUNCH_CHECK();
+  note_prelaunch("rank", s);
   hipLaunchKernelGGL(rank_kernel, dim3(nblk), dim3(64), 0, s, idx, T, E, k, nblk, base, counts,
                      offsets, dest_row, src_token);
   note_launch("rank", s);
@@ -578,6 +582,7 @@ hipError_t launch_dispatch_meta(const int32_t* idx, int T, int E, int k, int32_t
 template <typename TS>
 static hipError_t copy_impl(const void* x, const int32_t* dest, int T, int d, int k, void* Xs,
                             hipStream_t s) {
+  note_prelaunch("dispatch_copy", s);
   hipLaunchKernelGGL(dispatch_scatter_kernel<TS>, dim3((T + 3) / 4), dim3(256), 0, s,
                      static_cast<const TS*>(x), dest, T, d, k, static_cast<TS*>(Xs));
   note_launch("dispatch_copy", s);
@@ -594,6 +599,7 @@ hipError_t launch_dispatch_copy(int dtype, const void* x, const int32_t* dest_ro
 hipError_t launch_combine(int dtype, const void* Ys, const float* w, const int32_t* dest, int T,
                           int d, int k, void* y, hipStream_t s) {
   dim3 grid((T + 3) / 4);
+  note_prelaunch("combine", s);
   if (dtype)
     hipLaunchKernelGGL(combine_kernel<bf16_t>, grid, dim3(256), 0, s,
                        static_cast<const bf16_t*>(Ys), w, dest, T, d, k, static_cast<bf16_t*>(y));
@@ -609,6 +615,7 @@ hipError_t launch_combine_bwd(int dtype, const void* dY, const void* Ys, const f
                               void* dYs_q, uint8_t* dYs_q_scale, hipStream_t s) {
   dim3 grid((T + 3) / 4);
   const long pitch = ((long)T * k + 15) / 16 * 16;
+  note_prelaunch("combine_bwd", s);
   if (dtype && dYs_q)
     hipLaunchKernelGGL((combine_bwd_kernel<bf16_t, true>), grid, dim3(256), 0, s,
                        static_cast<const bf16_t*>(dY), static_cast<const bf16_t*>(Ys), w, dest,
@@ -665,6 +672,7 @@ hipError_t launch_split_reduce(int dtype, const float* part, int S, long n, int 
                                void* out, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   const dim3 grid((unsigned)((n + 255) / 256));
+  note_prelaunch("router_dwr_reduce", s);
   if (dtype)
     hipLaunchKernelGGL(split_reduce_kernel<bf16_t>, grid, dim3(64), 0, s, part, S, n, accumulate,
                        static_cast<bf16_t*>(out));
@@ -678,6 +686,7 @@ hipError_t launch_split_reduce(int dtype, const float* part, int S, long n, int 
 hipError_t launch_gather_sum(int dtype, const void* dXs, const int32_t* dest, int T, int d, int k,
                              int accumulate, void* dx, hipStream_t s) {
   dim3 grid((T + 3) / 4);
+  note_prelaunch("gather_sum", s);
   if (dtype)
     hipLaunchKernelGGL(gather_sum_kernel<bf16_t>, grid, dim3(256), 0, s,
                        static_cast<const bf16_t*>(dXs), dest, T, d, k, accumulate,
@@ -693,6 +702,7 @@ hipError_t launch_gather_sum(int dtype, const void* dXs, const int32_t* dest, in
 hipError_t launch_router_bwd_softmax(const float* logits, const int32_t* idx, const float* dw,
                                      int T, int E, int k, int renorm, const float* aux_dp,
                                      float* dl, bf16_t* dl16, int ld16, hipStream_t s) {
+  note_prelaunch("router_bwd_softmax", s);
   hipLaunchKernelGGL(router_bwd_softmax_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, idx,
                      dw, T, E, k, renorm, aux_dp, dl, dl16, ld16);
   note_launch("router_bwd_softmax", s);
@@ -706,9 +716,11 @@ namespace moe {
 hipError_t launch_router_aux(const float* logits, const int32_t* counts, int T, int E, int k,
                              float coef, float* part, float* loss, float* dp, hipStream_t s) {
   const int nblk = (T + 63) / 64;
+  note_prelaunch("router_aux_partial", s);
   hipLaunchKernelGGL(aux_partial_kernel, dim3(nblk), dim3(256), 0, s, logits, T, E, part);
   note_launch("router_aux_partial", s);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  note_prelaunch("router_aux_final", s);
   hipLaunchKernelGGL(aux_final_kernel, dim3(1), dim3(256), 0, s, part, nblk, counts, T, E, k, coef,
                      loss, dp);
   note_launch("router_aux_final", s);

@@ -216,6 +216,7 @@ hipError_t launch_router_logits(const uint16_t* x, const uint16_t* Wr, int T, in
   const dim3 grid((T + kRlTokens - 1) / kRlTokens);
   const int nb = (E + 15) / 16;
   // expert blocks rounded up to a power of two (the padding experts are zero)
+  note_prelaunch("router_logits", s);
   if (nb <= 1)
     hipLaunchKernelGGL(router_logits_kernel<1>, grid, dim3(256), rl_lds(1), s, x, Wr, T, d, E, logits);
   else if (nb <= 2)
@@ -346,6 +347,7 @@ hipError_t launch_router_dx(const uint16_t* dl16, int ld, const uint16_t* Wr, in
   int P = 2;
   while (2 * P <= d / 64 && (long)tiles * 2 * P < 4096) P *= 2;
   const dim3 grid(tiles, P / 2);
+  note_prelaunch("router_dx", s);
   switch (ld / 32) {
     case 2:
       hipLaunchKernelGGL(router_dx_kernel<2>, grid, dim3(256), 0, s, dl16, ld, Wr, T, d, E, dx);
@@ -462,6 +464,7 @@ hipError_t launch_router_dwr(const uint16_t* x, const uint16_t* dl16, int ld, in
                              int S, float* part, hipStream_t s) {
   const int ts = ((T + S - 1) / S + kRdwChunk - 1) / kRdwChunk * kRdwChunk;
   const dim3 grid(d / 64, S, (E + 63) / 64);
+  note_prelaunch("router_dwr", s);
   hipLaunchKernelGGL(router_dwr_kernel, grid, dim3(256), 0, s, x, dl16, ld, T, d, E, ts, part);
   note_launch("router_dwr", s);
   return hipGetLastError();

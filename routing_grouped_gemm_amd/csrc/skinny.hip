@@ -268,12 +268,14 @@ hipError_t launch_skinny_ffn_fwd(const int* offsets, int E, int R, int d, int f,
   g.S = skinny_splits(E, R, d, f / 64); g.kc = d / g.S;
   g.c0 = Hg; g.c1 = Hu; g.c2 = A; g.ldc = f;
   g.part = ws; g.part_ld = 2L * f;
+  note_prelaunch("skinny_fwd_gateup", st);
   hipLaunchKernelGGL(sk::skinny_kernel<0>, dim3(f / 64, g.S, E), dim3(sk::NTHR), 0, st, g);
   note_launch("skinny_fwd_gateup", st);
   if (hipError_t err = hipGetLastError(); err != hipSuccess) return err;
   if (g.S > 1) {
     const long n = (long)R * (f / 8);
     const int blocks = (int)((n + 255) / 256 < 2048 ? (n + 255) / 256 : 2048);
+    note_prelaunch("skinny_reduce_gateup", st);
     hipLaunchKernelGGL(sk::skinny_reduce_kernel<0>, dim3(blocks), dim3(256), 0, st, g);
     note_launch("skinny_reduce_gateup", st);
     if (hipError_t err = hipGetLastError(); err != hipSuccess) return err;
@@ -285,6 +287,7 @@ hipError_t launch_skinny_ffn_fwd(const int* offsets, int E, int R, int d, int f,
   h.S = skinny_splits(E, R, f, (d + 127) / 128); h.kc = f / h.S;
   h.c0 = Ys; h.ldc = d;
   h.part = ws; h.part_ld = d;
+  note_prelaunch("skinny_fwd_down", st);
   hipLaunchKernelGGL(sk::skinny_kernel<1>, dim3((d + 127) / 128, h.S, E), dim3(sk::NTHR), 0, st,
                      h);
   note_launch("skinny_fwd_down", st);
@@ -292,6 +295,7 @@ hipError_t launch_skinny_ffn_fwd(const int* offsets, int E, int R, int d, int f,
   if (h.S > 1) {
     const long n = (long)R * (d / 8);
     const int blocks = (int)((n + 255) / 256 < 2048 ? (n + 255) / 256 : 2048);
+    note_prelaunch("skinny_reduce_down", st);
     hipLaunchKernelGGL(sk::skinny_reduce_kernel<1>, dim3(blocks), dim3(256), 0, st, h);
     note_launch("skinny_reduce_down", st);
   }

@@ -274,10 +274,12 @@ hipError_t launch_route_small(const uint16_t* x, const uint16_t* Wr, int T, int 
                               int renorm, float* part, float* logits, int32_t* idx, float* w,
                               hipStream_t s) {
   const int P = (d + kRouteSlice - 1) / kRouteSlice;
+  note_prelaunch("route_small_part", s);
   hipLaunchKernelGGL(route_part_kernel, dim3(P, (T + 3) / 4), dim3(256), 0, s, x, Wr, T, d, E,
                      part);
   note_launch("route_small_part", s);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  note_prelaunch("route_small_final", s);
   hipLaunchKernelGGL(route_final_kernel, dim3((T + 3) / 4), dim3(256), 0, s, part, P, T, E, k,
                      renorm, logits, idx, w);
   note_launch("route_small_final", s);
@@ -291,6 +293,7 @@ hipError_t launch_dispatch_small(int dtype, const void* x, const int32_t* idx, i
                                  int32_t* src_token, void* Xs, hipStream_t s) {
   const int R = T * k;
   const int blocks = max(1, min(256, (R + 7) / 8));
+  note_prelaunch("dispatch_small", s);
   if (dtype)
     hipLaunchKernelGGL(dispatch_small_kernel<bf16_t>, dim3(blocks), dim3(256), 0, s,
                        static_cast<const bf16_t*>(x), idx, T, d, E, k, counts, offsets, dest_row,
@@ -308,6 +311,7 @@ bool combine_small_applies(int T) { return T <= kSmallMaxTokens; }
 hipError_t launch_combine_small(int dtype, const void* Ys, const float* w, const int32_t* dest,
                                 int T, int d, int k, void* y, hipStream_t s) {
   dim3 grid((d + 2047) / 2048, T);
+  note_prelaunch("combine_small", s);
   if (dtype)
     hipLaunchKernelGGL(combine_small_kernel<bf16_t>, grid, dim3(256), 0, s,
                        static_cast<const bf16_t*>(Ys), w, dest, T, d, k, static_cast<bf16_t*>(y));

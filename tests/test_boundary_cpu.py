@@ -36,7 +36,7 @@ def declared_entry_points():
 
 def test_exports_every_declared_symbol(L):
     names = declared_entry_points()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     for n in names:
         assert hasattr(L, n), n
 
@@ -49,6 +49,11 @@ def test_kernel_event_hook_switches(L):
     assert L.moe_set_kernel_events(ev, None, 0, None) == SHAPE
     assert L.moe_set_kernel_events(ev, None, 4, ctypes.byref(cnt)) == OK and cnt.value == 0
     assert L.moe_set_kernel_events(None, None, 0, None) == OK
+    # the name filter is copied; a name of 64 characters or more is refused
+    assert L.moe_set_kernel_filter(b"gemm_fwd_gateup_swiglu") == OK
+    assert L.moe_set_kernel_filter(b"x" * 63) == OK
+    assert L.moe_set_kernel_filter(b"x" * 64) == SHAPE
+    assert L.moe_set_kernel_filter(None) == OK
 
 
 def test_status_strings(L):
