@@ -282,12 +282,15 @@ def main(argv=None) -> int:
     # Kernel table (untimed): an event after every kernel of a few steps
     # gives each kernel's share of a step, and names the dominant kernel.
     P = max(1, min(args.steps, 10))
-    full = rgg.KernelTimer(capacity=P * 32)
+    full = rgg.KernelTimer(capacity=P * 64)
     with full:
         for _ in range(P):
             step()
+    kern = full.durations()
+    if len(kern) >= full.capacity:
+        raise RuntimeError("bench: the kernel table filled its event capacity (launches lost)")
     per = {}
-    for name, dur in full.durations():
+    for name, dur in kern:
         c = per.setdefault(name, [0, 0.0])
         c[0] += 1
         c[1] += dur
@@ -319,8 +322,9 @@ def main(argv=None) -> int:
     ms = t_start.elapsed_time(t_end) / K
     step_ms = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(K)])
     dom_runs = [dur for _, dur in timer.durations()]
-    if not dom_runs:
-        raise RuntimeError(f"bench: no launch of {dom_name} was timed")
+    if not dom_runs or 2 * len(dom_runs) + 2 > timer.capacity:
+        raise RuntimeError(f"bench: {len(dom_runs)} launches of {dom_name} timed "
+                           f"(none, or the event capacity filled)")
     dom_launch_ms = float(np.mean(dom_runs))
     dom_flops = gemm_flops(dom_name, wl)
     peak = PEAK_TFLOPS[wl.prec]
@@ -431,6 +435,8 @@ def bench_forward(args, wl, inp, dev) -> int:
     torch.cuda.synchronize()
     eager_ms = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(K)])
     kern = timer.durations()
+    if len(kern) >= timer.capacity:
+        raise RuntimeError("bench: the kernel table filled its event capacity (launches lost)")
 
     # one capture, K replays
     side = torch.cuda.Stream()
@@ -470,8 +476,9 @@ def bench_forward(args, wl, inp, dev) -> int:
         for i in range(K):
             fwd()
     dom_runs = [dur for _, dur in only.durations()]
-    if not dom_runs:
-        raise RuntimeError(f"bench: no launch of {dom_name} was timed")
+    if not dom_runs or 2 * len(dom_runs) + 2 > only.capacity:
+        raise RuntimeError(f"bench: {len(dom_runs)} launches of {dom_name} timed "
+                           f"(none, or the event capacity filled)")
     dom_launch_ms = float(np.mean(dom_runs))
     nbytes = fwd_gemm_bytes(dom_name, wl, active)
     if nbytes > 0:
