@@ -50,6 +50,10 @@ SHAPES = {
     # real blocks padded to eight (E = 96)
     "router_E128": ("olmoe_bf16", dict(name="router_E128", T=200, d=384, E=128, f=64, k=4)),
     "router_E96": ("olmoe_bf16", dict(name="router_E96", T=100, d=448, E=96, f=64, k=6)),
+    # the 256x256 engine at output widths that end in a partial column tile
+    # in every GEMM (d = 320, f = 192: 64- and 128-column remainders), for
+    # the bf16-staged plain stores and the SwiGLU epilogues
+    "ragged_n_bf16": ("olmoe_bf16", dict(name="ragged_n_bf16", T=600, d=320, E=8, f=192, k=2)),
     "tiny_mxfp8": ("tiny_mxfp8", {}),
     # d = 576: an odd number of 64-deep K stages; f = 320: a half-filled last gate/up panel
     "mid_mxfp8_E8": ("olmoe_mxfp8", dict(name="mid_mxfp8_E8", T=1000, d=576, E=8, f=320, k=2)),
