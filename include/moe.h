@@ -242,15 +242,19 @@ int moe_route_bwd(const void* x, const void* Wr, const float* logits,
 
 /*
  * moe_route_aux -- load-balancing loss of the router and its gradient.
- * HF OLMoE walkthrough, section 4 (Switch-Transformer-style loss: expert
- * assignment frequencies times router probabilities, summed; coefficient
- * router_aux_loss_coef, default 0.01).  With f_e = counts[e] / (T*k) (the
- * share of routed slots, counts as written by moe_dispatch) and
+ * HF OLMoE walkthrough, section 4: load_balancing_loss_func in
+ * modeling_olmoe.py (Switch-Transformer-style: expert assignment frequencies
+ * times router probabilities, summed, times the expert count), scaled by
+ * router_aux_loss_coef (default 0.01) as the causal-LM head does.  With
+ * f_e = counts[e] / T (the per-slot assignment frequencies summed over the k
+ * slots; counts as written by moe_dispatch) and
  * P_e = (1/T) sum_t softmax(logits[t])[e]:
- *   aux_loss[0] = coef * E * sum_e f_e * P_e             (f32, device)
+ *   aux_loss[0] = coef * E * sum_e f_e * P_e             (f32, device; coef*k
+ *                 when every expert receives T*k/E slots)
  *   aux_dp[e]   = coef * E * f_e / T                      (f32 [E], the
  *                 gradient with respect to every token's probability of e;
  *                 pass it to moe_route_bwd)
+ *   k is checked (1 <= k <= E) and does not enter the formulas.
  *   Sums are in a fixed order (per 64-token block, then over blocks).
  *   Workspace: moe_workspace_size(MOE_OP_ROUTE_AUX, ...).
  */

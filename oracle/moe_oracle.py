@@ -46,7 +46,11 @@ rounding against torch's conversions; MX scale closed forms and worked
 blocks; top-k against brute-force enumeration; metadata invariants; a
 hand-worked routed layer (tests/golden/hand_worked_layer.json); special
 cases reducing to dense torch computations; the backward against torch
-autograd and against central finite differences.
+autograd and against central finite differences.  tests/test_oracle_hf.py
+pins the router, the expert layer (forward and autograd backward) and the
+load-balancing loss against the HF OLMoE modules themselves
+(transformers.models.olmoe.modeling_olmoe: OlmoeTopKRouter,
+OlmoeSparseMoeBlock, load_balancing_loss_func).
 """
 from __future__ import annotations
 
@@ -215,15 +219,17 @@ def route(logits, k: int, prec: str = "bf16", renorm: bool = False):
 
 def aux_loss(logits, topk_idx, E: int, coef: float = 0.01, prec: str = "bf16"):
     """Switch-style load-balancing loss of one layer (HF OLMoE walkthrough,
-    section 4: the experts' assignment frequencies times their mean router
-    probabilities, summed; scaled by router_aux_loss_coef, default 0.01).
+    section 4: load_balancing_loss_func in modeling_olmoe.py -- the experts'
+    assignment frequencies times their mean router probabilities, summed;
+    scaled by router_aux_loss_coef, default 0.01, before it joins the loss).
 
-    Reading of what the page leaves open: f_e is the share of the T*k routed
-    slots that go to expert e (sum_e f_e = 1), P_e the mean over tokens of the
-    softmax probability of e, and L = coef * E * sum_e f_e * P_e, so that
-    perfectly balanced routing gives L = coef.  The top-k choice (so f) is
-    piecewise constant in the logits; the gradient reaches the logits through
-    P only: dL/dp[t,e] = coef * E * f_e / T for every token t.
+    f_e = counts_e / T is the fraction of tokens that route one of their k
+    slots to expert e (the per-slot one-hot averaged over tokens and summed
+    over the k slots, so sum_e f_e = k), P_e the mean over tokens of the
+    softmax probability of e, and L = coef * E * sum_e f_e * P_e; perfectly
+    balanced routing gives L = coef * k.  The top-k choice (so f) is piecewise
+    constant in the logits; the gradient reaches the logits through P only:
+    dL/dp[t,e] = coef * E * f_e / T for every token t.
     Returns (L, dL/dp per expert [E], float32 unless prec is fp64)."""
     p = softmax(logits)
     T = p.shape[0]
@@ -233,7 +239,7 @@ def aux_loss(logits, topk_idx, E: int, coef: float = 0.01, prec: str = "bf16"):
     for t in range(T):
         for j in range(k):
             counts[idx[t, j]] += 1
-    f = counts / (T * k)
+    f = counts / T
     P = np.mean(p, axis=0)
     L = coef * E * float(np.sum(f * P))
     return L, _f32(prec)(coef * E * f / T)

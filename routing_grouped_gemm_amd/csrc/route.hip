@@ -480,7 +480,8 @@ __global__ __launch_bounds__(256) void router_bwd_softmax_kernel(
 // ---------------------------------------------------------------------------
 // load-balancing loss: per-expert mean router probability P_e (partial sums
 // per block of 64 tokens, then an ordered sum over blocks), then
-// L = coef * E * sum_e f_e P_e with f_e = counts[e] / (T k), and its gradient
+// L = coef * E * sum_e f_e P_e with f_e = counts[e] / T (the fraction of
+// tokens that route a slot to e; the per-slot frequencies summed), and its gradient
 // with respect to every token's probabilities, coef * E * f_e / T.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void aux_partial_kernel(const float* __restrict__ logits, int T,
@@ -529,7 +530,7 @@ __global__ __launch_bounds__(256) void aux_final_kernel(const float* __restrict_
     float P = 0.0f;
     for (int b = 0; b < nblk; ++b) P += part[(long)b * E + e];
     P /= (float)T;
-    const float f = (float)counts[e] / ((float)T * (float)k);
+    const float f = (float)counts[e] / (float)T;
     term = f * P;
     dp[e] = coef * (float)E * f / (float)T;
   }
