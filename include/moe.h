@@ -37,12 +37,23 @@
  *     MOE_BF16) or MOE_PREC_MXFP8 (dtype MOE_BF16; expert forward and dgrad
  *     GEMMs in e4m3 with one power-of-two E8M0 scale per 32 elements along
  *     the contraction axis, weight gradients in bf16).
+ *   - Size limits of the grouped GEMMs (their operands are addressed with
+ *     32-bit byte offsets from a per-tile or per-expert base; a larger call
+ *     returns MOE_ERR_UNSUPPORTED, it never wraps):
+ *       one expert's weights:         d * (f + 128) * 2 < 2^32 bytes;
+ *       weight gradients (bf16):      R * max(d, 2f) * 2 < 2^32 bytes;
+ *       weight gradients (MOE_WGRAD_MX), Kp = sum over experts of n_e rounded
+ *       up to 128 (bounded by (R + 127 E + 127) rounded down to 128):
+ *                                     256 * Kp < 2^32 and
+ *                                     (Kp / 32) * max(d, 2f) < 2^32.
  *   - Errors are detected on the host before anything is enqueued and come
  *     back as a negative status; nothing is launched then.  There is no
  *     silent fallback to another precision or algorithm.  Values the host
- *     cannot see (indices inside topk_idx, finiteness of logits) are
- *     preconditions: topk_idx entries must lie in [0, E) and be distinct
- *     within a token.
+ *     cannot see are not checked: logits must be finite, and the experts of
+ *     one token distinct (duplicates are taken as separate slots).  A
+ *     pre-routed topk_idx entry outside [0, E) makes its slot empty: it gets
+ *     no row (dest_row -1, not counted), adds nothing to y or dx, and its
+ *     dtopk_w is 0 (the rows after offsets[E] are then left unwritten).
  */
 #ifndef MOE_H
 #define MOE_H
@@ -61,7 +72,8 @@ enum moe_status {
   MOE_ERR_DTYPE = -3,       /* unknown dtype/prec, or a dtype/prec pair that does not exist */
   MOE_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned */
   MOE_ERR_WORKSPACE = -5,   /* ws_bytes below moe_workspace_size */
-  MOE_ERR_UNSUPPORTED = -6, /* E > 256, k > E, d or f not a multiple of 64 */
+  MOE_ERR_UNSUPPORTED = -6, /* E > 256, k > E, d or f not a multiple of 64, or an operand
+                               beyond the GEMM engines' 32-bit offsets (see below) */
   MOE_ERR_LAUNCH = -7       /* the HIP runtime rejected a launch */
 };
 
@@ -163,7 +175,10 @@ int moe_combine(const void* Ys, const float* topk_w, const int32_t* dest_row, in
                 int k, int dtype, void* y, void* stream);
 
 /*
- * moe_combine_bwd -- backward of moe_combine for upstream gradient dY[T,d]:
+ * moe_combine_bwd -- backward of moe_combine for upstream gradient dY[T,d].
+ * Differentiates the weighted index_add of the HF OLMoE walkthrough,
+ * section 3 (each expert output times its top-k weight, added back to the
+ * token): for L = sum_t <y[t], dY[t]>,
  *   dYs[dest_row[t,j]] = topk_w[t,j] * dY[t]       (dtype, [R,d])
  *   dtopk_w[t,j]       = <dY[t], Ys[dest_row[t,j]]> (f32, [T,k])
  *   dYs_q, dYs_q_scale (optional; both NULL or both set, bf16 only): the rows
@@ -214,14 +229,23 @@ int moe_grouped_ffn_bwd(const void* dYs, const void* dYs_q, const uint8_t* dYs_q
                         void* dWd, void* ws, size_t ws_bytes, void* stream);
 
 /*
- * moe_dispatch_bwd -- dx[t] = sum_j dXs[dest_row[t,j]] (float32 sum in slot
- * order, stored in dtype; with MOE_ACCUMULATE added to dx).
+ * moe_dispatch_bwd -- backward of moe_dispatch's row copy.  The forward
+ * writes each token row straight into the expert rows of its k slots
+ * (olmoforge README, module table, row-wise expert parallel; HF OLMoE
+ * walkthrough, section 3: hidden_states[token_idx] per expert), so the
+ * gradient of x gathers those rows back:
+ *   dx[t] = sum_j dXs[dest_row[t,j]]  (float32 sum in slot order, stored in
+ *   dtype; with MOE_ACCUMULATE added to dx).  dXs [R,d], dx [T,d] (dtype).
  */
 int moe_dispatch_bwd(const void* dXs, const int32_t* dest_row, int T, int d, int k,
                      int dtype, unsigned flags, void* dx, void* stream);
 
 /*
  * moe_route_bwd -- router backward for the weight gradient dtopk_w.
+ * Differentiates moe_route (HF OLMoE walkthrough, section 2: logits = x.Wr
+ * with no bias, float32 softmax over the experts, the chosen probabilities
+ * as weights, optionally renormalised); the top-k choice itself is piecewise
+ * constant and has no gradient:
  *   dp[t,e] = dtopk_w[t,j] where e = topk_idx[t,j], else 0; with
  *             MOE_ROUTE_RENORM (weights p/S, S = sum of the chosen p):
  *             dp[t,e_m] = (dtopk_w[t,m] - sum_j dtopk_w[t,j] w[t,j]) / S;

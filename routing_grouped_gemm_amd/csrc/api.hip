@@ -82,6 +82,31 @@ inline int check_elems(long long rows, long long cols) {
   return (rows * cols > (1LL << 46)) ? MOE_ERR_SHAPE : MOE_OK;
 }
 
+// The GEMM engines address their operands through buffer resources with
+// 32-bit byte offsets from a per-tile or per-expert base.  A larger problem
+// is refused (MOE_ERR_UNSUPPORTED) instead of wrapping:
+//  * one expert's weight matrix, gate/up panels padded to 128 columns
+//    included: d * (f + 128) * 2 bytes below 2^32;
+//  * the bf16 weight gradients stream one expert's rows of Xs [n_e][d],
+//    A [n_e][f], dH [n_e][2f] and dYs [n_e][d] along K = n_e from one base:
+//    R * max(d, 2f) * 2 bytes below 2^32 (n_e <= R);
+//  * the MXFP8 weight gradients read codes [features][Kp] (Kp = R padded per
+//    expert): 256 rows of a tile span 256 * Kp bytes, and a block-scale column
+//    (Kp / 32) * max(d, 2f) bytes, both below 2^32.
+constexpr long long kOff32 = 1LL << 32;
+inline int check_weight_offsets(int d, int f) {
+  return ((long long)d * (f + 128) * 2 >= kOff32) ? MOE_ERR_UNSUPPORTED : MOE_OK;
+}
+inline int check_wgrad_offsets(long long R, int d, int f) {
+  const long long w = d > 2LL * f ? d : 2LL * f;
+  return (R * w * 2 >= kOff32) ? MOE_ERR_UNSUPPORTED : MOE_OK;
+}
+inline int check_mx_wgrad_offsets(long long R, int d, int f, int E) {
+  const long long kp = (R + 127LL * E + 127) / 128 * 128;
+  const long long w = d > 2LL * f ? d : 2LL * f;
+  return (256 * kp >= kOff32 || (kp / 32) * w >= kOff32) ? MOE_ERR_UNSUPPORTED : MOE_OK;
+}
+
 template <typename... P>
 inline bool all_nonnull(P... p) { return ((p != nullptr) && ...); }
 template <typename... P>
@@ -130,7 +155,9 @@ const char* moe_status_string(int status) {
     case MOE_ERR_DTYPE: return "unknown dtype/precision or invalid dtype/precision pair";
     case MOE_ERR_ALIGN: return "pointer not 16-byte aligned";
     case MOE_ERR_WORKSPACE: return "workspace too small";
-    case MOE_ERR_UNSUPPORTED: return "unsupported shape (E > 256, k > E, or d/f not a multiple of 64)";
+    case MOE_ERR_UNSUPPORTED:
+      return "unsupported shape (E > 256, k > E, d/f not a multiple of 64, or an operand beyond "
+             "the GEMM engines' 32-bit offsets)";
     case MOE_ERR_LAUNCH: return "HIP kernel launch failed";
   }
   return "unknown status";
@@ -256,6 +283,7 @@ int moe_grouped_ffn_fwd(const void* Xs, const uint8_t* Xs_scale, const int32_t* 
   const long long R = (long long)T * k;
   if (int s = check_elems(R, 2LL * (d > f ? d : f))) return s;
   if (int s = check_elems(E, (long long)d * f)) return s;
+  if (int s = check_weight_offsets(d, f)) return s;
   if (!all_aligned(Xs, offsets, Wg, Wu, Wd, Hg, Hu, A, Ys, ws)) return MOE_ERR_ALIGN;
   if (prec == MOE_PREC_MXFP8 && !aligned16(Xs_scale)) return MOE_ERR_ALIGN;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -339,6 +367,12 @@ int moe_grouped_ffn_bwd(const void* dYs, const void* dYs_q, const uint8_t* dYs_q
   const long long R = (long long)T * k;
   if (int s = check_elems(R, 2LL * (d > f ? d : f))) return s;
   if (int s = check_elems(E, (long long)d * f)) return s;
+  if (int s = check_weight_offsets(d, f)) return s;
+  if (flags & MOE_WGRAD_MX) {
+    if (int s = check_mx_wgrad_offsets(R, d, f, E)) return s;
+  } else if (int s = check_wgrad_offsets(R, d, f)) {
+    return s;
+  }
   if (!all_aligned(dYs, Xs, Hg, Hu, A, offsets, Wg, Wu, Wd, dH, dXs, dWg, dWu, dWd, ws))
     return MOE_ERR_ALIGN;
   if (prec == MOE_PREC_MXFP8 && !all_aligned(dYs_q, dYs_q_scale)) return MOE_ERR_ALIGN;

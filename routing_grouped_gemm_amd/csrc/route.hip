@@ -234,6 +234,9 @@ __device__ __forceinline__ void load8_nt(const float* p, float (&v)[8]) {
 
 // y[t] = sum_j w[t,j] Ys[dest_row[t,j]], in float32 in slot order.
 // dXs gather (W == false): dx[t] (+)= sum_j dXs[dest_row[t,j]].
+// A slot whose row lies outside [0, R) (the rank kernel marks a slot with an
+// expert index outside [0, E) by -1) adds nothing; its load still goes to a
+// clamped row so that every load of a pass is issued without a branch.
 template <typename TS, bool W>
 __device__ __forceinline__ void gather_rows(const TS* __restrict__ src, const float* __restrict__ w,
                                             const int32_t* __restrict__ dest_row, long t, int T,
@@ -262,15 +265,15 @@ __device__ __forceinline__ void gather_rows(const TS* __restrict__ src, const fl
       for (int u = 0; u < kPassChunks; ++u) load8_nt(p0 + chunk_col(c0, u, d), v0[u]);
 #pragma unroll
       for (int u = 0; u < kPassChunks; ++u) load8_nt(p1 + chunk_col(c0, u, d), v1[u]);
-      add(v0, W ? w[t * k + j] : 1.0f);
-      add(v1, W ? w[t * k + j + 1] : 1.0f);
+      if ((unsigned)dr[j] < (unsigned)R) add(v0, W ? w[t * k + j] : 1.0f);
+      if ((unsigned)dr[j + 1] < (unsigned)R) add(v1, W ? w[t * k + j + 1] : 1.0f);
     }
     if (j < k) {
       const TS* p0 = src + (long)clamp_row(dr[j], R) * d;
       float v0[kPassChunks][8];
 #pragma unroll
       for (int u = 0; u < kPassChunks; ++u) load8_nt(p0 + chunk_col(c0, u, d), v0[u]);
-      add(v0, W ? w[t * k + j] : 1.0f);
+      if ((unsigned)dr[j] < (unsigned)R) add(v0, W ? w[t * k + j] : 1.0f);
     }
 #pragma unroll
     for (int u = 0; u < kPassChunks; ++u) {
@@ -309,7 +312,8 @@ __global__ __launch_bounds__(256) void gather_sum_kernel(const TS* __restrict__ 
 }
 
 // dYs[dest] = w * dY[t]; dw[t,j] = <dY[t], Ys[dest]>.  Each lane sums its
-// products in column order, then the wave sums the lanes.
+// products in column order, then the wave sums the lanes.  A slot whose row
+// lies outside [0, R) stores no dYs row and gets dw = 0.
 template <typename TS, bool MXQ>
 __device__ __forceinline__ void combine_bwd_slot(const float (&g)[8], const float (&v)[8], float wj,
                                                  long r, int c, TS* __restrict__ dYs,
@@ -352,7 +356,12 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const TS* __restrict__
     for (int u = 0; u < kPassChunks; ++u) load8(dY + t * d + chunk_col(c0, u, d), g[u]);
     int j = 0;
     auto slot = [&](int jj, const float (&v)[kPassChunks][8]) {
-      const long r = clamp_row(dest_row[t * k + jj], R);
+      const int rr = dest_row[t * k + jj];
+      if ((unsigned)rr >= (unsigned)R) {
+        if (lane == 0) dw[t * k + jj] = 0.0f;
+        return;
+      }
+      const long r = rr;
       const float wj = w[t * k + jj];
       float dot = 0.0f;
 #pragma unroll
@@ -383,7 +392,12 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const TS* __restrict__
     return;
   }
   for (int j = 0; j < k; ++j) {
-    const long r = clamp_row(dest_row[t * k + j], R);
+    const int rr = dest_row[t * k + j];
+    if ((unsigned)rr >= (unsigned)R) {
+      if (lane == 0) dw[t * k + j] = 0.0f;
+      continue;
+    }
+    const long r = rr;
     const float wj = w[t * k + j];
     float dot = 0.0f;
     for (int c = lane * 8; c < d; c += 64 * 8) {

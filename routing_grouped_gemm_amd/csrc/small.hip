@@ -220,7 +220,8 @@ __global__ __launch_bounds__(256) void dispatch_small_kernel(
 
 // ---------------------------------------------------------------------------
 // combine: y[t] = sum_j w[t,j] Ys[dest_row[t,j]], one workgroup per token and
-// 2048 columns, the k rows' loads in flight together
+// 2048 columns, the k rows' loads in flight together; a slot whose row lies
+// outside [0, R) adds nothing (its load goes to a clamped row)
 // ---------------------------------------------------------------------------
 template <typename TS>
 __global__ __launch_bounds__(256) void combine_small_kernel(const TS* __restrict__ Ys,
@@ -237,22 +238,27 @@ __global__ __launch_bounds__(256) void combine_small_kernel(const TS* __restrict
   for (; j + 4 <= k; j += 4) {
     float v[4][8];
     float wj[4];
+    bool ok[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int r = min(max(dest_row[t * k + j + u], 0), R - 1);
+      const int rr = dest_row[t * k + j + u];
+      const int r = min(max(rr, 0), R - 1);
+      ok[u] = (unsigned)rr < (unsigned)R;
       wj[u] = w[t * k + j + u];
       load8(Ys + (long)r * d + c, v[u]);
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u)
+      if (ok[u])
 #pragma unroll
-      for (int q = 0; q < 8; ++q) acc[q] = fmaf(wj[u], v[u][q], acc[q]);
+        for (int q = 0; q < 8; ++q) acc[q] = fmaf(wj[u], v[u][q], acc[q]);
   }
   for (; j < k; ++j) {
-    const int r = min(max(dest_row[t * k + j], 0), R - 1);
+    const int rr = dest_row[t * k + j];
+    if ((unsigned)rr >= (unsigned)R) continue;
     const float wj = w[t * k + j];
     float v[8];
-    load8(Ys + (long)r * d + c, v);
+    load8(Ys + (long)rr * d + c, v);
 #pragma unroll
     for (int q = 0; q < 8; ++q) acc[q] = fmaf(wj, v[q], acc[q]);
   }

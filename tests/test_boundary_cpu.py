@@ -229,3 +229,29 @@ def test_route_aux_validation(L):
     assert f(A, A, 16, 8, 2, float("nan"), A, A, A, 256, None) == SHAPE
     assert f(A, MIS, 16, 8, 2, 0.01, A, A, A, 256, None) == ALIGN
     assert f(A, A, 200, 8, 2, 0.01, A, A, A, 4 * 8 * 4 - 1, None) == WS
+
+
+def test_ffn_offset_limits(L):
+    """Shapes whose operands would pass the GEMM engines' 32-bit byte offsets
+    are refused with MOE_ERR_UNSUPPORTED before anything else; just inside
+    the limit the call gets as far as the alignment check (a misaligned
+    pointer makes it stop there, so nothing is launched)."""
+    fwd = lambda T, k, d, f, Wg=A: L.moe_grouped_ffn_fwd(A, A, A, T, k, d, f, 8, Wg, A, A, BF16,
+                                                         P_BF16, A, A, A, A, A, 1 << 20, None)
+    # one expert's weights: d * (f + 128) * 2 bytes below 2^32
+    assert fwd(16, 2, 65536, 32768) == UNSUP
+    assert fwd(16, 2, 32768, 32640, Wg=MIS) == ALIGN
+
+    def bwd(T, k, d, f, flags=0, prec=P_BF16, dH=A):
+        return L.moe_grouped_ffn_bwd(A, A, A, A, A, A, A, A, T, k, d, f, 8, A, A, A, BF16, prec,
+                                     flags, dH, A, A, A, A, A, 1 << 20, None)
+    # bf16 weight gradients: R * max(d, 2f) * 2 bytes below 2^32
+    assert bwd(1 << 20, 2, 1024, 512) == UNSUP            # R = 2^21, width 1024
+    assert bwd((1 << 20) - 1, 2, 1024, 512, dH=MIS) == ALIGN
+    assert bwd(1 << 19, 2, 512, 1024) == UNSUP            # width 2f = 2048
+    assert bwd(1 << 16, 1, 7168, 2048, dH=MIS) == ALIGN   # one GPU's share of a 1T MoE
+    assert bwd(300000, 1, 7168, 2048) == UNSUP            # ~300k rows at d = 7168
+    # MXFP8 weight gradients: 256 * Kp and (Kp / 32) * max(d, 2f) below 2^32
+    assert bwd(1 << 23, 2, 64, 64, flags=0x10, prec=P_MX) == UNSUP    # Kp >= 2^24
+    assert bwd(1 << 21, 2, 64, 64, flags=0x10, prec=P_MX, dH=MIS) == ALIGN
+    assert bwd(1 << 21, 1, 65536, 64, flags=0x10, prec=P_MX) == UNSUP  # scale column

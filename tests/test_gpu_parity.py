@@ -15,7 +15,8 @@ import torch
 
 from moe_synth import make_inputs, workload
 from oracle import moe_oracle as O
-from tests.parity import compare, dev_tensor, relerr, run_gpu, run_oracle, say, to_np
+from tests.parity import (TOL, check_gates, compare, dev_tensor, gate, relerr, run_gpu, run_oracle,
+                          say, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -375,3 +376,54 @@ def test_mx_quantisation_is_applied():
         e_mx, e_bf = relerr(gpu[n], ref_mx[n]), relerr(gpu[n], ref_bf[n])
         say(f"  {n}: vs mxfp8 oracle {e_mx:.2e}, vs bf16 oracle {e_bf:.2e}")
         assert e_mx < 0.2 * e_bf, (n, e_mx, e_bf)
+
+
+@pytest.mark.parametrize("T,k", [(700, 3), (40, 3)])
+def test_out_of_range_slots_are_empty(T, k):
+    """Pre-routed slots whose expert lies outside [0, E) (here -1, E and
+    1000) are empty slots: no row (dest_row -1, counts without them), no
+    contribution to y or dx, dtopk_w = 0, and nothing in the weight
+    gradients.  Reference: the oracle on E + 1 experts with every such slot
+    sent to the extra, last expert with weight 0 (whose rows then come after
+    every real expert's rows and contribute exactly 0).  T = 40 runs the
+    small-batch dispatch, experts and combine; T = 700 the general kernels."""
+    import routing_grouped_gemm_amd as rgg
+    E, d, f = 8, 256, 128
+    say(f"[case] out-of-range slots T={T} k={k} E={E}")
+    rng = np.random.Generator(np.random.PCG64(T + k))
+    wl = workload("olmoe_bf16", name="oor", T=T, d=d, E=E, f=f, k=k)
+    inp = make_inputs(wl, seed=3)
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    w = rng.uniform(0.0, 1.0, (T, k)).astype(np.float32)
+    bad = rng.random((T, k)) < 0.08
+    bad[0, 0] = True
+    idx_bad = idx.copy()
+    idx_bad[bad] = rng.choice(np.array([-1, E, 1000], np.int32), int(bad.sum()))
+    # reference: invalid slots -> expert E (zero weights), combine weight 0
+    idx_ref = idx.copy(); idx_ref[bad] = E
+    w_ref = w.copy(); w_ref[bad] = 0.0
+    z = lambda a: np.concatenate([a, np.zeros((1,) + a.shape[1:], a.dtype)])
+    ref = O.layer(inp["x"], None, z(inp["Wg"]), z(inp["Wu"]), z(inp["Wd"]), k, inp["dY"], "bf16",
+                  topk_idx=idx_ref, topk_w=w_ref)
+    dt = torch.bfloat16
+    layer = rgg.ExpertLayer(T, d, E, f, k, dt, "bf16", router=False)
+    layer.forward(dev_tensor(inp, "x", dt), None, dev_tensor(inp, "Wg", dt),
+                  dev_tensor(inp, "Wu", dt), dev_tensor(inp, "Wd", dt),
+                  topk_idx=rgg.upload(idx_bad), topk_w=rgg.upload(w))
+    layer.backward(dev_tensor(inp, "dY", dt))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(to_np(layer.counts), ref["counts"][:E])
+    np.testing.assert_array_equal(to_np(layer.offsets), ref["offsets"][:E + 1])
+    dr = to_np(layer.dest_row)
+    assert np.all(dr[bad] == -1)
+    np.testing.assert_array_equal(dr[~bad], ref["dest_row"][~bad])
+    dw = to_np(layer.dw)
+    assert np.all(dw[bad] == 0.0)
+    gpu = {n: to_np(getattr(layer, n)) for n in ("y", "dx", "dWg", "dWu", "dWd")}
+    gpu["dw_valid"] = dw[~bad]
+    refs = {"y": ref["y"], "dx": ref["dx"], "dWg": ref["dWg"][:E], "dWu": ref["dWu"][:E],
+            "dWd": ref["dWd"][:E], "dw_valid": np.asarray(ref["dw"])[~bad]}
+    errs = {}
+    for n in refs:
+        gate(n, gpu[n], refs[n], TOL["bf16"], errs)
+    check_gates(f"out-of-range T={T}", errs, TOL["bf16"])
