@@ -74,7 +74,8 @@ enum moe_status {
   MOE_ERR_WORKSPACE = -5,   /* ws_bytes below moe_workspace_size */
   MOE_ERR_UNSUPPORTED = -6, /* E > 256, k > E, d or f not a multiple of 64, or an operand
                                beyond the GEMM engines' 32-bit offsets (see below) */
-  MOE_ERR_LAUNCH = -7       /* the HIP runtime rejected a launch */
+  MOE_ERR_LAUNCH = -7,      /* the HIP runtime rejected a launch */
+  MOE_ERR_SCRATCH = -8      /* larger than a no-allocation entry point's static scratch */
 };
 
 enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 };
@@ -146,6 +147,29 @@ int moe_dispatch(const void* x, const int32_t* topk_idx, int T, int d, int E, in
                  int dtype, int prec, int32_t* counts, int32_t* offsets,
                  int32_t* dest_row, int32_t* src_token, void* Xs, void* Xq, uint8_t* Xq_scale,
                  void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_dispatch_noalloc -- moe_dispatch without a caller workspace, for
+ * callers that cannot allocate device memory at all: code being captured
+ * into a HIP graph, tight serving loops, and harnesses that forbid
+ * allocation.  Same arguments, results and errors as moe_dispatch, minus
+ * ws / ws_bytes: the per-block expert histograms and their scanned bases
+ * (2 * ceil(T/64) * E int32, each table padded to 256 bytes) live in a static
+ * device array of 4 MiB that the library holds on every GPU it runs on until
+ * the process ends; its address is looked up once per device on the first
+ * call made with that device current.  The call itself allocates nothing
+ * and, like every entry point, only enqueues kernels on `stream`.
+ *   MOE_ERR_SCRATCH: the tables would exceed 4 MiB (about T * E > 2^25, e.g.
+ *   T = 524288 tokens at E = 64); use moe_dispatch with a workspace then.
+ *   Calls on one GPU share that GPU's scratch (each call overwrites it fully
+ *   before reading it, so nothing carries over): two calls that can run at
+ *   the same time on one GPU (different streams, no ordering between them)
+ *   race on it and must not be issued.
+ */
+int moe_dispatch_noalloc(const void* x, const int32_t* topk_idx, int T, int d, int E, int k,
+                         int dtype, int prec, int32_t* counts, int32_t* offsets,
+                         int32_t* dest_row, int32_t* src_token, void* Xs, void* Xq,
+                         uint8_t* Xq_scale, void* stream);
 
 /*
  * moe_grouped_ffn_fwd -- all SwiGLU experts as grouped GEMMs.

@@ -22,7 +22,7 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "lib", "moe_route", "moe_dispatch", "moe_grouped_ffn_fwd", "moe_combine",
+    "lib", "moe_route", "moe_dispatch", "moe_dispatch_noalloc", "moe_grouped_ffn_fwd", "moe_combine",
     "moe_combine_bwd", "moe_grouped_ffn_bwd", "moe_dispatch_bwd", "moe_route_bwd",
     "moe_route_aux", "moe_workspace_size", "moe_status_string", "ExpertLayer", "LIB_PATH",
     "MOE_ROUTE_LOGITS_IN", "MOE_ROUTE_RENORM", "MOE_ACCUMULATE", "MOE_WGRAD_F32", "KernelTimer", "upload", "mx_scale_pitch",
@@ -45,6 +45,7 @@ _P, _I, _U, _S = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint, ctypes.c_size_t
 _SIGS = {
     "moe_route": [_P, _P, _I, _I, _I, _I, _I, _U, _P, _P, _P, _P, _S, _P],
     "moe_dispatch": [_P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _S, _P],
+    "moe_dispatch_noalloc": [_P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P],
     "moe_grouped_ffn_fwd": [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _I, _I, _P, _P, _P, _P,
                             _P, _S, _P],
     "moe_combine": [_P, _P, _P, _I, _I, _I, _I, _P, _P],
@@ -163,6 +164,17 @@ def moe_dispatch(x, topk_idx, E, counts, offsets, dest_row, src_token, Xs, ws, X
                               _ptr(counts), _ptr(offsets), _ptr(dest_row), _ptr(src_token),
                               _ptr(Xs), _ptr(Xq), _ptr(Xq_scale), wp, wb, _stream(stream)),
            "moe_dispatch")
+
+
+def moe_dispatch_noalloc(x, topk_idx, E, counts, offsets, dest_row, src_token, Xs, Xq=None,
+                         Xq_scale=None, prec="bf16", stream=None):
+    T, d = x.shape
+    k = topk_idx.shape[1]
+    _check(lib().moe_dispatch_noalloc(_ptr(x), _ptr(topk_idx), T, d, E, k, _dtype(x), PREC[prec],
+                                      _ptr(counts), _ptr(offsets), _ptr(dest_row),
+                                      _ptr(src_token), _ptr(Xs), _ptr(Xq), _ptr(Xq_scale),
+                                      _stream(stream)),
+           "moe_dispatch_noalloc")
 
 
 def mx_scale_pitch(R: int) -> int:

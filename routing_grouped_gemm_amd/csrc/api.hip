@@ -4,6 +4,7 @@
 
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/moe.h"
 #include "gemm.h"
@@ -159,6 +160,8 @@ const char* moe_status_string(int status) {
       return "unsupported shape (E > 256, k > E, d/f not a multiple of 64, or an operand beyond "
              "the GEMM engines' 32-bit offsets)";
     case MOE_ERR_LAUNCH: return "HIP kernel launch failed";
+    case MOE_ERR_SCRATCH:
+      return "problem larger than the static scratch of a no-allocation entry point";
   }
   return "unknown status";
 }
@@ -241,21 +244,19 @@ int moe_route(const void* x, const void* Wr, int T, int d, int E, int k, int dty
   return status_of(launch_topk_softmax(logits, T, E, k, renorm, topk_idx, topk_w, st));
 }
 
-int moe_dispatch(const void* x, const int32_t* topk_idx, int T, int d, int E, int k, int dtype,
-                 int prec, int32_t* counts, int32_t* offsets, int32_t* dest_row,
-                 int32_t* src_token, void* Xs, void* Xq, uint8_t* Xq_scale, void* ws,
-                 size_t ws_bytes, void* stream) {
-  if (!all_nonnull(x, topk_idx, counts, offsets, dest_row, src_token, Xs, ws)) return MOE_ERR_NULL;
-  if (int s = check_prec(dtype, prec)) return s;
+}  // extern "C"
+
+namespace {
+
+// moe_dispatch's validation and launches; ws is device memory of ws_bytes.
+int dispatch_impl(const void* x, const int32_t* topk_idx, int T, int d, int E, int k, int dtype,
+                  int prec, int32_t* counts, int32_t* offsets, int32_t* dest_row,
+                  int32_t* src_token, void* Xs, void* Xq, uint8_t* Xq_scale, void* ws,
+                  size_t ws_bytes, hipStream_t st) {
   const bool mx = prec == MOE_PREC_MXFP8;
-  if (mx && !all_nonnull(Xq, Xq_scale)) return MOE_ERR_NULL;
-  if (int s = check_route_shape(T, E, k)) return s;
-  if (int s = check_width(d)) return s;
-  if (int s = check_elems((long long)T * k, d)) return s;
-  if (!all_aligned(x, topk_idx, counts, offsets, dest_row, src_token, Xs, ws)) return MOE_ERR_ALIGN;
-  if (mx && !all_aligned(Xq, Xq_scale)) return MOE_ERR_ALIGN;
-  if (ws_bytes < dispatch_ws(T, E)) return MOE_ERR_WORKSPACE;
-  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (!dispatch_small_applies(T, k) || mx) {
+    if (ws_bytes < dispatch_ws(T, E)) return MOE_ERR_WORKSPACE;
+  }
   clear_stale_error();
   if (!mx && dispatch_small_applies(T, k))
     return status_of(launch_dispatch_small(dtype, x, topk_idx, T, d, E, k, counts, offsets,
@@ -268,6 +269,89 @@ int moe_dispatch(const void* x, const int32_t* topk_idx, int T, int d, int E, in
   const int R = T * k;
   if (mx) return status_of(launch_mx_dispatch_copy(x, src_token, R, T, d, Xs, Xq, Xq_scale, st));
   return status_of(launch_dispatch_copy(dtype, x, dest_row, T, d, k, Xs, st));
+}
+
+// Argument checks of moe_dispatch that need no workspace.
+int dispatch_args(const void* x, const int32_t* topk_idx, int T, int d, int E, int k, int dtype,
+                  int prec, const int32_t* counts, const int32_t* offsets,
+                  const int32_t* dest_row, const int32_t* src_token, const void* Xs,
+                  const void* Xq, const uint8_t* Xq_scale) {
+  if (!all_nonnull(x, topk_idx, counts, offsets, dest_row, src_token, Xs)) return MOE_ERR_NULL;
+  if (int s = check_prec(dtype, prec)) return s;
+  const bool mx = prec == MOE_PREC_MXFP8;
+  if (mx && !all_nonnull(Xq, Xq_scale)) return MOE_ERR_NULL;
+  if (int s = check_route_shape(T, E, k)) return s;
+  if (int s = check_width(d)) return s;
+  if (int s = check_elems((long long)T * k, d)) return s;
+  if (!all_aligned(x, topk_idx, counts, offsets, dest_row, src_token, Xs)) return MOE_ERR_ALIGN;
+  if (mx && !all_aligned(Xq, Xq_scale)) return MOE_ERR_ALIGN;
+  return MOE_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Static scratch of moe_dispatch_noalloc: the dispatch's per-block expert
+// histograms and their scanned bases, in device memory that the library
+// holds from load to process end (one copy per GPU).  Every table is fully
+// written by the kernels before it is read, so nothing needs clearing.  In
+// host code `scratch` is only a stand-in for the symbol: its device address,
+// per device, comes from hipGetSymbolAddress and is what the kernels get.
+// ---------------------------------------------------------------------------
+constexpr size_t kNoAllocScratchBytes = size_t(4) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch (looked up once per device).
+int scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return status_of(e);
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) return status_of(e != hipSuccess ? e : hipErrorUnknown);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_dispatch(const void* x, const int32_t* topk_idx, int T, int d, int E, int k, int dtype,
+                 int prec, int32_t* counts, int32_t* offsets, int32_t* dest_row,
+                 int32_t* src_token, void* Xs, void* Xq, uint8_t* Xq_scale, void* ws,
+                 size_t ws_bytes, void* stream) {
+  if (int s = dispatch_args(x, topk_idx, T, d, E, k, dtype, prec, counts, offsets, dest_row,
+                            src_token, Xs, Xq, Xq_scale))
+    return s;
+  if (!ws) return MOE_ERR_NULL;
+  if (!aligned16(ws)) return MOE_ERR_ALIGN;
+  if (ws_bytes < dispatch_ws(T, E)) return MOE_ERR_WORKSPACE;
+  return dispatch_impl(x, topk_idx, T, d, E, k, dtype, prec, counts, offsets, dest_row, src_token,
+                       Xs, Xq, Xq_scale, ws, ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+int moe_dispatch_noalloc(const void* x, const int32_t* topk_idx, int T, int d, int E, int k,
+                         int dtype, int prec, int32_t* counts, int32_t* offsets,
+                         int32_t* dest_row, int32_t* src_token, void* Xs, void* Xq,
+                         uint8_t* Xq_scale, void* stream) {
+  if (int s = dispatch_args(x, topk_idx, T, d, E, k, dtype, prec, counts, offsets, dest_row,
+                            src_token, Xs, Xq, Xq_scale))
+    return s;
+  const size_t need = dispatch_ws(T, E);
+  if (need > kNoAllocScratchBytes) return MOE_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (int s = scratch_address(&ws)) return s;
+  return dispatch_impl(x, topk_idx, T, d, E, k, dtype, prec, counts, offsets, dest_row, src_token,
+                       Xs, Xq, Xq_scale, ws, kNoAllocScratchBytes,
+                       static_cast<hipStream_t>(stream));
 }
 
 int moe_grouped_ffn_fwd(const void* Xs, const uint8_t* Xs_scale, const int32_t* offsets, int T,

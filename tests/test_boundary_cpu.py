@@ -11,7 +11,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "moe.h")
 
-OK, NULL, SHAPE, DTYPE, ALIGN, WS, UNSUP = 0, -1, -2, -3, -4, -5, -6
+OK, NULL, SHAPE, DTYPE, ALIGN, WS, UNSUP, SCRATCH = 0, -1, -2, -3, -4, -5, -6, -8
 F32, BF16 = 0, 1
 P_F32, P_BF16, P_MX = 0, 1, 2
 
@@ -36,7 +36,7 @@ def declared_entry_points():
 
 def test_exports_every_declared_symbol(L):
     names = declared_entry_points()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(L, n), n
 
@@ -57,7 +57,7 @@ def test_kernel_event_hook_switches(L):
 
 
 def test_status_strings(L):
-    for s in (OK, NULL, SHAPE, DTYPE, ALIGN, WS, UNSUP, -7):
+    for s in (OK, NULL, SHAPE, DTYPE, ALIGN, WS, UNSUP, -7, SCRATCH):
         assert L.moe_status_string(s)
     assert b"unknown" in L.moe_status_string(12345)
     assert L.moe_last_launch_error() == b"none"
@@ -255,3 +255,19 @@ def test_ffn_offset_limits(L):
     assert bwd(1 << 23, 2, 64, 64, flags=0x10, prec=P_MX) == UNSUP    # Kp >= 2^24
     assert bwd(1 << 21, 2, 64, 64, flags=0x10, prec=P_MX, dH=MIS) == ALIGN
     assert bwd(1 << 21, 1, 65536, 64, flags=0x10, prec=P_MX) == UNSUP  # scale column
+
+
+def test_dispatch_noalloc_validation(L):
+    """The no-allocation dispatch checks its arguments like moe_dispatch and
+    refuses a problem whose tables exceed its 4 MiB static scratch before it
+    touches any device (2 * ceil(T/64) * E * 4 bytes, each table padded to
+    256 bytes)."""
+    f = L.moe_dispatch_noalloc
+    args = lambda T, E, x=A, xs=A, prec=P_BF16: (x, A, T, 64, E, 2, BF16, prec, A, A, A, A, xs,
+                                                 A, A, None)
+    assert f(*args(16, 8, x=None)) == NULL
+    assert f(*args(16, 8, xs=MIS)) == ALIGN
+    assert f(*args(16, 300)) == UNSUP
+    assert f(*args(1 << 20, 64)) == SCRATCH          # 2 * 16384 * 64 * 4 B = 8 MiB
+    assert f(*args(1 << 19, 64 + 1)) == SCRATCH       # just over 4 MiB
+    assert f(*args(1 << 18, 256, prec=P_MX)) == SCRATCH   # 8 MiB
