@@ -91,13 +91,18 @@ enum moe_prec { MOE_PREC_F32 = 0, MOE_PREC_BF16 = 1, MOE_PREC_MXFP8 = 2 };
 #define MOE_WGRAD_F32 0x8u
 /* moe_grouped_ffn_bwd flag (MXFP8): the weight-gradient GEMMs in MXFP8 too */
 #define MOE_WGRAD_MX 0x10u
+/* moe_grouped_ffn_fwd / moe_grouped_ffn_bwd flag (MXFP8): the forward quantises
+   each weight matrix once for both directions and keeps the backward's codes
+   in its workspace, which the backward then reads (see both entry points) */
+#define MOE_MX_KEEP_WEIGHTS 0x20u
 
 /* Operation ids for moe_workspace_size. */
 enum moe_op {
   MOE_OP_ROUTE = 0, MOE_OP_DISPATCH = 1, MOE_OP_FFN_FWD = 2, MOE_OP_COMBINE = 3,
   MOE_OP_COMBINE_BWD = 4, MOE_OP_FFN_BWD = 5, MOE_OP_DISPATCH_BWD = 6, MOE_OP_ROUTE_BWD = 7,
   MOE_OP_ROUTE_AUX = 8,
-  MOE_OP_FFN_BWD_MXW = 9   /* moe_grouped_ffn_bwd with MOE_WGRAD_MX */
+  MOE_OP_FFN_BWD_MXW = 9,  /* moe_grouped_ffn_bwd with MOE_WGRAD_MX (its own part) */
+  MOE_OP_FFN_FWD_KEEP = 10 /* moe_grouped_ffn_fwd with MOE_MX_KEEP_WEIGHTS */
 };
 
 /*
@@ -183,11 +188,18 @@ int moe_dispatch_noalloc(const void* x, const int32_t* topk_idx, int T, int d, i
  *   moe_dispatch wrote; the weights are block-quantised inside (Wg, Wu along
  *   d, Wd along f) and A along f before the down GEMM.  Workspace:
  *   moe_workspace_size(MOE_OP_FFN_FWD, ...) (0 bytes except for MXFP8).
+ *   flags: MOE_MX_KEEP_WEIGHTS (prec MXFP8 only, else MOE_ERR_DTYPE): each
+ *   weight matrix is read once and quantised for both directions of the
+ *   layer (Wg, Wu along d and along f; Wd along f and along d), and the
+ *   backward's codes stay in ws, which must then hold
+ *   moe_workspace_size(MOE_OP_FFN_FWD_KEEP, ...) bytes; pass that workspace,
+ *   unchanged, to moe_grouped_ffn_bwd with the same flag.  The results are
+ *   the same as without the flag (the codes are the same bytes).  0: no flag.
  */
 int moe_grouped_ffn_fwd(const void* Xs, const uint8_t* Xs_scale, const int32_t* offsets,
                         int T, int k, int d, int f, int E, const void* Wg, const void* Wu,
-                        const void* Wd, int dtype, int prec, void* Hg, void* Hu, void* A,
-                        void* Ys, void* ws, size_t ws_bytes, void* stream);
+                        const void* Wd, int dtype, int prec, unsigned flags, void* Hg, void* Hu,
+                        void* A, void* Ys, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * moe_combine -- weighted un-dispatch.
@@ -244,6 +256,13 @@ int moe_combine_bwd(const void* dY, const void* Ys, const float* topk_w,
  *   dgrad's epilogue writes it; the weight gradients take the unquantised
  *   operands.  Workspace: moe_workspace_size(MOE_OP_FFN_BWD, ...) (0 bytes
  *   except for MXFP8).
+ *   MOE_MX_KEEP_WEIGHTS (prec MXFP8 only, else MOE_ERR_DTYPE): ws begins with
+ *   the workspace that moe_grouped_ffn_fwd filled with the same flag,
+ *   unchanged since (moe_workspace_size(MOE_OP_FFN_FWD_KEEP, ...) bytes),
+ *   followed by the backward's own workspace (MOE_OP_FFN_BWD, or
+ *   MOE_OP_FFN_BWD_MXW with MOE_WGRAD_MX); ws_bytes covers both.  The
+ *   dgrad GEMMs read the weight codes the forward kept instead of quantising
+ *   Wg, Wu and Wd again; the results are the same bytes.
  */
 int moe_grouped_ffn_bwd(const void* dYs, const void* dYs_q, const uint8_t* dYs_q_scale,
                         const void* Xs, const void* Hg, const void* Hu,

@@ -25,7 +25,8 @@ __all__ = [
     "lib", "moe_route", "moe_dispatch", "moe_dispatch_noalloc", "moe_grouped_ffn_fwd", "moe_combine",
     "moe_combine_bwd", "moe_grouped_ffn_bwd", "moe_dispatch_bwd", "moe_route_bwd",
     "moe_route_aux", "moe_workspace_size", "moe_status_string", "ExpertLayer", "LIB_PATH",
-    "MOE_ROUTE_LOGITS_IN", "MOE_ROUTE_RENORM", "MOE_ACCUMULATE", "MOE_WGRAD_F32", "KernelTimer", "upload", "mx_scale_pitch",
+    "MOE_ROUTE_LOGITS_IN", "MOE_ROUTE_RENORM", "MOE_ACCUMULATE", "MOE_WGRAD_F32", "MOE_MX_KEEP_WEIGHTS",
+    "KernelTimer", "upload", "mx_scale_pitch",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_hip.so")
@@ -37,17 +38,18 @@ MOE_ACCUMULATE = 0x2
 MOE_ROUTE_RENORM = 0x4
 MOE_WGRAD_F32 = 0x8
 MOE_WGRAD_MX = 0x10
+MOE_MX_KEEP_WEIGHTS = 0x20
 OPS = {"route": 0, "dispatch": 1, "ffn_fwd": 2, "combine": 3, "combine_bwd": 4,
        "ffn_bwd": 5, "dispatch_bwd": 6, "route_bwd": 7, "route_aux": 8,
-       "ffn_bwd_mxw": 9}
+       "ffn_bwd_mxw": 9, "ffn_fwd_keep": 10}
 
 _P, _I, _U, _S = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint, ctypes.c_size_t
 _SIGS = {
     "moe_route": [_P, _P, _I, _I, _I, _I, _I, _U, _P, _P, _P, _P, _S, _P],
     "moe_dispatch": [_P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _S, _P],
     "moe_dispatch_noalloc": [_P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P],
-    "moe_grouped_ffn_fwd": [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _I, _I, _P, _P, _P, _P,
-                            _P, _S, _P],
+    "moe_grouped_ffn_fwd": [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _I, _I, _U, _P, _P, _P,
+                            _P, _P, _S, _P],
     "moe_combine": [_P, _P, _P, _I, _I, _I, _I, _P, _P],
     "moe_combine_bwd": [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P],
     "moe_grouped_ffn_bwd": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _I,
@@ -183,11 +185,12 @@ def mx_scale_pitch(R: int) -> int:
 
 
 def moe_grouped_ffn_fwd(Xs, Xs_scale, offsets, T, k, Wg, Wu, Wd, Hg, Hu, A, Ys, ws=None,
-                        prec="bf16", stream=None):
+                        prec="bf16", stream=None, keep_weights=False):
     E, d, f = Wg.shape
     wp, wb = _ws(ws)
+    flags = MOE_MX_KEEP_WEIGHTS if keep_weights else 0
     _check(lib().moe_grouped_ffn_fwd(_ptr(Xs), _ptr(Xs_scale), _ptr(offsets), T, k, d, f, E,
-                                     _ptr(Wg), _ptr(Wu), _ptr(Wd), _dtype(Wg), PREC[prec],
+                                     _ptr(Wg), _ptr(Wu), _ptr(Wd), _dtype(Wg), PREC[prec], flags,
                                      _ptr(Hg), _ptr(Hu), _ptr(A), _ptr(Ys), wp, wb,
                                      _stream(stream)), "moe_grouped_ffn_fwd")
 
@@ -210,13 +213,13 @@ def moe_combine_bwd(dY, Ys, topk_w, dest_row, dYs, dtopk_w, dYs_q=None, dYs_q_sc
 
 def moe_grouped_ffn_bwd(dYs, Xs, Hg, Hu, A, offsets, T, k, Wg, Wu, Wd, dH, dXs,
                         dWg, dWu, dWd, ws=None, prec="bf16", accumulate=False, dYs_q=None,
-                        dYs_q_scale=None, stream=None, mx_wgrad=False):
+                        dYs_q_scale=None, stream=None, mx_wgrad=False, keep_weights=False):
     E, d, f = Wg.shape
     wp, wb = _ws(ws)
     # float32 weight gradients of a bf16 layer select float32 accumulation
     flags = (MOE_ACCUMULATE if accumulate else 0) | \
         (MOE_WGRAD_F32 if dWg.dtype == torch.float32 and Wg.dtype == torch.bfloat16 else 0) | \
-        (MOE_WGRAD_MX if mx_wgrad else 0)
+        (MOE_WGRAD_MX if mx_wgrad else 0) | (MOE_MX_KEEP_WEIGHTS if keep_weights else 0)
     _check(lib().moe_grouped_ffn_bwd(_ptr(dYs), _ptr(dYs_q), _ptr(dYs_q_scale), _ptr(Xs),
                                      _ptr(Hg), _ptr(Hu), _ptr(A),
                                      _ptr(offsets), T, k, d, f, E, _ptr(Wg),
@@ -366,8 +369,18 @@ class ExpertLayer:
             return torch.empty(max(n, 256), dtype=torch.uint8, device=dev)
         self.ws_route = ws("route")
         self.ws_dispatch = ws("dispatch")
-        self.ws_fwd = ws("ffn_fwd")
-        self.ws_bwd = ws("ffn_bwd_mxw" if self.mx_wgrad else "ffn_bwd")
+        bwd_op = "ffn_bwd_mxw" if self.mx_wgrad else "ffn_bwd"
+        if prec == "mxfp8":
+            # one workspace for both directions: the forward quantises each
+            # weight once and keeps the backward's codes in its part, which
+            # the backward reads (MOE_MX_KEEP_WEIGHTS)
+            nf = moe_workspace_size("ffn_fwd_keep", T, d, E, f, k, dtype, prec)
+            nb = moe_workspace_size(bwd_op, T, d, E, f, k, dtype, prec)
+            self.ws_bwd = torch.empty(nf + nb, dtype=torch.uint8, device=dev)
+            self.ws_fwd = self.ws_bwd[:nf]
+        else:
+            self.ws_fwd = ws("ffn_fwd")
+            self.ws_bwd = ws(bwd_op)
         self.ws_route_bwd = ws("route_bwd")
         self.ws_route_aux = ws("route_aux")
 
@@ -391,7 +404,7 @@ class ExpertLayer:
         mx = self.prec == "mxfp8"
         moe_grouped_ffn_fwd(self.Xq if mx else self.Xs, self.Xq_scale, self.offsets, self.T,
                             self.k, Wg, Wu, Wd, self.Hg, self.Hu, self.A, self.Ys, self.ws_fwd,
-                            self.prec, stream)
+                            self.prec, stream, keep_weights=mx)
         moe_combine(self.Ys, self.topk_w, self.dest_row, self.y, stream)
         return self.y
 
@@ -401,7 +414,8 @@ class ExpertLayer:
         moe_grouped_ffn_bwd(self.dYs, self.Xs, self.Hg, self.Hu, self.A, self.offsets, self.T, self.k,
                             self.Wg, self.Wu, self.Wd, self.dH, self.dXs, self.dWg, self.dWu,
                             self.dWd, self.ws_bwd, self.prec, accumulate_wgrad, self.dYs_q,
-                            self.dYs_q_scale, stream, mx_wgrad=self.mx_wgrad)
+                            self.dYs_q_scale, stream, mx_wgrad=self.mx_wgrad,
+                            keep_weights=self.prec == "mxfp8")
         moe_dispatch_bwd(self.dXs, self.dest_row, self.dx, False, stream)
         if self.router:
             aux = self.aux_dp if self.aux_coef != 0.0 else None

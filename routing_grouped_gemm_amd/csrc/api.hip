@@ -204,6 +204,10 @@ int moe_workspace_size(int op, int T, int d, int E, int f, int k, int dtype, int
       if (prec != MOE_PREC_MXFP8) return MOE_ERR_DTYPE;
       *bytes = mx_wgrad_workspace(R, d, f, E);
       return MOE_OK;
+    case MOE_OP_FFN_FWD_KEEP:
+      if (prec != MOE_PREC_MXFP8) return MOE_ERR_DTYPE;
+      *bytes = mx_fwd_workspace(R, d, f, E, true);
+      return MOE_OK;
   }
   return MOE_ERR_SHAPE;
 }
@@ -267,7 +271,7 @@ int dispatch_impl(const void* x, const int32_t* topk_idx, int T, int d, int E, i
   MOE_TRY(launch_dispatch_meta(topk_idx, T, E, k, hist, base, counts, offsets, dest_row,
                                src_token, st));
   const int R = T * k;
-  if (mx) return status_of(launch_mx_dispatch_copy(x, src_token, R, T, d, Xs, Xq, Xq_scale, st));
+  if (mx) return status_of(launch_mx_dispatch_copy(x, dest_row, T, d, k, Xs, Xq, Xq_scale, st));
   return status_of(launch_dispatch_copy(dtype, x, dest_row, T, d, k, Xs, st));
 }
 
@@ -356,10 +360,12 @@ int moe_dispatch_noalloc(const void* x, const int32_t* topk_idx, int T, int d, i
 
 int moe_grouped_ffn_fwd(const void* Xs, const uint8_t* Xs_scale, const int32_t* offsets, int T,
                         int k, int d, int f, int E, const void* Wg, const void* Wu,
-                        const void* Wd, int dtype, int prec, void* Hg, void* Hu, void* A,
-                        void* Ys, void* ws, size_t ws_bytes, void* stream) {
+                        const void* Wd, int dtype, int prec, unsigned flags, void* Hg, void* Hu,
+                        void* A, void* Ys, void* ws, size_t ws_bytes, void* stream) {
   if (!all_nonnull(Xs, offsets, Wg, Wu, Wd, Hg, Hu, A, Ys)) return MOE_ERR_NULL;
   if (int s = check_prec(dtype, prec)) return s;
+  const bool keep = (flags & MOE_MX_KEEP_WEIGHTS) != 0;
+  if (keep && prec != MOE_PREC_MXFP8) return MOE_ERR_DTYPE;
   if (prec == MOE_PREC_MXFP8 && !all_nonnull(Xs_scale, ws)) return MOE_ERR_NULL;
   if (int s = check_route_shape(T, E, k)) return s;
   if (int s = check_width(d)) return s;
@@ -373,9 +379,9 @@ int moe_grouped_ffn_fwd(const void* Xs, const uint8_t* Xs_scale, const int32_t* 
   hipStream_t st = static_cast<hipStream_t>(stream);
   clear_stale_error();
   if (prec == MOE_PREC_MXFP8) {
-    if (ws_bytes < mx_fwd_workspace(R, d, f, E)) return MOE_ERR_WORKSPACE;
+    if (ws_bytes < mx_fwd_workspace(R, d, f, E, keep)) return MOE_ERR_WORKSPACE;
     return status_of(mx_ffn_fwd(Xs, Xs_scale, offsets, (int)R, d, f, E, Wg, Wu, Wd, Hg, Hu, A,
-                                Ys, ws, num_cu(), st));
+                                Ys, ws, keep, num_cu(), st));
   }
   if (prec == MOE_PREC_BF16 && skinny_applies((int)R, E, d, f)) {
     // a few rows per expert: the weight-streaming small-batch engine
@@ -465,12 +471,19 @@ int moe_grouped_ffn_bwd(const void* dYs, const void* dYs_q, const uint8_t* dYs_q
   const int acc = (flags & MOE_ACCUMULATE) ? 1 : 0;
   const int eng = gemm_engine(dtype);
   const bool mxw = (flags & MOE_WGRAD_MX) != 0;
-  if (mxw && prec != MOE_PREC_MXFP8) return MOE_ERR_DTYPE;
-  if (mxw && ws_bytes < mx_wgrad_workspace(R, d, f, E)) return MOE_ERR_WORKSPACE;
+  const bool kept = (flags & MOE_MX_KEEP_WEIGHTS) != 0;
+  if ((mxw || kept) && prec != MOE_PREC_MXFP8) return MOE_ERR_DTYPE;
+  // kept: ws = the forward's workspace (with the backward's weight codes),
+  // then the backward's own
+  const size_t kept_bytes = kept ? mx_fwd_workspace(R, d, f, E, true) : 0;
+  if (ws_bytes < kept_bytes) return MOE_ERR_WORKSPACE;
+  void* own = static_cast<char*>(ws) + kept_bytes;
+  const size_t own_bytes = ws_bytes - kept_bytes;
+  if (mxw && own_bytes < mx_wgrad_workspace(R, d, f, E)) return MOE_ERR_WORKSPACE;
   if (prec == MOE_PREC_MXFP8) {
-    if (ws_bytes < mx_bwd_workspace(R, d, f, E)) return MOE_ERR_WORKSPACE;
+    if (own_bytes < mx_bwd_workspace(R, d, f, E)) return MOE_ERR_WORKSPACE;
     MOE_TRY(mx_ffn_dgrad(dYs_q, dYs_q_scale, Hg, Hu, offsets, (int)R, d, f, E, Wg, Wu, Wd, dH,
-                         dXs, ws, num_cu(), st));
+                         dXs, own, kept ? ws : nullptr, num_cu(), st));
   } else {
     GemmArgs g{};
     g.E = E; g.offsets = offsets; g.rows_total = (int)R; g.ragged = RAG_M;
@@ -490,7 +503,7 @@ int moe_grouped_ffn_bwd(const void* dYs, const void* dYs_q, const uint8_t* dYs_q
   }
   if (mxw)
     return status_of(mx_ffn_wgrad(Xs, dH, A, dYs, offsets, (int)R, d, f, E,
-                                  (flags & MOE_WGRAD_F32) ? 1 : 0, acc, dWg, dWu, dWd, ws,
+                                  (flags & MOE_WGRAD_F32) ? 1 : 0, acc, dWg, dWu, dWd, own,
                                   num_cu(), st));
   // weight gradients: dWg|dWu = Xs^T . dH, dWd = A^T . dYs (ragged K = rows of e)
   const GemmKind wk =

@@ -597,9 +597,11 @@ __device__ __forceinline__ void plan_tile(const GemmArgs& g, const Tile& t, int 
   constexpr int BSP = KT<KIND>::BSP;
   // ---- A ----
   if constexpr (KT<KIND>::AK) {
-    // rows t.row0.. of A (global rows), K contiguous
+    // rows t.row0 .. t.row0 + mlim of A (global rows), K contiguous: the
+    // range ends at the tile's last row that exists, so the DMA lanes of the
+    // rows past it (a ragged tail) read zeros without a memory request
     const bf16_t* base = A + (long)t.row0 * g.lda;
-    const long long bytes = ((long long)g.rows_total - t.row0) * g.lda * 2;
+    const long long bytes = (long long)t.mlim * g.lda * 2;
     plan_km<DPO>(pa, base, bytes, nullptr, 0, 1 << 30, g.lda * 2, wave, lane);
   } else {
     // k-rows t.row0 .. t.row0 + klen of A, M contiguous; columns t.m0 + 128 p
@@ -949,10 +951,12 @@ __device__ __forceinline__ void epilogue_lds(const GemmArgs& g, const Tile& tile
   Tile t = tile;
   int lane = lane_in;
   asm volatile("" : "+v"(t.row0), "+v"(t.n0), "+v"(t.m0), "+v"(t.e), "+v"(t.mlim), "+v"(lane));
-  epilogue_block<KIND, 0>(g, t, slice, acc, wm, wn, lane);
-  epilogue_block<KIND, 1>(g, t, slice, acc, wm, wn, lane);
-  epilogue_block<KIND, 2>(g, t, slice, acc, wm, wn, lane);
-  epilogue_block<KIND, 3>(g, t, slice, acc, wm, wn, lane);
+  // 32-row blocks past the tile's last row (a ragged tail) store nothing
+  const int rows = t.mlim - wm * 128;
+  if (rows > 0) epilogue_block<KIND, 0>(g, t, slice, acc, wm, wn, lane);
+  if (rows > 32) epilogue_block<KIND, 1>(g, t, slice, acc, wm, wn, lane);
+  if (rows > 64) epilogue_block<KIND, 2>(g, t, slice, acc, wm, wn, lane);
+  if (rows > 96) epilogue_block<KIND, 3>(g, t, slice, acc, wm, wn, lane);
 }
 
 }  // namespace mf

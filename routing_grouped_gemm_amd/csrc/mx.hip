@@ -35,27 +35,52 @@ namespace moe {
 // ---------------------------------------------------------------------------
 // quantisation kernels
 // ---------------------------------------------------------------------------
-// Dispatch row copy with quantisation: Xs[r] = x[src[r]] in bf16 (for the
-// weight gradients) and Xq[r] / scales along d.  One wave per row.
+// Dispatch row copy with quantisation, token-major: each token row of x is
+// read once (non-temporal: read once), quantised along d once, and written to
+// every one of its k rows r = dest_row[t, j] as Xs[r] (bf16, for the weight
+// gradients), Xq[r] (e4m3 codes) and the block scales of row r.  One wave per
+// token; a lane holds four 8-value chunks 512 columns apart (a 32-value
+// block spans the 4 lanes 4g..4g+3).  A slot whose row lies outside [0, R)
+// writes nothing.
 __global__ __launch_bounds__(256) void mx_dispatch_kernel(const bf16_t* __restrict__ x,
-                                                          const int32_t* __restrict__ src_token,
-                                                          int R, int T, int d, bf16_t* __restrict__ Xs,
+                                                          const int32_t* __restrict__ dest_row,
+                                                          int T, int d, int k,
+                                                          bf16_t* __restrict__ Xs,
                                                           uint8_t* __restrict__ Xq,
                                                           uint8_t* __restrict__ scale, long pitch) {
   const int lane = threadIdx.x & 63;
-  const long r = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (r >= R) return;
-  const int t = min(max(src_token[r], 0), T - 1);
-  const bf16_t* src = x + (long)t * d;
-  for (int c = lane * 8; c < d; c += 512) {
-    const uint4 raw = *reinterpret_cast<const uint4*>(src + c);
-    *reinterpret_cast<uint4*>(Xs + r * d + c) = raw;
-    float v[8];
-    load8(src + c, v);
-    uint32_t codes[2];
-    const int E = quant8(v, codes);
-    *reinterpret_cast<uint2*>(Xq + r * d + c) = make_uint2(codes[0], codes[1]);
-    if ((lane & 3) == 0) scale[(long)(c >> 5) * pitch + r] = (uint8_t)(E + 127);
+  const long t = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int R = T * k;
+  for (int c0 = lane * 8; c0 < d; c0 += 2048) {
+    uint4 raw[4];
+    uint2 q[4];
+    int E[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = min(c0 + 512 * u, d - 8);
+      const u32x4_t w = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(x + t * d + c));
+      raw[u] = uint4{w[0], w[1], w[2], w[3]};
+      float v[8];
+      unpack8(raw[u], v);
+      uint32_t codes[2];
+      E[u] = quant8(v, codes);
+      q[u] = make_uint2(codes[0], codes[1]);
+    }
+    for (int j = 0; j < k; ++j) {
+      const int r = dest_row[t * k + j];
+      if (r < 0 || r >= R) continue;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int c = c0 + 512 * u;
+        if (c < d) {
+          const u32x4_t w = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+          __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t*>(Xs + (long)r * d + c));
+          *reinterpret_cast<uint2*>(Xq + (long)r * d + c) = q[u];
+          if ((lane & 3) == 0) scale[(long)(c >> 5) * pitch + r] = (uint8_t)(E[u] + 127);
+        }
+      }
+    }
   }
 }
 
@@ -148,6 +173,83 @@ __global__ __launch_bounds__(256) void mx_quant_cols_kernel(
       scale[(long)e * s_es + (long)((k0 >> 5) + (q >> 1)) * pitch + row] = (uint8_t)(E + 127);
   }
   (void)lane;
+}
+
+// One pass over W[e][K][N] for both directions of the MXFP8 layer: a tile of
+// 128 (k) x 128 (n) is read from HBM once (16 lanes a 256-byte row), staged
+// in LDS, and quantised
+//  * along N, written as stored exactly as mx_quant_rows_kernel writes it:
+//    codes at dstR + (e*K + k)*dstR_ld + col0 + n, the scale of block b of row
+//    k at sR[e*sR_es + (block0 + b)*pitchR + k] (the input-gradient GEMM's
+//    operand); 16 lanes quantise one row, 8 values each, and write its 128
+//    code bytes as one line;
+//  * along K, written transposed exactly as mx_quant_cols_kernel writes it
+//    (the forward GEMM's operand); a thread takes one column and 64
+//    consecutive k (two whole 32-value blocks), and the two threads of a
+//    column write its 128 code bytes as one line.
+// K and N are multiples of 64 (every width the layer accepts); a tile's
+// halves past them are skipped.
+__global__ __launch_bounds__(256) void mx_quant_both_kernel(
+    const bf16_t* __restrict__ W, int K, int N, uint8_t* __restrict__ dstC, long dstC_es, int half,
+    uint8_t* __restrict__ sC, long sC_es, long pitchC, uint8_t* __restrict__ dstR, long dstR_ld,
+    long col0, uint8_t* __restrict__ sR, long sR_es, long pitchR, int block0) {
+  constexpr int TP = 136;  // LDS row pitch (bf16): 128 + 8
+  __shared__ __attribute__((aligned(16))) bf16_t tile[128 * TP];
+  const int e = blockIdx.z, k0 = blockIdx.y * 128, n0 = blockIdx.x * 128;
+  const int t = threadIdx.x, lane = t & 63;
+  const bf16_t* We = W + (long)e * K * N;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int ch = t + 256 * i, r = ch >> 4, c = (ch & 15) * 8;
+    uint4 a = make_uint4(0, 0, 0, 0);
+    if (k0 + r < K && n0 + c < N)
+      a = *reinterpret_cast<const uint4*>(We + (long)(k0 + r) * N + n0 + c);
+    *reinterpret_cast<uint4*>(&tile[r * TP + c]) = a;
+  }
+  __syncthreads();
+  // along N: rows 16p + t/16, columns 8*(t%16) .. +7
+#pragma unroll 2
+  for (int p = 0; p < 8; ++p) {
+    const int r = 16 * p + (t >> 4), c = (t & 15) * 8;
+    float v[8];
+    unpack8(*reinterpret_cast<const uint4*>(&tile[r * TP + c]), v);
+    const long k = k0 + r;
+    // K and N are multiples of 64: the 4 lanes of a block leave together
+    if (k < K && n0 + c < N)
+      quant8_store(v, dstR + ((long)e * K + k) * dstR_ld + col0 + n0 + c,
+                   sR + (long)e * sR_es + (long)(block0 + ((n0 + c) >> 5)) * pitchR + k, lane);
+  }
+  // along K: column n0 + t%128, k = k0 + 64*(t/128) .. +63
+  const int n = t & 127, h = t >> 7;
+  const int col = n0 + n, kb = k0 + 64 * h;
+  if (col >= N || kb >= K) return;
+  const long row = half >= 0 ? (long)((col >> 7) << 8) + 128 * half + (col & 127) : (long)col;
+  uint32_t w[16];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    float v[32];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      v[i] = bf16_to_f32(tile[(64 * h + 32 * b + i) * TP + n]);
+      amax = fmaxf(amax, fabsf(v[i]));
+    }
+    const int E = mx_block_exponent(amax);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      float sv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sv[i] = ldexpf(v[8 * g + i], -E);
+      uint32_t c2[2];
+      e4m3_codes8(sv, c2);
+      w[8 * b + 2 * g] = c2[0];
+      w[8 * b + 2 * g + 1] = c2[1];
+    }
+    sC[(long)e * sC_es + (long)((kb >> 5) + b) * pitchC + row] = (uint8_t)(E + 127);
+  }
+  uint4* dst = reinterpret_cast<uint4*>(dstC + (long)e * dstC_es + row * K + kb);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dst[i] = make_uint4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
 }
 
 // Weight-gradient operands, quantised along the tokens of each expert.
@@ -381,8 +483,10 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mx_kernel(GemmArgs g) {
       // rows of B for this tile: gate/up panels hold 256 rows per 128 f columns
       const long brow0 = DUAL ? 2L * t.n0 : (long)t.n0;
       const long brows = DUAL ? 2L * ((g.N + 127) / 128) * 128 : (long)g.N;
-      plan_km(P.a, A + (long)t.row0 * g.lda, ((long long)g.rows_total - t.row0) * g.lda, nullptr,
-              0, 1 << 30, g.lda, wave, lane);
+      // A's range ends at the tile's last row that exists: the DMA lanes of
+      // the rows past it (a ragged tail) read zeros without a memory request
+      plan_km(P.a, A + (long)t.row0 * g.lda, (long long)t.mlim * g.lda, nullptr, 0, 1 << 30,
+              g.lda, wave, lane);
       plan_km(P.b, B + (long)t.e * g.b_es + brow0 * g.ldb, (brows - brow0) * g.ldb, nullptr, 0,
               1 << 30, g.ldb, wave, lane);
       const int row_al = t.row0 & ~15;
@@ -547,14 +651,32 @@ hipError_t quant_cols(const void* W, int E, int K, int N, uint8_t* dst, long dst
   return hipGetLastError();
 }
 
+// W[E][K][N] quantised along K into the forward's transposed layout (as
+// quant_cols) and along N into the input gradient's layout (as quant_rows
+// with groups of K rows), from one read of W.
+hipError_t quant_both(const void* W, int E, int K, int N, uint8_t* dstC, long dstC_es, int half,
+                      uint8_t* sC, long sC_es, long pitchC, uint8_t* dstR, long dstR_ld, long col0,
+                      uint8_t* sR, long sR_es, long pitchR, int block0, hipStream_t s) {
+  note_prelaunch("mx_quant_weights", s);
+  hipLaunchKernelGGL(mx_quant_both_kernel, dim3((N + 127) / 128, (K + 127) / 128, E), dim3(256), 0, s,
+                     static_cast<const bf16_t*>(W), K, N, dstC, dstC_es, half, sC, sC_es, pitchC,
+                     dstR, dstR_ld, col0, sR, sR_es, pitchR, block0);
+  note_launch("mx_quant_weights", s);
+  return hipGetLastError();
+}
+
 inline long pitch_rows(long R) { return (R + 15) / 16 * 16; }
 inline long fpanel(int f) { return (f + 127) / 128 * 128; }
 
 // Forward workspace pieces, in carving order.
+// keep: the backward's weight codes follow (moe_grouped_ffn_fwd with
+// MOE_MX_KEEP_WEIGHTS writes them, moe_grouped_ffn_bwd with the flag reads
+// them): Wd along d [E][f][d], and Wg | Wu along f [E][d][2f], with scales.
 struct FwdWs {
   uint8_t *wgu, *wgu_s, *wd, *wd_s, *aq, *aq_s;
+  uint8_t *bwd_wd, *bwd_wd_s, *bwd_wgu, *bwd_wgu_s;
 };
-FwdWs carve_fwd(void* ws, long long R, int d, int f, int E, size_t* total) {
+FwdWs carve_fwd(void* ws, long long R, int d, int f, int E, bool keep, size_t* total) {
   Carve c{static_cast<char*>(ws)};
   FwdWs w;
   const long fp = fpanel(f), Rp = pitch_rows(R);
@@ -564,6 +686,13 @@ FwdWs carve_fwd(void* ws, long long R, int d, int f, int E, size_t* total) {
   w.wd_s = c.take<uint8_t>((size_t)E * (f / 32) * d);
   w.aq = c.take<uint8_t>((size_t)R * f);
   w.aq_s = c.take<uint8_t>((size_t)(f / 32) * Rp);
+  w.bwd_wd = w.bwd_wd_s = w.bwd_wgu = w.bwd_wgu_s = nullptr;
+  if (keep) {
+    w.bwd_wd = c.take<uint8_t>((size_t)E * f * d);
+    w.bwd_wd_s = c.take<uint8_t>((size_t)E * (d / 32) * f);
+    w.bwd_wgu = c.take<uint8_t>((size_t)E * d * 2 * f);
+    w.bwd_wgu_s = c.take<uint8_t>((size_t)E * (2 * f / 32) * d);
+  }
   if (total) *total = c.used;
   return w;
 }
@@ -626,9 +755,9 @@ hipError_t launch_grouped_gemm_mx(GemmKind kind, const GemmArgs& g, int num_cu, 
 
 long mx_scale_pitch(long long R) { return pitch_rows(R); }
 
-size_t mx_fwd_workspace(long long R, int d, int f, int E) {
+size_t mx_fwd_workspace(long long R, int d, int f, int E, bool keep) {
   size_t t = 0;
-  carve_fwd(nullptr, R, d, f, E, &t);
+  carve_fwd(nullptr, R, d, f, E, keep, &t);
   return t;
 }
 
@@ -644,26 +773,37 @@ size_t mx_wgrad_workspace(long long R, int d, int f, int E) {
   return t;
 }
 
-hipError_t launch_mx_dispatch_copy(const void* x, const int32_t* src_token, int R, int T, int d,
+hipError_t launch_mx_dispatch_copy(const void* x, const int32_t* dest_row, int T, int d, int k,
                                    void* Xs, void* Xq, uint8_t* Xq_scale, hipStream_t s) {
-  if (R == 0) return hipSuccess;
+  if (T == 0) return hipSuccess;
   note_prelaunch("mx_dispatch_quant", s);
-  hipLaunchKernelGGL(mx_dispatch_kernel, dim3((R + 3) / 4), dim3(256), 0, s,
-                     static_cast<const bf16_t*>(x), src_token, R, T, d, static_cast<bf16_t*>(Xs),
-                     static_cast<uint8_t*>(Xq), Xq_scale, pitch_rows(R));
+  hipLaunchKernelGGL(mx_dispatch_kernel, dim3((T + 3) / 4), dim3(256), 0, s,
+                     static_cast<const bf16_t*>(x), dest_row, T, d, k, static_cast<bf16_t*>(Xs),
+                     static_cast<uint8_t*>(Xq), Xq_scale, pitch_rows((long)T * k));
   note_launch("mx_dispatch_quant", s);
   return hipGetLastError();
 }
 
 hipError_t mx_ffn_fwd(const void* Xq, const uint8_t* Xscale, const int32_t* offsets, int R, int d,
                       int f, int E, const void* Wg, const void* Wu, const void* Wd, void* Hg,
-                      void* Hu, void* A, void* Ys, void* ws, int num_cu, hipStream_t s) {
-  const FwdWs w = carve_fwd(ws, R, d, f, E, nullptr);
+                      void* Hu, void* A, void* Ys, void* ws, bool keep, int num_cu,
+                      hipStream_t s) {
+  const FwdWs w = carve_fwd(ws, R, d, f, E, keep, nullptr);
   const long fp = fpanel(f), Rp = pitch_rows(R);
-  // weights: Wg, Wu along d into the gate/up panels; Wd along f, transposed
-  MX_TRY(quant_cols(Wg, E, d, f, w.wgu, 2 * fp * d, 0, w.wgu_s, (d / 32) * 2 * fp, 2 * fp, s));
-  MX_TRY(quant_cols(Wu, E, d, f, w.wgu, 2 * fp * d, 1, w.wgu_s, (d / 32) * 2 * fp, 2 * fp, s));
-  MX_TRY(quant_cols(Wd, E, f, d, w.wd, (long)d * f, -1, w.wd_s, (long)(f / 32) * d, d, s));
+  // weights: Wg, Wu along d into the gate/up panels; Wd along f, transposed;
+  // keep: in the same pass, Wd along d and Wg | Wu along f for the backward
+  if (keep) {
+    MX_TRY(quant_both(Wg, E, d, f, w.wgu, 2 * fp * d, 0, w.wgu_s, (d / 32) * 2 * fp, 2 * fp,
+                      w.bwd_wgu, 2L * f, 0, w.bwd_wgu_s, (long)(2 * f / 32) * d, d, 0, s));
+    MX_TRY(quant_both(Wu, E, d, f, w.wgu, 2 * fp * d, 1, w.wgu_s, (d / 32) * 2 * fp, 2 * fp,
+                      w.bwd_wgu, 2L * f, f, w.bwd_wgu_s, (long)(2 * f / 32) * d, d, f / 32, s));
+    MX_TRY(quant_both(Wd, E, f, d, w.wd, (long)d * f, -1, w.wd_s, (long)(f / 32) * d, d,
+                      w.bwd_wd, d, 0, w.bwd_wd_s, (long)(d / 32) * f, f, 0, s));
+  } else {
+    MX_TRY(quant_cols(Wg, E, d, f, w.wgu, 2 * fp * d, 0, w.wgu_s, (d / 32) * 2 * fp, 2 * fp, s));
+    MX_TRY(quant_cols(Wu, E, d, f, w.wgu, 2 * fp * d, 1, w.wgu_s, (d / 32) * 2 * fp, 2 * fp, s));
+    MX_TRY(quant_cols(Wd, E, f, d, w.wd, (long)d * f, -1, w.wd_s, (long)(f / 32) * d, d, s));
+  }
   GemmArgs g{};
   g.E = E; g.offsets = offsets; g.rows_total = R; g.ragged = RAG_M;
   g.N = f; g.K = d;
@@ -686,11 +826,17 @@ hipError_t mx_ffn_fwd(const void* Xq, const uint8_t* Xscale, const int32_t* offs
 hipError_t mx_ffn_dgrad(const void* dYsq, const uint8_t* dYsq_scale, const void* Hg,
                         const void* Hu, const int32_t* offsets, int R, int d, int f, int E,
                         const void* Wg, const void* Wu, const void* Wd, void* dH, void* dXs,
-                        void* ws, int num_cu, hipStream_t s) {
-  const BwdWs w = carve_bwd(ws, R, d, f, E, nullptr);
+                        void* ws, const void* kept, int num_cu, hipStream_t s) {
+  BwdWs w = carve_bwd(ws, R, d, f, E, nullptr);
   const long Rp = pitch_rows(R);
-  // down dgrad: dYs (quantised along d by the combine backward) and Wd along d
-  MX_TRY(quant_rows(Wd, (long)E * f, d, d, w.wd, d, 0, w.wd_s, f, (long)(d / 32) * f, f, 0, s));
+  if (kept) {
+    // the forward's workspace holds Wd along d and Wg | Wu along f already
+    const FwdWs k = carve_fwd(const_cast<void*>(kept), R, d, f, E, true, nullptr);
+    w.wd = k.bwd_wd; w.wd_s = k.bwd_wd_s; w.wgu = k.bwd_wgu; w.wgu_s = k.bwd_wgu_s;
+  } else {
+    // down dgrad: dYs (quantised along d by the combine backward) and Wd along d
+    MX_TRY(quant_rows(Wd, (long)E * f, d, d, w.wd, d, 0, w.wd_s, f, (long)(d / 32) * f, f, 0, s));
+  }
   GemmArgs g{};
   g.E = E; g.offsets = offsets; g.rows_total = R; g.ragged = RAG_M;
   g.N = f; g.K = d;
@@ -702,10 +848,12 @@ hipError_t mx_ffn_dgrad(const void* dYsq, const uint8_t* dYsq_scale, const void*
   g.q0 = w.dhq; g.qs = w.dhq_s; g.qs_pitch = Rp;   // dH quantised along 2f in the epilogue
   MX_TRY(launch_grouped_gemm_mx(GK_MX_DGRAD_DOWN, g, num_cu, s));
   // gate/up dgrad: Wg | Wu along f into one [d][2f] matrix per expert
-  MX_TRY(quant_rows(Wg, (long)E * d, f, f, w.wgu, 2L * f, 0, w.wgu_s, d, (long)(2 * f / 32) * d, d,
-                    0, s));
-  MX_TRY(quant_rows(Wu, (long)E * d, f, f, w.wgu, 2L * f, f, w.wgu_s, d, (long)(2 * f / 32) * d, d,
-                    f / 32, s));
+  if (!kept) {
+    MX_TRY(quant_rows(Wg, (long)E * d, f, f, w.wgu, 2L * f, 0, w.wgu_s, d, (long)(2 * f / 32) * d,
+                      d, 0, s));
+    MX_TRY(quant_rows(Wu, (long)E * d, f, f, w.wgu, 2L * f, f, w.wgu_s, d, (long)(2 * f / 32) * d,
+                      d, f / 32, s));
+  }
   GemmArgs h{};
   h.E = E; h.offsets = offsets; h.rows_total = R; h.ragged = RAG_M;
   h.N = d; h.K = 2 * f;

@@ -158,7 +158,7 @@ def test_dispatch_validation(L):
 
 
 def ffn_fwd(L, T=16, k=2, d=64, f=64, E=8, dt=BF16, prec=P_BF16, Xs=A, Wg=A):
-    return L.moe_grouped_ffn_fwd(Xs, A, A, T, k, d, f, E, Wg, A, A, dt, prec, A, A, A, A,
+    return L.moe_grouped_ffn_fwd(Xs, A, A, T, k, d, f, E, Wg, A, A, dt, prec, 0, A, A, A, A,
                                  A, 1 << 20, None)
 
 
@@ -237,7 +237,7 @@ def test_ffn_offset_limits(L):
     the limit the call gets as far as the alignment check (a misaligned
     pointer makes it stop there, so nothing is launched)."""
     fwd = lambda T, k, d, f, Wg=A: L.moe_grouped_ffn_fwd(A, A, A, T, k, d, f, 8, Wg, A, A, BF16,
-                                                         P_BF16, A, A, A, A, A, 1 << 20, None)
+                                                         P_BF16, 0, A, A, A, A, A, 1 << 20, None)
     # one expert's weights: d * (f + 128) * 2 bytes below 2^32
     assert fwd(16, 2, 65536, 32768) == UNSUP
     assert fwd(16, 2, 32768, 32640, Wg=MIS) == ALIGN
@@ -271,3 +271,25 @@ def test_dispatch_noalloc_validation(L):
     assert f(*args(1 << 20, 64)) == SCRATCH          # 2 * 16384 * 64 * 4 B = 8 MiB
     assert f(*args(1 << 19, 64 + 1)) == SCRATCH       # just over 4 MiB
     assert f(*args(1 << 18, 256, prec=P_MX)) == SCRATCH   # 8 MiB
+
+
+def test_mx_keep_weights_flag(L):
+    """MOE_MX_KEEP_WEIGHTS exists for the MXFP8 precision only, and both
+    directions check that the workspace holds the kept codes."""
+    KEEP = 0x20
+    fwd = lambda prec, flags, wsb: L.moe_grouped_ffn_fwd(A, A, A, 16, 2, 64, 64, 8, A, A, A, BF16,
+                                                         prec, flags, A, A, A, A, A, wsb, None)
+    assert fwd(P_BF16, KEEP, 1 << 30) == DTYPE
+    need = ws_size(L, 10, 16, 64, 8, 64, 2, BF16, P_MX)[1]
+    plain = ws_size(L, 2, 16, 64, 8, 64, 2, BF16, P_MX)[1]
+    assert need > plain > 0
+    assert fwd(P_MX, KEEP, need - 1) == WS
+    assert fwd(P_MX, 0, plain - 1) == WS
+    bwd = lambda prec, flags, wsb: L.moe_grouped_ffn_bwd(A, A, A, A, A, A, A, A, 16, 2, 64, 64, 8,
+                                                         A, A, A, BF16, prec, flags, A, A, A, A,
+                                                         A, A, wsb, None)
+    own = ws_size(L, 5, 16, 64, 8, 64, 2, BF16, P_MX)[1]
+    assert bwd(P_BF16, KEEP, 1 << 30) == DTYPE
+    assert bwd(P_MX, KEEP, need + own - 1) == WS
+    out = ctypes.c_size_t(0)
+    assert L.moe_workspace_size(10, 16, 64, 8, 64, 2, BF16, P_BF16, ctypes.byref(out)) == DTYPE

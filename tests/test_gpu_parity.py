@@ -427,3 +427,41 @@ def test_out_of_range_slots_are_empty(T, k):
     for n in refs:
         gate(n, gpu[n], refs[n], TOL["bf16"], errs)
     check_gates(f"out-of-range T={T}", errs, TOL["bf16"])
+
+
+@pytest.mark.parametrize("name", ["mid_mxfp8_E8", "share_zipf_mxfp8"])
+def test_mx_keep_weights_same_bytes(name):
+    """The MXFP8 layer quantises each weight matrix once for both directions
+    and hands the backward's codes over in the forward's workspace
+    (MOE_MX_KEEP_WEIGHTS, the layer's default); the grouped FFN forward and
+    backward run again without the flag, each quantising its own weights,
+    give the same bytes in every output."""
+    import routing_grouped_gemm_amd as rgg
+    wl, inp, logits = _layer_case(name)
+    dt = torch.bfloat16
+    router = wl.routing == "router"
+    layer = rgg.ExpertLayer(wl.T, wl.d, wl.E, wl.f, wl.k, dt, "mxfp8", router=router)
+    x = dev_tensor(inp, "x", dt)
+    Wg, Wu, Wd = (dev_tensor(inp, n, dt) for n in ("Wg", "Wu", "Wd"))
+    kw = dict(logits=rgg.upload(np.ascontiguousarray(logits, np.float32))) if router else \
+        dict(topk_idx=rgg.upload(inp["topk_idx"]), topk_w=rgg.upload(inp["topk_w"]))
+    layer.forward(x, dev_tensor(inp, "Wr", dt) if router else None, Wg, Wu, Wd, **kw)
+    layer.backward(dev_tensor(inp, "dY", dt))
+    torch.cuda.synchronize()
+    kept = {n: getattr(layer, n).clone() for n in ("Hg", "Hu", "A", "Ys", "dH", "dXs", "dWg",
+                                                    "dWu", "dWd")}
+    T, d, E, f, k = wl.T, wl.d, wl.E, wl.f, wl.k
+    ws_f = torch.empty(rgg.moe_workspace_size("ffn_fwd", T, d, E, f, k, dt, "mxfp8"),
+                       dtype=torch.uint8, device="cuda")
+    ws_b = torch.empty(rgg.moe_workspace_size("ffn_bwd", T, d, E, f, k, dt, "mxfp8"),
+                       dtype=torch.uint8, device="cuda")
+    out = {n: torch.empty_like(v) for n, v in kept.items()}
+    rgg.moe_grouped_ffn_fwd(layer.Xq, layer.Xq_scale, layer.offsets, T, k, Wg, Wu, Wd, out["Hg"],
+                            out["Hu"], out["A"], out["Ys"], ws_f, "mxfp8")
+    rgg.moe_grouped_ffn_bwd(layer.dYs, layer.Xs, out["Hg"], out["Hu"], out["A"], layer.offsets, T,
+                            k, Wg, Wu, Wd, out["dH"], out["dXs"], out["dWg"], out["dWu"],
+                            out["dWd"], ws_b, "mxfp8", False, layer.dYs_q, layer.dYs_q_scale)
+    torch.cuda.synchronize()
+    for n in kept:
+        assert torch.equal(kept[n].view(torch.int16), out[n].view(torch.int16)), n
+    say(f"  {name}: kept-code layer equals the self-quantising FFN bit for bit")
