@@ -15,6 +15,10 @@ kernel give the per-kernel table and name the dominant kernel; inside the
 timed region only that kernel's launches are bracketed by HIP events on the
 library's stream, and their mean duration gives the `roofline` object.
 `cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+`clock` is read by a pure-MFMA probe right after the timed steps.  For the
+default (OLMoE-shaped, bf16) workload, the two ends of the expert-count scan
+and the MXFP8 layer are also timed in the same run ("companions"), for the
+E=128 / E=8 throughput ratio and the MXFP8 speed-up.
 """
 from __future__ import annotations
 
@@ -166,6 +170,78 @@ def write_traffic(workload_name, fetch_dir, write_dir, cal_fetch_dir, cal_write_
     return 0
 
 
+def mfma_summary(workload_name: str, directory: str) -> int:
+    """Per-kernel MFMA utilisation and clock from one rocprofv3 --pmc run.
+
+    SQ_VALU_MFMA_BUSY_CYCLES counts 32 SIMD cycles per issued 32x32x16 bf16
+    MFMA (64 per scaled fp8 32x32x64), so against 4 SIMDs x SQ_BUSY_CU_CYCLES
+    (busy cycles summed over the CUs) it is the fraction of SIMD cycles the
+    matrix cores were busy; the clock probe (pure MFMA work) reads 100% this
+    way.  GRBM_GUI_ACTIVE sums the busy cycles of the 8 XCDs, so / 8 over the
+    dispatch's duration is the clock it ran at."""
+    import csv
+    import glob
+    from moe_synth import workload
+    wl = workload(workload_name)
+    files = glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {directory}")
+    disp = {}
+    for path in files:
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                d = disp.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"],
+                                                            "ns": int(r["End_Timestamp"]) -
+                                                            int(r["Start_Timestamp"])})
+                d[r["Counter_Name"]] = float(r["Counter_Value"])
+    seen, acc = {}, {}
+    for i in sorted(disp):
+        d = disp[i]
+        name = d["name"].split("(")[0].replace("void ", "")
+        for pre in ("moe::mf::", "moe::mf8::", "moe::sk::", "moe::"):
+            name = name.replace(pre, "")
+        sym = next((k for k in _SYMBOLS if name.startswith(k.split("<")[0]) and
+                    (("<" not in k) or name.startswith(k))), name)
+        if "clock_probe" in d["name"]:
+            launch = "clock_probe (pure MFMA, every CU)"
+        else:
+            n = seen.get(sym, 0)
+            seen[sym] = n + 1
+            names = _SYMBOLS.get(sym, [sym])
+            launch = names[n % len(names)]
+        acc.setdefault(launch, []).append(d)
+    print("| kernel | launches | mean µs | clock MHz | MFMA busy (% of SIMD cycles) | "
+          "algorithmic TFLOP/s | frac of 2.5 PF | frac of peak at its clock |")
+    print("|---|---:|---:|---:|---:|---:|---:|---:|")
+    order = sorted(acc, key=lambda k: -sum(x["ns"] for x in acc[k]))
+    for k in order:
+        ds = acc[k]
+        need = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES", "GRBM_GUI_ACTIVE")
+        if not all(c in ds[0] for c in need):
+            continue
+        us = sum(x["ns"] for x in ds) / len(ds) / 1e3
+        mhz = sum(x["GRBM_GUI_ACTIVE"] / 8.0 / (x["ns"] * 1e-3) for x in ds) / len(ds)
+        busy = sum(x["SQ_VALU_MFMA_BUSY_CYCLES"] for x in ds) / \
+            max(1.0, 4.0 * sum(x["SQ_BUSY_CU_CYCLES"] for x in ds))
+        fl = gemm_flops(k, wl)
+        peak = PEAK_TFLOPS["mxfp8" if k.startswith("gemm_mx_") else "bf16"]
+        if k.startswith("clock_probe"):
+            fl = None
+        if fl:
+            tf = fl / (us * 1e-6) / 1e12
+            at_clk = f"{tf / (peak * mhz / 2400.0):.3f}" if us >= 100.0 else "-"
+            cols = f"{tf:.0f} | {tf / peak:.3f} | {at_clk}"
+        else:
+            cols = "- | - | -"
+        if busy == 0.0 and not fl and not k.startswith("clock_probe"):
+            continue
+        # the busy-cycle window of a dispatch shorter than ~0.1 ms does not
+        # match its timestamps well enough for a clock
+        clk = f"{mhz:.0f}" if us >= 100.0 else "-"
+        print(f"| `{k}` | {len(ds)} | {us:.1f} | {clk} | {100.0 * busy:.1f} | {cols} |")
+    return 0
+
+
 def measured_traffic(workload_name: str, kernel: str):
     """HBM bytes per launch of `kernel` from the committed counter summary, or
     None when there is none or the sources changed since it was taken."""
@@ -216,9 +292,16 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-tokens", type=int, default=2048,
                     help="tokens of the CPU-oracle sample (0 = skip the CPU baseline)")
     ap.add_argument("--kernels", action="store_true", help="per-kernel table on stderr")
+    ap.add_argument("--no-companions", action="store_true",
+                    help="skip the companion runs of the default workload (expert-count scan "
+                         "ends and MXFP8, timed in the same run for the ratio keys)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times (the "
                          "known-size reference for HBM byte counters) and exit")
+    ap.add_argument("--mfma-summary", metavar="PMC_DIR",
+                    help="only summarise a rocprofv3 --pmc run of SQ_VALU_MFMA_BUSY_CYCLES, "
+                         "SQ_BUSY_CU_CYCLES and GRBM_GUI_ACTIVE (this workload, with the clock "
+                         "probe) as a markdown table on stdout and exit")
     ap.add_argument("--traffic", nargs=4, metavar=("FETCH", "WRITE", "CAL_FETCH", "CAL_WRITE"),
                     help="only summarise four rocprofv3 --pmc output directories (FETCH_SIZE and "
                          "WRITE_SIZE of this workload, then of --calibrate-copy 1024) into "
@@ -227,6 +310,8 @@ def main(argv=None) -> int:
 
     if args.traffic:
         return write_traffic(args.workload, *args.traffic)
+    if args.mfma_summary:
+        return mfma_summary(args.workload, args.mfma_summary)
 
     if args.calibrate_copy:
         import torch
@@ -351,6 +436,16 @@ def main(argv=None) -> int:
     if args.cpu_tokens > 0:
         cpu = cpu_baseline(wl, inp, args.cpu_tokens)
 
+    # clock under MFMA load and the sustained dense MFMA rate, right after the
+    # timed steps (a pure-MFMA probe on every CU)
+    clk = rgg.probe_clock()
+
+    companions = None
+    if wl.name == "olmoe_bf16" and not args.no_companions:
+        del layer, x, dY, Wg, Wu, Wd, Wr, kw, inp
+        torch.cuda.empty_cache()
+        companions = {n: time_workload(n, args.seed) for n in COMPANIONS}
+
     if args.kernels:
         print(f"{'kernel':32s} {'launches/step':>13s} {'ms/step':>9s} {'ms/launch':>10s}",
               file=sys.stderr)
@@ -384,9 +479,74 @@ def main(argv=None) -> int:
         "kernels_ms_per_step": {n: round(tot, 4) for n, _, tot, _ in table},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "clock": {"mhz_under_mfma_load": round(clk["clock_mhz"], 1),
+                  "mhz_over_event_time": round(clk["event_clock_mhz"], 1),
+                  "realtime_counter_mhz_over_event_time": round(clk["realtime_mhz"], 2),
+                  "probe_mfma_tflops": round(clk["mfma_tflops"], 1),
+                  "bf16_peak_at_measured_clock_tflops":
+                      round(PEAK_TFLOPS["bf16"] * clk["clock_mhz"] / 2400.0, 1)},
     }
+    if ffn_tflops is not None:
+        out["ffn_gemm_pct_of_peak_at_measured_clock"] = round(
+            100.0 * ffn_tflops / (peak * clk["clock_mhz"] / 2400.0), 2)
+    if companions:
+        out["companions"] = companions
+        e8, e128 = companions["escan_e8_bf16"], companions["escan_e128_bf16"]
+        out["expert_scan_tokens_ratio_e128_over_e8"] = round(e128["tokens_per_s"] /
+                                                             e8["tokens_per_s"], 4)
+        out["mxfp8_speedup_over_bf16"] = round(ms / companions["olmoe_mxfp8"]["ms_per_step"], 4)
     print(json.dumps(out), flush=True)
     return 0
+
+
+# Workloads timed beside the default one (same run, same box): both ends of
+# the expert-count scan (16384 tokens, d 4096, f 1536, top-4; 8 and 128
+# experts) and the OLMoE-shaped layer with MXFP8 expert GEMMs.
+COMPANIONS = ("escan_e8_bf16", "escan_e128_bf16", "olmoe_mxfp8")
+
+
+def time_workload(name: str, seed: int, steps: int = 10, warmup: int = 3):
+    """ms per forward+backward step of a workload (events around the steps,
+    nothing else timed), with its inputs resident on the GPU."""
+    import numpy as np
+    import torch
+    import routing_grouped_gemm_amd as rgg
+    from moe_synth import workload, make_inputs
+    wl = workload(name)
+    inp = make_inputs(wl, seed=seed)
+    up = lambda n: rgg.upload(inp[n + "_bits"], torch.bfloat16)
+    router = wl.routing == "router"
+    x, dY, Wg, Wu, Wd = up("x"), up("dY"), up("Wg"), up("Wu"), up("Wd")
+    Wr = up("Wr") if router else None
+    kw = {} if router else dict(topk_idx=rgg.upload(inp["topk_idx"]),
+                                topk_w=rgg.upload(inp["topk_w"]))
+    del inp
+    layer = rgg.ExpertLayer(wl.T, wl.d, wl.E, wl.f, wl.k, torch.bfloat16, wl.prec, router=router,
+                            mx_wgrad=wl.mx_wgrad)
+
+    def step():
+        layer.forward(x, Wr, Wg, Wu, Wd, **kw)
+        layer.backward(dY)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    for i in range(steps):
+        marks[i].record()
+        step()
+    marks[steps].record()
+    torch.cuda.synchronize()
+    per = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(steps)])
+    ms = float(marks[0].elapsed_time(marks[steps])) / steps
+    out = {"ms_per_step": round(ms, 4), "tokens_per_s": round(wl.T / (ms * 1e-3), 1),
+           "tflops": round(wl.flops() / (ms * 1e-3) / 1e12, 2), "steps": steps,
+           "warmup": warmup, "step_ms_median": round(float(np.median(per)), 4),
+           "config": {"T": wl.T, "d_model": wl.d, "experts": wl.E, "d_ff": wl.f, "top_k": wl.k,
+                      "precision": wl.prec}}
+    del layer, x, dY, Wg, Wu, Wd, Wr, kw
+    torch.cuda.empty_cache()
+    return out
 
 
 def fwd_gemm_bytes(name: str, wl, active: int) -> float:

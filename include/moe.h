@@ -367,6 +367,21 @@ int moe_set_kernel_events(void* const* events, const char** names, int capacity,
  */
 int moe_set_kernel_filter(const char* name);
 
+/*
+ * moe_probe_clock -- clock probe (observability only).  Launches `grid`
+ * workgroups of 256 threads on `stream`; each runs `iters` rounds of 8
+ * independent v_mfma_f32_32x32x16_bf16 per wave on register data (no memory
+ * traffic), the load the expert GEMMs put on the matrix cores, and its first
+ * thread writes the shader clock counter (s_memtime) and the constant-rate
+ * counter (s_memrealtime) before and after that work to
+ * ticks[4b .. 4b+3] = {memtime start, memtime end, realtime start, realtime
+ * end} (device memory, 16-byte aligned, 4*grid entries, owned by the
+ * caller).  With the launch timed by events, (memtime end - start) / time
+ * gives the clock under MFMA load, and 8 * 32768 * 4 * iters * grid FLOP /
+ * time the sustained dense bf16 MFMA rate.
+ */
+int moe_probe_clock(unsigned long long* ticks, int grid, int iters, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

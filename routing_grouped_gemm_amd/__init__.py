@@ -26,7 +26,7 @@ __all__ = [
     "moe_combine_bwd", "moe_grouped_ffn_bwd", "moe_dispatch_bwd", "moe_route_bwd",
     "moe_route_aux", "moe_workspace_size", "moe_status_string", "ExpertLayer", "LIB_PATH",
     "MOE_ROUTE_LOGITS_IN", "MOE_ROUTE_RENORM", "MOE_ACCUMULATE", "MOE_WGRAD_F32", "MOE_MX_KEEP_WEIGHTS",
-    "KernelTimer", "upload", "mx_scale_pitch",
+    "KernelTimer", "upload", "mx_scale_pitch", "probe_clock",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_hip.so")
@@ -79,6 +79,8 @@ def lib() -> ctypes.CDLL:
         L.moe_set_kernel_events.restype = ctypes.c_int
         L.moe_set_kernel_filter.argtypes = [ctypes.c_char_p]
         L.moe_set_kernel_filter.restype = ctypes.c_int
+        L.moe_probe_clock.argtypes = [_P, _I, _I, _P]
+        L.moe_probe_clock.restype = ctypes.c_int
         L.moe_last_launch_error.argtypes = []
         L.moe_last_launch_error.restype = ctypes.c_char_p
         L.moe_status_string.argtypes = [ctypes.c_int]
@@ -177,6 +179,36 @@ def moe_dispatch_noalloc(x, topk_idx, E, counts, offsets, dest_row, src_token, X
                                       _ptr(src_token), _ptr(Xs), _ptr(Xq), _ptr(Xq_scale),
                                       _stream(stream)),
            "moe_dispatch_noalloc")
+
+
+REALTIME_MHZ = 100.0   # rate of the constant-rate counter that s_memrealtime reads
+
+
+def probe_clock(grid: int = 256, iters: int = 20000, stream=None):
+    """Clock under MFMA load and the sustained dense bf16 MFMA rate, from one
+    moe_probe_clock launch (after an untimed one that loads the kernel).
+    clock_mhz: shader clock cycles per constant-rate tick x 100 MHz;
+    event_clock_mhz / realtime_mhz: the same counts over the launch's HIP-event
+    time (a check: realtime_mhz near 100 means the event window is the
+    kernel's); mfma_tflops: the probe's FLOPs over its constant-rate time."""
+    ticks = torch.zeros(4 * grid, dtype=torch.int64, device="cuda")
+    st = torch.cuda.current_stream() if stream is None else stream
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(st):
+        _check(lib().moe_probe_clock(_ptr(ticks), grid, 16, _stream(st)), "moe_probe_clock")
+        e0.record()
+        _check(lib().moe_probe_clock(_ptr(ticks), grid, iters, _stream(st)), "moe_probe_clock")
+        e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3
+    t = ticks.view(grid, 4).cpu().double()
+    cyc = float((t[:, 1] - t[:, 0]).mean())
+    rt = float((t[:, 3] - t[:, 2]).mean())
+    rt_us = rt / REALTIME_MHZ
+    flops = 8.0 * 32768 * 4 * iters * grid
+    return {"clock_mhz": cyc / rt * REALTIME_MHZ, "event_clock_mhz": cyc / us,
+            "realtime_mhz": rt / us, "mfma_tflops": flops / (rt_us * 1e-6) / 1e12,
+            "probe_us": rt_us}
 
 
 def mx_scale_pitch(R: int) -> int:

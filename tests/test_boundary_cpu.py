@@ -36,7 +36,7 @@ def declared_entry_points():
 
 def test_exports_every_declared_symbol(L):
     names = declared_entry_points()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     for n in names:
         assert hasattr(L, n), n
 
