@@ -328,6 +328,22 @@ int moe_route_bwd(const void* x, const void* Wr, const float* logits,
 int moe_route_aux(const float* logits, const int32_t* counts, int T, int E, int k, float coef,
                   float* aux_loss, float* aux_dp, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * moe_check_routing -- device-side check of pre-routed expert indices (the
+ * preconditions the host cannot see without a copy; an optional debugging
+ * step before moe_dispatch, in the spirit of the pages' convention of
+ * failing early rather than silently changing behaviour: OLMo-core 3 release
+ * summary, technical principle section).  Enqueues two small kernels that
+ * write, once they have run,
+ *   report[0] = number of entries of topk_idx[T,k] outside [0, E)
+ *   report[1] = number of tokens whose in-range experts are not all distinct
+ * (report: 2 int32 in device memory, 16-byte aligned, owned by the caller;
+ * read it after the stream reaches this point).  Nothing else is written and
+ * nothing synchronises.  E <= 256, else MOE_ERR_UNSUPPORTED.
+ */
+int moe_check_routing(const int32_t* topk_idx, int T, int E, int k, int32_t* report,
+                      void* stream);
+
 /* Workspace bytes an operation needs for these sizes (0 is a valid answer). */
 int moe_workspace_size(int op, int T, int d, int E, int f, int k, int dtype, int prec,
                        size_t* bytes);

@@ -24,7 +24,8 @@ import torch
 __all__ = [
     "lib", "moe_route", "moe_dispatch", "moe_dispatch_noalloc", "moe_grouped_ffn_fwd", "moe_combine",
     "moe_combine_bwd", "moe_grouped_ffn_bwd", "moe_dispatch_bwd", "moe_route_bwd",
-    "moe_route_aux", "moe_workspace_size", "moe_status_string", "ExpertLayer", "LIB_PATH",
+    "moe_route_aux", "moe_check_routing", "moe_workspace_size", "moe_status_string",
+    "ExpertLayer", "LIB_PATH",
     "MOE_ROUTE_LOGITS_IN", "MOE_ROUTE_RENORM", "MOE_ACCUMULATE", "MOE_WGRAD_F32", "MOE_MX_KEEP_WEIGHTS",
     "KernelTimer", "upload", "mx_scale_pitch", "probe_clock",
 ]
@@ -58,6 +59,7 @@ _SIGS = {
     "moe_route_bwd": [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _U, _P, _P, _P, _P, _S, _P],
     "moe_route_aux": [_P, _P, _I, _I, _I, ctypes.c_float, _P, _P, _P, _S, _P],
     "moe_workspace_size": [_I, _I, _I, _I, _I, _I, _I, _I, ctypes.POINTER(ctypes.c_size_t)],
+    "moe_check_routing": [_P, _I, _I, _I, _P, _P],
 }
 
 _lib: Optional[ctypes.CDLL] = None
@@ -209,6 +211,15 @@ def probe_clock(grid: int = 256, iters: int = 20000, stream=None):
     return {"clock_mhz": cyc / rt * REALTIME_MHZ, "event_clock_mhz": cyc / us,
             "realtime_mhz": rt / us, "mfma_tflops": flops / (rt_us * 1e-6) / 1e12,
             "probe_us": rt_us}
+
+
+def moe_check_routing(topk_idx, E, report, stream=None):
+    """Enqueue the device check of pre-routed indices; report (int32 [2], on
+    the GPU) receives the out-of-range entry count and the count of tokens
+    with a repeated expert."""
+    T, k = topk_idx.shape
+    _check(lib().moe_check_routing(_ptr(topk_idx), T, E, k, _ptr(report), _stream(stream)),
+           "moe_check_routing")
 
 
 def mx_scale_pitch(R: int) -> int:

@@ -601,6 +601,17 @@ int moe_route_bwd(const void* x, const void* Wr, const float* logits, const int3
   return status_of(launch_grouped_gemm(GK_ROUTER_DX, eng, h, num_cu(), st));
 }
 
+int moe_check_routing(const int32_t* topk_idx, int T, int E, int k, int32_t* report,
+                      void* stream) {
+  if (!all_nonnull(topk_idx, report)) return MOE_ERR_NULL;
+  if (T <= 0 || E <= 0 || k <= 0 || (long long)T * k > 0x7fffffffLL) return MOE_ERR_SHAPE;
+  if (E > 256) return MOE_ERR_UNSUPPORTED;
+  if (!all_aligned(topk_idx, report)) return MOE_ERR_ALIGN;
+  clear_stale_error();
+  return status_of(launch_check_routing(topk_idx, T, E, k, report,
+                                        static_cast<hipStream_t>(stream)));
+}
+
 int moe_route_aux(const float* logits, const int32_t* counts, int T, int E, int k, float coef,
                   float* aux_loss, float* aux_dp, void* ws, size_t ws_bytes, void* stream) {
   if (!all_nonnull(logits, counts, aux_loss, aux_dp, ws)) return MOE_ERR_NULL;

@@ -184,9 +184,10 @@ __global__ __launch_bounds__(256) void mx_quant_cols_kernel(
 //    operand); 16 lanes quantise one row, 8 values each, and write its 128
 //    code bytes as one line;
 //  * along K, written transposed exactly as mx_quant_cols_kernel writes it
-//    (the forward GEMM's operand); a thread takes one column and 64
-//    consecutive k (two whole 32-value blocks), and the two threads of a
-//    column write its 128 code bytes as one line.
+//    (the forward GEMM's operand); a thread takes two adjacent columns (one
+//    4-byte LDS read gives both) and one whole 32-value block of each, and
+//    the four threads of a column pair write each column's 128 code bytes
+//    as one line.
 // K and N are multiples of 64 (every width the layer accepts); a tile's
 // halves past them are skipped.
 __global__ __launch_bounds__(256) void mx_quant_both_kernel(
@@ -219,22 +220,26 @@ __global__ __launch_bounds__(256) void mx_quant_both_kernel(
       quant8_store(v, dstR + ((long)e * K + k) * dstR_ld + col0 + n0 + c,
                    sR + (long)e * sR_es + (long)(block0 + ((n0 + c) >> 5)) * pitchR + k, lane);
   }
-  // along K: column n0 + t%128, k = k0 + 64*(t/128) .. +63
-  const int n = t & 127, h = t >> 7;
-  const int col = n0 + n, kb = k0 + 64 * h;
-  if (col >= N || kb >= K) return;
-  const long row = half >= 0 ? (long)((col >> 7) << 8) + 128 * half + (col & 127) : (long)col;
-  uint32_t w[16];
+  // along K: columns n0 + 2*(t%64) and +1, k = k0 + 32*(t/64) .. +31 (one
+  // whole 32-value block of each of the two columns, read 4 bytes at a time)
+  const int n = 2 * (t & 63), b = t >> 6;
+  const int kb = k0 + 32 * b;
+  if (n0 + n >= N || kb >= K) return;
+  float v0[32], v1[32];
+  float a0 = 0.0f, a1 = 0.0f;
 #pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    float v[32];
-    float amax = 0.0f;
+  for (int i = 0; i < 32; ++i) {
+    const uint32_t w2 = *reinterpret_cast<const uint32_t*>(&tile[(32 * b + i) * TP + n]);
+    v0[i] = __uint_as_float(w2 << 16);
+    v1[i] = __uint_as_float(w2 & 0xffff0000u);
+    a0 = fmaxf(a0, fabsf(v0[i]));
+    a1 = fmaxf(a1, fabsf(v1[i]));
+  }
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      v[i] = bf16_to_f32(tile[(64 * h + 32 * b + i) * TP + n]);
-      amax = fmaxf(amax, fabsf(v[i]));
-    }
-    const int E = mx_block_exponent(amax);
+  for (int c = 0; c < 2; ++c) {
+    const float(&v)[32] = c ? v1 : v0;
+    const int E = mx_block_exponent(c ? a1 : a0);
+    uint32_t w[8];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       float sv[8];
@@ -242,14 +247,16 @@ __global__ __launch_bounds__(256) void mx_quant_both_kernel(
       for (int i = 0; i < 8; ++i) sv[i] = ldexpf(v[8 * g + i], -E);
       uint32_t c2[2];
       e4m3_codes8(sv, c2);
-      w[8 * b + 2 * g] = c2[0];
-      w[8 * b + 2 * g + 1] = c2[1];
+      w[2 * g] = c2[0];
+      w[2 * g + 1] = c2[1];
     }
-    sC[(long)e * sC_es + (long)((kb >> 5) + b) * pitchC + row] = (uint8_t)(E + 127);
+    const int col = n0 + n + c;
+    const long row = half >= 0 ? (long)((col >> 7) << 8) + 128 * half + (col & 127) : (long)col;
+    uint4* dst = reinterpret_cast<uint4*>(dstC + (long)e * dstC_es + row * K + kb);
+    dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    sC[(long)e * sC_es + (long)(kb >> 5) * pitchC + row] = (uint8_t)(E + 127);
   }
-  uint4* dst = reinterpret_cast<uint4*>(dstC + (long)e * dstC_es + row * K + kb);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) dst[i] = make_uint4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
 }
 
 // Weight-gradient operands, quantised along the tokens of each expert.

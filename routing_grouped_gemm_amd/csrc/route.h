@@ -82,5 +82,9 @@ hipError_t launch_router_bwd_softmax(const float* logits, const int32_t* idx, co
 // workspace of E * ceil(T/64).
 hipError_t launch_router_aux(const float* logits, const int32_t* counts, int T, int E, int k,
                              float coef, float* part, float* loss, float* dp, hipStream_t s);
+// report[0] = entries of idx[T][k] outside [0, E); report[1] = tokens with a
+// repeated expert (device, written after the launch completes).
+hipError_t launch_check_routing(const int32_t* idx, int T, int E, int k, int32_t* report,
+                                hipStream_t s);
 
 }  // namespace moe

@@ -728,6 +728,59 @@ hipError_t launch_router_bwd_softmax(const float* logits, const int32_t* idx, co
 
 namespace moe {
 
+// ---------------------------------------------------------------------------
+// routing check: pre-routed expert indices outside [0, E) and tokens whose
+// experts repeat (one thread per token, a 256-bit set of the experts seen)
+// ---------------------------------------------------------------------------
+__global__ void check_init_kernel(int32_t* __restrict__ report) {
+  report[0] = 0;
+  report[1] = 0;
+}
+
+__global__ __launch_bounds__(256) void check_routing_kernel(const int32_t* __restrict__ idx, int T,
+                                                            int E, int k,
+                                                            int32_t* __restrict__ report) {
+  int bad = 0, dup = 0;
+  for (long t = (long)blockIdx.x * 256 + threadIdx.x; t < T; t += (long)gridDim.x * 256) {
+    uint32_t seen[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    bool rep = false;
+    for (int j = 0; j < k; ++j) {
+      const int e = idx[t * k + j];
+      if (e < 0 || e >= E) {
+        ++bad;
+        continue;
+      }
+      const uint32_t bit = 1u << (e & 31);
+#pragma unroll
+      for (int w = 0; w < 8; ++w)
+        if (w == (e >> 5)) {
+          rep = rep || (seen[w] & bit) != 0;
+          seen[w] |= bit;
+        }
+    }
+    dup += rep ? 1 : 0;
+  }
+  const float b = wave_sum((float)bad), d = wave_sum((float)dup);
+  if ((threadIdx.x & 63) == 0) {
+    if (b > 0.0f) atomicAdd(&report[0], (int)b);
+    if (d > 0.0f) atomicAdd(&report[1], (int)d);
+  }
+}
+
+hipError_t launch_check_routing(const int32_t* idx, int T, int E, int k, int32_t* report,
+                                hipStream_t s) {
+  note_prelaunch("check_init", s);
+  hipLaunchKernelGGL(check_init_kernel, dim3(1), dim3(1), 0, s, report);
+  note_launch("check_init", s);
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  const long nb = ((long)T + 255) / 256;
+  note_prelaunch("check_routing", s);
+  hipLaunchKernelGGL(check_routing_kernel, dim3((unsigned)(nb < 1024 ? nb : 1024)), dim3(256), 0, s,
+                     idx, T, E, k, report);
+  note_launch("check_routing", s);
+  return hipGetLastError();
+}
+
 hipError_t launch_router_aux(const float* logits, const int32_t* counts, int T, int E, int k,
                              float coef, float* part, float* loss, float* dp, hipStream_t s) {
   const int nblk = (T + 63) / 64;

@@ -36,7 +36,7 @@ def declared_entry_points():
 
 def test_exports_every_declared_symbol(L):
     names = declared_entry_points()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     for n in names:
         assert hasattr(L, n), n
 
@@ -293,3 +293,12 @@ def test_mx_keep_weights_flag(L):
     assert bwd(P_MX, KEEP, need + own - 1) == WS
     out = ctypes.c_size_t(0)
     assert L.moe_workspace_size(10, 16, 64, 8, 64, 2, BF16, P_BF16, ctypes.byref(out)) == DTYPE
+
+
+def test_check_routing_validation(L):
+    f = L.moe_check_routing
+    assert f(None, 16, 8, 2, A, None) == NULL
+    assert f(A, 16, 8, 2, None, None) == NULL
+    assert f(A, 0, 8, 2, A, None) == SHAPE
+    assert f(A, 16, 300, 2, A, None) == UNSUP
+    assert f(A, 16, 8, 2, MIS, None) == ALIGN

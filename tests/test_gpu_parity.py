@@ -465,3 +465,34 @@ def test_mx_keep_weights_same_bytes(name):
     for n in kept:
         assert torch.equal(kept[n].view(torch.int16), out[n].view(torch.int16)), n
     say(f"  {name}: kept-code layer equals the self-quantising FFN bit for bit")
+
+
+@pytest.mark.parametrize("T,E,k", [(5000, 64, 8), (300, 8, 2), (1, 256, 16)])
+def test_check_routing(T, E, k):
+    """moe_check_routing counts the entries outside [0, E) and the tokens
+    with a repeated expert, as a host loop over the same indices does; a
+    valid routing reports zeros."""
+    import routing_grouped_gemm_amd as rgg
+    say(f"[case] check_routing T={T} E={E} k={k}")
+    rng = np.random.Generator(np.random.PCG64(T + E))
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    rep = torch.full((4,), 7, dtype=torch.int32, device="cuda")
+    rgg.moe_check_routing(rgg.upload(idx), E, rep)
+    torch.cuda.synchronize()
+    assert to_np(rep)[:2].tolist() == [0, 0]
+    bad = idx.copy()
+    m = rng.random((T, k)) < 0.05
+    bad[m] = rng.choice(np.array([-1, E, 1000, -7], np.int32), int(m.sum()))
+    if k > 1:
+        for t in rng.choice(T, max(1, T // 20), replace=False):
+            bad[t, 1] = bad[t, 0] if 0 <= bad[t, 0] < E else bad[t, 1]
+    n_bad = int(np.sum((bad < 0) | (bad >= E)))
+    n_dup = 0
+    for t in range(T):
+        ok = [e for e in bad[t] if 0 <= e < E]
+        n_dup += len(ok) != len(set(ok))
+    rgg.moe_check_routing(rgg.upload(bad), E, rep)
+    torch.cuda.synchronize()
+    got = to_np(rep)[:2].tolist()
+    say(f"  report {got}, expected {[n_bad, n_dup]}")
+    assert got == [n_bad, n_dup]
