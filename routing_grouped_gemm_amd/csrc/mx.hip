@@ -373,7 +373,7 @@ typedef __attribute__((ext_vector_type(8))) int i32x8_t;
 struct MxPlan {
   Plan a, b;
   i32x4_t srs;       // this wave's scale resource (waves 0-1: A, 2-3: B)
-  uint32_t svoff;    // per-lane offset of the scale DMA
+  uint32_t svoff;    // per-lane offset of the scale DMA (kOutside past the tile's rows)
   uint32_t spitch;   // bytes between consecutive K blocks of the scales
   int sblk;          // first of the two K blocks of a stage this wave loads (0 or 2)
   int amis;          // A rows: tile row 0 sits amis bytes into an A scale block
@@ -419,6 +419,16 @@ __device__ __forceinline__ void load_mx_frags(const char* smem, int kt, int j, i
   }
 }
 
+// The first k-step of a tile: accumulators from a zero operand.
+__device__ __forceinline__ void mx_mfma16_first(f32x16_t (&acc)[4][4], const MxFrags& F) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.b[j], F.a[i], f32x16_t{}, 0, 0,
+                                                                  0, F.sb[j], 0, F.sa[i]);
+}
+
 __device__ __forceinline__ void mx_mfma16(f32x16_t (&acc)[4][4], const MxFrags& F) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -428,7 +438,19 @@ __device__ __forceinline__ void mx_mfma16(f32x16_t (&acc)[4][4], const MxFrags& 
                                                                   0, F.sb[j], 0, F.sa[i]);
 }
 
-__device__ __forceinline__ void mx_issue(const MxPlan& P, int kt, uint32_t st_base, int wave) {
+// Per-lane scale offset of the lanes past a tile's rows: outside every scale
+// buffer (each is under 2^27 bytes: 1/32 of a code array, whose offsets the
+// host keeps below 2^32), also after the K-block offsets are added, so the
+// lane makes no memory request and writes zeros to LDS bytes never read.
+constexpr uint32_t kOutside = 0x80000000u;
+
+// DMA of stage kt (codes of both operands, then this wave's two scale
+// blocks), then the L2 prefetch of stage kt + PF_AHEAD of this wave's
+// operand: one 4-byte load per 128-byte line, rows (wave&1)*128 + lane and
+// 64 rows further (waves 0-1: A, 2-3: B).  Every call adds MX_DMA_PER_STAGE
+// + PF_PER_STAGE loads to vmcnt, the prefetch last.
+__device__ __forceinline__ void mx_issue(const MxPlan& P, uint32_t pfv, uint32_t pfs, int kt,
+                                         uint32_t st_base, uint32_t sink, int wave) {
   issue<false>(P.a, kt, st_base, wave);
   issue<false>(P.b, kt, st_base + OPB, wave);
   // the block offset goes into the per-lane offset, which the range check covers
@@ -438,6 +460,10 @@ __device__ __forceinline__ void mx_issue(const MxPlan& P, int kt, uint32_t st_ba
     const uint32_t voff = P.svoff + (uint32_t)(4 * kt + P.sblk + b) * P.spitch;
     dma16(P.srs, dst + b * 1024, voff, 0u);
   }
+  const i32x4_t rs = wave < 2 ? P.a.rs0 : P.b.rs0;
+  const uint32_t soff = (uint32_t)(kt + PF_AHEAD) * ROWB;
+  pf4(rs, sink, pfv, soff);
+  pf4(rs, sink, pfv, soff + pfs);
 }
 
 // Ask the scheduler to alternate MFMAs and LDS reads in the current region.
@@ -453,13 +479,19 @@ template <int KIND>
 __global__ __launch_bounds__(NTHR, 1) void gemm_mx_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) char smem[NST * MSTAGE];
   __shared__ Sched sch;
+  __shared__ __attribute__((aligned(256))) uint32_t pf_sink[64];
   constexpr bool DUAL = KT<KIND>::BSP == BS_DUAL_N;
   constexpr int BNT = DUAL ? BN / 2 : BN;
   const int ntiles = sched_setup<BM, BNT>(g, sch);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const uint32_t lds0 = lds_u32(smem);
+  const uint32_t lds0 = lds_u32(smem), sink = lds_u32(pf_sink);
+  // L2 prefetch, two stages ahead, of every line of both operands (all
+  // K-contiguous code rows): waves 0-1 the A rows, 2-3 the B rows
+  const long pld = wave < 2 ? g.lda : g.ldb;
+  const uint32_t pfv = (uint32_t)(((wave & 1) * 128 + lane) * pld);
+  const uint32_t pfs = (uint32_t)__builtin_amdgcn_readfirstlane((int)(64 * pld));
   const uint8_t* A = static_cast<const uint8_t*>(g.a);
   const uint8_t* B = static_cast<const uint8_t*>(g.b0);
 
@@ -477,13 +509,13 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mx_kernel(GemmArgs g) {
       plan_km(P.b, B + boff, bbytes - boff, nullptr, 0, 1 << 30, g.ldb, wave, lane);
       P.amis = 0;
       const int kb = t.row0 >> 5;
-      if (wave < 2) {
+            if (wave < 2) {
         P.srs = make_rsrc(g.sa, (long long)(g.K / 32) * g.sa_pitch);
-        P.svoff = (uint32_t)((long)kb * g.sa_pitch + t.m0 + lane * 16);
+        P.svoff = lane < BM / 16 ? (uint32_t)((long)kb * g.sa_pitch + t.m0 + lane * 16) : kOutside;
         P.spitch = (uint32_t)g.sa_pitch;
       } else {
         P.srs = make_rsrc(g.sb, (long long)(g.K / 32) * g.sb_pitch);
-        P.svoff = (uint32_t)((long)kb * g.sb_pitch + t.n0 + lane * 16);
+        P.svoff = lane < BM / 16 ? (uint32_t)((long)kb * g.sb_pitch + t.n0 + lane * 16) : kOutside;
         P.spitch = (uint32_t)g.sb_pitch;
       }
     } else {
@@ -500,11 +532,12 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mx_kernel(GemmArgs g) {
       P.amis = t.row0 - row_al;
       if (wave < 2) {
         P.srs = make_rsrc(g.sa, (long long)(g.K / 32) * g.sa_pitch);
-        P.svoff = (uint32_t)(row_al + lane * 16);
+        // scale bytes amis .. amis + 255 of the 16-aligned run
+        P.svoff = lane * 16 < P.amis + BM ? (uint32_t)(row_al + lane * 16) : kOutside;
         P.spitch = (uint32_t)g.sa_pitch;
       } else {
         P.srs = make_rsrc(g.sb + (long)t.e * g.sb_es, (long long)(g.K / 32) * g.sb_pitch);
-        P.svoff = (uint32_t)(brow0 + lane * 16);
+        P.svoff = lane < BM / 16 ? (uint32_t)(brow0 + lane * 16) : kOutside;
         P.spitch = (uint32_t)g.sb_pitch;
       }
     }
@@ -519,47 +552,62 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mx_kernel(GemmArgs g) {
   plan(t, P);
   // K is a multiple of 64: a last stage may hold a single k-step
   int ns = t.klen / MX_KSTEP, nk = (ns + 1) / 2;
-  if (nk > 0) mx_issue(P, 0, stage_base(0), wave);
-  if (nk > 1) mx_issue(P, 1, stage_base(1), wave);
+  if (nk > 0) mx_issue(P, pfv, pfs, 0, stage_base(0), sink, wave);
+  if (nk > 1) mx_issue(P, pfv, pfs, 1, stage_base(1), sink, wave);
 
   for (;;) {
+    // Stages 0 and 1 of tile t are in flight (as far as they exist).  A
+    // stage is two k-steps; K an odd multiple of 64 ends with a half stage.
+    // The first k-step writes the accumulators from a zero operand, so they
+    // are cleared only for a tile without a full stage.
+    const int nfull = ns >> 1;
     f32x16_t acc[4][4];
+    if (nfull == 0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
+    }
 
-    // k-steps q = 0 .. ns-1; step q reads stage q/2, half q%2.  After the
-    // reads of a stage's second step, one barrier publishes the next stage
-    // and frees this one for the stage after next.
+    // Per stage: the fragments of step 1 are read while the MFMAs of step 0
+    // run; after them one barrier publishes stage kt+1 (each wave waited for
+    // its own DMA) and frees stage kt's buffer for stage kt+2, whose DMA
+    // then runs under the MFMAs of step 1 and of all of stage kt+1; the
+    // fragments of stage kt+1's step 0 are read under step 1's MFMAs.  The
+    // fragment sets keep their roles from stage to stage (straight-line
+    // code, no register copies).
     MxFrags F0, F1;
-    auto step = [&](int q, MxFrags& cur, MxFrags& nxt) {
-      __builtin_amdgcn_s_waitcnt(kLgkm0);
-      const int kt = q >> 1;
-      if ((q & 1) == 0) {
-        if (q + 1 < ns) load_mx_frags<DUAL>(smem, kt, 1, wm, wn, lane, P.amis, nxt);
-      } else {
-        const bool more = q + 1 < ns;
-        if (more) wait_vmcnt<0>();
-        barrier();
-        if (kt + 2 < nk) mx_issue(P, kt + 2, stage_base(kt), wave);
-        if (more) load_mx_frags<DUAL>(smem, kt + 1, 0, wm, wn, lane, P.amis, nxt);
-      }
-      mx_mfma16(acc, cur);
-      interleave_mx();
-      __builtin_amdgcn_sched_barrier(0);
-    };
     if (nk > 0) {
-      if (nk > 1) wait_vmcnt<MX_DMA_PER_STAGE>(); else wait_vmcnt<0>();
+      // stage 1 and both prefetches may still be in flight
+      if (nk > 1) wait_vmcnt<MX_DMA_PER_STAGE + 2 * PF_PER_STAGE>(); else wait_vmcnt<0>();
       barrier();
       load_mx_frags<DUAL>(smem, 0, 0, wm, wn, lane, P.amis, F0);
     }
-    int q = 0;
-    for (; q + 1 < ns; q += 2) {
-      step(q, F0, F1);
-      step(q + 1, F1, F0);
+    for (int kt = 0; kt < nfull; ++kt) {
+      __builtin_amdgcn_s_waitcnt(kLgkm0);
+      load_mx_frags<DUAL>(smem, kt, 1, wm, wn, lane, P.amis, F1);
+      if (kt == 0) mx_mfma16_first(acc, F0); else mx_mfma16(acc, F0);
+      interleave_mx();
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(kLgkm0);
+      const bool more = kt + 1 < nk;
+      // stage kt+1 has landed once only its prefetch loads may be pending
+      if (more) wait_vmcnt<PF_PER_STAGE>();
+      barrier();
+      if (kt + 2 < nk) mx_issue(P, pfv, pfs, kt + 2, stage_base(kt), sink, wave);
+      // read even past the last stage (stale bytes, never used), so that
+      // the fragment registers have one definition
+      load_mx_frags<DUAL>(smem, kt + 1, 0, wm, wn, lane, P.amis, F0);
+      mx_mfma16(acc, F1);
+      interleave_mx();
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (q < ns) step(q, F0, F1);
+    if (ns & 1) {
+      // the half stage: its step 0 was read into F0
+      __builtin_amdgcn_s_waitcnt(kLgkm0);
+      mx_mfma16(acc, F0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     __builtin_amdgcn_s_waitcnt(kLgkm0);
     barrier();
 
@@ -575,12 +623,12 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mx_kernel(GemmArgs g) {
       plan(tn, Pn);
       nsn = tn.klen / MX_KSTEP;
       nkn = (nsn + 1) / 2;
-      if (nkn > 0) mx_issue(Pn, 0, stage_base(0), wave);
+      if (nkn > 0) mx_issue(Pn, pfv, pfs, 0, stage_base(0), sink, wave);
     }
     epilogue_lds<KIND>(g, t, smem + MSTAGE + wave * EPI_SLICE, acc, wm, wn, lane);
     barrier();
     if (!has_next) break;
-    if (nkn > 1) mx_issue(Pn, 1, stage_base(1), wave);
+    if (nkn > 1) mx_issue(Pn, pfv, pfs, 1, stage_base(1), sink, wave);
     t = tn; P = Pn; ns = nsn; nk = nkn;
   }
 }
