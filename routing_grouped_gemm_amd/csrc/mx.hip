@@ -448,22 +448,66 @@ constexpr uint32_t kOutside = 0x80000000u;
 // blocks), then the L2 prefetch of stage kt + PF_AHEAD of this wave's
 // operand: one 4-byte load per 128-byte line, rows (wave&1)*128 + lane and
 // 64 rows further (waves 0-1: A, 2-3: B).  Every call adds MX_DMA_PER_STAGE
-// + PF_PER_STAGE loads to vmcnt, the prefetch last.
+// + PF_PER_STAGE loads to vmcnt, the prefetch last.  live == false (a stage
+// past the tile's K) issues the same loads with an empty buffer range: no
+// memory request, zeros into the stage buffer (free at that point; the K
+// loop waits for these loads before the buffer is used again), and the
+// vmcnt accounting of every other stage, without a branch.
+__device__ __forceinline__ i32x4_t live_rsrc(i32x4_t r, bool live) {
+  r.z = live ? r.z : 0;
+  return r;
+}
 __device__ __forceinline__ void mx_issue(const MxPlan& P, uint32_t pfv, uint32_t pfs, int kt,
-                                         uint32_t st_base, uint32_t sink, int wave) {
-  issue<false>(P.a, kt, st_base, wave);
-  issue<false>(P.b, kt, st_base + OPB, wave);
+                                         bool live, uint32_t st_base, uint32_t sink, int wave) {
+  const i32x4_t ra = live_rsrc(P.a.rs0, live), rb = live_rsrc(P.b.rs0, live);
+  const uint32_t soa = (uint32_t)kt * P.a.kstep, sob = (uint32_t)kt * P.b.kstep;
+#pragma unroll
+  for (int i = 0; i < DMA_PER_OP; ++i)
+    dma16(ra, st_base + plan_lds(wave, i), (i & 1) ? P.a.v1 : P.a.v0, soa + (uint32_t)i * P.a.bstep);
+#pragma unroll
+  for (int i = 0; i < DMA_PER_OP; ++i)
+    dma16(rb, st_base + OPB + plan_lds(wave, i), (i & 1) ? P.b.v1 : P.b.v0, sob + (uint32_t)i * P.b.bstep);
   // the block offset goes into the per-lane offset, which the range check covers
+  const i32x4_t rsc = live_rsrc(P.srs, live);
   const uint32_t dst = st_base + STAGE + (wave >> 1) * 4096 + P.sblk * 1024;
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
     const uint32_t voff = P.svoff + (uint32_t)(4 * kt + P.sblk + b) * P.spitch;
-    dma16(P.srs, dst + b * 1024, voff, 0u);
+    dma16(rsc, dst + b * 1024, voff, 0u);
   }
-  const i32x4_t rs = wave < 2 ? P.a.rs0 : P.b.rs0;
+  const i32x4_t rpf = live_rsrc(wave < 2 ? P.a.rs0 : P.b.rs0, live);
   const uint32_t soff = (uint32_t)(kt + PF_AHEAD) * ROWB;
-  pf4(rs, sink, pfv, soff);
-  pf4(rs, sink, pfv, soff + pfs);
+  pf4(rpf, sink, pfv, soff);
+  pf4(rpf, sink, pfv, soff + pfs);
+}
+
+// The same loads as mx_issue in pieces: piece q < 16 is code block q of the
+// wave (A's eight, then B's), piece 16 the scales and the prefetch.
+__device__ __forceinline__ void mx_issue_piece(const MxPlan& P, uint32_t pfv, uint32_t pfs, int kt,
+                                               bool live, uint32_t st_base, uint32_t sink, int wave,
+                                               int q) {
+  if (q < DMA_PER_OP) {
+    const i32x4_t ra = live_rsrc(P.a.rs0, live);
+    dma16(ra, st_base + plan_lds(wave, q), (q & 1) ? P.a.v1 : P.a.v0,
+          (uint32_t)kt * P.a.kstep + (uint32_t)q * P.a.bstep);
+  } else if (q < 2 * DMA_PER_OP) {
+    const int i = q - DMA_PER_OP;
+    const i32x4_t rb = live_rsrc(P.b.rs0, live);
+    dma16(rb, st_base + OPB + plan_lds(wave, i), (i & 1) ? P.b.v1 : P.b.v0,
+          (uint32_t)kt * P.b.kstep + (uint32_t)i * P.b.bstep);
+  } else {
+    const i32x4_t rsc = live_rsrc(P.srs, live);
+    const uint32_t dst = st_base + STAGE + (wave >> 1) * 4096 + P.sblk * 1024;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const uint32_t voff = P.svoff + (uint32_t)(4 * kt + P.sblk + b) * P.spitch;
+      dma16(rsc, dst + b * 1024, voff, 0u);
+    }
+    const i32x4_t rpf = live_rsrc(wave < 2 ? P.a.rs0 : P.b.rs0, live);
+    const uint32_t soff = (uint32_t)(kt + PF_AHEAD) * ROWB;
+    pf4(rpf, sink, pfv, soff);
+    pf4(rpf, sink, pfv, soff + pfs);
+  }
 }
 
 // Ask the scheduler to alternate MFMAs and LDS reads in the current region.
@@ -552,8 +596,8 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mx_kernel(GemmArgs g) {
   plan(t, P);
   // K is a multiple of 64: a last stage may hold a single k-step
   int ns = t.klen / MX_KSTEP, nk = (ns + 1) / 2;
-  if (nk > 0) mx_issue(P, pfv, pfs, 0, stage_base(0), sink, wave);
-  if (nk > 1) mx_issue(P, pfv, pfs, 1, stage_base(1), sink, wave);
+  mx_issue(P, pfv, pfs, 0, nk > 0, stage_base(0), sink, wave);
+  mx_issue(P, pfv, pfs, 1, nk > 1, stage_base(1), sink, wave);
 
   for (;;) {
     // Stages 0 and 1 of tile t are in flight (as far as they exist).  A
@@ -579,28 +623,50 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mx_kernel(GemmArgs g) {
     MxFrags F0, F1;
     if (nk > 0) {
       // stage 1 and both prefetches may still be in flight
-      if (nk > 1) wait_vmcnt<MX_DMA_PER_STAGE + 2 * PF_PER_STAGE>(); else wait_vmcnt<0>();
+      wait_vmcnt<MX_DMA_PER_STAGE + 2 * PF_PER_STAGE>();
       barrier();
       load_mx_frags<DUAL>(smem, 0, 0, wm, wn, lane, P.amis, F0);
     }
-    for (int kt = 0; kt < nfull; ++kt) {
+    // One full stage (FIRST: the tile's first, accumulators from a zero
+    // operand).  The loop body is one basic block: with a branch between
+    // the two k-steps the compiler sank the first step's MFMAs below the
+    // barrier and the DMA issue.
+    auto stage = [&](int kt, auto FIRST) {
       __builtin_amdgcn_s_waitcnt(kLgkm0);
       load_mx_frags<DUAL>(smem, kt, 1, wm, wn, lane, P.amis, F1);
-      if (kt == 0) mx_mfma16_first(acc, F0); else mx_mfma16(acc, F0);
+      if constexpr (decltype(FIRST)::value) mx_mfma16_first(acc, F0); else mx_mfma16(acc, F0);
       interleave_mx();
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_waitcnt(kLgkm0);
-      const bool more = kt + 1 < nk;
-      // stage kt+1 has landed once only its prefetch loads may be pending
-      if (more) wait_vmcnt<PF_PER_STAGE>();
+      // stage kt+1 (possibly an empty one past K) has landed once only its
+      // prefetch loads may be pending
+      wait_vmcnt<PF_PER_STAGE>();
       barrier();
-      if (kt + 2 < nk) mx_issue(P, pfv, pfs, kt + 2, stage_base(kt), sink, wave);
       // read even past the last stage (stale bytes, never used), so that
       // the fragment registers have one definition
       load_mx_frags<DUAL>(smem, kt + 1, 0, wm, wn, lane, P.amis, F0);
-      mx_mfma16(acc, F1);
-      interleave_mx();
       __builtin_amdgcn_sched_barrier(0);
+      // Stage kt+2's loads (an empty stage's past K) go out one after each
+      // MFMA of step 1: a wave stalls while the load path takes a load, and
+      // the MFMA issued just before it keeps the matrix core busy meanwhile
+      // (one burst after the barrier left it idle for the whole issue).
+      {
+        const bool live = kt + 2 < nk;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int i = q >> 2, j = q & 3;
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F1.b[j], F1.a[i], acc[i][j], 0,
+                                                                      0, 0, F1.sb[j], 0, F1.sa[i]);
+          mx_issue_piece(P, pfv, pfs, kt + 2, live, stage_base(kt), sink, wave, q);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        mx_issue_piece(P, pfv, pfs, kt + 2, live, stage_base(kt), sink, wave, 16);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    if (nfull > 0) {
+      stage(0, std::true_type{});
+      for (int kt = 1; kt < nfull; ++kt) stage(kt, std::false_type{});
     }
     if (ns & 1) {
       // the half stage: its step 0 was read into F0
@@ -608,6 +674,10 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mx_kernel(GemmArgs g) {
       mx_mfma16(acc, F0);
       __builtin_amdgcn_sched_barrier(0);
     }
+    // the loads of the last stages (empty ones, which write zeros into the
+    // stage buffers) are done before the epilogue stages through buffer 1
+    // and the next tile's stage 0 loads into buffer 0
+    wait_vmcnt<0>();
     __builtin_amdgcn_s_waitcnt(kLgkm0);
     barrier();
 
@@ -623,12 +693,12 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mx_kernel(GemmArgs g) {
       plan(tn, Pn);
       nsn = tn.klen / MX_KSTEP;
       nkn = (nsn + 1) / 2;
-      if (nkn > 0) mx_issue(Pn, pfv, pfs, 0, stage_base(0), sink, wave);
+      mx_issue(Pn, pfv, pfs, 0, nkn > 0, stage_base(0), sink, wave);
     }
     epilogue_lds<KIND>(g, t, smem + MSTAGE + wave * EPI_SLICE, acc, wm, wn, lane);
     barrier();
     if (!has_next) break;
-    if (nkn > 1) mx_issue(Pn, pfv, pfs, 1, stage_base(1), sink, wave);
+    mx_issue(Pn, pfv, pfs, 1, nkn > 1, stage_base(1), sink, wave);
     t = tn; P = Pn; ns = nsn; nk = nkn;
   }
 }
