@@ -185,9 +185,8 @@ __global__ __launch_bounds__(256) void mx_quant_cols_kernel(
 //    code bytes as one line;
 //  * along K, written transposed exactly as mx_quant_cols_kernel writes it
 //    (the forward GEMM's operand); a thread takes two adjacent columns (one
-//    4-byte LDS read gives both) and one whole 32-value block of each, and
-//    the four threads of a column pair write each column's 128 code bytes
-//    as one line.
+//    4-byte LDS read gives both) and one whole 32-value block of each; the
+//    codes and scales are staged in LDS and written back as whole lines.
 // K and N are multiples of 64 (every width the layer accepts); a tile's
 // halves past them are skipped.
 __global__ __launch_bounds__(256) void mx_quant_both_kernel(
@@ -224,38 +223,80 @@ __global__ __launch_bounds__(256) void mx_quant_both_kernel(
   // whole 32-value block of each of the two columns, read 4 bytes at a time)
   const int n = 2 * (t & 63), b = t >> 6;
   const int kb = k0 + 32 * b;
-  if (n0 + n >= N || kb >= K) return;
-  float v0[32], v1[32];
-  float a0 = 0.0f, a1 = 0.0f;
+  const bool cval = n0 + n < N && kb < K;
+  uint32_t wc[2][8];
+  int ec[2] = {0, 0};
+  if (cval) {
+    float v0[32], v1[32];
+    float a0 = 0.0f, a1 = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const uint32_t w2 = *reinterpret_cast<const uint32_t*>(&tile[(32 * b + i) * TP + n]);
-    v0[i] = __uint_as_float(w2 << 16);
-    v1[i] = __uint_as_float(w2 & 0xffff0000u);
-    a0 = fmaxf(a0, fabsf(v0[i]));
-    a1 = fmaxf(a1, fabsf(v1[i]));
-  }
-#pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    const float(&v)[32] = c ? v1 : v0;
-    const int E = mx_block_exponent(c ? a1 : a0);
-    uint32_t w[8];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      float sv[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) sv[i] = ldexpf(v[8 * g + i], -E);
-      uint32_t c2[2];
-      e4m3_codes8(sv, c2);
-      w[2 * g] = c2[0];
-      w[2 * g + 1] = c2[1];
+    for (int i = 0; i < 32; ++i) {
+      const uint32_t w2 = *reinterpret_cast<const uint32_t*>(&tile[(32 * b + i) * TP + n]);
+      v0[i] = __uint_as_float(w2 << 16);
+      v1[i] = __uint_as_float(w2 & 0xffff0000u);
+      a0 = fmaxf(a0, fabsf(v0[i]));
+      a1 = fmaxf(a1, fabsf(v1[i]));
     }
-    const int col = n0 + n + c;
-    const long row = half >= 0 ? (long)((col >> 7) << 8) + 128 * half + (col & 127) : (long)col;
-    uint4* dst = reinterpret_cast<uint4*>(dstC + (long)e * dstC_es + row * K + kb);
-    dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
-    dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
-    sC[(long)e * sC_es + (long)(kb >> 5) * pitchC + row] = (uint8_t)(E + 127);
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const float(&v)[32] = c ? v1 : v0;
+      const int E = mx_block_exponent(c ? a1 : a0);
+      ec[c] = E;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float sv[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sv[i] = ldexpf(v[8 * g + i], -E);
+        uint32_t c2[2];
+        e4m3_codes8(sv, c2);
+        wc[c][2 * g] = c2[0];
+        wc[c][2 * g + 1] = c2[1];
+      }
+    }
+  }
+  // The transposed codes go out as whole 128-byte lines: staged in the tile's
+  // LDS (free once every thread has read it) as 128 code rows, one per
+  // column, of the tile's 128 k (16-byte chunks XOR-swizzled by the row),
+  // plus the four blocks' scales of the 128 columns, then written back a
+  // row's eight chunks by eight consecutive threads.  (Each thread writing
+  // its own 32 bytes to four lines shared with three other waves took 60%
+  // longer than the row half of the pass.)
+  __syncthreads();
+  uint8_t* cs = reinterpret_cast<uint8_t*>(tile);   // 16 KiB of codes, then 512 B of scales
+  auto cswz = [](int r) { return (r >> 1) & 7; };
+  if (cval) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int r = n + c;
+      *reinterpret_cast<uint4*>(cs + r * 128 + (((2 * b) ^ cswz(r)) << 4)) =
+          make_uint4(wc[c][0], wc[c][1], wc[c][2], wc[c][3]);
+      *reinterpret_cast<uint4*>(cs + r * 128 + (((2 * b + 1) ^ cswz(r)) << 4)) =
+          make_uint4(wc[c][4], wc[c][5], wc[c][6], wc[c][7]);
+      cs[16384 + b * 128 + r] = (uint8_t)(ec[c] + 127);
+    }
+  }
+  __syncthreads();
+  const int kvalid = min(128, K - k0), nvalid = min(128, N - n0);
+  // code row of column col (the gate/up panels interleave 128 gate and 128 up rows)
+  auto rowof = [&](int col) -> long {
+    return half >= 0 ? (long)((col >> 7) << 8) + 128 * half + (col & 127) : (long)col;
+  };
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q = t + 256 * i, r = q >> 3, ch = q & 7;
+    if (r < nvalid && ch * 16 < kvalid) {
+      const uint4 w = *reinterpret_cast<const uint4*>(cs + r * 128 + ((ch ^ cswz(r)) << 4));
+      *reinterpret_cast<uint4*>(dstC + (long)e * dstC_es + rowof(n0 + r) * K + k0 + ch * 16) = w;
+    }
+  }
+  // scales: block bb of the 128 columns is 128 consecutive bytes (their code
+  // rows are consecutive), written as eight 16-byte pieces
+  if (t < 32) {
+    const int bb = t >> 3, piece = t & 7;
+    if (bb * 32 < kvalid && piece * 16 < nvalid)
+      *reinterpret_cast<uint4*>(sC + (long)e * sC_es + (long)((k0 >> 5) + bb) * pitchC + rowof(n0) +
+                                piece * 16) =
+          *reinterpret_cast<const uint4*>(cs + 16384 + bb * 128 + piece * 16);
   }
 }
 
