@@ -50,11 +50,17 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(GemmArgs g) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform in the wave
   const int wm = wave >> 1, wn = wave & 1;
   const uint32_t lds0 = lds_u32(smem), sink = lds_u32(pf_sink);
-  // L2 prefetch of the K-contiguous operands (waves 0-1: A, 2-3: B); an
-  // operand that is contiguous along M or N is not prefetched, as measured
-  // prefetching it slows the kernel down.
-  const bool pf_on = (wave < 2) ? !AMN : !BMN;
-  const Pf pf = plan_pf_km((wave < 2 ? g.lda : g.ldb) * 2, wave, lane);
+  // L2 prefetch of a quarter of each K-contiguous operand's rows (wave 0:
+  // A, wave 2: B); an operand that is contiguous along M or N is not
+  // prefetched, as measured prefetching it does not pay.
+  const bool pf_a = wave == 0 && !AMN, pf_b = wave == 2 && !BMN;
+  const bool pf_on = pf_a || pf_b;
+  // the lane's prefetch offset for tile tt (the quarter follows the tile)
+  auto pf_plan = [&](const Tile& tt) -> uint32_t {
+    return pf_a ? pf_quarter(tt.n0 / BNT, lane, (long)g.lda * 2)
+                : pf_quarter(tt.m0 / BM, lane, (long)g.ldb * 2);
+  };
+  uint32_t pfv = 0;
   // DMA of stage s, then the prefetch of stage s + PF_AHEAD (issued even past
   // the last stage, where it touches no memory or a line of another row, so
   // that every stage adds the same number of loads to vmcnt)
@@ -62,10 +68,10 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(GemmArgs g) {
     issue<AMN>(qa, s, lds0 + (s & 1) * STAGE, wave);
     issue<BMN>(qb, s, lds0 + (s & 1) * STAGE + OPB, wave);
     if constexpr (!AMN) {
-      if (wave < 2) issue_pf<false>(qa, pf, s + PF_AHEAD, sink, wave);
+      if (pf_a) issue_pf(qa, pfv, s + PF_AHEAD, sink);
     }
     if constexpr (!BMN) {
-      if (wave >= 2) issue_pf<false>(qb, pf, s + PF_AHEAD, sink, wave);
+      if (pf_b) issue_pf(qb, pfv, s + PF_AHEAD, sink);
     }
   };
 
@@ -75,6 +81,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(GemmArgs g) {
   Tile t = sched_decode<BM, BNT>(g, sch, L);
   Plan pa, pb;
   plan_tile<KIND>(g, t, wave, lane, pa, pb);
+  pfv = pf_plan(t);
   int nk = (t.klen + BK - 1) / BK;
   if (nk > 0) issue_stage(pa, pb, 0);
   if (nk > 1) issue_stage(pa, pb, 1);
@@ -135,10 +142,10 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(GemmArgs g) {
         }
         if (dma) {
           if constexpr (!AMN) {
-            if (wave < 2) issue_pf<false>(pa, pf, pend_stage + PF_AHEAD, sink, wave);
+            if (pf_a) issue_pf(pa, pfv, pend_stage + PF_AHEAD, sink);
           }
           if constexpr (!BMN) {
-            if (wave >= 2) issue_pf<false>(pb, pf, pend_stage + PF_AHEAD, sink, wave);
+            if (pf_b) issue_pf(pb, pfv, pend_stage + PF_AHEAD, sink);
           }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -200,6 +207,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(GemmArgs g) {
     if (has_next) {
       plan_tile<KIND>(g, tn, wave, lane, pan, pbn);
       nkn = (tn.klen + BK - 1) / BK;
+      pfv = pf_plan(tn);
       if (nkn > 0) issue_stage(pan, pbn, 0);
     }
     epilogue_lds<KIND>(g, t, smem + STAGE + wave * EPI_SLICE, acc, wm, wn, lane);

@@ -486,10 +486,11 @@ __device__ __forceinline__ void mx_mfma16(f32x16_t (&acc)[4][4], const MxFrags& 
 constexpr uint32_t kOutside = 0x80000000u;
 
 // DMA of stage kt (codes of both operands, then this wave's two scale
-// blocks), then the L2 prefetch of stage kt + PF_AHEAD of this wave's
-// operand: one 4-byte load per 128-byte line, rows (wave&1)*128 + lane and
-// 64 rows further (waves 0-1: A, 2-3: B).  Every call adds MX_DMA_PER_STAGE
-// + PF_PER_STAGE loads to vmcnt, the prefetch last.  live == false (a stage
+// blocks), then the L2 prefetch of stage kt + PF_AHEAD: one 4-byte load per
+// 128-byte line of a quarter of the tile's rows at per-lane offset pfv
+// (wave 0: A, wave 2: B; waves 1 and 3 issue theirs against an empty range
+// so that every wave counts the same).  Every call adds MX_DMA_PER_STAGE +
+// PF_PER_STAGE loads to vmcnt, the prefetch last.  live == false (a stage
 // past the tile's K) issues the same loads with an empty buffer range: no
 // memory request, zeros into the stage buffer (free at that point; the K
 // loop waits for these loads before the buffer is used again), and the
@@ -498,8 +499,8 @@ __device__ __forceinline__ i32x4_t live_rsrc(i32x4_t r, bool live) {
   r.z = live ? r.z : 0;
   return r;
 }
-__device__ __forceinline__ void mx_issue(const MxPlan& P, uint32_t pfv, uint32_t pfs, int kt,
-                                         bool live, uint32_t st_base, uint32_t sink, int wave) {
+__device__ __forceinline__ void mx_issue(const MxPlan& P, uint32_t pfv, int kt, bool live,
+                                         uint32_t st_base, uint32_t sink, int wave) {
   const i32x4_t ra = live_rsrc(P.a.rs0, live), rb = live_rsrc(P.b.rs0, live);
   const uint32_t soa = (uint32_t)kt * P.a.kstep, sob = (uint32_t)kt * P.b.kstep;
 #pragma unroll
@@ -516,17 +517,14 @@ __device__ __forceinline__ void mx_issue(const MxPlan& P, uint32_t pfv, uint32_t
     const uint32_t voff = P.svoff + (uint32_t)(4 * kt + P.sblk + b) * P.spitch;
     dma16(rsc, dst + b * 1024, voff, 0u);
   }
-  const i32x4_t rpf = live_rsrc(wave < 2 ? P.a.rs0 : P.b.rs0, live);
-  const uint32_t soff = (uint32_t)(kt + PF_AHEAD) * ROWB;
-  pf4(rpf, sink, pfv, soff);
-  pf4(rpf, sink, pfv, soff + pfs);
+  const i32x4_t rpf = live_rsrc(wave < 2 ? P.a.rs0 : P.b.rs0, live && (wave & 1) == 0);
+  pf4(rpf, sink, pfv, (uint32_t)(kt + PF_AHEAD) * ROWB);
 }
 
 // The same loads as mx_issue in pieces: piece q < 16 is code block q of the
 // wave (A's eight, then B's), piece 16 the scales and the prefetch.
-__device__ __forceinline__ void mx_issue_piece(const MxPlan& P, uint32_t pfv, uint32_t pfs, int kt,
-                                               bool live, uint32_t st_base, uint32_t sink, int wave,
-                                               int q) {
+__device__ __forceinline__ void mx_issue_piece(const MxPlan& P, uint32_t pfv, int kt, bool live,
+                                               uint32_t st_base, uint32_t sink, int wave, int q) {
   if (q < DMA_PER_OP) {
     const i32x4_t ra = live_rsrc(P.a.rs0, live);
     dma16(ra, st_base + plan_lds(wave, q), (q & 1) ? P.a.v1 : P.a.v0,
@@ -544,10 +542,8 @@ __device__ __forceinline__ void mx_issue_piece(const MxPlan& P, uint32_t pfv, ui
       const uint32_t voff = P.svoff + (uint32_t)(4 * kt + P.sblk + b) * P.spitch;
       dma16(rsc, dst + b * 1024, voff, 0u);
     }
-    const i32x4_t rpf = live_rsrc(wave < 2 ? P.a.rs0 : P.b.rs0, live);
-    const uint32_t soff = (uint32_t)(kt + PF_AHEAD) * ROWB;
-    pf4(rpf, sink, pfv, soff);
-    pf4(rpf, sink, pfv, soff + pfs);
+    const i32x4_t rpf = live_rsrc(wave < 2 ? P.a.rs0 : P.b.rs0, live && (wave & 1) == 0);
+    pf4(rpf, sink, pfv, (uint32_t)(kt + PF_AHEAD) * ROWB);
   }
 }
 
@@ -572,11 +568,6 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mx_kernel(GemmArgs g) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const uint32_t lds0 = lds_u32(smem), sink = lds_u32(pf_sink);
-  // L2 prefetch, two stages ahead, of every line of both operands (all
-  // K-contiguous code rows): waves 0-1 the A rows, 2-3 the B rows
-  const long pld = wave < 2 ? g.lda : g.ldb;
-  const uint32_t pfv = (uint32_t)(((wave & 1) * 128 + lane) * pld);
-  const uint32_t pfs = (uint32_t)__builtin_amdgcn_readfirstlane((int)(64 * pld));
   const uint8_t* A = static_cast<const uint8_t*>(g.a);
   const uint8_t* B = static_cast<const uint8_t*>(g.b0);
 
@@ -628,6 +619,12 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mx_kernel(GemmArgs g) {
     }
   };
   auto stage_base = [&](int s) { return lds0 + (s & 1) * MSTAGE; };
+  // the lane's L2 prefetch offset for tile t: a quarter of its A rows
+  // (shared with the other N-tiles of the M-block) or of its B rows (shared
+  // with the other M-tiles of the expert)
+  auto pf_plan = [&](const Tile& t) -> uint32_t {
+    return wave < 2 ? pf_quarter(t.n0 / BNT, lane, g.lda) : pf_quarter(t.m0 / BM, lane, g.ldb);
+  };
 
   int it = 0;
   int L = logical_tile(it);
@@ -635,10 +632,11 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mx_kernel(GemmArgs g) {
   Tile t = sched_decode<BM, BNT>(g, sch, L);
   MxPlan P;
   plan(t, P);
+  uint32_t pfv = pf_plan(t);
   // K is a multiple of 64: a last stage may hold a single k-step
   int ns = t.klen / MX_KSTEP, nk = (ns + 1) / 2;
-  mx_issue(P, pfv, pfs, 0, nk > 0, stage_base(0), sink, wave);
-  mx_issue(P, pfv, pfs, 1, nk > 1, stage_base(1), sink, wave);
+  mx_issue(P, pfv, 0, nk > 0, stage_base(0), sink, wave);
+  mx_issue(P, pfv, 1, nk > 1, stage_base(1), sink, wave);
 
   for (;;) {
     // Stages 0 and 1 of tile t are in flight (as far as they exist).  A
@@ -698,10 +696,10 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mx_kernel(GemmArgs g) {
           const int i = q >> 2, j = q & 3;
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F1.b[j], F1.a[i], acc[i][j], 0,
                                                                       0, 0, F1.sb[j], 0, F1.sa[i]);
-          mx_issue_piece(P, pfv, pfs, kt + 2, live, stage_base(kt), sink, wave, q);
+          mx_issue_piece(P, pfv, kt + 2, live, stage_base(kt), sink, wave, q);
           __builtin_amdgcn_sched_barrier(0);
         }
-        mx_issue_piece(P, pfv, pfs, kt + 2, live, stage_base(kt), sink, wave, 16);
+        mx_issue_piece(P, pfv, kt + 2, live, stage_base(kt), sink, wave, 16);
         __builtin_amdgcn_sched_barrier(0);
       }
     };
@@ -732,14 +730,15 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mx_kernel(GemmArgs g) {
     if (has_next) {
       tn = sched_decode<BM, BNT>(g, sch, L);
       plan(tn, Pn);
+      pfv = pf_plan(tn);
       nsn = tn.klen / MX_KSTEP;
       nkn = (nsn + 1) / 2;
-      mx_issue(Pn, pfv, pfs, 0, nkn > 0, stage_base(0), sink, wave);
+      mx_issue(Pn, pfv, 0, nkn > 0, stage_base(0), sink, wave);
     }
     epilogue_lds<KIND>(g, t, smem + MSTAGE + wave * EPI_SLICE, acc, wm, wn, lane);
     barrier();
     if (!has_next) break;
-    mx_issue(Pn, pfv, pfs, 1, nkn > 1, stage_base(1), sink, wave);
+    mx_issue(Pn, pfv, 1, nkn > 1, stage_base(1), sink, wave);
     t = tn; P = Pn; ns = nsn; nk = nkn;
   }
 }
