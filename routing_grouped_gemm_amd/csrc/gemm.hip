@@ -12,8 +12,7 @@
 // stage of both operands arrives by buffer->LDS DMA (16 bytes per lane, no
 // register staging); one stage is in flight while the other is consumed.
 // A wave that issues a DMA load stalls until the load path accepts it, and
-// the MFMAs behind it in program order wait too; so (except in the forward
-// gate/up GEMM, where measurement favours one burst) each wave's 16 loads of
+// the MFMAs behind it in program order wait too; so each wave's 16 loads of
 // a stage are spread over two k16 steps, one load after every two MFMAs.
 // Operands that are K-contiguous in HBM sit in LDS as rows of 64 k (whole
 // 128-byte lines); operands that are
@@ -43,7 +42,6 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(GemmArgs g) {
   constexpr bool DUAL = KT<KIND>::BSP == BS_DUAL_N;
   constexpr bool AMN = !KT<KIND>::AK, BMN = !KT<KIND>::BK_;
   constexpr int BNT = DUAL ? BN / 2 : BN;
-  constexpr bool SPLIT = KIND != GK_FWD_GATEUP;  // spread the stage DMA over two k16 steps
   const int ntiles = sched_setup<BM, BNT>(g, sch);
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -114,8 +112,8 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(GemmArgs g) {
       barrier();
       load_frags<AMN, BMN, DUAL>(smem, 0, 0, wm, wn, lane, fa0, fb0);
     }
-    // SPLIT: the A loads of stage kt+2 go with the MFMAs of step 3 of stage
-    // kt, its B loads and prefetches with step 0 of stage kt+1 (pend_b).
+    // The A loads of stage kt+2 go with the MFMAs of step 3 of stage kt, its
+    // B loads and prefetches with step 0 of stage kt+1 (pend_b).
     bool pend_b = false;
     int pend_stage = 0;
     // The next tile's coordinates are decoded while this tile's first stage
@@ -131,7 +129,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(GemmArgs g) {
         mfma16_first(acc, fa0, fb0);
         interleave_mfma_ds();
         __builtin_amdgcn_sched_barrier(0);
-      } else if constexpr (SPLIT) {
+      } else {
         const bool dma = pend_b;
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -150,10 +148,6 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(GemmArgs g) {
         }
         __builtin_amdgcn_sched_barrier(0);
         pend_b = false;
-      } else {
-        mfma16(acc, fa0, fb0);
-        interleave_mfma_ds();
-        __builtin_amdgcn_sched_barrier(0);
       }
       __builtin_amdgcn_s_waitcnt(kLgkm0);
       load_frags<AMN, BMN, DUAL>(smem, kt, 2, wm, wn, lane, fa0, fb0);
@@ -172,25 +166,17 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(GemmArgs g) {
         if (pf_on) wait_vmcnt<PF_PER_STAGE>(); else wait_vmcnt<0>();
       }
       barrier();
-      if constexpr (SPLIT) {
-        if (more) load_frags<AMN, BMN, DUAL>(smem, kt + 1, 0, wm, wn, lane, fa0, fb0);
-        const bool dma = kt + 2 < nk;
-        if (dma) pend_stage = kt + 2;
-        __builtin_amdgcn_sched_barrier(0);
+      if (more) load_frags<AMN, BMN, DUAL>(smem, kt + 1, 0, wm, wn, lane, fa0, fb0);
+      const bool dma = kt + 2 < nk;
+      if (dma) pend_stage = kt + 2;
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          mfma_pair(acc, fa1, fb1, q);
-          if (dma) issue_one<AMN>(pa, pend_stage, lds0 + (pend_stage & 1) * STAGE, wave, q);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        pend_b = dma;
-      } else {
-        if (kt + 2 < nk) issue_stage(pa, pb, kt + 2);
-        if (more) load_frags<AMN, BMN, DUAL>(smem, kt + 1, 0, wm, wn, lane, fa0, fb0);
-        mfma16(acc, fa1, fb1);
-        interleave_mfma_ds();
+      for (int q = 0; q < 8; ++q) {
+        mfma_pair(acc, fa1, fb1, q);
+        if (dma) issue_one<AMN>(pa, pend_stage, lds0 + (pend_stage & 1) * STAGE, wave, q);
         __builtin_amdgcn_sched_barrier(0);
       }
+      pend_b = dma;
     }
     // every wave is done reading the ring
     __builtin_amdgcn_s_waitcnt(kLgkm0);
