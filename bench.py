@@ -98,6 +98,7 @@ _SYMBOLS = {
     "route_part_kernel": ["route_small_part"],
     "route_final_kernel": ["route_small_final"],
     "dispatch_small_kernel": ["dispatch_small"],
+    "mx_quant_both_kernel": ["mx_quant_weights"],
     "combine_small_kernel": ["combine_small"],
 }
 
@@ -210,6 +211,24 @@ def mfma_summary(workload_name: str, directory: str) -> int:
             names = _SYMBOLS.get(sym, [sym])
             launch = names[n % len(names)]
         acc.setdefault(launch, []).append(d)
+    w = workload_name
+    comp = " --no-companions" if w == "olmoe_bf16" else ""
+    print(f"# {w}: matrix-core utilisation and clock per kernel\n")
+    print(f"Workload: T={wl.T}, d={wl.d}, E={wl.E}, f={wl.f}, k={wl.k}, {wl.prec}.  One MI355X.  "
+          f"Source digest (`bench.py` `source_hash()`): `{source_hash()}`.\n")
+    print("`SQ_VALU_MFMA_BUSY_CYCLES` counts 32 SIMD cycles per 32x32x16 bf16 MFMA (64 per "
+          "scaled fp8 32x32x64); against 4 x `SQ_BUSY_CU_CYCLES` it is the fraction of SIMD "
+          "cycles the matrix cores were busy (the clock probe, pure MFMA work on every CU, reads "
+          "~100%).  `GRBM_GUI_ACTIVE` / 8 XCDs over a dispatch's duration is the clock it ran at "
+          "(shown for dispatches of 100 µs or more).  TFLOP/s count routed rows only.\n")
+    print("Commands (repository root; `export TMPDIR=/tmp` first; OUT is any scratch directory):\n")
+    print("```")
+    print(f"rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES GRBM_GUI_ACTIVE -d "
+          f"OUT/pmc_mfma_{w} -o run --output-format csv -- python3 bench.py --workload {w} "
+          f"--steps 5 --warmup 2 --cpu-tokens 0{comp}")
+    print(f"python3 bench.py --workload {w} --mfma-summary OUT/pmc_mfma_{w} > "
+          f"profiles/{w}_mfma_counters.md")
+    print("```\n")
     print("| kernel | launches | mean µs | clock MHz | MFMA busy (% of SIMD cycles) | "
           "algorithmic TFLOP/s | frac of 2.5 PF | frac of peak at its clock |")
     print("|---|---:|---:|---:|---:|---:|---:|---:|")
@@ -239,6 +258,92 @@ def mfma_summary(workload_name: str, directory: str) -> int:
         # match its timestamps well enough for a clock
         clk = f"{mhz:.0f}" if us >= 100.0 else "-"
         print(f"| `{k}` | {len(ds)} | {us:.1f} | {clk} | {100.0 * busy:.1f} | {cols} |")
+    return 0
+
+
+def _symbol_of(kernel_name: str) -> str:
+    name = kernel_name.split("(")[0].replace("void ", "")
+    for pre in ("moe::mf::", "moe::mf8::", "moe::sk::", "moe::st::", "moe::"):
+        name = name.replace(pre, "")
+    return name
+
+
+def profile_markdown(workload_name: str, kt_dir: str) -> int:
+    """The committed per-workload profile summary: the rocprofv3 kernel trace
+    of a bench run (kernel_stats.csv under kt_dir) and, while the sources are
+    the ones they were taken on, the calibrated HBM bytes per launch of
+    profiles/traffic.json; printed as markdown on stdout."""
+    import csv
+    import glob
+    from moe_synth import workload
+    wl = workload(workload_name)
+    files = glob.glob(os.path.join(kt_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_stats.csv under {kt_dir}")
+    with open(files[0]) as fh:
+        rows = list(csv.DictReader(fh))
+    fwd_only = workload_name.startswith("olmoe_decode")
+    w = workload_name
+    steps = "--steps 200 --warmup 20" if fwd_only else "--steps 20 --warmup 2"
+    comp = "" if fwd_only or w != "olmoe_bf16" else " --no-companions"
+    what = "the small-batch forward" if fwd_only else "one forward+backward step"
+    routed = wl.T * wl.k
+    print(f"# {w}: per-kernel profile of {what}\n")
+    print(f"Workload: T={wl.T}, d={wl.d}, E={wl.E}, f={wl.f}, k={wl.k}, {wl.prec}, routing "
+          f"{wl.routing} (R={routed} routed rows).  One MI355X.  Source digest of the kernels "
+          f"profiled (`bench.py` `source_hash()`): `{source_hash()}`.\n")
+    print("Commands (repository root; `export TMPDIR=/tmp` first; OUT is any scratch directory):\n")
+    print("```")
+    print(f"rocprofv3 --kernel-trace --stats -d OUT/kt_{w} -o run --output-format csv -- "
+          f"python3 bench.py --workload {w} {steps} --cpu-tokens 0{comp}")
+    if not fwd_only:
+        for c, tag in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
+            print(f"rocprofv3 --pmc {c} -d OUT/{tag}_{w} -o run --output-format csv -- python3 "
+                  f"bench.py --workload {w} --steps 2 --warmup 1 --cpu-tokens 0{comp}")
+        for c, tag in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
+            print(f"rocprofv3 --pmc {c} -d OUT/cal_{tag} -o run --output-format csv -- python3 "
+                  f"bench.py --calibrate-copy 1024")
+        print(f"python3 bench.py --workload {w} --traffic OUT/fetch_{w} OUT/write_{w} "
+              f"OUT/cal_fetch OUT/cal_write   # -> profiles/traffic.json")
+    print(f"python3 bench.py --workload {w} --profile-md OUT/kt_{w} > profiles/{w}_layer_kernels.md")
+    print("```\n")
+    total = sum(float(r["TotalDurationNs"]) for r in rows)
+    print("## Kernel trace (`run_kernel_stats.csv`; the run's warm-up, per-kernel-event and "
+          "timed steps together)\n")
+    print("| kernel | launch name(s) | calls | average µs | share |")
+    print("|---|---|---:|---:|---:|")
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        name = _symbol_of(r["Name"])
+        if name.startswith("__amd_rocclr") or "elementwise" in name or "at::" in name:
+            continue
+        sym = next((k for k in _SYMBOLS if name.startswith(k.split("<")[0]) and
+                    (("<" not in k) or name.startswith(k))), None)
+        launches = " + ".join(dict.fromkeys(_SYMBOLS[sym])) if sym else ""
+        share = 100.0 * float(r["TotalDurationNs"]) / total
+        print(f"| `{name}` | {launches} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+              f"{share:.2f}% |")
+    print()
+    try:
+        with open(TRAFFIC_JSON) as fh:
+            data = json.load(fh)
+    except (OSError, ValueError):
+        data = {}
+    tw = data.get("workloads", {}).get(w) if data.get("source_hash") == source_hash() else None
+    if tw:
+        cal = tw["calibration"]
+        print("## HBM traffic per launch (calibrated)\n")
+        print(f"A 1 GiB device-to-device copy reads FETCH_SIZE x {1.0 / cal['fetch_scale']:.4f} and "
+              f"writes WRITE_SIZE x {1.0 / cal['write_scale']:.4f} of its true bytes; every counter "
+              "below is scaled by those factors.\n")
+        print("| launch | fetch MB | write MB | total MB |")
+        print("|---|---:|---:|---:|")
+        ks = tw["kernels"]
+        for k in sorted(ks, key=lambda k: -(ks[k]["fetch_bytes"] + ks[k]["write_bytes"])):
+            f_, w_ = ks[k]["fetch_bytes"] / 1e6, ks[k]["write_bytes"] / 1e6
+            if f_ + w_ < 1.0:
+                continue
+            print(f"| `{k}` | {f_:.0f} | {w_:.0f} | {f_ + w_:.0f} |")
+        print()
     return 0
 
 
@@ -302,6 +407,10 @@ def main(argv=None) -> int:
                     help="only summarise a rocprofv3 --pmc run of SQ_VALU_MFMA_BUSY_CYCLES, "
                          "SQ_BUSY_CU_CYCLES and GRBM_GUI_ACTIVE (this workload, with the clock "
                          "probe) as a markdown table on stdout and exit")
+    ap.add_argument("--profile-md", metavar="KT_DIR",
+                    help="only print the markdown profile summary of this workload from a "
+                         "rocprofv3 --kernel-trace --stats directory (and the committed traffic "
+                         "counters) and exit")
     ap.add_argument("--traffic", nargs=4, metavar=("FETCH", "WRITE", "CAL_FETCH", "CAL_WRITE"),
                     help="only summarise four rocprofv3 --pmc output directories (FETCH_SIZE and "
                          "WRITE_SIZE of this workload, then of --calibrate-copy 1024) into "
@@ -312,6 +421,8 @@ def main(argv=None) -> int:
         return write_traffic(args.workload, *args.traffic)
     if args.mfma_summary:
         return mfma_summary(args.workload, args.mfma_summary)
+    if args.profile_md:
+        return profile_markdown(args.workload, args.profile_md)
 
     if args.calibrate_copy:
         import torch
