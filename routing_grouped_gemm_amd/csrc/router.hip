@@ -237,10 +237,12 @@ hipError_t launch_router_logits(const uint16_t* x, const uint16_t* Wr, int T, in
 // ---------------------------------------------------------------------------
 // dl16 [T][ld] bf16 (zero past E, ld = 64 * ceil(E / 64)) and Wr [d][E] both
 // run along e in memory, so both MFMA operands come straight from global
-// memory (Wr from L2).  A wave takes 16 tokens and one of P column parts (P
-// sized so that the chip holds four such waves per SIMD), 64 columns at a
-// time as four 16x16 blocks (D[column][token] on 16x16x32 bf16 MFMAs over
-// K = ld).  The block sums pass through a private LDS slice so that dx is
+// memory (Wr from L2).  A workgroup takes 32 tokens and each of its waves one
+// of P column parts (P sized for about 4096 waves), 64 columns at a time as
+// four 16x16 blocks per 16-token half (D[column][token] on 16x16x32 bf16
+// MFMAs over K = ld); each weight fragment read from L2 feeds both halves'
+// MFMAs (with 16 tokens a wave, Wr was read twice as often: 156 -> 104 us
+// at 16384 tokens x 4096 x 128 experts, 30 -> 24 us at 8192 x 2048 x 64).  The block sums pass through a private LDS slice so that dx is
 // read and written in 16-byte pieces along its rows (8 tokens x 128 bytes
 // per instruction); each element gets one bf16 rounding of old + sum.  The
 // old dx of the next 64 columns is loaded while the current ones are
@@ -253,19 +255,24 @@ template <int NK>
 __global__ __launch_bounds__(256) void router_dx_kernel(const uint16_t* __restrict__ dl16, int ld,
                                                         const uint16_t* __restrict__ Wr, int T,
                                                         int d, int E, uint16_t* __restrict__ dx) {
-  __shared__ __attribute__((aligned(16))) float slice_all[4][16 * kRdxPitch];
+  __shared__ __attribute__((aligned(16))) float slice_all[4][32 * kRdxPitch];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int tg = wave & 1, part = blockIdx.y * 2 + (wave >> 1), P = gridDim.y * 2;
+  // the workgroup's 32 tokens, each wave a column part of them
+  const int part = blockIdx.y * 4 + wave, P = gridDim.y * 4;
   const int tl = lane & 15, G = lane >> 4;
-  const int tbase = blockIdx.x * 32 + tg * 16;
+  const int tbase = blockIdx.x * 32;
   float* const slice = slice_all[wave];
-  // MFMA side: lane (row tl, k-group G) supplies k = 32s + 8G + (0..7)
-  const long trow = min(tbase + tl, T - 1);
-  bf16x8_t bfr[NK];
+  // MFMA side: token set h (tokens 16h + tl), lane k-group G supplies
+  // k = 32s + 8G + (0..7); each weight fragment serves both sets
+  bf16x8_t bfr[2][NK];
 #pragma unroll
-  for (int s = 0; s < NK; ++s)
-    bfr[s] = __builtin_bit_cast(bf16x8_t,
-                                *reinterpret_cast<const u32x4_t*>(dl16 + trow * ld + 32 * s + 8 * G));
+  for (int h = 0; h < 2; ++h) {
+    const long trow = min(tbase + 16 * h + tl, T - 1);
+#pragma unroll
+    for (int s = 0; s < NK; ++s)
+      bfr[h][s] = __builtin_bit_cast(
+          bf16x8_t, *reinterpret_cast<const u32x4_t*>(dl16 + trow * ld + 32 * s + 8 * G));
+  }
   bool eok[NK];
   int eoff[NK];
 #pragma unroll
@@ -274,11 +281,15 @@ __global__ __launch_bounds__(256) void router_dx_kernel(const uint16_t* __restri
     eok[s] = e < E;
     eoff[s] = min(e, E - 8);
   }
-  // dx side: lane (row r and r + 8, 8 columns at 8cq)
+  // dx side: lane (rows r + 8q, q = 0..3; 8 columns at 8cq)
   const int r = lane >> 3, cq = lane & 7;
-  const int ta = tbase + r, tb = tbase + r + 8;
-  uint16_t* const xa = dx + (long)min(ta, T - 1) * d + 8 * cq;
-  uint16_t* const xb = dx + (long)min(tb, T - 1) * d + 8 * cq;
+  int trw[4];
+  uint16_t* xr[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    trw[q] = tbase + r + 8 * q;
+    xr[q] = dx + (long)min(trw[q], T - 1) * d + 8 * cq;
+  }
 
   const int ngrp = d / 64;
   const int per = (ngrp + P - 1) / P;  // 64-column groups of each part
@@ -286,12 +297,12 @@ __global__ __launch_bounds__(256) void router_dx_kernel(const uint16_t* __restri
   const int ng = min(per, ngrp - g0);
   if (ng <= 0) return;
 
-  auto load_old = [&](int gi, u32x4_t& oa, u32x4_t& ob) __attribute__((always_inline)) {
+  auto load_old = [&](int gi, u32x4_t (&o)[4]) __attribute__((always_inline)) {
     const int c0 = 64 * (g0 + min(gi, ng - 1));
-    oa = *reinterpret_cast<const u32x4_t*>(xa + c0);
-    ob = *reinterpret_cast<const u32x4_t*>(xb + c0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] = *reinterpret_cast<const u32x4_t*>(xr[q] + c0);
   };
-  auto compute = [&](int gi, const u32x4_t& oa, const u32x4_t& ob) __attribute__((always_inline)) {
+  auto compute = [&](int gi, const u32x4_t (&o)[4]) __attribute__((always_inline)) {
     const int c0 = 64 * (g0 + gi);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -299,41 +310,47 @@ __global__ __launch_bounds__(256) void router_dx_kernel(const uint16_t* __restri
       u32x4_t w[NK];
 #pragma unroll
       for (int s = 0; s < NK; ++s) w[s] = *reinterpret_cast<const u32x4_t*>(wr + eoff[s]);
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < NK; ++s) {
-        const u32x4_t a = eok[s] ? w[s] : u32x4_t{0, 0, 0, 0};
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), bfr[s], acc,
-                                                      0, 0, 0);
+        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, eok[s] ? w[s] : u32x4_t{0, 0, 0, 0});
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bfr[0][s], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bfr[1][s], acc1, 0, 0, 0);
       }
-      // columns 16j + 4G + (0..3) of token tl
-      *reinterpret_cast<f32x4_t*>(slice + tl * kRdxPitch + 16 * j + 4 * G) = acc;
+      // columns 16j + 4G + (0..3) of tokens tl and 16 + tl
+      *reinterpret_cast<f32x4_t*>(slice + tl * kRdxPitch + 16 * j + 4 * G) = acc0;
+      *reinterpret_cast<f32x4_t*>(slice + (16 + tl) * kRdxPitch + 16 * j + 4 * G) = acc1;
     }
     // the slice is private to the wave and LDS accesses of a wave complete in order
     __builtin_amdgcn_wave_barrier();
-    float va[8], vb[8], oa8[8], ob8[8];
-    const f32x4_t* pa = reinterpret_cast<const f32x4_t*>(slice + r * kRdxPitch + 8 * cq);
-    const f32x4_t* pb = reinterpret_cast<const f32x4_t*>(slice + (r + 8) * kRdxPitch + 8 * cq);
-    const f32x4_t a0 = pa[0], a1 = pa[1], b0 = pb[0], b1 = pb[1];
-    __builtin_amdgcn_wave_barrier();
-    unpack8(uint4{oa[0], oa[1], oa[2], oa[3]}, oa8);
-    unpack8(uint4{ob[0], ob[1], ob[2], ob[3]}, ob8);
+    f32x4_t v0[4], v1[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      va[q] = a0[q] + oa8[q]; va[q + 4] = a1[q] + oa8[q + 4];
-      vb[q] = b0[q] + ob8[q]; vb[q + 4] = b1[q] + ob8[q + 4];
+      const f32x4_t* pv = reinterpret_cast<const f32x4_t*>(slice + (r + 8 * q) * kRdxPitch + 8 * cq);
+      v0[q] = pv[0];
+      v1[q] = pv[1];
     }
-    if (ta < T) store8(xa + c0, va);
-    if (tb < T) store8(xb + c0, vb);
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float o8[8], v[8];
+      unpack8(uint4{o[q][0], o[q][1], o[q][2], o[q][3]}, o8);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        v[u] = v0[q][u] + o8[u];
+        v[u + 4] = v1[q][u] + o8[u + 4];
+      }
+      if (trw[q] < T) store8(xr[q] + c0, v);
+    }
   };
 
-  u32x4_t oa0, ob0, oa1, ob1;
-  load_old(0, oa0, ob0);
+  u32x4_t oa[4], ob[4];
+  load_old(0, oa);
   for (int gi = 0; gi < ng; gi += 2) {
-    load_old(gi + 1, oa1, ob1);
-    compute(gi, oa0, ob0);
-    load_old(gi + 2, oa0, ob0);
-    if (gi + 1 < ng) compute(gi + 1, oa1, ob1);
+    load_old(gi + 1, ob);
+    compute(gi, oa);
+    load_old(gi + 2, oa);
+    if (gi + 1 < ng) compute(gi + 1, ob);
   }
 }
 
@@ -342,11 +359,11 @@ bool router_dx_applies(int d, int E) { return E % 8 == 0 && E <= 256 && d % 64 =
 hipError_t launch_router_dx(const uint16_t* dl16, int ld, const uint16_t* Wr, int T, int d, int E,
                             uint16_t* dx, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  // column parts: about 4096 waves in all, 2 to d/64 parts
+  // column parts: about 4096 waves in all, 4 to d/64 parts (four a workgroup)
   const int tiles = (T + 31) / 32;
-  int P = 2;
-  while (2 * P <= d / 64 && (long)tiles * 2 * P < 4096) P *= 2;
-  const dim3 grid(tiles, P / 2);
+  int P = 4;
+  while (2 * P <= d / 64 && (long)tiles * P < 4096) P *= 2;
+  const dim3 grid(tiles, P / 4);
   note_prelaunch("router_dx", s);
   switch (ld / 32) {
     case 2:
