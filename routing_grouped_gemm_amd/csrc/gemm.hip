@@ -123,19 +123,25 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(GemmArgs g) {
     Tile tn = t;
     if (has_next) tn = sched_decode<BM, BNT>(g, sch, L);
     for (int kt = 0; kt < nk; ++kt) {
-      __builtin_amdgcn_s_waitcnt(kLgkm0);
-      load_frags<AMN, BMN, DUAL>(smem, kt, 1, wm, wn, lane, fa1, fb1);
+      // step 0 (set F0), reading F1 for step 1
       if (kt == 0) {
-        mfma16_first(acc, fa0, fb0);
-        interleave_mfma_ds();
-        __builtin_amdgcn_sched_barrier(0);
+        kstep<AMN, BMN, DUAL, true>(acc, fa0, fb0, fa1, fb1, smem, kt, 1, wm, wn, lane);
       } else {
+        // with the B loads (and prefetches) of stage kt+1 between MFMA pairs
         const bool dma = pend_b;
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
+          if (q == 2) {
+            __builtin_amdgcn_s_waitcnt(kLgkm0);
+            __builtin_amdgcn_sched_barrier(0);
+          }
           mfma_pair(acc, fa0, fb0, q);
           if (dma) issue_one<BMN>(pb, pend_stage, lds0 + (pend_stage & 1) * STAGE + OPB, wave, q);
+          if (q >= 2 && q < 6) {
+            load_frag<AMN, BMN, DUAL>(smem, kt, 1, wm, wn, lane, fa1, fb1, 2 * (q - 2));
+            load_frag<AMN, BMN, DUAL>(smem, kt, 1, wm, wn, lane, fa1, fb1, 2 * (q - 2) + 1);
+          }
           __builtin_amdgcn_sched_barrier(0);
         }
         if (dma) {
@@ -149,16 +155,8 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(GemmArgs g) {
         __builtin_amdgcn_sched_barrier(0);
         pend_b = false;
       }
-      __builtin_amdgcn_s_waitcnt(kLgkm0);
-      load_frags<AMN, BMN, DUAL>(smem, kt, 2, wm, wn, lane, fa0, fb0);
-      mfma16(acc, fa1, fb1);
-      interleave_mfma_ds();
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_waitcnt(kLgkm0);
-      load_frags<AMN, BMN, DUAL>(smem, kt, 3, wm, wn, lane, fa1, fb1);
-      mfma16(acc, fa0, fb0);
-      interleave_mfma_ds();
-      __builtin_amdgcn_sched_barrier(0);
+      kstep<AMN, BMN, DUAL, false>(acc, fa1, fb1, fa0, fb0, smem, kt, 2, wm, wn, lane);
+      kstep<AMN, BMN, DUAL, false>(acc, fa0, fb0, fa1, fb1, smem, kt, 3, wm, wn, lane);
       __builtin_amdgcn_s_waitcnt(kLgkm0);
       const bool more = kt + 1 < nk;
       // stage kt+1 has landed once only its prefetch loads may be pending
@@ -166,7 +164,9 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(GemmArgs g) {
         if (pf_on) wait_vmcnt<PF_PER_STAGE>(); else wait_vmcnt<0>();
       }
       barrier();
-      if (more) load_frags<AMN, BMN, DUAL>(smem, kt + 1, 0, wm, wn, lane, fa0, fb0);
+      // step 3 (set F1) with the A loads of stage kt+2 between MFMA pairs,
+      // reading F0 for step 0 of stage kt+1 (past the last stage the reads
+      // land in the idle buffer and go unused)
       const bool dma = kt + 2 < nk;
       if (dma) pend_stage = kt + 2;
       __builtin_amdgcn_sched_barrier(0);
@@ -174,6 +174,10 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(GemmArgs g) {
       for (int q = 0; q < 8; ++q) {
         mfma_pair(acc, fa1, fb1, q);
         if (dma) issue_one<AMN>(pa, pend_stage, lds0 + (pend_stage & 1) * STAGE, wave, q);
+        if (q < 4) {
+          load_frag<AMN, BMN, DUAL>(smem, kt + 1, 0, wm, wn, lane, fa0, fb0, 2 * q);
+          load_frag<AMN, BMN, DUAL>(smem, kt + 1, 0, wm, wn, lane, fa0, fb0, 2 * q + 1);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
       pend_b = dma;

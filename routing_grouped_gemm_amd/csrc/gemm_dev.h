@@ -572,8 +572,64 @@ __device__ __forceinline__ void mfma_pair(f32x16_t (&acc)[4][4], const bf16x8_t 
   acc[i][j + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j + 1], fa[i], acc[i][j + 1], 0, 0, 0);
 }
 
+// One fragment of a k16 step: p = 0-3 the B fragments (columns of wave
+// column wn; gate/up pairs when DUAL), p = 4-7 the A fragments (rows
+// wm*128 + 32(p-4)).  The B fragments come first: the MFMAs of row block 0
+// need all four of them and only the first A fragment.
+template <bool AMN, bool BMN, bool DUAL>
+__device__ __forceinline__ void load_frag(const char* smem, int kt, int s, int wm, int wn, int lane,
+                                          bf16x8_t (&fa)[4], bf16x8_t (&fb)[4], int p) {
+  const char* As = smem + (kt & (NST - 1)) * STAGE;
+  const char* Bs = As + OPB;
+  if (p < 4) {
+    const int col = DUAL ? ((p >> 1) * 128 + wn * 64 + (p & 1) * 32) : (wn * 128 + p * 32);
+    fb[p] = frag<BMN>(Bs, col, s, lane);
+  } else {
+    fa[p - 4] = frag<AMN>(As, wm * 128 + (p - 4) * 32, s, lane);
+  }
+}
+
+// MFMA m (0-15) of a k16 step: row block m/4, column block m%4; FIRST: the
+// tile's first step, from a zero accumulator.
+template <bool FIRST>
+__device__ __forceinline__ void mfma_one(f32x16_t (&acc)[4][4], const bf16x8_t (&fa)[4],
+                                         const bf16x8_t (&fb)[4], int m) {
+  const int i = m >> 2, j = m & 3;
+  acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], FIRST ? f32x16_t{} : acc[i][j],
+                                                      0, 0, 0);
+}
+
 // s_waitcnt with lgkmcnt(0) and the other counters left alone (gfx9 encoding).
 constexpr int kLgkm0 = 0xC07F;
+
+// A k16 step without DMA: the 16 MFMAs of fragment set (ca, cb), and the
+// reads of the next step's set into (na, nb) at (kt, s).  Row block 0 goes
+// first (it needs the first reads of the current set); then one wait for the
+// rest of the current set, after which the next set's reads go out two
+// between each of the next MFMAs, so that the last of them has about ten
+// MFMAs to land before the next step's wait.
+template <bool AMN, bool BMN, bool DUAL, bool FIRST>
+__device__ __forceinline__ void kstep(f32x16_t (&acc)[4][4], const bf16x8_t (&ca)[4],
+                                      const bf16x8_t (&cb)[4], bf16x8_t (&na)[4], bf16x8_t (&nb)[4],
+                                      const char* smem, int kt, int s, int wm, int wn, int lane) {
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int m = 0; m < 4; ++m) mfma_one<FIRST>(acc, ca, cb, m);
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(kLgkm0);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int p = 0; p < 8; ++p) load_frag<AMN, BMN, DUAL>(smem, kt, s, wm, wn, lane, na, nb, p);
+#pragma unroll
+  for (int m = 4; m < 16; ++m) mfma_one<FIRST>(acc, ca, cb, m);
+#pragma unroll
+  for (int i = 0; i < 6; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS reads
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+  __builtin_amdgcn_sched_barrier(0);
+}
 
 // Ask the scheduler to alternate MFMAs and LDS reads (16 each at most) in the
 // region since the last scheduling barrier.
