@@ -82,6 +82,54 @@ __device__ __forceinline__ void mfma8_pair(f32x16_t (&acc)[4][2], const bf16x8_t
   acc[q][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[0], fa[q], acc[q][0], 0, 0, 0);
   acc[q][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[1], fa[q], acc[q][1], 0, 0, 0);
 }
+// One fragment of a k16 step: p = 0-1 the B fragments, p = 2-5 the A
+// fragments.  B first: the MFMAs of row block 0 need both B fragments and
+// only the first A fragment.
+template <bool AMN, bool BMN, bool DUAL>
+__device__ __forceinline__ void load_frag8(const char* smem, int kt, int s, int wm, int wn, int lane,
+                                           bf16x8_t (&fa)[4], bf16x8_t (&fb)[2], int p) {
+  const char* As = smem + (kt & (NST - 1)) * STAGE;
+  const char* Bs = As + OPB;
+  if (p < 2) {
+    const int col = DUAL ? (p * 128 + wn * 32) : (wn * 64 + p * 32);
+    fb[p] = frag<BMN>(Bs, col, s, lane);
+  } else {
+    fa[p - 2] = frag<AMN>(As, wm * 128 + (p - 2) * 32, s, lane);
+  }
+}
+// The reads of a whole fragment set, B first.
+template <bool AMN, bool BMN, bool DUAL>
+__device__ __forceinline__ void load_set8(const char* smem, int kt, int s, int wm, int wn, int lane,
+                                          bf16x8_t (&fa)[4], bf16x8_t (&fb)[2]) {
+#pragma unroll
+  for (int p = 0; p < 6; ++p) load_frag8<AMN, BMN, DUAL>(smem, kt, s, wm, wn, lane, fa, fb, p);
+}
+template <bool FIRST>
+__device__ __forceinline__ void mfma8_row(f32x16_t (&acc)[4][2], const bf16x8_t (&fa)[4],
+                                          const bf16x8_t (&fb)[2], int q) {
+  acc[q][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[0], fa[q], FIRST ? f32x16_t{} : acc[q][0], 0, 0, 0);
+  acc[q][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[1], fa[q], FIRST ? f32x16_t{} : acc[q][1], 0, 0, 0);
+}
+// A k16 step without DMA: the MFMAs of row block 0 of set (ca, cb) (they
+// need only its first reads), one wait for the rest of the set, the reads of
+// the next step's set into (na, nb), then the remaining MFMAs.  The next
+// reads thus have most of a step to land before the next step's wait.
+template <bool AMN, bool BMN, bool DUAL, bool FIRST>
+__device__ __forceinline__ void kstep8(f32x16_t (&acc)[4][2], const bf16x8_t (&ca)[4],
+                                       const bf16x8_t (&cb)[2], bf16x8_t (&na)[4], bf16x8_t (&nb)[2],
+                                       const char* smem, int kt, int s, int wm, int wn, int lane) {
+  __builtin_amdgcn_sched_barrier(0);
+  mfma8_row<FIRST>(acc, ca, cb, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(kLgkm0);
+  __builtin_amdgcn_sched_barrier(0);
+  load_set8<AMN, BMN, DUAL>(smem, kt, s, wm, wn, lane, na, nb);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int q = 1; q < 4; ++q) mfma8_row<FIRST>(acc, ca, cb, q);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 __device__ __forceinline__ void interleave8() {
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -337,13 +385,11 @@ __global__ __launch_bounds__(NTHR8, 1) void gemm8_kernel(GemmArgs g) {
     Tile tn = t;
     if (has_next) tn = sched_decode<BM, BNT>(g, sch, L);
     for (int kt = 0; kt < nk; ++kt) {
-      __builtin_amdgcn_s_waitcnt(kLgkm0);
-      load_frags8<AMN, BMN, DUAL>(smem, kt, 1, wm, wn, lane, fa1, fb1);
+      // step 0 (set F0), reading F1 for step 1
       if (kt == 0) {
-        mfma8_first(acc, fa0, fb0);
-        interleave8();
-        __builtin_amdgcn_sched_barrier(0);
+        kstep8<AMN, BMN, DUAL, true>(acc, fa0, fb0, fa1, fb1, smem, kt, 1, wm, wn, lane);
       } else if constexpr (SPLIT) {
+        // with the B loads (and prefetches) of stage kt+1 between MFMA pairs
         const bool dma = pend_b;
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -351,6 +397,12 @@ __global__ __launch_bounds__(NTHR8, 1) void gemm8_kernel(GemmArgs g) {
           mfma8_pair(acc, fa0, fb0, q);
           if (dma)
             issue_one<BMN, DPO8, NW>(pb, pend_stage, lds0 + (pend_stage & 1) * STAGE + OPB, wave, q);
+          if (q == 0) {
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_waitcnt(kLgkm0);
+            __builtin_amdgcn_sched_barrier(0);
+            load_set8<AMN, BMN, DUAL>(smem, kt, 1, wm, wn, lane, fa1, fb1);
+          }
           __builtin_amdgcn_sched_barrier(0);
         }
         if (dma) {
@@ -364,20 +416,11 @@ __global__ __launch_bounds__(NTHR8, 1) void gemm8_kernel(GemmArgs g) {
         __builtin_amdgcn_sched_barrier(0);
         pend_b = false;
       } else {
-        mfma8(acc, fa0, fb0);
-        interleave8();
-        __builtin_amdgcn_sched_barrier(0);
+        kstep8<AMN, BMN, DUAL, false>(acc, fa0, fb0, fa1, fb1, smem, kt, 1, wm, wn, lane);
       }
-      __builtin_amdgcn_s_waitcnt(kLgkm0);
-      load_frags8<AMN, BMN, DUAL>(smem, kt, 2, wm, wn, lane, fa0, fb0);
-      mfma8(acc, fa1, fb1);
-      interleave8();
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_waitcnt(kLgkm0);
-      load_frags8<AMN, BMN, DUAL>(smem, kt, 3, wm, wn, lane, fa1, fb1);
-      mfma8(acc, fa0, fb0);
-      interleave8();
-      __builtin_amdgcn_sched_barrier(0);
+      kstep8<AMN, BMN, DUAL, false>(acc, fa1, fb1, fa0, fb0, smem, kt, 2, wm, wn, lane);
+      // step 2 (set F0), reading F1 for step 3
+      kstep8<AMN, BMN, DUAL, false>(acc, fa0, fb0, fa1, fb1, smem, kt, 3, wm, wn, lane);
       __builtin_amdgcn_s_waitcnt(kLgkm0);
       const bool more = kt + 1 < nk;
       // stage kt+1 has landed once only its prefetch loads may be pending
@@ -385,8 +428,9 @@ __global__ __launch_bounds__(NTHR8, 1) void gemm8_kernel(GemmArgs g) {
         if (pf_on) wait_vmcnt<PF8>(); else wait_vmcnt<0>();
       }
       barrier();
+      // step 3 (set F1), reading F0 for step 0 of stage kt+1 (past the last
+      // stage the reads land in the idle buffer and go unused)
       if constexpr (SPLIT) {
-        if (more) load_frags8<AMN, BMN, DUAL>(smem, kt + 1, 0, wm, wn, lane, fa0, fb0);
         const bool dma = kt + 2 < nk;
         if (dma) pend_stage = kt + 2;
         __builtin_amdgcn_sched_barrier(0);
@@ -394,14 +438,19 @@ __global__ __launch_bounds__(NTHR8, 1) void gemm8_kernel(GemmArgs g) {
         for (int q = 0; q < 4; ++q) {
           mfma8_pair(acc, fa1, fb1, q);
           if (dma) issue_one<AMN, DPO8, NW>(pa, pend_stage, lds0 + (pend_stage & 1) * STAGE, wave, q);
+          if (q == 0) load_set8<AMN, BMN, DUAL>(smem, kt + 1, 0, wm, wn, lane, fa0, fb0);
           __builtin_amdgcn_sched_barrier(0);
         }
         pend_b = dma;
       } else {
         if (kt + 2 < nk) issue_stage(pa, pb, kt + 2);
-        if (more) load_frags8<AMN, BMN, DUAL>(smem, kt + 1, 0, wm, wn, lane, fa0, fb0);
-        mfma8(acc, fa1, fb1);
-        interleave8();
+        __builtin_amdgcn_sched_barrier(0);
+        mfma8_row<false>(acc, fa1, fb1, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        load_set8<AMN, BMN, DUAL>(smem, kt + 1, 0, wm, wn, lane, fa0, fb0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int q = 1; q < 4; ++q) mfma8_row<false>(acc, fa1, fb1, q);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
