@@ -264,6 +264,74 @@ def mfma_summary(workload_name: str, directory: str) -> int:
     return 0
 
 
+SQ_PASSES = (
+    "SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_BUSY_CU_CYCLES SQ_VALU_MFMA_BUSY_CYCLES "
+    "SQ_WAIT_INST_LDS SQ_ACTIVE_INST_LDS SQ_ACTIVE_INST_VMEM",
+    "SQ_VMEM_TA_CMD_FIFO_FULL SQ_VMEM_TA_ADDR_FIFO_FULL SQ_LDS_DATA_FIFO_FULL "
+    "SQ_LDS_CMD_FIFO_FULL SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_INSTS_LDS SQ_INSTS_VMEM",
+)
+
+
+def sq_summary(workload_name: str, dirs) -> int:
+    """Where the expert GEMMs' waves spend their cycles, from the two
+    rocprofv3 --pmc passes of SQ_PASSES: per-wave stall fractions (the
+    SQ_WAIT_*/SQ_ACTIVE_* counters are in wave quad-cycles against
+    SQ_WAVE_CYCLES) and, per CU and clock cycle of the dispatch, how often the
+    TA and LDS queues were full and the LDS busy."""
+    import csv
+    import glob
+    acc, ns = {}, {}
+    for d in dirs:
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(path) as fh:
+                for r in csv.DictReader(fh):
+                    name = _symbol_of(r["Kernel_Name"])
+                    if not (name.startswith("gemm_bf16_kernel") or name.startswith("gemm8_kernel")):
+                        continue
+                    acc.setdefault(name, {}).setdefault(r["Counter_Name"], []).append(
+                        float(r["Counter_Value"]))
+                    if r["Counter_Name"] == "SQ_INSTS_LDS":
+                        ns.setdefault(name, []).append(
+                            int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    w = workload_name
+    comp = " --no-companions" if w == "olmoe_bf16" else ""
+    print(f"# {w}: where the GEMM waves wait (SQ counters)\n")
+    print(f"Source digest (`bench.py` `source_hash()`): `{source_hash()}`.  One MI355X.\n")
+    print("Commands (repository root; `export TMPDIR=/tmp` first; OUT is any scratch directory):\n")
+    print("```")
+    for i, p in enumerate(SQ_PASSES):
+        print(f"rocprofv3 --pmc {p} -d OUT/sq{i + 1}_{w} -o run --output-format csv -- python3 "
+              f"bench.py --workload {w} --steps 3 --warmup 1 --cpu-tokens 0{comp}")
+    print(f"python3 bench.py --workload {w} --sq-summary OUT/sq1_{w} OUT/sq2_{w} > "
+          f"profiles/{w}_sq_counters.md")
+    print("```\n")
+    print("Per wave cycle: waiting on `s_waitcnt` or a barrier (WAIT_ANY), an instruction "
+          "ready but not issued (WAIT_INST_ANY: mostly an MFMA waiting for the matrix core), "
+          "issuing LDS and vector-memory instructions.  Per CU and cycle (the device-wide sums "
+          "over 256 CUs times the dispatch's duration at 2.05 GHz): TA command/address queue full, "
+          "LDS data queue full, LDS busy with indexed accesses, LDS bank-conflict stalls.\n")
+    print("| kernel | µs | MFMA busy | WAIT_ANY | WAIT_INST_ANY | LDS issue | VMEM issue | "
+          "TA cmd full | TA addr full | LDS data full | LDS busy | bank conflict |")
+    print("|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|")
+    for name in sorted(acc):
+        m = {k: sum(v) / len(v) for k, v in acc[name].items()}
+        if "SQ_WAVE_CYCLES" not in m or "SQ_INSTS_LDS" not in m:
+            continue
+        wc = 4.0 * m["SQ_WAVE_CYCLES"]
+        dur = sum(ns[name]) / len(ns[name])
+        cyc = 256.0 * dur * 2.05
+        f = lambda k: 4.0 * m[k] / wc
+        c = lambda k: m[k] / cyc
+        busy = m["SQ_VALU_MFMA_BUSY_CYCLES"] / (4.0 * m["SQ_BUSY_CU_CYCLES"])
+        launches = " + ".join(dict.fromkeys(_SYMBOLS.get(name, [name])))
+        print(f"| `{name}` ({launches}) | {dur / 1e3:.0f} | {busy:.2f} | {f('SQ_WAIT_ANY'):.2f} | "
+              f"{f('SQ_WAIT_INST_ANY'):.2f} | {f('SQ_ACTIVE_INST_LDS'):.2f} | "
+              f"{f('SQ_ACTIVE_INST_VMEM'):.2f} | {c('SQ_VMEM_TA_CMD_FIFO_FULL'):.3f} | "
+              f"{c('SQ_VMEM_TA_ADDR_FIFO_FULL'):.3f} | {c('SQ_LDS_DATA_FIFO_FULL'):.3f} | "
+              f"{c('SQ_LDS_IDX_ACTIVE'):.3f} | {c('SQ_LDS_BANK_CONFLICT'):.3f} |")
+    return 0
+
+
 def _symbol_of(kernel_name: str) -> str:
     name = kernel_name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
     for pre in ("moe::mf::", "moe::mf8::", "moe::sk::", "moe::st::", "moe::"):
@@ -413,6 +481,9 @@ def main(argv=None) -> int:
                     help="only summarise a rocprofv3 --pmc run of SQ_VALU_MFMA_BUSY_CYCLES, "
                          "SQ_BUSY_CU_CYCLES and GRBM_GUI_ACTIVE (this workload, with the clock "
                          "probe) as a markdown table on stdout and exit")
+    ap.add_argument("--sq-summary", nargs=2, metavar=("PASS1_DIR", "PASS2_DIR"),
+                    help="only summarise the two rocprofv3 --pmc passes of SQ_PASSES (GEMM wave "
+                         "stalls, queue-full and LDS counters) as markdown on stdout and exit")
     ap.add_argument("--profile-md", metavar="KT_DIR",
                     help="only print the markdown profile summary of this workload from a "
                          "rocprofv3 --kernel-trace --stats directory (and the committed traffic "
@@ -429,6 +500,8 @@ def main(argv=None) -> int:
         return mfma_summary(args.workload, args.mfma_summary)
     if args.profile_md:
         return profile_markdown(args.workload, args.profile_md)
+    if args.sq_summary:
+        return sq_summary(args.workload, args.sq_summary)
 
     if args.calibrate_copy:
         import torch
