@@ -60,22 +60,6 @@ __device__ __forceinline__ void load_frags8(const char* smem, int kt, int s, int
   }
 }
 
-__device__ __forceinline__ void mfma8(f32x16_t (&acc)[4][2], const bf16x8_t (&fa)[4],
-                                      const bf16x8_t (&fb)[2]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
-}
-__device__ __forceinline__ void mfma8_first(f32x16_t (&acc)[4][2], const bf16x8_t (&fa)[4],
-                                            const bf16x8_t (&fb)[2]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], f32x16_t{}, 0, 0, 0);
-}
 // The two MFMAs of row block q.
 __device__ __forceinline__ void mfma8_pair(f32x16_t (&acc)[4][2], const bf16x8_t (&fa)[4],
                                            const bf16x8_t (&fb)[2], int q) {
@@ -130,13 +114,6 @@ __device__ __forceinline__ void kstep8(f32x16_t (&acc)[4][2], const bf16x8_t (&c
   __builtin_amdgcn_sched_barrier(0);
 }
 
-__device__ __forceinline__ void interleave8() {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-  }
-}
 
 // Epilogue staging slice of one wave: 32 rows x 64 floats (256 bytes), the
 // 16-byte chunks of a row XOR-permuted by the row.

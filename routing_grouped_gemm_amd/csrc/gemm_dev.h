@@ -545,26 +545,7 @@ __device__ __forceinline__ void load_frags(const char* smem, int kt, int s, int 
   }
 }
 
-__device__ __forceinline__ void mfma16(f32x16_t (&acc)[4][4], const bf16x8_t (&fa)[4],
-                                       const bf16x8_t (&fb)[4]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
-}
-
-// The first k16 step of a tile: accumulators from a zero operand.
-__device__ __forceinline__ void mfma16_first(f32x16_t (&acc)[4][4], const bf16x8_t (&fa)[4],
-                                             const bf16x8_t (&fb)[4]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], f32x16_t{}, 0, 0, 0);
-}
-
-// MFMAs 2q and 2q+1 of mfma16 (row block q/2, column blocks 2(q%2), +1).
+// MFMAs 2q and 2q+1 of a k16 step (row block q/2, column blocks 2(q%2), +1).
 __device__ __forceinline__ void mfma_pair(f32x16_t (&acc)[4][4], const bf16x8_t (&fa)[4],
                                           const bf16x8_t (&fb)[4], int q) {
   const int i = q >> 1, j = 2 * (q & 1);
@@ -631,15 +612,6 @@ __device__ __forceinline__ void kstep(f32x16_t (&acc)[4][4], const bf16x8_t (&ca
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Ask the scheduler to alternate MFMAs and LDS reads (16 each at most) in the
-// region since the last scheduling barrier.
-__device__ __forceinline__ void interleave_mfma_ds() {
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-  }
-}
 
 // Operand plans of one tile for each bf16 GEMM kind (NWV waves, DPO DMA
 // blocks per wave and operand).
