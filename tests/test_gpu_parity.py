@@ -55,6 +55,12 @@ SHAPES = {
     # in every GEMM (d = 320, f = 192: 64- and 128-column remainders), for
     # the bf16-staged plain stores and the SwiGLU epilogues
     "ragged_n_bf16": ("olmoe_bf16", dict(name="ragged_n_bf16", T=600, d=320, E=8, f=192, k=2)),
+    # the largest expert count and a wide top-k: 256 experts of ~12 rows
+    # (many one-row and empty segments) through the 256x256 engine, and the
+    # same width on the small-batch forward engine (R = 1536 rows)
+    "max_E256_k16": ("olmoe_bf16", dict(name="max_E256_k16", T=200, d=128, E=256, f=64, k=16)),
+    "max_E256_k16_small": ("olmoe_bf16", dict(name="max_E256_k16_small", T=96, d=128, E=256, f=64,
+                                              k=16)),
     "tiny_mxfp8": ("tiny_mxfp8", {}),
     # d = 576: an odd number of 64-deep K stages; f = 320: a half-filled last gate/up panel
     "mid_mxfp8_E8": ("olmoe_mxfp8", dict(name="mid_mxfp8_E8", T=1000, d=576, E=8, f=320, k=2)),
