@@ -67,6 +67,8 @@ SHAPES = {
     "mid_mxfp8_E64": ("olmoe_mxfp8", dict(name="mid_mxfp8_E64", T=512, d=256, E=64, f=128, k=8)),
     "share_zipf_mxfp8": ("share1t_bf16", dict(name="share_zipf_mxfp8", T=3000, d=256, f=320,
                                               prec="mxfp8")),
+    "max_E256_k16_mxfp8": ("olmoe_mxfp8", dict(name="max_E256_k16_mxfp8", T=200, d=128, E=256,
+                                                f=64, k=16)),
 }
 
 
