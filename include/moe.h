@@ -45,7 +45,9 @@
  *       weight gradients (MOE_WGRAD_MX), Kp = sum over experts of n_e rounded
  *       up to 128 (bounded by (R + 127 E + 127) rounded down to 128):
  *                                     256 * Kp < 2^32 and
- *                                     (Kp / 32) * max(d, 2f) < 2^32.
+ *                                     (Kp / 32) * max(d, 2f) < 2^30;
+ *       MXFP8 activation scales:      ceil(max(d, 2f) / 128) * 4 * Rp < 2^30
+ *                                     (Rp = R rounded up to 16).
  *   - Errors are detected on the host before anything is enqueued and come
  *     back as a negative status; nothing is launched then.  There is no
  *     silent fallback to another precision or algorithm.  Values the host
@@ -143,9 +145,11 @@ int moe_route(const void* x, const void* Wr, int T, int d, int E, int k, int dty
  *   Xq, Xq_scale  prec MXFP8 only (ignored, may be NULL, otherwise): the
  *                 rows of Xs block-quantised along d.  Xq[R,d] holds e4m3
  *                 codes (1 byte each); Xq_scale holds the E8M0 bytes (2^E
- *                 stored as E + 127) block-major: the scale of block b
- *                 (elements 32b..32b+31) of row r is Xq_scale[b*Rp + r],
- *                 Rp = R rounded up to a multiple of 16, (d/32)*Rp bytes.
+ *                 stored as E + 127) in groups of four blocks: the scale
+ *                 of block b (elements 32b..32b+31) of row r is
+ *                 Xq_scale[((b/4)*Rp + r)*4 + b%4], Rp = R rounded up to a
+ *                 multiple of 16, ceil(d/128)*4*Rp bytes (the words of a
+ *                 partial last group hold unwritten bytes).
  *   Workspace: moe_workspace_size(MOE_OP_DISPATCH, ...).
  */
 int moe_dispatch(const void* x, const int32_t* topk_idx, int T, int d, int E, int k,
@@ -220,7 +224,8 @@ int moe_combine(const void* Ys, const float* topk_w, const int32_t* dest_row, in
  *   dYs_q, dYs_q_scale (optional; both NULL or both set, bf16 only): the rows
  *   of dYs as stored, block-quantised along d for an MXFP8 backward, laid out
  *   like moe_dispatch's Xq / Xq_scale (codes [R,d]; scale of block b of row r
- *   at dYs_q_scale[b*Rp + r], Rp = R rounded up to 16).
+ *   at dYs_q_scale[((b/4)*Rp + r)*4 + b%4], Rp = R rounded up to 16,
+ *   ceil(d/128)*4*Rp bytes).
  */
 int moe_combine_bwd(const void* dY, const void* Ys, const float* topk_w,
                     const int32_t* dest_row, int T, int d, int k, int dtype, void* dYs,

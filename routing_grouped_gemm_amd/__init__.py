@@ -27,7 +27,7 @@ __all__ = [
     "moe_route_aux", "moe_check_routing", "moe_workspace_size", "moe_status_string",
     "ExpertLayer", "LIB_PATH",
     "MOE_ROUTE_LOGITS_IN", "MOE_ROUTE_RENORM", "MOE_ACCUMULATE", "MOE_WGRAD_F32", "MOE_MX_KEEP_WEIGHTS",
-    "KernelTimer", "upload", "mx_scale_pitch", "probe_clock",
+    "KernelTimer", "upload", "mx_scale_pitch", "mx_scale_shape", "mx_scale_rows", "probe_clock",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_hip.so")
@@ -223,8 +223,21 @@ def moe_check_routing(topk_idx, E, report, stream=None):
 
 
 def mx_scale_pitch(R: int) -> int:
-    """Row pitch of the block-major MXFP8 activation scales: R rounded up to 16."""
+    """Row pitch of the MXFP8 activation scales: R rounded up to 16."""
     return (R + 15) // 16 * 16
+
+
+def mx_scale_shape(R: int, K: int):
+    """Shape of the MXFP8 activation scales of R rows of K elements: groups of
+    four 32-element blocks, [ceil(K/128)][Rp][4] bytes (Rp = mx_scale_pitch(R));
+    block b of row r is element [b // 4][r][b % 4]."""
+    return ((K + 127) // 128, mx_scale_pitch(R), 4)
+
+
+def mx_scale_rows(scale, R: int, K: int):
+    """View of an activation scale array as [R][K/32] (row r, block b)."""
+    G, Rp, _ = mx_scale_shape(R, K)
+    return scale.reshape(G, Rp, 4).permute(1, 0, 2).reshape(Rp, 4 * G)[:R, :K // 32]
 
 
 def moe_grouped_ffn_fwd(Xs, Xs_scale, offsets, T, k, Wg, Wu, Wd, Hg, Hu, A, Ys, ws=None,
@@ -387,9 +400,9 @@ class ExpertLayer:
         self.Xs = z(R, d)
         if prec == "mxfp8":
             self.Xq = z(R, d, dt=torch.uint8)
-            self.Xq_scale = z(d // 32, mx_scale_pitch(R), dt=torch.uint8)
+            self.Xq_scale = z(*mx_scale_shape(R, d), dt=torch.uint8)
             self.dYs_q = z(R, d, dt=torch.uint8)
-            self.dYs_q_scale = z(d // 32, mx_scale_pitch(R), dt=torch.uint8)
+            self.dYs_q_scale = z(*mx_scale_shape(R, d), dt=torch.uint8)
         else:
             self.Xq = self.Xq_scale = self.dYs_q = self.dYs_q_scale = None
         self.Hg, self.Hu, self.A = z(R, f), z(R, f), z(R, f)

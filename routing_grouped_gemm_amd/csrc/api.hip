@@ -92,9 +92,13 @@ inline int check_elems(long long rows, long long cols) {
 //    A [n_e][f], dH [n_e][2f] and dYs [n_e][d] along K = n_e from one base:
 //    R * max(d, 2f) * 2 bytes below 2^32 (n_e <= R);
 //  * the MXFP8 weight gradients read codes [features][Kp] (Kp = R padded per
-//    expert): 256 rows of a tile span 256 * Kp bytes, and a block-scale column
-//    (Kp / 32) * max(d, 2f) bytes, both below 2^32.
+//    expert): 256 rows of a tile span 256 * Kp bytes, below 2^32;
+//  * every MXFP8 scale array a GEMM reads through one resource stays below
+//    2^30 bytes (offsets past it mark lanes and loads that read nothing):
+//    the token-quantised scales (Kp / 32) * max(d, 2f), the activation
+//    scales ceil(max(d, 2f) / 128) * 4 * Rp (Rp = R rounded up to 16).
 constexpr long long kOff32 = 1LL << 32;
+constexpr long long kScaleRange = 1LL << 30;
 inline int check_weight_offsets(int d, int f) {
   return ((long long)d * (f + 128) * 2 >= kOff32) ? MOE_ERR_UNSUPPORTED : MOE_OK;
 }
@@ -105,7 +109,12 @@ inline int check_wgrad_offsets(long long R, int d, int f) {
 inline int check_mx_wgrad_offsets(long long R, int d, int f, int E) {
   const long long kp = (R + 127LL * E + 127) / 128 * 128;
   const long long w = d > 2LL * f ? d : 2LL * f;
-  return (256 * kp >= kOff32 || (kp / 32) * w >= kOff32) ? MOE_ERR_UNSUPPORTED : MOE_OK;
+  return (256 * kp >= kOff32 || (kp / 32) * w >= kScaleRange) ? MOE_ERR_UNSUPPORTED : MOE_OK;
+}
+inline int check_mx_scale_offsets(long long R, int d, int f) {
+  const long long w = d > 2LL * f ? d : 2LL * f;
+  const long long rp = (R + 15) / 16 * 16;
+  return ((w + 127) / 128 * 4 * rp >= kScaleRange) ? MOE_ERR_UNSUPPORTED : MOE_OK;
 }
 
 template <typename... P>
@@ -374,6 +383,8 @@ int moe_grouped_ffn_fwd(const void* Xs, const uint8_t* Xs_scale, const int32_t* 
   if (int s = check_elems(R, 2LL * (d > f ? d : f))) return s;
   if (int s = check_elems(E, (long long)d * f)) return s;
   if (int s = check_weight_offsets(d, f)) return s;
+  if (prec == MOE_PREC_MXFP8)
+    if (int s = check_mx_scale_offsets(R, d, f)) return s;
   if (!all_aligned(Xs, offsets, Wg, Wu, Wd, Hg, Hu, A, Ys, ws)) return MOE_ERR_ALIGN;
   if (prec == MOE_PREC_MXFP8 && !aligned16(Xs_scale)) return MOE_ERR_ALIGN;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -458,6 +469,8 @@ int moe_grouped_ffn_bwd(const void* dYs, const void* dYs_q, const uint8_t* dYs_q
   if (int s = check_elems(R, 2LL * (d > f ? d : f))) return s;
   if (int s = check_elems(E, (long long)d * f)) return s;
   if (int s = check_weight_offsets(d, f)) return s;
+  if (prec == MOE_PREC_MXFP8)
+    if (int s = check_mx_scale_offsets(R, d, f)) return s;
   if (flags & MOE_WGRAD_MX) {
     if (int s = check_mx_wgrad_offsets(R, d, f, E)) return s;
   } else if (int s = check_wgrad_offsets(R, d, f)) {

@@ -58,10 +58,12 @@ struct GemmArgs {
   const void* h1;  // SWIGLU_BWD: Hu
   long ldh;
   int accumulate;
-  // MXFP8 kinds: E8M0 scale bytes, block-major.  Block b (32 consecutive k)
-  // of A row r is sa[b * sa_pitch + r]; of B row n of group e is
-  // sb[e * sb_es + b * sb_pitch + n].  Operands a / b0 hold e4m3 codes, and
-  // lda / ldb / b_es are in bytes (= elements).
+  // MXFP8 kinds: E8M0 scale bytes.  Block b (32 consecutive k) of B row n
+  // of group e is sb[e * sb_es + b * sb_pitch + n] (block-major); of A row r
+  // sa[b * sa_pitch + r] for the weight gradients (token-quantised operands)
+  // and sa[((b / 4) * sa_pitch + r) * 4 + b % 4] otherwise (activation rows:
+  // four blocks per group, mx_scale_at).  Operands a / b0 hold e4m3 codes,
+  // and lda / ldb / b_es are in bytes (= elements).
   const uint8_t* sa;
   long sa_pitch;
   const uint8_t* sb;
@@ -69,8 +71,8 @@ struct GemmArgs {
   long sb_pitch;
   // MXFP8 kinds whose epilogue output feeds the next MX GEMM (gate/up: A,
   // down dgrad: dH): that output, as stored, block-quantised along its row:
-  // codes at q0 (same layout as the output), block b of row r at
-  // qs[b * qs_pitch + r].
+  // codes at q0 (same layout as the output), scales at qs in the grouped
+  // activation layout with pitch qs_pitch.
   uint8_t* q0;
   uint8_t* qs;
   long qs_pitch;

@@ -878,7 +878,7 @@ __device__ __forceinline__ void epilogue_block(const GemmArgs& g, const Tile& t,
           if constexpr (qout_of<KIND>()) {
             float ar[8];
             round_bf16_8(a, ar);
-            quant8_store(ar, g.q0 + off, g.qs + (n >> 5) * g.qs_pitch + row, lane);
+            quant8_store(ar, g.q0 + off, g.qs + mx_scale_at(row, n, g.qs_pitch), lane);
           }
         }
       }
@@ -912,10 +912,10 @@ __device__ __forceinline__ void epilogue_block(const GemmArgs& g, const Tile& t,
           if constexpr (qout_of<KIND>()) {
             float r[8];
             round_bf16_8(dg, r);
-            quant8_store(r, g.q0 + row * g.ldc + n, g.qs + (n >> 5) * g.qs_pitch + row, lane);
+            quant8_store(r, g.q0 + row * g.ldc + n, g.qs + mx_scale_at(row, n, g.qs_pitch), lane);
             round_bf16_8(du, r);
             quant8_store(r, g.q0 + row * g.ldc + g.c_split + n,
-                         g.qs + ((g.c_split + n) >> 5) * g.qs_pitch + row, lane);
+                         g.qs + mx_scale_at(row, (int)g.c_split + n, g.qs_pitch), lane);
           }
         }
       }

@@ -14,12 +14,15 @@ size_t mx_bwd_workspace(long long R, int d, int f, int E);
 // Backward workspace when the weight gradients are MXFP8 too (the dgrad
 // workspace, then the token-quantised operands).
 size_t mx_wgrad_workspace(long long R, int d, int f, int E);
-// Row pitch of block-major activation scales: R rounded up to 16.
+// Row pitch of the activation scales: R rounded up to 16.  Block b of row r
+// sits at ((b / 4) * pitch + r) * 4 + b % 4, ceil(K / 128) * 4 * pitch bytes
+// for rows of K elements.
 long mx_scale_pitch(long long R);
 
 // For every slot (t, j) with row r = dest_row[t, j] in [0, T*k): Xs[r] = x[t]
-// (bf16); Xq[r] = its e4m3 codes along d and Xq_scale[b * pitch + r] =
-// E_b + 127 for each 32-element block b (pitch: T*k rounded up to 16).
+// (bf16); Xq[r] = its e4m3 codes along d and the scale of each 32-element
+// block b, E_b + 127, at Xq_scale[((b / 4) * pitch + r) * 4 + b % 4] (pitch:
+// T*k rounded up to 16).
 hipError_t launch_mx_dispatch_copy(const void* x, const int32_t* dest_row, int T, int d, int k,
                                    void* Xs, void* Xq, uint8_t* Xq_scale, hipStream_t s);
 // keep: every weight matrix is quantised in one pass for both directions, and

@@ -16,8 +16,10 @@
 //   forward down     Aq[R,f]   x WdT[e][d, f]      (Wd along f, transposed)
 //   down dgrad       dYsq[R,d] x Wd[e][f, d]       (Wd along d, as stored)
 //   gate/up dgrad    dHq[R,2f] x Wgu[e][d, 2f]     (Wg | Wu along f, as stored)
-// Scales are block-major ([block][row]) with the activation row pitch rounded
-// up to 16, so each stage's scales arrive by the same buffer->LDS DMA as the
+// Weight scales are block-major ([block][row]); activation scales come in
+// groups of four blocks, [K/128][row][4] with the row pitch rounded up to 16
+// (mx_scale_at), so a stage's scales of a tile's 256 rows are one contiguous
+// kilobyte.  Either way they arrive by the same buffer->LDS DMA as the
 // codes.  The MFMA is v_mfma_scale_f32_32x32x64_f8f6f4 (e4m3 x e4m3, float32
 // accumulate): within a lane's 32 code bytes, bytes 0-15 belong to the first
 // 32-element K block (scale from lanes 0-31) and bytes 16-31 to the second
@@ -77,7 +79,7 @@ __global__ __launch_bounds__(256) void mx_dispatch_kernel(const bf16_t* __restri
           const u32x4_t w = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
           __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t*>(Xs + (long)r * d + c));
           *reinterpret_cast<uint2*>(Xq + (long)r * d + c) = q[u];
-          if ((lane & 3) == 0) scale[(long)(c >> 5) * pitch + r] = (uint8_t)(E[u] + 127);
+          if ((lane & 3) == 0) scale[mx_scale_at(r, c, pitch)] = (uint8_t)(E[u] + 127);
         }
       }
     }
@@ -401,8 +403,10 @@ __global__ __launch_bounds__(256) void mx_quant_tokens_kernel(
 namespace mf {
 
 // A stage holds 128 code bytes (four 32-element scale blocks) of every tile
-// row of both operands, plus those rows' scales: block b of the A rows at
-// STAGE + b*1024, of the B rows at STAGE + 4096 + b*1024.  One MFMA k-step
+// row of both operands, plus those rows' scales: block b of the B rows at
+// STAGE + 4096 + b*1024; of the A rows of a weight gradient at STAGE +
+// b*1024, of other A rows (grouped activation scales) the 4-byte word of
+// tile row i at STAGE + (amis + i)*4, amis the tile's first row modulo 4.  One MFMA k-step
 // takes 64 codes (two blocks), so a stage is two k-steps.
 constexpr int MX_KSTEP = 64;
 constexpr int SCALE_BYTES = 8192;
@@ -414,10 +418,11 @@ typedef __attribute__((ext_vector_type(8))) int i32x8_t;
 struct MxPlan {
   Plan a, b;
   i32x4_t srs;       // this wave's scale resource (waves 0-1: A, 2-3: B)
-  uint32_t svoff;    // per-lane offset of the scale DMA (kOutside past the tile's rows)
-  uint32_t spitch;   // bytes between consecutive K blocks of the scales
-  int sblk;          // first of the two K blocks of a stage this wave loads (0 or 2)
-  int amis;          // A rows: tile row 0 sits amis bytes into an A scale block
+  uint32_t svoff;    // per-lane offset of the first scale DMA of stage 0 (kOutside: none)
+  uint32_t sdelta;   // offset of the second scale DMA from the first
+  uint32_t sstage;   // bytes between the scales of consecutive stages
+  uint32_t sdst[2];  // LDS offsets of the two scale DMAs in the wave pair's 4 KiB
+  int amis;          // A rows of grouped scales: the tile's first row modulo 4
 };
 
 // Codes of one row for k-step j of a stage: lane half h takes 16-byte chunks
@@ -438,7 +443,7 @@ struct MxFrags {
 
 // Fragments and scales of k-step j of stage kt.  Lanes 0-31 supply the
 // scale of the first block of the k-step, lanes 32-63 of the second.
-template <bool DUAL>
+template <bool DUAL, bool RK>
 __device__ __forceinline__ void load_mx_frags(const char* smem, int kt, int j, int wm, int wn,
                                               int lane, int amis, MxFrags& F) {
   const char* st = smem + (kt & (NST - 1)) * MSTAGE;
@@ -450,7 +455,7 @@ __device__ __forceinline__ void load_mx_frags(const char* smem, int kt, int j, i
   for (int i = 0; i < 4; ++i) {
     const int row = wm * 128 + i * 32;
     F.a[i] = fragq(As, row, j, lane);
-    F.sa[i] = Ss[blk * 1024 + amis + row + (lane & 31)];
+    F.sa[i] = RK ? Ss[blk * 1024 + row + (lane & 31)] : Ss[(amis + row + (lane & 31)) * 4 + blk];
   }
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -480,9 +485,9 @@ __device__ __forceinline__ void mx_mfma16(f32x16_t (&acc)[4][4], const MxFrags& 
 }
 
 // Per-lane scale offset of the lanes past a tile's rows: outside every scale
-// buffer (each is under 2^27 bytes: 1/32 of a code array, whose offsets the
-// host keeps below 2^32), also after the K-block offsets are added, so the
-// lane makes no memory request and writes zeros to LDS bytes never read.
+// buffer (the host keeps each below 2^30 bytes), also after the stage and
+// second-load offsets (each below 2^30) are added, so the lane makes no
+// memory request and writes zeros to LDS bytes never read.
 constexpr uint32_t kOutside = 0x80000000u;
 
 // DMA of stage kt (codes of both operands, then this wave's two scale
@@ -509,14 +514,12 @@ __device__ __forceinline__ void mx_issue(const MxPlan& P, uint32_t pfv, int kt, 
 #pragma unroll
   for (int i = 0; i < DMA_PER_OP; ++i)
     dma16(rb, st_base + OPB + plan_lds(wave, i), (i & 1) ? P.b.v1 : P.b.v0, sob + (uint32_t)i * P.b.bstep);
-  // the block offset goes into the per-lane offset, which the range check covers
+  // the stage offset goes into the per-lane offset, which the range check covers
   const i32x4_t rsc = live_rsrc(P.srs, live);
-  const uint32_t dst = st_base + STAGE + (wave >> 1) * 4096 + P.sblk * 1024;
+  const uint32_t dst = st_base + STAGE + (wave >> 1) * 4096;
 #pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    const uint32_t voff = P.svoff + (uint32_t)(4 * kt + P.sblk + b) * P.spitch;
-    dma16(rsc, dst + b * 1024, voff, 0u);
-  }
+  for (int b = 0; b < 2; ++b)
+    dma16(rsc, dst + P.sdst[b], P.svoff + (uint32_t)b * P.sdelta + (uint32_t)kt * P.sstage, 0u);
   const i32x4_t rpf = live_rsrc(wave < 2 ? P.a.rs0 : P.b.rs0, live && (wave & 1) == 0);
   pf4(rpf, sink, pfv, (uint32_t)(kt + PF_AHEAD) * ROWB);
 }
@@ -536,12 +539,10 @@ __device__ __forceinline__ void mx_issue_piece(const MxPlan& P, uint32_t pfv, in
           (uint32_t)kt * P.b.kstep + (uint32_t)i * P.b.bstep);
   } else {
     const i32x4_t rsc = live_rsrc(P.srs, live);
-    const uint32_t dst = st_base + STAGE + (wave >> 1) * 4096 + P.sblk * 1024;
+    const uint32_t dst = st_base + STAGE + (wave >> 1) * 4096;
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const uint32_t voff = P.svoff + (uint32_t)(4 * kt + P.sblk + b) * P.spitch;
-      dma16(rsc, dst + b * 1024, voff, 0u);
-    }
+    for (int b = 0; b < 2; ++b)
+      dma16(rsc, dst + P.sdst[b], P.svoff + (uint32_t)b * P.sdelta + (uint32_t)kt * P.sstage, 0u);
     const i32x4_t rpf = live_rsrc(wave < 2 ? P.a.rs0 : P.b.rs0, live && (wave & 1) == 0);
     pf4(rpf, sink, pfv, (uint32_t)(kt + PF_AHEAD) * ROWB);
   }
@@ -576,8 +577,18 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mx_kernel(GemmArgs g) {
   // and the expert's K segment starts at byte t.row0 of every row (scale
   // block t.row0 / 32).  g.K is the padded token count.
   constexpr bool RK = KIND == GK_MX_WGRAD || KIND == GK_MX_WGRAD_F32;
+  // Block-major scales (weights; both operands of a weight gradient): the
+  // wave loads blocks sblk and sblk + 1 of every stage, 16 lanes x 16 bytes
+  // each; base is the lane's offset of stage 0's block 0.
+  auto plan_blockmajor = [&](MxPlan& P, long base, long pitch, bool lane_live) {
+    const int sblk = 2 * (wave & 1);
+    P.svoff = lane_live ? (uint32_t)(base + sblk * pitch) : kOutside;
+    P.sdelta = (uint32_t)pitch;
+    P.sstage = (uint32_t)(4 * pitch);
+    P.sdst[0] = (uint32_t)sblk * 1024;
+    P.sdst[1] = P.sdst[0] + 1024;
+  };
   auto plan = [&](const Tile& t, MxPlan& P) {
-    P.sblk = 2 * (wave & 1);
     if constexpr (RK) {
       const long long abytes = (long long)g.M * g.lda, bbytes = (long long)g.N * g.ldb;
       const long aoff = (long)t.m0 * g.lda + t.row0, boff = (long)t.n0 * g.ldb + t.row0;
@@ -585,14 +596,12 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mx_kernel(GemmArgs g) {
       plan_km(P.b, B + boff, bbytes - boff, nullptr, 0, 1 << 30, g.ldb, wave, lane);
       P.amis = 0;
       const int kb = t.row0 >> 5;
-            if (wave < 2) {
+      if (wave < 2) {
         P.srs = make_rsrc(g.sa, (long long)(g.K / 32) * g.sa_pitch);
-        P.svoff = lane < BM / 16 ? (uint32_t)((long)kb * g.sa_pitch + t.m0 + lane * 16) : kOutside;
-        P.spitch = (uint32_t)g.sa_pitch;
+        plan_blockmajor(P, (long)kb * g.sa_pitch + t.m0 + lane * 16, g.sa_pitch, lane < BM / 16);
       } else {
         P.srs = make_rsrc(g.sb, (long long)(g.K / 32) * g.sb_pitch);
-        P.svoff = lane < BM / 16 ? (uint32_t)((long)kb * g.sb_pitch + t.n0 + lane * 16) : kOutside;
-        P.spitch = (uint32_t)g.sb_pitch;
+        plan_blockmajor(P, (long)kb * g.sb_pitch + t.n0 + lane * 16, g.sb_pitch, lane < BM / 16);
       }
     } else {
       // rows of B for this tile: gate/up panels hold 256 rows per 128 f columns
@@ -604,17 +613,26 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mx_kernel(GemmArgs g) {
               g.lda, wave, lane);
       plan_km(P.b, B + (long)t.e * g.b_es + brow0 * g.ldb, (brows - brow0) * g.ldb, nullptr, 0,
               1 << 30, g.ldb, wave, lane);
-      const int row_al = t.row0 & ~15;
+      // every wave reads A fragments, so every wave needs amis
+      const int row_al = t.row0 & ~3;
       P.amis = t.row0 - row_al;
       if (wave < 2) {
-        P.srs = make_rsrc(g.sa, (long long)(g.K / 32) * g.sa_pitch);
-        // scale bytes amis .. amis + 255 of the 16-aligned run
-        P.svoff = lane * 16 < P.amis + BM ? (uint32_t)(row_al + lane * 16) : kOutside;
-        P.spitch = (uint32_t)g.sa_pitch;
+        // Grouped activation scales: stage kt's scales of rows row_al .. are
+        // the run of (amis + 256) 4-byte words at (kt * pitch + row_al) * 4;
+        // wave 0 loads its first kilobyte, wave 1 the rest (at most 12
+        // bytes).  The second DMA of each wave is an empty one (offset past
+        // the range, zeros into LDS bytes never read) so that every wave
+        // counts the same loads.
+        const int o = (wave & 1) * 1024 + lane * 16;
+        P.srs = make_rsrc(g.sa, (long long)((g.K + 127) / 128) * 4 * g.sa_pitch);
+        P.svoff = o < (P.amis + BM) * 4 ? (uint32_t)(row_al * 4 + o) : kOutside;
+        P.sdelta = 1u << 30;
+        P.sstage = (uint32_t)(4 * g.sa_pitch);
+        P.sdst[0] = (uint32_t)(wave & 1) * 1024;
+        P.sdst[1] = 2048 + P.sdst[0];
       } else {
         P.srs = make_rsrc(g.sb + (long)t.e * g.sb_es, (long long)(g.K / 32) * g.sb_pitch);
-        P.svoff = lane < BM / 16 ? (uint32_t)(brow0 + lane * 16) : kOutside;
-        P.spitch = (uint32_t)g.sb_pitch;
+        plan_blockmajor(P, brow0 + lane * 16, g.sb_pitch, lane < BM / 16);
       }
     }
   };
@@ -664,7 +682,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mx_kernel(GemmArgs g) {
       // stage 1 and both prefetches may still be in flight
       wait_vmcnt<MX_DMA_PER_STAGE + 2 * PF_PER_STAGE>();
       barrier();
-      load_mx_frags<DUAL>(smem, 0, 0, wm, wn, lane, P.amis, F0);
+      load_mx_frags<DUAL, RK>(smem, 0, 0, wm, wn, lane, P.amis, F0);
     }
     // One full stage (FIRST: the tile's first, accumulators from a zero
     // operand).  The loop body is one basic block: with a branch between
@@ -672,7 +690,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mx_kernel(GemmArgs g) {
     // barrier and the DMA issue.
     auto stage = [&](int kt, auto FIRST) {
       __builtin_amdgcn_s_waitcnt(kLgkm0);
-      load_mx_frags<DUAL>(smem, kt, 1, wm, wn, lane, P.amis, F1);
+      load_mx_frags<DUAL, RK>(smem, kt, 1, wm, wn, lane, P.amis, F1);
       if constexpr (decltype(FIRST)::value) mx_mfma16_first(acc, F0); else mx_mfma16(acc, F0);
       interleave_mx();
       __builtin_amdgcn_sched_barrier(0);
@@ -683,7 +701,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mx_kernel(GemmArgs g) {
       barrier();
       // read even past the last stage (stale bytes, never used), so that
       // the fragment registers have one definition
-      load_mx_frags<DUAL>(smem, kt + 1, 0, wm, wn, lane, P.amis, F0);
+      load_mx_frags<DUAL, RK>(smem, kt + 1, 0, wm, wn, lane, P.amis, F0);
       __builtin_amdgcn_sched_barrier(0);
       // Stage kt+2's loads (an empty stage's past K) go out one after each
       // MFMA of step 1: a wave stalls while the load path takes a load, and
@@ -831,6 +849,8 @@ hipError_t quant_both(const void* W, int E, int K, int N, uint8_t* dstC, long ds
 }
 
 inline long pitch_rows(long R) { return (R + 15) / 16 * 16; }
+// bytes of the grouped activation scales of R rows of K elements
+inline size_t act_scale_bytes(long R, long K) { return (size_t)((K + 127) / 128) * 4 * pitch_rows(R); }
 inline long fpanel(int f) { return (f + 127) / 128 * 128; }
 
 // Forward workspace pieces, in carving order.
@@ -844,13 +864,13 @@ struct FwdWs {
 FwdWs carve_fwd(void* ws, long long R, int d, int f, int E, bool keep, size_t* total) {
   Carve c{static_cast<char*>(ws)};
   FwdWs w;
-  const long fp = fpanel(f), Rp = pitch_rows(R);
+  const long fp = fpanel(f);
   w.wgu = c.take<uint8_t>((size_t)E * 2 * fp * d);
   w.wgu_s = c.take<uint8_t>((size_t)E * (d / 32) * 2 * fp);
   w.wd = c.take<uint8_t>((size_t)E * d * f);
   w.wd_s = c.take<uint8_t>((size_t)E * (f / 32) * d);
   w.aq = c.take<uint8_t>((size_t)R * f);
-  w.aq_s = c.take<uint8_t>((size_t)(f / 32) * Rp);
+  w.aq_s = c.take<uint8_t>(act_scale_bytes(R, f));
   w.bwd_wd = w.bwd_wd_s = w.bwd_wgu = w.bwd_wgu_s = nullptr;
   if (keep) {
     w.bwd_wd = c.take<uint8_t>((size_t)E * f * d);
@@ -893,11 +913,10 @@ struct BwdWs {
 BwdWs carve_bwd(void* ws, long long R, int d, int f, int E, size_t* total) {
   Carve c{static_cast<char*>(ws)};
   BwdWs w;
-  const long Rp = pitch_rows(R);
   w.wd = c.take<uint8_t>((size_t)E * f * d);
   w.wd_s = c.take<uint8_t>((size_t)E * (d / 32) * f);
   w.dhq = c.take<uint8_t>((size_t)R * 2 * f);
-  w.dhq_s = c.take<uint8_t>((size_t)(2 * f / 32) * Rp);
+  w.dhq_s = c.take<uint8_t>(act_scale_bytes(R, 2L * f));
   w.wgu = c.take<uint8_t>((size_t)E * d * 2 * f);
   w.wgu_s = c.take<uint8_t>((size_t)E * (2 * f / 32) * d);
   if (total) *total = c.used;

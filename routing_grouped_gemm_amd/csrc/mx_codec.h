@@ -51,6 +51,16 @@ __device__ __forceinline__ int quant8(const float (&v)[8], uint32_t (&codes)[2])
   return E;
 }
 
+// Byte offset of the scale of column col's 32-element block in row row of an
+// activation scale array: groups of four consecutive blocks, each group
+// [rows][4] with pitch rows (the row count rounded up to 16).  A row's four
+// scales of one 128-column group are one 4-byte word, a 128-column stage of
+// 256 consecutive rows one contiguous kilobyte, and the four lanes that
+// write a row's scales of one group hit the same word.
+__device__ __forceinline__ long mx_scale_at(long row, int col, long pitch) {
+  return (((long)(col >> 7) * pitch + row) << 2) + ((col >> 5) & 3);
+}
+
 // Block-quantise 8 values of each lane (already rounded to their stored
 // precision) in 32-element blocks held by 4 consecutive lanes, and write the
 // codes to q (8 bytes) and, from the first lane of the block, the biased

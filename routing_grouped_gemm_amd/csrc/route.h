@@ -62,7 +62,8 @@ hipError_t launch_dispatch_copy(int dtype, const void* x, const int32_t* dest_ro
 hipError_t launch_combine(int dtype, const void* Ys, const float* w, const int32_t* dest, int T,
                           int d, int k, void* y, hipStream_t s);
 // dYs_q / dYs_q_scale (optional, bf16 only): the stored dYs rows block-quantised
-// along d (e4m3 codes, E8M0 scales block-major with pitch roundup(T*k, 16)).
+// along d (e4m3 codes; E8M0 scales in the dispatch's Xq_scale layout, pitch
+// roundup(T*k, 16)).
 hipError_t launch_combine_bwd(int dtype, const void* dY, const void* Ys, const float* w,
                               const int32_t* dest, int T, int d, int k, void* dYs, float* dw,
                               void* dYs_q, uint8_t* dYs_q_scale, hipStream_t s);

@@ -330,7 +330,7 @@ __device__ __forceinline__ void combine_bwd_slot(const float (&g)[8], const floa
     // the stored (bf16) row, block-quantised along d for the down dgrad
     float ro[8];
     round_bf16_8(o, ro);
-    quant8_store(ro, q + r * d + c, qs + (long)(c >> 5) * pitch + r, lane);
+    quant8_store(ro, q + r * d + c, qs + mx_scale_at(r, c, pitch), lane);
   }
 }
 

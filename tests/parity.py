@@ -135,6 +135,13 @@ def run_gpu(wl: Workload, inp: Dict[str, np.ndarray], logits: Optional[np.ndarra
     if router and aux_coef:
         names += ["aux_loss", "aux_dp"]
     out = {n: to_np(getattr(layer, n)) for n in names}
+    if wl.prec == "mxfp8":
+        # activation scales as [R][d/32] (row, block); the raw shape is checked too
+        R = wl.T * wl.k
+        for n in ("Xq_scale", "dYs_q_scale"):
+            raw = getattr(layer, n)
+            assert tuple(raw.shape) == rgg.mx_scale_shape(R, wl.d), (n, tuple(raw.shape))
+            out[n] = to_np(rgg.mx_scale_rows(raw, R, wl.d))
     f = wl.f
     out["dHg"], out["dHu"] = out["dH"][:, :f], out["dH"][:, f:]
     return out

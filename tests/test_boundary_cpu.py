@@ -255,6 +255,12 @@ def test_ffn_offset_limits(L):
     assert bwd(1 << 23, 2, 64, 64, flags=0x10, prec=P_MX) == UNSUP    # Kp >= 2^24
     assert bwd(1 << 21, 2, 64, 64, flags=0x10, prec=P_MX, dH=MIS) == ALIGN
     assert bwd(1 << 21, 1, 65536, 64, flags=0x10, prec=P_MX) == UNSUP  # scale column
+    # MXFP8 activation scales: ceil(max(d, 2f) / 128) * 4 * Rp bytes below 2^30
+    fwd_mx = lambda T, k, d, f, Wg=A: L.moe_grouped_ffn_fwd(A, A, A, T, k, d, f, 8, Wg, A, A, BF16,
+                                                            P_MX, 0, A, A, A, A, A, 1 << 20, None)
+    assert fwd_mx(1 << 20, 8, 4096, 64) == UNSUP                      # 32 * 4 * 2^23 = 2^30
+    assert fwd_mx((1 << 20) - 16, 8, 4096, 64, Wg=MIS) == ALIGN       # 2^30 - 2^14
+    # (in the backward the weight-gradient limits are the tighter ones)
 
 
 def test_dispatch_noalloc_validation(L):
@@ -302,3 +308,23 @@ def test_check_routing_validation(L):
     assert f(A, 0, 8, 2, A, None) == SHAPE
     assert f(A, 16, 300, 2, A, None) == UNSUP
     assert f(A, 16, 8, 2, MIS, None) == ALIGN
+
+
+def test_mx_activation_scale_layout():
+    """mx_scale_shape / mx_scale_rows follow the byte layout include/moe.h
+    documents for the activation scales: block b of row r at byte
+    ((b / 4) * Rp + r) * 4 + b % 4 (Rp = R rounded up to 16), including a
+    partial last group (d = 576: 18 blocks) and rows past R in the pitch."""
+    import torch
+    import routing_grouped_gemm_amd as rgg
+    for R, K in ((37, 576), (16, 128), (1, 64), (300, 4096)):
+        G, Rp, four = rgg.mx_scale_shape(R, K)
+        assert (G, Rp, four) == (-(-K // 128), -(-R // 16) * 16, 4)
+        flat = torch.full((G * Rp * 4,), 255, dtype=torch.int64)
+        for r in range(R):
+            for b in range(K // 32):
+                flat[((b // 4) * Rp + r) * 4 + b % 4] = (r * 7 + b * 3) % 251
+        rows = rgg.mx_scale_rows(flat.reshape(G, Rp, 4), R, K)
+        assert tuple(rows.shape) == (R, K // 32)
+        want = (torch.arange(R)[:, None] * 7 + torch.arange(K // 32)[None, :] * 3) % 251
+        assert torch.equal(rows, want)

@@ -49,13 +49,12 @@ def _gpu_quantise(rows_bits: np.ndarray):
     dest, src = torch.empty(T, 1, **i32), torch.empty(T, **i32)
     Xs = torch.empty(T, D, dtype=torch.bfloat16, device="cuda")
     Xq = torch.empty(T, D, dtype=torch.uint8, device="cuda")
-    Rp = rgg.mx_scale_pitch(T)
-    Xq_scale = torch.empty(D // 32, Rp, dtype=torch.uint8, device="cuda")
+    Xq_scale = torch.empty(rgg.mx_scale_shape(T, D), dtype=torch.uint8, device="cuda")
     n = rgg.moe_workspace_size("dispatch", T, D, 1, 64, 1, torch.bfloat16, "mxfp8")
     ws = torch.empty(max(n, 256), dtype=torch.uint8, device="cuda")
     rgg.moe_dispatch(x, idx, 1, counts, offsets, dest, src, Xs, ws, Xq, Xq_scale, "mxfp8")
     torch.cuda.synchronize()
-    return Xq.cpu().numpy(), Xq_scale[:, :T].cpu().numpy().T
+    return Xq.cpu().numpy(), rgg.mx_scale_rows(Xq_scale, T, D).cpu().numpy()
 
 
 def _check(rows_bits: np.ndarray, label: str):

@@ -30,7 +30,7 @@ def _buffers(T, d, E, k, mx):
              Xs=torch.full((R, d), -3.0, dtype=torch.bfloat16, device="cuda"))
     if mx:
         b["Xq"] = torch.full((R, d), 0x55, dtype=torch.uint8, device="cuda")
-        b["Xq_scale"] = torch.full((d // 32, rgg.mx_scale_pitch(R)), 0x55, dtype=torch.uint8,
+        b["Xq_scale"] = torch.full(rgg.mx_scale_shape(R, d), 0x55, dtype=torch.uint8,
                                    device="cuda")
     return b
 
@@ -53,7 +53,7 @@ def _run_pair(T, d, E, k, prec, seed):
     for n in ref:
         a, b = ref[n], got[n]
         if n == "Xq_scale":
-            a, b = a[:, :T * k], b[:, :T * k]
+            a, b = rgg.mx_scale_rows(a, T * k, d), rgg.mx_scale_rows(b, T * k, d)
         assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
                            b.view(torch.int16) if b.dtype == torch.bfloat16 else b), (n, T, E)
     counts, offsets, dest_row, src_token = O.routing_metadata(idx_h, E)
