@@ -190,115 +190,146 @@ __global__ __launch_bounds__(256) void mx_quant_cols_kernel(
 //    4-byte LDS read gives both) and one whole 32-value block of each; the
 //    codes and scales are staged in LDS and written back as whole lines.
 // K and N are multiples of 64 (every width the layer accepts); a tile's
-// halves past them are skipped.
+// halves past them are skipped.  The grid is persistent (about as many
+// workgroups as the chip holds at once): a workgroup takes tiles blockIdx.x,
+// + gridDim.x, ..., and loads its next tile into registers before it
+// quantises the current one, so the loads stream under the arithmetic.
 __global__ __launch_bounds__(256) void mx_quant_both_kernel(
-    const bf16_t* __restrict__ W, int K, int N, uint8_t* __restrict__ dstC, long dstC_es, int half,
-    uint8_t* __restrict__ sC, long sC_es, long pitchC, uint8_t* __restrict__ dstR, long dstR_ld,
-    long col0, uint8_t* __restrict__ sR, long sR_es, long pitchR, int block0) {
+    const bf16_t* __restrict__ W, int E, int K, int N, uint8_t* __restrict__ dstC, long dstC_es,
+    int half, uint8_t* __restrict__ sC, long sC_es, long pitchC, uint8_t* __restrict__ dstR,
+    long dstR_ld, long col0, uint8_t* __restrict__ sR, long sR_es, long pitchR, int block0) {
   constexpr int TP = 136;  // LDS row pitch (bf16): 128 + 8
   __shared__ __attribute__((aligned(16))) bf16_t tile[128 * TP];
-  const int e = blockIdx.z, k0 = blockIdx.y * 128, n0 = blockIdx.x * 128;
   const int t = threadIdx.x, lane = t & 63;
-  const bf16_t* We = W + (long)e * K * N;
+  const int nN = (N + 127) / 128, nK = (K + 127) / 128, ntiles = nN * nK * E;
+  // tile L: n tiles fastest, then k tiles, then experts
+  auto corner = [&](int L, int& e, int& k0, int& n0) {
+    const int q = L / nN;
+    n0 = (L - q * nN) * 128;
+    e = q / nK;
+    k0 = (q - e * nK) * 128;
+  };
+  // this thread's eight 16-byte pieces of tile L: rows t/16 + 16i, columns 8*(t%16) .. +7
+  auto fetch = [&](int L, uint4 (&a)[8]) {
+    int e, k0, n0;
+    corner(L, e, k0, n0);
+    const bf16_t* We = W + (long)e * K * N;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int ch = t + 256 * i, r = ch >> 4, c = (ch & 15) * 8;
-    uint4 a = make_uint4(0, 0, 0, 0);
-    if (k0 + r < K && n0 + c < N)
-      a = *reinterpret_cast<const uint4*>(We + (long)(k0 + r) * N + n0 + c);
-    *reinterpret_cast<uint4*>(&tile[r * TP + c]) = a;
-  }
-  __syncthreads();
-  // along N: rows 16p + t/16, columns 8*(t%16) .. +7
-#pragma unroll 2
-  for (int p = 0; p < 8; ++p) {
-    const int r = 16 * p + (t >> 4), c = (t & 15) * 8;
-    float v[8];
-    unpack8(*reinterpret_cast<const uint4*>(&tile[r * TP + c]), v);
-    const long k = k0 + r;
-    // K and N are multiples of 64: the 4 lanes of a block leave together
-    if (k < K && n0 + c < N)
-      quant8_store(v, dstR + ((long)e * K + k) * dstR_ld + col0 + n0 + c,
-                   sR + (long)e * sR_es + (long)(block0 + ((n0 + c) >> 5)) * pitchR + k, lane);
-  }
-  // along K: columns n0 + 2*(t%64) and +1, k = k0 + 32*(t/64) .. +31 (one
-  // whole 32-value block of each of the two columns, read 4 bytes at a time)
-  const int n = 2 * (t & 63), b = t >> 6;
-  const int kb = k0 + 32 * b;
-  const bool cval = n0 + n < N && kb < K;
-  uint32_t wc[2][8];
-  int ec[2] = {0, 0};
-  if (cval) {
-    float v0[32], v1[32];
-    float a0 = 0.0f, a1 = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const uint32_t w2 = *reinterpret_cast<const uint32_t*>(&tile[(32 * b + i) * TP + n]);
-      v0[i] = __uint_as_float(w2 << 16);
-      v1[i] = __uint_as_float(w2 & 0xffff0000u);
-      a0 = fmaxf(a0, fabsf(v0[i]));
-      a1 = fmaxf(a1, fabsf(v1[i]));
+    for (int i = 0; i < 8; ++i) {
+      const int r = (t >> 4) + 16 * i, c = (t & 15) * 8;
+      a[i] = make_uint4(0, 0, 0, 0);
+      if (k0 + r < K && n0 + c < N)
+        a[i] = *reinterpret_cast<const uint4*>(We + (long)(k0 + r) * N + n0 + c);
     }
+  };
+  int L = blockIdx.x;
+  if (L >= ntiles) return;
+  uint4 nx[8];
+  fetch(L, nx);
+  for (; L < ntiles; L += gridDim.x) {
+    int e, k0, n0;
+    corner(L, e, k0, n0);
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const float(&v)[32] = c ? v1 : v0;
-      const int E = mx_block_exponent(c ? a1 : a0);
-      ec[c] = E;
+    for (int i = 0; i < 8; ++i) {
+      const int r = (t >> 4) + 16 * i, c = (t & 15) * 8;
+      *reinterpret_cast<uint4*>(&tile[r * TP + c]) = nx[i];
+    }
+    __syncthreads();
+    // the next tile's loads are in flight while this one is quantised and written
+    if (L + (int)gridDim.x < ntiles) fetch(L + gridDim.x, nx);
+    // along N: rows 16p + t/16, columns 8*(t%16) .. +7
+#pragma unroll 2
+    for (int p = 0; p < 8; ++p) {
+      const int r = 16 * p + (t >> 4), c = (t & 15) * 8;
+      float v[8];
+      unpack8(*reinterpret_cast<const uint4*>(&tile[r * TP + c]), v);
+      const long k = k0 + r;
+      // K and N are multiples of 64: the 4 lanes of a block leave together
+      if (k < K && n0 + c < N)
+        quant8_store(v, dstR + ((long)e * K + k) * dstR_ld + col0 + n0 + c,
+                     sR + (long)e * sR_es + (long)(block0 + ((n0 + c) >> 5)) * pitchR + k, lane);
+    }
+    // along K: columns n0 + 2*(t%64) and +1, k = k0 + 32*(t/64) .. +31 (one
+    // whole 32-value block of each of the two columns, read 4 bytes at a time)
+    const int n = 2 * (t & 63), b = t >> 6;
+    const int kb = k0 + 32 * b;
+    const bool cval = n0 + n < N && kb < K;
+    uint32_t wc[2][8];
+    int ec[2] = {0, 0};
+    if (cval) {
+      float v0[32], v1[32];
+      float a0 = 0.0f, a1 = 0.0f;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        float sv[8];
+      for (int i = 0; i < 32; ++i) {
+        const uint32_t w2 = *reinterpret_cast<const uint32_t*>(&tile[(32 * b + i) * TP + n]);
+        v0[i] = __uint_as_float(w2 << 16);
+        v1[i] = __uint_as_float(w2 & 0xffff0000u);
+        a0 = fmaxf(a0, fabsf(v0[i]));
+        a1 = fmaxf(a1, fabsf(v1[i]));
+      }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) sv[i] = ldexpf(v[8 * g + i], -E);
-        uint32_t c2[2];
-        e4m3_codes8(sv, c2);
-        wc[c][2 * g] = c2[0];
-        wc[c][2 * g + 1] = c2[1];
+      for (int c = 0; c < 2; ++c) {
+        const float(&v)[32] = c ? v1 : v0;
+        const int ex = mx_block_exponent(c ? a1 : a0);
+        ec[c] = ex;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          float sv[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) sv[i] = ldexpf(v[8 * g + i], -ex);
+          uint32_t c2[2];
+          e4m3_codes8(sv, c2);
+          wc[c][2 * g] = c2[0];
+          wc[c][2 * g + 1] = c2[1];
+        }
       }
     }
-  }
-  // The transposed codes go out as whole 128-byte lines: staged in the tile's
-  // LDS (free once every thread has read it) as 128 code rows, one per
-  // column, of the tile's 128 k (16-byte chunks XOR-swizzled by the row),
-  // plus the four blocks' scales of the 128 columns, then written back a
-  // row's eight chunks by eight consecutive threads.  (Each thread writing
-  // its own 32 bytes to four lines shared with three other waves took 60%
-  // longer than the row half of the pass.)
-  __syncthreads();
-  uint8_t* cs = reinterpret_cast<uint8_t*>(tile);   // 16 KiB of codes, then 512 B of scales
-  auto cswz = [](int r) { return (r >> 1) & 7; };
-  if (cval) {
+    // The transposed codes go out as whole 128-byte lines: staged in the tile's
+    // LDS (free once every thread has read it) as 128 code rows, one per
+    // column, of the tile's 128 k (16-byte chunks XOR-swizzled by the row),
+    // plus the four blocks' scales of the 128 columns, then written back a
+    // row's eight chunks by eight consecutive threads.  (Each thread writing
+    // its own 32 bytes to four lines shared with three other waves took 60%
+    // longer than the row half of the pass.)
+    __syncthreads();
+    uint8_t* cs = reinterpret_cast<uint8_t*>(tile);   // 16 KiB of codes, then 512 B of scales
+    auto cswz = [](int r) { return (r >> 1) & 7; };
+    if (cval) {
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int r = n + c;
-      *reinterpret_cast<uint4*>(cs + r * 128 + (((2 * b) ^ cswz(r)) << 4)) =
-          make_uint4(wc[c][0], wc[c][1], wc[c][2], wc[c][3]);
-      *reinterpret_cast<uint4*>(cs + r * 128 + (((2 * b + 1) ^ cswz(r)) << 4)) =
-          make_uint4(wc[c][4], wc[c][5], wc[c][6], wc[c][7]);
-      cs[16384 + b * 128 + r] = (uint8_t)(ec[c] + 127);
+      for (int c = 0; c < 2; ++c) {
+        const int r = n + c;
+        *reinterpret_cast<uint4*>(cs + r * 128 + (((2 * b) ^ cswz(r)) << 4)) =
+            make_uint4(wc[c][0], wc[c][1], wc[c][2], wc[c][3]);
+        *reinterpret_cast<uint4*>(cs + r * 128 + (((2 * b + 1) ^ cswz(r)) << 4)) =
+            make_uint4(wc[c][4], wc[c][5], wc[c][6], wc[c][7]);
+        cs[16384 + b * 128 + r] = (uint8_t)(ec[c] + 127);
+      }
     }
-  }
-  __syncthreads();
-  const int kvalid = min(128, K - k0), nvalid = min(128, N - n0);
-  // code row of column col (the gate/up panels interleave 128 gate and 128 up rows)
-  auto rowof = [&](int col) -> long {
-    return half >= 0 ? (long)((col >> 7) << 8) + 128 * half + (col & 127) : (long)col;
-  };
+    __syncthreads();
+    const int kvalid = min(128, K - k0), nvalid = min(128, N - n0);
+    // code row of column col (the gate/up panels interleave 128 gate and 128 up rows)
+    auto rowof = [&](int col) -> long {
+      return half >= 0 ? (long)((col >> 7) << 8) + 128 * half + (col & 127) : (long)col;
+    };
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int q = t + 256 * i, r = q >> 3, ch = q & 7;
-    if (r < nvalid && ch * 16 < kvalid) {
-      const uint4 w = *reinterpret_cast<const uint4*>(cs + r * 128 + ((ch ^ cswz(r)) << 4));
-      *reinterpret_cast<uint4*>(dstC + (long)e * dstC_es + rowof(n0 + r) * K + k0 + ch * 16) = w;
+    for (int i = 0; i < 4; ++i) {
+      const int q = t + 256 * i, r = q >> 3, ch = q & 7;
+      if (r < nvalid && ch * 16 < kvalid) {
+        const uint4 w = *reinterpret_cast<const uint4*>(cs + r * 128 + ((ch ^ cswz(r)) << 4));
+        *reinterpret_cast<uint4*>(dstC + (long)e * dstC_es + rowof(n0 + r) * K + k0 + ch * 16) = w;
+      }
     }
-  }
-  // scales: block bb of the 128 columns is 128 consecutive bytes (their code
-  // rows are consecutive), written as eight 16-byte pieces
-  if (t < 32) {
-    const int bb = t >> 3, piece = t & 7;
-    if (bb * 32 < kvalid && piece * 16 < nvalid)
-      *reinterpret_cast<uint4*>(sC + (long)e * sC_es + (long)((k0 >> 5) + bb) * pitchC + rowof(n0) +
-                                piece * 16) =
-          *reinterpret_cast<const uint4*>(cs + 16384 + bb * 128 + piece * 16);
+    // scales: block bb of the 128 columns is 128 consecutive bytes (their code
+    // rows are consecutive), written as eight 16-byte pieces
+    if (t < 32) {
+      const int bb = t >> 3, piece = t & 7;
+      if (bb * 32 < kvalid && piece * 16 < nvalid)
+        *reinterpret_cast<uint4*>(sC + (long)e * sC_es + (long)((k0 >> 5) + bb) * pitchC + rowof(n0) +
+                                  piece * 16) =
+            *reinterpret_cast<const uint4*>(cs + 16384 + bb * 128 + piece * 16);
+    }
+    // every thread is done with the staged codes before the next tile is staged
+    __syncthreads();
   }
 }
 
@@ -839,11 +870,20 @@ hipError_t quant_cols(const void* W, int E, int K, int N, uint8_t* dst, long dst
 // with groups of K rows), from one read of W.
 hipError_t quant_both(const void* W, int E, int K, int N, uint8_t* dstC, long dstC_es, int half,
                       uint8_t* sC, long sC_es, long pitchC, uint8_t* dstR, long dstR_ld, long col0,
-                      uint8_t* sR, long sR_es, long pitchR, int block0, hipStream_t s) {
+                      uint8_t* sR, long sR_es, long pitchR, int block0, int num_cu,
+                      hipStream_t s) {
+  const long ntiles = (long)((N + 127) / 128) * ((K + 127) / 128) * E;
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mx_quant_both_kernel, 256, 0) !=
+          hipSuccess ||
+      per_cu < 1)
+    per_cu = 1;
+  const long cap = (long)num_cu * per_cu;
+  const int grid = (int)(ntiles < cap ? ntiles : cap);
   note_prelaunch("mx_quant_weights", s);
-  hipLaunchKernelGGL(mx_quant_both_kernel, dim3((N + 127) / 128, (K + 127) / 128, E), dim3(256), 0, s,
-                     static_cast<const bf16_t*>(W), K, N, dstC, dstC_es, half, sC, sC_es, pitchC,
-                     dstR, dstR_ld, col0, sR, sR_es, pitchR, block0);
+  hipLaunchKernelGGL(mx_quant_both_kernel, dim3(grid), dim3(256), 0, s,
+                     static_cast<const bf16_t*>(W), E, K, N, dstC, dstC_es, half, sC, sC_es,
+                     pitchC, dstR, dstR_ld, col0, sR, sR_es, pitchR, block0);
   note_launch("mx_quant_weights", s);
   return hipGetLastError();
 }
@@ -978,11 +1018,11 @@ hipError_t mx_ffn_fwd(const void* Xq, const uint8_t* Xscale, const int32_t* offs
   // keep: in the same pass, Wd along d and Wg | Wu along f for the backward
   if (keep) {
     MX_TRY(quant_both(Wg, E, d, f, w.wgu, 2 * fp * d, 0, w.wgu_s, (d / 32) * 2 * fp, 2 * fp,
-                      w.bwd_wgu, 2L * f, 0, w.bwd_wgu_s, (long)(2 * f / 32) * d, d, 0, s));
+                      w.bwd_wgu, 2L * f, 0, w.bwd_wgu_s, (long)(2 * f / 32) * d, d, 0, num_cu, s));
     MX_TRY(quant_both(Wu, E, d, f, w.wgu, 2 * fp * d, 1, w.wgu_s, (d / 32) * 2 * fp, 2 * fp,
-                      w.bwd_wgu, 2L * f, f, w.bwd_wgu_s, (long)(2 * f / 32) * d, d, f / 32, s));
+                      w.bwd_wgu, 2L * f, f, w.bwd_wgu_s, (long)(2 * f / 32) * d, d, f / 32, num_cu, s));
     MX_TRY(quant_both(Wd, E, f, d, w.wd, (long)d * f, -1, w.wd_s, (long)(f / 32) * d, d,
-                      w.bwd_wd, d, 0, w.bwd_wd_s, (long)(d / 32) * f, f, 0, s));
+                      w.bwd_wd, d, 0, w.bwd_wd_s, (long)(d / 32) * f, f, 0, num_cu, s));
   } else {
     MX_TRY(quant_cols(Wg, E, d, f, w.wgu, 2 * fp * d, 0, w.wgu_s, (d / 32) * 2 * fp, 2 * fp, s));
     MX_TRY(quant_cols(Wu, E, d, f, w.wgu, 2 * fp * d, 1, w.wgu_s, (d / 32) * 2 * fp, 2 * fp, s));
