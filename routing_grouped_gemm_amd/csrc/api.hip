@@ -412,6 +412,7 @@ int moe_grouped_ffn_fwd(const void* Xs, const uint8_t* Xs_scale, const int32_t* 
   g.a = Xs; g.lda = d;
   g.b0 = Wg; g.b1 = Wu; g.ldb = f; g.b_es = (long)d * f;
   g.c0 = Hg; g.c1 = Hu; g.c2 = A; g.ldc = f;
+  g.m_fast = 1;
   MOE_TRY(launch_grouped_gemm(GK_FWD_GATEUP, eng, g, num_cu(), st));
   GemmArgs h{};
   h.E = E; h.offsets = offsets; h.rows_total = (int)R; h.ragged = RAG_M;
@@ -419,6 +420,7 @@ int moe_grouped_ffn_fwd(const void* Xs, const uint8_t* Xs_scale, const int32_t* 
   h.a = A; h.lda = f;
   h.b0 = Wd; h.ldb = d; h.b_es = (long)f * d;
   h.c0 = Ys; h.ldc = d;
+  h.m_fast = 1;
   return status_of(launch_grouped_gemm(GK_FWD_DOWN, eng, h, num_cu(), st));
 }
 

@@ -76,6 +76,9 @@ struct GemmArgs {
   uint8_t* q0;
   uint8_t* qs;
   long qs_pitch;
+  // RAG_M tile order within a group: 0 = N-tiles fastest; 1 = M-tiles fastest
+  // whenever the group has fewer M-tiles than N-tiles (sched_decode).
+  int m_fast;
 };
 
 // Operand layouts of the five GEMM kinds of the layer and of the router.

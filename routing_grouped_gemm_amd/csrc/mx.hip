@@ -1036,6 +1036,7 @@ hipError_t mx_ffn_fwd(const void* Xq, const uint8_t* Xscale, const int32_t* offs
   g.sb = w.wgu_s; g.sb_es = (d / 32) * 2 * fp; g.sb_pitch = 2 * fp;
   g.c0 = Hg; g.c1 = Hu; g.c2 = A; g.ldc = f;
   g.q0 = w.aq; g.qs = w.aq_s; g.qs_pitch = Rp;   // A quantised along f in the epilogue
+  g.m_fast = 1;
   MX_TRY(launch_grouped_gemm_mx(GK_MX_GATEUP, g, num_cu, s));
   GemmArgs h{};
   h.E = E; h.offsets = offsets; h.rows_total = R; h.ragged = RAG_M;
@@ -1044,6 +1045,7 @@ hipError_t mx_ffn_fwd(const void* Xq, const uint8_t* Xscale, const int32_t* offs
   h.b0 = w.wd; h.ldb = f; h.b_es = (long)d * f;
   h.sb = w.wd_s; h.sb_es = (long)(f / 32) * d; h.sb_pitch = d;
   h.c0 = Ys; h.ldc = d;
+  h.m_fast = 1;
   return launch_grouped_gemm_mx(GK_MX_DOWN, h, num_cu, s);
 }
 
@@ -1070,6 +1072,7 @@ hipError_t mx_ffn_dgrad(const void* dYsq, const uint8_t* dYsq_scale, const void*
   g.c0 = dH; g.ldc = 2L * f; g.c_split = f;
   g.h0 = Hg; g.h1 = Hu; g.ldh = f;
   g.q0 = w.dhq; g.qs = w.dhq_s; g.qs_pitch = Rp;   // dH quantised along 2f in the epilogue
+  g.m_fast = 1;
   MX_TRY(launch_grouped_gemm_mx(GK_MX_DGRAD_DOWN, g, num_cu, s));
   // gate/up dgrad: Wg | Wu along f into one [d][2f] matrix per expert
   if (!kept) {
@@ -1085,6 +1088,7 @@ hipError_t mx_ffn_dgrad(const void* dYsq, const uint8_t* dYsq_scale, const void*
   h.b0 = w.wgu; h.ldb = 2L * f; h.b_es = (long)d * 2 * f;
   h.sb = w.wgu_s; h.sb_es = (long)(2 * f / 32) * d; h.sb_pitch = d;
   h.c0 = dXs; h.ldc = d;
+  h.m_fast = 1;
   return launch_grouped_gemm_mx(GK_MX_DGRAD_GATEUP, h, num_cu, s);
 }
 
