@@ -61,6 +61,13 @@ SHAPES = {
     "max_E256_k16": ("olmoe_bf16", dict(name="max_E256_k16", T=200, d=128, E=256, f=64, k=16)),
     "max_E256_k16_small": ("olmoe_bf16", dict(name="max_E256_k16_small", T=96, d=128, E=256, f=64,
                                               k=16)),
+    # both tile orders of an expert in one launch: Zipf loads give the
+    # largest expert 8 M-tiles (more than the 5 gate/up and 4 down N-tiles:
+    # N-tiles fastest), the next ones 2-4 (M-tiles fastest where that is fewer
+    # than the N-tiles), the rest one tile or none
+    "order_mix_bf16": ("share1t_bf16", dict(name="order_mix_bf16", T=6000, d=1024, f=640)),
+    "order_mix_mxfp8": ("share1t_bf16", dict(name="order_mix_mxfp8", T=6000, d=1024, f=640,
+                                             prec="mxfp8")),
     "tiny_mxfp8": ("tiny_mxfp8", {}),
     # d = 576: an odd number of 64-deep K stages; f = 320: a half-filled last gate/up panel
     "mid_mxfp8_E8": ("olmoe_mxfp8", dict(name="mid_mxfp8_E8", T=1000, d=576, E=8, f=320, k=2)),
