@@ -356,7 +356,11 @@ def profile_markdown(workload_name: str, kt_dir: str) -> int:
         rows = list(csv.DictReader(fh))
     fwd_only = workload_name.startswith("olmoe_decode")
     w = workload_name
-    steps = "--steps 200 --warmup 20" if fwd_only else "--steps 20 --warmup 2"
+    # the default workload is traced with the bench's own step counts (50
+    # timed after 10 warm-up), so that the trace's average of the priced
+    # kernel compares with the per-launch time of the bench line
+    steps = ("--steps 200 --warmup 20" if fwd_only else
+             "--steps 50 --warmup 10" if w == "olmoe_bf16" else "--steps 20 --warmup 2")
     comp = "" if fwd_only or w != "olmoe_bf16" else " --no-companions"
     what = "the small-batch forward" if fwd_only else "one forward+backward step"
     routed = wl.T * wl.k
