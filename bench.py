@@ -16,10 +16,11 @@ timed region only that kernel's launches are bracketed by HIP events on the
 library's stream, and their mean duration gives the `roofline` object.
 `cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
 `clock` is read by a pure-MFMA probe right after the timed steps.  For the
-default (OLMoE-shaped, bf16) workload, the two ends of the expert-count scan
-and the bf16 and MXFP8 layers are also timed in the same run, one after
-the other and in the same way ("companions"), for the E=128 / E=8
-throughput ratio and the MXFP8 speed-up over bf16.
+default (OLMoE-shaped, bf16) workload, the expert-count scan (E = 8, 32,
+128), the bf16 and MXFP8 layers and one GPU's share of the trillion-scale
+layer are also timed in the same run, one after the other and in the same
+way ("companions"), for the E=128 / E=8 throughput ratio and the MXFP8
+speed-up over bf16.
 """
 from __future__ import annotations
 
@@ -693,6 +694,9 @@ def main(argv=None) -> int:
         e8, e128 = companions["escan_e8_bf16"], companions["escan_e128_bf16"]
         out["expert_scan_tokens_ratio_e128_over_e8"] = round(e128["tokens_per_s"] /
                                                              e8["tokens_per_s"], 4)
+        out["expert_scan_tokens_per_s"] = {
+            str(companions[n]["config"]["experts"]): companions[n]["tokens_per_s"]
+            for n in ("escan_e8_bf16", "escan_e32_bf16", "escan_e128_bf16")}
         out["mxfp8_speedup_over_bf16"] = round(companions["olmoe_bf16"]["ms_per_step"] /
                                                companions["olmoe_mxfp8"]["ms_per_step"], 4)
     print(json.dumps(out), flush=True)
@@ -704,7 +708,8 @@ def main(argv=None) -> int:
 # experts) and the OLMoE-shaped layer with MXFP8 expert GEMMs.
 # the MXFP8 layer is compared with the bf16 layer timed the same way right
 # before it (same step count, no per-kernel events in either)
-COMPANIONS = ("escan_e8_bf16", "escan_e128_bf16", "olmoe_bf16", "olmoe_mxfp8")
+COMPANIONS = ("escan_e8_bf16", "escan_e32_bf16", "escan_e128_bf16", "olmoe_bf16", "olmoe_mxfp8",
+              "share1t_bf16")
 
 
 def time_workload(name: str, seed: int, steps: int = 20, warmup: int = 5):

@@ -104,6 +104,12 @@ enum GemmKind : int {
   GK_MX_WGRAD_F32 = 15    // as GK_MX_WGRAD into float32 gradients
 };
 
+// The weight-gradient kinds: ragged K over each expert's tokens, so their
+// tiles' lengths follow the experts' loads.
+constexpr bool wgrad_kind(int k) {
+  return k == GK_WGRAD || k == GK_WGRAD_F32 || k == GK_MX_WGRAD || k == GK_MX_WGRAD_F32;
+}
+
 // Engines: float32 storage on the SIMT engine, bf16 on MFMA, and bf16 on the
 // SIMT engine for router shapes the MFMA engine does not take (E % 8 != 0).
 enum GemmEngine : int { GEMM_F32_SIMT = 0, GEMM_BF16_MFMA = 1, GEMM_BF16_SIMT = 2 };

@@ -42,7 +42,8 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(GemmArgs g) {
   constexpr bool DUAL = KT<KIND>::BSP == BS_DUAL_N;
   constexpr bool AMN = !KT<KIND>::AK, BMN = !KT<KIND>::BK_;
   constexpr int BNT = DUAL ? BN / 2 : BN;
-  const int ntiles = sched_setup<BM, BNT>(g, sch);
+  const int ntiles = sched_setup<BM, BNT, wgrad_kind(KIND)>(g, sch);
+  const bool alt = wgrad_kind(KIND) && sch.alt;  // alternating rounds (logical_tile)
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform in the wave
@@ -74,9 +75,9 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(GemmArgs g) {
   };
 
   int it = 0;
-  int L = logical_tile(it);
+  int L = logical_tile(it, alt);
   if (L >= ntiles) return;
-  Tile t = sched_decode<BM, BNT>(g, sch, L);
+  Tile t = sched_decode<BM, BNT, wgrad_kind(KIND)>(g, sch, L);
   Plan pa, pb;
   plan_tile<KIND>(g, t, wave, lane, pa, pb);
   pfv = pf_plan(t);
@@ -118,10 +119,10 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(GemmArgs g) {
     int pend_stage = 0;
     // The next tile's coordinates are decoded while this tile's first stage
     // lands (a binary search over the group table in LDS).
-    L = logical_tile(it + 1);
+    L = logical_tile(it + 1, alt);
     const bool has_next = L < ntiles;
     Tile tn = t;
-    if (has_next) tn = sched_decode<BM, BNT>(g, sch, L);
+    if (has_next) tn = sched_decode<BM, BNT, wgrad_kind(KIND)>(g, sch, L);
     for (int kt = 0; kt < nk; ++kt) {
       // step 0 (set F0), reading F1 for step 1
       if (kt == 0) {
@@ -257,10 +258,10 @@ __global__ __launch_bounds__(NTHR) void gemm_simt_kernel(GemmArgs g) {
   __shared__ float As[BK][BM + 4];
   __shared__ float Bs[DUAL ? 2 : 1][BK][BN + 4];
   __shared__ Sched sch;
-  const int ntiles = sched_setup<BM, BN>(g, sch);
+  const int ntiles = sched_setup<BM, BN, wgrad_kind(KIND)>(g, sch);
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
   for (int L = blockIdx.x; L < ntiles; L += gridDim.x) {
-    const Tile t = sched_decode<BM, BN>(g, sch, L);
+    const Tile t = sched_decode<BM, BN, wgrad_kind(KIND)>(g, sch, L);
     float acc[2][4][4] = {};
     for (int k0 = 0; k0 < t.klen; k0 += BK) {
       for (int q = tid; q < BK * BM; q += NTHR) {

@@ -306,7 +306,8 @@ __global__ __launch_bounds__(NTHR8, 1) void gemm8_kernel(GemmArgs g) {
   constexpr bool AMN = !KT<KIND>::AK, BMN = !KT<KIND>::BK_;
   constexpr int BNT = DUAL ? BN / 2 : BN;
   constexpr bool SPLIT = KIND != GK_FWD_GATEUP;  // spread the stage DMA over two k16 steps
-  const int ntiles = sched_setup<BM, BNT>(g, sch);
+  const int ntiles = sched_setup<BM, BNT, wgrad_kind(KIND)>(g, sch);
+  const bool alt = wgrad_kind(KIND) && sch.alt;  // alternating rounds (logical_tile)
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform in the wave
@@ -329,9 +330,9 @@ __global__ __launch_bounds__(NTHR8, 1) void gemm8_kernel(GemmArgs g) {
   };
 
   int it = 0;
-  int L = logical_tile(it);
+  int L = logical_tile(it, alt);
   if (L >= ntiles) return;
-  Tile t = sched_decode<BM, BNT>(g, sch, L);
+  Tile t = sched_decode<BM, BNT, wgrad_kind(KIND)>(g, sch, L);
   Plan pa, pb;
   plan_tile<KIND, DPO8, NW>(g, t, wave, lane, pa, pb);
   int nk = (t.klen + BK - 1) / BK;
@@ -357,10 +358,10 @@ __global__ __launch_bounds__(NTHR8, 1) void gemm8_kernel(GemmArgs g) {
     }
     bool pend_b = false;
     int pend_stage = 0;
-    L = logical_tile(it + 1);
+    L = logical_tile(it + 1, alt);
     const bool has_next = L < ntiles;
     Tile tn = t;
-    if (has_next) tn = sched_decode<BM, BNT>(g, sch, L);
+    if (has_next) tn = sched_decode<BM, BNT, wgrad_kind(KIND)>(g, sch, L);
     for (int kt = 0; kt < nk; ++kt) {
       // step 0 (set F0), reading F1 for step 1
       if (kt == 0) {

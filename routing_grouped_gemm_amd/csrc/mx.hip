@@ -595,7 +595,8 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mx_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(256))) uint32_t pf_sink[64];
   constexpr bool DUAL = KT<KIND>::BSP == BS_DUAL_N;
   constexpr int BNT = DUAL ? BN / 2 : BN;
-  const int ntiles = sched_setup<BM, BNT>(g, sch);
+  const int ntiles = sched_setup<BM, BNT, wgrad_kind(KIND)>(g, sch);
+  const bool alt = wgrad_kind(KIND) && sch.alt;  // alternating rounds (logical_tile)
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
@@ -676,9 +677,9 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mx_kernel(GemmArgs g) {
   };
 
   int it = 0;
-  int L = logical_tile(it);
+  int L = logical_tile(it, alt);
   if (L >= ntiles) return;
-  Tile t = sched_decode<BM, BNT>(g, sch, L);
+  Tile t = sched_decode<BM, BNT, wgrad_kind(KIND)>(g, sch, L);
   MxPlan P;
   plan(t, P);
   uint32_t pfv = pf_plan(t);
@@ -771,13 +772,13 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mx_kernel(GemmArgs g) {
 
     // next tile's stage 0 loads into buffer 0 during this epilogue, which
     // stages through buffer 1; its stage 1 follows the epilogue
-    L = logical_tile(++it);
+    L = logical_tile(++it, alt);
     const bool has_next = L < ntiles;
     Tile tn = t;
     MxPlan Pn = P;
     int nsn = 0, nkn = 0;
     if (has_next) {
-      tn = sched_decode<BM, BNT>(g, sch, L);
+      tn = sched_decode<BM, BNT, wgrad_kind(KIND)>(g, sch, L);
       plan(tn, Pn);
       pfv = pf_plan(tn);
       nsn = tn.klen / MX_KSTEP;

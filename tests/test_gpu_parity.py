@@ -244,7 +244,8 @@ def test_route_bwd_aux_gradient_alone(name):
     assert e1 <= 1e-4 and e2 <= tol and e3 <= tol
 
 
-@pytest.mark.parametrize("name", ["mid_bf16_E64", "share_zipf_bf16", "mid_mxfp8_E8", "tiny_fp32"])
+@pytest.mark.parametrize("name", ["mid_bf16_E64", "share_zipf_bf16", "mid_mxfp8_E8", "tiny_fp32",
+                                  "order_mix_bf16"])
 def test_wgrad_f32(name):
     """Float32 weight gradients of a bf16 layer (MOE_WGRAD_F32) against the
     oracle's float32 variant; a float32 layer is unchanged by the option."""
@@ -271,12 +272,16 @@ def test_wgrad_f32_accumulation_keeps_small_increments(name):
         assert e <= 2e-2, (n, e)
 
 
-@pytest.mark.parametrize("name", ["mid_bf16_E64", "share_zipf_bf16", "mid_bf16_E8"])
+@pytest.mark.parametrize("name", ["mid_bf16_E64", "share_zipf_bf16", "mid_bf16_E8",
+                                  "order_mix_bf16"])
 def test_wgrad_bf16_accumulation(name):
     """bf16 weight gradients accumulated into buffers that hold random
     bf16 values G0 (the same order of magnitude as dW): the result is G0 + dW
     with one bf16 rounding, including the experts that receive no rows (Zipf
-    loads), whose gradients must keep G0."""
+    loads), whose gradients must keep G0.  The Zipf loads of order_mix_bf16
+    (the largest expert several times the mean, about four rounds of
+    weight-gradient tiles) take the longest-first, alternating-round tile
+    order."""
     wl, inp, logits = _layer_case(name)
     ref = run_oracle(wl, inp, logits)
     rng = np.random.default_rng(7)
@@ -290,7 +295,7 @@ def test_wgrad_bf16_accumulation(name):
         e = relerr(gpu[n], init[n].astype(np.float64) + ref[n])
         say(f"  {n}: relerr of G0 + dW {e:.2e}")
         assert e <= 2e-2, (n, e)
-    if name == "share_zipf_bf16":
+    if name in ("share_zipf_bf16", "order_mix_bf16"):
         empty = np.flatnonzero(np.diff(gpu["offsets"]) == 0)
         say(f"  empty experts {empty.tolist()}")
         assert empty.size > 0
@@ -299,7 +304,8 @@ def test_wgrad_bf16_accumulation(name):
 
 
 @pytest.mark.parametrize("name,f32", [("tiny_mxfp8", False), ("mid_mxfp8_E8", False),
-                                      ("mid_mxfp8_E64", True), ("share_zipf_mxfp8", False)])
+                                      ("mid_mxfp8_E64", True), ("share_zipf_mxfp8", False),
+                                      ("order_mix_mxfp8", True)])
 def test_mx_weight_gradients(name, f32):
     """MOE_WGRAD_MX: the weight gradients in MXFP8 too, operands quantised
     along each expert's tokens (odd segment lengths, experts with more and
