@@ -237,36 +237,40 @@ hipError_t launch_router_logits(const uint16_t* x, const uint16_t* Wr, int T, in
 // ---------------------------------------------------------------------------
 // dl16 [T][ld] bf16 (zero past E, ld = 64 * ceil(E / 64)) and Wr [d][E] both
 // run along e in memory, so both MFMA operands come straight from global
-// memory (Wr from L2).  A workgroup takes 32 tokens and each of its waves one
-// of P column parts (P sized for about 4096 waves), 64 columns at a time as
-// four 16x16 blocks per 16-token half (D[column][token] on 16x16x32 bf16
-// MFMAs over K = ld); each weight fragment read from L2 feeds both halves'
-// MFMAs (with 16 tokens a wave, Wr was read twice as often: 156 -> 104 us
-// at 16384 tokens x 4096 x 128 experts, 30 -> 24 us at 8192 x 2048 x 64).  The block sums pass through a private LDS slice so that dx is
+// memory (Wr from L2).  A workgroup takes 64 tokens (32 when ld > 128) and
+// each of its waves one of P column parts, 64 columns at a time as four
+// 16x16 blocks per 16-token quarter (D[column][token] on 16x16x32 bf16
+// MFMAs over K = ld); each weight fragment read from L2 feeds the MFMAs of
+// every quarter, so Wr is read once per 64 tokens (with 16 tokens a wave it
+// was read four times as often: 156 -> 104 us at 16384 tokens x 4096 x 128
+// experts going from 16 to 32 tokens).  The block sums pass through a private LDS slice so that dx is
 // read and written in 16-byte pieces along its rows (8 tokens x 128 bytes
 // per instruction); each element gets one bf16 rounding of old + sum.  The
 // old dx of the next 64 columns is loaded while the current ones are
 // computed; loads are unconditional (clamped to the last group, whose
 // duplicate is not stored).
-// NK = ld / 32 K-steps.
+// NK = ld / 32 K-steps; H 16-token halves per wave (2 or 4: 32 or 64 tokens,
+// each weight fragment feeding H MFMAs).
 constexpr int kRdxPitch = 68;  // floats per token row of a wave's LDS slice (64 + skew)
 
-template <int NK>
+template <int NK, int H>
 __global__ __launch_bounds__(256) void router_dx_kernel(const uint16_t* __restrict__ dl16, int ld,
                                                         const uint16_t* __restrict__ Wr, int T,
                                                         int d, int E, uint16_t* __restrict__ dx) {
-  __shared__ __attribute__((aligned(16))) float slice_all[4][32 * kRdxPitch];
+  constexpr int TW = 16 * H;   // tokens of the workgroup
+  constexpr int NQ = TW / 8;   // dx row groups of a lane
+  __shared__ __attribute__((aligned(16))) float slice_all[4][TW * kRdxPitch];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  // the workgroup's 32 tokens, each wave a column part of them
+  // the workgroup's TW tokens, each wave a column part of them
   const int part = blockIdx.y * 4 + wave, P = gridDim.y * 4;
   const int tl = lane & 15, G = lane >> 4;
-  const int tbase = blockIdx.x * 32;
+  const int tbase = blockIdx.x * TW;
   float* const slice = slice_all[wave];
   // MFMA side: token set h (tokens 16h + tl), lane k-group G supplies
-  // k = 32s + 8G + (0..7); each weight fragment serves both sets
-  bf16x8_t bfr[2][NK];
+  // k = 32s + 8G + (0..7); each weight fragment serves every set
+  bf16x8_t bfr[H][NK];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
+  for (int h = 0; h < H; ++h) {
     const long trow = min(tbase + 16 * h + tl, T - 1);
 #pragma unroll
     for (int s = 0; s < NK; ++s)
@@ -281,12 +285,12 @@ __global__ __launch_bounds__(256) void router_dx_kernel(const uint16_t* __restri
     eok[s] = e < E;
     eoff[s] = min(e, E - 8);
   }
-  // dx side: lane (rows r + 8q, q = 0..3; 8 columns at 8cq)
+  // dx side: lane (rows r + 8q, q = 0..NQ-1; 8 columns at 8cq)
   const int r = lane >> 3, cq = lane & 7;
-  int trw[4];
-  uint16_t* xr[4];
+  int trw[NQ];
+  uint16_t* xr[NQ];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < NQ; ++q) {
     trw[q] = tbase + r + 8 * q;
     xr[q] = dx + (long)min(trw[q], T - 1) * d + 8 * cq;
   }
@@ -297,12 +301,12 @@ __global__ __launch_bounds__(256) void router_dx_kernel(const uint16_t* __restri
   const int ng = min(per, ngrp - g0);
   if (ng <= 0) return;
 
-  auto load_old = [&](int gi, u32x4_t (&o)[4]) __attribute__((always_inline)) {
+  auto load_old = [&](int gi, u32x4_t (&o)[NQ]) __attribute__((always_inline)) {
     const int c0 = 64 * (g0 + min(gi, ng - 1));
 #pragma unroll
-    for (int q = 0; q < 4; ++q) o[q] = *reinterpret_cast<const u32x4_t*>(xr[q] + c0);
+    for (int q = 0; q < NQ; ++q) o[q] = *reinterpret_cast<const u32x4_t*>(xr[q] + c0);
   };
-  auto compute = [&](int gi, const u32x4_t (&o)[4]) __attribute__((always_inline)) {
+  auto compute = [&](int gi, const u32x4_t (&o)[NQ]) __attribute__((always_inline)) {
     const int c0 = 64 * (g0 + gi);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -310,29 +314,33 @@ __global__ __launch_bounds__(256) void router_dx_kernel(const uint16_t* __restri
       u32x4_t w[NK];
 #pragma unroll
       for (int s = 0; s < NK; ++s) w[s] = *reinterpret_cast<const u32x4_t*>(wr + eoff[s]);
-      f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+      f32x4_t acc[H];
+#pragma unroll
+      for (int h = 0; h < H; ++h) acc[h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < NK; ++s) {
         const bf16x8_t a = __builtin_bit_cast(bf16x8_t, eok[s] ? w[s] : u32x4_t{0, 0, 0, 0});
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bfr[0][s], acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bfr[1][s], acc1, 0, 0, 0);
+#pragma unroll
+        for (int h = 0; h < H; ++h)
+          acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bfr[h][s], acc[h], 0, 0, 0);
       }
-      // columns 16j + 4G + (0..3) of tokens tl and 16 + tl
-      *reinterpret_cast<f32x4_t*>(slice + tl * kRdxPitch + 16 * j + 4 * G) = acc0;
-      *reinterpret_cast<f32x4_t*>(slice + (16 + tl) * kRdxPitch + 16 * j + 4 * G) = acc1;
+      // columns 16j + 4G + (0..3) of tokens 16h + tl
+#pragma unroll
+      for (int h = 0; h < H; ++h)
+        *reinterpret_cast<f32x4_t*>(slice + (16 * h + tl) * kRdxPitch + 16 * j + 4 * G) = acc[h];
     }
     // the slice is private to the wave and LDS accesses of a wave complete in order
     __builtin_amdgcn_wave_barrier();
-    f32x4_t v0[4], v1[4];
+    f32x4_t v0[NQ], v1[NQ];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < NQ; ++q) {
       const f32x4_t* pv = reinterpret_cast<const f32x4_t*>(slice + (r + 8 * q) * kRdxPitch + 8 * cq);
       v0[q] = pv[0];
       v1[q] = pv[1];
     }
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < NQ; ++q) {
       float o8[8], v[8];
       unpack8(uint4{o[q][0], o[q][1], o[q][2], o[q][3]}, o8);
 #pragma unroll
@@ -344,7 +352,7 @@ __global__ __launch_bounds__(256) void router_dx_kernel(const uint16_t* __restri
     }
   };
 
-  u32x4_t oa[4], ob[4];
+  u32x4_t oa[NQ], ob[NQ];
   load_old(0, oa);
   for (int gi = 0; gi < ng; gi += 2) {
     load_old(gi + 1, ob);
@@ -359,24 +367,31 @@ bool router_dx_applies(int d, int E) { return E % 8 == 0 && E <= 256 && d % 64 =
 hipError_t launch_router_dx(const uint16_t* dl16, int ld, const uint16_t* Wr, int T, int d, int E,
                             uint16_t* dx, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  // column parts: about 4096 waves in all, 4 to d/64 parts (four a workgroup)
-  const int tiles = (T + 31) / 32;
+  // Up to 128 experts (ld <= 128) a wave takes 64 tokens, so that each weight
+  // fragment read from L2 feeds four MFMAs (the weights are read once per
+  // 64 tokens instead of per 32); wider rows keep 32 tokens a wave (the
+  // token operands' registers).  Column parts: about W waves in all (2048
+  // for 64 tokens, 4096 for 32), 4 to d/64 parts (four a workgroup).
+  const int nk = ld / 32;
+  const int tw = nk <= 4 ? 64 : 32;
+  const int tiles = (T + tw - 1) / tw;
+  const long W = tw == 64 ? 2048 : 4096;
   int P = 4;
-  while (2 * P <= d / 64 && (long)tiles * P < 4096) P *= 2;
+  while (2 * P <= d / 64 && (long)tiles * P < W) P *= 2;
   const dim3 grid(tiles, P / 4);
   note_prelaunch("router_dx", s);
-  switch (ld / 32) {
+  switch (nk) {
     case 2:
-      hipLaunchKernelGGL(router_dx_kernel<2>, grid, dim3(256), 0, s, dl16, ld, Wr, T, d, E, dx);
+      hipLaunchKernelGGL((router_dx_kernel<2, 4>), grid, dim3(256), 0, s, dl16, ld, Wr, T, d, E, dx);
       break;
     case 4:
-      hipLaunchKernelGGL(router_dx_kernel<4>, grid, dim3(256), 0, s, dl16, ld, Wr, T, d, E, dx);
+      hipLaunchKernelGGL((router_dx_kernel<4, 4>), grid, dim3(256), 0, s, dl16, ld, Wr, T, d, E, dx);
       break;
     case 6:
-      hipLaunchKernelGGL(router_dx_kernel<6>, grid, dim3(256), 0, s, dl16, ld, Wr, T, d, E, dx);
+      hipLaunchKernelGGL((router_dx_kernel<6, 2>), grid, dim3(256), 0, s, dl16, ld, Wr, T, d, E, dx);
       break;
     case 8:
-      hipLaunchKernelGGL(router_dx_kernel<8>, grid, dim3(256), 0, s, dl16, ld, Wr, T, d, E, dx);
+      hipLaunchKernelGGL((router_dx_kernel<8, 2>), grid, dim3(256), 0, s, dl16, ld, Wr, T, d, E, dx);
       break;
     default:
       return hipErrorInvalidValue;
