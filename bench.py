@@ -389,6 +389,7 @@ def profile_markdown(workload_name: str, kt_dir: str) -> int:
           "timed steps together)\n")
     print("| kernel | launch name(s) | calls | average µs | share |")
     print("|---|---|---:|---:|---:|")
+    avg_us = {}  # launch name (one name per kernel only) or kernel symbol -> average µs
     for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
         name = _symbol_of(r["Name"])
         if name.startswith("__amd_rocclr") or "elementwise" in name or "at::" in name:
@@ -401,6 +402,9 @@ def profile_markdown(workload_name: str, kt_dir: str) -> int:
         share = 100.0 * float(r["TotalDurationNs"]) / total
         print(f"| `{name}` | {launches} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
               f"{share:.2f}% |")
+        avg_us[name] = float(r["AverageNs"]) / 1e3
+        if sym and len(set(_SYMBOLS[sym])) == 1:
+            avg_us[_SYMBOLS[sym][0]] = float(r["AverageNs"]) / 1e3
     print()
     try:
         with open(TRAFFIC_JSON) as fh:
@@ -415,14 +419,24 @@ def profile_markdown(workload_name: str, kt_dir: str) -> int:
               f"and WRITE_SIZE {1.0 / cal['write_scale']:.4f} of the true bytes, so every counter "
               f"below is multiplied by {cal['fetch_scale']:.4f} (fetch) and "
               f"{cal['write_scale']:.4f} (write).\n")
-        print("| launch | fetch MB | write MB | total MB |")
-        print("|---|---:|---:|---:|")
+        print("The rate is the launch's bytes over its average duration in the trace above, "
+              "where that kernel serves this launch alone (a kernel shared by two launches, "
+              "such as the eight-wave weight-gradient GEMM, has no per-launch average), "
+              f"against the {HBM_PEAK_GBS / 1000:.0f} TB/s HBM peak.\n")
+        print("| launch | fetch MB | write MB | total MB | average µs | GB/s | frac of HBM peak |")
+        print("|---|---:|---:|---:|---:|---:|---:|")
         ks = tw["kernels"]
         for k in sorted(ks, key=lambda k: -(ks[k]["fetch_bytes"] + ks[k]["write_bytes"])):
             f_, w_ = ks[k]["fetch_bytes"] / 1e6, ks[k]["write_bytes"] / 1e6
             if f_ + w_ < 1.0:
                 continue
-            print(f"| `{k}` | {f_:.0f} | {w_:.0f} | {f_ + w_:.0f} |")
+            us = avg_us.get(k)
+            if us:
+                gbs = (f_ + w_) * 1e6 / (us * 1e-6) / 1e9
+                rate = f"{us:.1f} | {gbs:.0f} | {gbs / HBM_PEAK_GBS:.2f}"
+            else:
+                rate = "- | - | -"
+            print(f"| `{k}` | {f_:.0f} | {w_:.0f} | {f_ + w_:.0f} | {rate} |")
         print()
     return 0
 
